@@ -1,0 +1,200 @@
+/*
+ * lit.h -- C ABI of liblit.so: the sparse-attention step of a DeepSeek-V3.2 /
+ * V4.1-style model on one AMD Instinct MI355X (gfx950).
+ *
+ * The step has three parts, each a call below, plus a fused call:
+ *   1. lit_indexer_scores : the lightning indexer scores every visible
+ *      compressed-KV row for every query (head-weighted ReLU of q.k over e4m3
+ *      codes with one ue8m0 scale per 32 values);
+ *   2. lit_topk           : a per-query selector keeps the index_topk best rows;
+ *   3. lit_sparse_attn    : attention with an online softmax over the sliding
+ *      window and the selected compressed rows, one shared KV head (K = V).
+ *   lit_window_indices builds the window row lists; lit_sparse_step runs 1-3
+ *   (window rows derived in-kernel) as one stream-ordered sequence.
+ *
+ * Sources (page title, symbol):
+ *   [V4.1] DeepSeek-V4.1-Flash-NVFP4, inference/model.py -- module globals
+ *          (fp8 block size 32, ue8m0 scales), get_window_topk_idxs,
+ *          Indexer.__init__/forward, Attention._window_kv/_compress_kv/forward
+ *          (the sparse_attn call and its int32 [b, m, topk] index lists).
+ *   [V3.2] DeepSeek-V3.2-Exp, inference/model.py -- Indexer.forward
+ *          (fp8_index over e4m3 key cache + block scales), MLA.forward.
+ *
+ * Conventions for every call:
+ *   - Pointers marked (device) are HIP device pointers, 16-byte aligned; the
+ *     caller owns every buffer and keeps it alive until the stream reaches the
+ *     work.  Nothing is allocated or freed inside a call.
+ *   - All layouts are dense row-major in the order the brackets give.
+ *     "bf16" buffers hold bfloat16 bit patterns (uint16).
+ *   - stream is a hipStream_t (NULL = the default stream).  Every launch is
+ *     asynchronous on it; no call synchronises the host.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     refused call launches nothing and returns the status saying why.
+ *     LIT_E_HIP reports a launch failure (the HIP error is then cleared).
+ *   - Calls are thread-safe and keep no state between calls.
+ */
+#ifndef LIT_H
+#define LIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LIT_ABI_VERSION 1
+
+typedef enum {
+    LIT_OK = 0,
+    LIT_E_NULL = 1,        /* a required pointer is NULL                       */
+    LIT_E_SHAPE = 2,       /* a size is negative, zero where it must not be,   */
+                           /* or sizes are inconsistent with each other        */
+    LIT_E_ALIGN = 3,       /* a pointer or leading dimension is misaligned     */
+    LIT_E_UNSUPPORTED = 4, /* valid, but outside what the kernels implement    */
+    LIT_E_WORKSPACE = 5,   /* workspace NULL or smaller than required          */
+    LIT_E_HIP = 6          /* a HIP launch failed                              */
+} lit_status;
+
+/* Human-readable name of a status (static string, never NULL). */
+const char *lit_status_str(int status);
+
+/* LIT_ABI_VERSION of the loaded library. */
+int lit_abi_version(void);
+
+/*
+ * lit_indexer_scores -- [V4.1] Indexer.forward (score einsum, ReLU, head-weighted
+ * sum, then the -inf mask of rows a query cannot see yet); [V3.2] fp8_index.
+ *
+ *   scores[b,i,t] = sum_h w[b,i,h] * relu( sum_d qhat[b,i,h,d] * khat[b,t,d] )
+ *   qhat = e4m3(q8) * 2^(q_sc - 127), khat = e4m3(k8) * 2^(k_sc - 127), one
+ *   scale byte per 32 consecutive d.
+ *
+ * Row t of the compressed cache stands for tokens t*ratio .. t*ratio+ratio-1; a
+ * query at position P = start_pos + i sees rows t < (P + 1) / ratio.
+ *
+ *   q8    (device) u8   [B, S, Hi, Di]   e4m3 codes of the index queries
+ *   q_sc  (device) u8   [B, S, Hi, Di/32] ue8m0 scale bytes
+ *   w     (device) f32  [B, S, Hi]       final head weights (every constant
+ *                                        factor already folded in)
+ *   k8    (device) u8   [B, T_cap, Di]   e4m3 index-key cache
+ *   k_sc  (device) u8   [B, T_cap, Di/32] ue8m0 scale bytes of the cache
+ *   scores(device) f32  [B, S, ld_scores] output; columns t < T are written,
+ *                       T = (start_pos + S) / ratio; t >= visible -> -inf.
+ * Requirements: Di in {64, 128}; Hi a multiple of 16, at most 64; ratio >= 1;
+ * T <= T_cap; ld_scores >= T and a multiple of 4.  A scale byte of 255 (NaN)
+ * or a NaN e4m3 code gives unspecified scores.
+ */
+lit_status lit_indexer_scores(const uint8_t *q8, const uint8_t *q_sc, const float *w,
+                              const uint8_t *k8, const uint8_t *k_sc, int B, int S,
+                              int Hi, int Di, int T_cap, int start_pos, int ratio,
+                              float *scores, int ld_scores, void *stream);
+
+/*
+ * lit_topk -- [V4.1] Indexer.forward (top-k, re-sorted into position order,
+ * unreachable picks -> -1); [V3.2] Indexer.forward (topk of min(index_topk, T)).
+ *
+ * Every row (b, i) gets k_eff = min(index_topk, (start_pos + S) / ratio) entries:
+ * the row numbers of its k_eff highest scores among its visible rows
+ * t < (start_pos + i + 1) / ratio, in ascending order, followed by -1 in the
+ * slots a short row cannot fill.  Equal scores are taken lowest row first.
+ *
+ *   scores (device) f32 [B, S, ld_scores]  (only visible columns are read)
+ *   idx    (device) i32 [B, S, k_eff]      output
+ *   ws, ws_bytes    workspace; lit_topk_workspace_bytes() gives the size
+ *                   (currently 0: NULL is accepted)
+ * Requirements: ld_scores multiple of 4 and >= T; NaN scores unspecified.
+ */
+lit_status lit_topk(const float *scores, int ld_scores, int B, int S, int start_pos,
+                    int ratio, int index_topk, int32_t *idx, void *ws, size_t ws_bytes,
+                    void *stream);
+size_t lit_topk_workspace_bytes(int B, int S, int start_pos, int ratio, int index_topk);
+
+/*
+ * lit_window_indices -- [V4.1] get_window_topk_idxs, generalised to a chunk
+ * that starts after position 0.
+ *
+ * The window source is a ring of R slots holding position p in slot p mod R.
+ * The query at P = start_pos + i attends to positions max(0, P-W+1) .. P:
+ *   start_pos == 0: width min(S, W); entry j is position max(0, i-W+1) + j, or -1
+ *                   when that lies past the query;
+ *   start_pos  > 0: width W; entry j is position P-W+1+j (oldest first), or -1
+ *                   when that is before the sequence start.
+ * Each listed position is written as its slot p mod R.
+ *
+ *   win_idx (device) i32 [B, S, width] output (same for every b)
+ * Requirements: R >= the span of needed positions (S when start_pos == 0,
+ * else min(start_pos + S, W + S - 1)).
+ */
+lit_status lit_window_indices(int B, int S, int start_pos, int W, int R, int32_t *win_idx,
+                              void *stream);
+int lit_window_width(int S, int start_pos, int W);
+
+/*
+ * lit_sparse_attn -- [V4.1] Attention.forward's sparse_attn call over the window
+ * KV and the compressed KV; [V3.2] MLA.forward gives the dense equivalent.
+ *
+ * For each (b, i, h) the row set J is the window slots listed in win_idx
+ * followed by the compressed rows listed in comp_idx (-1 entries skipped,
+ * repeats kept).  One bf16 row serves as key and value:
+ *   l_j = scale * sum_{d<D} q[b,i,h,d] * row_j[d]
+ *   out[b,i,h,d] = sum_j e^(l_j) row_j[d] / (sum_j e^(l_j) + e^(sink[h])), d < dv
+ * The sink (nullable) is an extra logit per head that enters only the
+ * normaliser.  An empty J gives 0.
+ *
+ *   q        (device) bf16 [B, S, H, D]  post-RoPE queries
+ *   win_kv   (device) bf16 [B, R, D]     window source (ring slots); NULL if W == 0
+ *   win_idx  (device) i32  [B, S, W]     slots, or -1
+ *   comp_kv  (device) bf16 [B, T_cap, D] compressed KV; NULL if K == 0
+ *   comp_idx (device) i32  [B, S, K]     rows, or -1
+ *   sink     (device) f32  [H] or NULL
+ *   out      (device) bf16 [B, S, H, dv] output
+ *   ws, ws_bytes  workspace, lit_sparse_attn_workspace_bytes() bytes
+ * Requirements: H == 16; D in {64, 128, 192, 256}; dv a multiple of 16 and
+ * <= D; every listed slot < R and row < T_cap (checked on the device: an
+ * out-of-range entry is treated as -1).
+ */
+lit_status lit_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv,
+                           const uint16_t *win_kv, int R, const int32_t *win_idx, int W,
+                           const uint16_t *comp_kv, int T_cap, const int32_t *comp_idx,
+                           int K, const float *sink, float scale, uint16_t *out, void *ws,
+                           size_t ws_bytes, void *stream);
+size_t lit_sparse_attn_workspace_bytes(int B, int S, int H, int dv, int W, int K);
+
+/*
+ * lit_sparse_step -- the whole step for one layer: lit_indexer_scores, lit_topk
+ * and lit_sparse_attn, with the window rows of lit_window_indices derived
+ * in-kernel from (start_pos, W, R).  [V4.1] Attention.forward with
+ * _compress_topk_idxs; the -1 / position-order contract of the top-k list is
+ * that of lit_topk.  Scores and attention partials live in the workspace.
+ */
+typedef struct lit_step_args {
+    /* positions */
+    int B, S, start_pos, ratio;
+    /* indexer */
+    int Hi, Di, index_topk, T_cap;
+    const uint8_t *q8;   /* [B,S,Hi,Di]      */
+    const uint8_t *q_sc; /* [B,S,Hi,Di/32]   */
+    const float *w;      /* [B,S,Hi]         */
+    const uint8_t *k8;   /* [B,T_cap,Di]     */
+    const uint8_t *k_sc; /* [B,T_cap,Di/32]  */
+    /* attention */
+    int H, D, dv, W, R;
+    const uint16_t *q;       /* [B,S,H,D] bf16     */
+    const uint16_t *win_kv;  /* [B,R,D] bf16       */
+    const uint16_t *comp_kv; /* [B,T_cap,D] bf16   */
+    const float *sink;       /* [H] or NULL        */
+    float scale;
+    /* outputs */
+    int32_t *topk_idx; /* [B,S,k_eff]  (device) */
+    uint16_t *out;     /* [B,S,H,dv] bf16        */
+} lit_step_args;
+
+lit_status lit_sparse_step(const lit_step_args *args, void *ws, size_t ws_bytes, void *stream);
+size_t lit_sparse_step_workspace_bytes(const lit_step_args *args);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIT_H */

@@ -1,0 +1,179 @@
+"""Seeded synthetic inputs for the sparse-attention step.
+
+This module is shared by the tests, the bench and the smoke check, and is the only
+code both the HIP path's callers and the CPU oracle's callers use.  It holds no part
+of the method's arithmetic: only random draws, the bf16 / e4m3 casts of a library
+(torch), and the block quantiser that writes e4m3 codes with one ue8m0 scale per 32
+values (the format of the DeepSeek-V4.1-Flash-NVFP4 ``inference/model.py`` module
+globals).  The quantiser's rounding rule is not on the pages; any rule that yields
+valid bytes will do, because both sides consume the same bytes.
+
+Recipe (per workload, ``numpy.random.Generator(PCG64(seed))``):
+
+* attention q, window KV, compressed KV ~ N(0, 1), rounded to bf16 (RNE);
+* indexer q and keys ~ N(0, 1), quantised to e4m3 with a ue8m0 scale per 32
+  values: scale exponent e = ceil(log2(amax / 448)), codes = RNE(x / 2^e);
+* head weights w ~ U(0, 1) in fp32;
+* ``keys="boost"``: 5% of each sequence's key rows multiplied by 4, which leaves
+  the e4m3 codes unchanged and adds 2 to each of the row's scale bytes;
+* ``keys="mixture"``: keys = mu_z + 0.1 * eps with 64 centroids mu ~ N(0, I),
+  z uniform, eps ~ N(0, I).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float array -> uint16 bf16 bit patterns (round to nearest even, via torch)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def quantize_e4m3_ue8m0(x: torch.Tensor, block: int = 32):
+    """Block quantiser: x [..., D] -> (codes uint8 [..., D], scales uint8 [..., D/block]).
+
+    Works on CPU or GPU tensors.  The scale is the smallest power of two 2^e with
+    amax / 2^e <= 448; an all-zero block gets the smallest scale byte (0).
+    """
+    assert x.shape[-1] % block == 0
+    xf = x.float()
+    xb = xf.unflatten(-1, (-1, block))
+    amax = xb.abs().amax(dim=-1)
+    safe = torch.where(amax > 0, amax, torch.ones_like(amax))
+    e = torch.ceil(torch.log2(safe / E4M3_MAX))
+    # guard the float log2 rounding: make sure amax / 2^e <= 448 really holds
+    e = torch.where(safe / torch.exp2(e) > E4M3_MAX, e + 1, e)
+    e = torch.where(amax > 0, e, torch.full_like(e, -127.0)).clamp(-127, 127)
+    y = xb / torch.exp2(e).unsqueeze(-1)
+    codes = y.clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+    scales = (e + 127).to(torch.uint8)
+    return codes.flatten(-2), scales
+
+
+def _quant_np(x: np.ndarray):
+    c, s = quantize_e4m3_ue8m0(torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)))
+    return c.numpy().copy(), s.numpy().copy()
+
+
+@dataclasses.dataclass
+class StepInputs:
+    """Host arrays for one step plus its sizes.  bf16 tensors are uint16 bit patterns."""
+    name: str
+    B: int
+    S: int
+    start_pos: int
+    ratio: int
+    Hi: int
+    Di: int
+    H: int
+    D: int
+    dv: int
+    W: int
+    R: int
+    T_cap: int
+    index_topk: int
+    scale: float
+    q8: np.ndarray       # [B,S,Hi,Di] u8 e4m3
+    q_sc: np.ndarray     # [B,S,Hi,Di/32] u8 e8m0
+    w: np.ndarray        # [B,S,Hi] f32
+    k8: np.ndarray       # [B,T_cap,Di] u8 e4m3
+    k_sc: np.ndarray     # [B,T_cap,Di/32] u8 e8m0
+    q: np.ndarray        # [B,S,H,D] bf16 bits
+    win_kv: np.ndarray   # [B,R,D] bf16 bits
+    comp_kv: np.ndarray  # [B,T_cap,D] bf16 bits
+    sink: Optional[np.ndarray] = None  # [H] f32 or None
+    seed: int = 0
+
+    @property
+    def end_pos(self) -> int:
+        return self.start_pos + self.S
+
+    @property
+    def T(self) -> int:
+        return self.end_pos // self.ratio if self.ratio > 0 else 0
+
+    @property
+    def k_eff(self) -> int:
+        return min(self.index_topk, self.T)
+
+
+def make_step(*, B: int, S: int, start_pos: int, ratio: int, Hi: int, Di: int, H: int,
+              D: int, W: int, index_topk: int, seed: int, dv: Optional[int] = None,
+              R: Optional[int] = None, T_cap: Optional[int] = None, keys: str = "normal",
+              sink: Optional[np.ndarray] = None, scale: Optional[float] = None,
+              name: str = "custom") -> StepInputs:
+    """Draw one step's inputs.  R defaults to the smallest window source that holds
+    every needed position; T_cap defaults to the visible compressed row count."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    end_pos = start_pos + S
+    T = end_pos // ratio if ratio > 0 else 0
+    if T_cap is None:
+        T_cap = max(T, 1)
+    if R is None:
+        R = max(1, S if start_pos == 0 else W + S - 1)
+    dv = D if dv is None else dv
+    scale = D ** -0.5 if scale is None else scale
+    f32 = np.float32
+
+    q8, q_sc = _quant_np(rng.standard_normal((B, S, Hi, Di), dtype=f32))
+    w = rng.random((B, S, Hi), dtype=f32)
+    if keys == "mixture":
+        mu = rng.standard_normal((64, Di), dtype=f32)
+        z = rng.integers(0, 64, size=(B, T_cap))
+        kf = mu[z] + f32(0.1) * rng.standard_normal((B, T_cap, Di), dtype=f32)
+    else:
+        kf = rng.standard_normal((B, T_cap, Di), dtype=f32)
+    k8, k_sc = _quant_np(kf)
+    if keys == "boost":
+        n_boost = max(1, int(round(0.05 * T_cap)))
+        for b in range(B):
+            rows = rng.choice(T_cap, size=n_boost, replace=False)
+            # x4 = 2^2: codes stay, every block scale of the row rises by 2
+            k_sc[b, rows] = np.minimum(k_sc[b, rows].astype(np.int32) + 2, 254).astype(np.uint8)
+    q = to_bf16_bits(rng.standard_normal((B, S, H, D), dtype=f32))
+    win_kv = to_bf16_bits(rng.standard_normal((B, R, D), dtype=f32))
+    comp_kv = to_bf16_bits(rng.standard_normal((B, T_cap, D), dtype=f32))
+    return StepInputs(name=name, B=B, S=S, start_pos=start_pos, ratio=ratio, Hi=Hi, Di=Di,
+                      H=H, D=D, dv=dv, W=W, R=R, T_cap=T_cap, index_topk=index_topk,
+                      scale=scale, q8=q8, q_sc=q_sc, w=w, k8=k8, k_sc=k_sc, q=q,
+                      win_kv=win_kv, comp_kv=comp_kv, sink=sink, seed=seed)
+
+
+# The five workloads of the sparse-attention step.  Decode with "context L" is one query
+# at start_pos = L-1 (so end_pos = L and L/r compressed rows are visible).
+WORKLOADS = {
+    "decode-1k": dict(B=1, S=1, start_pos=1023, ratio=2, Hi=16, Di=64, H=16, D=128, W=128,
+                      index_topk=64, seed=20261212),
+    "decode-4k-r2": dict(B=4, S=1, start_pos=4095, ratio=2, Hi=16, Di=64, H=16, D=128, W=128,
+                         index_topk=64, seed=20261222, keys="boost"),
+    "decode-4k-r1": dict(B=4, S=1, start_pos=4095, ratio=1, Hi=16, Di=64, H=16, D=128, W=128,
+                         index_topk=64, seed=20261223, keys="boost"),
+    "decode-16k": dict(B=8, S=1, start_pos=16383, ratio=2, Hi=64, Di=128, H=16, D=192, W=128,
+                       index_topk=2048, seed=20261232),
+    "prefill-16k": dict(B=1, S=4096, start_pos=12288, ratio=2, Hi=16, Di=64, H=16, D=128,
+                        W=128, index_topk=512, seed=20261242),
+    "decode-128k": dict(B=2, S=1, start_pos=131071, ratio=4, Hi=64, Di=128, H=16, D=128,
+                        W=128, index_topk=2048, seed=20261252, keys="mixture"),
+}
+
+
+def workload(name: str, **overrides) -> StepInputs:
+    kw = dict(WORKLOADS[name])
+    kw.update(overrides)
+    return make_step(name=name, **kw)
+
+
+def random_scores(B: int, S: int, T: int, seed: int, ties: bool = False) -> np.ndarray:
+    """fp32 score rows for testing a selector alone; with ``ties`` the values come from
+    a small set so that many rows share a score."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if ties:
+        return rng.integers(-4, 5, size=(B, S, T)).astype(np.float32)
+    return rng.standard_normal((B, S, T), dtype=np.float32)

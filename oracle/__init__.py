@@ -1,0 +1,246 @@
+"""Plain fp64 CPU oracle for the sparse-attention step (indexer -> top-k -> attention).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's CPU-baseline leg
+are the only callers.  The product path (``lightning_indexer_top_amd``) never imports
+this package, and this package never imports the product path: the two share nothing
+but the seeded input generator.
+
+The arithmetic lives in ``lit_oracle.c`` (plain C, double precision, OpenMP over
+queries); this module only marshals numpy arrays into it and composes the steps.
+Sources are cited per function there:
+
+* DeepSeek-V4.1-Flash-NVFP4 ``inference/model.py``: module globals (e4m3 with one
+  ue8m0 scale per 32 values), ``get_window_topk_idxs``, ``Indexer.forward``,
+  ``Attention.forward``.
+* DeepSeek-V3.2-Exp ``inference/model.py``: ``Indexer.forward`` (``fp8_index``) and
+  ``MLA.forward`` (dense scores, index mask, softmax).
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py`` (closed
+forms, library routines on special cases, invariants, derived integer cases); the
+composed step has no end-to-end expected values on the pages and is pinned only
+through its parts.
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lit_oracle.c")
+_LIB = os.path.join(_HERE, "liblit_oracle.so")
+
+ORC_E_ARG = -1
+ORC_E_CODE = -2
+ORC_E_INDEX = -3
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, no FMA contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _bind(path: str):
+    """Open a compiled oracle library and declare its signatures."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.orc_e4m3.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3.restype = ctypes.c_double
+    lib.orc_e8m0.argtypes = [ctypes.c_uint8]
+    lib.orc_e8m0.restype = ctypes.c_double
+    lib.orc_bf16.argtypes = [ctypes.c_uint16]
+    lib.orc_bf16.restype = ctypes.c_double
+    lib.orc_n_visible.argtypes = [I, I, I]
+    lib.orc_n_visible.restype = I
+    lib.orc_index_scores.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.orc_index_scores.restype = I
+    lib.orc_topk_width.argtypes = [I, I, I, I]
+    lib.orc_topk_width.restype = I
+    lib.orc_topk.argtypes = [P, I, I, I, I, I, I, P]
+    lib.orc_topk.restype = I
+    lib.orc_window_width.argtypes = [I, I, I]
+    lib.orc_window_width.restype = I
+    lib.orc_window_indices.argtypes = [I, I, I, I, I, P]
+    lib.orc_window_indices.restype = I
+    lib.orc_sparse_attn.argtypes = [P, I, I, I, I, I, P, I, P, I, P, I, P, I, P,
+                                    ctypes.c_double, P]
+    lib.orc_sparse_attn.restype = I
+    lib.orc_num_threads.argtypes = []
+    lib.orc_num_threads.restype = I
+    lib.orc_set_num_threads.argtypes = [I]
+    lib.orc_set_num_threads.restype = None
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        _lib = _bind(_LIB)
+    return _lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Run the wrappers against another build of the oracle source (used by the
+    mutation tests, which compile deliberately broken copies on the CPU)."""
+    global _lib
+    saved = _load()
+    _lib = _bind(path)
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise OracleError(f"{what} refused its arguments (code {rc})")
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# -- byte formats -----------------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    return _load().orc_e4m3(code)
+
+
+def e8m0_value(code: int) -> float:
+    return _load().orc_e8m0(code)
+
+
+def bf16_value(bits: int) -> float:
+    return _load().orc_bf16(bits)
+
+
+def decode_e4m3(codes) -> np.ndarray:
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.orc_e4m3(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+# -- steps --------------------------------------------------------------------
+
+def n_visible(start_pos: int, i: int, ratio: int) -> int:
+    return _load().orc_n_visible(start_pos, i, ratio)
+
+
+def topk_width(S: int, start_pos: int, ratio: int, index_topk: int) -> int:
+    return _load().orc_topk_width(S, start_pos, ratio, index_topk)
+
+
+def window_width(S: int, start_pos: int, W: int) -> int:
+    return _load().orc_window_width(S, start_pos, W)
+
+
+def index_scores(q8, q_sc, w, k8, k_sc, start_pos: int, ratio: int) -> np.ndarray:
+    """Scores [B,S,T] (float64, -inf where invisible), T = (start_pos+S)//ratio."""
+    q8 = _c(q8, np.uint8)
+    q_sc = _c(q_sc, np.uint8)
+    w = _c(w, np.float32)
+    k8 = _c(k8, np.uint8)
+    k_sc = _c(k_sc, np.uint8)
+    B, S, Hi, Di = q8.shape
+    T_cap = k8.shape[1]
+    T = (start_pos + S) // ratio
+    out = np.empty((B, S, T), dtype=np.float64)
+    rc = _load().orc_index_scores(_ptr(q8), _ptr(q_sc), _ptr(w), _ptr(k8), _ptr(k_sc),
+                                  B, S, Hi, Di, T_cap, start_pos, ratio, _ptr(out))
+    _check(rc, "orc_index_scores")
+    return out
+
+
+def topk(scores, start_pos: int, ratio: int, index_topk: int) -> np.ndarray:
+    """Top-k row lists [B,S,k_eff] int32: ascending, -1 padded."""
+    scores = _c(scores, np.float64)
+    B, S, ld = scores.shape
+    keff = topk_width(S, start_pos, ratio, index_topk)
+    out = np.empty((B, S, keff), dtype=np.int32)
+    rc = _load().orc_topk(_ptr(scores), ld, B, S, start_pos, ratio, index_topk, _ptr(out))
+    _check(rc, "orc_topk")
+    return out
+
+
+def window_indices(B: int, S: int, start_pos: int, W: int, R: int) -> np.ndarray:
+    width = window_width(S, start_pos, W)
+    out = np.empty((B, S, width), dtype=np.int32)
+    rc = _load().orc_window_indices(B, S, start_pos, W, R, _ptr(out))
+    _check(rc, "orc_window_indices")
+    return out
+
+
+def sparse_attn(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float,
+                dv: int | None = None) -> np.ndarray:
+    """Attention output [B,S,H,dv] float64 from bf16 bit patterns (uint16 arrays)."""
+    q = _c(q, np.uint16)
+    B, S, H, D = q.shape
+    dv = D if dv is None else dv
+    if win_idx is None or win_idx.shape[-1] == 0:
+        W, R, win_kv_c, win_idx_c = 0, 0, None, None
+    else:
+        win_kv_c = _c(win_kv, np.uint16)
+        win_idx_c = _c(win_idx, np.int32)
+        W, R = win_idx_c.shape[-1], win_kv_c.shape[1]
+    if comp_idx is None or comp_idx.shape[-1] == 0:
+        K, T_cap, comp_kv_c, comp_idx_c = 0, 0, None, None
+    else:
+        comp_kv_c = _c(comp_kv, np.uint16)
+        comp_idx_c = _c(comp_idx, np.int32)
+        K, T_cap = comp_idx_c.shape[-1], comp_kv_c.shape[1]
+    sink_c = None if sink is None else _c(sink, np.float32)
+    out = np.empty((B, S, H, dv), dtype=np.float64)
+    rc = _load().orc_sparse_attn(_ptr(q), B, S, H, D, dv, _ptr(win_kv_c), R, _ptr(win_idx_c), W,
+                                 _ptr(comp_kv_c), T_cap, _ptr(comp_idx_c), K, _ptr(sink_c),
+                                 float(scale), _ptr(out))
+    _check(rc, "orc_sparse_attn")
+    return out
+
+
+def step(inp, fp32_scores: bool = True) -> dict:
+    """The whole step: index scores -> top-k -> window rows -> attention.
+
+    ``inp`` is a ``lightning_indexer_top_amd.synth.StepInputs``-like object (numpy
+    arrays plus sizes).  With ``fp32_scores`` the scores are rounded to float32 before
+    selection, so the oracle takes its top-k decision in the precision the kernel keeps
+    its scores in; the scores themselves are still the exact fp64 values.
+    """
+    s = index_scores(inp.q8, inp.q_sc, inp.w, inp.k8, inp.k_sc, inp.start_pos, inp.ratio)
+    sel = s.astype(np.float32).astype(np.float64) if fp32_scores else s
+    idx = topk(sel, inp.start_pos, inp.ratio, inp.index_topk)
+    win = window_indices(inp.B, inp.S, inp.start_pos, inp.W, inp.R)
+    o = sparse_attn(inp.q, inp.win_kv, win, inp.comp_kv, idx, inp.sink, inp.scale, inp.dv)
+    return {"scores": s, "idx": idx, "win_idx": win, "out": o}
+
+
+def num_threads() -> int:
+    return _load().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    _load().orc_set_num_threads(n)

@@ -1,0 +1,359 @@
+/*
+ * lit_oracle.c -- plain fp64 CPU oracle for the sparse-attention step
+ * (lightning indexer -> per-query top-k -> attention over window + selected rows).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  It shares no code, header, table or
+ * helper with the HIP library: it decodes the byte formats itself, loops over
+ * the definitions in the order the pages state them, and accumulates in double.
+ * It is deliberately slow and unblocked so that every line can be checked
+ * against the pages by eye.
+ *
+ * Sources (cited by page title and symbol):
+ *   [V4.1] DeepSeek-V4.1-Flash-NVFP4, inference/model.py
+ *          module globals (fp8 block size, ue8m0 scale format), get_window_topk_idxs,
+ *          Indexer.forward, Attention._window_kv, Attention.forward.
+ *   [V3.2] DeepSeek-V3.2-Exp, inference/model.py
+ *          Indexer.forward (fp8_index over e4m3 keys with block scales),
+ *          MLA.forward (dense scores + index mask + softmax: the brute-force form).
+ *
+ * Every function returns 0 on success and a negative code for an argument it
+ * refuses (documented per function); nothing here aborts.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_E_ARG (-1)   /* a size or pointer argument is invalid  */
+#define ORC_E_CODE (-2)  /* a NaN-coded fp8 / e8m0 byte was met     */
+#define ORC_E_INDEX (-3) /* an index list entry is out of range     */
+
+/* ------------------------------------------------------------------------ */
+/* Byte formats.  [V4.1] module globals: the activation format is e4m3 with  */
+/* one power-of-two (ue8m0) scale per 32 elements.                           */
+/* ------------------------------------------------------------------------ */
+
+/* OCP e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits, no
+ * infinities; exponent 15 with mantissa 7 is NaN; exponent 0 is subnormal. */
+double orc_e4m3(uint8_t code) {
+    int s = (code >> 7) & 1;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* ue8m0: an unsigned biased exponent, value 2^(c-127); 255 is NaN. */
+double orc_e8m0(uint8_t code) {
+    if (code == 255) return NAN;
+    return ldexp(1.0, (int)code - 127);
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+double orc_bf16(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Visibility.  [V4.1] Indexer.forward: compressed row j covers tokens        */
+/* j*r .. j*r+r-1 and becomes visible once the query has passed its last      */
+/* token, so a query at absolute position P sees rows j < (P+1)//r.  The     */
+/* prefill form there (arange(1, S+1)//r) and the decode form (end_pos//r)   */
+/* are the cases start_pos == 0 and S == 1 of this rule.                     */
+/* ------------------------------------------------------------------------ */
+int orc_n_visible(int start_pos, int i, int ratio) {
+    if (ratio <= 0) return 0;
+    return (start_pos + i + 1) / ratio;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Indexer score.  [V4.1] Indexer.forward: index_score[b,s,t] =              */
+/*   sum_h  w[b,s,h] * relu( q[b,s,h,:] . k[b,t,:] ),                        */
+/* with q and k the dequantised fp8 values ([V3.2] fp8_index takes the e4m3  */
+/* codes and their block scales).  Each operand is dequantised per block of  */
+/* 32 along the head dimension: x = code * 2^(scale-127).                    */
+/*                                                                           */
+/* Layouts (row-major): q8 [B,S,Hi,Di], q_sc [B,S,Hi,Di/32], w [B,S,Hi] f32, */
+/* k8 [B,T_cap,Di], k_sc [B,T_cap,Di/32].  Output scores [B,S,T] doubles     */
+/* with T = (start_pos+S)//ratio; entries of rows a query cannot see are     */
+/* -inf.  Returns ORC_E_ARG for bad sizes, ORC_E_CODE for a NaN code.        */
+/* ------------------------------------------------------------------------ */
+int orc_index_scores(const uint8_t *q8, const uint8_t *q_sc, const float *w,
+                     const uint8_t *k8, const uint8_t *k_sc, int B, int S,
+                     int Hi, int Di, int T_cap, int start_pos, int ratio,
+                     double *scores) {
+    if (B < 0 || S < 0 || Hi <= 0 || Di <= 0 || Di % 32 != 0 || ratio <= 0 ||
+        start_pos < 0)
+        return ORC_E_ARG;
+    const int T = (start_pos + S) / ratio;
+    if (T > T_cap) return ORC_E_ARG;
+    const int nb = Di / 32;
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic) reduction(| : bad)
+    for (int b = 0; b < B; ++b) {
+        for (int i = 0; i < S; ++i) {
+            const int nvis = orc_n_visible(start_pos, i, ratio);
+            double *srow = scores + ((size_t)b * S + i) * T;
+            double *qh = (double *)malloc(sizeof(double) * (size_t)Hi * Di);
+            /* dequantise this query's heads */
+            for (int h = 0; h < Hi; ++h)
+                for (int d = 0; d < Di; ++d) {
+                    size_t qi = (((size_t)b * S + i) * Hi + h) * Di + d;
+                    size_t si = (((size_t)b * S + i) * Hi + h) * nb + d / 32;
+                    double v = orc_e4m3(q8[qi]) * orc_e8m0(q_sc[si]);
+                    if (isnan(v)) bad = 1;
+                    qh[(size_t)h * Di + d] = v;
+                }
+            for (int t = 0; t < T; ++t) {
+                if (t >= nvis) {
+                    srow[t] = -INFINITY;
+                    continue;
+                }
+                double s = 0.0;
+                for (int h = 0; h < Hi; ++h) {
+                    double dot = 0.0;
+                    for (int d = 0; d < Di; ++d) {
+                        size_t ki = ((size_t)b * T_cap + t) * Di + d;
+                        size_t ks = ((size_t)b * T_cap + t) * nb + d / 32;
+                        double kv = orc_e4m3(k8[ki]) * orc_e8m0(k_sc[ks]);
+                        if (isnan(kv)) bad = 1;
+                        dot += qh[(size_t)h * Di + d] * kv;
+                    }
+                    double wh = (double)w[((size_t)b * S + i) * Hi + h];
+                    s += wh * (dot > 0.0 ? dot : 0.0);
+                }
+                srow[t] = s;
+            }
+            free(qh);
+        }
+    }
+    return bad ? ORC_E_CODE : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Top-k.  [V4.1] Indexer.forward: k_eff = min(index_topk, end_pos//r); the  */
+/* k_eff best scores are taken, their row numbers listed in ascending order, */
+/* and a pick the query cannot see becomes -1 (which, being a larger row     */
+/* number than every visible one, sorts to the end).                         */
+/*                                                                           */
+/* Here the picks are made among the visible rows only, ordered by score     */
+/* descending and, for equal scores, by row ascending (the pages leave ties  */
+/* open; this is the reading taken).  The first min(k_eff, n_visible) rows   */
+/* are emitted in ascending row order and the rest of the k_eff slots are    */
+/* -1.  scores: [B,S,ld] doubles.  idx: [B,S,k_eff] int32.                   */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    double s;
+    int t;
+} orc_pick;
+
+static int orc_pick_cmp(const void *a, const void *b) {
+    const orc_pick *x = (const orc_pick *)a, *y = (const orc_pick *)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->t > y->t) - (x->t < y->t);
+}
+
+static int orc_int_cmp(const void *a, const void *b) {
+    int x = *(const int *)a, y = *(const int *)b;
+    return (x > y) - (x < y);
+}
+
+int orc_topk_width(int S, int start_pos, int ratio, int index_topk) {
+    if (ratio <= 0 || index_topk < 0) return 0;
+    int T = (start_pos + S) / ratio;
+    return index_topk < T ? index_topk : T;
+}
+
+int orc_topk(const double *scores, int ld, int B, int S, int start_pos,
+             int ratio, int index_topk, int32_t *idx) {
+    if (B < 0 || S < 0 || ratio <= 0 || index_topk < 0 || start_pos < 0)
+        return ORC_E_ARG;
+    const int T = (start_pos + S) / ratio;
+    if (ld < T) return ORC_E_ARG;
+    const int keff = orc_topk_width(S, start_pos, ratio, index_topk);
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic) reduction(| : bad)
+    for (int b = 0; b < B; ++b) {
+        for (int i = 0; i < S; ++i) {
+            const double *srow = scores + ((size_t)b * S + i) * ld;
+            int32_t *orow = idx + ((size_t)b * S + i) * keff;
+            int nvis = orc_n_visible(start_pos, i, ratio);
+            if (nvis > T) nvis = T;
+            orc_pick *p = (orc_pick *)malloc(sizeof(orc_pick) * (size_t)(nvis > 0 ? nvis : 1));
+            int *sel = (int *)malloc(sizeof(int) * (size_t)(keff > 0 ? keff : 1));
+            for (int t = 0; t < nvis; ++t) {
+                p[t].s = srow[t];
+                p[t].t = t;
+                if (isnan(srow[t])) bad = 1;
+            }
+            qsort(p, (size_t)nvis, sizeof(orc_pick), orc_pick_cmp);
+            int take = keff < nvis ? keff : nvis;
+            for (int j = 0; j < take; ++j) sel[j] = p[j].t;
+            qsort(sel, (size_t)take, sizeof(int), orc_int_cmp);
+            for (int j = 0; j < keff; ++j) orow[j] = j < take ? sel[j] : -1;
+            free(p);
+            free(sel);
+        }
+    }
+    return bad ? ORC_E_ARG : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Window rows.  [V4.1] get_window_topk_idxs and Attention._window_kv: a     */
+/* query at absolute position P attends to the window positions              */
+/* max(0, P-W+1) .. P.  The window source is a ring of R slots holding       */
+/* position p in slot p mod R.                                               */
+/*   * start_pos == 0 (prefill of the chunk itself): each row has             */
+/*     min(S, W) entries, positions max(0, i-W+1) + j, and an entry past the */
+/*     query (p > i) is -1.                                                  */
+/*   * start_pos > 0: each row has W entries, positions P-W+1+j oldest       */
+/*     first, and a position before the sequence start is -1.  With S == 1  */
+/*     and R == W this is the decode ring of the pages; with S > 1 it is the */
+/*     chunked-prefill generalisation (requires R >= W + S - 1 so that no    */
+/*     two needed positions share a slot).                                   */
+/* win_idx: [B,S,width] int32, the same for every b.                         */
+/* ------------------------------------------------------------------------ */
+int orc_window_width(int S, int start_pos, int W) {
+    if (W <= 0) return 0;
+    if (start_pos == 0) return S < W ? S : W;
+    return W;
+}
+
+int orc_window_indices(int B, int S, int start_pos, int W, int R,
+                       int32_t *win_idx) {
+    if (B < 0 || S < 0 || W < 0 || start_pos < 0 || R <= 0) return ORC_E_ARG;
+    const int width = orc_window_width(S, start_pos, W);
+    const long need = start_pos == 0 ? (long)S : (long)W + S - 1;
+    if (width > 0 && R < (need < (long)start_pos + S ? need : (long)start_pos + S))
+        return ORC_E_ARG;
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < S; ++i) {
+            int32_t *row = win_idx + ((size_t)b * S + i) * width;
+            const long P = (long)start_pos + i;
+            for (int j = 0; j < width; ++j) {
+                long p;
+                int valid;
+                if (start_pos == 0) {
+                    long base = P - W + 1 > 0 ? P - W + 1 : 0;
+                    p = base + j;
+                    valid = p <= P;
+                } else {
+                    p = P - W + 1 + j;
+                    valid = p >= 0;
+                }
+                row[j] = valid ? (int32_t)(p % R) : -1;
+            }
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention.  [V4.1] Attention.forward hands sparse_attn the concatenation  */
+/* of the window KV and the compressed KV plus the concatenated index lists; */
+/* one KV row serves as both key and value (a single shared latent head).    */
+/* [V3.2] MLA.forward gives the dense form: scores over positions, -inf      */
+/* outside the index set, softmax, weighted sum of values.                   */
+/*                                                                           */
+/* For each (b, i, h): J = the window rows listed in win_idx (slots of       */
+/* win_kv) followed by the compressed rows listed in comp_idx (rows of       */
+/* comp_kv); -1 entries are skipped, repeats are kept.  l_j = scale * q.kv_j  */
+/* over all D dims; with an optional per-head sink logit s_h:                 */
+/*   m = max(l_j, s_h),  Z = sum_j e^(l_j-m) + e^(s_h-m),                     */
+/*   o[d] = sum_j e^(l_j-m) kv_j[d] / Z   for d < dv.                        */
+/* The sink enters the normaliser only (the pages pass attn_sink without     */
+/* stating its role; this is the reading taken).  Empty J gives o = 0.       */
+/* Two passes over J (max, then sums): the plain definition, not the online  */
+/* recurrence a kernel would use.                                            */
+/*                                                                           */
+/* Layouts: q [B,S,H,D] bf16 bits; win_kv [B,R,D]; win_idx [B,S,W];          */
+/* comp_kv [B,T_cap,D]; comp_idx [B,S,K]; sink [H] float or NULL;            */
+/* out [B,S,H,dv] doubles.  Returns ORC_E_INDEX for an entry out of range.   */
+/* ------------------------------------------------------------------------ */
+int orc_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv,
+                    const uint16_t *win_kv, int R, const int32_t *win_idx,
+                    int W, const uint16_t *comp_kv, int T_cap,
+                    const int32_t *comp_idx, int K, const float *sink,
+                    double scale, double *out) {
+    if (B < 0 || S < 0 || H <= 0 || D <= 0 || dv <= 0 || dv > D || W < 0 ||
+        K < 0)
+        return ORC_E_ARG;
+    if ((W > 0 && (win_kv == NULL || win_idx == NULL || R <= 0)) ||
+        (K > 0 && (comp_kv == NULL || comp_idx == NULL || T_cap <= 0)))
+        return ORC_E_ARG;
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic) reduction(| : bad)
+    for (int b = 0; b < B; ++b) {
+        for (int i = 0; i < S; ++i) {
+            const int n = W + K;
+            const uint16_t **rows = (const uint16_t **)malloc(sizeof(void *) * (size_t)(n > 0 ? n : 1));
+            int nj = 0;
+            for (int j = 0; j < W; ++j) {
+                int32_t s = win_idx[((size_t)b * S + i) * W + j];
+                if (s < 0) continue;
+                if (s >= R) { bad = 1; continue; }
+                rows[nj++] = win_kv + ((size_t)b * R + s) * D;
+            }
+            for (int j = 0; j < K; ++j) {
+                int32_t t = comp_idx[((size_t)b * S + i) * K + j];
+                if (t < 0) continue;
+                if (t >= T_cap) { bad = 1; continue; }
+                rows[nj++] = comp_kv + ((size_t)b * T_cap + t) * D;
+            }
+            double *l = (double *)malloc(sizeof(double) * (size_t)(nj > 0 ? nj : 1));
+            for (int h = 0; h < H; ++h) {
+                const uint16_t *qh = q + (((size_t)b * S + i) * H + h) * D;
+                double *oh = out + (((size_t)b * S + i) * H + h) * dv;
+                for (int d = 0; d < dv; ++d) oh[d] = 0.0;
+                if (nj == 0) continue;
+                double m = -INFINITY;
+                for (int j = 0; j < nj; ++j) {
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d) dot += orc_bf16(qh[d]) * orc_bf16(rows[j][d]);
+                    l[j] = scale * dot;
+                    if (l[j] > m) m = l[j];
+                }
+                double sk = sink ? (double)sink[h] : -INFINITY;
+                if (sk > m) m = sk;
+                double Z = sink ? exp(sk - m) : 0.0;
+                for (int j = 0; j < nj; ++j) Z += exp(l[j] - m);
+                for (int j = 0; j < nj; ++j) {
+                    double p = exp(l[j] - m) / Z;
+                    for (int d = 0; d < dv; ++d) oh[d] += p * orc_bf16(rows[j][d]);
+                }
+            }
+            free(l);
+            free(rows);
+        }
+    }
+    return bad ? ORC_E_INDEX : 0;
+}
+
+/* Threads the OpenMP loops above will use (1 without OpenMP). */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -1,0 +1,145 @@
+"""Pins for the oracle's sparse attention.
+
+Definition: DeepSeek-V4.1-Flash-NVFP4 model.py, Attention.forward (sparse_attn over the
+window KV and the compressed KV, one shared row as key and value, an attention sink
+per head); DeepSeek-V3.2-Exp model.py, MLA.forward (dense scores, -inf outside the
+index set, softmax, weighted values).
+
+Pins:
+* index set = every compressed row, no window, no sink: torch's
+  scaled_dot_product_attention in float64 (library routine);
+* arbitrary sets over both sources with dv < D: the dense masked softmax form of the
+  V3.2 page evaluated with torch.softmax over the concatenated KV (library routine);
+* a single row gives that row (closed form); q = 0 with a sink gives
+  sum(rows) / (n + e^sink) (closed form); sink = -inf is no sink; a huge sink gives 0;
+* invariance under reordering of the list, under a permutation of the KV rows, and
+  under listing every row twice; an empty set gives 0.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from lightning_indexer_top_amd import synth
+
+
+def bf(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(torch.float64)
+
+
+def rand_case(B=2, S=3, H=4, D=64, R=10, T=24, seed=0):
+    rng = np.random.default_rng(seed)
+    q = synth.to_bf16_bits(rng.standard_normal((B, S, H, D)))
+    win = synth.to_bf16_bits(rng.standard_normal((B, R, D)))
+    comp = synth.to_bf16_bits(rng.standard_normal((B, T, D)))
+    return q, win, comp
+
+
+def test_all_rows_equals_library_sdpa(orc):
+    B, S, H, D, T = 2, 3, 4, 64, 24
+    q, _, comp = rand_case(B, S, H, D, 1, T, seed=1)
+    idx = np.broadcast_to(np.arange(T, dtype=np.int32), (B, S, T)).copy()
+    scale = D ** -0.5
+    got = orc.sparse_attn(q, None, None, comp, idx, None, scale)
+    qt = bf(q).reshape(B * S, H, 1, D)
+    kv = bf(comp).unsqueeze(1).expand(B, S, T, D).reshape(B * S, 1, T, D).expand(B * S, H, T, D)
+    want = F.scaled_dot_product_attention(qt, kv, kv, scale=scale).reshape(B, S, H, D)
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_dense_masked_softmax_two_sources(orc):
+    B, S, H, D, dv, R, T, W, K = 2, 3, 4, 64, 48, 10, 24, 5, 7
+    q, win, comp = rand_case(B, S, H, D, R, T, seed=2)
+    rng = np.random.default_rng(3)
+    win_idx = np.full((B, S, W), -1, np.int32)
+    comp_idx = np.full((B, S, K), -1, np.int32)
+    for b in range(B):
+        for i in range(S):
+            ws = rng.choice(R, size=W - 1 - i % 2, replace=False)
+            win_idx[b, i, :len(ws)] = ws
+            cs = rng.choice(T, size=K - i, replace=False)
+            comp_idx[b, i, :len(cs)] = np.sort(cs)
+    scale = 0.125
+    got = orc.sparse_attn(q, win, win_idx, comp, comp_idx, None, scale, dv)
+    kv = torch.cat([bf(win), bf(comp)], dim=1)           # [B, R+T, D]
+    for b in range(B):
+        for i in range(S):
+            mask = torch.full((R + T,), -math.inf, dtype=torch.float64)
+            for s in win_idx[b, i]:
+                if s >= 0:
+                    mask[s] = 0
+            for t in comp_idx[b, i]:
+                if t >= 0:
+                    mask[R + t] = 0
+            scores = bf(q)[b, i] @ kv[b].T * scale + mask   # [H, R+T]
+            want = torch.softmax(scores, dim=-1) @ kv[b, :, :dv]
+            np.testing.assert_allclose(got[b, i], want.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_single_row_and_empty_set(orc):
+    q, win, comp = rand_case(seed=4)
+    idx = np.full((2, 3, 3), -1, np.int32)
+    idx[:, :, 1] = 7
+    got = orc.sparse_attn(q, None, None, comp, idx, None, 0.3, 32)
+    for b in range(2):
+        for i in range(3):
+            for h in range(4):
+                assert np.array_equal(got[b, i, h], bf(comp)[b, 7, :32].numpy())
+    empty = np.full((2, 3, 4), -1, np.int32)
+    got = orc.sparse_attn(q, win, empty, comp, empty, None, 0.3)
+    assert np.array_equal(got, np.zeros_like(got))
+    sink = np.zeros(4, np.float32)
+    got = orc.sparse_attn(q, win, empty, comp, empty, sink, 0.3)
+    assert np.array_equal(got, np.zeros_like(got))
+
+
+def test_sink_closed_forms(orc):
+    B, S, H, D, T = 1, 2, 4, 64, 9
+    _, _, comp = rand_case(B, S, H, D, 1, T, seed=5)
+    q0 = np.zeros((B, S, H, D), np.uint16)                # all logits 0
+    idx = np.broadcast_to(np.arange(T, dtype=np.int32), (B, S, T)).copy()
+    sink = np.array([0.0, 1.5, -2.0, 4.0], np.float32)
+    got = orc.sparse_attn(q0, None, None, comp, idx, sink, 0.5)
+    rows = bf(comp)[0].numpy()
+    for h in range(H):
+        want = rows.sum(0) / (T + math.exp(float(sink[h])))
+        np.testing.assert_allclose(got[0, 0, h], want, rtol=1e-13, atol=1e-14)
+    q, _, _ = rand_case(B, S, H, D, 1, T, seed=6)
+    none = orc.sparse_attn(q, None, None, comp, idx, None, 0.2)
+    ninf = orc.sparse_attn(q, None, None, comp, idx, np.full(H, -np.inf, np.float32), 0.2)
+    assert np.array_equal(none, ninf)
+    huge = orc.sparse_attn(q, None, None, comp, idx, np.full(H, 1e4, np.float32), 0.2)
+    assert np.abs(huge).max() < 1e-300
+
+
+def test_order_permutation_and_duplication_invariance(orc):
+    B, S, H, D, R, T, W, K = 1, 2, 4, 64, 8, 30, 8, 10
+    q, win, comp = rand_case(B, S, H, D, R, T, seed=7)
+    rng = np.random.default_rng(8)
+    win_idx = np.broadcast_to(np.arange(W, dtype=np.int32), (B, S, W)).copy()
+    comp_idx = np.stack([np.sort(rng.choice(T, K, replace=False)) for _ in range(S)])[None].astype(np.int32)
+    base = orc.sparse_attn(q, win, win_idx, comp, comp_idx, None, 0.15)
+    # list order
+    shuf = comp_idx[..., rng.permutation(K)]
+    np.testing.assert_allclose(orc.sparse_attn(q, win, win_idx[..., ::-1], comp, shuf, None, 0.15),
+                               base, rtol=1e-13, atol=1e-14)
+    # KV row permutation with the index lists remapped
+    perm = rng.permutation(T)
+    inv = np.argsort(perm)
+    comp_p = comp[:, perm]
+    np.testing.assert_allclose(orc.sparse_attn(q, win, win_idx, comp_p, inv[comp_idx].astype(np.int32),
+                                               None, 0.15), base, rtol=1e-13, atol=1e-14)
+    # every row listed twice
+    dup = np.concatenate([comp_idx, comp_idx], -1)
+    wdup = np.concatenate([win_idx, win_idx], -1)
+    np.testing.assert_allclose(orc.sparse_attn(q, win, wdup, comp, dup, None, 0.15),
+                               base, rtol=1e-13, atol=1e-14)
+
+
+def test_refuses_out_of_range_rows(orc):
+    q, win, comp = rand_case(seed=9)
+    bad = np.full((2, 3, 2), 24, np.int32)
+    with pytest.raises(orc.OracleError):
+        orc.sparse_attn(q, None, None, comp, bad, None, 0.1)

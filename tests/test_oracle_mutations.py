@@ -1,0 +1,96 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case below plants one mistake in a temporary copy of ``oracle/lit_oracle.c``
+(on the CPU; nothing here touches a GPU), compiles it, and runs the pins that should
+notice it.  At least one of them has to fail; a mutant that passes every pin means the
+pins are too weak.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_attention as TA
+from tests import test_oracle_formats as TF
+from tests import test_oracle_indexer as TI
+from tests import test_oracle_topk as TT
+from tests import test_oracle_window as TW
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "lit_oracle.c")
+
+
+def _window_derived(orc):
+    for case in TW.DERIVED:
+        TW.test_derived_cases(orc, *case)
+
+
+def _one_hot(orc):
+    TI.test_one_hot_weights_reduce_to_library_matmul(orc, 64)
+    TI.test_one_hot_weights_reduce_to_library_matmul(orc, 128)
+
+
+MUTANTS = [
+    # (name, original text, mutated text, pins expected to notice)
+    ("relu dropped", "s += wh * (dot > 0.0 ? dot : 0.0);", "s += wh * dot;",
+     [TI.test_closed_form_constant_blocks, TI.test_relu_identity_gives_linear_form]),
+    ("relu sign flipped", "s += wh * (dot > 0.0 ? dot : 0.0);", "s += wh * (dot < 0.0 ? -dot : 0.0);",
+     [TI.test_closed_form_constant_blocks, TI.test_relu_identity_gives_linear_form]),
+    ("key scale dropped", "double kv = orc_e4m3(k8[ki]) * orc_e8m0(k_sc[ks]);",
+     "double kv = orc_e4m3(k8[ki]);", [TI.test_closed_form_constant_blocks, _one_hot]),
+    ("key scale block reversed", "size_t ks = ((size_t)b * T_cap + t) * nb + d / 32;",
+     "size_t ks = ((size_t)b * T_cap + t) * nb + (nb - 1 - d / 32);",
+     [TI.test_closed_form_constant_blocks, _one_hot]),
+    ("query scale block off", "size_t si = (((size_t)b * S + i) * Hi + h) * nb + d / 32;",
+     "size_t si = (((size_t)b * S + i) * Hi + h) * nb;",
+     [TI.test_closed_form_constant_blocks, _one_hot]),
+    ("head weight index", "double wh = (double)w[((size_t)b * S + i) * Hi + h];",
+     "double wh = (double)w[((size_t)b * S + i) * Hi + (Hi - 1 - h)];",
+     [TI.test_closed_form_constant_blocks, TI.test_relu_identity_gives_linear_form]),
+    ("visibility off by one", "return (start_pos + i + 1) / ratio;", "return (start_pos + i) / ratio;",
+     [TI.test_visibility_prefill_decode_and_chunk]),
+    ("e4m3 bias", "v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);",
+     [TF.test_e4m3_all_codes_match_torch, TF.test_e4m3_closed_forms]),
+    ("e4m3 subnormal exponent", "v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);",
+     [TF.test_e4m3_all_codes_match_torch, TF.test_e4m3_closed_forms]),
+    ("topk tie rule reversed", "return (x->t > y->t) - (x->t < y->t);",
+     "return (x->t < y->t) - (x->t > y->t);", [TT.test_property_checker_with_ties_and_prefill]),
+    ("topk ascending sort dropped", "qsort(sel, (size_t)take, sizeof(int), orc_int_cmp);", "",
+     [TT.test_matches_torch_topk_on_distinct_scores, TT.test_property_checker_with_ties_and_prefill]),
+    ("topk ignores visibility", "if (nvis > T) nvis = T;", "nvis = T;",
+     [TT.test_property_checker_with_ties_and_prefill, TT.test_k_at_least_visible_selects_everything]),
+    ("window shifted", "p = P - W + 1 + j;", "p = P - W + j;", [_window_derived]),
+    ("window slot not wrapped", "row[j] = valid ? (int32_t)(p % R) : -1;", "row[j] = valid ? (int32_t)p : -1;",
+     [_window_derived, lambda o: TW.test_brute_force_sets(o, 128, 1, 1023, 128)]),
+    ("softmax scale dropped", "l[j] = scale * dot;", "l[j] = dot;",
+     [TA.test_all_rows_equals_library_sdpa, TA.test_dense_masked_softmax_two_sources]),
+    ("logit over dv dims only", "for (int d = 0; d < D; ++d) dot += orc_bf16(qh[d]) * orc_bf16(rows[j][d]);",
+     "for (int d = 0; d < dv; ++d) dot += orc_bf16(qh[d]) * orc_bf16(rows[j][d]);",
+     [TA.test_dense_masked_softmax_two_sources]),
+    ("sink left out of normaliser", "double Z = sink ? exp(sk - m) : 0.0;", "double Z = 0.0;",
+     [TA.test_sink_closed_forms]),
+    ("window rows dropped", "rows[nj++] = win_kv + ((size_t)b * R + s) * D;", "(void)s;",
+     [TA.test_dense_masked_softmax_two_sources, TA.test_order_permutation_and_duplication_invariance]),
+]
+
+
+@pytest.mark.parametrize("name,orig,mut,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(orc, name, orig, mut, pins):
+    src = open(SRC).read()
+    assert src.count(orig) == 1, f"mutation anchor not found once: {orig!r}"
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "mut.c")
+        lib = os.path.join(d, "libmut.so")
+        with open(path, "w") as f:
+            f.write(src.replace(orig, mut))
+        subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-w",
+                        "-o", lib, path, "-lm"], check=True)
+        caught = []
+        with oracle.using_library(lib):
+            for pin in pins:
+                try:
+                    pin(oracle)
+                except (AssertionError, oracle.OracleError):
+                    caught.append(getattr(pin, "__name__", "pin"))
+    assert caught, f"mutant '{name}' passed every pin"
