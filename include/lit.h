@@ -81,7 +81,7 @@ int lit_abi_version(void);
  *   k_sc  (device) u8   [B, T_cap, Di/32] ue8m0 scale bytes of the cache
  *   scores(device) f32  [B, S, ld_scores] output; columns t < T are written,
  *                       T = (start_pos + S) / ratio; t >= visible -> -inf.
- * Requirements: Di in {64, 128}; Hi a multiple of 16, at most 64; ratio >= 1;
+ * Requirements: Di in {64, 128}; Hi a multiple of 16, at most 64; B*S <= 65535; ratio >= 1;
  * T <= T_cap; ld_scores >= T and a multiple of 4.  A scale byte of 255 (NaN)
  * or a NaN e4m3 code gives unspecified scores.
  */
@@ -150,7 +150,7 @@ int lit_window_width(int S, int start_pos, int W);
  *   sink     (device) f32  [H] or NULL
  *   out      (device) bf16 [B, S, H, dv] output
  *   ws, ws_bytes  workspace, lit_sparse_attn_workspace_bytes() bytes
- * Requirements: H == 16; D in {64, 128, 192, 256}; dv a multiple of 16 and
+ * Requirements: H == 16; D in {64, 128, 192, 256}; B*S <= 65535; dv a multiple of 16 and
  * <= D; every listed slot < R and row < T_cap (checked on the device: an
  * out-of-range entry is treated as -1).
  */

@@ -1,0 +1,10 @@
+"""MI355X-native sparse-attention step: lightning indexer -> top-k -> sparse attention.
+
+The kernels live in ``liblit.so`` (hand-written HIP for gfx950, C ABI in
+``include/lit.h``); ``lit`` is the ctypes binding with the same function names.
+``synth`` draws seeded synthetic inputs for the tests and the bench.
+"""
+from .lit import (LitError, library, lit_indexer_scores, lit_sparse_attn,  # noqa: F401
+                  lit_sparse_attn_workspace_bytes, lit_sparse_step,
+                  lit_sparse_step_workspace_bytes, lit_step_args, lit_topk,
+                  lit_window_indices, lit_window_width, make_step_args, topk_width)

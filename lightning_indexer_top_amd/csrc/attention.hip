@@ -1,0 +1,310 @@
+// attention.hip -- sparse gather-attention over the sliding window and the selected
+// compressed rows, plus the window row lists.
+//
+// What is computed (DeepSeek-V4.1-Flash-NVFP4 inference/model.py, Attention.forward
+// and its sparse_attn call; DeepSeek-V3.2-Exp inference/model.py, MLA.forward gives
+// the dense equivalent): for every query (b, i) and head h, over the row set J = the
+// listed window slots followed by the listed compressed rows (-1 skipped),
+//   l_j = scale * q[h] . row_j,   o[h] = sum_j e^(l_j) row_j[:dv] / (sum_j e^(l_j) + e^(sink_h)).
+// One bf16 row is both key and value (a single shared latent head).
+//
+// Mapping onto the chip.  A wave takes 32 listed rows at a time.  Each lane (g, c)
+// gathers 16-byte pieces of row c (and row 16+c) straight from HBM: these are the
+// A operands of V_MFMA_F32_16X16X32_BF16 for S^T = rows x Q^T (32 head dims per
+// instruction; Q^T stays in VGPRs), so lane (g, h) ends up holding the 8 logits of
+// head h for rows 4g..4g+3 and 16+4g..16+4g+3.  The online softmax for head h is
+// therefore per lane (plus two cross-lane max/sum steps), and the 8 probabilities,
+// rounded to bf16, are already the B operand of O^T = V^T x P^T.  V^T needs the same
+// rows column-wise, so the gathered rows are also written once to LDS and read back
+// transposed (8 row entries of one column per lane).  O^T accumulates in fp32 VGPRs,
+// lane (g, h) owning dims 4g..4g+3 of every 16-dim tile for head h.
+//
+// A query's list is cut into splits (workgroups of 4 waves); the 4 waves of a split
+// merge through LDS, and a second kernel merges splits (log-sum-exp), adds the sink
+// and writes bf16.  With a single split the first kernel writes bf16 itself.
+#include "lit_internal.h"
+
+namespace lit {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kHeads = 16;
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ inline const uint16_t *list_row(const AttnArgs &a, int b, int i, int nwin, int p) {
+    const size_t bs = (size_t)b * a.S + i;
+    if (p < nwin) {
+        const int slot = a.win_idx ? a.win_idx[bs * a.W + p]
+                                   : window_slot(a.S, a.start_pos, a.W, a.R, i, p);
+        if (slot < 0 || slot >= a.R) return nullptr;
+        return a.win_kv + ((size_t)b * a.R + slot) * a.D;
+    }
+    const int t = a.comp_idx[bs * a.K + (p - nwin)];
+    if (t < 0 || t >= a.T_cap) return nullptr;
+    return a.comp_kv + ((size_t)b * a.T_cap + t) * a.D;
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a, AttnPlan pl) {
+    constexpr int KS = D / 32;      // 32-dim MFMA steps of the logit contraction
+    constexpr int NT = D / 16;      // 16-dim output tiles (dv <= D)
+    constexpr int LD = D + 4;       // LDS row stride in bf16 (8 bytes of padding)
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * 32 * LD];
+    __shared__ float wm[kWaves][kHeads], wl[kWaves][kHeads];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int bs = blockIdx.y;
+    const int b = bs / a.S;
+    const int i = bs % a.S;
+    const int split = blockIdx.x;
+    const int nwin = a.win_idx ? a.W : (a.W > 0 ? window_width(a.S, a.start_pos, a.W) : 0);
+    const int list_len = nwin + a.K;
+    const int ndt = a.dv / 16;
+    const float sl2 = a.scale * kLog2e;
+
+    // Q^T operands: lane (g, c) holds head c, dims 32s+8g .. 32s+8g+7.
+    bf16x8 qb[KS];
+    {
+        const uint16_t *qrow = a.q + ((size_t)bs * kHeads + c) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            qb[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qrow + 32 * s + 8 * g));
+    }
+
+    float m_run = -INFINITY;  // running max of log2-domain logits, head c
+    float l_run = 0.f;        // this lane's share of the running normaliser
+    f32x4 o[NT];
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint16_t *tile = lds + wave * 32 * LD;
+    const int split_begin = split * kWaves * pl.tiles_per_wave * 32;
+    const int split_end = min(list_len, split_begin + kWaves * pl.tiles_per_wave * 32);
+
+    for (int it = 0; it < pl.tiles_per_wave; ++it) {
+        const int base = split_begin + (wave * pl.tiles_per_wave + it) * 32;
+        f32x4 sc[2];
+        uint64_t valid_mask[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int p = base + 16 * half + c;
+            const uint16_t *rp = p < split_end ? list_row(a, b, i, nwin, p) : nullptr;
+            valid_mask[half] = __ballot(rp != nullptr);
+            u32x4 kr[KS];
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                kr[s] = rp ? *reinterpret_cast<const u32x4 *>(rp + 32 * s + 8 * g)
+                           : u32x4{0u, 0u, 0u, 0u};
+            sc[half] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                sc[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[s]), qb[s], sc[half], 0, 0, 0);
+            uint16_t *dst = tile + (16 * half + c) * LD + 8 * g;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                *reinterpret_cast<u32x2 *>(dst + 32 * s) = u32x2{kr[s][0], kr[s][1]};
+                *reinterpret_cast<u32x2 *>(dst + 32 * s + 4) = u32x2{kr[s][2], kr[s][3]};
+            }
+        }
+
+        // Logits of head c for rows 4g+r (half 0) and 16+4g+r (half 1).
+        float x[8];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool v = (valid_mask[half] >> (4 * g + r)) & 1ull;
+                const float val = v ? sc[half][r] * sl2 : -INFINITY;
+                x[4 * half + r] = val;
+                tmax = fmaxf(tmax, val);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+        bf16x8 pb;
+        float psum = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float pk = x[k] == -INFINITY ? 0.f : exp2f(x[k] - m_new);
+            psum += pk;
+            pb[k] = (__bf16)pk;
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) o[dt] *= alpha;
+
+        __syncthreads();  // this wave's rows are in LDS
+        // V^T operand: lane (g, c) reads column 16dt+c of rows 4g..4g+3, 16+4g..16+4g+3.
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) {
+            if (dt < ndt) {
+                bf16x8 va;
+                const uint16_t *col = tile + 16 * dt + c;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    va[m] = __builtin_bit_cast(__bf16, col[(4 * g + m) * LD]);
+                    va[4 + m] = __builtin_bit_cast(__bf16, col[(16 + 4 * g + m) * LD]);
+                }
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[dt], 0, 0, 0);
+            }
+        }
+        __syncthreads();  // LDS tile free for the next rows
+    }
+
+    // Wave totals for head c.
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (g == 0) {
+        wm[wave][c] = m_run;
+        wl[wave][c] = l_run;
+    }
+    // Reuse the tile buffer for the 4 waves' O (float, [wave][head][dv]).
+    float *ow = reinterpret_cast<float *>(lds);
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt)
+        if (dt < ndt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ow[(wave * kHeads + c) * a.dv + 16 * dt + 4 * g + r] = o[dt][r];
+    __syncthreads();
+
+    const bool direct = pl.n_splits == 1;
+    for (int e = threadIdx.x; e < kHeads * a.dv; e += kWaves * 64) {
+        const int h = e / a.dv;
+        const int d = e - h * a.dv;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][h]);
+        float O = 0.f, L = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float f = wm[w][h] == -INFINITY ? 0.f : exp2f(wm[w][h] - M);
+                O += f * ow[(w * kHeads + h) * a.dv + d];
+                L += f * wl[w][h];
+            }
+        }
+        if (direct) {
+            if (a.sink) {
+                const float s2 = a.sink[h] * kLog2e;
+                const float M2 = fmaxf(M, s2);
+                if (M2 != -INFINITY) {
+                    const float f = M == -INFINITY ? 0.f : exp2f(M - M2);
+                    O *= f;
+                    L = L * f + exp2f(s2 - M2);
+                }
+            }
+            const float val = L > 0.f ? O / L : 0.f;
+            a.out[((size_t)bs * kHeads + h) * a.dv + d] = __builtin_bit_cast(uint16_t, (__bf16)val);
+        } else {
+            float *dst = a.part + (((size_t)bs * pl.n_splits + split) * kHeads + h) * (a.dv + 2);
+            dst[d] = O;
+            if (d == 0) {
+                dst[a.dv] = M;
+                dst[a.dv + 1] = L;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, AttnPlan pl) {
+    const int bs = blockIdx.x;
+    for (int e = threadIdx.x; e < kHeads * a.dv; e += 256) {
+        const int h = e / a.dv;
+        const int d = e - h * a.dv;
+        const float *src = a.part + ((size_t)bs * pl.n_splits * kHeads + h) * (a.dv + 2);
+        const size_t stride = (size_t)kHeads * (a.dv + 2);
+        float M = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+        for (int s = 0; s < pl.n_splits; ++s) M = fmaxf(M, src[s * stride + a.dv]);
+        float O = 0.f, L = 0.f;
+        if (M != -INFINITY) {
+            for (int s = 0; s < pl.n_splits; ++s) {
+                const float ms = src[s * stride + a.dv];
+                const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
+                O += f * src[s * stride + d];
+                L += f * src[s * stride + a.dv + 1];
+            }
+            if (a.sink) L += exp2f(a.sink[h] * kLog2e - M);
+        }
+        const float val = L > 0.f ? O / L : 0.f;
+        a.out[((size_t)bs * kHeads + h) * a.dv + d] = __builtin_bit_cast(uint16_t, (__bf16)val);
+    }
+}
+
+__global__ void window_indices_kernel(int B, int S, int start_pos, int W, int R, int width,
+                                      int32_t *win_idx) {
+    const long n = (long)B * S * width;
+    for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
+        const int j = (int)(e % width);
+        const int i = (int)((e / width) % S);
+        win_idx[e] = window_slot(S, start_pos, W, R, i, j);
+    }
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs &a, const AttnPlan &p, hipStream_t stream) {
+    dim3 grid(p.n_splits, a.B * a.S);
+    hipLaunchKernelGGL(sparse_attn_kernel<D>, grid, dim3(kWaves * 64), 0, stream, a, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.n_splits == 1) return e;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.B * a.S), dim3(256), 0, stream, a, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+AttnPlan plan_attention(int B, int S, int list_len) {
+    AttnPlan p;
+    p.list_len = list_len;
+    const int tiles = (list_len + 31) / 32;
+    const int queries = B * S;
+    // Aim for at least ~512 workgroups, but never fewer than one tile per wave.
+    int splits = (512 + queries - 1) / queries;
+    const int max_splits = (tiles + kWaves - 1) / kWaves;
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    p.tiles_per_wave = (tiles + kWaves * splits - 1) / (kWaves * splits);
+    if (p.tiles_per_wave < 1) p.tiles_per_wave = 1;
+    p.n_splits = (tiles + kWaves * p.tiles_per_wave - 1) / (kWaves * p.tiles_per_wave);
+    if (p.n_splits < 1) p.n_splits = 1;
+    return p;
+}
+
+size_t attention_partial_bytes(int B, int S, int H, int dv, const AttnPlan &p) {
+    if (p.n_splits <= 1) return 0;
+    return (size_t)B * S * p.n_splits * H * (dv + 2) * sizeof(float);
+}
+
+hipError_t launch_sparse_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t stream) {
+    if (a.B <= 0 || a.S <= 0) return hipSuccess;
+    switch (a.D) {
+        case 64: return launch_d<64>(a, p, stream);
+        case 128: return launch_d<128>(a, p, stream);
+        case 192: return launch_d<192>(a, p, stream);
+        case 256: return launch_d<256>(a, p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_window_indices(int B, int S, int start_pos, int W, int R, int32_t *win_idx,
+                                 hipStream_t stream) {
+    const int width = window_width(S, start_pos, W);
+    const long n = (long)B * S * width;
+    if (n <= 0) return hipSuccess;
+    const int threads = 256;
+    long blocks = (n + threads - 1) / threads;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(window_indices_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, B, S,
+                       start_pos, W, R, width, win_idx);
+    return hipGetLastError();
+}
+
+}  // namespace lit

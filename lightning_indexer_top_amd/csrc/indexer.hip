@@ -1,0 +1,169 @@
+// indexer.hip -- lightning-indexer scores on gfx950 MX-scaled fp8 MFMA.
+//
+// What is computed (DeepSeek-V4.1-Flash-NVFP4 inference/model.py, Indexer.forward;
+// DeepSeek-V3.2-Exp inference/model.py, fp8_index):
+//   score[b,i,t] = sum_h w[b,i,h] * relu( qhat[b,i,h,:] . khat[b,t,:] )
+// with e4m3 operands carrying one ue8m0 scale per 32 values, and -inf for the rows a
+// query cannot see yet (t >= (start_pos+i+1)/ratio).
+//
+// Mapping onto the chip.  The q.k contraction of 16 heads against 16 keys is one
+// V_MFMA_SCALE_F32_16X16X128_F8F6F4: A = 16 query heads (rows), B = 16 keys
+// (columns), K = 128 head dims, with the ue8m0 scales applied by the instruction.
+// Measured operand layout (probed on gfx950): lane l = 16*g + c holds row/column c;
+// its bytes 0-15 are K = 16g..16g+15 and bytes 16-31 are K = 64+16g..64+16g+15; the
+// scale byte lane group g supplies covers K block 32g..32g+31.  So a lane loads row
+// bytes [16g, 16g+16) and [64+16g, 64+16g+16) and the scale of block g -- memory
+// order is K order.  Di = 64 uses only the low half (K 0..63, the high half zero).
+// C comes back as lane (g, c), register r = head 4g+r, key c; the ReLU, the head
+// weights and the sum over the lane's 4 heads run in registers, and two cross-lane
+// adds finish the head sum.
+//
+// The key stream is the HBM-bound part at decode: every wave owns 16*U consecutive
+// keys of one sequence, issues all their loads before the first MFMA, and writes 16*U
+// fp32 scores.  Query heads stay in VGPRs.  For several queries per sequence
+// (chunked prefill) a wave scores QG queries against the same keys, so the keys are
+// read once per QG queries.
+#include "lit_internal.h"
+
+namespace lit {
+
+namespace {
+
+constexpr int kWaves = 4;  // waves per workgroup
+constexpr int kU = 4;      // 16-key tiles per wave
+
+__device__ inline i32x8 load_operand(const uint8_t *row, int g, bool wide) {
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(row + 16 * g);
+    u32x4 hi = {0u, 0u, 0u, 0u};
+    if (wide) hi = *reinterpret_cast<const u32x4 *>(row + 64 + 16 * g);
+    i32x8 v;
+    v[0] = (int)lo[0]; v[1] = (int)lo[1]; v[2] = (int)lo[2]; v[3] = (int)lo[3];
+    v[4] = (int)hi[0]; v[5] = (int)hi[1]; v[6] = (int)hi[2]; v[7] = (int)hi[3];
+    return v;
+}
+
+template <int DI, int HT, int QG>
+__global__ __launch_bounds__(kWaves * 64) void indexer_scores_kernel(IndexerArgs a) {
+    constexpr int NB = DI / 32;       // scale bytes per row
+    constexpr bool WIDE = DI == 128;  // uses the high K half
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+
+    const int n_groups = (a.S + QG - 1) / QG;
+    const int b = blockIdx.y / n_groups;
+    const int i0 = (blockIdx.y % n_groups) * QG;
+    const int t0 = (blockIdx.x * kWaves + wave) * (16 * kU);
+    if (t0 >= a.T) return;
+    const int i_last = min(i0 + QG - 1, a.S - 1);
+    const int vis_max = min(a.T, (a.start_pos + i_last + 1) / a.ratio);
+    const size_t bs0 = (size_t)b * a.S;
+
+    if (t0 >= vis_max) {  // nothing visible to any query of the group in this chunk
+        if (g == 0) {
+            for (int qq = 0; qq < QG; ++qq) {
+                const int i = i0 + qq;
+                if (i >= a.S) break;
+                float *dst = a.scores + (bs0 + i) * a.ld;
+                for (int u = 0; u < kU; ++u) {
+                    const int t = t0 + 16 * u + c;
+                    if (t < a.T) dst[t] = -INFINITY;
+                }
+            }
+        }
+        return;
+    }
+
+    // Keys first: they are the long-latency stream.
+    i32x8 kb[kU];
+    int ks[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int t = min(t0 + 16 * u + c, a.T - 1);
+        const size_t row = (size_t)b * a.T_cap + t;
+        kb[u] = load_operand(a.k8 + row * DI, g, WIDE);
+        ks[u] = g < NB ? (int)a.k_sc[row * NB + g] : 127;
+    }
+
+    // Query heads of the group, with their scales and head weights.
+    i32x8 qa[QG][HT];
+    int qs[QG][HT];
+    float wr[QG][HT][4];
+#pragma unroll
+    for (int qq = 0; qq < QG; ++qq) {
+        const int i = i0 + qq;
+        const bool valid = i < a.S;
+        const size_t qi = bs0 + (valid ? i : 0);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const size_t head = qi * a.Hi + 16 * ht + c;
+            if (valid) {
+                qa[qq][ht] = load_operand(a.q8 + head * DI, g, WIDE);
+                qs[qq][ht] = g < NB ? (int)a.q_sc[head * NB + g] : 127;
+            } else {
+                qa[qq][ht] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+                qs[qq][ht] = 127;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                wr[qq][ht][r] = valid ? a.w[qi * a.Hi + 16 * ht + 4 * g + r] : 0.f;
+        }
+    }
+
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int t = t0 + 16 * u + c;
+#pragma unroll
+        for (int qq = 0; qq < QG; ++qq) {
+            float part = 0.f;
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    qa[qq][ht], kb[u], acc, 0 /*A e4m3*/, 0 /*B e4m3*/, 0, qs[qq][ht], 0, ks[u]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) part += wr[qq][ht][r] * fmaxf(acc[r], 0.f);
+            }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            const int i = i0 + qq;
+            if (g == 0 && i < a.S && t < a.T) {
+                const int vis = (a.start_pos + i + 1) / a.ratio;
+                a.scores[(bs0 + i) * a.ld + t] = t < vis ? part : -INFINITY;
+            }
+        }
+    }
+}
+
+template <int DI, int HT, int QG>
+hipError_t launch_cfg(const IndexerArgs &a, hipStream_t stream) {
+    const int keys_per_block = kWaves * 16 * kU;
+    dim3 grid((a.T + keys_per_block - 1) / keys_per_block, a.B * ((a.S + QG - 1) / QG));
+    hipLaunchKernelGGL((indexer_scores_kernel<DI, HT, QG>), grid, dim3(kWaves * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DI>
+hipError_t launch_di(const IndexerArgs &a, hipStream_t stream) {
+    const int HT = a.Hi / 16;
+    const bool multi = a.S > 1;
+    switch (HT) {
+        case 1: return multi ? launch_cfg<DI, 1, 4>(a, stream) : launch_cfg<DI, 1, 1>(a, stream);
+        case 2: return multi ? launch_cfg<DI, 2, 2>(a, stream) : launch_cfg<DI, 2, 1>(a, stream);
+        case 3: return launch_cfg<DI, 3, 1>(a, stream);
+        case 4: return launch_cfg<DI, 4, 1>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_indexer_scores(const IndexerArgs &a, hipStream_t stream) {
+    if (a.T <= 0 || a.B <= 0 || a.S <= 0) return hipSuccess;
+    if (a.Di == 64) return launch_di<64>(a, stream);
+    if (a.Di == 128) return launch_di<128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace lit

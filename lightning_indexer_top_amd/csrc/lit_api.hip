@@ -1,0 +1,252 @@
+// lit_api.hip -- the C ABI declared in include/lit.h: host-side argument checks,
+// workspace sizing, and the stream-ordered launches of the kernels in indexer.hip,
+// topk.hip and attention.hip.  Nothing here allocates, frees or synchronises.
+#include "../../include/lit.h"
+
+#include <limits.h>
+
+#include "lit_internal.h"
+
+using namespace lit;
+
+namespace {
+
+// Queries (b, i) index the second grid dimension of the indexer and attention launches.
+constexpr long kMaxQueries = 65535;
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+lit_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return LIT_OK;
+    (void)hipGetLastError();
+    return LIT_E_HIP;
+}
+
+int topk_width(int S, int start_pos, int ratio, int index_topk) {
+    if (ratio <= 0 || index_topk <= 0) return 0;
+    const long T = ((long)start_pos + S) / ratio;
+    return (int)(index_topk < T ? index_topk : T);
+}
+
+lit_status check_indexer(const uint8_t *q8, const uint8_t *q_sc, const float *w, const uint8_t *k8,
+                         const uint8_t *k_sc, int B, int S, int Hi, int Di, int T_cap, int start_pos,
+                         int ratio, const float *scores, int ld_scores) {
+    if (B < 0 || S < 0 || start_pos < 0 || ratio < 1 || T_cap < 0) return LIT_E_SHAPE;
+    if ((long)start_pos + S > INT_MAX) return LIT_E_SHAPE;
+    const long T = ((long)start_pos + S) / ratio;
+    if (T > T_cap) return LIT_E_SHAPE;
+    if (Hi <= 0 || Hi % 16 != 0) return Hi <= 0 ? LIT_E_SHAPE : LIT_E_UNSUPPORTED;
+    if (Hi > 64) return LIT_E_UNSUPPORTED;
+    if ((long)B * S > kMaxQueries) return LIT_E_UNSUPPORTED;
+    if (Di != 64 && Di != 128) return Di <= 0 || Di % 32 ? LIT_E_SHAPE : LIT_E_UNSUPPORTED;
+    if (ld_scores < T) return LIT_E_SHAPE;
+    if (ld_scores % 4 != 0) return LIT_E_ALIGN;
+    if (B == 0 || S == 0 || T == 0) return LIT_OK;
+    if (!q8 || !q_sc || !w || !k8 || !k_sc || !scores) return LIT_E_NULL;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(scores)) return LIT_E_ALIGN;
+    return LIT_OK;
+}
+
+lit_status check_topk(const float *scores, int ld_scores, int B, int S, int start_pos, int ratio,
+                      int index_topk, const int32_t *idx) {
+    if (B < 0 || S < 0 || start_pos < 0 || ratio < 1 || index_topk < 0) return LIT_E_SHAPE;
+    if ((long)start_pos + S > INT_MAX) return LIT_E_SHAPE;
+    const long T = ((long)start_pos + S) / ratio;
+    if (ld_scores < T) return LIT_E_SHAPE;
+    if (ld_scores % 4 != 0) return LIT_E_ALIGN;
+    const int keff = topk_width(S, start_pos, ratio, index_topk);
+    if (B == 0 || S == 0 || keff == 0) return LIT_OK;
+    if (!scores || !idx) return LIT_E_NULL;
+    if (!aligned16(scores)) return LIT_E_ALIGN;
+    return LIT_OK;
+}
+
+long window_need(int S, int start_pos, int W) {
+    if (W <= 0 || S <= 0) return 0;
+    const long span = start_pos == 0 ? (long)S : (long)W + S - 1;
+    const long seen = (long)start_pos + S;
+    return span < seen ? span : seen;
+}
+
+lit_status check_attn(const uint16_t *q, int B, int S, int H, int D, int dv, const uint16_t *win_kv,
+                      int R, const int32_t *win_idx, int W, const uint16_t *comp_kv, int T_cap,
+                      const int32_t *comp_idx, int K, const uint16_t *out) {
+    if (B < 0 || S < 0 || W < 0 || K < 0 || R < 0 || T_cap < 0) return LIT_E_SHAPE;
+    if ((long)B * S > kMaxQueries) return LIT_E_UNSUPPORTED;
+    if (H <= 0 || D <= 0 || dv <= 0 || dv > D) return LIT_E_SHAPE;
+    if (H != 16) return LIT_E_UNSUPPORTED;
+    if (D != 64 && D != 128 && D != 192 && D != 256) return LIT_E_UNSUPPORTED;
+    if (dv % 16 != 0) return LIT_E_UNSUPPORTED;
+    if (W > 0 && R <= 0) return LIT_E_SHAPE;
+    if (K > 0 && T_cap <= 0) return LIT_E_SHAPE;
+    if (B == 0 || S == 0) return LIT_OK;
+    if (!q || !out) return LIT_E_NULL;
+    if (W > 0 && (!win_kv || !win_idx)) return LIT_E_NULL;
+    if (K > 0 && (!comp_kv || !comp_idx)) return LIT_E_NULL;
+    if (!aligned16(q) || (W > 0 && !aligned16(win_kv)) || (K > 0 && !aligned16(comp_kv)))
+        return LIT_E_ALIGN;
+    return LIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lit_status_str(int status) {
+    switch (status) {
+        case LIT_OK: return "LIT_OK";
+        case LIT_E_NULL: return "LIT_E_NULL: a required pointer is NULL";
+        case LIT_E_SHAPE: return "LIT_E_SHAPE: sizes are invalid or inconsistent";
+        case LIT_E_ALIGN: return "LIT_E_ALIGN: a pointer or leading dimension is misaligned";
+        case LIT_E_UNSUPPORTED: return "LIT_E_UNSUPPORTED: shape outside the implemented kernels";
+        case LIT_E_WORKSPACE: return "LIT_E_WORKSPACE: workspace missing or too small";
+        case LIT_E_HIP: return "LIT_E_HIP: a HIP launch failed";
+        default: return "unknown lit_status";
+    }
+}
+
+int lit_abi_version(void) { return LIT_ABI_VERSION; }
+
+lit_status lit_indexer_scores(const uint8_t *q8, const uint8_t *q_sc, const float *w,
+                              const uint8_t *k8, const uint8_t *k_sc, int B, int S, int Hi, int Di,
+                              int T_cap, int start_pos, int ratio, float *scores, int ld_scores,
+                              void *stream) {
+    lit_status st = check_indexer(q8, q_sc, w, k8, k_sc, B, S, Hi, Di, T_cap, start_pos, ratio,
+                                  scores, ld_scores);
+    if (st != LIT_OK) return st;
+    IndexerArgs a{q8, q_sc, w, k8, k_sc, B, S, Hi, Di, T_cap, start_pos, ratio,
+                  (start_pos + S) / ratio, scores, (long)ld_scores};
+    return hip_status(launch_indexer_scores(a, (hipStream_t)stream));
+}
+
+size_t lit_topk_workspace_bytes(int B, int S, int start_pos, int ratio, int index_topk) {
+    (void)B; (void)S; (void)start_pos; (void)ratio; (void)index_topk;
+    return 0;
+}
+
+lit_status lit_topk(const float *scores, int ld_scores, int B, int S, int start_pos, int ratio,
+                    int index_topk, int32_t *idx, void *ws, size_t ws_bytes, void *stream) {
+    (void)ws; (void)ws_bytes;
+    lit_status st = check_topk(scores, ld_scores, B, S, start_pos, ratio, index_topk, idx);
+    if (st != LIT_OK) return st;
+    TopkArgs a{scores, (long)ld_scores, B, S, start_pos, ratio, (start_pos + S) / ratio,
+               topk_width(S, start_pos, ratio, index_topk), idx};
+    return hip_status(launch_topk(a, (hipStream_t)stream));
+}
+
+int lit_window_width(int S, int start_pos, int W) {
+    if (S < 0 || start_pos < 0) return 0;
+    return window_width(S, start_pos, W);
+}
+
+lit_status lit_window_indices(int B, int S, int start_pos, int W, int R, int32_t *win_idx,
+                              void *stream) {
+    if (B < 0 || S < 0 || start_pos < 0 || W < 0 || R < 0) return LIT_E_SHAPE;
+    const long width = window_width(S, start_pos, W);
+    if ((long)B * S * width == 0) return LIT_OK;
+    if (R < window_need(S, start_pos, W)) return LIT_E_SHAPE;
+    if (!win_idx) return LIT_E_NULL;
+    return hip_status(launch_window_indices(B, S, start_pos, W, R, win_idx, (hipStream_t)stream));
+}
+
+size_t lit_sparse_attn_workspace_bytes(int B, int S, int H, int dv, int W, int K) {
+    if (B <= 0 || S <= 0 || H <= 0 || dv <= 0 || W < 0 || K < 0) return 0;
+    const AttnPlan p = plan_attention(B, S, W + K);
+    return attention_partial_bytes(B, S, H, dv, p);
+}
+
+lit_status lit_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv,
+                           const uint16_t *win_kv, int R, const int32_t *win_idx, int W,
+                           const uint16_t *comp_kv, int T_cap, const int32_t *comp_idx, int K,
+                           const float *sink, float scale, uint16_t *out, void *ws, size_t ws_bytes,
+                           void *stream) {
+    lit_status st = check_attn(q, B, S, H, D, dv, win_kv, R, win_idx, W, comp_kv, T_cap, comp_idx,
+                               K, out);
+    if (st != LIT_OK) return st;
+    if (B == 0 || S == 0) return LIT_OK;
+    const AttnPlan p = plan_attention(B, S, W + K);
+    const size_t need = attention_partial_bytes(B, S, H, dv, p);
+    if (need > 0 && (!ws || ws_bytes < need)) return LIT_E_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return LIT_E_ALIGN;
+    // An explicit window list of width W (W == 0: no window rows).  The kernel derives
+    // the window itself only when win_idx is NULL with W > 0, which only the fused
+    // step asks for.
+    AttnArgs a{q, B, S, H, D, dv, W > 0 ? win_kv : nullptr, R, W > 0 ? win_idx : nullptr, W, 0,
+               K > 0 ? comp_kv : nullptr, T_cap, K > 0 ? comp_idx : nullptr, K, sink, scale, out,
+               (float *)ws};
+    return hip_status(launch_sparse_attn(a, p, (hipStream_t)stream));
+}
+
+// Workspace of the fused step: scores [B*S, ld] fp32, then the attention partials.
+static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld, AttnPlan *plan) {
+    const long T = ((long)s->start_pos + s->S) / s->ratio;
+    *ld = (long)round_up((size_t)(T > 0 ? T : 1), 4);
+    *scores_bytes = round_up((size_t)s->B * s->S * (*ld) * sizeof(float), 256);
+    const int nwin = window_width(s->S, s->start_pos, s->W);
+    const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
+    *plan = plan_attention(s->B, s->S, nwin + keff);
+    return *scores_bytes + round_up(attention_partial_bytes(s->B, s->S, s->H, s->dv, *plan), 256);
+}
+
+static lit_status check_step(const lit_step_args *s) {
+    if (!s) return LIT_E_NULL;
+    if (s->ratio < 1 || s->B < 0 || s->S < 0 || s->start_pos < 0) return LIT_E_SHAPE;
+    if ((long)s->start_pos + s->S > INT_MAX) return LIT_E_SHAPE;
+    const long T = ((long)s->start_pos + s->S) / s->ratio;
+    if (T > INT_MAX / 4) return LIT_E_SHAPE;
+    const int ld = (int)round_up((size_t)(T > 0 ? T : 1), 4);
+    lit_status st = check_indexer(s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->B, s->S, s->Hi, s->Di,
+                                  s->T_cap, s->start_pos, s->ratio, (const float *)16, ld);
+    if (st != LIT_OK) return st;
+    const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
+    if (s->index_topk < 0) return LIT_E_SHAPE;
+    if (s->W > 0 && s->R < window_need(s->S, s->start_pos, s->W)) return LIT_E_SHAPE;
+    st = check_attn(s->q, s->B, s->S, s->H, s->D, s->dv, s->win_kv, s->R, (const int32_t *)16,
+                    window_width(s->S, s->start_pos, s->W), s->comp_kv, s->T_cap,
+                    (const int32_t *)16, keff, s->out);
+    if (st != LIT_OK) return st;
+    if (s->B > 0 && s->S > 0 && keff > 0 && !s->topk_idx) return LIT_E_NULL;
+    return LIT_OK;
+}
+
+size_t lit_sparse_step_workspace_bytes(const lit_step_args *s) {
+    if (check_step(s) != LIT_OK) return 0;
+    size_t sb;
+    long ld;
+    AttnPlan p;
+    return step_layout(s, &sb, &ld, &p);
+}
+
+lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, void *stream) {
+    lit_status st = check_step(s);
+    if (st != LIT_OK) return st;
+    if (s->B == 0 || s->S == 0) return LIT_OK;
+    size_t scores_bytes;
+    long ld;
+    AttnPlan plan;
+    const size_t need = step_layout(s, &scores_bytes, &ld, &plan);
+    if (!ws || ws_bytes < need) return LIT_E_WORKSPACE;
+    if (((uintptr_t)ws & 255u) != 0) return LIT_E_ALIGN;
+    hipStream_t hs = (hipStream_t)stream;
+    const int T = (s->start_pos + s->S) / s->ratio;
+    const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
+    float *scores = (float *)ws;
+    hipError_t e = hipSuccess;
+    if (keff > 0) {
+        IndexerArgs ia{s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->B, s->S, s->Hi, s->Di, s->T_cap,
+                       s->start_pos, s->ratio, T, scores, ld};
+        e = launch_indexer_scores(ia, hs);
+        if (e != hipSuccess) return hip_status(e);
+        TopkArgs ta{scores, ld, s->B, s->S, s->start_pos, s->ratio, T, keff, s->topk_idx};
+        e = launch_topk(ta, hs);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    AttnArgs aa{s->q, s->B, s->S, s->H, s->D, s->dv, s->W > 0 ? s->win_kv : nullptr, s->R,
+                nullptr, s->W, s->start_pos, keff > 0 ? s->comp_kv : nullptr, s->T_cap,
+                keff > 0 ? s->topk_idx : nullptr, keff, s->sink, s->scale, s->out,
+                (float *)((char *)ws + scores_bytes)};
+    return hip_status(launch_sparse_attn(aa, plan, hs));
+}
+
+}  // extern "C"

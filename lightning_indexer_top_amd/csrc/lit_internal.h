@@ -1,0 +1,103 @@
+// lit_internal.h -- device-side types, helpers and the launchers each kernel file
+// exports to the C-ABI layer (lit_api.hip).  gfx950 (CDNA4) only: 64-lane waves,
+// MFMA matrix cores, 160 KiB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lit {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Indexer scores (indexer.hip)
+// ---------------------------------------------------------------------------
+struct IndexerArgs {
+    const uint8_t *q8;    // [B,S,Hi,Di]
+    const uint8_t *q_sc;  // [B,S,Hi,Di/32]
+    const float *w;       // [B,S,Hi]
+    const uint8_t *k8;    // [B,T_cap,Di]
+    const uint8_t *k_sc;  // [B,T_cap,Di/32]
+    int B, S, Hi, Di, T_cap, start_pos, ratio;
+    int T;                // (start_pos + S) / ratio, columns written per row
+    float *scores;        // [B,S,ld]
+    long ld;
+};
+hipError_t launch_indexer_scores(const IndexerArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Top-k selection (topk.hip)
+// ---------------------------------------------------------------------------
+struct TopkArgs {
+    const float *scores;  // [B,S,ld]
+    long ld;
+    int B, S, start_pos, ratio;
+    int T;                // columns that exist per row
+    int keff;             // entries written per row
+    int32_t *idx;         // [B,S,keff]
+};
+hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Sparse attention (attention.hip) and window lists
+// ---------------------------------------------------------------------------
+struct AttnArgs {
+    const uint16_t *q;        // [B,S,H,D] bf16
+    int B, S, H, D, dv;
+    const uint16_t *win_kv;   // [B,R,D]
+    int R;
+    const int32_t *win_idx;   // [B,S,W] explicit list, or NULL: derive from start_pos
+    int W;                    // list width (explicit) or window size (derived)
+    int start_pos;            // used when win_idx == NULL
+    const uint16_t *comp_kv;  // [B,T_cap,D]
+    int T_cap;
+    const int32_t *comp_idx;  // [B,S,K]
+    int K;
+    const float *sink;        // [H] or NULL
+    float scale;
+    uint16_t *out;            // [B,S,H,dv] bf16
+    float *part;              // split partials (workspace), may be NULL when 1 split
+};
+// Split plan: how many workgroups share one query's row list.
+struct AttnPlan {
+    int list_len;        // window width + K
+    int tiles_per_wave;  // 32-row tiles each wave handles
+    int n_splits;        // workgroups per query
+};
+AttnPlan plan_attention(int B, int S, int list_len);
+size_t attention_partial_bytes(int B, int S, int H, int dv, const AttnPlan &p);
+hipError_t launch_sparse_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t stream);
+
+// Entries per window list: min(S, W) for a chunk starting at position 0, else W.
+__host__ __device__ inline int window_width(int S, int start_pos, int W) {
+    if (W <= 0) return 0;
+    if (start_pos == 0) return S < W ? S : W;
+    return W;
+}
+hipError_t launch_window_indices(int B, int S, int start_pos, int W, int R, int32_t *win_idx,
+                                 hipStream_t stream);
+
+// The window rule shared by the list builder and the attention kernel: entry j of
+// query i's window list, as a ring slot, or -1.
+__host__ __device__ inline int window_slot(int S, int start_pos, int W, int R, int i, int j) {
+    long p;
+    bool valid;
+    if (start_pos == 0) {
+        long base = i - W + 1 > 0 ? i - W + 1 : 0;
+        p = base + j;
+        valid = p <= i;
+    } else {
+        p = (long)start_pos + i - W + 1 + j;
+        valid = p >= 0;
+    }
+    return valid ? (int)(p % R) : -1;
+}
+
+}  // namespace lit

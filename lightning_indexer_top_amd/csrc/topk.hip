@@ -1,0 +1,200 @@
+// topk.hip -- per-query top-k of the indexer scores, in position order.
+//
+// What is computed (DeepSeek-V4.1-Flash-NVFP4 inference/model.py, Indexer.forward):
+// the k_eff = min(index_topk, end_pos/ratio) best-scoring visible rows of each query,
+// listed in ascending row order, with -1 filling the slots of a query that sees fewer
+// rows.  Ties go to the lower row.
+//
+// Design.  One 1024-thread workgroup per query row.  Scores become order-preserving
+// 32-bit keys (larger float -> larger key, -0 folded onto +0) kept in VGPRs, blocked
+// so that thread j owns a contiguous run of positions.  A three-pass radix select
+// (11 + 11 + 10 bits, most significant first) finds the exact key of the k-th pick:
+// each pass histograms the keys that still match the prefix into 2048 LDS bins, and
+// a block-wide scan over the bins from the top finds the bin where the running count
+// reaches the number still to pick.  A final pass counts, per thread, keys above the
+// threshold and keys equal to it; one packed block scan turns those counts into
+// output offsets, so each selected position lands in its ascending slot with no sort.
+// Rows longer than 1024*ITEMS are processed in segments re-read from L2.
+#include "lit_internal.h"
+
+namespace lit {
+
+namespace {
+
+constexpr int kThreads = 1024;
+
+__device__ inline uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;  // -0 ranks as +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive scan over the workgroup (ascending thread id); *total gets the sum.
+__device__ inline uint32_t block_scan(uint32_t v, uint32_t *wsum, uint32_t *total) {
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+    }
+    if (lane == 63) wsum[wid] = v;
+    __syncthreads();
+    if (wid == 0) {
+        uint32_t s = lane < kThreads / 64 ? wsum[lane] : 0u;
+#pragma unroll
+        for (int off = 1; off < kThreads / 64; off <<= 1) {
+            const uint32_t t = __shfl_up(s, off);
+            if (lane >= off) s += t;
+        }
+        if (lane < kThreads / 64) wsum[lane] = s;
+    }
+    __syncthreads();
+    if (wid > 0) v += wsum[wid - 1];
+    *total = wsum[kThreads / 64 - 1];
+    __syncthreads();
+    return v;
+}
+
+template <int ITEMS>
+__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
+    __shared__ int hist[2048];
+    __shared__ uint32_t wsum[kThreads / 64];
+    __shared__ int sel_bin;
+    __shared__ int sel_above;
+
+    const int row = blockIdx.x;
+    const int i = row % a.S;
+    const int tid = threadIdx.x;
+    int n = (a.start_pos + i + 1) / a.ratio;
+    if (n > a.T) n = a.T;
+    int32_t *out = a.idx + (size_t)row * a.keff;
+    const float *src = a.scores + (size_t)row * a.ld;
+
+    if (n <= a.keff) {  // every visible row is picked
+        for (int j = tid; j < a.keff; j += kThreads) out[j] = j < n ? j : -1;
+        return;
+    }
+
+    constexpr int SEG = kThreads * ITEMS;
+    const int nseg = (n + SEG - 1) / SEG;
+    uint32_t keys[ITEMS];
+    auto load = [&](int seg) -> int {
+        const int base = seg * SEG + tid * ITEMS;
+        const int cnt = max(0, min(ITEMS, n - base));
+        if (cnt == ITEMS) {
+#pragma unroll
+            for (int u = 0; u < ITEMS; u += 4) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(src + base + u);
+                keys[u] = order_key(v[0]);
+                keys[u + 1] = order_key(v[1]);
+                keys[u + 2] = order_key(v[2]);
+                keys[u + 3] = order_key(v[3]);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < ITEMS; ++u) keys[u] = u < cnt ? order_key(src[base + u]) : 0u;
+        }
+        return cnt;
+    };
+
+    int cnt0 = 0;
+    if (nseg == 1) cnt0 = load(0);
+
+    uint32_t prefix = 0u, pmask = 0u;
+    int remaining = a.keff;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nbins = pass == 2 ? 1024 : 2048;
+        for (int j = tid; j < 2048; j += kThreads) hist[j] = 0;
+        __syncthreads();
+        for (int seg = 0; seg < nseg; ++seg) {
+            const int cnt = nseg == 1 ? cnt0 : load(seg);
+#pragma unroll
+            for (int u = 0; u < ITEMS; ++u)
+                if (u < cnt && (keys[u] & pmask) == prefix)
+                    atomicAdd(&hist[(keys[u] >> shift) & (nbins - 1)], 1);
+        }
+        __syncthreads();
+        // Thread j owns bins hi = nbins-1-2j and hi-1 (descending); the scan over
+        // threads counts the keys in the bins above.
+        int c_hi = 0, c_lo = 0;
+        const int hi = nbins - 1 - 2 * tid;
+        if (hi >= 1) {
+            c_hi = hist[hi];
+            c_lo = hist[hi - 1];
+        }
+        uint32_t total;
+        const uint32_t incl = block_scan((uint32_t)(c_hi + c_lo), wsum, &total);
+        const int above = (int)incl - c_hi - c_lo;
+        if (hi >= 1) {
+            if (above < remaining && remaining <= above + c_hi) {
+                sel_bin = hi;
+                sel_above = above;
+            } else if (above + c_hi < remaining && remaining <= above + c_hi + c_lo) {
+                sel_bin = hi - 1;
+                sel_above = above + c_hi;
+            }
+        }
+        __syncthreads();
+        remaining -= sel_above;
+        prefix |= (uint32_t)sel_bin << shift;
+        pmask |= (uint32_t)(nbins - 1) << shift;
+    }
+
+    // prefix is now the exact key of the k-th pick; take every key above it and the
+    // first `remaining` keys equal to it, in position order.
+    const uint32_t thr = prefix;
+    const int need_eq = remaining;
+    int base_gt = 0, base_eq = 0;
+    for (int seg = 0; seg < nseg; ++seg) {
+        const int cnt = nseg == 1 ? cnt0 : load(seg);
+        uint32_t ngt = 0, neq = 0;
+#pragma unroll
+        for (int u = 0; u < ITEMS; ++u) {
+            if (u < cnt) {
+                ngt += keys[u] > thr;
+                neq += keys[u] == thr;
+            }
+        }
+        const uint32_t packed = (ngt << 16) | neq;
+        uint32_t total;
+        const uint32_t excl = block_scan(packed, wsum, &total) - packed;
+        int gt = base_gt + (int)(excl >> 16);
+        int eq = base_eq + (int)(excl & 0xffffu);
+        const int pos0 = seg * SEG + tid * ITEMS;
+#pragma unroll
+        for (int u = 0; u < ITEMS; ++u) {
+            if (u < cnt) {
+                if (keys[u] > thr) {
+                    const int dst = gt + min(eq, need_eq);
+                    if (dst < a.keff) out[dst] = pos0 + u;
+                    ++gt;
+                } else if (keys[u] == thr) {
+                    if (eq < need_eq && gt + eq < a.keff) out[gt + eq] = pos0 + u;
+                    ++eq;
+                }
+            }
+        }
+        base_gt += (int)(total >> 16);
+        base_eq += (int)(total & 0xffffu);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
+    if (a.B <= 0 || a.S <= 0 || a.keff <= 0) return hipSuccess;
+    dim3 grid(a.B * a.S), block(kThreads);
+    if (a.T <= kThreads * 4)
+        hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, stream, a);
+    else if (a.T <= kThreads * 8)
+        hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, stream, a);
+    else if (a.T <= kThreads * 16)
+        hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace lit

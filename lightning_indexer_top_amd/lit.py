@@ -1,0 +1,215 @@
+"""ctypes binding of liblit.so (the C ABI in include/lit.h).
+
+Argument marshalling only: every step runs in the HIP kernels of liblit.so.  PyTorch
+is used for device memory (outputs and workspace are torch tensors the caller may
+pass in) and for the current HIP stream.  There is no fallback: if liblit.so is
+missing or a call is refused, a ``LitError`` is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblit.so")
+
+LIT_OK = 0
+STATUS_NAMES = {0: "LIT_OK", 1: "LIT_E_NULL", 2: "LIT_E_SHAPE", 3: "LIT_E_ALIGN",
+                4: "LIT_E_UNSUPPORTED", 5: "LIT_E_WORKSPACE", 6: "LIT_E_HIP"}
+
+# Every function include/lit.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_Z = ctypes.c_size_t
+_F = ctypes.c_float
+
+
+class lit_step_args(ctypes.Structure):
+    _fields_ = [("B", _I), ("S", _I), ("start_pos", _I), ("ratio", _I),
+                ("Hi", _I), ("Di", _I), ("index_topk", _I), ("T_cap", _I),
+                ("q8", _P), ("q_sc", _P), ("w", _P), ("k8", _P), ("k_sc", _P),
+                ("H", _I), ("D", _I), ("dv", _I), ("W", _I), ("R", _I),
+                ("q", _P), ("win_kv", _P), ("comp_kv", _P), ("sink", _P), ("scale", _F),
+                ("topk_idx", _P), ("out", _P)]
+
+
+SIGNATURES = {
+    "lit_status_str": (ctypes.c_char_p, [_I]),
+    "lit_abi_version": (_I, []),
+    "lit_indexer_scores": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P]),
+    "lit_topk": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
+    "lit_topk_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "lit_window_indices": (_I, [_I, _I, _I, _I, _I, _P, _P]),
+    "lit_window_width": (_I, [_I, _I, _I]),
+    "lit_sparse_attn": (_I, [_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _I, _P, _F,
+                             _P, _P, _Z, _P]),
+    "lit_sparse_attn_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "lit_sparse_step": (_I, [ctypes.POINTER(lit_step_args), _P, _Z, _P]),
+    "lit_sparse_step_workspace_bytes": (_Z, [ctypes.POINTER(lit_step_args)]),
+}
+
+
+class LitError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(status, status)}")
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load liblit.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != LIT_OK:
+        raise LitError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t: torch.Tensor, dtype, name: str) -> None:
+    if t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {dtype} tensor, got {t.dtype}")
+
+
+def topk_width(S: int, start_pos: int, ratio: int, index_topk: int) -> int:
+    return min(index_topk, (start_pos + S) // ratio) if ratio > 0 and index_topk > 0 else 0
+
+
+def lit_window_width(S: int, start_pos: int, W: int) -> int:
+    return library().lit_window_width(S, start_pos, W)
+
+
+def lit_indexer_scores(q8, q_sc, w, k8, k_sc, start_pos: int, ratio: int, scores=None,
+                       stream=None) -> torch.Tensor:
+    """Scores [B,S,ld] fp32 (ld = T rounded up to 4); columns >= T are untouched."""
+    for t, dt, n in ((q8, torch.uint8, "q8"), (q_sc, torch.uint8, "q_sc"), (w, torch.float32, "w"),
+                     (k8, torch.uint8, "k8"), (k_sc, torch.uint8, "k_sc")):
+        _need(t, dt, n)
+    B, S, Hi, Di = q8.shape
+    T_cap = k8.shape[1]
+    T = (start_pos + S) // ratio
+    if scores is None:
+        scores = torch.empty((B, S, max(4, (T + 3) // 4 * 4)), dtype=torch.float32, device=q8.device)
+    _need(scores, torch.float32, "scores")
+    _check("lit_indexer_scores", library().lit_indexer_scores(
+        _ptr(q8), _ptr(q_sc), _ptr(w), _ptr(k8), _ptr(k_sc), B, S, Hi, Di, T_cap, start_pos, ratio,
+        _ptr(scores), scores.shape[-1], _stream(stream)))
+    return scores
+
+
+def lit_topk(scores, start_pos: int, ratio: int, index_topk: int, idx=None, ws=None,
+             stream=None) -> torch.Tensor:
+    """Top-k row lists [B,S,k_eff] int32 (ascending, -1 padded)."""
+    _need(scores, torch.float32, "scores")
+    B, S, ld = scores.shape
+    keff = topk_width(S, start_pos, ratio, index_topk)
+    if idx is None:
+        idx = torch.empty((B, S, keff), dtype=torch.int32, device=scores.device)
+    _need(idx, torch.int32, "idx")
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("lit_topk", library().lit_topk(_ptr(scores), ld, B, S, start_pos, ratio, index_topk,
+                                          _ptr(idx), _ptr(ws), nbytes, _stream(stream)))
+    return idx
+
+
+def lit_window_indices(B: int, S: int, start_pos: int, W: int, R: int, win_idx=None,
+                       device="cuda", stream=None) -> torch.Tensor:
+    width = lit_window_width(S, start_pos, W)
+    if win_idx is None:
+        win_idx = torch.empty((B, S, width), dtype=torch.int32, device=device)
+    _need(win_idx, torch.int32, "win_idx")
+    _check("lit_window_indices", library().lit_window_indices(B, S, start_pos, W, R, _ptr(win_idx),
+                                                              _stream(stream)))
+    return win_idx
+
+
+def lit_sparse_attn_workspace_bytes(B, S, H, dv, W, K) -> int:
+    return library().lit_sparse_attn_workspace_bytes(B, S, H, dv, W, K)
+
+
+def lit_sparse_attn(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float, dv=None,
+                    out=None, ws=None, stream=None) -> torch.Tensor:
+    """Attention [B,S,H,dv] bf16 over the window slots in win_idx and the compressed rows in
+    comp_idx (either source may be None)."""
+    _need(q, torch.bfloat16, "q")
+    B, S, H, D = q.shape
+    dv = D if dv is None else dv
+    W = 0 if win_idx is None else win_idx.shape[-1]
+    K = 0 if comp_idx is None else comp_idx.shape[-1]
+    R = 0 if win_kv is None else win_kv.shape[1]
+    T_cap = 0 if comp_kv is None else comp_kv.shape[1]
+    for t, dt, n in ((win_kv, torch.bfloat16, "win_kv"), (comp_kv, torch.bfloat16, "comp_kv"),
+                     (win_idx, torch.int32, "win_idx"), (comp_idx, torch.int32, "comp_idx"),
+                     (sink, torch.float32, "sink")):
+        if t is not None:
+            _need(t, dt, n)
+    if out is None:
+        out = torch.empty((B, S, H, dv), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out")
+    need = lit_sparse_attn_workspace_bytes(B, S, H, dv, W, K)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("lit_sparse_attn", library().lit_sparse_attn(
+        _ptr(q), B, S, H, D, dv, _ptr(win_kv), R, _ptr(win_idx), W, _ptr(comp_kv), T_cap,
+        _ptr(comp_idx), K, _ptr(sink), float(scale), _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int, ratio: int,
+                   index_topk: int, W: int, scale: float, dv=None, sink=None, topk_idx=None,
+                   out=None) -> tuple:
+    """Build the lit_step_args struct (and allocate outputs the caller did not pass)."""
+    B, S, Hi, Di = q8.shape
+    H, D = q.shape[2], q.shape[3]
+    dv = D if dv is None else dv
+    keff = topk_width(S, start_pos, ratio, index_topk)
+    if topk_idx is None:
+        topk_idx = torch.empty((B, S, keff), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty((B, S, H, dv), dtype=torch.bfloat16, device=q.device)
+    a = lit_step_args(B=B, S=S, start_pos=start_pos, ratio=ratio, Hi=Hi, Di=Di,
+                      index_topk=index_topk, T_cap=k8.shape[1], q8=q8.data_ptr(),
+                      q_sc=q_sc.data_ptr(), w=w.data_ptr(), k8=k8.data_ptr(), k_sc=k_sc.data_ptr(),
+                      H=H, D=D, dv=dv, W=W, R=win_kv.shape[1], q=q.data_ptr(),
+                      win_kv=win_kv.data_ptr(), comp_kv=comp_kv.data_ptr(),
+                      sink=0 if sink is None else sink.data_ptr(), scale=scale,
+                      topk_idx=topk_idx.data_ptr(), out=out.data_ptr())
+    return a, topk_idx, out
+
+
+def lit_sparse_step_workspace_bytes(args: lit_step_args) -> int:
+    return library().lit_sparse_step_workspace_bytes(ctypes.byref(args))
+
+
+def lit_sparse_step(args: lit_step_args, ws: torch.Tensor, stream=None) -> None:
+    """Run indexer -> top-k -> attention for one layer on the stream."""
+    nbytes = ws.numel() * ws.element_size()
+    _check("lit_sparse_step", library().lit_sparse_step(ctypes.byref(args), _ptr(ws), nbytes,
+                                                        _stream(stream)))

@@ -1,0 +1,62 @@
+"""Helpers shared by the GPU tests: host arrays -> device tensors and back."""
+import numpy as np
+import torch
+
+
+def dev(a: np.ndarray, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def bf16_dev(bits: np.ndarray) -> torch.Tensor:
+    return dev(np.ascontiguousarray(bits).view(np.int16), torch.bfloat16)
+
+
+def bf16_host(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def step_inputs_dev(inp):
+    """Device copies of every array of a synth.StepInputs."""
+    return dict(q8=dev(inp.q8), q_sc=dev(inp.q_sc), w=dev(inp.w), k8=dev(inp.k8),
+                k_sc=dev(inp.k_sc), q=bf16_dev(inp.q), win_kv=bf16_dev(inp.win_kv),
+                comp_kv=bf16_dev(inp.comp_kv),
+                sink=None if inp.sink is None else dev(inp.sink))
+
+
+def lib_dequant(codes, scales):
+    """e4m3 codes x ue8m0 scales decoded with torch's casts (for tolerance scales)."""
+    c = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64)
+    s = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e8m0fnu).to(torch.float64)
+    return (c.unflatten(-1, (-1, 32)) * s.unsqueeze(-1)).flatten(-2).numpy()
+
+
+def score_tolerance(inp):
+    """Per-entry bound for fp32/MFMA scores: 1e-4 of sum_h w_h sum_d |q_hd k_td| (the
+    magnitude the contraction accumulates) plus 1e-6 relative; see the design doc."""
+    qd = np.abs(lib_dequant(inp.q8, inp.q_sc))          # [B,S,Hi,Di]
+    kd = np.abs(lib_dequant(inp.k8, inp.k_sc))          # [B,T_cap,Di]
+    T = inp.T
+    out = np.empty((inp.B, inp.S, T))
+    for b in range(inp.B):
+        wq = np.einsum("sh,shd->sd", inp.w[b].astype(np.float64), qd[b])   # [S,Di]
+        out[b] = wq @ kd[b, :T].T
+    return out
+
+
+def topk_sets_agree(orc_scores, orc_idx, gpu_idx, rel=1e-3):
+    """The acceptance rule for top-k: identical sets, except that every row in the
+    symmetric difference scores within rel * |s_k| of the oracle's k-th score s_k."""
+    o = set(int(x) for x in orc_idx if x >= 0)
+    g = set(int(x) for x in gpu_idx if x >= 0)
+    if len(o) != len(g):
+        return False, f"sizes differ {len(o)} vs {len(g)}"
+    if o == g:
+        return True, ""
+    sk = min(orc_scores[t] for t in o)
+    for t in o ^ g:
+        if abs(orc_scores[t] - sk) > rel * abs(sk):
+            return False, f"row {t} score {orc_scores[t]} vs k-th {sk}"
+    return True, f"{len(o ^ g)} near-tie swaps"

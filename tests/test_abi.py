@@ -1,0 +1,139 @@
+"""CPU checks of the C ABI: liblit.so loads, exports every entry point include/lit.h
+declares, and refuses bad arguments on the host before anything is launched.  No call
+here reaches a kernel launch (no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lightning_indexer_top_amd as L
+from lightning_indexer_top_amd import lit as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lit.h")
+A = 0x10000      # a 16-byte aligned stand-in address; never dereferenced on refusal
+MIS = 0x10001    # misaligned stand-in
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from lightning_indexer_top_amd import build as bld
+        bld.build()
+    return L.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lit_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in B.SIGNATURES, f"binding lacks {n}"
+    assert set(B.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.lit_abi_version() == 1
+    for code, name in B.STATUS_NAMES.items():
+        assert lib.lit_status_str(code).decode().startswith(name)
+    assert b"unknown" in lib.lit_status_str(99)
+
+
+def scores_call(lib, **kw):
+    a = dict(q8=A, q_sc=A, w=A, k8=A, k_sc=A, B=1, S=1, Hi=16, Di=64, T_cap=512, start_pos=1023,
+             ratio=2, scores=A, ld=512)
+    a.update(kw)
+    return lib.lit_indexer_scores(a["q8"], a["q_sc"], a["w"], a["k8"], a["k_sc"], a["B"], a["S"],
+                                  a["Hi"], a["Di"], a["T_cap"], a["start_pos"], a["ratio"],
+                                  a["scores"], a["ld"], None)
+
+
+def test_indexer_refusals(lib):
+    assert scores_call(lib, Di=48) == 2
+    assert scores_call(lib, Di=96) == 4
+    assert scores_call(lib, Hi=8) == 4
+    assert scores_call(lib, Hi=80) == 4
+    assert scores_call(lib, Hi=0) == 2
+    assert scores_call(lib, T_cap=511) == 2          # T = 512 rows visible
+    assert scores_call(lib, ld=510) == 2
+    assert scores_call(lib, ld=514) == 3
+    assert scores_call(lib, ratio=0) == 2
+    assert scores_call(lib, k8=None) == 1
+    assert scores_call(lib, scores=None) == 1
+    assert scores_call(lib, k8=MIS) == 3
+    assert scores_call(lib, B=0) == 0                 # nothing to do
+    assert scores_call(lib, start_pos=0, S=1, ratio=2) == 0   # T = 0
+
+
+def test_topk_refusals(lib):
+    f = lib.lit_topk
+    assert f(A, 8, 1, 1, 1023, 2, 64, A, None, 0, None) == 2        # ld < T
+    assert f(A, 514, 1, 1, 1023, 2, 64, A, None, 0, None) == 3      # ld not a multiple of 4
+    assert f(None, 512, 1, 1, 1023, 2, 64, A, None, 0, None) == 1
+    assert f(A, 512, 1, 1, 1023, 2, 64, None, None, 0, None) == 1
+    assert f(A, 512, 1, 1, 1023, 2, -1, A, None, 0, None) == 2
+    assert f(A, 512, 1, 1, 1023, 2, 0, None, None, 0, None) == 0    # k = 0: nothing
+    assert lib.lit_topk_workspace_bytes(8, 1, 16383, 2, 2048) == 0
+
+
+def attn_call(lib, **kw):
+    a = dict(q=A, B=1, S=1, H=16, D=128, dv=128, win_kv=A, R=128, win_idx=A, W=128, comp_kv=A,
+             T_cap=512, comp_idx=A, K=64, sink=None, scale=0.1, out=A, ws=A, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.lit_sparse_attn(a["q"], a["B"], a["S"], a["H"], a["D"], a["dv"], a["win_kv"], a["R"],
+                               a["win_idx"], a["W"], a["comp_kv"], a["T_cap"], a["comp_idx"], a["K"],
+                               a["sink"], a["scale"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+def test_attention_refusals(lib):
+    assert attn_call(lib, H=32) == 4
+    assert attn_call(lib, D=96, dv=96) == 4
+    assert attn_call(lib, dv=256) == 2
+    assert attn_call(lib, dv=40) == 4
+    assert attn_call(lib, R=0) == 2
+    assert attn_call(lib, q=None) == 1
+    assert attn_call(lib, comp_idx=None) == 1
+    assert attn_call(lib, win_kv=None) == 1
+    assert attn_call(lib, comp_kv=MIS) == 3
+    need = lib.lit_sparse_attn_workspace_bytes(1, 1, 16, 128, 128, 2048)
+    assert need > 0
+    assert attn_call(lib, K=2048, T_cap=4096, ws=None, ws_bytes=0) == 5
+    assert attn_call(lib, K=2048, T_cap=4096, ws_bytes=need - 1) == 5
+    assert attn_call(lib, B=0) == 0
+
+
+def test_window_refusals(lib):
+    assert lib.lit_window_indices(1, 8, 100, 16, 16, A, None) == 2   # needs 23 slots
+    assert lib.lit_window_indices(1, 8, 100, 16, 23, None, None) == 1
+    assert lib.lit_window_indices(-1, 8, 100, 16, 23, A, None) == 2
+    assert lib.lit_window_indices(0, 8, 100, 16, 23, None, None) == 0
+    assert lib.lit_window_width(5, 0, 128) == 5
+    assert lib.lit_window_width(1, 1023, 128) == 128
+
+
+def test_step_refusals(lib):
+    args = B.lit_step_args(B=8, S=1, start_pos=16383, ratio=2, Hi=64, Di=128, index_topk=2048,
+                           T_cap=8192, q8=A, q_sc=A, w=A, k8=A, k_sc=A, H=16, D=192, dv=192, W=128,
+                           R=128, q=A, win_kv=A, comp_kv=A, sink=0, scale=0.07, topk_idx=A, out=A)
+    need = lib.lit_sparse_step_workspace_bytes(ctypes.byref(args))
+    assert need >= 8 * 8192 * 4
+    assert lib.lit_sparse_step(None, A, need, None) == 1
+    assert lib.lit_sparse_step(ctypes.byref(args), A, need - 1, None) == 5
+    assert lib.lit_sparse_step(ctypes.byref(args), None, 0, None) == 5
+    assert lib.lit_sparse_step(ctypes.byref(args), A + 16, need, None) == 3   # not 256-aligned
+    args.T_cap = 4000
+    assert lib.lit_sparse_step(ctypes.byref(args), A, need, None) == 2
+    args.T_cap = 8192
+    args.R = 64                                                             # window ring too small
+    assert lib.lit_sparse_step(ctypes.byref(args), A, need, None) == 2
+    args.R = 128
+    args.topk_idx = 0
+    assert lib.lit_sparse_step(ctypes.byref(args), A, need, None) == 1
+    assert lib.lit_sparse_step_workspace_bytes(None) == 0

@@ -1,0 +1,294 @@
+"""GPU parity: every entry point of liblit.so against the fp64 oracle, through the C ABI.
+
+Acceptance rules (the tolerances of the sparse-attention step):
+* window lists and top-k of identical fp32 scores: bit-exact;
+* indexer scores: |gpu - oracle| <= 1e-4 * sum_h w_h sum_d |q_hd k_td| + 1e-6 |s| (the
+  MX-scaled MFMA's accumulation error, bounded by the magnitudes it sums), and -inf
+  exactly where the oracle has -inf;
+* top-k from the full pipeline: sets identical, except rows within 1e-3 relative of the
+  oracle's k-th score;
+* attention: max |gpu - oracle| <= 2e-2 (bf16 output) given the same selected set.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lightning_indexer_top_amd as L
+from lightning_indexer_top_amd import synth
+from tests.gpu_util import (bf16_dev, bf16_host, dev, score_tolerance, step_inputs_dev,
+                            topk_sets_agree)
+
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.library()
+
+
+# ---------------------------------------------------------------------------------
+# indexer scores
+# ---------------------------------------------------------------------------------
+INDEXER_CASES = [
+    # B, S, start_pos, ratio, Hi, Di
+    (2, 1, 999, 2, 16, 64),      # ragged tail: 500 rows
+    (1, 1, 1023, 2, 16, 64),     # the 1K decode shape
+    (3, 1, 2047, 1, 32, 128),
+    (2, 1, 4095, 2, 64, 128),
+    (1, 70, 0, 2, 16, 64),       # prefill from 0, causal rows
+    (2, 37, 100, 3, 32, 64),     # chunk after cached tokens, groups of 2 queries
+    (1, 45, 300, 4, 64, 128),
+    (1, 9, 20, 1, 48, 128),      # three head tiles
+]
+
+
+@pytest.mark.parametrize("B,S,start_pos,ratio,Hi,Di", INDEXER_CASES)
+def test_indexer_scores(orc, B, S, start_pos, ratio, Hi, Di):
+    inp = synth.make_step(B=B, S=S, start_pos=start_pos, ratio=ratio, Hi=Hi, Di=Di, H=16, D=64,
+                          W=8, index_topk=16, seed=1000 + B * 7 + S + Hi + Di)
+    d = step_inputs_dev(inp)
+    got = L.lit_indexer_scores(d["q8"], d["q_sc"], d["w"], d["k8"], d["k_sc"], start_pos, ratio)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().astype(np.float64)[..., :inp.T]
+    want = orc.index_scores(inp.q8, inp.q_sc, inp.w, inp.k8, inp.k_sc, start_pos, ratio)
+    inf = np.isneginf(want)
+    assert np.array_equal(np.isneginf(got), inf)
+    tol = 1e-4 * score_tolerance(inp) + 1e-6 * np.abs(np.where(inf, 0, want))
+    err = np.abs(np.where(inf, 0.0, got) - np.where(inf, 0.0, want))
+    assert np.all(err <= tol), f"max err {err.max()} (tol at argmax {tol.flat[err.argmax()]})"
+
+
+def test_indexer_keys_scaled_by_four(orc):
+    """The decode-4k shape whose boosted key rows (x4: +2 on every scale byte) stand out."""
+    inp = synth.workload("decode-4k-r2")
+    d = step_inputs_dev(inp)
+    got = L.lit_indexer_scores(d["q8"], d["q_sc"], d["w"], d["k8"], d["k_sc"], inp.start_pos,
+                               inp.ratio).cpu().numpy().astype(np.float64)[..., :inp.T]
+    want = orc.index_scores(inp.q8, inp.q_sc, inp.w, inp.k8, inp.k_sc, inp.start_pos, inp.ratio)
+    tol = 1e-4 * score_tolerance(inp) + 1e-6 * np.abs(want)
+    assert np.all(np.abs(got - want) <= tol)
+
+
+# ---------------------------------------------------------------------------------
+# top-k on identical fp32 scores: bit-exact
+# ---------------------------------------------------------------------------------
+TOPK_CASES = [
+    # B, S, start_pos, ratio, k, ties
+    (1, 1, 1023, 2, 64, False),
+    (4, 1, 4095, 1, 64, False),
+    (8, 1, 16383, 2, 2048, False),
+    (2, 1, 131071, 4, 2048, False),
+    (3, 1, 4095, 2, 300, True),          # many equal scores at the threshold
+    (1, 1, 79999, 2, 1000, False),       # 40000 rows: segmented path
+    (1, 64, 0, 2, 16, False),            # prefill from 0: short rows padded with -1
+    (2, 33, 500, 3, 100, True),
+    (1, 1, 9, 1, 64, False),             # k larger than the rows: all of them
+]
+
+
+@pytest.mark.parametrize("B,S,start_pos,ratio,k,ties", TOPK_CASES)
+def test_topk_exact(orc, B, S, start_pos, ratio, k, ties):
+    T = (start_pos + S) // ratio
+    ld = (T + 3) // 4 * 4
+    sc = synth.random_scores(B, S, ld, seed=B * 131 + S + k, ties=ties)
+    got = L.lit_topk(dev(sc), start_pos, ratio, k)
+    torch.cuda.synchronize()
+    want = orc.topk(sc.astype(np.float64), start_pos, ratio, k)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_topk_all_equal_and_signed_zero(orc):
+    sc = np.zeros((2, 1, 1024), np.float32)
+    sc[1, 0, ::3] = -0.0
+    got = L.lit_topk(dev(sc), 1023, 1, 100)
+    want = orc.topk(sc.astype(np.float64), 1023, 1, 100)
+    assert np.array_equal(got.cpu().numpy(), want)
+    assert np.array_equal(want[0, 0], np.arange(100))
+
+
+# ---------------------------------------------------------------------------------
+# window lists
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("B,S,start_pos,W,R", [(2, 1, 2, 4, 4), (1, 5, 0, 3, 5), (2, 1, 1023, 128, 128),
+                                               (1, 4096, 12288, 128, 4223), (1, 300, 0, 128, 300),
+                                               (3, 7, 100, 4, 10)])
+def test_window_indices(orc, B, S, start_pos, W, R):
+    got = L.lit_window_indices(B, S, start_pos, W, R)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), orc.window_indices(B, S, start_pos, W, R))
+
+
+# ---------------------------------------------------------------------------------
+# sparse attention on oracle-chosen index lists
+# ---------------------------------------------------------------------------------
+def _attn_case(orc, B, S, start_pos, ratio, D, dv, W, k, seed, sink=None, minus_ones=0,
+               repeat=False, R=None):
+    inp = synth.make_step(B=B, S=S, start_pos=start_pos, ratio=ratio, Hi=16, Di=64, H=16, D=D,
+                          W=W, index_topk=k, seed=seed, dv=dv, R=R, sink=sink)
+    rng = np.random.default_rng(seed)
+    T = inp.T
+    keff = inp.k_eff
+    comp_idx = np.stack([np.stack([np.sort(rng.choice(T, keff, replace=False)) for _ in range(S)])
+                         for _ in range(B)]).astype(np.int32) if keff > 0 else np.zeros((B, S, 0), np.int32)
+    if minus_ones and keff > 0:
+        comp_idx[..., -minus_ones:] = -1
+    if repeat and keff > 1:
+        comp_idx[..., 1] = comp_idx[..., 0]
+    win_idx = orc.window_indices(B, S, start_pos, W, inp.R) if W > 0 else None
+    return inp, win_idx, comp_idx
+
+
+ATTN_CASES = [
+    # B, S, start_pos, ratio, D, dv, W, k, extra
+    (1, 1, 1023, 2, 128, 128, 128, 64, {}),
+    (4, 1, 4095, 1, 128, 128, 128, 64, {}),
+    (2, 1, 16383, 2, 192, 192, 128, 2048, {}),
+    (2, 1, 16383, 2, 192, 128, 128, 300, {}),               # dv < D
+    (1, 1, 600, 2, 256, 256, 128, 100, {"minus_ones": 7}),
+    (2, 1, 4000, 2, 64, 64, 0, 77, {}),                     # compressed rows only
+    (2, 1, 300, 2, 128, 128, 128, 0, {}),                   # window only (k = 0)
+    (1, 200, 1000, 2, 128, 128, 128, 50, {}),               # many queries: one split each
+    (1, 40, 0, 2, 128, 64, 16, 8, {"repeat": True}),        # prefill from 0, repeated rows
+    (2, 1, 5000, 2, 128, 128, 128, 500, {"sink": "mixed"}),
+]
+
+
+@pytest.mark.parametrize("B,S,start_pos,ratio,D,dv,W,k,extra", ATTN_CASES)
+def test_sparse_attn(orc, B, S, start_pos, ratio, D, dv, W, k, extra):
+    extra = dict(extra)
+    sink = None
+    if extra.pop("sink", None) == "mixed":
+        sink = np.linspace(-3.0, 6.0, 16).astype(np.float32)
+    inp, win_idx, comp_idx = _attn_case(orc, B, S, start_pos, ratio, D, dv, W, k,
+                                        seed=77 + B + S + D + k, sink=sink, **extra)
+    d = step_inputs_dev(inp)
+    got = L.lit_sparse_attn(d["q"], d["win_kv"] if W else None,
+                            dev(win_idx) if win_idx is not None else None,
+                            d["comp_kv"], dev(comp_idx) if comp_idx.shape[-1] else None,
+                            d["sink"], inp.scale, dv=dv)
+    torch.cuda.synchronize()
+    want = orc.sparse_attn(inp.q, inp.win_kv, win_idx, inp.comp_kv,
+                           comp_idx if comp_idx.shape[-1] else None, inp.sink, inp.scale, dv)
+    err = np.abs(bf16_host(got) - want).max()
+    assert err <= ATTN_TOL, err
+
+
+def test_sparse_attn_empty_lists_and_huge_sink(orc):
+    inp, win_idx, comp_idx = _attn_case(orc, 2, 3, 0, 2, 128, 128, 0, 4, seed=5)
+    comp_idx[:] = -1
+    d = step_inputs_dev(inp)
+    got = L.lit_sparse_attn(d["q"], None, None, d["comp_kv"], dev(comp_idx), None, inp.scale)
+    assert torch.count_nonzero(got.float()).item() == 0
+    comp_idx[..., 0] = 0
+    big = torch.full((16,), 1e4, dtype=torch.float32, device="cuda")
+    got = L.lit_sparse_attn(d["q"], None, None, d["comp_kv"], dev(comp_idx), big, inp.scale)
+    assert got.float().abs().max().item() == 0.0
+
+
+# ---------------------------------------------------------------------------------
+# the fused step
+# ---------------------------------------------------------------------------------
+def _run_step(d, inp):
+    args, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
+                                      k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
+                                      comp_kv=d["comp_kv"], start_pos=inp.start_pos,
+                                      ratio=inp.ratio, index_topk=inp.index_topk, W=inp.W,
+                                      scale=inp.scale, dv=inp.dv, sink=d["sink"])
+    ws = torch.empty(max(256, L.lit_sparse_step_workspace_bytes(args)), dtype=torch.uint8,
+                     device="cuda")
+    L.lit_sparse_step(args, ws)
+    torch.cuda.synchronize()
+    return idx, out
+
+
+def _check_step(orc, inp, idx, out, queries=None):
+    """Compare a step's outputs with the oracle, query by query (b, i)."""
+    d_idx = idx.cpu().numpy()
+    d_out = bf16_host(out)
+    queries = queries or [(b, i) for b in range(inp.B) for i in range(inp.S)]
+    swaps = 0
+    for (b, i) in queries:
+        sub = _one_query(inp, b, i)
+        ref = orc.step(sub)
+        keff_i = ref["idx"].shape[-1]
+        g_idx = d_idx[b, i]
+        assert np.all(g_idx[keff_i:] == -1)
+        ok, why = topk_sets_agree(ref["scores"][0, 0], ref["idx"][0, 0], g_idx[:keff_i])
+        assert ok, f"query {(b, i)}: {why}"
+        if set(ref["idx"][0, 0]) == set(g_idx[:keff_i]):
+            err = np.abs(d_out[b, i] - ref["out"][0, 0]).max()
+            assert err <= ATTN_TOL, f"query {(b, i)}: attention err {err}"
+        else:
+            swaps += 1
+    return swaps
+
+
+def _one_query(inp, b, i):
+    """The same query as a single-query decode at its own position (the oracle then
+    computes exactly that query's scores, picks and output)."""
+    import dataclasses
+    P = inp.start_pos + i
+    sub = dataclasses.replace(
+        inp, B=1, S=1, start_pos=P, q8=inp.q8[b:b + 1, i:i + 1], q_sc=inp.q_sc[b:b + 1, i:i + 1],
+        w=inp.w[b:b + 1, i:i + 1], q=inp.q[b:b + 1, i:i + 1], k8=inp.k8[b:b + 1],
+        k_sc=inp.k_sc[b:b + 1], win_kv=inp.win_kv[b:b + 1], comp_kv=inp.comp_kv[b:b + 1])
+    return sub
+
+
+STEP_SMALL = [
+    dict(B=2, S=1, start_pos=700, ratio=2, Hi=16, Di=64, H=16, D=128, W=128, index_topk=64),
+    dict(B=1, S=50, start_pos=2000, ratio=2, Hi=16, Di=64, H=16, D=128, W=128, index_topk=100),
+    dict(B=2, S=1, start_pos=3000, ratio=4, Hi=64, Di=128, H=16, D=192, W=128, index_topk=300),
+    dict(B=1, S=1, start_pos=2, ratio=4, Hi=16, Di=64, H=16, D=128, W=128, index_topk=64),  # T = 0
+]
+
+
+@pytest.mark.parametrize("cfg", STEP_SMALL, ids=lambda c: f"B{c['B']}S{c['S']}p{c['start_pos']}r{c['ratio']}")
+def test_step_small(orc, cfg):
+    inp = synth.make_step(seed=4242 + cfg["start_pos"], **cfg)
+    idx, out = _run_step(step_inputs_dev(inp), inp)
+    _check_step(orc, inp, idx, out)
+
+
+@pytest.mark.parametrize("name", ["decode-1k", "decode-4k-r2", "decode-4k-r1", "decode-16k",
+                                  "decode-128k"])
+def test_step_workloads(orc, name):
+    inp = synth.workload(name)
+    idx, out = _run_step(step_inputs_dev(inp), inp)
+    swaps = _check_step(orc, inp, idx, out)
+    assert swaps <= max(1, inp.B // 2), f"{swaps} queries with near-tie swaps"
+
+
+def test_step_prefill_sampled(orc):
+    """The 4096-query chunk at full size; 24 sampled queries checked one by one."""
+    inp = synth.workload("prefill-16k")
+    idx, out = _run_step(step_inputs_dev(inp), inp)
+    rng = np.random.default_rng(1)
+    sample = sorted(set([0, 1, inp.S - 1] + list(rng.choice(inp.S, 21, replace=False))))
+    _check_step(orc, inp, idx, out, [(0, int(i)) for i in sample])
+
+
+def test_step_deterministic():
+    inp = synth.workload("decode-16k")
+    d = step_inputs_dev(inp)
+    i1, o1 = _run_step(d, inp)
+    i2, o2 = _run_step(d, inp)
+    assert torch.equal(i1, i2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_step_matches_separate_calls():
+    """The fused step and the three separate entry points give identical results."""
+    inp = synth.workload("decode-4k-r2")
+    d = step_inputs_dev(inp)
+    idx, out = _run_step(d, inp)
+    sc = L.lit_indexer_scores(d["q8"], d["q_sc"], d["w"], d["k8"], d["k_sc"], inp.start_pos, inp.ratio)
+    idx2 = L.lit_topk(sc, inp.start_pos, inp.ratio, inp.index_topk)
+    win = L.lit_window_indices(inp.B, inp.S, inp.start_pos, inp.W, inp.R)
+    out2 = L.lit_sparse_attn(d["q"], d["win_kv"], win, d["comp_kv"], idx2, None, inp.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
