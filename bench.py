@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse-attention step (indexer -> top-k -> sparse attention) on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode-16k]
+
+A step is one lit_sparse_step call over one batch of synthetic inputs resident in HBM:
+index scores for every visible compressed row, the per-query top-k, and attention over
+the sliding window plus the selected rows.  Inputs rotate over enough independent
+instances that the 256 MB Infinity Cache cannot serve repeats (cold-cache protocol), and
+the steps are replayed from a HIP graph.  Exactly K steps are timed between two
+device synchronisations.  Per-stage kernel durations come from HIP events recorded on
+the same stream around replays of graphs holding one stage's launches over the same
+rotating instances.  One JSON line is printed on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode queries/sec + achieved HBM GB/s vs peak, indexer+topk+sparse_attn"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_bytes(sp: dict) -> dict:
+    """Algorithmic bytes of one step, by stage (what the method must move: inputs read
+    once, outputs written once; the fp32 score buffer is counted for the indexer that
+    writes it and the selector that reads it)."""
+    B, S, sp0, r = sp["B"], sp["S"], sp["start_pos"], sp["ratio"]
+    Hi, Di, H, D, W, k = sp["Hi"], sp["Di"], sp["H"], sp["D"], sp["W"], sp["index_topk"]
+    dv = sp.get("dv", D)
+    T = (sp0 + S) // r
+    keff = min(k, T)
+    key_row = Di + Di // 32
+    indexer = B * T * key_row + B * S * Hi * (key_row + 4) + 4 * B * S * T
+    topk = 4 * B * S * T + 4 * B * S * keff
+    if S == 1:
+        attn = B * ((W + keff) * (2 * D + 4) + 2 * H * D + 2 * H * dv)
+        # the survey's per-query figure: keys + q/w + indices written + gathered rows
+        # with their indices + q/out
+        step = B * (T * key_row + Hi * key_row + 4 * Hi + 4 * keff + (W + keff) * (2 * D + 4)
+                    + 2 * H * D + 2 * H * dv)
+    else:
+        R = S if sp0 == 0 else W + S - 1
+        attn = (4 * B * S * keff + B * R * 2 * D + B * T * 2 * D + B * S * H * (2 * D + 2 * dv))
+        step = (B * T * key_row + B * S * Hi * (key_row + 4) + 8 * B * S * keff + B * R * 2 * D
+                + B * T * 2 * D + B * S * H * (2 * D + 2 * dv))
+    return {"step": step, "indexer": indexer, "topk": topk, "attention": attn}
+
+
+def traffic_for(kernel: str, src: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(name: str, budget_s: float) -> dict:
+    import oracle
+    from lightning_indexer_top_amd import synth
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    inp = synth.workload(name)
+    log(f"[bench] oracle inputs drawn in {time.perf_counter() - t0:.1f}s")
+    runs, elapsed = 0, 0.0
+    while runs == 0 or (elapsed < budget_s and runs < 8):
+        t = time.perf_counter()
+        oracle.step(inp)
+        elapsed += time.perf_counter() - t
+        runs += 1
+        log(f"[bench] oracle run {runs}: {elapsed:.1f}s")
+    q = inp.B * inp.S * runs
+    return {"value": q / elapsed, "unit": "queries/s",
+            "cores": min(oracle.num_threads(), inp.B * inp.S), "kind": "oracle",
+            "sample": f"{runs} full step(s) of {name} ({inp.B * inp.S} queries each), "
+                      f"{elapsed:.1f}s of oracle time"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="decode-16k")
+    ap.add_argument("--instances", type=int, default=0, help="input instances (0 = cold-cache rule)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has "
+              "no multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import torch
+    import lightning_indexer_top_amd as L
+    from lightning_indexer_top_amd import synth
+
+    spec = dict(synth.WORKLOADS[args.workload])
+    sb = step_bytes(spec)
+    n_inst = args.instances or max(2, min(512, math.ceil(3 * MALL_BYTES / sb["step"])))
+    K, Wm = args.steps, args.warmup
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] {args.workload}: {n_inst} instances, step bytes {sb['step']}")
+
+    # -- inputs and per-instance step arguments (all resident in HBM) ------------------
+    insts, argv, keep = [], [], []
+    t0 = time.perf_counter()
+    for j in range(n_inst):
+        d = synth.draw_step_device(spec, seed=spec["seed"] * 1000 + j, device=dev)
+        a, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
+                                       k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
+                                       comp_kv=d["comp_kv"], start_pos=spec["start_pos"],
+                                       ratio=spec["ratio"], index_topk=spec["index_topk"],
+                                       W=spec["W"], scale=spec["D"] ** -0.5)
+        insts.append(d)
+        argv.append(a)
+        keep.append((idx, out))
+    ws_bytes = L.lit_sparse_step_workspace_bytes(argv[0])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s; workspace {ws_bytes} B")
+
+    # -- warmup (eager), then one graph of n_inst steps ----------------------------------
+    for s in range(Wm):
+        L.lit_sparse_step(argv[s % n_inst], ws)
+    torch.cuda.synchronize()
+
+    def capture(calls):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    step_calls = [(lambda j=j: L.lit_sparse_step(argv[j], ws)) for j in range(n_inst)]
+    reps, rem = divmod(K, n_inst)
+    g_full = capture(step_calls) if reps else None
+    g_rem = capture(step_calls[:rem]) if rem else None
+    log(f"[bench] graphs captured (reps {reps}, remainder {rem})")
+
+    # -- timed region: exactly K steps ---------------------------------------------------
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record()
+    for _ in range(reps):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = 1e3 * t_total / K
+    queries = spec["B"] * spec["S"]
+    value = queries * K / t_total
+    log(f"[bench] {K} steps in {t_total * 1e3:.2f} ms wall ({gpu_ms:.2f} ms between events): "
+        f"{ms_per_step * 1e3:.2f} us/step")
+
+    # -- per-stage kernel durations: graphs of n_inst launches of one stage, timed by
+    # events on the same stream around their replays --------------------------------------
+    T = (spec["start_pos"] + spec["S"]) // spec["ratio"]
+    ld = (T + 3) // 4 * 4
+    keff = L.topk_width(spec["S"], spec["start_pos"], spec["ratio"], spec["index_topk"])
+    scores = [torch.empty((spec["B"], spec["S"], ld), dtype=torch.float32, device=dev)
+              for _ in range(n_inst)]
+    win = L.lit_window_indices(spec["B"], spec["S"], spec["start_pos"], spec["W"],
+                               insts[0]["R"])
+    stage_calls = {
+        "indexer": [(lambda j=j: L.lit_indexer_scores(
+            insts[j]["q8"], insts[j]["q_sc"], insts[j]["w"], insts[j]["k8"], insts[j]["k_sc"],
+            spec["start_pos"], spec["ratio"], scores=scores[j])) for j in range(n_inst)],
+        "topk": [(lambda j=j: L.lit_topk(scores[j], spec["start_pos"], spec["ratio"],
+                                         spec["index_topk"], idx=keep[j][0]))
+                 for j in range(n_inst)],
+        "attention": [(lambda j=j: L.lit_sparse_attn(
+            insts[j]["q"], insts[j]["win_kv"], win, insts[j]["comp_kv"], keep[j][0], None,
+            spec["D"] ** -0.5, out=keep[j][1], ws=ws)) for j in range(n_inst)],
+    }
+    stage_reps = max(1, min(20, 2000 // n_inst))
+    stages_us = {}
+    for name, calls in stage_calls.items():
+        g = capture(calls)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(stage_reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        stages_us[name] = e0.elapsed_time(e1) * 1e3 / (stage_reps * n_inst)
+        del g
+    log("[bench] stage means (us): " + ", ".join(f"{k} {v:.2f}" for k, v in stages_us.items()))
+
+    step_gbps = sb["step"] / (ms_per_step * 1e-3) / 1e9
+    dom = max(stages_us, key=stages_us.get)
+    kernels = {"indexer": ("indexer_scores_kernel", "indexer.hip"),
+               "topk": ("topk_kernel", "topk.hip"),
+               "attention": ("sparse_attn_kernel+attn_merge_kernel", "attention.hip")}
+    kname, ksrc = kernels[dom]
+    dom_us = stages_us[dom]
+    achieved = sb[dom] / (dom_us * 1e-6) / 1e9
+    src = os.path.join(ROOT, "lightning_indexer_top_amd", "csrc", ksrc)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_for(kname.split("+")[0], src),
+                "kernel": kname, "stage": dom, "bytes_per_launch": sb[dom],
+                "avg_launch_us": round(dom_us, 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, args.cpu_budget)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": K, "warmup": Wm, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3+bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": spec["B"], "query_tokens": spec["S"],
+                   "context": spec["start_pos"] + spec["S"], "compress_ratio": spec["ratio"],
+                   "window": spec["W"], "heads": spec["H"], "head_dim": spec["D"],
+                   "index_heads": spec["Hi"], "index_dim": spec["Di"],
+                   "index_topk": spec["index_topk"], "input_instances": n_inst,
+                   "timing": "HIP graph replay over rotating cold-cache instances"},
+        "hbm": {"step_bytes": sb["step"], "achieved_gbps": round(step_gbps, 1),
+                "peak_gbps": HBM_PEAK_GBPS, "frac": round(step_gbps / HBM_PEAK_GBPS, 4)},
+        "stages_us": {k: round(v, 3) for k, v in stages_us.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -188,6 +188,10 @@ typedef struct lit_step_args {
     /* outputs */
     int32_t *topk_idx; /* [B,S,k_eff]  (device) */
     uint16_t *out;     /* [B,S,H,dv] bf16        */
+    /* optional timing: hipEvent_t handles (each may be NULL) recorded on the stream
+     * before the indexer, after the indexer, after the top-k and after the
+     * attention, so a caller can time the stages without a profiler */
+    void *stage_events[4];
 } lit_step_args;
 
 lit_status lit_sparse_step(const lit_step_args *args, void *ws, size_t ws_bytes, void *stream);

@@ -215,27 +215,49 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a, At
     }
 }
 
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, AttnPlan pl) {
+// Split merge: one wave per (query, head).  Lane s holds split s's max and
+// normaliser (several splits per lane when there are more than 64); the wave reduces
+// them, leaves each split's weight e^(m_s - M) / L in LDS, and then every lane sums
+// its output dims over the splits with independent loads.
+constexpr int kMaxSplits = 1024;
+
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, AttnPlan pl) {
+    __shared__ float wgt[kMaxSplits];
     const int bs = blockIdx.x;
-    for (int e = threadIdx.x; e < kHeads * a.dv; e += 256) {
-        const int h = e / a.dv;
-        const int d = e - h * a.dv;
-        const float *src = a.part + ((size_t)bs * pl.n_splits * kHeads + h) * (a.dv + 2);
-        const size_t stride = (size_t)kHeads * (a.dv + 2);
-        float M = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-        for (int s = 0; s < pl.n_splits; ++s) M = fmaxf(M, src[s * stride + a.dv]);
-        float O = 0.f, L = 0.f;
-        if (M != -INFINITY) {
-            for (int s = 0; s < pl.n_splits; ++s) {
-                const float ms = src[s * stride + a.dv];
-                const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
-                O += f * src[s * stride + d];
-                L += f * src[s * stride + a.dv + 1];
-            }
-            if (a.sink) L += exp2f(a.sink[h] * kLog2e - M);
+    const int h = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int ns = pl.n_splits;
+    const size_t stride = (size_t)kHeads * (a.dv + 2);
+    const float *src = a.part + ((size_t)bs * ns * kHeads + h) * (a.dv + 2);
+    const float s2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+    float M = s2;
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, src[s * stride + a.dv]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float L = 0.f;
+    for (int s = lane; s < ns; s += 64) {
+        const float ms = src[s * stride + a.dv];
+        const float f = (ms == -INFINITY || M == -INFINITY) ? 0.f : exp2f(ms - M);
+        wgt[s] = f;
+        L += f * src[s * stride + a.dv + 1];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+    if (a.sink && M != -INFINITY) L += exp2f(s2 - M);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    __syncthreads();
+    for (int d = lane; d < a.dv; d += 64) {
+        float O = 0.f;
+        int s = 0;
+        for (; s + 8 <= ns; s += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = src[(s + u) * stride + d];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) O += wgt[s + u] * v[u];
         }
-        const float val = L > 0.f ? O / L : 0.f;
-        a.out[((size_t)bs * kHeads + h) * a.dv + d] = __builtin_bit_cast(uint16_t, (__bf16)val);
+        for (; s < ns; ++s) O += wgt[s] * src[s * stride + d];
+        a.out[((size_t)bs * kHeads + h) * a.dv + d] = __builtin_bit_cast(uint16_t, (__bf16)(O * inv));
     }
 }
 
@@ -255,7 +277,7 @@ hipError_t launch_d(const AttnArgs &a, const AttnPlan &p, hipStream_t stream) {
     hipLaunchKernelGGL(sparse_attn_kernel<D>, grid, dim3(kWaves * 64), 0, stream, a, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_splits == 1) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.B * a.S), dim3(256), 0, stream, a, p);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.B * a.S, kHeads), dim3(64), 0, stream, a, p);
     return hipGetLastError();
 }
 
@@ -270,6 +292,7 @@ AttnPlan plan_attention(int B, int S, int list_len) {
     int splits = (512 + queries - 1) / queries;
     const int max_splits = (tiles + kWaves - 1) / kWaves;
     if (splits > max_splits) splits = max_splits;
+    if (splits > kMaxSplits) splits = kMaxSplits;
     if (splits < 1) splits = 1;
     p.tiles_per_wave = (tiles + kWaves * splits - 1) / (kWaves * splits);
     if (p.tiles_per_wave < 1) p.tiles_per_wave = 1;

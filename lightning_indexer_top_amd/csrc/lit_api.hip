@@ -233,20 +233,27 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
     float *scores = (float *)ws;
     hipError_t e = hipSuccess;
+    auto mark = [&](int k) -> hipError_t {
+        return s->stage_events[k] ? hipEventRecord((hipEvent_t)s->stage_events[k], hs) : hipSuccess;
+    };
+    if ((e = mark(0)) != hipSuccess) return hip_status(e);
     if (keff > 0) {
         IndexerArgs ia{s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->B, s->S, s->Hi, s->Di, s->T_cap,
                        s->start_pos, s->ratio, T, scores, ld};
-        e = launch_indexer_scores(ia, hs);
-        if (e != hipSuccess) return hip_status(e);
-        TopkArgs ta{scores, ld, s->B, s->S, s->start_pos, s->ratio, T, keff, s->topk_idx};
-        e = launch_topk(ta, hs);
-        if (e != hipSuccess) return hip_status(e);
+        if ((e = launch_indexer_scores(ia, hs)) != hipSuccess) return hip_status(e);
     }
+    if ((e = mark(1)) != hipSuccess) return hip_status(e);
+    if (keff > 0) {
+        TopkArgs ta{scores, ld, s->B, s->S, s->start_pos, s->ratio, T, keff, s->topk_idx};
+        if ((e = launch_topk(ta, hs)) != hipSuccess) return hip_status(e);
+    }
+    if ((e = mark(2)) != hipSuccess) return hip_status(e);
     AttnArgs aa{s->q, s->B, s->S, s->H, s->D, s->dv, s->W > 0 ? s->win_kv : nullptr, s->R,
                 nullptr, s->W, s->start_pos, keff > 0 ? s->comp_kv : nullptr, s->T_cap,
                 keff > 0 ? s->topk_idx : nullptr, keff, s->sink, s->scale, s->out,
                 (float *)((char *)ws + scores_bytes)};
-    return hip_status(launch_sparse_attn(aa, plan, hs));
+    if ((e = launch_sparse_attn(aa, plan, hs)) != hipSuccess) return hip_status(e);
+    return hip_status(mark(3));
 }
 
 }  // extern "C"

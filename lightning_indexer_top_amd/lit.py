@@ -33,7 +33,7 @@ class lit_step_args(ctypes.Structure):
                 ("q8", _P), ("q_sc", _P), ("w", _P), ("k8", _P), ("k_sc", _P),
                 ("H", _I), ("D", _I), ("dv", _I), ("W", _I), ("R", _I),
                 ("q", _P), ("win_kv", _P), ("comp_kv", _P), ("sink", _P), ("scale", _F),
-                ("topk_idx", _P), ("out", _P)]
+                ("topk_idx", _P), ("out", _P), ("stage_events", _P * 4)]
 
 
 SIGNATURES = {
@@ -184,7 +184,7 @@ def lit_sparse_attn(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float, d
 
 def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int, ratio: int,
                    index_topk: int, W: int, scale: float, dv=None, sink=None, topk_idx=None,
-                   out=None) -> tuple:
+                   out=None, stage_events=None) -> tuple:
     """Build the lit_step_args struct (and allocate outputs the caller did not pass)."""
     B, S, Hi, Di = q8.shape
     H, D = q.shape[2], q.shape[3]
@@ -201,6 +201,10 @@ def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int,
                       win_kv=win_kv.data_ptr(), comp_kv=comp_kv.data_ptr(),
                       sink=0 if sink is None else sink.data_ptr(), scale=scale,
                       topk_idx=topk_idx.data_ptr(), out=out.data_ptr())
+    if stage_events is not None:
+        # hipEvent_t handles (e.g. torch.cuda.Event(...).cuda_event after one record)
+        for k, ev in enumerate(stage_events):
+            a.stage_events[k] = ev or None
     return a, topk_idx, out
 
 

@@ -177,3 +177,37 @@ def random_scores(B: int, S: int, T: int, seed: int, ties: bool = False) -> np.n
     if ties:
         return rng.integers(-4, 5, size=(B, S, T)).astype(np.float32)
     return rng.standard_normal((B, S, T), dtype=np.float32)
+
+
+def draw_step_device(spec: dict, seed: int, device="cuda") -> dict:
+    """The same recipe drawn directly on the GPU with torch's generator (for the bench's
+    rotating input instances, which only need the shapes and distributions, not the
+    host copies).  Returns device tensors keyed like StepInputs' arrays."""
+    B, S, start_pos, ratio = spec["B"], spec["S"], spec["start_pos"], spec["ratio"]
+    Hi, Di, H, D, W = spec["Hi"], spec["Di"], spec["H"], spec["D"], spec["W"]
+    T = (start_pos + S) // ratio
+    T_cap = max(T, 1)
+    R = max(1, S if start_pos == 0 else W + S - 1)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    f32 = dict(dtype=torch.float32, device=device, generator=g)
+    q8, q_sc = quantize_e4m3_ue8m0(torch.randn(B, S, Hi, Di, **f32))
+    w = torch.rand(B, S, Hi, **f32)
+    keys = spec.get("keys", "normal")
+    if keys == "mixture":
+        mu = torch.randn(64, Di, **f32)
+        z = torch.randint(0, 64, (B, T_cap), device=device, generator=g)
+        kf = mu[z] + 0.1 * torch.randn(B, T_cap, Di, **f32)
+    else:
+        kf = torch.randn(B, T_cap, Di, **f32)
+    k8, k_sc = quantize_e4m3_ue8m0(kf)
+    if keys == "boost":
+        n_boost = max(1, int(round(0.05 * T_cap)))
+        for b in range(B):
+            rows = torch.randperm(T_cap, device=device, generator=g)[:n_boost]
+            k_sc[b, rows] = (k_sc[b, rows].int() + 2).clamp(max=254).to(torch.uint8)
+    bf = torch.bfloat16
+    return dict(q8=q8.contiguous(), q_sc=q_sc.contiguous(), w=w, k8=k8.contiguous(),
+                k_sc=k_sc.contiguous(), q=torch.randn(B, S, H, D, **f32).to(bf),
+                win_kv=torch.randn(B, R, D, **f32).to(bf),
+                comp_kv=torch.randn(B, T_cap, D, **f32).to(bf), R=R, T_cap=T_cap)
