@@ -167,7 +167,27 @@ size_t lit_sparse_attn_workspace_bytes(int B, int S, int H, int dv, int W, int K
  * in-kernel from (start_pos, W, R).  [V4.1] Attention.forward with
  * _compress_topk_idxs; the -1 / position-order contract of the top-k list is
  * that of lit_topk.  Scores and attention partials live in the workspace.
+ *
+ * Decode-sized batches (B*S queries that fit the device's co-resident
+ * workgroups) run as ONE kernel: a team of workgroups per query scores, selects,
+ * gathers and merges, synchronising through counters in the workspace.  Larger
+ * batches (chunked prefill) run the indexer, top-k and attention kernels in turn.
+ * flags & LIT_STEP_UNFUSED forces the multi-kernel form.
+ *
+ * Workspace: lit_sparse_step_workspace_bytes() bytes of scratch, 256-byte
+ * aligned, contents irrelevant.
+ *
+ * State (fused form only): lit_sparse_step_state_bytes() bytes, 256-byte
+ * aligned, ZERO-FILLED ONCE before first use.  It holds the teams' counters and
+ * histograms, which every fused call leaves at zero again, so one state buffer
+ * can serve calls of any shape on one stream.  With state == NULL (or too
+ * small) the step uses the multi-kernel form.  State bytes [0, 4) are a sticky
+ * error word: nonzero means a fused call's team did not assemble within its
+ * bounded wait (its workgroups were not all resident, e.g. another kernel held
+ * compute units); that call's outputs are undefined.  Zero the state to clear
+ * it.  Calls that share a workspace or a state must be ordered on one stream.
  */
+#define LIT_STEP_UNFUSED 1
 typedef struct lit_step_args {
     /* positions */
     int B, S, start_pos, ratio;
@@ -192,10 +212,16 @@ typedef struct lit_step_args {
      * before the indexer, after the indexer, after the top-k and after the
      * attention, so a caller can time the stages without a profiler */
     void *stage_events[4];
+    /* fused-form state (see above); NULL selects the multi-kernel form */
+    void *state;
+    size_t state_bytes;
+    int flags; /* LIT_STEP_* bits */
 } lit_step_args;
 
 lit_status lit_sparse_step(const lit_step_args *args, void *ws, size_t ws_bytes, void *stream);
 size_t lit_sparse_step_workspace_bytes(const lit_step_args *args);
+/* State bytes the fused form needs for these sizes (0 when it does not apply). */
+size_t lit_sparse_step_state_bytes(const lit_step_args *args);
 
 #ifdef __cplusplus
 }

@@ -7,4 +7,6 @@ The kernels live in ``liblit.so`` (hand-written HIP for gfx950, C ABI in
 from .lit import (LitError, library, lit_indexer_scores, lit_sparse_attn,  # noqa: F401
                   lit_sparse_attn_workspace_bytes, lit_sparse_step,
                   lit_sparse_step_workspace_bytes, lit_step_args, lit_topk,
-                  lit_window_indices, lit_window_width, make_step_args, topk_width)
+                  lit_window_indices, lit_window_width, make_step_args, step_workspace,
+                  topk_width, LIT_STEP_UNFUSED, attach_state,
+                  lit_sparse_step_state_bytes, state_error)

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build", "lit")
 LIB = os.path.join(HERE, "liblit.so")
-SOURCES = ["lit_api.hip", "indexer.hip", "topk.hip", "attention.hip"]
+SOURCES = ["lit_api.hip", "indexer.hip", "topk.hip", "attention.hip", "fused_decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

@@ -22,7 +22,7 @@
 // A query's list is cut into splits (workgroups of 4 waves); the 4 waves of a split
 // merge through LDS, and a second kernel merges splits (log-sum-exp), adds the sink
 // and writes bf16.  With a single split the first kernel writes bf16 itself.
-#include "lit_internal.h"
+#include "tile_ops.h"
 
 namespace lit {
 
@@ -30,8 +30,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kHeads = 16;
-
-__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ inline const uint16_t *list_row(const AttnArgs &a, int b, int i, int nwin, int p) {
     const size_t bs = (size_t)b * a.S + i;
@@ -48,8 +46,6 @@ __device__ inline const uint16_t *list_row(const AttnArgs &a, int b, int i, int 
 
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a, AttnPlan pl) {
-    constexpr int KS = D / 32;      // 32-dim MFMA steps of the logit contraction
-    constexpr int NT = D / 16;      // 16-dim output tiles (dv <= D)
     constexpr int LD = D + 4;       // LDS row stride in bf16 (8 bytes of padding)
     __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * 32 * LD];
     __shared__ float wm[kWaves][kHeads], wl[kWaves][kHeads];
@@ -67,20 +63,10 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a, At
     const int ndt = a.dv / 16;
     const float sl2 = a.scale * kLog2e;
 
-    // Q^T operands: lane (g, c) holds head c, dims 32s+8g .. 32s+8g+7.
-    bf16x8 qb[KS];
-    {
-        const uint16_t *qrow = a.q + ((size_t)bs * kHeads + c) * D;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            qb[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qrow + 32 * s + 8 * g));
-    }
-
-    float m_run = -INFINITY;  // running max of log2-domain logits, head c
-    float l_run = 0.f;        // this lane's share of the running normaliser
-    f32x4 o[NT];
-#pragma unroll
-    for (int dt = 0; dt < NT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 qb[D / 32];
+    load_q_operands<D>(qb, a.q, (size_t)bs, g, c);
+    AttnState<D> st;
+    attn_init<D>(st);
 
     uint16_t *tile = lds + wave * 32 * LD;
     const int split_begin = split * kWaves * pl.tiles_per_wave * 32;
@@ -88,122 +74,27 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a, At
 
     for (int it = 0; it < pl.tiles_per_wave; ++it) {
         const int base = split_begin + (wave * pl.tiles_per_wave + it) * 32;
-        f32x4 sc[2];
-        uint64_t valid_mask[2];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int p = base + 16 * half + c;
-            const uint16_t *rp = p < split_end ? list_row(a, b, i, nwin, p) : nullptr;
-            valid_mask[half] = __ballot(rp != nullptr);
-            u32x4 kr[KS];
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                kr[s] = rp ? *reinterpret_cast<const u32x4 *>(rp + 32 * s + 8 * g)
-                           : u32x4{0u, 0u, 0u, 0u};
-            sc[half] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                sc[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[s]), qb[s], sc[half], 0, 0, 0);
-            uint16_t *dst = tile + (16 * half + c) * LD + 8 * g;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                *reinterpret_cast<u32x2 *>(dst + 32 * s) = u32x2{kr[s][0], kr[s][1]};
-                *reinterpret_cast<u32x2 *>(dst + 32 * s + 4) = u32x2{kr[s][2], kr[s][3]};
-            }
-        }
-
-        // Logits of head c for rows 4g+r (half 0) and 16+4g+r (half 1).
-        float x[8];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool v = (valid_mask[half] >> (4 * g + r)) & 1ull;
-                const float val = v ? sc[half][r] * sl2 : -INFINITY;
-                x[4 * half + r] = val;
-                tmax = fmaxf(tmax, val);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
-        bf16x8 pb;
-        float psum = 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float pk = x[k] == -INFINITY ? 0.f : exp2f(x[k] - m_new);
-            psum += pk;
-            pb[k] = (__bf16)pk;
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt) o[dt] *= alpha;
-
-        __syncthreads();  // this wave's rows are in LDS
-        // V^T operand: lane (g, c) reads column 16dt+c of rows 4g..4g+3, 16+4g..16+4g+3.
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt) {
-            if (dt < ndt) {
-                bf16x8 va;
-                const uint16_t *col = tile + 16 * dt + c;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    va[m] = __builtin_bit_cast(__bf16, col[(4 * g + m) * LD]);
-                    va[4 + m] = __builtin_bit_cast(__bf16, col[(16 + 4 * g + m) * LD]);
-                }
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[dt], 0, 0, 0);
-            }
-        }
-        __syncthreads();  // LDS tile free for the next rows
+        if (base >= split_end) break;
+        const int p0 = base + c, p1 = base + 16 + c;
+        AttnRows<D> rows;
+        attn_tile_load<D>(rows, p0 < split_end ? list_row(a, b, i, nwin, p0) : nullptr,
+                          p1 < split_end ? list_row(a, b, i, nwin, p1) : nullptr, g);
+        attn_tile_compute<D>(st, qb, rows, tile, ndt, sl2, g, c);
     }
-
-    // Wave totals for head c.
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (g == 0) {
-        wm[wave][c] = m_run;
-        wl[wave][c] = l_run;
-    }
-    // Reuse the tile buffer for the 4 waves' O (float, [wave][head][dv]).
+    __syncthreads();  // every wave is done with its LDS rows
+    // Reuse the row buffer for the 4 waves' states.
     float *ow = reinterpret_cast<float *>(lds);
-#pragma unroll
-    for (int dt = 0; dt < NT; ++dt)
-        if (dt < ndt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                ow[(wave * kHeads + c) * a.dv + 16 * dt + 4 * g + r] = o[dt][r];
+    attn_wave_publish<D>(st, ow, &wm[0][0], &wl[0][0], wave, a.dv, g, c);
     __syncthreads();
 
     const bool direct = pl.n_splits == 1;
     for (int e = threadIdx.x; e < kHeads * a.dv; e += kWaves * 64) {
         const int h = e / a.dv;
         const int d = e - h * a.dv;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][h]);
-        float O = 0.f, L = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float f = wm[w][h] == -INFINITY ? 0.f : exp2f(wm[w][h] - M);
-                O += f * ow[(w * kHeads + h) * a.dv + d];
-                L += f * wl[w][h];
-            }
-        }
+        float O, M, L;
+        attn_combine(ow, &wm[0][0], &wl[0][0], kWaves, h, d, a.dv, O, M, L);
         if (direct) {
-            if (a.sink) {
-                const float s2 = a.sink[h] * kLog2e;
-                const float M2 = fmaxf(M, s2);
-                if (M2 != -INFINITY) {
-                    const float f = M == -INFINITY ? 0.f : exp2f(M - M2);
-                    O *= f;
-                    L = L * f + exp2f(s2 - M2);
-                }
-            }
-            const float val = L > 0.f ? O / L : 0.f;
-            a.out[((size_t)bs * kHeads + h) * a.dv + d] = __builtin_bit_cast(uint16_t, (__bf16)val);
+            a.out[((size_t)bs * kHeads + h) * a.dv + d] = attn_finish(O, M, L, a.sink, h);
         } else {
             float *dst = a.part + (((size_t)bs * pl.n_splits + split) * kHeads + h) * (a.dv + 2);
             dst[d] = O;

@@ -23,7 +23,7 @@
 // fp32 scores.  Query heads stay in VGPRs.  For several queries per sequence
 // (chunked prefill) a wave scores QG queries against the same keys, so the keys are
 // read once per QG queries.
-#include "lit_internal.h"
+#include "tile_ops.h"
 
 namespace lit {
 
@@ -32,20 +32,8 @@ namespace {
 constexpr int kWaves = 4;  // waves per workgroup
 constexpr int kU = 4;      // 16-key tiles per wave
 
-__device__ inline i32x8 load_operand(const uint8_t *row, int g, bool wide) {
-    const u32x4 lo = *reinterpret_cast<const u32x4 *>(row + 16 * g);
-    u32x4 hi = {0u, 0u, 0u, 0u};
-    if (wide) hi = *reinterpret_cast<const u32x4 *>(row + 64 + 16 * g);
-    i32x8 v;
-    v[0] = (int)lo[0]; v[1] = (int)lo[1]; v[2] = (int)lo[2]; v[3] = (int)lo[3];
-    v[4] = (int)hi[0]; v[5] = (int)hi[1]; v[6] = (int)hi[2]; v[7] = (int)hi[3];
-    return v;
-}
-
 template <int DI, int HT, int QG>
 __global__ __launch_bounds__(kWaves * 64) void indexer_scores_kernel(IndexerArgs a) {
-    constexpr int NB = DI / 32;       // scale bytes per row
-    constexpr bool WIDE = DI == 128;  // uses the high K half
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;
@@ -76,39 +64,16 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_kernel(IndexerArgs
     }
 
     // Keys first: they are the long-latency stream.
-    i32x8 kb[kU];
-    int ks[kU];
+    IdxKeys kb[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        const int t = min(t0 + 16 * u + c, a.T - 1);
-        const size_t row = (size_t)b * a.T_cap + t;
-        kb[u] = load_operand(a.k8 + row * DI, g, WIDE);
-        ks[u] = g < NB ? (int)a.k_sc[row * NB + g] : 127;
-    }
+    for (int u = 0; u < kU; ++u)
+        kb[u] = load_idx_keys<DI>(a, (size_t)b * a.T_cap + min(t0 + 16 * u + c, a.T - 1), g);
 
-    // Query heads of the group, with their scales and head weights.
-    i32x8 qa[QG][HT];
-    int qs[QG][HT];
-    float wr[QG][HT][4];
+    IdxQuery<DI, HT> qs[QG];
 #pragma unroll
     for (int qq = 0; qq < QG; ++qq) {
         const int i = i0 + qq;
-        const bool valid = i < a.S;
-        const size_t qi = bs0 + (valid ? i : 0);
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            const size_t head = qi * a.Hi + 16 * ht + c;
-            if (valid) {
-                qa[qq][ht] = load_operand(a.q8 + head * DI, g, WIDE);
-                qs[qq][ht] = g < NB ? (int)a.q_sc[head * NB + g] : 127;
-            } else {
-                qa[qq][ht] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-                qs[qq][ht] = 127;
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                wr[qq][ht][r] = valid ? a.w[qi * a.Hi + 16 * ht + 4 * g + r] : 0.f;
-        }
+        load_idx_query<DI, HT>(qs[qq], a, bs0 + (i < a.S ? i : 0), i < a.S, g, c);
     }
 
 #pragma unroll
@@ -116,21 +81,11 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_kernel(IndexerArgs
         const int t = t0 + 16 * u + c;
 #pragma unroll
         for (int qq = 0; qq < QG; ++qq) {
-            float part = 0.f;
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    qa[qq][ht], kb[u], acc, 0 /*A e4m3*/, 0 /*B e4m3*/, 0, qs[qq][ht], 0, ks[u]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) part += wr[qq][ht][r] * fmaxf(acc[r], 0.f);
-            }
-            part += __shfl_xor(part, 16);
-            part += __shfl_xor(part, 32);
+            const float s = idx_tile_score<DI, HT>(qs[qq], kb[u]);
             const int i = i0 + qq;
             if (g == 0 && i < a.S && t < a.T) {
                 const int vis = (a.start_pos + i + 1) / a.ratio;
-                a.scores[(bs0 + i) * a.ld + t] = t < vis ? part : -INFINITY;
+                a.scores[(bs0 + i) * a.ld + t] = t < vis ? s : -INFINITY;
             }
         }
     }

@@ -178,7 +178,7 @@ lit_status lit_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv
     return hip_status(launch_sparse_attn(a, p, (hipStream_t)stream));
 }
 
-// Workspace of the fused step: scores [B*S, ld] fp32, then the attention partials.
+// Workspace of the multi-kernel step: scores [B*S, ld] fp32, then the attention partials.
 static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld, AttnPlan *plan) {
     const long T = ((long)s->start_pos + s->S) / s->ratio;
     *ld = (long)round_up((size_t)(T > 0 ? T : 1), 4);
@@ -187,6 +187,14 @@ static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
     *plan = plan_attention(s->B, s->S, nwin + keff);
     return *scores_bytes + round_up(attention_partial_bytes(s->B, s->S, s->H, s->dv, *plan), 256);
+}
+
+static FusedPlan step_fused_plan(const lit_step_args *s) {
+    FusedPlan p{};
+    p.ok = false;
+    if (s->flags & LIT_STEP_UNFUSED) return p;
+    const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
+    return plan_fused(s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D, s->dv, s->W, keff);
 }
 
 static lit_status check_step(const lit_step_args *s) {
@@ -215,7 +223,19 @@ size_t lit_sparse_step_workspace_bytes(const lit_step_args *s) {
     size_t sb;
     long ld;
     AttnPlan p;
-    return step_layout(s, &sb, &ld, &p);
+    size_t need = step_layout(s, &sb, &ld, &p);
+    const FusedPlan fp = step_fused_plan(s);
+    if (fp.ok) {
+        const size_t fused = fused_ws_bytes(fp, s->dv);
+        if (fused > need) need = fused;
+    }
+    return need;
+}
+
+size_t lit_sparse_step_state_bytes(const lit_step_args *s) {
+    if (check_step(s) != LIT_OK) return 0;
+    const FusedPlan fp = step_fused_plan(s);
+    return fp.ok ? fused_state_bytes(fp) : 0;
 }
 
 lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, void *stream) {
@@ -237,6 +257,24 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
         return s->stage_events[k] ? hipEventRecord((hipEvent_t)s->stage_events[k], hs) : hipSuccess;
     };
     if ((e = mark(0)) != hipSuccess) return hip_status(e);
+    const FusedPlan fp = step_fused_plan(s);
+    if (fp.ok && s->state && s->state_bytes >= fused_state_bytes(fp)) {
+        if (((uintptr_t)s->state & 255u) != 0) return LIT_E_ALIGN;
+        if (ws_bytes < fused_ws_bytes(fp, s->dv)) return LIT_E_WORKSPACE;
+        FusedArgs f{};
+        f.ia = IndexerArgs{s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->B, s->S, s->Hi, s->Di, s->T_cap,
+                           s->start_pos, s->ratio, T, nullptr, 0};
+        f.aa = AttnArgs{s->q, s->B, s->S, s->H, s->D, s->dv, s->W > 0 ? s->win_kv : nullptr, s->R,
+                        nullptr, s->W, s->start_pos, s->comp_kv, s->T_cap, nullptr, keff, s->sink,
+                        s->scale, s->out, nullptr};
+        f.topk_out = s->topk_idx;
+        f.keff = keff;
+        f.spin_limit = 1u << 22;
+        if ((e = launch_fused(f, fp, ws, s->state, hs)) != hipSuccess) return hip_status(e);
+        for (int k = 1; k < 4; ++k)
+            if ((e = mark(k)) != hipSuccess) return hip_status(e);
+        return LIT_OK;
+    }
     if (keff > 0) {
         IndexerArgs ia{s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->B, s->S, s->Hi, s->Di, s->T_cap,
                        s->start_pos, s->ratio, T, scores, ld};

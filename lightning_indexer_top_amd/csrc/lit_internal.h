@@ -100,4 +100,32 @@ __host__ __device__ inline int window_slot(int S, int start_pos, int W, int R, i
     return valid ? (int)(p % R) : -1;
 }
 
+
+// ---------------------------------------------------------------------------
+// Fused decode step (fused_decode.hip)
+// ---------------------------------------------------------------------------
+struct FusedArgs {
+    IndexerArgs ia;       // scores / ld unused
+    AttnArgs aa;          // win_idx unused (window derived), comp_idx unused, part unused
+    int32_t *topk_out;    // [B,S,keff] output
+    int keff;
+    int team_size, chunk, win_tiles, n_slots;
+    long ld;              // team score array stride
+    uint32_t spin_limit;
+    uint32_t *err, *ctrl;         // zero between launches
+    float *scores;                // per team: scores of the visible rows
+    float *part;                  // per member: partial attention state
+    int slot_floats;              // floats per member state
+};
+struct FusedPlan {
+    bool ok;
+    int n_teams, team_size, chunk, win_tiles, n_slots, grid;
+    long ld;
+    size_t dyn_bytes;
+};
+FusedPlan plan_fused(int B, int S, int start_pos, int ratio, int Hi, int Di, int D, int dv, int W, int keff);
+size_t fused_state_bytes(const FusedPlan &p);  // zero between launches
+size_t fused_ws_bytes(const FusedPlan &p, int dv);
+hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream);
+
 }  // namespace lit

@@ -1,0 +1,313 @@
+// tile_ops.h -- wave-level building blocks shared by the standalone kernels and the
+// fused decode kernel: the MX-scaled fp8 indexer tile, the 32-row gather-attention
+// tile with its online softmax, and workgroup scans.
+#pragma once
+
+#include "lit_internal.h"
+
+namespace lit {
+
+// Orders this wave's earlier LDS writes before its later LDS reads (the lanes of a wave
+// exchange data through a wave-private LDS region; no workgroup barrier is involved).
+__device__ inline void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// ---------------------------------------------------------------------------
+// Indexer tile (V_MFMA_SCALE_F32_16X16X128_F8F6F4).
+//
+// Operand layout measured on gfx950: lane l = 16g + c holds row/column c; its bytes
+// 0-15 are K = 16g..16g+15, bytes 16-31 are K = 64+16g..64+16g+15, and the scale byte
+// lane group g supplies covers K block 32g..32g+31.  A lane therefore loads row bytes
+// [16g, 16g+16) and [64+16g, 64+16g+16) and the scale of block g: memory order is K
+// order.  A 64-dim row uses only the low half (K 0..63).  C comes back as lane (g, c),
+// register r = A row 4g+r, B column c.
+// ---------------------------------------------------------------------------
+__device__ inline i32x8 mx_operand(const uint8_t *row, int g, bool wide) {
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(row + 16 * g);
+    u32x4 hi = {0u, 0u, 0u, 0u};
+    if (wide) hi = *reinterpret_cast<const u32x4 *>(row + 64 + 16 * g);
+    i32x8 v;
+    v[0] = (int)lo[0]; v[1] = (int)lo[1]; v[2] = (int)lo[2]; v[3] = (int)lo[3];
+    v[4] = (int)hi[0]; v[5] = (int)hi[1]; v[6] = (int)hi[2]; v[7] = (int)hi[3];
+    return v;
+}
+
+// One query's index heads as MFMA A operands: HT tiles of 16 heads, their scale bytes,
+// and the head weights of the 4 C rows each lane receives.
+template <int DI, int HT>
+struct IdxQuery {
+    i32x8 a[HT];
+    int s[HT];
+    float w[HT][4];
+};
+
+template <int DI, int HT>
+__device__ inline void load_idx_query(IdxQuery<DI, HT> &q, const IndexerArgs &a, size_t qi, bool valid,
+                                      int g, int c) {
+    constexpr int NB = DI / 32;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const size_t head = qi * a.Hi + 16 * ht + c;
+        if (valid) {
+            q.a[ht] = mx_operand(a.q8 + head * DI, g, DI == 128);
+            q.s[ht] = g < NB ? (int)a.q_sc[head * NB + g] : 127;
+        } else {
+            q.a[ht] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+            q.s[ht] = 127;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) q.w[ht][r] = valid ? a.w[qi * a.Hi + 16 * ht + 4 * g + r] : 0.f;
+    }
+}
+
+// Keys of one 16-key tile as MFMA B operands (key c of the tile per lane column).
+struct IdxKeys {
+    i32x8 b;
+    int s;
+};
+
+template <int DI>
+__device__ inline IdxKeys load_idx_keys(const IndexerArgs &a, size_t row, int g) {
+    constexpr int NB = DI / 32;
+    IdxKeys k;
+    k.b = mx_operand(a.k8 + row * DI, g, DI == 128);
+    k.s = g < NB ? (int)a.k_sc[row * NB + g] : 127;
+    return k;
+}
+
+// Score of key c of the tile for one query (every lane of the wave returns the score
+// of its column c): sum over heads of w_h * relu(q_h . k_c).
+template <int DI, int HT>
+__device__ inline float idx_tile_score(const IdxQuery<DI, HT> &q, const IdxKeys &k) {
+    float part = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[ht], k.b, acc, 0 /*A e4m3*/,
+                                                              0 /*B e4m3*/, 0, q.s[ht], 0, k.s);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part += q.w[ht][r] * fmaxf(acc[r], 0.f);
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    return part;
+}
+
+// ---------------------------------------------------------------------------
+// Gather-attention tile (V_MFMA_F32_16X16X32_BF16), 16 heads.
+//
+// Logits: A = 16 gathered rows (lane (g, c): row c, dims 32s+8g..+7), B = Q^T (lane
+// (g, c): head c, same dims) -> lane (g, h) holds head h's logits for rows 4g+r.  Two
+// such halves give rows 4g..4g+3 and 16+4g..16+4g+3, which as bf16 are the B operand
+// (P^T, k-slots in that row order) of O^T = V^T P^T; V^T comes from an LDS copy of
+// the rows read column-wise with the same row order.  O^T lands as lane (g, h),
+// register r = dim 16dt+4g+r of head h: every lane owns one head throughout.
+// ---------------------------------------------------------------------------
+template <int D>
+struct AttnState {
+    float m;  // running max of log2-domain logits of head c
+    float l;  // this lane's share of the running normaliser
+    f32x4 o[D / 16];
+};
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <int D>
+__device__ inline void attn_init(AttnState<D> &st) {
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int D>
+__device__ inline void load_q_operands(bf16x8 (&qb)[D / 32], const uint16_t *q, size_t bs, int g, int c) {
+    const uint16_t *qrow = q + (bs * 16 + c) * D;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+        qb[s] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qrow + 32 * s + 8 * g));
+}
+
+// Loads of one tile's rows (issued early, consumed by attn_tile_compute).
+template <int D>
+struct AttnRows {
+    u32x4 r[2][D / 32];
+    uint64_t valid[2];
+};
+
+template <int D>
+__device__ inline void attn_tile_load(AttnRows<D> &t, const uint16_t *rp0, const uint16_t *rp1, int g) {
+    t.valid[0] = __ballot(rp0 != nullptr);
+    t.valid[1] = __ballot(rp1 != nullptr);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+        t.r[0][s] = rp0 ? *reinterpret_cast<const u32x4 *>(rp0 + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+        t.r[1][s] = rp1 ? *reinterpret_cast<const u32x4 *>(rp1 + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// One 32-row tile: logits, online softmax, P.V.  `tile` is this wave's LDS region of
+// 32 rows x (D+4) bf16.  ndt = dv/16 output tiles are accumulated.
+template <int D>
+__device__ inline void attn_tile_compute(AttnState<D> &st, const bf16x8 (&qb)[D / 32], const AttnRows<D> &t,
+                                         uint16_t *tile, int ndt, float sl2, int g, int c) {
+    constexpr int KS = D / 32;
+    constexpr int NT = D / 16;
+    constexpr int LD = D + 4;
+    f32x4 sc[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        sc[half] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            sc[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.r[half][s]), qb[s], sc[half], 0, 0, 0);
+        uint16_t *dst = tile + (16 * half + c) * LD + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            *reinterpret_cast<u32x2 *>(dst + 32 * s) = u32x2{t.r[half][s][0], t.r[half][s][1]};
+            *reinterpret_cast<u32x2 *>(dst + 32 * s + 4) = u32x2{t.r[half][s][2], t.r[half][s][3]};
+        }
+    }
+    float x[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool v = (t.valid[half] >> (4 * g + r)) & 1ull;
+            const float val = v ? sc[half][r] * sl2 : -INFINITY;
+            x[4 * half + r] = val;
+            tmax = fmaxf(tmax, val);
+        }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(st.m, tmax);
+    const float alpha = st.m == -INFINITY ? 0.f : exp2f(st.m - m_new);
+    bf16x8 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float pk = x[k] == -INFINITY ? 0.f : exp2f(x[k] - m_new);
+        psum += pk;
+        pb[k] = (__bf16)pk;
+    }
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) st.o[dt] *= alpha;
+
+    wave_lds_sync();  // the rows this wave wrote are readable by its other lanes
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+        if (dt < ndt) {
+            bf16x8 va;
+            const uint16_t *col = tile + 16 * dt + c;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                va[m] = __builtin_bit_cast(__bf16, col[(4 * g + m) * LD]);
+                va[4 + m] = __builtin_bit_cast(__bf16, col[(16 + 4 * g + m) * LD]);
+            }
+            st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.o[dt], 0, 0, 0);
+        }
+    }
+    wave_lds_sync();  // reads done before the next tile overwrites the region
+}
+
+// Finish a wave: the normaliser summed over the wave (m is already uniform per head).
+template <int D>
+__device__ inline void attn_wave_total(AttnState<D> &st) {
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+}
+
+// A wave's finished state into LDS: ow [nwaves][16][dv] floats, wm / wl [nwaves][16].
+template <int D>
+__device__ inline void attn_wave_publish(AttnState<D> &st, float *ow, float *wm, float *wl, int wave,
+                                         int dv, int g, int c) {
+    attn_wave_total<D>(st);
+    if (g == 0) {
+        wm[wave * 16 + c] = st.m;
+        wl[wave * 16 + c] = st.l;
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        if (16 * dt < dv)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ow[(wave * 16 + c) * dv + 16 * dt + 4 * g + r] = st.o[dt][r];
+}
+
+// Log-sum-exp combination of `n` published states for head h, dim d: unnormalised O,
+// the common max M (log2 domain) and the normaliser L at that max.
+__device__ inline void attn_combine(const float *ow, const float *wm, const float *wl, int n, int h, int d,
+                                    int dv, float &O, float &M, float &L) {
+    M = -INFINITY;
+    for (int w = 0; w < n; ++w) M = fmaxf(M, wm[w * 16 + h]);
+    O = 0.f;
+    L = 0.f;
+    if (M == -INFINITY) return;
+    for (int w = 0; w < n; ++w) {
+        const float mw = wm[w * 16 + h];
+        const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+        O += f * ow[(w * 16 + h) * dv + d];
+        L += f * wl[w * 16 + h];
+    }
+}
+
+// Final normalisation with an optional sink logit (natural-log units), bf16 bits out.
+__device__ inline uint16_t attn_finish(float O, float M, float L, const float *sink, int h) {
+    if (sink) {
+        const float s2 = sink[h] * kLog2e;
+        const float M2 = fmaxf(M, s2);
+        if (M2 != -INFINITY) {
+            const float f = M == -INFINITY ? 0.f : exp2f(M - M2);
+            O *= f;
+            L = L * f + exp2f(s2 - M2);
+        }
+    }
+    const float val = L > 0.f ? O / L : 0.f;
+    return __builtin_bit_cast(uint16_t, (__bf16)val);
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup scans (inclusive, ascending thread id); *total gets the sum.  Every thread
+// of the workgroup must call them.  wsum needs blockDim.x / 64 entries.
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t wg_scan(uint32_t v, uint32_t *wsum, uint32_t *total) {
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+    }
+    if (lane == 63) wsum[wid] = v;
+    __syncthreads();
+    if (wid == 0) {
+        uint32_t s = lane < nw ? wsum[lane] : 0u;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t t = __shfl_up(s, off);
+            if (lane >= off) s += t;
+        }
+        if (lane < nw) wsum[lane] = s;
+    }
+    __syncthreads();
+    if (wid > 0) v += wsum[wid - 1];
+    *total = wsum[nw - 1];
+    __syncthreads();
+    return v;
+}
+
+// Order-preserving 32-bit key of a float: a larger float gives a larger key; -0 ranks
+// as +0.
+__device__ inline uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace lit

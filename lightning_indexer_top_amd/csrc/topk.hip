@@ -15,46 +15,13 @@
 // threshold and keys equal to it; one packed block scan turns those counts into
 // output offsets, so each selected position lands in its ascending slot with no sort.
 // Rows longer than 1024*ITEMS are processed in segments re-read from L2.
-#include "lit_internal.h"
+#include "tile_ops.h"
 
 namespace lit {
 
 namespace {
 
 constexpr int kThreads = 1024;
-
-__device__ inline uint32_t order_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0u;  // -0 ranks as +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Inclusive scan over the workgroup (ascending thread id); *total gets the sum.
-__device__ inline uint32_t block_scan(uint32_t v, uint32_t *wsum, uint32_t *total) {
-    const int lane = threadIdx.x & 63;
-    const int wid = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = __shfl_up(v, off);
-        if (lane >= off) v += t;
-    }
-    if (lane == 63) wsum[wid] = v;
-    __syncthreads();
-    if (wid == 0) {
-        uint32_t s = lane < kThreads / 64 ? wsum[lane] : 0u;
-#pragma unroll
-        for (int off = 1; off < kThreads / 64; off <<= 1) {
-            const uint32_t t = __shfl_up(s, off);
-            if (lane >= off) s += t;
-        }
-        if (lane < kThreads / 64) wsum[lane] = s;
-    }
-    __syncthreads();
-    if (wid > 0) v += wsum[wid - 1];
-    *total = wsum[kThreads / 64 - 1];
-    __syncthreads();
-    return v;
-}
 
 template <int ITEMS>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
@@ -125,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
             c_lo = hist[hi - 1];
         }
         uint32_t total;
-        const uint32_t incl = block_scan((uint32_t)(c_hi + c_lo), wsum, &total);
+        const uint32_t incl = wg_scan((uint32_t)(c_hi + c_lo), wsum, &total);
         const int above = (int)incl - c_hi - c_lo;
         if (hi >= 1) {
             if (above < remaining && remaining <= above + c_hi) {
@@ -159,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         }
         const uint32_t packed = (ngt << 16) | neq;
         uint32_t total;
-        const uint32_t excl = block_scan(packed, wsum, &total) - packed;
+        const uint32_t excl = wg_scan(packed, wsum, &total) - packed;
         int gt = base_gt + (int)(excl >> 16);
         int eq = base_eq + (int)(excl & 0xffffu);
         const int pos0 = seg * SEG + tid * ITEMS;

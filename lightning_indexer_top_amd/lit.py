@@ -33,7 +33,11 @@ class lit_step_args(ctypes.Structure):
                 ("q8", _P), ("q_sc", _P), ("w", _P), ("k8", _P), ("k_sc", _P),
                 ("H", _I), ("D", _I), ("dv", _I), ("W", _I), ("R", _I),
                 ("q", _P), ("win_kv", _P), ("comp_kv", _P), ("sink", _P), ("scale", _F),
-                ("topk_idx", _P), ("out", _P), ("stage_events", _P * 4)]
+                ("topk_idx", _P), ("out", _P), ("stage_events", _P * 4), ("state", _P), ("state_bytes", _Z),
+                ("flags", _I)]
+
+
+LIT_STEP_UNFUSED = 1
 
 
 SIGNATURES = {
@@ -49,6 +53,7 @@ SIGNATURES = {
     "lit_sparse_attn_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
     "lit_sparse_step": (_I, [ctypes.POINTER(lit_step_args), _P, _Z, _P]),
     "lit_sparse_step_workspace_bytes": (_Z, [ctypes.POINTER(lit_step_args)]),
+    "lit_sparse_step_state_bytes": (_Z, [ctypes.POINTER(lit_step_args)]),
 }
 
 
@@ -184,7 +189,7 @@ def lit_sparse_attn(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float, d
 
 def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int, ratio: int,
                    index_topk: int, W: int, scale: float, dv=None, sink=None, topk_idx=None,
-                   out=None, stage_events=None) -> tuple:
+                   out=None, stage_events=None, flags: int = 0) -> tuple:
     """Build the lit_step_args struct (and allocate outputs the caller did not pass)."""
     B, S, Hi, Di = q8.shape
     H, D = q.shape[2], q.shape[3]
@@ -200,7 +205,7 @@ def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int,
                       H=H, D=D, dv=dv, W=W, R=win_kv.shape[1], q=q.data_ptr(),
                       win_kv=win_kv.data_ptr(), comp_kv=comp_kv.data_ptr(),
                       sink=0 if sink is None else sink.data_ptr(), scale=scale,
-                      topk_idx=topk_idx.data_ptr(), out=out.data_ptr())
+                      topk_idx=topk_idx.data_ptr(), out=out.data_ptr(), flags=flags)
     if stage_events is not None:
         # hipEvent_t handles (e.g. torch.cuda.Event(...).cuda_event after one record)
         for k, ev in enumerate(stage_events):
@@ -210,6 +215,35 @@ def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int,
 
 def lit_sparse_step_workspace_bytes(args: lit_step_args) -> int:
     return library().lit_sparse_step_workspace_bytes(ctypes.byref(args))
+
+
+def step_workspace(args: lit_step_args, device="cuda") -> torch.Tensor:
+    """Scratch workspace of the size the step needs."""
+    return torch.empty(max(256, lit_sparse_step_workspace_bytes(args)), dtype=torch.uint8,
+                       device=device)
+
+
+def lit_sparse_step_state_bytes(args: lit_step_args) -> int:
+    return library().lit_sparse_step_state_bytes(ctypes.byref(args))
+
+
+def attach_state(args: lit_step_args, state: Optional[torch.Tensor] = None, device="cuda"):
+    """Give the step a zero-filled fused-form state (allocated when not passed); returns
+    it, or None when the fused form does not apply to these sizes."""
+    need = lit_sparse_step_state_bytes(args)
+    if need == 0:
+        args.state, args.state_bytes = None, 0
+        return None
+    if state is None:
+        state = torch.zeros(need, dtype=torch.uint8, device=device)
+    args.state = state.data_ptr()
+    args.state_bytes = state.numel() * state.element_size()
+    return state
+
+
+def state_error(state: Optional[torch.Tensor]) -> int:
+    """The sticky error word of a fused-form state (0 = no team timed out)."""
+    return 0 if state is None else int(state[:4].view(torch.int32).item())
 
 
 def lit_sparse_step(args: lit_step_args, ws: torch.Tensor, stream=None) -> None:

@@ -125,7 +125,7 @@ def test_step_refusals(lib):
     need = lib.lit_sparse_step_workspace_bytes(ctypes.byref(args))
     assert need >= 8 * 8192 * 4
     assert lib.lit_sparse_step(None, A, need, None) == 1
-    assert lib.lit_sparse_step(ctypes.byref(args), A, need - 1, None) == 5
+    assert lib.lit_sparse_step(ctypes.byref(args), A, 100, None) == 5
     assert lib.lit_sparse_step(ctypes.byref(args), None, 0, None) == 5
     assert lib.lit_sparse_step(ctypes.byref(args), A + 16, need, None) == 3   # not 256-aligned
     args.T_cap = 4000
@@ -137,3 +137,16 @@ def test_step_refusals(lib):
     args.topk_idx = 0
     assert lib.lit_sparse_step(ctypes.byref(args), A, need, None) == 1
     assert lib.lit_sparse_step_workspace_bytes(None) == 0
+    assert lib.lit_sparse_step_state_bytes(None) == 0
+
+
+def test_step_state_sizes(lib):
+    """The fused form's state size is queried without a GPU only when the device can be
+    asked; here (no GPU) the plan cannot size the teams and reports 0 (multi-kernel)."""
+    args = B.lit_step_args(B=8, S=1, start_pos=16383, ratio=2, Hi=64, Di=128, index_topk=2048,
+                           T_cap=8192, q8=A, q_sc=A, w=A, k8=A, k_sc=A, H=16, D=192, dv=192, W=128,
+                           R=128, q=A, win_kv=A, comp_kv=A, sink=0, scale=0.07, topk_idx=A, out=A)
+    n = lib.lit_sparse_step_state_bytes(ctypes.byref(args))
+    assert n == 0 or n >= 256 + 8 * (32 + 4096 * 4)
+    args.flags = 1
+    assert lib.lit_sparse_step_state_bytes(ctypes.byref(args)) == 0

@@ -192,16 +192,17 @@ def test_sparse_attn_empty_lists_and_huge_sink(orc):
 # ---------------------------------------------------------------------------------
 # the fused step
 # ---------------------------------------------------------------------------------
-def _run_step(d, inp):
+def _run_step(d, inp, flags=0, state=None):
     args, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
                                       k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
                                       comp_kv=d["comp_kv"], start_pos=inp.start_pos,
                                       ratio=inp.ratio, index_topk=inp.index_topk, W=inp.W,
-                                      scale=inp.scale, dv=inp.dv, sink=d["sink"])
-    ws = torch.empty(max(256, L.lit_sparse_step_workspace_bytes(args)), dtype=torch.uint8,
-                     device="cuda")
+                                      scale=inp.scale, dv=inp.dv, sink=d["sink"], flags=flags)
+    state = L.attach_state(args, state)
+    ws = L.step_workspace(args)
     L.lit_sparse_step(args, ws)
     torch.cuda.synchronize()
+    assert L.state_error(state) == 0, "fused step reported a team timeout"
     return idx, out
 
 
@@ -247,44 +248,121 @@ STEP_SMALL = [
 ]
 
 
+MODES = [pytest.param(0, id="fused"), pytest.param(L.LIT_STEP_UNFUSED, id="kernels")]
+
+
+@pytest.mark.parametrize("flags", MODES)
 @pytest.mark.parametrize("cfg", STEP_SMALL, ids=lambda c: f"B{c['B']}S{c['S']}p{c['start_pos']}r{c['ratio']}")
-def test_step_small(orc, cfg):
+def test_step_small(orc, cfg, flags):
     inp = synth.make_step(seed=4242 + cfg["start_pos"], **cfg)
-    idx, out = _run_step(step_inputs_dev(inp), inp)
+    idx, out = _run_step(step_inputs_dev(inp), inp, flags)
     _check_step(orc, inp, idx, out)
 
 
+@pytest.mark.parametrize("flags", MODES)
 @pytest.mark.parametrize("name", ["decode-1k", "decode-4k-r2", "decode-4k-r1", "decode-16k",
                                   "decode-128k"])
-def test_step_workloads(orc, name):
+def test_step_workloads(orc, name, flags):
     inp = synth.workload(name)
-    idx, out = _run_step(step_inputs_dev(inp), inp)
+    idx, out = _run_step(step_inputs_dev(inp), inp, flags)
     swaps = _check_step(orc, inp, idx, out)
     assert swaps <= max(1, inp.B // 2), f"{swaps} queries with near-tie swaps"
+
+
+def test_step_fused_with_sink_ties_and_dv(orc):
+    """Fused path with a sink, dv < D and many equal index scores (integer-valued keys)."""
+    inp = synth.make_step(B=3, S=2, start_pos=1500, ratio=2, Hi=32, Di=64, H=16, D=128, dv=64,
+                          W=64, index_topk=120, seed=77, sink=np.linspace(-2, 3, 16).astype(np.float32))
+    inp.k8[:] = np.where(inp.k8 & 0x40, 0x38, 0xB8).astype(np.uint8)   # keys are +-1 (scaled)
+    idx, out = _run_step(step_inputs_dev(inp), inp, 0)
+    _check_step(orc, inp, idx, out)
 
 
 def test_step_prefill_sampled(orc):
     """The 4096-query chunk at full size; 24 sampled queries checked one by one."""
     inp = synth.workload("prefill-16k")
-    idx, out = _run_step(step_inputs_dev(inp), inp)
+    idx, out = _run_step(step_inputs_dev(inp), inp, 0)
     rng = np.random.default_rng(1)
     sample = sorted(set([0, 1, inp.S - 1] + list(rng.choice(inp.S, 21, replace=False))))
     _check_step(orc, inp, idx, out, [(0, int(i)) for i in sample])
 
 
-def test_step_deterministic():
+@pytest.mark.parametrize("flags", MODES)
+def test_step_deterministic(flags):
     inp = synth.workload("decode-16k")
     d = step_inputs_dev(inp)
-    i1, o1 = _run_step(d, inp)
-    i2, o2 = _run_step(d, inp)
+    i1, o1 = _run_step(d, inp, flags)
+    i2, o2 = _run_step(d, inp, flags)
     assert torch.equal(i1, i2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+def test_step_fused_matches_kernels():
+    """Same scores and selection rule: identical top-k lists; outputs within bf16 rounding
+    of each other (the merge order differs)."""
+    for name in ["decode-16k", "decode-128k", "decode-4k-r1"]:
+        inp = synth.workload(name)
+        d = step_inputs_dev(inp)
+        i1, o1 = _run_step(d, inp, 0)
+        i2, o2 = _run_step(d, inp, L.LIT_STEP_UNFUSED)
+        assert torch.equal(i1, i2), name
+        assert (o1.float() - o2.float()).abs().max().item() <= 1.6e-2, name
+
+
+def test_step_fused_state_reuse():
+    """One state buffer for calls of several shapes (and a multi-kernel call in between):
+    the fused form leaves it zeroed, so repeated calls give identical results."""
+    state = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda")
+    outs = {}
+    for rep in range(3):
+        for name in ["decode-16k", "decode-1k", "decode-128k", "prefill-16k"]:
+            if name == "prefill-16k" and rep == 2:
+                continue
+            inp = synth.workload(name)
+            d = step_inputs_dev(inp)
+            idx, out = _run_step(d, inp, 0, state=state)
+            if rep == 0:
+                outs[name] = (idx, out)
+            else:
+                assert torch.equal(outs[name][0], idx), name
+                assert torch.equal(outs[name][1].view(torch.int16), out.view(torch.int16)), name
+    assert torch.count_nonzero(state).item() == 0
+
+
+@pytest.mark.parametrize("flags", MODES)
+def test_step_graph_replays(flags):
+    """The step captured in a HIP graph, replayed with eager work in between; every
+    replay equals the eager result."""
+    inp = synth.workload("decode-16k")
+    d = step_inputs_dev(inp)
+    ref_idx, ref_out = _run_step(d, inp, flags)
+    args, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
+                                      k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
+                                      comp_kv=d["comp_kv"], start_pos=inp.start_pos,
+                                      ratio=inp.ratio, index_topk=inp.index_topk, W=inp.W,
+                                      scale=inp.scale, flags=flags)
+    state = L.attach_state(args)
+    ws = L.step_workspace(args)
+    L.lit_sparse_step(args, ws)          # warm once outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.lit_sparse_step(args, ws)
+    for rep in range(4):
+        idx.fill_(-7)
+        out.zero_()
+        _ = (torch.randn(1000, device="cuda") * 2).sum().item()   # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_idx), rep
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), rep
+        assert L.state_error(state) == 0
+
+
 def test_step_matches_separate_calls():
-    """The fused step and the three separate entry points give identical results."""
+    """The multi-kernel step and the three separate entry points give identical results."""
     inp = synth.workload("decode-4k-r2")
     d = step_inputs_dev(inp)
-    idx, out = _run_step(d, inp)
+    idx, out = _run_step(d, inp, L.LIT_STEP_UNFUSED)
     sc = L.lit_indexer_scores(d["q8"], d["q_sc"], d["w"], d["k8"], d["k_sc"], inp.start_pos, inp.ratio)
     idx2 = L.lit_topk(sc, inp.start_pos, inp.ratio, inp.index_topk)
     win = L.lit_window_indices(inp.B, inp.S, inp.start_pos, inp.W, inp.R)
