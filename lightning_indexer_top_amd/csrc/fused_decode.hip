@@ -57,7 +57,7 @@ constexpr int kHeads = 16;
 constexpr int kBins = 4096;
 constexpr int kCandCap = 2048;  // candidates held in LDS (more are re-read from memory)
 
-enum : int { kBarA = 0, kBarB = 1, kBarC = 2, kDone = 3, kCtrlWords = 8 };
+enum : int { kBarA = 0, kBarB = 1, kBarC = 2, kDone = 3, kKeyMax = 4, kKeyMinC = 5, kCtrlWords = 8 };
 
 __device__ inline uint32_t ld_agent(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -111,23 +111,30 @@ __device__ inline void find_bin(const uint32_t *hist, int nbins, int need, uint3
         *out_bin = 0;
         *out_above = 0;
     }
-    const int per = nbins / kThreads;
+    const int per = nbins / kThreads;  // 1 .. 16
     const int hi = nbins - 1 - threadIdx.x * per;  // this thread's bins: hi, hi-1, ..., hi-per+1
+    uint32_t cnt[16];
     uint32_t mine = 0;
-    for (int j = 0; j < per; ++j) mine += hist[hi - j];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        cnt[j] = j < per ? hist[hi - j] : 0u;
+        mine += cnt[j];
+    }
     uint32_t total;
     const uint32_t incl = wg_scan(mine, wsum, &total);
     int above = (int)(incl - mine);
     if (above < need && need <= (int)incl) {
-        for (int j = 0; j < per; ++j) {
-            const int c = (int)hist[hi - j];
-            if (above + c >= need) {
-                *out_bin = hi - j;
-                *out_above = above;
-                break;
+        int found = -1, fa = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (found < 0 && above + (int)cnt[j] >= need) {
+                found = j;
+                fa = above;
             }
-            above += c;
+            above += (int)cnt[j];
         }
+        *out_bin = hi - found;
+        *out_above = fa;
     }
     __syncthreads();
 }
@@ -139,6 +146,7 @@ struct FusedLds {
     int bin, above, ncand, npick, overflow;
     uint32_t kstar;
     int pstar;
+    uint32_t mm[kThreads / 64][2];
 };
 
 __device__ inline uint64_t pack2(float a, float b) {
@@ -151,6 +159,21 @@ __device__ inline uint64_t ld64_agent(const uint64_t *p) {
 }
 __device__ inline void st64_agent(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kSc1 = 16;  // buffer cache policy: coherent at agent scope (sc1)
+__device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ inline u32x4 ld128_agent(rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kSc1);
+}
+__device__ inline void st128_agent(rsrc_t r, uint32_t byte_off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, kSc1);
+}
+__device__ inline float key_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
 // Workgroup max / min / sum (every thread gets the result).
@@ -244,10 +267,11 @@ __device__ inline void radix_resolve(FusedLds &sm, const float *ts, int nvis, fl
 template <int D, int DI, int HT>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     constexpr int LD = D + 4;
-    constexpr int kCache = 16;  // score pairs per thread kept in registers during selection
+    constexpr int kCacheQ = 8;  // score quads per thread kept in registers during selection
     __shared__ FusedLds sm;
     __shared__ __attribute__((aligned(16))) uint16_t attn_lds[4 * 32 * LD];  // rows / candidates / merge
     __shared__ float wm[4 * kHeads], wl[4 * kHeads];
+    __shared__ float hf[4 * kHeads], hl[kHeads], hm[kHeads];  // per-head merge factors
     extern __shared__ float dyn[];  // chunk scores [chunk], then picks [chunk] (ints)
 
     const int tid = threadIdx.x;
@@ -272,6 +296,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     const int n = max(0, c1 - c0);
     uint32_t *ctrl = f.ctrl + (size_t)q * kCtrlWords;
     float *ts = f.scores + (size_t)q * f.ld;  // the team's scores
+    const rsrc_t ts_r = make_rsrc(ts, (uint32_t)f.ld * 4u);
     float *sc = dyn;
     int *picks = reinterpret_cast<int *>(dyn + f.chunk);
 
@@ -297,10 +322,41 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         }
     }
     __syncthreads();
-    if (select) {  // publish this chunk's scores (pairs; chunks start at even positions)
-        uint64_t *dst = reinterpret_cast<uint64_t *>(ts + c0);
-        for (int j = 2 * tid; j < n; j += 2 * kThreads)
-            st64_agent(dst + j / 2, pack2(sc[j], j + 1 < n ? sc[j + 1] : 0.f));
+    if (select) {
+        // publish this chunk's scores (16-byte coherent stores; chunks start at multiples of 256)
+        uint32_t kmax = 0u, kminc = 0u;  // team max key, and max of complemented keys (= min)
+        for (int j = tid; 4 * j < n; j += kThreads) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = 4 * j + e < n ? sc[4 * j + e] : sc[4 * j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t k = order_key(v[e]);
+                kmax = max(kmax, k);
+                kminc = max(kminc, ~k);
+            }
+            st128_agent(ts_r, (uint32_t)(c0 + 4 * j) * 4u,
+                        u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                              __float_as_uint(v[3])});
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+            kminc = max(kminc, (uint32_t)__shfl_xor((int)kminc, off));
+        }
+        if (lane == 0) {
+            sm.mm[wave][0] = kmax;
+            sm.mm[wave][1] = kminc;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t a = 0u, cmin = 0u;
+            for (int w = 0; w < kThreads / 64; ++w) {
+                a = max(a, sm.mm[w][0]);
+                cmin = max(cmin, sm.mm[w][1]);
+            }
+            st64_agent(f.minmax + (size_t)q * f.team_size + m, (uint64_t)a | ((uint64_t)cmin << 32));
+        }
         team_arrive(&ctrl[kBarA]);
     }
 
@@ -324,54 +380,76 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     int off = c0;         // where this member's picks start in the output list
     if (select) {
         team_wait(&ctrl[kBarA], (uint32_t)f.team_size, f.spin_limit, f.err);
-        const uint64_t *tp = reinterpret_cast<const uint64_t *>(ts);
-        const int npair = (nvis + 1) / 2;
-        const bool cached = npair <= kCache * kThreads;
-        uint64_t vals[kCache];
+        const int nquad = (nvis + 3) / 4;
+        const bool cached = nquad <= kCacheQ * kThreads;
+        u32x4 vals[kCacheQ];
         if (cached) {
 #pragma unroll
-            for (int r = 0; r < kCache; ++r) {
-                const int pi = tid + r * kThreads;
-                vals[r] = pi < npair ? ld64_agent(tp + pi) : 0ull;
+            for (int r = 0; r < kCacheQ; ++r) {
+                const int qi = tid + r * kThreads;
+                vals[r] = qi < nquad ? ld128_agent(ts_r, (uint32_t)qi * 16u) : u32x4{0u, 0u, 0u, 0u};
             }
         }
-        // visit every (pair index, pair) of the team's scores
+        // every visible (position, score) of the team, read from the team buffer
         auto each = [&](auto &&fn) {
-            if (cached) {
+            for (int qi = tid; qi < nquad; qi += kThreads) {
+                const u32x4 v = ld128_agent(ts_r, (uint32_t)qi * 16u);
 #pragma unroll
-                for (int r = 0; r < kCache; ++r) {
-                    const int pi = tid + r * kThreads;
-                    if (pi < npair) fn(pi, vals[r]);
-                }
-            } else {
-                for (int pi = tid; pi < npair; pi += kThreads) fn(pi, ld64_agent(tp + pi));
+                for (int e = 0; e < 4; ++e)
+                    if (4 * qi + e < nvis) fn(4 * qi + e, __uint_as_float(v[e]));
             }
         };
-        // pass 1: team min / max
-        float mx = -INFINITY, mn = INFINITY;
-        each([&](int pi, uint64_t v) {
-            mx = fmaxf(mx, lo_f(v));
-            mn = fminf(mn, lo_f(v));
-            if (2 * pi + 1 < nvis) {
-                mx = fmaxf(mx, hi_f(v));
-                mn = fminf(mn, hi_f(v));
+        // team max / min from the members' slots
+        {
+            uint32_t a = 0u, cmin = 0u;
+            for (int j = tid; j < f.team_size; j += kThreads) {
+                const uint64_t v = ld64_agent(f.minmax + (size_t)q * f.team_size + j);
+                a = max(a, (uint32_t)v);
+                cmin = max(cmin, (uint32_t)(v >> 32));
             }
-        });
+#pragma unroll
+            for (int o2 = 32; o2 >= 1; o2 >>= 1) {
+                a = max(a, (uint32_t)__shfl_xor((int)a, o2));
+                cmin = max(cmin, (uint32_t)__shfl_xor((int)cmin, o2));
+            }
+            if (lane == 0) {
+                sm.mm[wave][0] = a;
+                sm.mm[wave][1] = cmin;
+            }
+        }
         for (int j = tid; j < kBins; j += kThreads) sm.hist[j] = 0u;
-        mx = wg_max(mx, sm.fred);
-        mn = wg_min(mn, sm.fred);
+        __syncthreads();
+        uint32_t kmax = 0u, kminc = 0u;
+        for (int w = 0; w < kThreads / 64; ++w) {
+            kmax = max(kmax, sm.mm[w][0]);
+            kminc = max(kminc, sm.mm[w][1]);
+        }
+        const float mx = key_float(kmax);
+        const float mn = key_float(~kminc);
         const float scale = mx > mn ? (float)kBins / (mx - mn) : 0.f;
-        // pass 2: value histogram
-        each([&](int pi, uint64_t v) {
-            atomicAdd(&sm.hist[value_bin(lo_f(v), mn, scale)], 1u);
-            if (2 * pi + 1 < nvis) atomicAdd(&sm.hist[value_bin(hi_f(v), mn, scale)], 1u);
-        });
+        // pass 1: value bins (kept, 16 bits each, when the scores are cached) and histogram
+        uint32_t bins[kCacheQ * 2];
+        if (cached) {
+#pragma unroll
+            for (int r = 0; r < kCacheQ; ++r) {
+                const int qi = tid + r * kThreads;
+                uint32_t bb[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bb[e] = (uint32_t)value_bin(__uint_as_float(vals[r][e]), mn, scale);
+                    if (qi < nquad && 4 * qi + e < nvis) atomicAdd(&sm.hist[bb[e]], 1u);
+                }
+                bins[2 * r] = bb[0] | (bb[1] << 16);
+                bins[2 * r + 1] = bb[2] | (bb[3] << 16);
+            }
+        } else {
+            each([&](int t, float x) { atomicAdd(&sm.hist[value_bin(x, mn, scale)], 1u); });
+        }
         __syncthreads();
         find_bin(sm.hist, kBins, f.keff, sm.wsum, &sm.bin, &sm.above);
         const int vb = sm.bin;
         const int need = f.keff - sm.above;
         const int cnt = (int)sm.hist[vb];
-        // pass 3: the candidates (scores in bin vb) into LDS when they fit
         uint32_t *ckey = reinterpret_cast<uint32_t *>(attn_lds);
         int *cpos = reinterpret_cast<int *>(ckey + kCandCap);
         if (tid == 0) {
@@ -380,25 +458,39 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             sm.pstar = 0x7fffffff;
         }
         __syncthreads();
+        uint32_t before = 0;  // this thread's certain picks before the member's chunk
         if (cnt <= kCandCap) {
-            each([&](int pi, uint64_t v) {
+            // pass 2: candidates (bin vb) into LDS; count bins above vb before c0
+            auto visit = [&](int t, float x, int bin) {
+                before += t < c0 && bin > vb;
+                if (bin == vb) {
+                    const int sidx = atomicAdd(&sm.ncand, 1);
+                    ckey[sidx] = order_key(x);
+                    cpos[sidx] = t;
+                }
+            };
+            if (cached) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const float x = h ? hi_f(v) : lo_f(v);
-                    const int t = 2 * pi + h;
-                    if (t < nvis && value_bin(x, mn, scale) == vb) {
-                        const int sidx = atomicAdd(&sm.ncand, 1);
-                        ckey[sidx] = order_key(x);
-                        cpos[sidx] = t;
+                for (int r = 0; r < kCacheQ; ++r) {
+                    const int qi = tid + r * kThreads;
+                    if (qi < nquad) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int bin = (int)((bins[2 * r + (e >> 1)] >> (16 * (e & 1))) & 0xffffu);
+                            if (4 * qi + e < nvis) visit(4 * qi + e, __uint_as_float(vals[r][e]), bin);
+                        }
                     }
                 }
-            });
+            } else {
+                each([&](int t, float x) { visit(t, x, value_bin(x, mn, scale)); });
+            }
             __syncthreads();
             // rank every candidate by (key desc, position asc); the (need-1)-th is the cut
             for (int j = tid; j < cnt; j += kThreads) {
                 const uint32_t kj = ckey[j];
                 const int pj = cpos[j];
                 int rank = 0;
+#pragma unroll 8
                 for (int o = 0; o < cnt; ++o) {
                     const uint32_t ko = ckey[o];
                     rank += ko > kj || (ko == kj && cpos[o] < pj);
@@ -409,21 +501,21 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                 }
             }
             __syncthreads();
+            kstar = sm.kstar;
+            pstar = sm.pstar;
+            for (int j = tid; j < cnt; j += kThreads) {
+                const uint32_t kj = ckey[j];
+                before += cpos[j] < c0 && (kj > kstar || (kj == kstar && cpos[j] <= pstar));
+            }
         } else {
             radix_resolve(sm, ts, nvis, mn, scale, vb, need);
-        }
-        kstar = sm.kstar;
-        pstar = sm.pstar;
-        // pass 4: picks at positions before this member's chunk
-        uint32_t before = 0;
-        each([&](int pi, uint64_t v) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int t = 2 * pi + h;
-                const uint32_t k = order_key(h ? hi_f(v) : lo_f(v));
+            kstar = sm.kstar;
+            pstar = sm.pstar;
+            each([&](int t, float x) {
+                const uint32_t k = order_key(x);
                 before += t < c0 && (k > kstar || (k == kstar && t <= pstar));
-            }
-        });
+            });
+        }
         off = (int)wg_sum(before, sm.wsum);
     }
 
@@ -453,6 +545,9 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             for (int j = nvis + tid; j < f.keff; j += kThreads) idx_row[j] = -1;
         __syncthreads();
     }
+    const int slot_bytes = f.slot_floats * 4;
+    const rsrc_t part_r = make_rsrc(f.part + (size_t)q * f.team_size * f.slot_floats,
+                                    (uint32_t)(f.team_size * slot_bytes));
     {
         const float sl2 = aa.scale * kLog2e;
         uint16_t *tile = attn_lds + wave * 32 * LD;
@@ -483,21 +578,42 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         float *ow = reinterpret_cast<float *>(attn_lds);
         attn_wave_publish<D>(st, ow, wm, wl, wave, aa.dv, g, c);
         __syncthreads();
-        // this member's state: O [16][dv] then (M, L) [16], as float pairs
-        uint64_t *slot = reinterpret_cast<uint64_t *>(f.part + ((size_t)q * f.team_size + m) * f.slot_floats);
-        const int half_dv = aa.dv / 2;
-        for (int e = tid; e < kHeads * half_dv; e += kThreads) {
-            const int h = e / half_dv;
-            const int d = 2 * (e - h * half_dv);
-            float O0, O1, M, L;
-            attn_combine(ow, wm, wl, 4, h, d, aa.dv, O0, M, L);
-            attn_combine(ow, wm, wl, 4, h, d + 1, aa.dv, O1, M, L);
-            st64_agent(slot + (h * aa.dv + d) / 2, pack2(O0, O1));
-        }
+        // per-head factors of the 4 waves, once
         if (tid < kHeads) {
-            float O, M, L;
-            attn_combine(ow, wm, wl, 4, tid, 0, aa.dv, O, M, L);
-            st64_agent(slot + (kHeads * aa.dv) / 2 + tid, pack2(M, L));
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w * kHeads + tid]);
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float mw = wm[w * kHeads + tid];
+                const float fw = (mw == -INFINITY || M == -INFINITY) ? 0.f : exp2f(mw - M);
+                hf[w * kHeads + tid] = fw;
+                L += fw * wl[w * kHeads + tid];
+            }
+            hm[tid] = M;
+            hl[tid] = L;
+        }
+        __syncthreads();
+        // this member's state: O [16][dv] then (M, L) [16], 16-byte coherent stores
+        const int qdv = aa.dv / 4;
+        const uint32_t my_off = (uint32_t)(m * slot_bytes);
+        for (int e = tid; e < kHeads * qdv; e += kThreads) {
+            const int h = e / qdv;
+            const int d = 4 * (e - h * qdv);
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(&ow[(w * kHeads + h) * aa.dv + d]);
+                O += hf[w * kHeads + h] * x;
+            }
+            st128_agent(part_r, my_off + (uint32_t)(h * aa.dv + d) * 4u, __builtin_bit_cast(u32x4, O));
+        }
+        if (tid < kHeads / 2) {
+            const int h = 2 * tid;
+            st128_agent(part_r, my_off + (uint32_t)(kHeads * aa.dv + 2 * h) * 4u,
+                        u32x4{__float_as_uint(hm[h]), __float_as_uint(hl[h]), __float_as_uint(hm[h + 1]),
+                              __float_as_uint(hl[h + 1])});
         }
     }
     team_arrive(&ctrl[kBarC]);
@@ -505,41 +621,89 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
 
     // ------------------------------------------------------------------ phase M
     {
-        // this member's slice of the (head, dim-pair) outputs
-        const int half_dv = aa.dv / 2;
-        const int n_out = kHeads * half_dv;
+        // this member's slice of the (head, dim-quad) outputs
+        const int qdv = aa.dv / 4;
+        const int n_out = kHeads * qdv;
         const int per = (n_out + f.team_size - 1) / f.team_size;
         const int e0 = m * per, e1 = min(e0 + per, n_out);
-        float *smax = reinterpret_cast<float *>(attn_lds);
-        float *snrm = smax + f.team_size * kHeads;
-        const uint64_t *tp = reinterpret_cast<const uint64_t *>(f.part + (size_t)q * f.team_size * f.slot_floats);
-        const int slot_pairs = f.slot_floats / 2;
-        for (int j = tid; j < f.team_size * kHeads; j += kThreads) {
-            const int s = j / kHeads, h = j % kHeads;
-            const uint64_t ml = ld64_agent(tp + (size_t)s * slot_pairs + (kHeads * aa.dv) / 2 + h);
-            smax[j] = lo_f(ml);
-            snrm[j] = hi_f(ml);
-        }
-        __syncthreads();
-        for (int e = e0 + tid; e < e1; e += kThreads) {
-            const int h = e / half_dv;
-            const int d = 2 * (e - h * half_dv);
-            float M = -INFINITY;
-            for (int s = 0; s < f.team_size; ++s) M = fmaxf(M, smax[s * kHeads + h]);
-            float O0 = 0.f, O1 = 0.f, L = 0.f;
-            if (M != -INFINITY) {
-                for (int s = 0; s < f.team_size; ++s) {
-                    const float ms = smax[s * kHeads + h];
-                    const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-                    const uint64_t o = ld64_agent(tp + (size_t)s * slot_pairs + (h * aa.dv + d) / 2);
-                    O0 += w * lo_f(o);
-                    O1 += w * hi_f(o);
-                    L += w * snrm[s * kHeads + h];
+        float *wts = reinterpret_cast<float *>(attn_lds);  // [team_size][16] slot weights
+        __shared__ float hsum[kHeads], hmax[kHeads];
+        if (e1 > e0) {
+            const int h_lo = e0 / qdv, h_hi = (e1 - 1) / qdv;
+            // one wave per head of the slice: max over slots, weights e^(m_s - M), 1 / L
+            for (int h = h_lo + wave; h <= h_hi; h += kThreads / 64) {
+                float ms[4], ls[4];
+                float M = -INFINITY;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int sl = lane + 64 * r;
+                    ms[r] = -INFINITY;
+                    ls[r] = 0.f;
+                    if (sl < f.team_size) {
+                        const uint64_t ml = ld64_agent(reinterpret_cast<const uint64_t *>(
+                                                           f.part + ((size_t)q * f.team_size + sl) * f.slot_floats +
+                                                           kHeads * aa.dv) + h);
+                        ms[r] = lo_f(ml);
+                        ls[r] = hi_f(ml);
+                    }
+                    M = fmaxf(M, ms[r]);
+                }
+#pragma unroll
+                for (int o2 = 32; o2 >= 1; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2));
+                float L = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int sl = lane + 64 * r;
+                    const float wgt = (ms[r] == -INFINITY || M == -INFINITY) ? 0.f : exp2f(ms[r] - M);
+                    if (sl < f.team_size) wts[sl * kHeads + h] = wgt;
+                    L += wgt * ls[r];
+                }
+#pragma unroll
+                for (int o2 = 32; o2 >= 1; o2 >>= 1) L += __shfl_xor(L, o2);
+                if (lane == 0) {
+                    hmax[h] = M;
+                    hsum[h] = L;
                 }
             }
-            uint16_t *dst = aa.out + ((size_t)q * kHeads + h) * aa.dv + d;
-            dst[0] = attn_finish(O0, M, L, aa.sink, h);
-            dst[1] = attn_finish(O1, M, L, aa.sink, h);
+        }
+        __syncthreads();
+        if (e1 > e0) {
+            // lanes per output quad (a power of two), each summing a stride of the slots
+            const int items = e1 - e0;
+            int lpi = 1;
+            while (lpi * 2 * items <= kThreads && lpi * 2 <= 64) lpi *= 2;
+            const int item = tid / lpi, sub = tid % lpi;
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
+            int h = 0, d = 0;
+            if (item < items) {
+                const int e = e0 + item;
+                h = e / qdv;
+                d = 4 * (e - h * qdv);
+                u32x4 o[8];
+                for (int s0 = sub; s0 < f.team_size; s0 += 8 * lpi) {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int sl = s0 + u * lpi;
+                        o[u] = sl < f.team_size
+                                   ? ld128_agent(part_r, (uint32_t)(sl * slot_bytes + (h * aa.dv + d) * 4))
+                                   : u32x4{0u, 0u, 0u, 0u};
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int sl = s0 + u * lpi;
+                        if (sl < f.team_size) O += wts[sl * kHeads + h] * __builtin_bit_cast(f32x4, o[u]);
+                    }
+                }
+            }
+            for (int o2 = lpi / 2; o2 >= 1; o2 >>= 1) {
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) O[e4] += __shfl_xor(O[e4], o2);
+            }
+            if (item < items && sub == 0) {
+                uint16_t *dst = aa.out + ((size_t)q * kHeads + h) * aa.dv + d;
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) dst[e4] = attn_finish(O[e4], hmax[h], hsum[h], aa.sink, h);
+            }
         }
     }
     // the last member to finish zeroes the team's control words for the next launch
@@ -649,10 +813,11 @@ size_t fused_state_bytes(const FusedPlan &p) {
     return 256 + (size_t)p.n_teams * kCtrlWords * 4;
 }
 
-static int slot_floats(int dv) { return (kHeads * dv + 2 * kHeads + 63) / 64 * 64; }
+static int slot_floats(int dv) { return (kHeads * dv + 2 * kHeads + 63) / 64 * 64; }  // 16-byte multiple
 
 size_t fused_ws_bytes(const FusedPlan &p, int dv) {
-    return (size_t)p.n_teams * p.ld * 4 + 256 +                              // team scores
+    return (size_t)p.n_teams * p.team_size * 8 + 256 +                       // min / max slots
+           (size_t)p.n_teams * p.ld * 4 + 256 +                              // team scores
            (size_t)p.n_teams * p.team_size * slot_floats(dv) * 4 + 256;      // partial states
 }
 
@@ -666,6 +831,7 @@ hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, 
         rest += (bytes + 255) / 256 * 256;
         return r;
     };
+    f.minmax = (uint64_t *)bump((size_t)p.n_teams * p.team_size * 8);
     f.scores = (float *)bump((size_t)p.n_teams * p.ld * 4);
     f.part = (float *)bump((size_t)p.n_teams * p.team_size * slot_floats(f.aa.dv) * 4);
     f.slot_floats = slot_floats(f.aa.dv);

@@ -113,6 +113,7 @@ struct FusedArgs {
     long ld;              // team score array stride
     uint32_t spin_limit;
     uint32_t *err, *ctrl;         // zero between launches
+    uint64_t *minmax;             // per member: (max key, max complemented key) of its chunk
     float *scores;                // per team: scores of the visible rows
     float *part;                  // per member: partial attention state
     int slot_floats;              // floats per member state

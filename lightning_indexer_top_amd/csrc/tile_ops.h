@@ -272,34 +272,37 @@ __device__ inline uint16_t attn_finish(float O, float M, float L, const float *s
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup scans (inclusive, ascending thread id); *total gets the sum.  Every thread
-// of the workgroup must call them.  wsum needs blockDim.x / 64 entries.
+// Wave and workgroup scans.  The wave scan uses DPP lane shifts within rows of 16
+// lanes and the row broadcasts of 64-lane waves (no LDS traffic).
 // ---------------------------------------------------------------------------
+__device__ inline uint32_t wave_scan(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
+// Inclusive scan over the workgroup (ascending thread id); *total gets the sum.  Every
+// thread of the workgroup must call it.  wsum needs blockDim.x / 64 entries.
 __device__ inline uint32_t wg_scan(uint32_t v, uint32_t *wsum, uint32_t *total) {
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = __shfl_up(v, off);
-        if (lane >= off) v += t;
-    }
+    v = wave_scan(v);
     if (lane == 63) wsum[wid] = v;
     __syncthreads();
-    if (wid == 0) {
-        uint32_t s = lane < nw ? wsum[lane] : 0u;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t t = __shfl_up(s, off);
-            if (lane >= off) s += t;
-        }
-        if (lane < nw) wsum[lane] = s;
+    uint32_t before = 0, all = 0;
+    for (int w = 0; w < nw; ++w) {
+        const uint32_t x = wsum[w];
+        before += w < wid ? x : 0u;
+        all += x;
     }
+    *total = all;
     __syncthreads();
-    if (wid > 0) v += wsum[wid - 1];
-    *total = wsum[nw - 1];
-    __syncthreads();
-    return v;
+    return v + before;
 }
 
 // Order-preserving 32-bit key of a float: a larger float gives a larger key; -0 ranks
