@@ -54,7 +54,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kHeads = 16;
-constexpr int kBins = 4096;
+constexpr int kBins = 4096;    // radix-level histogram size (12-bit digits)
+constexpr int kVBins = 4096;   // value bins of the first selection level (+ one spill bin)
 constexpr int kCandCap = 2048;  // candidates held in LDS (more are re-read from memory)
 
 enum : int { kBarA = 0, kBarB = 1, kBarC = 2, kDone = 3, kKeyMax = 4, kKeyMinC = 5, kCtrlWords = 8 };
@@ -103,44 +104,56 @@ __device__ inline void team_wait(uint32_t *ctr, uint32_t target, uint32_t limit,
     __syncthreads();
 }
 
-// Bin search from the top over `nbins` LDS counters (nbins a multiple of 256): the bin
-// where the count from the top reaches `need`, and the count strictly above it.
+// Bin search from the top over `nbins` LDS counters (256, 1024 or 4096): the bin where
+// the count from the top reaches `need`, and the count strictly above it.  Thread t holds
+// the contiguous bins [nbins - per*(t+1), nbins - per*t), read as 16-byte words.
 __device__ inline void find_bin(const uint32_t *hist, int nbins, int need, uint32_t *wsum, int *out_bin,
                                 int *out_above) {
     if (threadIdx.x == 0) {
         *out_bin = 0;
         *out_above = 0;
     }
-    const int per = nbins / kThreads;  // 1 .. 16
-    const int hi = nbins - 1 - threadIdx.x * per;  // this thread's bins: hi, hi-1, ..., hi-per+1
+    const int per = nbins / kThreads;
+    const int lo = nbins - per * ((int)threadIdx.x + 1);
     uint32_t cnt[16];
+    if (per == 1) {
+        cnt[0] = hist[lo];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) cnt[j] = 0u;
+    } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const u32x4 x = 4 * v < per ? *reinterpret_cast<const u32x4 *>(hist + lo + 4 * v) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cnt[4 * v + e] = x[e];
+        }
+    }
     uint32_t mine = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        cnt[j] = j < per ? hist[hi - j] : 0u;
-        mine += cnt[j];
-    }
+    for (int j = 0; j < 16; ++j) mine += cnt[j];
     uint32_t total;
     const uint32_t incl = wg_scan(mine, wsum, &total);
     int above = (int)(incl - mine);
     if (above < need && need <= (int)incl) {
-        int found = -1, fa = 0;
+        int found = 0, fa = 0;
+        bool done = false;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            if (found < 0 && above + (int)cnt[j] >= need) {
+        for (int j = 15; j >= 0; --j) {
+            if (!done && j < per && above + (int)cnt[j] >= need) {
                 found = j;
                 fa = above;
+                done = true;
             }
-            above += (int)cnt[j];
+            if (j < per) above += (int)cnt[j];
         }
-        *out_bin = hi - found;
+        *out_bin = lo + found;
         *out_above = fa;
     }
     __syncthreads();
 }
 
 struct FusedLds {
-    uint32_t hist[kBins];
+    alignas(16) uint32_t hist[kBins + 4];  // + the spill bin of the value level
     uint32_t wsum[kThreads / 64];
     float fred[kThreads / 64];
     int bin, above, ncand, npick, overflow;
@@ -210,19 +223,19 @@ __device__ inline uint32_t wg_sum(uint32_t v, uint32_t *red) {
 
 // Linear value bin between the team's min and max: monotonic in the value, so every
 // score in a higher bin is larger than every score in a lower one.
-__device__ inline int value_bin(float v, float mn, float scale) {
-    const float fb = fminf(fmaxf((v - mn) * scale, 0.f), (float)(kBins - 1));
-    return (int)fb;
+__device__ inline int value_bin(float v, float scale, float bias) {
+    // fma is monotone in v for scale >= 0, so bins are ordered like the scores
+    return (int)__builtin_amdgcn_fmed3f(fmaf(v, scale, bias), 0.f, (float)(kVBins - 1));
 }
 
 // Exact resolution by radix levels over the team's scores (heavy ties): among the
 // scores in value bin vb, the need-th by (order key desc, position asc).  Threads take
 // contiguous position ranges so the final tie cut can walk positions in order.
-__device__ inline void radix_resolve(FusedLds &sm, const float *ts, int nvis, float mn, float scale, int vb,
+__device__ inline void radix_resolve(FusedLds &sm, const float *ts, int nvis, float scale, float bias, int vb,
                                      int need) {
     const int per = (nvis + kThreads - 1) / kThreads;
     const int t0 = threadIdx.x * per, t1 = min(t0 + per, nvis);
-    auto in_bin = [&](float v) { return value_bin(v, mn, scale) == vb; };
+    auto in_bin = [&](float v) { return value_bin(v, scale, bias) == vb; };
     uint32_t prefix = 0u, pmask = 0u;
     const int shifts[3] = {20, 8, 0};
     const int widths[3] = {12, 12, 8};
@@ -381,12 +394,14 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     if (select) {
         team_wait(&ctrl[kBarA], (uint32_t)f.team_size, f.spin_limit, f.err);
         const int nquad = (nvis + 3) / 4;
+        // cached form: thread t keeps the score quads t + kThreads*r (positions 4(t + kThreads*r) + e)
         const bool cached = nquad <= kCacheQ * kThreads;
+        const bool full = 4 * (tid + kThreads * (kCacheQ - 1)) + 4 <= nvis;  // all 32 visible
         u32x4 vals[kCacheQ];
         if (cached) {
 #pragma unroll
             for (int r = 0; r < kCacheQ; ++r) {
-                const int qi = tid + r * kThreads;
+                const int qi = tid + kThreads * r;
                 vals[r] = qi < nquad ? ld128_agent(ts_r, (uint32_t)qi * 16u) : u32x4{0u, 0u, 0u, 0u};
             }
         }
@@ -417,7 +432,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                 sm.mm[wave][1] = cmin;
             }
         }
-        for (int j = tid; j < kBins; j += kThreads) sm.hist[j] = 0u;
+        for (int j = tid; j < kVBins / 4 + 1; j += kThreads)  // + the spill bin
+            reinterpret_cast<u32x4 *>(sm.hist)[j] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
         uint32_t kmax = 0u, kminc = 0u;
         for (int w = 0; w < kThreads / 64; ++w) {
@@ -426,89 +442,130 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         }
         const float mx = key_float(kmax);
         const float mn = key_float(~kminc);
-        const float scale = mx > mn ? (float)kBins / (mx - mn) : 0.f;
-        // pass 1: value bins (kept, 16 bits each, when the scores are cached) and histogram
+        const float scale = mx > mn ? (float)kVBins / (mx - mn) : 0.f;
+        const float bias = -mn * scale;
+        // pass 1: value bins (kept, 16 bits each) and histogram; cached positions past the
+        // visible rows take the spill bin kVBins
         uint32_t bins[kCacheQ * 2];
         if (cached) {
+            if (full) {
 #pragma unroll
-            for (int r = 0; r < kCacheQ; ++r) {
-                const int qi = tid + r * kThreads;
-                uint32_t bb[4];
+                for (int r = 0; r < kCacheQ; ++r) {
+                    uint32_t bb[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    bb[e] = (uint32_t)value_bin(__uint_as_float(vals[r][e]), mn, scale);
-                    if (qi < nquad && 4 * qi + e < nvis) atomicAdd(&sm.hist[bb[e]], 1u);
+                    for (int e = 0; e < 4; ++e) {
+                        bb[e] = (uint32_t)value_bin(__uint_as_float(vals[r][e]), scale, bias);
+                        atomicAdd(&sm.hist[bb[e]], 1u);
+                    }
+                    bins[2 * r] = bb[0] | (bb[1] << 16);
+                    bins[2 * r + 1] = bb[2] | (bb[3] << 16);
                 }
-                bins[2 * r] = bb[0] | (bb[1] << 16);
-                bins[2 * r + 1] = bb[2] | (bb[3] << 16);
+            } else {
+#pragma unroll
+                for (int r = 0; r < kCacheQ; ++r) {
+                    uint32_t bb[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        bb[e] = 4 * (tid + kThreads * r) + e < nvis
+                                    ? (uint32_t)value_bin(__uint_as_float(vals[r][e]), scale, bias)
+                                    : (uint32_t)kVBins;
+                        atomicAdd(&sm.hist[bb[e]], 1u);
+                    }
+                    bins[2 * r] = bb[0] | (bb[1] << 16);
+                    bins[2 * r + 1] = bb[2] | (bb[3] << 16);
+                }
             }
         } else {
-            each([&](int t, float x) { atomicAdd(&sm.hist[value_bin(x, mn, scale)], 1u); });
+            each([&](int t, float x) { atomicAdd(&sm.hist[value_bin(x, scale, bias)], 1u); });
         }
         __syncthreads();
-        find_bin(sm.hist, kBins, f.keff, sm.wsum, &sm.bin, &sm.above);
+        find_bin(sm.hist, kVBins, f.keff, sm.wsum, &sm.bin, &sm.above);
         const int vb = sm.bin;
         const int need = f.keff - sm.above;
         const int cnt = (int)sm.hist[vb];
-        uint32_t *ckey = reinterpret_cast<uint32_t *>(attn_lds);
-        int *cpos = reinterpret_cast<int *>(ckey + kCandCap);
+        // candidates as (key << 32 | ~position): larger means ahead in (key desc, position asc)
+        uint64_t *cand = reinterpret_cast<uint64_t *>(attn_lds);
         if (tid == 0) {
-            sm.ncand = 0;
             sm.kstar = 0u;
             sm.pstar = 0x7fffffff;
+            sm.ncand = 0;
         }
         __syncthreads();
-        uint32_t before = 0;  // this thread's certain picks before the member's chunk
+        uint32_t before = 0;  // this thread's share of the picks before the member's chunk
         if (cnt <= kCandCap) {
-            // pass 2: candidates (bin vb) into LDS; count bins above vb before c0
-            auto visit = [&](int t, float x, int bin) {
-                before += t < c0 && bin > vb;
-                if (bin == vb) {
-                    const int sidx = atomicAdd(&sm.ncand, 1);
-                    ckey[sidx] = order_key(x);
-                    cpos[sidx] = t;
-                }
-            };
+            // pass 2: the candidates (bin vb) into LDS, and the scores above bin vb before c0
+            // counted.  Cached: two 16-bit bins per word; adding 0x7fff - vb (0x8000 - vb) to
+            // a half sets its bit 15 exactly when the bin is above (at least) vb, and bins stay
+            // <= kVBins, so no half carries into the next.  Chunks start at multiples of 256
+            // positions, so "quad tid + kThreads*r lies before c0" holds for all 64 lanes of a
+            // wave or for none.
             if (cached) {
+                const uint32_t kgt = (0x7fffu - (uint32_t)vb) * 0x10001u;
+                const uint32_t kge = (0x8000u - (uint32_t)vb) * 0x10001u;
+                uint32_t cmask = 0;  // bit 4r + e: element e of quad r is a candidate
 #pragma unroll
                 for (int r = 0; r < kCacheQ; ++r) {
-                    const int qi = tid + r * kThreads;
-                    if (qi < nquad) {
+                    const uint32_t a0 = bins[2 * r] + kgt, a1 = bins[2 * r + 1] + kgt;
+                    const uint32_t b0 = bins[2 * r] + kge, b1 = bins[2 * r + 1] + kge;
+                    if (4 * (wave * 64 + kThreads * r) < c0)
+                        before += __builtin_popcount(a0 & 0x80008000u) + __builtin_popcount(a1 & 0x80008000u);
+                    const uint32_t e0 = (a0 ^ b0) & 0x80008000u, e1 = (a1 ^ b1) & 0x80008000u;
+                    cmask |= ((e0 >> 15) & 1u | (e0 >> 30) & 2u | (e1 >> 13) & 4u | (e1 >> 28) & 8u) << (4 * r);
+                }
+                if (cmask) {
+                    int ci = atomicAdd(&sm.ncand, __builtin_popcount(cmask));
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int bin = (int)((bins[2 * r + (e >> 1)] >> (16 * (e & 1))) & 0xffffu);
-                            if (4 * qi + e < nvis) visit(4 * qi + e, __uint_as_float(vals[r][e]), bin);
+                    for (int r = 0; r < kCacheQ; ++r) {
+                        uint32_t m4 = (cmask >> (4 * r)) & 15u;
+                        while (m4) {
+                            const int e = __builtin_ctz(m4);
+                            m4 &= m4 - 1u;
+                            const uint32_t xv = e == 0 ? vals[r][0] : e == 1 ? vals[r][1] : e == 2 ? vals[r][2] : vals[r][3];
+                            const int t = 4 * (tid + kThreads * r) + e;
+                            cand[ci++] = ((uint64_t)order_key(__uint_as_float(xv)) << 32) | (uint32_t)~(uint32_t)t;
                         }
                     }
                 }
             } else {
-                each([&](int t, float x) { visit(t, x, value_bin(x, mn, scale)); });
+                each([&](int t, float x) {
+                    const int bin = value_bin(x, scale, bias);
+                    before += (t < c0 && bin > vb) ? 1u : 0u;
+                    if (bin == vb) cand[atomicAdd(&sm.ncand, 1)] = ((uint64_t)order_key(x) << 32) | (uint32_t)~(uint32_t)t;
+                });
             }
             __syncthreads();
-            // rank every candidate by (key desc, position asc); the (need-1)-th is the cut
+            // rank every candidate; the one with need-1 ahead of it is the cut
             for (int j = tid; j < cnt; j += kThreads) {
-                const uint32_t kj = ckey[j];
-                const int pj = cpos[j];
+                const uint64_t cj = cand[j];
                 int rank = 0;
-#pragma unroll 8
-                for (int o = 0; o < cnt; ++o) {
-                    const uint32_t ko = ckey[o];
-                    rank += ko > kj || (ko == kj && cpos[o] < pj);
+                int o = 0;
+                for (; o + 8 <= cnt; o += 8) {
+                    const u32x4 *p4 = reinterpret_cast<const u32x4 *>(cand + o);
+                    u32x4 x[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) x[v] = p4[v];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        rank += ((uint64_t)x[v][1] << 32 | x[v][0]) > cj;
+                        rank += ((uint64_t)x[v][3] << 32 | x[v][2]) > cj;
+                    }
                 }
+                for (; o < cnt; ++o) rank += cand[o] > cj;
                 if (rank == need - 1) {
-                    sm.kstar = kj;
-                    sm.pstar = pj;
+                    sm.kstar = (uint32_t)(cj >> 32);
+                    sm.pstar = (int)~(uint32_t)cj;
                 }
             }
             __syncthreads();
             kstar = sm.kstar;
             pstar = sm.pstar;
+            const uint64_t cstar = ((uint64_t)kstar << 32) | (uint32_t)~(uint32_t)pstar;
             for (int j = tid; j < cnt; j += kThreads) {
-                const uint32_t kj = ckey[j];
-                before += cpos[j] < c0 && (kj > kstar || (kj == kstar && cpos[j] <= pstar));
+                const uint64_t cj = cand[j];
+                before += ((int)~(uint32_t)cj < c0 && cj >= cstar) ? 1u : 0u;
             }
         } else {
-            radix_resolve(sm, ts, nvis, mn, scale, vb, need);
+            radix_resolve(sm, ts, nvis, scale, bias, vb, need);
             kstar = sm.kstar;
             pstar = sm.pstar;
             each([&](int t, float x) {
@@ -621,88 +678,70 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
 
     // ------------------------------------------------------------------ phase M
     {
-        // this member's slice of the (head, dim-quad) outputs
+        // this member's slice of the (head, dim-quad) outputs; each output quad is summed
+        // by a group of lpi lanes, every lane loading the O quad and the (max, sum) pair of
+        // a stride of the slots in one round trip and combining them online
         const int qdv = aa.dv / 4;
         const int n_out = kHeads * qdv;
         const int per = (n_out + f.team_size - 1) / f.team_size;
-        const int e0 = m * per, e1 = min(e0 + per, n_out);
-        float *wts = reinterpret_cast<float *>(attn_lds);  // [team_size][16] slot weights
-        __shared__ float hsum[kHeads], hmax[kHeads];
-        if (e1 > e0) {
-            const int h_lo = e0 / qdv, h_hi = (e1 - 1) / qdv;
-            // one wave per head of the slice: max over slots, weights e^(m_s - M), 1 / L
-            for (int h = h_lo + wave; h <= h_hi; h += kThreads / 64) {
-                float ms[4], ls[4];
-                float M = -INFINITY;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int sl = lane + 64 * r;
-                    ms[r] = -INFINITY;
-                    ls[r] = 0.f;
-                    if (sl < f.team_size) {
-                        const uint64_t ml = ld64_agent(reinterpret_cast<const uint64_t *>(
-                                                           f.part + ((size_t)q * f.team_size + sl) * f.slot_floats +
-                                                           kHeads * aa.dv) + h);
-                        ms[r] = lo_f(ml);
-                        ls[r] = hi_f(ml);
-                    }
-                    M = fmaxf(M, ms[r]);
-                }
-#pragma unroll
-                for (int o2 = 32; o2 >= 1; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2));
-                float L = 0.f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int sl = lane + 64 * r;
-                    const float wgt = (ms[r] == -INFINITY || M == -INFINITY) ? 0.f : exp2f(ms[r] - M);
-                    if (sl < f.team_size) wts[sl * kHeads + h] = wgt;
-                    L += wgt * ls[r];
-                }
-#pragma unroll
-                for (int o2 = 32; o2 >= 1; o2 >>= 1) L += __shfl_xor(L, o2);
-                if (lane == 0) {
-                    hmax[h] = M;
-                    hsum[h] = L;
-                }
-            }
-        }
-        __syncthreads();
-        if (e1 > e0) {
-            // lanes per output quad (a power of two), each summing a stride of the slots
-            const int items = e1 - e0;
+        const int e0 = m * per;
+        const int items = max(0, min(e0 + per, n_out) - e0);
+        if (items > 0) {
             int lpi = 1;
             while (lpi * 2 * items <= kThreads && lpi * 2 <= 64) lpi *= 2;
             const int item = tid / lpi, sub = tid % lpi;
+            const bool act = item < items;
+            const int e = e0 + (act ? item : 0);
+            const int h = e / qdv;
+            const int d = 4 * (e - h * qdv);
+            const float *mlp = f.part + (size_t)q * f.team_size * f.slot_floats + kHeads * aa.dv + 2 * h;
+            constexpr int kU = 8;
             f32x4 O = {0.f, 0.f, 0.f, 0.f};
-            int h = 0, d = 0;
-            if (item < items) {
-                const int e = e0 + item;
-                h = e / qdv;
-                d = 4 * (e - h * qdv);
-                u32x4 o[8];
-                for (int s0 = sub; s0 < f.team_size; s0 += 8 * lpi) {
+            float M = -INFINITY, L = 0.f;
+            for (int s0 = sub; s0 < f.team_size; s0 += kU * lpi) {
+                u32x4 o[kU];
+                uint64_t ml[kU];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const int sl = s0 + u * lpi;
-                        o[u] = sl < f.team_size
-                                   ? ld128_agent(part_r, (uint32_t)(sl * slot_bytes + (h * aa.dv + d) * 4))
-                                   : u32x4{0u, 0u, 0u, 0u};
-                    }
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const int sl = s0 + u * lpi;
-                        if (sl < f.team_size) O += wts[sl * kHeads + h] * __builtin_bit_cast(f32x4, o[u]);
-                    }
+                for (int u = 0; u < kU; ++u) {
+                    const int sl = s0 + u * lpi;
+                    const bool ok = act && sl < f.team_size;
+                    o[u] = ok ? ld128_agent(part_r, (uint32_t)(sl * slot_bytes + (h * aa.dv + d) * 4))
+                              : u32x4{0u, 0u, 0u, 0u};
+                    ml[u] = ok ? ld64_agent(reinterpret_cast<const uint64_t *>(mlp + (size_t)sl * f.slot_floats))
+                               : pack2(-INFINITY, 0.f);
                 }
+                float Mn = M;
+#pragma unroll
+                for (int u = 0; u < kU; ++u) Mn = fmaxf(Mn, lo_f(ml[u]));
+                const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
+                O *= a;
+                L *= a;
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const float ms = lo_f(ml[u]);
+                    const float w = ms == -INFINITY ? 0.f : exp2f(ms - Mn);
+                    O += w * __builtin_bit_cast(f32x4, o[u]);
+                    L += w * hi_f(ml[u]);
+                }
+                M = Mn;
             }
             for (int o2 = lpi / 2; o2 >= 1; o2 >>= 1) {
+                const float M2 = __shfl_xor(M, o2);
+                const float L2 = __shfl_xor(L, o2);
+                f32x4 O2;
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) O[e4] += __shfl_xor(O[e4], o2);
+                for (int e4 = 0; e4 < 4; ++e4) O2[e4] = __shfl_xor(O[e4], o2);
+                const float Mn = fmaxf(M, M2);
+                const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
+                const float bb = M2 == -INFINITY ? 0.f : exp2f(M2 - Mn);
+                O = a * O + bb * O2;
+                L = a * L + bb * L2;
+                M = Mn;
             }
-            if (item < items && sub == 0) {
+            if (act && sub == 0) {
                 uint16_t *dst = aa.out + ((size_t)q * kHeads + h) * aa.dv + d;
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) dst[e4] = attn_finish(O[e4], hmax[h], hsum[h], aa.sink, h);
+                for (int e4 = 0; e4 < 4; ++e4) dst[e4] = attn_finish(O[e4], M, L, aa.sink, h);
             }
         }
     }
