@@ -61,17 +61,78 @@ def step_bytes(sp: dict) -> dict:
     return {"step": step, "indexer": indexer, "topk": topk, "attention": attn}
 
 
-def traffic_for(kernel: str, src: str):
+def source_sha(srcs) -> str:
+    h = hashlib.sha256()
+    for src in srcs:
+        h.update(open(src, "rb").read())
+    return h.hexdigest()
+
+
+def traffic_for(kernel: str, srcs):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
-    kernel source changed since the counters were taken."""
+    kernel's sources changed since the counters were taken."""
     path = os.path.join(PROFILES, f"{kernel}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != source_sha(srcs):
         return None
     return rec.get("bytes_per_launch")
+
+
+def kernel_sources(ksrc: str):
+    csrc = os.path.join(ROOT, "lightning_indexer_top_amd", "csrc")
+    return [os.path.join(csrc, f) for f in (ksrc, "tile_ops.h", "lit_internal.h")]
+
+
+def read_counters(path: str, counter: str) -> dict:
+    """Per-kernel-name lists of one counter's per-dispatch values from a rocprofv3
+    counter_collection.csv (a file, or a directory searched for one)."""
+    import csv
+    if os.path.isdir(path):
+        found = [os.path.join(d, f) for d, _, fs in os.walk(path) for f in fs
+                 if f.endswith("counter_collection.csv")]
+        if not found:
+            raise SystemExit(f"no counter_collection.csv under {path}")
+        path = found[0]
+    out: dict = {}
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic_record(fetch_path: str, write_path: str, kernel: str, ksrc: str, copy_mb: int, cmd: str) -> dict:
+    """HBM bytes of one launch of `kernel` from FETCH_SIZE and WRITE_SIZE runs, each scaled
+    by what the same counter reads for the plain device copy of copy_mb MiB in the run."""
+    fetch, write = read_counters(fetch_path, "FETCH_SIZE"), read_counters(write_path, "WRITE_SIZE")
+
+    def pick(d, key):
+        vals = [v for n, vs in d.items() if key(n) for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatch matched for {kernel}")
+        return vals
+
+    def copy_vals(d):
+        # the probe copies are the largest copy dispatches of the run
+        vals = [v for n, vs in d.items() if "copy" in n.lower() for v in vs]
+        top = max(vals)
+        return [v for v in vals if v >= 0.9 * top]
+
+    kf = pick(fetch, lambda n: kernel in n)
+    kw = pick(write, lambda n: kernel in n)
+    cf, cw = copy_vals(fetch), copy_vals(write)
+    kib = copy_mb * 1024.0
+    ff = (sum(cf) / len(cf)) / kib
+    wf = (sum(cw) / len(cw)) / kib
+    f_kib = sum(kf) / len(kf)
+    w_kib = sum(kw) / len(kw)
+    return {"kernel": kernel, "source_sha256": source_sha(kernel_sources(ksrc)),
+            "dispatches": {"fetch": len(kf), "write": len(kw)},
+            "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
+            "copy_probe_mib": copy_mb, "copy_fetch_factor": round(ff, 4), "copy_write_factor": round(wf, 4),
+            "bytes_per_launch": int(round((f_kib / ff + w_kib / wf) * 1024)), "command": cmd}
 
 
 def cpu_baseline(name: str, budget_s: float) -> dict:
@@ -104,7 +165,22 @@ def main() -> int:
     ap.add_argument("--instances", type=int, default=0, help="input instances (0 = cold-cache rule)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after the timed region, copy this many MiB three times (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH", "WRITE"),
+                    help="write profiles/<kernel>_traffic.json from rocprofv3 FETCH_SIZE / WRITE_SIZE "
+                         "counter runs of this script with --copy-probe-mb, then exit (no GPU)")
+    ap.add_argument("--traffic-cmd", default="", help="the profiled command, recorded with --traffic-from")
     args = ap.parse_args()
+    if args.traffic_from:
+        rec = traffic_record(args.traffic_from[0], args.traffic_from[1], "fused_decode_kernel",
+                             "fused_decode.hip", args.copy_probe_mb or 256, args.traffic_cmd)
+        path = os.path.join(PROFILES, "fused_decode_kernel_traffic.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has "
               "no multi-GPU path.", file=sys.stderr)
@@ -236,12 +312,22 @@ def main() -> int:
         dom_us = stages_us[dom]
         dom_bytes = sb[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    src = os.path.join(ROOT, "lightning_indexer_top_amd", "csrc", ksrc)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_for(kname.split("+")[0], src),
+                "traffic": traffic_for(kname.split("+")[0], kernel_sources(ksrc)),
                 "kernel": kname, "stage": dom, "bytes_per_launch": dom_bytes,
                 "avg_launch_us": round(dom_us, 3)}
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * 2 ** 20 // 4
+        src_t = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst_t = torch.empty_like(src_t)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 3 copies of {args.copy_probe_mb} MiB")
+        del src_t, dst_t
 
     cpu = None
     if not args.no_cpu_baseline:
