@@ -661,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(&ow[(w * kHeads + h) * aa.dv + d]);
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(&ow[(w * kHeads + h) * attn_ow_ld(aa.dv) + d]);
                 O += hf[w * kHeads + h] * x;
             }
             st128_agent(part_r, my_off + (uint32_t)(h * aa.dv + d) * 4u, __builtin_bit_cast(u32x4, O));

@@ -223,7 +223,13 @@ __device__ inline void attn_wave_total(AttnState<D> &st) {
     st.l += __shfl_xor(st.l, 32);
 }
 
-// A wave's finished state into LDS: ow [nwaves][16][dv] floats, wm / wl [nwaves][16].
+// Row stride (floats) of the wave states in LDS: dv plus 4, so that the 16 heads of a wave
+// start in different banks (dv itself is a multiple of 64 floats for the usual head sizes,
+// which would put every head row in the same bank).
+__host__ __device__ constexpr int attn_ow_ld(int dv) { return dv + 4; }
+
+// A wave's finished state into LDS: ow [nwaves][16][attn_ow_ld(dv)] floats, wm / wl
+// [nwaves][16].  Lane (g, c) holds dims 16dt+4g..16dt+4g+3 of head c: one 16-byte store per dt.
 template <int D>
 __device__ inline void attn_wave_publish(AttnState<D> &st, float *ow, float *wm, float *wl, int wave,
                                          int dv, int g, int c) {
@@ -232,15 +238,13 @@ __device__ inline void attn_wave_publish(AttnState<D> &st, float *ow, float *wm,
         wm[wave * 16 + c] = st.m;
         wl[wave * 16 + c] = st.l;
     }
+    float *row = ow + (wave * 16 + c) * attn_ow_ld(dv) + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-        if (16 * dt < dv)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ow[(wave * 16 + c) * dv + 16 * dt + 4 * g + r] = st.o[dt][r];
+        if (16 * dt < dv) *reinterpret_cast<f32x4 *>(row + 16 * dt) = st.o[dt];
 }
 
-// Log-sum-exp combination of `n` published states for head h, dim d: unnormalised O,
-// the common max M (log2 domain) and the normaliser L at that max.
+// Combine the n waves' states of head h at dim d (log-sum-exp).
 __device__ inline void attn_combine(const float *ow, const float *wm, const float *wl, int n, int h, int d,
                                     int dv, float &O, float &M, float &L) {
     M = -INFINITY;
@@ -251,7 +255,7 @@ __device__ inline void attn_combine(const float *ow, const float *wm, const floa
     for (int w = 0; w < n; ++w) {
         const float mw = wm[w * 16 + h];
         const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-        O += f * ow[(w * 16 + h) * dv + d];
+        O += f * ow[(w * 16 + h) * attn_ow_ld(dv) + d];
         L += f * wl[w * 16 + h];
     }
 }
