@@ -115,6 +115,11 @@ struct AttnState {
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
 template <int D>
 __device__ inline void attn_init(AttnState<D> &st) {
     st.m = -INFINITY;
@@ -200,16 +205,18 @@ __device__ inline void attn_tile_compute(AttnState<D> &st, const bf16x8 (&qb)[D 
     for (int dt = 0; dt < NT; ++dt) st.o[dt] *= alpha;
 
     wave_lds_sync();  // the rows this wave wrote are readable by its other lanes
+    // V^T operand by DS_READ_B64_TR_B16.  Within a 16-lane group, output lane i's element k
+    // is element i&3 of the 8 bytes addressed by lane 4k + (i>>2) (probed on gfx950).  So lane
+    // (g, c) addresses row 4g + (c>>2), dims 16dt + 4(c&3), and receives dim 16dt + c of rows
+    // 4g..4g+3; a second read 16 rows down gives rows 16+4g..16+4g+3.
+    lds_v4s *v0 = (lds_v4s *)((lds_u16 *)tile + (4 * g + (c >> 2)) * LD + 4 * (c & 3));
+    lds_v4s *v1 = (lds_v4s *)((lds_u16 *)tile + (16 + 4 * g + (c >> 2)) * LD + 4 * (c & 3));
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt) {
         if (dt < ndt) {
-            bf16x8 va;
-            const uint16_t *col = tile + 16 * dt + c;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                va[m] = __builtin_bit_cast(__bf16, col[(4 * g + m) * LD]);
-                va[4 + m] = __builtin_bit_cast(__bf16, col[(16 + 4 * g + m) * LD]);
-            }
+            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v0 + 4 * dt);
+            const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v1 + 4 * dt);
+            const bf16x8 va = __builtin_bit_cast(bf16x8, (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
             st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.o[dt], 0, 0, 0);
         }
     }
