@@ -178,14 +178,16 @@ size_t lit_sparse_attn_workspace_bytes(int B, int S, int H, int dv, int W, int K
  * aligned, contents irrelevant.
  *
  * State (fused form only): lit_sparse_step_state_bytes() bytes, 256-byte
- * aligned, ZERO-FILLED ONCE before first use.  It holds the teams' counters and
- * histograms, which every fused call leaves at zero again, so one state buffer
- * can serve calls of any shape on one stream.  With state == NULL (or too
- * small) the step uses the multi-kernel form.  State bytes [0, 4) are a sticky
- * error word: nonzero means a fused call's team did not assemble within its
- * bounded wait (its workgroups were not all resident, e.g. another kernel held
- * compute units); that call's outputs are undefined.  Zero the state to clear
- * it.  Calls that share a workspace or a state must be ordered on one stream.
+ * aligned, ZERO-FILLED ONCE before first use and afterwards passed only to
+ * fused calls.  It holds, per query, a launch count and the teams' barrier
+ * flags, which every fused call leaves consistent for the next, so one state
+ * buffer serves calls of any shape on one stream (its size must cover the
+ * largest).  With state == NULL (or too small) the step uses the multi-kernel
+ * form.  State bytes [0, 4) are a sticky error word: nonzero means a fused
+ * call's team did not assemble within its bounded wait (its workgroups were not
+ * all resident, e.g. another kernel held compute units); that call's outputs
+ * are undefined.  Zero the whole state to clear it.  Calls that share a
+ * workspace or a state must be ordered on one stream.
  */
 #define LIT_STEP_UNFUSED 1
 typedef struct lit_step_args {

@@ -12,33 +12,30 @@
 // of the device), and the teams are laid out XCD-major so that a team shares one XCD
 // where the sizes allow.  Member m of a team owns key chunk [m*chunk, (m+1)*chunk) of
 // its query's visible rows and keeps that chunk's scores in LDS.
-//   A. Every member scores its chunk (MX-scaled fp8 MFMA, as in indexer.hip) and, when
-//      the query sees more rows than it keeps, adds a 4096-bin histogram of the top 12
-//      bits of the scores' order keys to the team histogram.
-//   -- team barrier A --
-//   B. Every member reads the team histogram and finds the bin b1 where the count from
-//      the top reaches k.  It publishes how many of its scores lie above b1 and its
-//      scores inside b1 (the candidates, in position order).
-//   -- team barrier B --
-//   S. Every member reads all candidates and finds, on its own, the exact k-th
-//      (key, position): a 4096-bin histogram of the next 12 key bits, then ranks among
-//      the few left (or, for heavy ties, the last 8 bits and a position scan).  From
-//      the published counts it also knows where its picks start in the output list.
+//   A. Every member scores its chunk (MX-scaled fp8 MFMA, as in indexer.hip).  When the
+//      query sees more rows than it keeps, it publishes the chunk's scores to the team
+//      buffer and its chunk's max / min score keys in its barrier-A flag.
+//   -- team barrier A (skipped when every visible row is kept) --
+//   S. Every member loads all of the team's scores into registers and finds, on its own,
+//      the exact k-th (key, position): a 4096-bin value histogram between the team's min
+//      and max, the bin where the count from the top reaches k, then a rank among the few
+//      scores of that bin (heavy ties: three radix levels over the order keys and a
+//      position scan).  It also counts the picks before its chunk, i.e. where its picks
+//      start in the output list.  Every member reaches the same cut from the same data.
 //   D. Every member writes its picks (ascending) to the top-k list, gathers those rows
-//      and its share of the window rows, and runs the attention tiles (as in
-//      attention.hip) into its partial state.
+//      and its share of the window rows, runs the attention tiles (as in attention.hip)
+//      and publishes its partial state.
 //   -- team barrier C --
 //   M. Members merge the team's partial states (log-sum-exp) for a slice of the
-//      (head, dim) outputs, add the sink, and write bf16.  The last member to finish
-//      zeroes the team's control words.
-// When the query keeps every visible row, barriers A and B and the histogram are
-// skipped.
+//      (head, dim) outputs, add the sink, and write bf16.
 //
-// Cross-workgroup data (histogram, candidates, counts, partial states, counters) moves
-// through agent-scope atomic stores and loads, which are performed at the device's
-// coherence point; a workgroup waits for its own stores to complete (vmcnt) before it
-// bumps a barrier counter.  No agent-scope fence is used: on this device such a fence
-// writes back or invalidates a whole XCD's L2.
+// Cross-workgroup data moves through agent-scope relaxed atomic loads and stores and
+// coherent (sc1) 16-byte buffer loads and stores.  The barriers are flag arrays, not
+// counters: a member waits for its own stores to complete (vmcnt) and then writes a
+// 16-byte flag tagged with the query index and the query's launch count, kept in the
+// state buffer; waiters poll one flag per lane.  No two workgroups update one address
+// and no agent-scope fence is used (on this device such a fence writes back or
+// invalidates a whole XCD's L2).
 //
 // Every wait is a bounded spin: if a team does not assemble in time (workgroups not
 // co-resident, e.g. another kernel holding CUs), the waiter sets the sticky error word
@@ -58,7 +55,12 @@ constexpr int kBins = 4096;    // radix-level histogram size (12-bit digits)
 constexpr int kVBins = 4096;   // value bins of the first selection level (+ one spill bin)
 constexpr int kCandCap = 2048;  // candidates held in LDS (more are re-read from memory)
 
-enum : int { kBarA = 0, kBarB = 1, kBarC = 2, kDone = 3, kKeyMax = 4, kKeyMinC = 5, kCtrlWords = 8 };
+// Per-query region of the state buffer, at a fixed stride whatever the team size: the
+// query's launch counter, then one 16-byte flag slot per member for each of the two
+// team barriers (A: scores published, C: partial state published).
+constexpr int kTeamMax = kThreads;
+constexpr size_t kQCtrl = 256;
+constexpr size_t kQState = kQCtrl + 2 * (size_t)kTeamMax * 16;
 
 __device__ inline uint32_t ld_agent(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -80,28 +82,6 @@ __device__ inline void stores_done() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt(7), lgkmcnt(15)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// Arrive at a team barrier once this workgroup's stores are complete.
-__device__ inline void team_arrive(uint32_t *ctr) {
-    stores_done();
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait until the counter reaches `target` (bounded).
-__device__ inline void team_wait(uint32_t *ctr, uint32_t target, uint32_t limit, uint32_t *err) {
-    if (threadIdx.x == 0) {
-        uint32_t n = 0;
-        while (ld_agent(ctr) < target) {
-            if (++n > limit) {
-                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-    }
-    __syncthreads();
 }
 
 // Bin search from the top over `nbins` LDS counters (256, 1024 or 4096): the bin where
@@ -184,6 +164,37 @@ __device__ inline u32x4 ld128_agent(rsrc_t r, uint32_t byte_off) {
 }
 __device__ inline void st128_agent(rsrc_t r, uint32_t byte_off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, kSc1);
+}
+
+// Team barrier by flags.  A member publishes its slot {x, y, q, epoch} once every one of
+// its earlier stores has completed; a waiter polls slot j on lane j until the slot carries
+// this launch's tag.  The tag holds the query index as well as the query's launch count,
+// so a slot left by an earlier launch (of any shape) never matches.  Waits are bounded:
+// past `limit` polls the sticky error word is set and the wait gives up.
+__device__ inline void team_flag(const rsrc_t &slots, int m, uint32_t x, uint32_t y, uint32_t q, uint32_t ep) {
+    stores_done();
+    __syncthreads();
+    if (threadIdx.x == 0) st128_agent(slots, (uint32_t)m * 16u, u32x4{x, y, q, ep});
+}
+
+__device__ inline u32x4 team_poll(const rsrc_t &slots, int team, uint32_t q, uint32_t ep, uint32_t limit,
+                                  uint32_t *err) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    const int j = threadIdx.x;
+    if (j < team) {
+        uint32_t n = 0;
+        for (;;) {
+            v = ld128_agent(slots, (uint32_t)j * 16u);
+            if (v[2] == q && v[3] == ep) break;
+            if (++n > limit) {
+                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    __syncthreads();
+    return v;
 }
 __device__ inline float key_float(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
@@ -307,7 +318,11 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     const int c0 = m * f.chunk;
     const int c1 = min(c0 + f.chunk, nvis);
     const int n = max(0, c1 - c0);
-    uint32_t *ctrl = f.ctrl + (size_t)q * kCtrlWords;
+    char *qstate = f.qstate + (size_t)q * kQState;
+    uint32_t *epoch = reinterpret_cast<uint32_t *>(qstate);
+    const uint32_t ep = ld_agent(epoch) + 1u;  // this launch's tag
+    const rsrc_t slot_a = make_rsrc(qstate + kQCtrl, kTeamMax * 16u);
+    const rsrc_t slot_c = make_rsrc(qstate + kQCtrl + kTeamMax * 16, kTeamMax * 16u);
     float *ts = f.scores + (size_t)q * f.ld;  // the team's scores
     const rsrc_t ts_r = make_rsrc(ts, (uint32_t)f.ld * 4u);
     float *sc = dyn;
@@ -362,15 +377,12 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             sm.mm[wave][1] = kminc;
         }
         __syncthreads();
-        if (tid == 0) {
-            uint32_t a = 0u, cmin = 0u;
-            for (int w = 0; w < kThreads / 64; ++w) {
-                a = max(a, sm.mm[w][0]);
-                cmin = max(cmin, sm.mm[w][1]);
-            }
-            st64_agent(f.minmax + (size_t)q * f.team_size + m, (uint64_t)a | ((uint64_t)cmin << 32));
+        uint32_t a = 0u, cmin = 0u;
+        for (int w = 0; w < kThreads / 64; ++w) {
+            a = max(a, sm.mm[w][0]);
+            cmin = max(cmin, sm.mm[w][1]);
         }
-        team_arrive(&ctrl[kBarA]);
+        team_flag(slot_a, m, a, cmin, (uint32_t)q, ep);  // barrier A: scores published
     }
 
     // window rows of this member, prefetched by waves 3, 2, ... (tile w -> wave 3 - w)
@@ -392,7 +404,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     int pstar = 0x7fffffff;
     int off = c0;         // where this member's picks start in the output list
     if (select) {
-        team_wait(&ctrl[kBarA], (uint32_t)f.team_size, f.spin_limit, f.err);
+        // barrier A; the members' slots also carry their chunks' max / min keys
+        const u32x4 sa = team_poll(slot_a, f.team_size, (uint32_t)q, ep, f.spin_limit, f.err);
         const int nquad = (nvis + 3) / 4;
         // cached form: thread t keeps the score quads t + kThreads*r (positions 4(t + kThreads*r) + e)
         const bool cached = nquad <= kCacheQ * kThreads;
@@ -416,12 +429,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         };
         // team max / min from the members' slots
         {
-            uint32_t a = 0u, cmin = 0u;
-            for (int j = tid; j < f.team_size; j += kThreads) {
-                const uint64_t v = ld64_agent(f.minmax + (size_t)q * f.team_size + j);
-                a = max(a, (uint32_t)v);
-                cmin = max(cmin, (uint32_t)(v >> 32));
-            }
+            uint32_t a = tid < f.team_size ? sa[0] : 0u, cmin = tid < f.team_size ? sa[1] : 0u;
 #pragma unroll
             for (int o2 = 32; o2 >= 1; o2 >>= 1) {
                 a = max(a, (uint32_t)__shfl_xor((int)a, o2));
@@ -673,8 +681,10 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                               __float_as_uint(hl[h + 1])});
         }
     }
-    team_arrive(&ctrl[kBarC]);
-    team_wait(&ctrl[kBarC], (uint32_t)f.team_size, f.spin_limit, f.err);
+    team_flag(slot_c, m, 0u, 0u, (uint32_t)q, ep);  // barrier C: partial state published
+    team_poll(slot_c, f.team_size, (uint32_t)q, ep, f.spin_limit, f.err);
+    // every member has read the launch count (it passed barrier C): advance it
+    if (m == 0 && tid == 0) st_agent(epoch, ep);
 
     // ------------------------------------------------------------------ phase M
     {
@@ -744,13 +754,6 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                 for (int e4 = 0; e4 < 4; ++e4) dst[e4] = attn_finish(O[e4], M, L, aa.sink, h);
             }
         }
-    }
-    // the last member to finish zeroes the team's control words for the next launch
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&ctrl[kDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == (uint32_t)f.team_size - 1u)
-            for (int j = 0; j < kCtrlWords; ++j) st_agent(&ctrl[j], 0u);
     }
 }
 
@@ -848,29 +851,27 @@ FusedPlan plan_fused(int B, int S, int start_pos, int ratio, int Hi, int Di, int
 }
 
 size_t fused_state_bytes(const FusedPlan &p) {
-    // error word + per-team control words
-    return 256 + (size_t)p.n_teams * kCtrlWords * 4;
+    // error word, then one fixed-size region per query
+    return 256 + (size_t)p.n_teams * kQState;
 }
 
 static int slot_floats(int dv) { return (kHeads * dv + 2 * kHeads + 63) / 64 * 64; }  // 16-byte multiple
 
 size_t fused_ws_bytes(const FusedPlan &p, int dv) {
-    return (size_t)p.n_teams * p.team_size * 8 + 256 +                       // min / max slots
-           (size_t)p.n_teams * p.ld * 4 + 256 +                              // team scores
+    return (size_t)p.n_teams * p.ld * 4 + 256 +                              // team scores
            (size_t)p.n_teams * p.team_size * slot_floats(dv) * 4 + 256;      // partial states
 }
 
 hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream) {
     char *st = (char *)state;
     f.err = (uint32_t *)st;
-    f.ctrl = (uint32_t *)(st + 256);
+    f.qstate = st + 256;
     char *rest = (char *)ws;
     auto bump = [&](size_t bytes) {
         char *r = rest;
         rest += (bytes + 255) / 256 * 256;
         return r;
     };
-    f.minmax = (uint64_t *)bump((size_t)p.n_teams * p.team_size * 8);
     f.scores = (float *)bump((size_t)p.n_teams * p.ld * 4);
     f.part = (float *)bump((size_t)p.n_teams * p.team_size * slot_floats(f.aa.dv) * 4);
     f.slot_floats = slot_floats(f.aa.dv);

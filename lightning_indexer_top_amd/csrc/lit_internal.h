@@ -112,8 +112,8 @@ struct FusedArgs {
     int team_size, chunk, win_tiles, n_slots;
     long ld;              // team score array stride
     uint32_t spin_limit;
-    uint32_t *err, *ctrl;         // zero between launches
-    uint64_t *minmax;             // per member: (max key, max complemented key) of its chunk
+    uint32_t *err;                // sticky error word (state)
+    char *qstate;                 // per query: launch count and barrier flag slots (state)
     float *scores;                // per team: scores of the visible rows
     float *part;                  // per member: partial attention state
     int slot_floats;              // floats per member state
@@ -125,7 +125,7 @@ struct FusedPlan {
     size_t dyn_bytes;
 };
 FusedPlan plan_fused(int B, int S, int start_pos, int ratio, int Hi, int Di, int D, int dv, int W, int keff);
-size_t fused_state_bytes(const FusedPlan &p);  // zero between launches
+size_t fused_state_bytes(const FusedPlan &p);  // zero-filled before first use
 size_t fused_ws_bytes(const FusedPlan &p, int dv);
 hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream);
 

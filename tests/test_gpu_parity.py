@@ -309,8 +309,10 @@ def test_step_fused_matches_kernels():
 
 
 def test_step_fused_state_reuse():
-    """One state buffer for calls of several shapes (and a multi-kernel call in between):
-    the fused form leaves it zeroed, so repeated calls give identical results."""
+    """One state buffer for calls of several shapes: every fused call leaves it
+    consistent for the next (per-query launch counts, barrier flags tagged with the
+    query and its count), so repeated calls in any shape order give identical results
+    and the error word stays clear."""
     state = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda")
     outs = {}
     for rep in range(3):
@@ -325,7 +327,7 @@ def test_step_fused_state_reuse():
             else:
                 assert torch.equal(outs[name][0], idx), name
                 assert torch.equal(outs[name][1].view(torch.int16), out.view(torch.int16)), name
-    assert torch.count_nonzero(state).item() == 0
+    assert L.state_error(state) == 0
 
 
 @pytest.mark.parametrize("flags", MODES)
