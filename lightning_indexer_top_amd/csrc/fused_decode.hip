@@ -54,6 +54,7 @@ constexpr int kHeads = 16;
 constexpr int kBins = 4096;    // radix-level histogram size (12-bit digits)
 constexpr int kVBins = 4096;   // value bins of the first selection level (+ one spill bin)
 constexpr int kCandCap = 2048;  // candidates held in LDS (more are re-read from memory)
+constexpr int kCacheQ = 8;      // team score quads per thread kept in registers (and LDS)
 
 // Per-query region of the state buffer, at a fixed stride whatever the team size: the
 // query's launch counter, then one 16-byte flag slot per member for each of the two
@@ -291,12 +292,11 @@ __device__ inline void radix_resolve(FusedLds &sm, const float *ts, int nvis, fl
 template <int D, int DI, int HT>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     constexpr int LD = D + 4;
-    constexpr int kCacheQ = 8;  // score quads per thread kept in registers during selection
     __shared__ FusedLds sm;
     __shared__ __attribute__((aligned(16))) uint16_t attn_lds[4 * 32 * LD];  // rows / candidates / merge
     __shared__ float wm[4 * kHeads], wl[4 * kHeads];
     __shared__ float hf[4 * kHeads], hl[kHeads], hm[kHeads];  // per-head merge factors
-    extern __shared__ float dyn[];  // chunk scores [chunk], then picks [chunk] (ints)
+    extern __shared__ __attribute__((aligned(16))) float dyn[];  // chunk scores, picks (ints), team scores
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -327,6 +327,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     const rsrc_t ts_r = make_rsrc(ts, (uint32_t)f.ld * 4u);
     float *sc = dyn;
     int *picks = reinterpret_cast<int *>(dyn + f.chunk);
+    float *tsl = dyn + 2 * f.chunk;  // the team's scores in position order (cached form)
 
     // attention operands that do not depend on the selection: issued first
     bf16x8 qb[D / 32];
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         const u32x4 sa = team_poll(slot_a, f.team_size, (uint32_t)q, ep, f.spin_limit, f.err);
         const int nquad = (nvis + 3) / 4;
         // cached form: thread t keeps the score quads t + kThreads*r (positions 4(t + kThreads*r) + e)
-        const bool cached = nquad <= kCacheQ * kThreads;
+        const bool cached = f.cache_lds && nquad <= kCacheQ * kThreads;
         const bool full = 4 * (tid + kThreads * (kCacheQ - 1)) + 4 <= nvis;  // all 32 visible
         u32x4 vals[kCacheQ];
         if (cached) {
@@ -459,6 +460,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             if (full) {
 #pragma unroll
                 for (int r = 0; r < kCacheQ; ++r) {
+                    *reinterpret_cast<u32x4 *>(tsl + 4 * (tid + kThreads * r)) = vals[r];
                     uint32_t bb[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -471,6 +473,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             } else {
 #pragma unroll
                 for (int r = 0; r < kCacheQ; ++r) {
+                    if (tid + kThreads * r < nquad) *reinterpret_cast<u32x4 *>(tsl + 4 * (tid + kThreads * r)) = vals[r];
                     uint32_t bb[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -520,19 +523,14 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                     const uint32_t e0 = (a0 ^ b0) & 0x80008000u, e1 = (a1 ^ b1) & 0x80008000u;
                     cmask |= ((e0 >> 15) & 1u | (e0 >> 30) & 2u | (e1 >> 13) & 4u | (e1 >> 28) & 8u) << (4 * r);
                 }
-                if (cmask) {
+                if (cmask) {  // few lanes: their candidates' scores are read back from LDS
                     int ci = atomicAdd(&sm.ncand, __builtin_popcount(cmask));
-#pragma unroll
-                    for (int r = 0; r < kCacheQ; ++r) {
-                        uint32_t m4 = (cmask >> (4 * r)) & 15u;
-                        while (m4) {
-                            const int e = __builtin_ctz(m4);
-                            m4 &= m4 - 1u;
-                            const uint32_t xv = e == 0 ? vals[r][0] : e == 1 ? vals[r][1] : e == 2 ? vals[r][2] : vals[r][3];
-                            const int t = 4 * (tid + kThreads * r) + e;
-                            cand[ci++] = ((uint64_t)order_key(__uint_as_float(xv)) << 32) | (uint32_t)~(uint32_t)t;
-                        }
-                    }
+                    do {
+                        const int bit = __builtin_ctz(cmask);
+                        cmask &= cmask - 1u;
+                        const int t = 4 * (tid + kThreads * (bit >> 2)) + (bit & 3);
+                        cand[ci++] = ((uint64_t)order_key(tsl[t]) << 32) | (uint32_t)~(uint32_t)t;
+                    } while (cmask);
                 }
             } else {
                 each([&](int t, float x) {
@@ -822,12 +820,14 @@ FusedPlan plan_fused(int B, int S, int start_pos, int ratio, int Hi, int Di, int
     if ((Di != 64 && Di != 128) || Hi % 16 || Hi > 64) return p;
     const int nwin = window_width(S, start_pos, W);
     p.win_tiles = (nwin + 31) / 32;
+    p.cache_lds = T <= (long)kCacheQ * 4 * kThreads;
     int chunk = 256;
     size_t dyn = 0;
     int cap = 0;
     for (;; chunk *= 2) {
         if (chunk > 8192) return p;
-        dyn = (size_t)chunk * 2 * sizeof(float);  // chunk scores + picks
+        // chunk scores + picks, and the team's scores when they fit the register cache
+        dyn = (size_t)chunk * 2 * sizeof(float) + (p.cache_lds ? (size_t)kCacheQ * 4 * kThreads * sizeof(float) : 0);
         cap = max_resident(D, Di, Hi / 16, dyn);
         const long team = (T + chunk - 1) / chunk;
         if (cap > 0 && team <= kThreads && (long)n_teams * team <= cap) {
@@ -880,6 +880,7 @@ hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, 
     f.win_tiles = p.win_tiles;
     f.n_slots = p.n_slots;
     f.ld = p.ld;
+    f.cache_lds = p.cache_lds;
     switch (f.aa.D) {
         case 64: return launch_fused_d<64>(f, p.grid, p.dyn_bytes, stream);
         case 128: return launch_fused_d<128>(f, p.grid, p.dyn_bytes, stream);

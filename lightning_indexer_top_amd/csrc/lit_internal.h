@@ -117,10 +117,12 @@ struct FusedArgs {
     float *scores;                // per team: scores of the visible rows
     float *part;                  // per member: partial attention state
     int slot_floats;              // floats per member state
+    bool cache_lds;               // the team's scores are kept in LDS during selection
 };
 struct FusedPlan {
     bool ok;
     int n_teams, team_size, chunk, win_tiles, n_slots, grid;
+    bool cache_lds;
     long ld;
     size_t dyn_bytes;
 };
