@@ -113,7 +113,7 @@ __device__ inline void find_bin(const uint32_t *hist, int nbins, int need, uint3
 #pragma unroll
     for (int j = 0; j < 16; ++j) mine += cnt[j];
     uint32_t total;
-    const uint32_t incl = wg_scan(mine, wsum, &total);
+    const uint32_t incl = wg_scan<kThreads / 64>(mine, wsum, &total);
     int above = (int)(incl - mine);
     if (above < need && need <= (int)incl) {
         int found = 0, fa = 0;
@@ -138,6 +138,7 @@ struct FusedLds {
     uint32_t wsum[kThreads / 64];
     float fred[kThreads / 64];
     int bin, above, ncand, npick, overflow;
+    int wcnt[kThreads / 64];
     uint32_t kstar;
     int pstar;
     uint32_t mm[kThreads / 64][2];
@@ -274,7 +275,7 @@ __device__ inline void radix_resolve(FusedLds &sm, const float *ts, int nvis, fl
         eq += in_bin(v) && order_key(v) == prefix;
     }
     uint32_t total;
-    const uint32_t incl = wg_scan(eq, sm.wsum, &total);
+    const uint32_t incl = wg_scan<kThreads / 64>(eq, sm.wsum, &total);
     int before = (int)(incl - eq);
     if (before < need && need <= (int)incl) {
         for (int t = t0; t < t1; ++t) {
@@ -342,12 +343,9 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 kb[u] = load_idx_keys<DI>(ia, (size_t)b * ia.T_cap + min(base + 16 * u + c, nvis - 1), g);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float s = idx_tile_score<DI, HT>(qr, kb[u]);
-                const int t = base + 16 * u + c;
-                if (g == 0 && t < c1) sc[t - c0] = s;
-            }
+            const float s = idx_score4<DI, HT>(qr, kb, g);
+            const int t = base + 16 * g + c;
+            if (t < c1) sc[t - c0] = s;
         }
     }
     __syncthreads();
@@ -399,6 +397,14 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         attn_tile_load<D>(wrows, s0 >= 0 ? aa.win_kv + ((size_t)b * aa.R + s0) * D : nullptr,
                           s1 >= 0 ? aa.win_kv + ((size_t)b * aa.R + s1) * D : nullptr, g);
     }
+
+    // Attention list: positions of this chunk's rows to attend.  With a cut it holds the
+    // chunk's scores in bins >= the cut's bin (sure picks and candidates, ascending); the
+    // candidates that miss the cut are masked when their tile is computed.
+    int *al = picks;
+    int na = 0;
+    AttnRows<D> pre;  // this wave's first tile of listed rows, requested during selection
+    bool have_pre = false;
 
     // ------------------------------------------------------------- phase S
     uint32_t kstar = 0u;  // a pick is key > kstar, or key == kstar with position <= pstar
@@ -494,8 +500,35 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         const int vb = sm.bin;
         const int need = f.keff - sm.above;
         const int cnt = (int)sm.hist[vb];
-        // candidates as (key << 32 | ~position): larger means ahead in (key desc, position asc)
-        uint64_t *cand = reinterpret_cast<uint64_t *>(attn_lds);
+        // the attention list, in position order (wave counts summed in wave order)
+        for (int j = 0; j * kThreads < n; ++j) {
+            const int t = tid + kThreads * j;
+            const bool in = t < n && value_bin(sc[t], scale, bias) >= vb;
+            const uint64_t bal = __ballot(in);
+            if (lane == 0) sm.wcnt[wave] = (int)__popcll(bal);
+            __syncthreads();
+            int base = na, tot = 0;
+#pragma unroll
+            for (int w = 0; w < kThreads / 64; ++w) {
+                base += w < wave ? sm.wcnt[w] : 0;
+                tot += sm.wcnt[w];
+            }
+            if (in) al[base + (int)__popcll(bal & ((1ull << lane) - 1ull))] = c0 + t;
+            na += tot;
+            __syncthreads();
+        }
+        // each wave's first tile of listed rows is requested now, so that the gather
+        // overlaps the rest of the selection (waves holding window rows take theirs later)
+        if (win_w >= my_win && 32 * wave < na) {
+            const int p0 = 32 * wave + c, p1 = p0 + 16;
+            attn_tile_load<D>(pre, p0 < na ? aa.comp_kv + ((size_t)b * aa.T_cap + al[p0]) * D : nullptr,
+                              p1 < na ? aa.comp_kv + ((size_t)b * aa.T_cap + al[p1]) * D : nullptr, g);
+            have_pre = true;
+        }
+        asm volatile("" ::: "memory");  // issue those loads here, not where they are used
+        // candidates as (key << 32 | ~position): larger means ahead in (key desc, position asc);
+        // they take the histogram's place, which is no longer read
+        uint64_t *cand = reinterpret_cast<uint64_t *>(sm.hist);
         if (tid == 0) {
             sm.kstar = 0u;
             sm.pstar = 0x7fffffff;
@@ -593,12 +626,12 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             mine += !select || k > kstar || (k == kstar && c0 + t <= pstar);
         }
         uint32_t total;
-        const uint32_t incl = wg_scan(mine, sm.wsum, &total);
+        const uint32_t incl = wg_scan<kThreads / 64>(mine, sm.wsum, &total);
         int o = (int)(incl - mine);
         for (int t = t0; t < t1; ++t) {
             const uint32_t k = order_key(sc[t]);
             if (!select || k > kstar || (k == kstar && c0 + t <= pstar)) {
-                picks[o] = c0 + t;
+                if (!select) picks[o] = c0 + t;  // with a cut the attention list is already built
                 if (off + o < f.keff) idx_row[off + o] = c0 + t;
                 ++o;
             }
@@ -614,8 +647,15 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     {
         const float sl2 = aa.scale * kLog2e;
         uint16_t *tile = attn_lds + wave * 32 * LD;
-        const int npick = sm.npick;
-        const int pick_tiles = (npick + 31) / 32;
+        if (!select) na = sm.npick;
+        const int pick_tiles = (na + 31) / 32;
+        auto is_pick = [&](int p) {
+            if (p >= na) return false;
+            if (!select) return true;
+            const int pos = al[p];
+            const uint32_t k = order_key(sc[pos - c0]);
+            return k > kstar || (k == kstar && pos <= pstar);
+        };
         AttnState<D> st;
         attn_init<D>(st);
         if (win_w < my_win) attn_tile_compute<D>(st, qb, wrows, tile, aa.dv / 16, sl2, g, c);
@@ -633,8 +673,13 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         for (int tt = wave; tt < pick_tiles; tt += 4) {
             const int p0 = 32 * tt + c, p1 = 32 * tt + 16 + c;
             AttnRows<D> rows;
-            attn_tile_load<D>(rows, p0 < npick ? aa.comp_kv + ((size_t)b * aa.T_cap + picks[p0]) * D : nullptr,
-                              p1 < npick ? aa.comp_kv + ((size_t)b * aa.T_cap + picks[p1]) * D : nullptr, g);
+            if (tt == wave && have_pre)
+                rows = pre;
+            else
+                attn_tile_load<D>(rows, p0 < na ? aa.comp_kv + ((size_t)b * aa.T_cap + al[p0]) * D : nullptr,
+                                  p1 < na ? aa.comp_kv + ((size_t)b * aa.T_cap + al[p1]) * D : nullptr, g);
+            rows.valid[0] = __ballot(is_pick(p0));
+            rows.valid[1] = __ballot(is_pick(p1));
             attn_tile_compute<D>(st, qb, rows, tile, aa.dv / 16, sl2, g, c);
         }
         __syncthreads();

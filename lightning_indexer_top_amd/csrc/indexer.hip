@@ -16,7 +16,8 @@
 // order is K order.  Di = 64 uses only the low half (K 0..63, the high half zero).
 // C comes back as lane (g, c), register r = head 4g+r, key c; the ReLU, the head
 // weights and the sum over the lane's 4 heads run in registers, and two cross-lane
-// adds finish the head sum.
+// adds finish the head sum.  Four key tiles are scored together so that their MFMAs
+// overlap and the cross-lane head sum of all four takes three exchanges.
 //
 // The key stream is the HBM-bound part at decode: every wave owns 16*U consecutive
 // keys of one sequence, issues all their loads before the first MFMA, and writes 16*U
@@ -76,17 +77,15 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_kernel(IndexerArgs
         load_idx_query<DI, HT>(qs[qq], a, bs0 + (i < a.S ? i : 0), i < a.S, g, c);
     }
 
+    static_assert(kU == 4, "idx_score4 scores four tiles");
+    const int t = t0 + 16 * g + c;  // lane group g receives tile g's scores
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        const int t = t0 + 16 * u + c;
-#pragma unroll
-        for (int qq = 0; qq < QG; ++qq) {
-            const float s = idx_tile_score<DI, HT>(qs[qq], kb[u]);
-            const int i = i0 + qq;
-            if (g == 0 && i < a.S && t < a.T) {
-                const int vis = (a.start_pos + i + 1) / a.ratio;
-                a.scores[(bs0 + i) * a.ld + t] = t < vis ? s : -INFINITY;
-            }
+    for (int qq = 0; qq < QG; ++qq) {
+        const float s = idx_score4<DI, HT>(qs[qq], kb, g);
+        const int i = i0 + qq;
+        if (i < a.S && t < a.T) {
+            const int vis = (a.start_pos + i + 1) / a.ratio;
+            a.scores[(bs0 + i) * a.ld + t] = t < vis ? s : -INFINITY;
         }
     }
 }

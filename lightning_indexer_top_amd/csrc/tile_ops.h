@@ -78,22 +78,37 @@ __device__ inline IdxKeys load_idx_keys(const IndexerArgs &a, size_t row, int g)
     return k;
 }
 
-// Score of key c of the tile for one query (every lane of the wave returns the score
-// of its column c): sum over heads of w_h * relu(q_h . k_c).
+// Scores of four 16-key tiles for one query.  All 4*HT MFMAs are issued first; each
+// lane then holds, per tile, the head-weighted ReLU sum over its 4 heads of every head
+// tile, and the sum over the four lane groups is a packed butterfly: across lanes 32
+// apart each lane keeps two tiles and sends two, across lanes 16 apart it keeps one and
+// sends one.  Lane (g, c) returns the score of key c of tile g.
 template <int DI, int HT>
-__device__ inline float idx_tile_score(const IdxQuery<DI, HT> &q, const IdxKeys &k) {
-    float part = 0.f;
+__device__ inline float idx_score4(const IdxQuery<DI, HT> &q, const IdxKeys (&k)[4], int g) {
+    f32x4 acc[4][HT];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[ht], k.b, acc, 0 /*A e4m3*/,
-                                                              0 /*B e4m3*/, 0, q.s[ht], 0, k.s);
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part += q.w[ht][r] * fmaxf(acc[r], 0.f);
+        for (int ht = 0; ht < HT; ++ht)
+            acc[u][ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                q.a[ht], k[u].b, f32x4{0.f, 0.f, 0.f, 0.f}, 0 /*A e4m3*/, 0 /*B e4m3*/, 0, q.s[ht], 0, k[u].s);
+    float part[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        part[u] = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part[u] += q.w[ht][r] * fmaxf(acc[u][ht][r], 0.f);
     }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    return part;
+    const bool hi2 = g >= 2, hi1 = g & 1;
+    float k0 = hi2 ? part[2] : part[0], k1 = hi2 ? part[3] : part[1];
+    const float s0 = hi2 ? part[0] : part[2], s1 = hi2 ? part[1] : part[3];
+    k0 += __shfl_xor(s0, 32);
+    k1 += __shfl_xor(s1, 32);
+    float keep = hi1 ? k1 : k0;
+    keep += __shfl_xor(hi1 ? k0 : k1, 16);
+    return keep;
 }
 
 // ---------------------------------------------------------------------------
@@ -297,16 +312,19 @@ __device__ inline uint32_t wave_scan(uint32_t v) {
 }
 
 // Inclusive scan over the workgroup (ascending thread id); *total gets the sum.  Every
-// thread of the workgroup must call it.  wsum needs blockDim.x / 64 entries.
+// thread of the workgroup must call it; NW = waves per workgroup (a constant, so that no
+// launch-size load -- and with it a wait on every outstanding load -- is emitted).
+// wsum needs NW entries.
+template <int NW>
 __device__ inline uint32_t wg_scan(uint32_t v, uint32_t *wsum, uint32_t *total) {
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
-    const int nw = blockDim.x >> 6;
     v = wave_scan(v);
     if (lane == 63) wsum[wid] = v;
     __syncthreads();
     uint32_t before = 0, all = 0;
-    for (int w = 0; w < nw; ++w) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
         const uint32_t x = wsum[w];
         before += w < wid ? x : 0u;
         all += x;

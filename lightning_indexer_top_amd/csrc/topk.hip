@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
             c_lo = hist[hi - 1];
         }
         uint32_t total;
-        const uint32_t incl = wg_scan((uint32_t)(c_hi + c_lo), wsum, &total);
+        const uint32_t incl = wg_scan<kThreads / 64>((uint32_t)(c_hi + c_lo), wsum, &total);
         const int above = (int)incl - c_hi - c_lo;
         if (hi >= 1) {
             if (above < remaining && remaining <= above + c_hi) {
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         }
         const uint32_t packed = (ngt << 16) | neq;
         uint32_t total;
-        const uint32_t excl = wg_scan(packed, wsum, &total) - packed;
+        const uint32_t excl = wg_scan<kThreads / 64>(packed, wsum, &total) - packed;
         int gt = base_gt + (int)(excl >> 16);
         int eq = base_eq + (int)(excl & 0xffffu);
         const int pos0 = seg * SEG + tid * ITEMS;
