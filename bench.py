@@ -143,7 +143,7 @@ def cpu_baseline(name: str, budget_s: float) -> dict:
     inp = synth.workload(name)
     log(f"[bench] oracle inputs drawn in {time.perf_counter() - t0:.1f}s")
     runs, elapsed = 0, 0.0
-    while runs == 0 or (elapsed < budget_s and runs < 8):
+    while runs == 0 or (elapsed < budget_s and runs < 64):
         t = time.perf_counter()
         oracle.step(inp)
         elapsed += time.perf_counter() - t
