@@ -68,14 +68,19 @@ def source_sha(srcs) -> str:
     return h.hexdigest()
 
 
-def traffic_for(kernel: str, srcs):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
-    kernel's sources changed since the counters were taken."""
-    path = os.path.join(PROFILES, f"{kernel}_traffic.json")
+def traffic_path(kernel: str, workload: str) -> str:
+    return os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+
+
+def traffic_for(kernel: str, workload: str, srcs):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this kernel on
+    this workload, or None when there is none or the kernel's sources changed since the
+    counters were taken."""
+    path = traffic_path(kernel, workload)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256") != source_sha(srcs):
+    if rec.get("workload") != workload or rec.get("source_sha256") != source_sha(srcs):
         return None
     return rec.get("bytes_per_launch")
 
@@ -103,7 +108,8 @@ def read_counters(path: str, counter: str) -> dict:
     return out
 
 
-def traffic_record(fetch_path: str, write_path: str, kernel: str, ksrc: str, copy_mb: int, cmd: str) -> dict:
+def traffic_record(fetch_path: str, write_path: str, kernel: str, ksrc: str, copy_mb: int, cmd: str,
+                   workload: str) -> dict:
     """HBM bytes of one launch of `kernel` from FETCH_SIZE and WRITE_SIZE runs, each scaled
     by what the same counter reads for the plain device copy of copy_mb MiB in the run."""
     fetch, write = read_counters(fetch_path, "FETCH_SIZE"), read_counters(write_path, "WRITE_SIZE")
@@ -128,7 +134,7 @@ def traffic_record(fetch_path: str, write_path: str, kernel: str, ksrc: str, cop
     wf = (sum(cw) / len(cw)) / kib
     f_kib = sum(kf) / len(kf)
     w_kib = sum(kw) / len(kw)
-    return {"kernel": kernel, "source_sha256": source_sha(kernel_sources(ksrc)),
+    return {"kernel": kernel, "workload": workload, "source_sha256": source_sha(kernel_sources(ksrc)),
             "dispatches": {"fetch": len(kf), "write": len(kw)},
             "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
             "copy_probe_mib": copy_mb, "copy_fetch_factor": round(ff, 4), "copy_write_factor": round(wf, 4),
@@ -168,14 +174,15 @@ def main() -> int:
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the timed region, copy this many MiB three times (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH", "WRITE"),
-                    help="write profiles/<kernel>_traffic.json from rocprofv3 FETCH_SIZE / WRITE_SIZE "
+                    help="write profiles/<kernel>_<workload>_traffic.json from rocprofv3 FETCH_SIZE / WRITE_SIZE "
                          "counter runs of this script with --copy-probe-mb, then exit (no GPU)")
     ap.add_argument("--traffic-cmd", default="", help="the profiled command, recorded with --traffic-from")
     args = ap.parse_args()
     if args.traffic_from:
         rec = traffic_record(args.traffic_from[0], args.traffic_from[1], "fused_decode_kernel",
-                             "fused_decode.hip", args.copy_probe_mb or 256, args.traffic_cmd)
-        path = os.path.join(PROFILES, "fused_decode_kernel_traffic.json")
+                             "fused_decode.hip", args.copy_probe_mb or 256, args.traffic_cmd,
+                             args.workload)
+        path = traffic_path("fused_decode_kernel", args.workload)
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")
@@ -314,7 +321,7 @@ def main() -> int:
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_for(kname.split("+")[0], kernel_sources(ksrc)),
+                "traffic": traffic_for(kname.split("+")[0], args.workload, kernel_sources(ksrc)),
                 "kernel": kname, "stage": dom, "bytes_per_launch": dom_bytes,
                 "avg_launch_us": round(dom_us, 3)}
 
