@@ -739,10 +739,11 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         const int per = (n_out + f.team_size - 1) / f.team_size;
         const int e0 = m * per;
         const int items = max(0, min(e0 + per, n_out) - e0);
-        if (items > 0) {
-            int lpi = 1;
-            while (lpi * 2 * items <= kThreads && lpi * 2 <= 64) lpi *= 2;
-            const int item = tid / lpi, sub = tid % lpi;
+        int lpi = 1;
+        while (lpi * 2 * items <= kThreads && lpi * 2 <= 64) lpi *= 2;
+        // rounds of kThreads / lpi items (one round unless lpi == 1 and items > kThreads)
+        for (int i0 = 0; i0 < items; i0 += kThreads / lpi) {
+            const int item = i0 + tid / lpi, sub = tid % lpi;
             const bool act = item < items;
             const int e = e0 + (act ? item : 0);
             const int h = e / qdv;

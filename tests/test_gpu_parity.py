@@ -245,6 +245,9 @@ STEP_SMALL = [
     dict(B=1, S=50, start_pos=2000, ratio=2, Hi=16, Di=64, H=16, D=128, W=128, index_topk=100),
     dict(B=2, S=1, start_pos=3000, ratio=4, Hi=64, Di=128, H=16, D=192, W=128, index_topk=300),
     dict(B=1, S=1, start_pos=2, ratio=4, Hi=16, Di=64, H=16, D=128, W=128, index_topk=64),  # T = 0
+    # one-member teams: the merge covers more output words than a workgroup has threads
+    dict(B=1, S=1, start_pos=400, ratio=2, Hi=16, Di=64, H=16, D=128, W=128, index_topk=64),
+    dict(B=2, S=1, start_pos=450, ratio=2, Hi=32, Di=128, H=16, D=256, W=64, index_topk=100),
 ]
 
 
@@ -310,7 +313,7 @@ def test_step_fused_matches_kernels():
 
 def test_step_fused_state_reuse():
     """One state buffer for calls of several shapes: every fused call leaves it
-    consistent for the next (per-query launch counts, barrier flags tagged with the
+    consistent for the next (per-query launch counts, exchange words tagged with the
     query and its count), so repeated calls in any shape order give identical results
     and the error word stays clear."""
     state = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda")
