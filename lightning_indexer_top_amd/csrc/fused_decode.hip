@@ -290,7 +290,11 @@ __device__ inline void radix_resolve(FusedLds &sm, const float *ts, int nvis, fl
     __syncthreads();
 }
 
-template <int D, int DI, int HT>
+// CACHED: the team's scores fit the per-thread register cache (and LDS).  The two forms
+// are separate kernels so that the re-reading form's loads never share a code path with
+// the cached form (a load pending on one path of a branch makes the compiler wait for
+// every load in flight where the paths join, which would stall the early row gather).
+template <int D, int DI, int HT, bool CACHED>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     constexpr int LD = D + 4;
     __shared__ FusedLds sm;
@@ -388,21 +392,31 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     const int nwin = window_width(ia.S, ia.start_pos, aa.W);
     const int my_win = m < f.win_tiles ? (f.win_tiles - 1 - m) / f.team_size + 1 : 0;
     const int win_w = 3 - wave;  // this wave's prefetched window tile, if < my_win
-    AttnRows<D> wrows;
-    if (win_w < my_win) {
-        const int j = m + win_w * f.team_size;
+    // rows of a window tile; a lane off the list reads the query's own slot instead (always
+    // attended), so that the loads need no branch
+    const int own_slot = (ia.start_pos + i) % max(aa.R, 1);
+    auto win_tile_load = [&](AttnRows<D> &rows, int j) {
         const int p0 = 32 * j + c, p1 = 32 * j + 16 + c;
         const int s0 = p0 < nwin ? window_slot(ia.S, ia.start_pos, aa.W, aa.R, i, p0) : -1;
         const int s1 = p1 < nwin ? window_slot(ia.S, ia.start_pos, aa.W, aa.R, i, p1) : -1;
-        attn_tile_load<D>(wrows, s0 >= 0 ? aa.win_kv + ((size_t)b * aa.R + s0) * D : nullptr,
-                          s1 >= 0 ? aa.win_kv + ((size_t)b * aa.R + s1) * D : nullptr, g);
-    }
+        attn_tile_load_rows<D>(rows, aa.win_kv + ((size_t)b * aa.R + (s0 >= 0 ? s0 : own_slot)) * D, s0 >= 0,
+                               aa.win_kv + ((size_t)b * aa.R + (s1 >= 0 ? s1 : own_slot)) * D, s1 >= 0, g);
+    };
+    AttnRows<D> wrows;
+    if (win_w < my_win) win_tile_load(wrows, m + win_w * f.team_size);
 
     // Attention list: positions of this chunk's rows to attend.  With a cut it holds the
     // chunk's scores in bins >= the cut's bin (sure picks and candidates, ascending); the
     // candidates that miss the cut are masked when their tile is computed.
     int *al = picks;
     int na = 0;
+    // rows of listed tile tt; a lane past the list reads the first listed row instead
+    auto pick_tile_load = [&](AttnRows<D> &rows, int tt) {
+        const int p0 = 32 * tt + c, p1 = p0 + 16;
+        const size_t rb = (size_t)b * aa.T_cap;
+        attn_tile_load_rows<D>(rows, aa.comp_kv + (rb + al[p0 < na ? p0 : 0]) * D, p0 < na,
+                               aa.comp_kv + (rb + al[p1 < na ? p1 : 0]) * D, p1 < na, g);
+    };
     AttnRows<D> pre;  // this wave's first tile of listed rows, requested during selection
     bool have_pre = false;
 
@@ -415,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         const u32x4 sa = team_poll(slot_a, f.team_size, (uint32_t)q, ep, f.spin_limit, f.err);
         const int nquad = (nvis + 3) / 4;
         // cached form: thread t keeps the score quads t + kThreads*r (positions 4(t + kThreads*r) + e)
-        const bool cached = f.cache_lds && nquad <= kCacheQ * kThreads;
+        constexpr bool cached = CACHED;  // the plan guarantees nquad <= kCacheQ * kThreads
         const bool full = 4 * (tid + kThreads * (kCacheQ - 1)) + 4 <= nvis;  // all 32 visible
         u32x4 vals[kCacheQ];
         if (cached) {
@@ -432,6 +446,9 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     if (4 * qi + e < nvis) fn(4 * qi + e, __uint_as_float(v[e]));
+                // the load is consumed under lane conditions: wait for it here, so that no
+                // load of this loop is still counted as in flight where the paths join
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             }
         };
         // team max / min from the members' slots
@@ -520,9 +537,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         // each wave's first tile of listed rows is requested now, so that the gather
         // overlaps the rest of the selection (waves holding window rows take theirs later)
         if (win_w >= my_win && 32 * wave < na) {
-            const int p0 = 32 * wave + c, p1 = p0 + 16;
-            attn_tile_load<D>(pre, p0 < na ? aa.comp_kv + ((size_t)b * aa.T_cap + al[p0]) * D : nullptr,
-                              p1 < na ? aa.comp_kv + ((size_t)b * aa.T_cap + al[p1]) * D : nullptr, g);
+            pick_tile_load(pre, wave);
             have_pre = true;
         }
         asm volatile("" ::: "memory");  // issue those loads here, not where they are used
@@ -661,13 +676,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         if (win_w < my_win) attn_tile_compute<D>(st, qb, wrows, tile, aa.dv / 16, sl2, g, c);
         // window tiles beyond the prefetched ones (more than 4 per member)
         for (int w = 4 + wave; w < my_win; w += 4) {
-            const int j = m + w * f.team_size;
-            const int p0 = 32 * j + c, p1 = 32 * j + 16 + c;
-            const int s0 = p0 < nwin ? window_slot(ia.S, ia.start_pos, aa.W, aa.R, i, p0) : -1;
-            const int s1 = p1 < nwin ? window_slot(ia.S, ia.start_pos, aa.W, aa.R, i, p1) : -1;
             AttnRows<D> rows;
-            attn_tile_load<D>(rows, s0 >= 0 ? aa.win_kv + ((size_t)b * aa.R + s0) * D : nullptr,
-                              s1 >= 0 ? aa.win_kv + ((size_t)b * aa.R + s1) * D : nullptr, g);
+            win_tile_load(rows, m + w * f.team_size);
             attn_tile_compute<D>(st, qb, rows, tile, aa.dv / 16, sl2, g, c);
         }
         for (int tt = wave; tt < pick_tiles; tt += 4) {
@@ -676,8 +686,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             if (tt == wave && have_pre)
                 rows = pre;
             else
-                attn_tile_load<D>(rows, p0 < na ? aa.comp_kv + ((size_t)b * aa.T_cap + al[p0]) * D : nullptr,
-                                  p1 < na ? aa.comp_kv + ((size_t)b * aa.T_cap + al[p1]) * D : nullptr, g);
+                pick_tile_load(rows, tt);
             rows.valid[0] = __ballot(is_pick(p0));
             rows.valid[1] = __ballot(is_pick(p1));
             attn_tile_compute<D>(st, qb, rows, tile, aa.dv / 16, sl2, g, c);
@@ -803,7 +812,10 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
 
 template <int D, int DI, int HT>
 hipError_t launch_fused_cfg(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream) {
-    hipLaunchKernelGGL((fused_decode_kernel<D, DI, HT>), dim3(grid), dim3(kThreads), dyn_bytes, stream, f);
+    if (f.cache_lds)
+        hipLaunchKernelGGL((fused_decode_kernel<D, DI, HT, true>), dim3(grid), dim3(kThreads), dyn_bytes, stream, f);
+    else
+        hipLaunchKernelGGL((fused_decode_kernel<D, DI, HT, false>), dim3(grid), dim3(kThreads), dyn_bytes, stream, f);
     return hipGetLastError();
 }
 
@@ -835,7 +847,7 @@ int device_cus(int dev) {
 }
 
 // Co-resident workgroups of the fused kernel on the current device.
-int max_resident(int D, int DI, int HT, size_t dyn) {
+int max_resident(int D, int DI, int HT, size_t dyn, bool cached) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     const int cus = device_cus(dev);
@@ -844,7 +856,10 @@ int max_resident(int D, int DI, int HT, size_t dyn) {
     hipError_t e = hipErrorInvalidValue;
 #define LIT_OCC(DD, II, HH)                                                                              \
     if (D == DD && DI == II && HT == HH)                                                                 \
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode_kernel<DD, II, HH>, kThreads, dyn);
+        e = cached ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode_kernel<DD, II, HH, true>,  \
+                                                                  kThreads, dyn)                                \
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode_kernel<DD, II, HH, false>, \
+                                                                  kThreads, dyn);
 #define LIT_OCC_D(DD) LIT_OCC(DD, 64, 1) LIT_OCC(DD, 64, 2) LIT_OCC(DD, 64, 3) LIT_OCC(DD, 64, 4) \
                       LIT_OCC(DD, 128, 1) LIT_OCC(DD, 128, 2) LIT_OCC(DD, 128, 3) LIT_OCC(DD, 128, 4)
     LIT_OCC_D(64) LIT_OCC_D(128) LIT_OCC_D(192) LIT_OCC_D(256)
@@ -874,7 +889,7 @@ FusedPlan plan_fused(int B, int S, int start_pos, int ratio, int Hi, int Di, int
         if (chunk > 8192) return p;
         // chunk scores + picks, and the team's scores when they fit the register cache
         dyn = (size_t)chunk * 2 * sizeof(float) + (p.cache_lds ? (size_t)kCacheQ * 4 * kThreads * sizeof(float) : 0);
-        cap = max_resident(D, Di, Hi / 16, dyn);
+        cap = max_resident(D, Di, Hi / 16, dyn, p.cache_lds);
         const long team = (T + chunk - 1) / chunk;
         if (cap > 0 && team <= kThreads && (long)n_teams * team <= cap) {
             p.team_size = (int)team;

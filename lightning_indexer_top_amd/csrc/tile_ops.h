@@ -169,6 +169,23 @@ __device__ inline void attn_tile_load(AttnRows<D> &t, const uint16_t *rp0, const
     }
 }
 
+// The same loads from addresses that are always valid: a lane whose row is not part of
+// the tile (v0 / v1 false) points at a stand-in row its wave attends anyway, so the data
+// is finite and its probability 0 adds nothing.  Unconditional loads let the compiler
+// leave them in flight where they are issued (a load under a branch is waited for at
+// the join).
+template <int D>
+__device__ inline void attn_tile_load_rows(AttnRows<D> &t, const uint16_t *rp0, bool v0, const uint16_t *rp1,
+                                           bool v1, int g) {
+    t.valid[0] = __ballot(v0);
+    t.valid[1] = __ballot(v1);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+        t.r[0][s] = *reinterpret_cast<const u32x4 *>(rp0 + 32 * s + 8 * g);
+        t.r[1][s] = *reinterpret_cast<const u32x4 *>(rp1 + 32 * s + 8 * g);
+    }
+}
+
 // One 32-row tile: logits, online softmax, P.V.  `tile` is this wave's LDS region of
 // 32 rows x (D+4) bf16.  ndt = dv/16 output tiles are accumulated.
 template <int D>
