@@ -144,6 +144,12 @@ struct FusedLds {
     uint32_t mm[kThreads / 64][2];
 };
 
+// Lane exchange within a row of 16 lanes by DPP (no LDS round trip).
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
 __device__ inline uint64_t pack2(float a, float b) {
     return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
 }
@@ -740,16 +746,17 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
 
     // ------------------------------------------------------------------ phase M
     {
-        // this member's slice of the (head, dim-quad) outputs; each output quad is summed
-        // by a group of lpi lanes, every lane loading the O quad and the (max, sum) pair of
-        // a stride of the slots in one round trip and combining them online
+        // This member's slice of the (head, dim-quad) outputs.  Each output quad is summed
+        // by a group of lpi <= 16 lanes (a power of two): every lane loads the O quad and
+        // the (max, normaliser) pair of a stride of the slots, all in one round trip, and
+        // the group combines its lanes with DPP exchanges.
         const int qdv = aa.dv / 4;
         const int n_out = kHeads * qdv;
         const int per = (n_out + f.team_size - 1) / f.team_size;
         const int e0 = m * per;
         const int items = max(0, min(e0 + per, n_out) - e0);
         int lpi = 1;
-        while (lpi * 2 * items <= kThreads && lpi * 2 <= 64) lpi *= 2;
+        while (lpi * 2 * items <= kThreads && lpi < 16) lpi *= 2;
         // rounds of kThreads / lpi items (one round unless lpi == 1 and items > kThreads)
         for (int i0 = 0; i0 < items; i0 += kThreads / lpi) {
             const int item = i0 + tid / lpi, sub = tid % lpi;
@@ -788,23 +795,29 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                 }
                 M = Mn;
             }
-            for (int o2 = lpi / 2; o2 >= 1; o2 >>= 1) {
-                const float M2 = __shfl_xor(M, o2);
-                const float L2 = __shfl_xor(L, o2);
+            // combine the group's lanes: partner lane^x for x = 8, 4, 2, 1 below lpi
+            auto level = [&](auto xchg) {
+                const float M2 = xchg(M), L2 = xchg(L);
                 f32x4 O2;
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) O2[e4] = __shfl_xor(O[e4], o2);
+                for (int e4 = 0; e4 < 4; ++e4) O2[e4] = xchg(O[e4]);
                 const float Mn = fmaxf(M, M2);
                 const float a = M == -INFINITY ? 0.f : exp2f(M - Mn);
                 const float bb = M2 == -INFINITY ? 0.f : exp2f(M2 - Mn);
                 O = a * O + bb * O2;
                 L = a * L + bb * L2;
                 M = Mn;
-            }
+            };
+            if (lpi > 8) level([](float v) { return dpp_f<0x128>(v); });  // row_ror:8 = lane ^ 8
+            if (lpi > 4) level([&](float v) {                                // lane ^ 4
+                const float up = dpp_f<0x104>(v), dn = dpp_f<0x114>(v);       // row_shl:4, row_shr:4
+                return (lane & 4) ? dn : up;
+            });
+            if (lpi > 2) level([](float v) { return dpp_f<0x4E>(v); });   // quad_perm [2,3,0,1]
+            if (lpi > 1) level([](float v) { return dpp_f<0xB1>(v); });   // quad_perm [1,0,3,2]
             if (act && sub == 0) {
                 uint16_t *dst = aa.out + ((size_t)q * kHeads + h) * aa.dv + d;
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) dst[e4] = attn_finish(O[e4], M, L, aa.sink, h);
+                *reinterpret_cast<u32x2 *>(dst) = attn_finish4(O, M, L, aa.sink, h);
             }
         }
     }

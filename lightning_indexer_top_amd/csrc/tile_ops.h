@@ -314,6 +314,25 @@ __device__ inline uint16_t attn_finish(float O, float M, float L, const float *s
     return __builtin_bit_cast(uint16_t, (__bf16)val);
 }
 
+// The same for four consecutive dims: one reciprocal of the normaliser, and the four
+// bf16 results packed for one 8-byte store.
+__device__ inline u32x2 attn_finish4(f32x4 O, float M, float L, const float *sink, int h) {
+    if (sink) {
+        const float s2 = sink[h] * kLog2e;
+        const float M2 = fmaxf(M, s2);
+        if (M2 != -INFINITY) {
+            const float f = M == -INFINITY ? 0.f : exp2f(M - M2);
+            O *= f;
+            L = L * f + exp2f(s2 - M2);
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint16_t r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = __builtin_bit_cast(uint16_t, (__bf16)(O[e] * inv));
+    return u32x2{(uint32_t)r[0] | ((uint32_t)r[1] << 16), (uint32_t)r[2] | ((uint32_t)r[3] << 16)};
+}
+
 // ---------------------------------------------------------------------------
 // Wave and workgroup scans.  The wave scan uses DPP lane shifts within rows of 16
 // lanes and the row broadcasts of 64-lane waves (no LDS traffic).
