@@ -142,6 +142,8 @@ struct FusedLds {
     uint32_t kstar;
     int pstar;
     uint32_t mm[kThreads / 64][2];
+    uint32_t cnt[kTeamMax];       // the team's pick counts (from barrier C)
+    uint32_t wpick[kThreads / 64];  // this member's picks counted by each wave
 };
 
 // Lane exchange within a row of 16 lanes by DPP (no LDS round trip).
@@ -186,7 +188,7 @@ __device__ inline void team_flag(const rsrc_t &slots, int m, uint32_t x, uint32_
 }
 
 __device__ inline u32x4 team_poll(const rsrc_t &slots, int team, uint32_t q, uint32_t ep, uint32_t limit,
-                                  uint32_t *err) {
+                                  uint32_t *err, uint32_t *x_out = nullptr) {
     u32x4 v = {0u, 0u, 0u, 0u};
     const int j = threadIdx.x;
     if (j < team) {
@@ -200,6 +202,7 @@ __device__ inline u32x4 team_poll(const rsrc_t &slots, int team, uint32_t q, uin
             }
             __builtin_amdgcn_s_sleep(1);
         }
+        if (x_out) x_out[j] = v[0];
     }
     __syncthreads();
     return v;
@@ -429,7 +432,6 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     // ------------------------------------------------------------- phase S
     uint32_t kstar = 0u;  // a pick is key > kstar, or key == kstar with position <= pstar
     int pstar = 0x7fffffff;
-    int off = c0;         // where this member's picks start in the output list
     if (select) {
         // barrier A; the members' slots also carry their chunks' max / min keys
         const u32x4 sa = team_poll(slot_a, f.team_size, (uint32_t)q, ep, f.spin_limit, f.err);
@@ -556,14 +558,10 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             sm.ncand = 0;
         }
         __syncthreads();
-        uint32_t before = 0;  // this thread's share of the picks before the member's chunk
         if (cnt <= kCandCap) {
-            // pass 2: the candidates (bin vb) into LDS, and the scores above bin vb before c0
-            // counted.  Cached: two 16-bit bins per word; adding 0x7fff - vb (0x8000 - vb) to
-            // a half sets its bit 15 exactly when the bin is above (at least) vb, and bins stay
-            // <= kVBins, so no half carries into the next.  Chunks start at multiples of 256
-            // positions, so "quad tid + kThreads*r lies before c0" holds for all 64 lanes of a
-            // wave or for none.
+            // pass 2: the candidates (bin vb) into LDS.  Cached: two 16-bit bins per word;
+            // adding 0x7fff - vb (0x8000 - vb) to a half sets its bit 15 exactly when the bin is
+            // above (at least) vb, and bins stay <= kVBins, so no half carries into the next.
             if (cached) {
                 const uint32_t kgt = (0x7fffu - (uint32_t)vb) * 0x10001u;
                 const uint32_t kge = (0x8000u - (uint32_t)vb) * 0x10001u;
@@ -572,8 +570,6 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                 for (int r = 0; r < kCacheQ; ++r) {
                     const uint32_t a0 = bins[2 * r] + kgt, a1 = bins[2 * r + 1] + kgt;
                     const uint32_t b0 = bins[2 * r] + kge, b1 = bins[2 * r + 1] + kge;
-                    if (4 * (wave * 64 + kThreads * r) < c0)
-                        before += __builtin_popcount(a0 & 0x80008000u) + __builtin_popcount(a1 & 0x80008000u);
                     const uint32_t e0 = (a0 ^ b0) & 0x80008000u, e1 = (a1 ^ b1) & 0x80008000u;
                     cmask |= ((e0 >> 15) & 1u | (e0 >> 30) & 2u | (e1 >> 13) & 4u | (e1 >> 28) & 8u) << (4 * r);
                 }
@@ -589,7 +585,6 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             } else {
                 each([&](int t, float x) {
                     const int bin = value_bin(x, scale, bias);
-                    before += (t < c0 && bin > vb) ? 1u : 0u;
                     if (bin == vb) cand[atomicAdd(&sm.ncand, 1)] = ((uint64_t)order_key(x) << 32) | (uint32_t)~(uint32_t)t;
                 });
             }
@@ -619,47 +614,24 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             __syncthreads();
             kstar = sm.kstar;
             pstar = sm.pstar;
-            const uint64_t cstar = ((uint64_t)kstar << 32) | (uint32_t)~(uint32_t)pstar;
-            for (int j = tid; j < cnt; j += kThreads) {
-                const uint64_t cj = cand[j];
-                before += ((int)~(uint32_t)cj < c0 && cj >= cstar) ? 1u : 0u;
-            }
         } else {
             radix_resolve(sm, ts, nvis, scale, bias, vb, need);
             kstar = sm.kstar;
             pstar = sm.pstar;
-            each([&](int t, float x) {
-                const uint32_t k = order_key(x);
-                before += t < c0 && (k > kstar || (k == kstar && t <= pstar));
-            });
         }
-        off = (int)wg_sum(before, sm.wsum);
     }
 
     // ------------------------------------------------------------------ phase D
     int32_t *idx_row = f.topk_out + (size_t)q * f.keff;
-    {
-        const int per = (n + kThreads - 1) / kThreads;
-        const int t0 = tid * per, t1 = min(t0 + per, n);
-        uint32_t mine = 0;
-        for (int t = t0; t < t1; ++t) {
-            const uint32_t k = order_key(sc[t]);
-            mine += !select || k > kstar || (k == kstar && c0 + t <= pstar);
-        }
-        uint32_t total;
-        const uint32_t incl = wg_scan<kThreads / 64>(mine, sm.wsum, &total);
-        int o = (int)(incl - mine);
-        for (int t = t0; t < t1; ++t) {
-            const uint32_t k = order_key(sc[t]);
-            if (!select || k > kstar || (k == kstar && c0 + t <= pstar)) {
-                if (!select) picks[o] = c0 + t;  // with a cut the attention list is already built
-                if (off + o < f.keff) idx_row[off + o] = c0 + t;
-                ++o;
-            }
-        }
-        if (tid == 0) sm.npick = (int)total;
-        if (m == 0 && !select)
-            for (int j = nvis + tid; j < f.keff; j += kThreads) idx_row[j] = -1;
+    // a pick: every visible row without a cut, else key > kstar or key == kstar at a
+    // position <= pstar
+    auto picked = [&](int t) {
+        const uint32_t k = order_key(sc[t]);
+        return !select || k > kstar || (k == kstar && c0 + t <= pstar);
+    };
+    if (!select) {
+        for (int p = tid; p < n; p += kThreads) al[p] = c0 + p;
+        na = n;
         __syncthreads();
     }
     const int slot_bytes = f.slot_floats * 4;
@@ -668,7 +640,6 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     {
         const float sl2 = aa.scale * kLog2e;
         uint16_t *tile = attn_lds + wave * 32 * LD;
-        if (!select) na = sm.npick;
         const int pick_tiles = (na + 31) / 32;
         auto is_pick = [&](int p) {
             if (p >= na) return false;
@@ -679,6 +650,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         };
         AttnState<D> st;
         attn_init<D>(st);
+        uint32_t npk = 0;  // picks among this wave's tiles
         if (win_w < my_win) attn_tile_compute<D>(st, qb, wrows, tile, aa.dv / 16, sl2, g, c);
         // window tiles beyond the prefetched ones (more than 4 per member)
         for (int w = 4 + wave; w < my_win; w += 4) {
@@ -695,8 +667,10 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                 pick_tile_load(rows, tt);
             rows.valid[0] = __ballot(is_pick(p0));
             rows.valid[1] = __ballot(is_pick(p1));
+            npk += __popcll(rows.valid[0] & 0xFFFFull) + __popcll(rows.valid[1] & 0xFFFFull);  // rows c of lanes c
             attn_tile_compute<D>(st, qb, rows, tile, aa.dv / 16, sl2, g, c);
         }
+        if (lane == 0) sm.wpick[wave] = npk;
         __syncthreads();
         float *ow = reinterpret_cast<float *>(attn_lds);
         attn_wave_publish<D>(st, ow, wm, wl, wave, aa.dv, g, c);
@@ -739,8 +713,9 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                               __float_as_uint(hl[h + 1])});
         }
     }
-    team_flag(slot_c, m, 0u, 0u, (uint32_t)q, ep);  // barrier C: partial state published
-    team_poll(slot_c, f.team_size, (uint32_t)q, ep, f.spin_limit, f.err);
+    // barrier C: partial state published; the flag carries the member's pick count
+    team_flag(slot_c, m, sm.wpick[0] + sm.wpick[1] + sm.wpick[2] + sm.wpick[3], 0u, (uint32_t)q, ep);
+    team_poll(slot_c, f.team_size, (uint32_t)q, ep, f.spin_limit, f.err, sm.cnt);
     // every member has read the launch count (it passed barrier C): advance it
     if (m == 0 && tid == 0) st_agent(epoch, ep);
 
@@ -759,6 +734,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         while (lpi * 2 * items <= kThreads && lpi < 16) lpi *= 2;
         // rounds of kThreads / lpi items (one round unless lpi == 1 and items > kThreads)
         for (int i0 = 0; i0 < items; i0 += kThreads / lpi) {
+            if (i0 + (wave * 64) / lpi >= items) continue;  // no item for this wave in this round
             const int item = i0 + tid / lpi, sub = tid % lpi;
             const bool act = item < items;
             const int e = e0 + (act ? item : 0);
@@ -820,6 +796,27 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                 *reinterpret_cast<u32x2 *>(dst) = attn_finish4(O, M, L, aa.sink, h);
             }
         }
+    }
+    // The member's picks into the top-k list, ascending, by the last wave (which usually
+    // has no merge work): they start after the picks of the members before it, whose
+    // counts came with barrier C.
+    if (wave == kThreads / 64 - 1) {
+        uint32_t pre = 0;
+        for (int j = lane; j < m; j += 64) pre += sm.cnt[j];
+#pragma unroll
+        for (int o2 = 32; o2 >= 1; o2 >>= 1) pre += (uint32_t)__shfl_xor((int)pre, o2);
+        const int per = (n + 63) / 64;
+        const int t0 = lane * per, t1 = min(t0 + per, n);
+        uint32_t mine = 0;
+        for (int t = t0; t < t1; ++t) mine += picked(t) ? 1u : 0u;
+        int o = (int)pre + (int)(wave_scan(mine) - mine);
+        for (int t = t0; t < t1; ++t)
+            if (picked(t)) {
+                if (o < f.keff) idx_row[o] = c0 + t;
+                ++o;
+            }
+        if (m == 0 && !select)
+            for (int j = nvis + lane; j < f.keff; j += 64) idx_row[j] = -1;
     }
 }
 
