@@ -55,6 +55,7 @@ constexpr int kBins = 4096;    // radix-level histogram size (12-bit digits)
 constexpr int kVBins = 4096;   // value bins of the first selection level (+ one spill bin)
 constexpr int kCandCap = 2048;  // candidates held in LDS (more are re-read from memory)
 constexpr int kCacheQ = 8;      // team score quads per thread kept in registers (and LDS)
+constexpr int kBatch = 16;      // team score quads per thread loaded per round (uncached form)
 
 // Per-query region of the state buffer, at a fixed stride whatever the team size: the
 // query's launch counter, then one 16-byte flag slot per member for each of the two
@@ -448,13 +449,21 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             }
         }
         // every visible (position, score) of the team, read from the team buffer
+        // (rounds of kBatch quads per thread, all requested before any is used; a quad past
+        // the team buffer reads as zeros)
         auto each = [&](auto &&fn) {
-            for (int qi = tid; qi < nquad; qi += kThreads) {
-                const u32x4 v = ld128_agent(ts_r, (uint32_t)qi * 16u);
+            for (int q0 = 0; q0 < nquad; q0 += kBatch * kThreads) {
+                u32x4 v[kBatch];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * qi + e < nvis) fn(4 * qi + e, __uint_as_float(v[e]));
-                // the load is consumed under lane conditions: wait for it here, so that no
+                for (int r = 0; r < kBatch; ++r) v[r] = ld128_agent(ts_r, (uint32_t)(q0 + tid + kThreads * r) * 16u);
+#pragma unroll
+                for (int r = 0; r < kBatch; ++r) {
+                    const int qi = q0 + tid + kThreads * r;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * qi + e < nvis) fn(4 * qi + e, __uint_as_float(v[r][e]));
+                }
+                // the loads are consumed under lane conditions: wait for them here, so that no
                 // load of this loop is still counted as in flight where the paths join
                 __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             }
@@ -518,7 +527,14 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                 }
             }
         } else {
-            each([&](int t, float x) { atomicAdd(&sm.hist[value_bin(x, scale, bias)], 1u); });
+            // the value bins of every team position are kept in LDS when they fit
+            uint16_t *bins16 = reinterpret_cast<uint16_t *>(dyn + 2 * f.chunk);
+            const bool keep = f.lds_bins;
+            each([&](int t, float x) {
+                const int bin = value_bin(x, scale, bias);
+                atomicAdd(&sm.hist[bin], 1u);
+                if (keep) bins16[t] = (uint16_t)bin;
+            });
         }
         __syncthreads();
         find_bin(sm.hist, kVBins, f.keff, sm.wsum, &sm.bin, &sm.above);
@@ -583,10 +599,28 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                     } while (cmask);
                 }
             } else {
-                each([&](int t, float x) {
-                    const int bin = value_bin(x, scale, bias);
-                    if (bin == vb) cand[atomicAdd(&sm.ncand, 1)] = ((uint64_t)order_key(x) << 32) | (uint32_t)~(uint32_t)t;
-                });
+                if (f.lds_bins) {
+                    // candidates from the LDS bins (8 positions per 16-byte read); their scores
+                    // are read back from the team buffer
+                    const uint16_t *bins16 = reinterpret_cast<const uint16_t *>(dyn + 2 * f.chunk);
+                    for (int w8 = tid; 8 * w8 < nvis; w8 += kThreads) {
+                        const u32x4 x = *reinterpret_cast<const u32x4 *>(bins16 + 8 * w8);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int t = 8 * w8 + e;
+                            const uint32_t bin = (x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                            if (t < nvis && bin == (uint32_t)vb)
+                                cand[atomicAdd(&sm.ncand, 1)] =
+                                    ((uint64_t)order_key(ldf_agent(ts + t)) << 32) | (uint32_t)~(uint32_t)t;
+                        }
+                    }
+                    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing left in flight
+                } else {
+                    each([&](int t, float x) {
+                        const int bin = value_bin(x, scale, bias);
+                        if (bin == vb) cand[atomicAdd(&sm.ncand, 1)] = ((uint64_t)order_key(x) << 32) | (uint32_t)~(uint32_t)t;
+                    });
+                }
             }
             __syncthreads();
             // rank every candidate; the one with need-1 ahead of it is the cut
@@ -897,8 +931,17 @@ FusedPlan plan_fused(int B, int S, int start_pos, int ratio, int Hi, int Di, int
     int cap = 0;
     for (;; chunk *= 2) {
         if (chunk > 8192) return p;
-        // chunk scores + picks, and the team's scores when they fit the register cache
+        // chunk scores + picks, and the team's scores when they fit the register cache, else
+        // (when they fit) 16-bit value bins of every team position
         dyn = (size_t)chunk * 2 * sizeof(float) + (p.cache_lds ? (size_t)kCacheQ * 4 * kThreads * sizeof(float) : 0);
+        p.lds_bins = false;
+        if (!p.cache_lds) {
+            const size_t with_bins = dyn + (size_t)(T + 7) / 8 * 16;
+            if (max_resident(D, Di, Hi / 16, with_bins, false) > 0) {
+                dyn = with_bins;
+                p.lds_bins = true;
+            }
+        }
         cap = max_resident(D, Di, Hi / 16, dyn, p.cache_lds);
         const long team = (T + chunk - 1) / chunk;
         if (cap > 0 && team <= kThreads && (long)n_teams * team <= cap) {
@@ -952,6 +995,7 @@ hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, 
     f.n_slots = p.n_slots;
     f.ld = p.ld;
     f.cache_lds = p.cache_lds;
+    f.lds_bins = p.lds_bins;
     switch (f.aa.D) {
         case 64: return launch_fused_d<64>(f, p.grid, p.dyn_bytes, stream);
         case 128: return launch_fused_d<128>(f, p.grid, p.dyn_bytes, stream);

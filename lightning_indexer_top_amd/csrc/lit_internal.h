@@ -118,11 +118,12 @@ struct FusedArgs {
     float *part;                  // per member: partial attention state
     int slot_floats;              // floats per member state
     bool cache_lds;               // the team's scores are kept in LDS during selection
+    bool lds_bins;                // otherwise: their 16-bit value bins are kept in LDS
 };
 struct FusedPlan {
     bool ok;
     int n_teams, team_size, chunk, win_tiles, n_slots, grid;
-    bool cache_lds;
+    bool cache_lds, lds_bins;
     long ld;
     size_t dyn_bytes;
 };
