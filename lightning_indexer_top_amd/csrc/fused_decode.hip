@@ -136,6 +136,7 @@ __device__ inline void find_bin(const uint32_t *hist, int nbins, int need, uint3
 
 struct FusedLds {
     alignas(16) uint32_t hist[kBins + 4];  // + the spill bin of the value level
+    uint64_t red64[kThreads / 64][2];
     uint32_t wsum[kThreads / 64];
     float fred[kThreads / 64];
     int bin, above, ncand, npick, overflow;
@@ -304,6 +305,68 @@ __device__ inline void radix_resolve(FusedLds &sm, const float *ts, int nvis, fl
 // are separate kernels so that the re-reading form's loads never share a code path with
 // the cached form (a load pending on one path of a branch makes the compiler wait for
 // every load in flight where the paths join, which would stall the early row gather).
+// Narrows the candidates cand[0..cnt) (distinct (key, position) composites) while more
+// than kRankDirect remain: a 4096-bin histogram of the candidates over their own
+// [min, max] range (a monotone map, so bins are ordered like the composites), the bin
+// where the count from the top reaches need, and only that bin's candidates kept; need
+// becomes the rank within them.  Clustered scores put hundreds of candidates into one
+// value bin, and the direct rank costs cnt^2 comparisons.  h2 is 4096 words of LDS.
+constexpr int kRankDirect = 128;
+__device__ inline void refine_candidates(uint64_t *cand, int &cnt, int &need, uint32_t *h2, FusedLds &sm) {
+    constexpr int kPer = kCandCap / kThreads;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int round = 0; round < 8 && cnt > kRankDirect; ++round) {
+        uint64_t cv[kPer];
+        uint64_t lo = ~0ull, hi = 0ull;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int j = tid + kThreads * r;
+            cv[r] = j < cnt ? cand[j] : 0ull;
+            if (j < cnt) {
+                lo = min(lo, cv[r]);
+                hi = max(hi, cv[r]);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint64_t l2 = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(lo >> 32), off) << 32) |
+                                (uint32_t)__shfl_xor((int)(uint32_t)lo, off);
+            const uint64_t h2v = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(hi >> 32), off) << 32) |
+                                 (uint32_t)__shfl_xor((int)(uint32_t)hi, off);
+            lo = min(lo, l2);
+            hi = max(hi, h2v);
+        }
+        if (lane == 0) {
+            sm.red64[wave][0] = lo;
+            sm.red64[wave][1] = hi;
+        }
+        for (int j = tid; j < kBins / 4; j += kThreads) reinterpret_cast<u32x4 *>(h2)[j] = u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
+        lo = ~0ull;
+        hi = 0ull;
+        for (int w = 0; w < kThreads / 64; ++w) {
+            lo = min(lo, sm.red64[w][0]);
+            hi = max(hi, sm.red64[w][1]);
+        }
+        const float s2 = (float)(kBins - 1) / (float)(hi - lo);
+        auto bin_of = [&](uint64_t v) { return min(kBins - 1, (int)((float)(v - lo) * s2)); };
+#pragma unroll
+        for (int r = 0; r < kPer; ++r)
+            if (tid + kThreads * r < cnt) atomicAdd(&h2[bin_of(cv[r])], 1u);
+        __syncthreads();
+        find_bin(h2, kBins, need, sm.wsum, &sm.bin, &sm.above);
+        const int sb = sm.bin;
+        need -= sm.above;
+        if (tid == 0) sm.ncand = 0;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kPer; ++r)
+            if (tid + kThreads * r < cnt && bin_of(cv[r]) == sb) cand[atomicAdd(&sm.ncand, 1)] = cv[r];
+        __syncthreads();
+        cnt = sm.ncand;
+    }
+}
+
 template <int D, int DI, int HT, bool CACHED>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     constexpr int LD = D + 4;
@@ -559,12 +622,17 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             __syncthreads();
         }
         // each wave's first tile of listed rows is requested now, so that the gather
-        // overlaps the rest of the selection (waves holding window rows take theirs later)
-        if (win_w >= my_win && 32 * wave < na) {
-            pick_tile_load(pre, wave);
-            have_pre = true;
-        }
-        asm volatile("" ::: "memory");  // issue those loads here, not where they are used
+        // overlaps the rest of the selection (waves holding window rows take theirs later);
+        // the re-reading form requests it after its candidate loads, which would otherwise
+        // wait behind the gather (the loads of a wave complete in order)
+        auto early_gather = [&]() {
+            if (win_w >= my_win && 32 * wave < na) {
+                pick_tile_load(pre, wave);
+                have_pre = true;
+            }
+            asm volatile("" ::: "memory");  // issue those loads here, not where they are used
+        };
+        if (cached) early_gather();
         // candidates as (key << 32 | ~position): larger means ahead in (key desc, position asc);
         // they take the histogram's place, which is no longer read
         uint64_t *cand = reinterpret_cast<uint64_t *>(sm.hist);
@@ -600,19 +668,23 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                 }
             } else {
                 if (f.lds_bins) {
-                    // candidates from the LDS bins (8 positions per 16-byte read); their scores
-                    // are read back from the team buffer
+                    // candidate positions from the LDS bins (8 per 16-byte read), then their
+                    // scores from the team buffer, one load per candidate, all in flight together
                     const uint16_t *bins16 = reinterpret_cast<const uint16_t *>(dyn + 2 * f.chunk);
+                    int *cpos = reinterpret_cast<int *>(dyn + 2 * f.chunk) + f.bins_words;
                     for (int w8 = tid; 8 * w8 < nvis; w8 += kThreads) {
                         const u32x4 x = *reinterpret_cast<const u32x4 *>(bins16 + 8 * w8);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const int t = 8 * w8 + e;
                             const uint32_t bin = (x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                            if (t < nvis && bin == (uint32_t)vb)
-                                cand[atomicAdd(&sm.ncand, 1)] =
-                                    ((uint64_t)order_key(ldf_agent(ts + t)) << 32) | (uint32_t)~(uint32_t)t;
+                            if (t < nvis && bin == (uint32_t)vb) cpos[atomicAdd(&sm.ncand, 1)] = t;
                         }
+                    }
+                    __syncthreads();
+                    for (int j = tid; j < cnt; j += kThreads) {
+                        const int t = cpos[j];
+                        cand[j] = ((uint64_t)order_key(ldf_agent(ts + t)) << 32) | (uint32_t)~(uint32_t)t;
                     }
                     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing left in flight
                 } else {
@@ -622,13 +694,16 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                     });
                 }
             }
+            if (!cached) early_gather();
             __syncthreads();
-            // rank every candidate; the one with need-1 ahead of it is the cut
-            for (int j = tid; j < cnt; j += kThreads) {
+            int ncand = cnt, nneed = need;
+            refine_candidates(cand, ncand, nneed, reinterpret_cast<uint32_t *>(attn_lds), sm);
+            // rank every candidate; the one with nneed-1 ahead of it is the cut
+            for (int j = tid; j < ncand; j += kThreads) {
                 const uint64_t cj = cand[j];
                 int rank = 0;
                 int o = 0;
-                for (; o + 8 <= cnt; o += 8) {
+                for (; o + 8 <= ncand; o += 8) {
                     const u32x4 *p4 = reinterpret_cast<const u32x4 *>(cand + o);
                     u32x4 x[4];
 #pragma unroll
@@ -639,8 +714,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                         rank += ((uint64_t)x[v][3] << 32 | x[v][2]) > cj;
                     }
                 }
-                for (; o < cnt; ++o) rank += cand[o] > cj;
-                if (rank == need - 1) {
+                for (; o < ncand; ++o) rank += cand[o] > cj;
+                if (rank == nneed - 1) {
                     sm.kstar = (uint32_t)(cj >> 32);
                     sm.pstar = (int)~(uint32_t)cj;
                 }
@@ -936,7 +1011,8 @@ FusedPlan plan_fused(int B, int S, int start_pos, int ratio, int Hi, int Di, int
         dyn = (size_t)chunk * 2 * sizeof(float) + (p.cache_lds ? (size_t)kCacheQ * 4 * kThreads * sizeof(float) : 0);
         p.lds_bins = false;
         if (!p.cache_lds) {
-            const size_t with_bins = dyn + (size_t)(T + 7) / 8 * 16;
+            // the bins (padded to 16 bytes), then kCandCap candidate positions
+            const size_t with_bins = dyn + (size_t)(T + 7) / 8 * 16 + (size_t)kCandCap * 4;
             if (max_resident(D, Di, Hi / 16, with_bins, false) > 0) {
                 dyn = with_bins;
                 p.lds_bins = true;
@@ -996,6 +1072,7 @@ hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, 
     f.ld = p.ld;
     f.cache_lds = p.cache_lds;
     f.lds_bins = p.lds_bins;
+    f.bins_words = (int)((p.ld + 7) / 8 * 4);  // 32-bit words of the padded bins
     switch (f.aa.D) {
         case 64: return launch_fused_d<64>(f, p.grid, p.dyn_bytes, stream);
         case 128: return launch_fused_d<128>(f, p.grid, p.dyn_bytes, stream);

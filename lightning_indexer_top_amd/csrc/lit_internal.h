@@ -119,6 +119,7 @@ struct FusedArgs {
     int slot_floats;              // floats per member state
     bool cache_lds;               // the team's scores are kept in LDS during selection
     bool lds_bins;                // otherwise: their 16-bit value bins are kept in LDS
+    int bins_words;               // 32-bit words those bins take (candidate positions follow)
 };
 struct FusedPlan {
     bool ok;
