@@ -18,8 +18,11 @@ LIB = os.path.join(HERE, "liblit.so")
 SOURCES = ["lit_api.hip", "indexer.hip", "topk.hip", "attention.hip", "fused_decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+# MFMA results are written to VGPRs rather than AGPRs: no accumulator reads before the
+# epilogues, and the kernels here have the VGPRs to spare.
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=true"]
 
 
 def _compile(src: str) -> str:

@@ -90,6 +90,71 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_kernel(IndexerArgs
     }
 }
 
+// Many queries per sequence (chunked prefill): each wave keeps its 64 keys in VGPRs and
+// streams kQB queries past them, the next query's operands loading while the current
+// one is scored (two alternating buffers), so the key loads and the launch cost are
+// spread over kQB queries instead of QG.  The four waves of a workgroup take 256
+// consecutive keys and the same queries (their query loads coalesce in the cache).
+constexpr int kQB = 32;
+
+template <int DI, int HT>
+__global__ __launch_bounds__(kWaves * 64) void indexer_scores_multi_kernel(IndexerArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+
+    const int n_groups = (a.S + kQB - 1) / kQB;
+    const int b = blockIdx.y / n_groups;
+    const int i0 = (blockIdx.y % n_groups) * kQB;
+    const int i1 = min(i0 + kQB, a.S);
+    const int t0 = (blockIdx.x * kWaves + wave) * (16 * kU);
+    if (t0 >= a.T) return;
+    const int vis_max = min(a.T, (a.start_pos + i1) / a.ratio);
+    const size_t bs0 = (size_t)b * a.S;
+    const int t = t0 + 16 * g + c;  // lane group g receives tile g's scores
+
+    if (t0 >= vis_max) {  // nothing visible to any query of the group in these keys
+        if (g == 0)
+            for (int i = i0; i < i1; ++i)
+                for (int u = 0; u < kU; ++u) {
+                    const int tt = t0 + 16 * u + c;
+                    if (tt < a.T) a.scores[(bs0 + i) * a.ld + tt] = -INFINITY;
+                }
+        return;
+    }
+
+    IdxKeys kb[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+        kb[u] = load_idx_keys<DI>(a, (size_t)b * a.T_cap + min(t0 + 16 * u + c, a.T - 1), g);
+
+    static_assert(kU == 4, "idx_score4 scores four tiles");
+    auto finish = [&](int i, float s) {
+        if (t < a.T) {
+            const int vis = (a.start_pos + i + 1) / a.ratio;
+            a.scores[(bs0 + i) * a.ld + t] = t < vis ? s : -INFINITY;
+        }
+    };
+    IdxQuery<DI, HT> qa, qb;
+    load_idx_query<DI, HT>(qa, a, bs0 + i0, true, g, c);
+    for (int i = i0; i < i1; i += 2) {
+        const bool second = i + 1 < i1;
+        load_idx_query<DI, HT>(qb, a, bs0 + (second ? i + 1 : i), true, g, c);
+        finish(i, idx_score4<DI, HT>(qa, kb, g));
+        if (i + 2 < i1) load_idx_query<DI, HT>(qa, a, bs0 + i + 2, true, g, c);
+        if (second) finish(i + 1, idx_score4<DI, HT>(qb, kb, g));
+    }
+}
+
+template <int DI, int HT>
+hipError_t launch_multi(const IndexerArgs &a, hipStream_t stream) {
+    const int keys_per_block = kWaves * 16 * kU;
+    dim3 grid((a.T + keys_per_block - 1) / keys_per_block, a.B * ((a.S + kQB - 1) / kQB));
+    hipLaunchKernelGGL((indexer_scores_multi_kernel<DI, HT>), grid, dim3(kWaves * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int DI, int HT, int QG>
 hipError_t launch_cfg(const IndexerArgs &a, hipStream_t stream) {
     const int keys_per_block = kWaves * 16 * kU;
@@ -102,6 +167,15 @@ template <int DI>
 hipError_t launch_di(const IndexerArgs &a, hipStream_t stream) {
     const int HT = a.Hi / 16;
     const bool multi = a.S > 1;
+    if (a.S >= kQB) {
+        switch (HT) {
+            case 1: return launch_multi<DI, 1>(a, stream);
+            case 2: return launch_multi<DI, 2>(a, stream);
+            case 3: return launch_multi<DI, 3>(a, stream);
+            case 4: return launch_multi<DI, 4>(a, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (HT) {
         case 1: return multi ? launch_cfg<DI, 1, 4>(a, stream) : launch_cfg<DI, 1, 1>(a, stream);
         case 2: return multi ? launch_cfg<DI, 2, 2>(a, stream) : launch_cfg<DI, 2, 1>(a, stream);

@@ -78,6 +78,11 @@ __device__ inline IdxKeys load_idx_keys(const IndexerArgs &a, size_t row, int g)
     return k;
 }
 
+// ReLU as an integer max on the float's bits: a negative float is a negative int, so
+// one v_max_i32 (no NaN canonicalisation, which fmaxf costs under IEEE mode); -0 maps
+// to +0.
+__device__ inline float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Scores of four 16-key tiles for one query.  All 4*HT MFMAs are issued first; each
 // lane then holds, per tile, the head-weighted ReLU sum over its 4 heads of every head
 // tile, and the sum over the four lane groups is a packed butterfly: across lanes 32
@@ -99,7 +104,7 @@ __device__ inline float idx_score4(const IdxQuery<DI, HT> &q, const IdxKeys (&k)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) part[u] += q.w[ht][r] * fmaxf(acc[u][ht][r], 0.f);
+            for (int r = 0; r < 4; ++r) part[u] += q.w[ht][r] * relu_bits(acc[u][ht][r]);
     }
     const bool hi2 = g >= 2, hi1 = g & 1;
     float k0 = hi2 ? part[2] : part[0], k1 = hi2 ? part[3] : part[1];

@@ -15,7 +15,13 @@
 // threshold and keys equal to it; one packed block scan turns those counts into
 // output offsets, so each selected position lands in its ascending slot with no sort.
 // Rows longer than 1024*ITEMS are processed in segments re-read from L2.
-#include "tile_ops.h"
+//
+// Many rows (chunked prefill) of at most 8192 visible scores take a lighter kernel
+// instead: one 256-thread workgroup per row, each thread owning 32
+// consecutive positions in VGPRs, and the value-bin selection of select_ops.h (one
+// histogram pass, then the few scores of the cut's bin ranked exactly), so a row costs
+// a few workgroup barriers rather than three radix passes of a 1024-thread workgroup.
+#include "select_ops.h"
 
 namespace lit {
 
@@ -148,11 +154,144 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     }
 }
 
+constexpr int kRowQ = 8;  // score quads per thread: rows of up to 8192 positions
+
+__global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(TopkArgs a) {
+    __shared__ SelLds sm;
+    __shared__ __attribute__((aligned(16))) uint32_t h2[kBins];  // candidate refinement
+    __shared__ uint32_t mm[kSelThreads / 64][2];
+
+    const int row = blockIdx.x;
+    const int i = row % a.S;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = min(a.T, (a.start_pos + i + 1) / a.ratio);
+    int32_t *out = a.idx + (size_t)row * a.keff;
+    const float *src = a.scores + (size_t)row * a.ld;
+
+    if (n <= a.keff) {  // every visible row is picked
+        for (int j = tid; j < a.keff; j += kSelThreads) out[j] = j < n ? j : -1;
+        return;
+    }
+
+    // thread tid owns positions [32 tid, 32 tid + 32); a quad past the row is not read
+    const int p0 = 32 * tid;
+    f32x4 v[kRowQ];
+#pragma unroll
+    for (int r = 0; r < kRowQ; ++r)
+        v[r] = p0 + 4 * r < n ? *reinterpret_cast<const f32x4 *>(src + p0 + 4 * r) : f32x4{0.f, 0.f, 0.f, 0.f};
+    auto valid = [&](int r, int e) { return p0 + 4 * r + e < n; };
+
+    // the row's max key and max complemented key (its min)
+    uint32_t kmax = 0u, kminc = 0u;
+#pragma unroll
+    for (int r = 0; r < kRowQ; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (valid(r, e)) {
+                const uint32_t k = order_key(v[r][e]);
+                kmax = max(kmax, k);
+                kminc = max(kminc, ~k);
+            }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+        kminc = max(kminc, (uint32_t)__shfl_xor((int)kminc, off));
+    }
+    if (lane == 0) {
+        mm[wave][0] = kmax;
+        mm[wave][1] = kminc;
+    }
+    for (int j = tid; j < kVBins / 4 + 1; j += kSelThreads)  // + the spill bin
+        reinterpret_cast<u32x4 *>(sm.hist)[j] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    kmax = 0u;
+    kminc = 0u;
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+        kmax = max(kmax, mm[w][0]);
+        kminc = max(kminc, mm[w][1]);
+    }
+    const float mx = key_float(kmax), mn = key_float(~kminc);
+    // an infinite end puts every score into one bin; the exact levels below then decide
+    const bool finite = mx - mn < INFINITY;
+    const float scale = finite && mx > mn ? (float)kVBins / (mx - mn) : 0.f;
+    const float bias = finite ? -mn * scale : 0.f;
+
+    // pass 1: value bins (16 bits each, kept) and the histogram
+    uint32_t bins[kRowQ * 2];
+#pragma unroll
+    for (int r = 0; r < kRowQ; ++r) {
+        uint32_t bb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bb[e] = valid(r, e) ? (uint32_t)value_bin(v[r][e], scale, bias) : (uint32_t)kVBins;
+            atomicAdd(&sm.hist[bb[e]], 1u);
+        }
+        bins[2 * r] = bb[0] | (bb[1] << 16);
+        bins[2 * r + 1] = bb[2] | (bb[3] << 16);
+    }
+    __syncthreads();
+    find_bin(sm.hist, kVBins, a.keff, sm.wsum, &sm.bin, &sm.above);
+    const int vb = sm.bin;
+    const int need = a.keff - sm.above;
+    const int cnt = (int)sm.hist[vb];
+    uint32_t kstar, pstar;
+    if (cnt <= kCandCap) {
+        // the scores of bin vb as (key << 32 | ~position), in the histogram's place
+        uint64_t *cand = reinterpret_cast<uint64_t *>(sm.hist);
+        __syncthreads();  // every thread has read hist[vb]
+        if (tid == 0) sm.ncand = 0;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kRowQ; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t bin = (bins[2 * r + (e >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
+                if (bin == (uint32_t)vb)
+                    cand[atomicAdd(&sm.ncand, 1)] =
+                        ((uint64_t)order_key(v[r][e]) << 32) | (uint32_t)~(uint32_t)(p0 + 4 * r + e);
+            }
+        __syncthreads();
+        int ncand = cnt, nneed = need;
+        refine_candidates(cand, ncand, nneed, h2, sm);
+        rank_candidates(cand, ncand, nneed, sm);
+    } else {
+        radix_resolve(sm, [&](int t) { return src[t]; }, n, scale, bias, vb, need);
+    }
+    kstar = sm.kstar;
+    pstar = (uint32_t)sm.pstar;
+
+    // output: a pick is key > kstar, or key == kstar at a position <= pstar; one block scan
+    // over the threads' pick counts gives each thread its first slot (ascending order)
+    auto picked = [&](int r, int e) {
+        const uint32_t k = order_key(v[r][e]);
+        return valid(r, e) && (k > kstar || (k == kstar && (uint32_t)(p0 + 4 * r + e) <= pstar));
+    };
+    uint32_t mine = 0;
+#pragma unroll
+    for (int r = 0; r < kRowQ; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mine += picked(r, e) ? 1u : 0u;
+    uint32_t total;
+    int o = (int)(wg_scan<kSelThreads / 64>(mine, sm.wsum, &total) - mine);
+#pragma unroll
+    for (int r = 0; r < kRowQ; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (picked(r, e)) {
+                if (o < a.keff) out[o] = p0 + 4 * r + e;
+                ++o;
+            }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
     if (a.B <= 0 || a.S <= 0 || a.keff <= 0) return hipSuccess;
     dim3 grid(a.B * a.S), block(kThreads);
+    if (a.T <= kSelThreads * 4 * kRowQ && a.B * a.S >= 256) {  // many rows (few: the radix kernel)
+        hipLaunchKernelGGL(topk_rows_kernel, grid, dim3(kSelThreads), 0, stream, a);
+        return hipGetLastError();
+    }
     if (a.T <= kThreads * 4)
         hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, stream, a);
     else if (a.T <= kThreads * 8)
