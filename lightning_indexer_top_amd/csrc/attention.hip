@@ -31,11 +31,11 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kHeads = 16;
 
-__device__ inline const uint16_t *list_row(const AttnArgs &a, int b, int i, int nwin, int p) {
+__device__ inline const uint16_t *list_row(const AttnArgs &a, int b, int i, int nwin, const WindowBase &wb,
+                                          int p) {
     const size_t bs = (size_t)b * a.S + i;
     if (p < nwin) {
-        const int slot = a.win_idx ? a.win_idx[bs * a.W + p]
-                                   : window_slot(a.S, a.start_pos, a.W, a.R, i, p);
+        const int slot = a.win_idx ? a.win_idx[bs * a.W + p] : window_slot_at(wb, a.start_pos, a.R, i, p);
         if (slot < 0 || slot >= a.R) return nullptr;
         return a.win_kv + ((size_t)b * a.R + slot) * a.D;
     }
@@ -59,6 +59,7 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a, At
     const int i = bs % a.S;
     const int split = blockIdx.x;
     const int nwin = a.win_idx ? a.W : (a.W > 0 ? window_width(a.S, a.start_pos, a.W) : 0);
+    const WindowBase wb = window_base(a.start_pos, a.W, a.R > 0 ? a.R : 1, i);
     const int list_len = nwin + a.K;
     const int ndt = a.dv / 16;
     const float sl2 = a.scale * kLog2e;
@@ -77,8 +78,8 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a, At
         if (base >= split_end) break;
         const int p0 = base + c, p1 = base + 16 + c;
         AttnRows<D> rows;
-        attn_tile_load<D>(rows, p0 < split_end ? list_row(a, b, i, nwin, p0) : nullptr,
-                          p1 < split_end ? list_row(a, b, i, nwin, p1) : nullptr, g);
+        attn_tile_load<D>(rows, p0 < split_end ? list_row(a, b, i, nwin, wb, p0) : nullptr,
+                          p1 < split_end ? list_row(a, b, i, nwin, wb, p1) : nullptr, g);
         attn_tile_compute<D>(st, qb, rows, tile, ndt, sl2, g, c);
     }
     __syncthreads();  // every wave is done with its LDS rows

@@ -289,10 +289,11 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     // rows of a window tile; a lane off the list reads the query's own slot instead (always
     // attended), so that the loads need no branch
     const int own_slot = (ia.start_pos + i) % max(aa.R, 1);
+    const WindowBase wbase = window_base(ia.start_pos, aa.W, max(aa.R, 1), i);
     auto win_tile_load = [&](AttnRows<D> &rows, int j) {
         const int p0 = 32 * j + c, p1 = 32 * j + 16 + c;
-        const int s0 = p0 < nwin ? window_slot(ia.S, ia.start_pos, aa.W, aa.R, i, p0) : -1;
-        const int s1 = p1 < nwin ? window_slot(ia.S, ia.start_pos, aa.W, aa.R, i, p1) : -1;
+        const int s0 = p0 < nwin ? window_slot_at(wbase, ia.start_pos, aa.R, i, p0) : -1;
+        const int s1 = p1 < nwin ? window_slot_at(wbase, ia.start_pos, aa.R, i, p1) : -1;
         attn_tile_load_rows<D>(rows, aa.win_kv + ((size_t)b * aa.R + (s0 >= 0 ? s0 : own_slot)) * D, s0 >= 0,
                                aa.win_kv + ((size_t)b * aa.R + (s1 >= 0 ? s1 : own_slot)) * D, s1 >= 0, g);
     };

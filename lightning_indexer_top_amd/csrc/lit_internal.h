@@ -100,6 +100,28 @@ __host__ __device__ inline int window_slot(int S, int start_pos, int W, int R, i
     return valid ? (int)(p % R) : -1;
 }
 
+// The same rule with the division done once per query: entry j of query i's list is
+// position p0 + j at ring slot (s0 + j) mod R.
+struct WindowBase {
+    long p0;  // position of entry 0
+    int s0;   // its slot, p0 mod R in [0, R)
+};
+__host__ __device__ inline WindowBase window_base(int start_pos, int W, int R, int i) {
+    WindowBase w;
+    w.p0 = start_pos == 0 ? (i - W + 1 > 0 ? i - W + 1 : 0) : (long)start_pos + i - W + 1;
+    const long m = w.p0 % R;
+    w.s0 = (int)(m < 0 ? m + R : m);
+    return w;
+}
+__host__ __device__ inline int window_slot_at(const WindowBase &w, int start_pos, int R, int i, int j) {
+    const long p = w.p0 + j;
+    const bool valid = start_pos == 0 ? p <= i : p >= 0;
+    int s = w.s0 + j;
+    if (s >= R) s -= R;
+    if (s >= R) s %= R;  // a ring shorter than the window (early in a sequence)
+    return valid ? s : -1;
+}
+
 
 // ---------------------------------------------------------------------------
 // Fused decode step (fused_decode.hip)

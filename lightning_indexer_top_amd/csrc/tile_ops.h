@@ -226,20 +226,29 @@ __device__ inline void attn_tile_compute(AttnState<D> &st, const bf16x8 (&qb)[D 
         }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(st.m, tmax);
-    const float alpha = st.m == -INFINITY ? 0.f : exp2f(st.m - m_new);
+    // Lazy rescale: the reference max st.m moves (and O and l are rescaled) only when the
+    // tile's max exceeds it by more than 8 in log2 units, so probabilities stay <= 2^8
+    // (exact in fp32, and within bf16 range for P) and most tiles skip the rescale.  The
+    // final normalisation uses the same reference, so the result is unchanged in exact
+    // arithmetic.  Exponents are <= 8 here; v_exp_f32 is used directly (its flush of
+    // results below 2^-126 is far under the bf16 output's resolution).
+    const bool move = tmax > st.m + 8.f;  // also the first finite tile (st.m = -inf)
+    if (__ballot(move)) {
+        const float alpha = !move ? 1.f : (st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - tmax));
+        st.l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) st.o[dt] *= alpha;
+        st.m = move ? tmax : st.m;
+    }
     bf16x8 pb;
     float psum = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const float pk = x[k] == -INFINITY ? 0.f : exp2f(x[k] - m_new);
+        const float pk = x[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[k] - st.m);
         psum += pk;
         pb[k] = (__bf16)pk;
     }
-    st.l = st.l * alpha + psum;
-    st.m = m_new;
-#pragma unroll
-    for (int dt = 0; dt < NT; ++dt) st.o[dt] *= alpha;
+    st.l += psum;
 
     wave_lds_sync();  // the rows this wave wrote are readable by its other lanes
     // V^T operand by DS_READ_B64_TR_B16.  Within a 16-lane group, output lane i's element k
