@@ -87,7 +87,7 @@ def traffic_for(kernel: str, workload: str, srcs):
 
 def kernel_sources(ksrc: str):
     csrc = os.path.join(ROOT, "lightning_indexer_top_amd", "csrc")
-    return [os.path.join(csrc, f) for f in (ksrc, "tile_ops.h", "lit_internal.h")]
+    return [os.path.join(csrc, f) for f in (ksrc, "tile_ops.h", "select_ops.h", "lit_internal.h")]
 
 
 def read_counters(path: str, counter: str) -> dict:
