@@ -16,18 +16,21 @@
 //      query sees more rows than it keeps, it publishes the chunk's scores to the team
 //      buffer and its chunk's max / min score keys in its barrier-A flag.
 //   -- team barrier A (skipped when every visible row is kept) --
-//   S. Every member loads all of the team's scores into registers and finds, on its own,
-//      the exact k-th (key, position): a 4096-bin value histogram between the team's min
-//      and max, the bin where the count from the top reaches k, then a rank among the few
-//      scores of that bin (heavy ties: three radix levels over the order keys and a
-//      position scan).  It also counts the picks before its chunk, i.e. where its picks
-//      start in the output list.  Every member reaches the same cut from the same data.
-//   D. Every member writes its picks (ascending) to the top-k list, gathers those rows
-//      and its share of the window rows, runs the attention tiles (as in attention.hip)
-//      and publishes its partial state.
-//   -- team barrier C --
+//   S. Every member loads all of the team's scores and finds, on its own, the exact k-th
+//      (key, position) with the value-bin selection of select_ops.h: a 4096-bin histogram
+//      between the team's min and max, the bin where the count from the top reaches k,
+//      then the few scores of that bin ranked exactly (narrowed first when there are
+//      many; radix levels when they overflow LDS).  Every member reaches the same cut
+//      from the same data.  Once the cut's bin is known, each wave requests its first
+//      tile of candidate rows, so the row gather overlaps the rest of the selection.
+//   D. Every member attends over its share of the window rows and over its chunk's picks
+//      (candidates that miss the cut are masked), counts its picks from the tiles'
+//      masks, and publishes its partial state.
+//   -- team barrier C (the flag carries the member's pick count) --
 //   M. Members merge the team's partial states (log-sum-exp) for a slice of the
-//      (head, dim) outputs, add the sink, and write bf16.
+//      (head, dim) outputs, add the sink, and write bf16.  Meanwhile the wave without
+//      merge work writes the member's picks to the top-k list (ascending), at the offset
+//      the pick counts of the members before it give.
 //
 // Cross-workgroup data moves through agent-scope relaxed atomic loads and stores and
 // coherent (sc1) 16-byte buffer loads and stores.  The barriers are flag arrays, not
