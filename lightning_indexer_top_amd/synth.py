@@ -3,19 +3,21 @@
 This module is shared by the tests, the bench and the smoke check, and is the only
 code both the HIP path's callers and the CPU oracle's callers use.  It holds no part
 of the method's arithmetic: only random draws, the bf16 / e4m3 casts of a library
-(torch), and the block quantiser that writes e4m3 codes with one ue8m0 scale per 32
-values (the format of the DeepSeek-V4.1-Flash-NVFP4 ``inference/model.py`` module
-globals).  The quantiser's rounding rule is not on the pages; any rule that yields
-valid bytes will do, because both sides consume the same bytes.
+(torch), and the block quantisers that write e4m3 (or fp4 e2m1) codes with one ue8m0
+scale per 32 values (the formats of the DeepSeek-V4.1-Flash-NVFP4 ``inference/model.py``
+module globals and its indexer).  The quantisers' rounding rules are not on the pages;
+any rule that yields valid bytes will do, because both sides consume the same bytes.
 
 Recipe (per workload, ``numpy.random.Generator(PCG64(seed))``):
 
 * attention q, window KV, compressed KV ~ N(0, 1), rounded to bf16 (RNE);
 * indexer q and keys ~ N(0, 1), quantised to e4m3 with a ue8m0 scale per 32
   values: scale exponent e = ceil(log2(amax / 448)), codes = RNE(x / 2^e);
+  with ``index_fmt="e2m1"`` to fp4 instead: e = ceil(log2(amax / 6)), codes = RNE
+  onto the e2m1 grid, two per byte (element 2j in the low nibble of byte j);
 * head weights w ~ U(0, 1) in fp32;
 * ``keys="boost"``: 5% of each sequence's key rows multiplied by 4, which leaves
-  the e4m3 codes unchanged and adds 2 to each of the row's scale bytes;
+  the codes unchanged and adds 2 to each of the row's scale bytes;
 * ``keys="mixture"``: keys = mu_z + 0.1 * eps with 64 centroids mu ~ N(0, I),
   z uniform, eps ~ N(0, I).
 """
@@ -28,6 +30,7 @@ import numpy as np
 import torch
 
 E4M3_MAX = 448.0
+E2M1_MAX = 6.0
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -57,8 +60,39 @@ def quantize_e4m3_ue8m0(x: torch.Tensor, block: int = 32):
     return codes.flatten(-2), scales
 
 
-def _quant_np(x: np.ndarray):
-    c, s = quantize_e4m3_ue8m0(torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)))
+def _pow2_scale(xb: torch.Tensor, vmax: float):
+    """Per-block ue8m0 exponent: the smallest e with amax / 2^e <= vmax (all-zero block:
+    -127).  Returns (e as float, scale bytes)."""
+    amax = xb.abs().amax(dim=-1)
+    safe = torch.where(amax > 0, amax, torch.ones_like(amax))
+    e = torch.ceil(torch.log2(safe / vmax))
+    e = torch.where(safe / torch.exp2(e) > vmax, e + 1, e)
+    e = torch.where(amax > 0, e, torch.full_like(e, -127.0)).clamp(-127, 127)
+    return e, (e + 127).to(torch.uint8)
+
+
+def quantize_e2m1_ue8m0(x: torch.Tensor, block: int = 32):
+    """fp4 block quantiser: x [..., D] -> (packed codes uint8 [..., D/2], scales uint8
+    [..., D/block]).  Codes round to the nearest e2m1 value (0, 0.5, 1, 1.5, 2, 3, 4,
+    6), ties to the even code; element 2j goes to the low nibble of byte j."""
+    assert x.shape[-1] % block == 0 and block % 2 == 0
+    xb = x.float().unflatten(-1, (-1, block))
+    e, scales = _pow2_scale(xb, E2M1_MAX)
+    y = (xb / torch.exp2(e).unsqueeze(-1)).clamp(-E2M1_MAX, E2M1_MAX)
+    m = y.abs()
+    # midpoints between neighbouring grid values; at a tie the even code wins, so the
+    # comparison is strict above an even code and inclusive above an odd one
+    code = ((m > 0.25).int() + (m >= 0.75).int() + (m > 1.25).int() + (m >= 1.75).int()
+            + (m > 2.5).int() + (m >= 3.5).int() + (m > 5.0).int())
+    code = code + 8 * (y < 0).int()
+    code = code.flatten(-2)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).to(torch.uint8)
+    return packed, scales
+
+
+def _quant_np(x: np.ndarray, fmt: str = "e4m3"):
+    q = quantize_e2m1_ue8m0 if fmt == "e2m1" else quantize_e4m3_ue8m0
+    c, s = q(torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)))
     return c.numpy().copy(), s.numpy().copy()
 
 
@@ -80,16 +114,17 @@ class StepInputs:
     T_cap: int
     index_topk: int
     scale: float
-    q8: np.ndarray       # [B,S,Hi,Di] u8 e4m3
+    q8: np.ndarray       # [B,S,Hi,Di] u8 e4m3 (e2m1: [B,S,Hi,Di/2], two codes a byte)
     q_sc: np.ndarray     # [B,S,Hi,Di/32] u8 e8m0
     w: np.ndarray        # [B,S,Hi] f32
-    k8: np.ndarray       # [B,T_cap,Di] u8 e4m3
+    k8: np.ndarray       # [B,T_cap,Di] u8 e4m3 (e2m1: [B,T_cap,Di/2])
     k_sc: np.ndarray     # [B,T_cap,Di/32] u8 e8m0
     q: np.ndarray        # [B,S,H,D] bf16 bits
     win_kv: np.ndarray   # [B,R,D] bf16 bits
     comp_kv: np.ndarray  # [B,T_cap,D] bf16 bits
     sink: Optional[np.ndarray] = None  # [H] f32 or None
     seed: int = 0
+    index_fmt: str = "e4m3"  # code format of q8 / k8: "e4m3" or "e2m1"
 
     @property
     def end_pos(self) -> int:
@@ -108,7 +143,7 @@ def make_step(*, B: int, S: int, start_pos: int, ratio: int, Hi: int, Di: int, H
               D: int, W: int, index_topk: int, seed: int, dv: Optional[int] = None,
               R: Optional[int] = None, T_cap: Optional[int] = None, keys: str = "normal",
               sink: Optional[np.ndarray] = None, scale: Optional[float] = None,
-              name: str = "custom") -> StepInputs:
+              index_fmt: str = "e4m3", name: str = "custom") -> StepInputs:
     """Draw one step's inputs.  R defaults to the smallest window source that holds
     every needed position; T_cap defaults to the visible compressed row count."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -122,7 +157,8 @@ def make_step(*, B: int, S: int, start_pos: int, ratio: int, Hi: int, Di: int, H
     scale = D ** -0.5 if scale is None else scale
     f32 = np.float32
 
-    q8, q_sc = _quant_np(rng.standard_normal((B, S, Hi, Di), dtype=f32))
+    assert index_fmt in ("e4m3", "e2m1")
+    q8, q_sc = _quant_np(rng.standard_normal((B, S, Hi, Di), dtype=f32), index_fmt)
     w = rng.random((B, S, Hi), dtype=f32)
     if keys == "mixture":
         mu = rng.standard_normal((64, Di), dtype=f32)
@@ -130,7 +166,7 @@ def make_step(*, B: int, S: int, start_pos: int, ratio: int, Hi: int, Di: int, H
         kf = mu[z] + f32(0.1) * rng.standard_normal((B, T_cap, Di), dtype=f32)
     else:
         kf = rng.standard_normal((B, T_cap, Di), dtype=f32)
-    k8, k_sc = _quant_np(kf)
+    k8, k_sc = _quant_np(kf, index_fmt)
     if keys == "boost":
         n_boost = max(1, int(round(0.05 * T_cap)))
         for b in range(B):
@@ -143,7 +179,7 @@ def make_step(*, B: int, S: int, start_pos: int, ratio: int, Hi: int, Di: int, H
     return StepInputs(name=name, B=B, S=S, start_pos=start_pos, ratio=ratio, Hi=Hi, Di=Di,
                       H=H, D=D, dv=dv, W=W, R=R, T_cap=T_cap, index_topk=index_topk,
                       scale=scale, q8=q8, q_sc=q_sc, w=w, k8=k8, k_sc=k_sc, q=q,
-                      win_kv=win_kv, comp_kv=comp_kv, sink=sink, seed=seed)
+                      win_kv=win_kv, comp_kv=comp_kv, sink=sink, seed=seed, index_fmt=index_fmt)
 
 
 # The five workloads of the sparse-attention step.  Decode with "context L" is one query
@@ -161,6 +197,13 @@ WORKLOADS = {
                         W=128, index_topk=512, seed=20261242),
     "decode-128k": dict(B=2, S=1, start_pos=131071, ratio=4, Hi=64, Di=128, H=16, D=128,
                         W=128, index_topk=2048, seed=20261252, keys="mixture"),
+    # the 16K and 128K decode shapes with fp4 (e2m1) index queries and keys, the
+    # indexer precision of DeepSeek-V4.1's own Indexer.forward
+    "decode-16k-fp4": dict(B=8, S=1, start_pos=16383, ratio=2, Hi=64, Di=128, H=16, D=192,
+                           W=128, index_topk=2048, seed=20261262, index_fmt="e2m1"),
+    "decode-128k-fp4": dict(B=2, S=1, start_pos=131071, ratio=4, Hi=64, Di=128, H=16, D=128,
+                            W=128, index_topk=2048, seed=20261272, keys="mixture",
+                            index_fmt="e2m1"),
 }
 
 
@@ -191,7 +234,8 @@ def draw_step_device(spec: dict, seed: int, device="cuda") -> dict:
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     f32 = dict(dtype=torch.float32, device=device, generator=g)
-    q8, q_sc = quantize_e4m3_ue8m0(torch.randn(B, S, Hi, Di, **f32))
+    quant = quantize_e2m1_ue8m0 if spec.get("index_fmt", "e4m3") == "e2m1" else quantize_e4m3_ue8m0
+    q8, q_sc = quant(torch.randn(B, S, Hi, Di, **f32))
     w = torch.rand(B, S, Hi, **f32)
     keys = spec.get("keys", "normal")
     if keys == "mixture":
@@ -200,7 +244,7 @@ def draw_step_device(spec: dict, seed: int, device="cuda") -> dict:
         kf = mu[z] + 0.1 * torch.randn(B, T_cap, Di, **f32)
     else:
         kf = torch.randn(B, T_cap, Di, **f32)
-    k8, k_sc = quantize_e4m3_ue8m0(kf)
+    k8, k_sc = quant(kf)
     if keys == "boost":
         n_boost = max(1, int(round(0.05 * T_cap)))
         for b in range(B):

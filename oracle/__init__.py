@@ -10,7 +10,8 @@ queries); this module only marshals numpy arrays into it and composes the steps.
 Sources are cited per function there:
 
 * DeepSeek-V4.1-Flash-NVFP4 ``inference/model.py``: module globals (e4m3 with one
-  ue8m0 scale per 32 values), ``get_window_topk_idxs``, ``Indexer.forward``,
+  ue8m0 scale per 32 values; fp4 e2m1 with the same scales for the indexer),
+  ``get_window_topk_idxs``, ``Indexer.forward``,
   ``Attention.forward``.
 * DeepSeek-V3.2-Exp ``inference/model.py``: ``Indexer.forward`` (``fp8_index``) and
   ``MLA.forward`` (dense scores, index mask, softmax).
@@ -66,7 +67,9 @@ def _bind(path: str):
     lib.orc_bf16.restype = ctypes.c_double
     lib.orc_n_visible.argtypes = [I, I, I]
     lib.orc_n_visible.restype = I
-    lib.orc_index_scores.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.orc_e2m1.argtypes = [ctypes.c_uint8]
+    lib.orc_e2m1.restype = ctypes.c_double
+    lib.orc_index_scores.argtypes = [I, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.orc_index_scores.restype = I
     lib.orc_topk_width.argtypes = [I, I, I, I]
     lib.orc_topk_width.restype = I
@@ -135,6 +138,11 @@ def e8m0_value(code: int) -> float:
     return _load().orc_e8m0(code)
 
 
+def e2m1_value(code: int) -> float:
+    """Value of one 4-bit e2m1 code (0..15)."""
+    return _load().orc_e2m1(code)
+
+
 def bf16_value(bits: int) -> float:
     return _load().orc_bf16(bits)
 
@@ -159,19 +167,32 @@ def window_width(S: int, start_pos: int, W: int) -> int:
     return _load().orc_window_width(S, start_pos, W)
 
 
-def index_scores(q8, q_sc, w, k8, k_sc, start_pos: int, ratio: int) -> np.ndarray:
-    """Scores [B,S,T] (float64, -inf where invisible), T = (start_pos+S)//ratio."""
+# index-code formats: one e4m3 byte per element, or two e2m1 codes per byte
+INDEX_FORMATS = {"e4m3": 0, "e2m1": 1}
+
+
+def index_scores(q8, q_sc, w, k8, k_sc, start_pos: int, ratio: int,
+                 fmt: str = "e4m3") -> np.ndarray:
+    """Scores [B,S,T] (float64, -inf where invisible), T = (start_pos+S)//ratio.
+
+    ``fmt`` names the code format of ``q8`` / ``k8``: "e4m3" ([..., Di] bytes) or
+    "e2m1" ([..., Di/2] bytes, element 2j in the low nibble of byte j).  Di is taken
+    from the scale arrays (one byte per 32 elements)."""
     q8 = _c(q8, np.uint8)
     q_sc = _c(q_sc, np.uint8)
     w = _c(w, np.float32)
     k8 = _c(k8, np.uint8)
     k_sc = _c(k_sc, np.uint8)
-    B, S, Hi, Di = q8.shape
+    B, S, Hi, _ = q8.shape
+    Di = 32 * q_sc.shape[-1]
+    per_byte = 2 if fmt == "e2m1" else 1
+    if q8.shape[-1] * per_byte != Di or k8.shape[-1] * per_byte != Di:
+        raise OracleError(f"code rows do not hold {Di} {fmt} elements")
     T_cap = k8.shape[1]
     T = (start_pos + S) // ratio
     out = np.empty((B, S, T), dtype=np.float64)
-    rc = _load().orc_index_scores(_ptr(q8), _ptr(q_sc), _ptr(w), _ptr(k8), _ptr(k_sc),
-                                  B, S, Hi, Di, T_cap, start_pos, ratio, _ptr(out))
+    rc = _load().orc_index_scores(INDEX_FORMATS[fmt], _ptr(q8), _ptr(q_sc), _ptr(w), _ptr(k8),
+                                  _ptr(k_sc), B, S, Hi, Di, T_cap, start_pos, ratio, _ptr(out))
     _check(rc, "orc_index_scores")
     return out
 
@@ -230,7 +251,8 @@ def step(inp, fp32_scores: bool = True) -> dict:
     selection, so the oracle takes its top-k decision in the precision the kernel keeps
     its scores in; the scores themselves are still the exact fp64 values.
     """
-    s = index_scores(inp.q8, inp.q_sc, inp.w, inp.k8, inp.k_sc, inp.start_pos, inp.ratio)
+    s = index_scores(inp.q8, inp.q_sc, inp.w, inp.k8, inp.k_sc, inp.start_pos, inp.ratio,
+                     getattr(inp, "index_fmt", "e4m3"))
     sel = s.astype(np.float32).astype(np.float64) if fp32_scores else s
     idx = topk(sel, inp.start_pos, inp.ratio, inp.index_topk)
     win = window_indices(inp.B, inp.S, inp.start_pos, inp.W, inp.R)

@@ -34,7 +34,8 @@
 
 /* ------------------------------------------------------------------------ */
 /* Byte formats.  [V4.1] module globals: the activation format is e4m3 with  */
-/* one power-of-two (ue8m0) scale per 32 elements.                           */
+/* one power-of-two (ue8m0) scale per 32 elements; the indexer's fp4 format  */
+/* is e2m1 with the same scales.                                             */
 /* ------------------------------------------------------------------------ */
 
 /* OCP e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits, no
@@ -49,6 +50,22 @@ double orc_e4m3(uint8_t code) {
         v = ldexp((double)m / 8.0, -6);
     else
         v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* OCP e2m1 (MXFP4 element), one 4-bit code: 1 sign bit, 2 exponent bits (bias
+ * 1), 1 mantissa bit, no infinities or NaN; exponent 0 is subnormal (0 or 0.5).
+ * [V4.1] quantises the index queries and keys to this format with one ue8m0
+ * scale per 32 elements (fp4 block size 32, Indexer.forward). */
+double orc_e2m1(uint8_t code) {
+    int s = (code >> 3) & 1;
+    int e = (code >> 1) & 3;
+    int m = code & 1;
+    double v;
+    if (e == 0)
+        v = (double)m / 2.0;
+    else
+        v = ldexp(1.0 + (double)m / 2.0, e - 1);
     return s ? -v : v;
 }
 
@@ -81,25 +98,47 @@ int orc_n_visible(int start_pos, int i, int ratio) {
 /* ------------------------------------------------------------------------ */
 /* Indexer score.  [V4.1] Indexer.forward: index_score[b,s,t] =              */
 /*   sum_h  w[b,s,h] * relu( q[b,s,h,:] . k[b,t,:] ),                        */
-/* with q and k the dequantised fp8 values ([V3.2] fp8_index takes the e4m3  */
-/* codes and their block scales).  Each operand is dequantised per block of  */
-/* 32 along the head dimension: x = code * 2^(scale-127).                    */
+/* with q and k the dequantised values ([V3.2] fp8_index takes the e4m3      */
+/* codes and their block scales; [V4.1] quantises both to fp4 with the same  */
+/* 32-element ue8m0 blocks).  Each operand is dequantised per block of 32    */
+/* along the head dimension: x = code * 2^(scale-127).                       */
 /*                                                                           */
-/* Layouts (row-major): q8 [B,S,Hi,Di], q_sc [B,S,Hi,Di/32], w [B,S,Hi] f32, */
-/* k8 [B,T_cap,Di], k_sc [B,T_cap,Di/32].  Output scores [B,S,T] doubles     */
-/* with T = (start_pos+S)//ratio; entries of rows a query cannot see are     */
-/* -inf.  Returns ORC_E_ARG for bad sizes, ORC_E_CODE for a NaN code.        */
+/* fmt selects the element codes: ORC_FMT_E4M3, one byte per element, or    */
+/* ORC_FMT_E2M1, two elements per byte with element 2j in the low nibble of  */
+/* byte j (the order is a reading: the pages store two fp4 values per byte   */
+/* without saying which comes first; a score does not depend on it as long   */
+/* as q and k share it, since both nibbles of a byte lie in one scale block).*/
+/*                                                                           */
+/* Layouts (row-major), E = Di for e4m3 and Di/2 for e2m1: q8 [B,S,Hi,E],    */
+/* q_sc [B,S,Hi,Di/32], w [B,S,Hi] f32, k8 [B,T_cap,E], k_sc [B,T_cap,Di/32].*/
+/* Output scores [B,S,T] doubles with T = (start_pos+S)//ratio; entries of   */
+/* rows a query cannot see are -inf.  Returns ORC_E_ARG for bad sizes or an  */
+/* unknown fmt, ORC_E_CODE for a NaN code.                                   */
 /* ------------------------------------------------------------------------ */
-int orc_index_scores(const uint8_t *q8, const uint8_t *q_sc, const float *w,
+#define ORC_FMT_E4M3 0
+#define ORC_FMT_E2M1 1
+
+/* Value of element d of a code row in format fmt (scale not applied). */
+static double orc_code_at(const uint8_t *row, int fmt, int d) {
+    if (fmt == ORC_FMT_E2M1) {
+        uint8_t byte = row[d / 2];
+        uint8_t nib = (d % 2 == 0) ? (byte & 15) : (byte >> 4);
+        return orc_e2m1(nib);
+    }
+    return orc_e4m3(row[d]);
+}
+
+int orc_index_scores(int fmt, const uint8_t *q8, const uint8_t *q_sc, const float *w,
                      const uint8_t *k8, const uint8_t *k_sc, int B, int S,
                      int Hi, int Di, int T_cap, int start_pos, int ratio,
                      double *scores) {
     if (B < 0 || S < 0 || Hi <= 0 || Di <= 0 || Di % 32 != 0 || ratio <= 0 ||
-        start_pos < 0)
+        start_pos < 0 || (fmt != ORC_FMT_E4M3 && fmt != ORC_FMT_E2M1))
         return ORC_E_ARG;
     const int T = (start_pos + S) / ratio;
     if (T > T_cap) return ORC_E_ARG;
     const int nb = Di / 32;
+    const size_t E = fmt == ORC_FMT_E2M1 ? (size_t)Di / 2 : (size_t)Di; /* bytes per row */
     int bad = 0;
 #pragma omp parallel for collapse(2) schedule(dynamic) reduction(| : bad)
     for (int b = 0; b < B; ++b) {
@@ -110,9 +149,9 @@ int orc_index_scores(const uint8_t *q8, const uint8_t *q_sc, const float *w,
             /* dequantise this query's heads */
             for (int h = 0; h < Hi; ++h)
                 for (int d = 0; d < Di; ++d) {
-                    size_t qi = (((size_t)b * S + i) * Hi + h) * Di + d;
+                    const uint8_t *qrow = q8 + (((size_t)b * S + i) * Hi + h) * E;
                     size_t si = (((size_t)b * S + i) * Hi + h) * nb + d / 32;
-                    double v = orc_e4m3(q8[qi]) * orc_e8m0(q_sc[si]);
+                    double v = orc_code_at(qrow, fmt, d) * orc_e8m0(q_sc[si]);
                     if (isnan(v)) bad = 1;
                     qh[(size_t)h * Di + d] = v;
                 }
@@ -125,9 +164,9 @@ int orc_index_scores(const uint8_t *q8, const uint8_t *q_sc, const float *w,
                 for (int h = 0; h < Hi; ++h) {
                     double dot = 0.0;
                     for (int d = 0; d < Di; ++d) {
-                        size_t ki = ((size_t)b * T_cap + t) * Di + d;
+                        const uint8_t *krow = k8 + ((size_t)b * T_cap + t) * E;
                         size_t ks = ((size_t)b * T_cap + t) * nb + d / 32;
-                        double kv = orc_e4m3(k8[ki]) * orc_e8m0(k_sc[ks]);
+                        double kv = orc_code_at(krow, fmt, d) * orc_e8m0(k_sc[ks]);
                         if (isnan(kv)) bad = 1;
                         dot += qh[(size_t)h * Di + d] * kv;
                     }

@@ -52,3 +52,28 @@ def test_bf16_all_codes_match_torch(orc):
     nan = np.isnan(lib)
     assert np.array_equal(np.isnan(ours), nan)
     assert np.array_equal(ours[~nan], lib[~nan])
+
+
+# OCP Microscaling Formats (MX) v1.0, element type FP4 (E2M1): magnitudes of codes 0-7
+# written out from the format's definition (2 exponent bits, bias 1, 1 mantissa bit,
+# exponent 0 subnormal); code + 8 is the negative.  No library here decodes fp4, so the
+# table is the independent side.
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_all_codes_match_table(orc):
+    for c in range(16):
+        want = E2M1_TABLE[c & 7] * (-1.0 if c & 8 else 1.0)
+        got = orc.e2m1_value(c)
+        assert got == want, (c, got, want)
+        assert math.copysign(1.0, got) == (-1.0 if c & 8 else 1.0), c
+    # only the low four bits are a code: the byte's other nibble is the neighbour element
+    assert orc.e2m1_value(0x07) == 6.0 and orc.e2m1_value(0x0F) == -6.0
+
+
+def test_e2m1_values_are_exact_e4m3_values():
+    # every fp4 value survives torch's e4m3 cast unchanged, which is what lets the
+    # indexer pins compare the two formats on shared values
+    vals = torch.tensor(E2M1_TABLE + [-v for v in E2M1_TABLE], dtype=torch.float64)
+    back = vals.to(torch.float8_e4m3fn).to(torch.float64)
+    assert torch.equal(back, vals)

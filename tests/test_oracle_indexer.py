@@ -120,3 +120,109 @@ def test_refuses_bad_sizes(orc):
     with pytest.raises(orc.OracleError):
         # T = 16 visible rows but a cache of only 8
         orc.index_scores(inp.q8, inp.q_sc, inp.w, inp.k8[:, :8], inp.k_sc[:, :8], 15, 1)
+
+
+# -- fp4 (e2m1) index codes: DeepSeek-V4.1-Flash-NVFP4 model.py, Indexer.forward
+# quantises queries and keys to fp4 with one ue8m0 scale per 32 elements --------------
+
+from tests.test_oracle_formats import E2M1_TABLE  # noqa: E402
+
+
+def fp4_table_decode(packed, scales):
+    """Test-local decoder: table lookup of both nibbles (element 2j low), then the
+    block scale from torch's e8m0 cast."""
+    p = np.asarray(packed, dtype=np.uint8)
+    lut = np.array(E2M1_TABLE + [-v for v in E2M1_TABLE])
+    vals = np.stack([lut[p & 15], lut[p >> 4]], axis=-1).reshape(*p.shape[:-1], 2 * p.shape[-1])
+    s = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e8m0fnu)
+    s = s.to(torch.float64).numpy()
+    return (vals.reshape(*vals.shape[:-1], -1, 32) * s[..., None]).reshape(vals.shape)
+
+
+def fp4_table_encode(codes):
+    """Pack 4-bit codes [..., Di] two per byte (element 2j in the low nibble)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("Di", [64, 128])
+def test_fp4_one_hot_weights_reduce_to_library_matmul(orc, Di):
+    inp = synth.make_step(B=2, S=1, start_pos=39, ratio=2, Hi=16, Di=Di, H=16, D=64, W=8,
+                          index_topk=8, seed=21 + Di, index_fmt="e2m1")
+    assert inp.q8.shape[-1] == Di // 2 and inp.k8.shape[-1] == Di // 2
+    qd = fp4_table_decode(inp.q8, inp.q_sc)     # [B,1,Hi,Di]
+    kd = fp4_table_decode(inp.k8, inp.k_sc)     # [B,T,Di]
+    for h in (0, 7, 15):
+        w = np.zeros_like(inp.w)
+        w[..., h] = 1.0
+        got = orc.index_scores(inp.q8, inp.q_sc, w, inp.k8, inp.k_sc, inp.start_pos, inp.ratio,
+                               "e2m1")
+        for bb in range(inp.B):
+            want = np.maximum((torch.from_numpy(kd[bb]) @ torch.from_numpy(qd[bb, 0, h])).numpy(), 0.0)
+            np.testing.assert_allclose(got[bb, 0], want, rtol=1e-12, atol=1e-12)
+
+
+def test_fp4_closed_form_constant_blocks(orc):
+    # constant codes per head / key, a distinct scale per (row, block): the closed form
+    # needs every element matched with its own block's scale
+    Hi, Di, T = 4, 128, 3
+    q_codes, q_vals = [2, 4, 10, 5], [1.0, 2.0, -1.0, 3.0]
+    k_codes, k_vals = [2, 1, 3], [1.0, 0.5, 1.5]
+    a = np.array([[127, 128, 125, 130], [120, 127, 131, 126],
+                  [129, 129, 127, 124], [126, 122, 128, 133]], dtype=np.uint8)
+    b = np.array([[127, 126, 130, 121], [132, 127, 127, 127], [125, 129, 122, 128]],
+                 dtype=np.uint8)
+    w = np.array([0.5, 0.25, 1.0, 0.125], dtype=np.float32)
+    q4 = fp4_table_encode(np.array(q_codes)[:, None].repeat(Di, 1)).reshape(1, 1, Hi, Di // 2)
+    k4 = fp4_table_encode(np.array(k_codes)[:, None].repeat(Di, 1)).reshape(1, T, Di // 2)
+    got = orc.index_scores(q4, a.reshape(1, 1, Hi, 4), w.reshape(1, 1, Hi), k4,
+                           b.reshape(1, T, 4), start_pos=T - 1, ratio=1, fmt="e2m1")
+    want = np.zeros(T)
+    for t in range(T):
+        for h in range(Hi):
+            dot = 32 * q_vals[h] * k_vals[t] * sum(
+                2.0 ** ((int(a[h, c]) - 127) + (int(b[t, c]) - 127)) for c in range(4))
+            want[t] += float(w[h]) * max(0.0, dot)
+    assert np.array_equal(got[0, 0], want)
+
+
+def test_fp4_equals_e4m3_on_shared_values(orc):
+    # the same values written as fp4 codes and as e4m3 bytes (torch's cast) give
+    # bit-identical scores: the two formats differ only in how codes are stored
+    rng = np.random.default_rng(17)
+    B, S, Hi, Di, T = 2, 3, 32, 128, 40
+    start_pos = T - S
+    qc = rng.integers(0, 16, size=(B, S, Hi, Di))
+    kc = rng.integers(0, 16, size=(B, T, Di))
+    q_sc = rng.integers(120, 135, size=(B, S, Hi, Di // 32)).astype(np.uint8)
+    k_sc = rng.integers(120, 135, size=(B, T, Di // 32)).astype(np.uint8)
+    w = rng.random((B, S, Hi), dtype=np.float32)
+    lut = np.array(E2M1_TABLE + [-v for v in E2M1_TABLE])
+
+    def e4m3(codes):
+        return torch.from_numpy(lut[codes]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+    s4 = orc.index_scores(fp4_table_encode(qc), q_sc, w, fp4_table_encode(kc), k_sc,
+                          start_pos, 1, "e2m1")
+    s8 = orc.index_scores(e4m3(qc), q_sc, w, e4m3(kc), k_sc, start_pos, 1, "e4m3")
+    assert np.array_equal(s4, s8)
+    assert np.isfinite(s4[:, -1]).all()
+
+
+def test_fp4_nibble_order_does_not_change_scores(orc):
+    # both nibbles of a byte share one scale block, so swapping them in q and k alike
+    # permutes the terms of every dot product and leaves each score as it is
+    inp = synth.make_step(B=1, S=2, start_pos=30, ratio=1, Hi=16, Di=64, H=16, D=64, W=8,
+                          index_topk=8, seed=23, index_fmt="e2m1")
+    swap = lambda p: ((p >> 4) | (p << 4)).astype(np.uint8)  # noqa: E731
+    s = orc.index_scores(inp.q8, inp.q_sc, inp.w, inp.k8, inp.k_sc, 30, 1, "e2m1")
+    t = orc.index_scores(swap(inp.q8), inp.q_sc, inp.w, swap(inp.k8), inp.k_sc, 30, 1, "e2m1")
+    np.testing.assert_allclose(t, s, rtol=1e-13, atol=0)
+
+
+def test_fp4_refuses_mismatched_rows(orc):
+    inp = synth.make_step(B=1, S=1, start_pos=15, ratio=1, Hi=16, Di=64, H=16, D=64, W=8,
+                          index_topk=8, seed=1)
+    with pytest.raises(orc.OracleError):
+        # e4m3 rows (Di bytes) passed as fp4 (Di/2 bytes expected)
+        orc.index_scores(inp.q8, inp.q_sc, inp.w, inp.k8, inp.k_sc, 15, 1, "e2m1")

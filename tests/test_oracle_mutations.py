@@ -31,14 +31,19 @@ def _one_hot(orc):
     TI.test_one_hot_weights_reduce_to_library_matmul(orc, 128)
 
 
+def _one_hot_fp4(orc):
+    TI.test_fp4_one_hot_weights_reduce_to_library_matmul(orc, 64)
+    TI.test_fp4_one_hot_weights_reduce_to_library_matmul(orc, 128)
+
+
 MUTANTS = [
     # (name, original text, mutated text, pins expected to notice)
     ("relu dropped", "s += wh * (dot > 0.0 ? dot : 0.0);", "s += wh * dot;",
      [TI.test_closed_form_constant_blocks, TI.test_relu_identity_gives_linear_form]),
     ("relu sign flipped", "s += wh * (dot > 0.0 ? dot : 0.0);", "s += wh * (dot < 0.0 ? -dot : 0.0);",
      [TI.test_closed_form_constant_blocks, TI.test_relu_identity_gives_linear_form]),
-    ("key scale dropped", "double kv = orc_e4m3(k8[ki]) * orc_e8m0(k_sc[ks]);",
-     "double kv = orc_e4m3(k8[ki]);", [TI.test_closed_form_constant_blocks, _one_hot]),
+    ("key scale dropped", "double kv = orc_code_at(krow, fmt, d) * orc_e8m0(k_sc[ks]);",
+     "double kv = orc_code_at(krow, fmt, d);", [TI.test_closed_form_constant_blocks, _one_hot]),
     ("key scale block reversed", "size_t ks = ((size_t)b * T_cap + t) * nb + d / 32;",
      "size_t ks = ((size_t)b * T_cap + t) * nb + (nb - 1 - d / 32);",
      [TI.test_closed_form_constant_blocks, _one_hot]),
@@ -54,6 +59,13 @@ MUTANTS = [
      [TF.test_e4m3_all_codes_match_torch, TF.test_e4m3_closed_forms]),
     ("e4m3 subnormal exponent", "v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);",
      [TF.test_e4m3_all_codes_match_torch, TF.test_e4m3_closed_forms]),
+    ("e2m1 bias", "v = ldexp(1.0 + (double)m / 2.0, e - 1);", "v = ldexp(1.0 + (double)m / 2.0, e - 2);",
+     [TF.test_e2m1_all_codes_match_table, _one_hot_fp4]),
+    ("e2m1 subnormal", "v = (double)m / 2.0;", "v = (double)m;", [TF.test_e2m1_all_codes_match_table]),
+    ("fp4 row stride", "const size_t E = fmt == ORC_FMT_E2M1 ? (size_t)Di / 2 : (size_t)Di;",
+     "const size_t E = (size_t)Di;", [_one_hot_fp4, TI.test_fp4_closed_form_constant_blocks]),
+    ("fp4 nibble from the wrong byte", "uint8_t byte = row[d / 2];", "uint8_t byte = row[d / 4];",
+     [_one_hot_fp4, TI.test_fp4_equals_e4m3_on_shared_values]),
     ("topk tie rule reversed", "return (x->t > y->t) - (x->t < y->t);",
      "return (x->t < y->t) - (x->t > y->t);", [TT.test_property_checker_with_ties_and_prefill]),
     ("topk ascending sort dropped", "qsort(sel, (size_t)take, sizeof(int), orc_int_cmp);", "",
