@@ -44,7 +44,9 @@ def step_bytes(sp: dict) -> dict:
     dv = sp.get("dv", D)
     T = (sp0 + S) // r
     keff = min(k, T)
-    key_row = Di + Di // 32
+    # an index row: its codes (one e4m3 byte, or half a byte of fp4, per element) and
+    # one scale byte per 32 elements
+    key_row = (Di // 2 if sp.get("index_fmt", "e4m3") == "e2m1" else Di) + Di // 32
     indexer = B * T * key_row + B * S * Hi * (key_row + 4) + 4 * B * S * T
     topk = 4 * B * S * T + 4 * B * S * keff
     if S == 1:
@@ -85,9 +87,16 @@ def traffic_for(kernel: str, workload: str, srcs):
     return rec.get("bytes_per_launch")
 
 
-def kernel_sources(ksrc: str):
+def kernel_sources(ksrc):
+    """The source files a kernel is built from (ksrc: its own file, or a tuple of them)."""
     csrc = os.path.join(ROOT, "lightning_indexer_top_amd", "csrc")
-    return [os.path.join(csrc, f) for f in (ksrc, "tile_ops.h", "select_ops.h", "lit_internal.h")]
+    own = (ksrc,) if isinstance(ksrc, str) else tuple(ksrc)
+    return [os.path.join(csrc, f) for f in own + ("tile_ops.h", "select_ops.h", "lit_internal.h")]
+
+
+def fused_sources(spec: dict):
+    fmt = spec.get("index_fmt", "e4m3")
+    return ("fused_kernel.h", f"fused_{fmt}.hip")
 
 
 def read_counters(path: str, counter: str) -> dict:
@@ -179,9 +188,10 @@ def main() -> int:
     ap.add_argument("--traffic-cmd", default="", help="the profiled command, recorded with --traffic-from")
     args = ap.parse_args()
     if args.traffic_from:
+        from lightning_indexer_top_amd import synth
         rec = traffic_record(args.traffic_from[0], args.traffic_from[1], "fused_decode_kernel",
-                             "fused_decode.hip", args.copy_probe_mb or 256, args.traffic_cmd,
-                             args.workload)
+                             fused_sources(synth.WORKLOADS[args.workload]), args.copy_probe_mb or 256,
+                             args.traffic_cmd, args.workload)
         path = traffic_path("fused_decode_kernel", args.workload)
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
@@ -198,6 +208,7 @@ def main() -> int:
     from lightning_indexer_top_amd import synth
 
     spec = dict(synth.WORKLOADS[args.workload])
+    fmt = spec.get("index_fmt", "e4m3")
     sb = step_bytes(spec)
     n_inst = args.instances or max(2, min(512, math.ceil(3 * MALL_BYTES / sb["step"])))
     K, Wm = args.steps, args.warmup
@@ -214,7 +225,7 @@ def main() -> int:
                                        k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
                                        comp_kv=d["comp_kv"], start_pos=spec["start_pos"],
                                        ratio=spec["ratio"], index_topk=spec["index_topk"],
-                                       W=spec["W"], scale=spec["D"] ** -0.5)
+                                       W=spec["W"], scale=spec["D"] ** -0.5, fmt=fmt)
         insts.append(d)
         argv.append(a)
         keep.append((idx, out))
@@ -282,7 +293,7 @@ def main() -> int:
     stage_calls = {
         "indexer": [(lambda j=j: L.lit_indexer_scores(
             insts[j]["q8"], insts[j]["q_sc"], insts[j]["w"], insts[j]["k8"], insts[j]["k_sc"],
-            spec["start_pos"], spec["ratio"], scores=scores[j])) for j in range(n_inst)],
+            spec["start_pos"], spec["ratio"], scores=scores[j], fmt=fmt)) for j in range(n_inst)],
         "topk": [(lambda j=j: L.lit_topk(scores[j], spec["start_pos"], spec["ratio"],
                                          spec["index_topk"], idx=keep[j][0]))
                  for j in range(n_inst)],
@@ -307,7 +318,7 @@ def main() -> int:
     step_gbps = sb["step"] / (ms_per_step * 1e-3) / 1e9
     if fused:
         # one kernel per step: its average duration is the event-timed region / K
-        dom, kname, ksrc = "step", "fused_decode_kernel", "fused_decode.hip"
+        dom, kname, ksrc = "step", "fused_decode_kernel", fused_sources(spec)
         dom_us = gpu_ms * 1e3 / K
         dom_bytes = sb["step"]
     else:
@@ -343,11 +354,12 @@ def main() -> int:
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "queries/s", "n_gpus": 1,
         "steps": K, "warmup": Wm, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3+bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": ("fp4-e2m1" if fmt == "e2m1" else "fp8-e4m3") + "+bf16", "data": "synthetic",
         "config": {"workload": args.workload, "batch": spec["B"], "query_tokens": spec["S"],
                    "context": spec["start_pos"] + spec["S"], "compress_ratio": spec["ratio"],
                    "window": spec["W"], "heads": spec["H"], "head_dim": spec["D"],
-                   "index_heads": spec["Hi"], "index_dim": spec["Di"],
+                   "index_heads": spec["Hi"], "index_dim": spec["Di"], "index_format": fmt,
                    "index_topk": spec["index_topk"], "input_instances": n_inst,
                    "timing": "HIP graph replay over rotating cold-cache instances",
                    "step_form": "fused single kernel" if fused else "indexer, top-k, attention kernels"},

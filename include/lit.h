@@ -5,7 +5,8 @@
  * The step has three parts, each a call below, plus a fused call:
  *   1. lit_indexer_scores : the lightning indexer scores every visible
  *      compressed-KV row for every query (head-weighted ReLU of q.k over e4m3
- *      codes with one ue8m0 scale per 32 values);
+ *      codes with one ue8m0 scale per 32 values; lit_indexer_scores_fmt also
+ *      takes fp4 e2m1 codes with the same scales);
  *   2. lit_topk           : a per-query selector keeps the index_topk best rows;
  *   3. lit_sparse_attn    : attention with an online softmax over the sliding
  *      window and the selected compressed rows, one shared KV head (K = V).
@@ -14,7 +15,7 @@
  *
  * Sources (page title, symbol):
  *   [V4.1] DeepSeek-V4.1-Flash-NVFP4, inference/model.py -- module globals
- *          (fp8 block size 32, ue8m0 scales), get_window_topk_idxs,
+ *          (fp8 and fp4 block size 32, ue8m0 scales), get_window_topk_idxs,
  *          Indexer.__init__/forward, Attention._window_kv/_compress_kv/forward
  *          (the sparse_attn call and its int32 [b, m, topk] index lists).
  *   [V3.2] DeepSeek-V3.2-Exp, inference/model.py -- Indexer.forward
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LIT_ABI_VERSION 1
+#define LIT_ABI_VERSION 2
 
 typedef enum {
     LIT_OK = 0,
@@ -89,6 +90,28 @@ lit_status lit_indexer_scores(const uint8_t *q8, const uint8_t *q_sc, const floa
                               const uint8_t *k8, const uint8_t *k_sc, int B, int S,
                               int Hi, int Di, int T_cap, int start_pos, int ratio,
                               float *scores, int ld_scores, void *stream);
+
+/*
+ * Index-code formats.  Both carry one ue8m0 scale byte per 32 elements.
+ *   LIT_INDEX_E4M3: one e4m3 byte per element, rows of Di bytes.
+ *   LIT_INDEX_E2M1: fp4 -- [V4.1] Indexer.forward quantises the index queries
+ *                   and keys to fp4 with 32-element ue8m0 blocks (fp4_act_quant
+ *                   with the module's fp4 block size); two e2m1 codes per byte,
+ *                   element 2j in the low nibble of byte j, rows of Di/2 bytes.
+ */
+typedef enum { LIT_INDEX_E4M3 = 0, LIT_INDEX_E2M1 = 1 } lit_index_format;
+
+/*
+ * lit_indexer_scores_fmt -- lit_indexer_scores with the code format of q8 and k8
+ * given by index_format (a lit_index_format; q and k share it).  With
+ * LIT_INDEX_E2M1, q8 is [B, S, Hi, Di/2] and k8 is [B, T_cap, Di/2] bytes; every
+ * other argument, requirement and result is as above (Di is the element count).
+ * An unknown format is refused with LIT_E_UNSUPPORTED.
+ */
+lit_status lit_indexer_scores_fmt(int index_format, const uint8_t *q8, const uint8_t *q_sc,
+                                  const float *w, const uint8_t *k8, const uint8_t *k_sc, int B,
+                                  int S, int Hi, int Di, int T_cap, int start_pos, int ratio,
+                                  float *scores, int ld_scores, void *stream);
 
 /*
  * lit_topk -- [V4.1] Indexer.forward (top-k, re-sorted into position order,
@@ -193,7 +216,7 @@ size_t lit_sparse_attn_workspace_bytes(int B, int S, int H, int dv, int W, int K
 typedef struct lit_step_args {
     /* positions */
     int B, S, start_pos, ratio;
-    /* indexer */
+    /* indexer (code rows are Di bytes, or Di/2 with index_format LIT_INDEX_E2M1) */
     int Hi, Di, index_topk, T_cap;
     const uint8_t *q8;   /* [B,S,Hi,Di]      */
     const uint8_t *q_sc; /* [B,S,Hi,Di/32]   */
@@ -218,6 +241,7 @@ typedef struct lit_step_args {
     void *state;
     size_t state_bytes;
     int flags; /* LIT_STEP_* bits */
+    int index_format; /* lit_index_format of q8 / k8 (0 = LIT_INDEX_E4M3) */
 } lit_step_args;
 
 lit_status lit_sparse_step(const lit_step_args *args, void *ws, size_t ws_bytes, void *stream);

@@ -3,8 +3,9 @@
 // What is computed (DeepSeek-V4.1-Flash-NVFP4 inference/model.py, Indexer.forward;
 // DeepSeek-V3.2-Exp inference/model.py, fp8_index):
 //   score[b,i,t] = sum_h w[b,i,h] * relu( qhat[b,i,h,:] . khat[b,t,:] )
-// with e4m3 operands carrying one ue8m0 scale per 32 values, and -inf for the rows a
-// query cannot see yet (t >= (start_pos+i+1)/ratio).
+// with e4m3 (or fp4 e2m1, V4.1's own indexer precision) operands carrying one ue8m0
+// scale per 32 values, and -inf for the rows a query cannot see yet
+// (t >= (start_pos+i+1)/ratio).
 //
 // Mapping onto the chip.  The q.k contraction of 16 heads against 16 keys is one
 // V_MFMA_SCALE_F32_16X16X128_F8F6F4: A = 16 query heads (rows), B = 16 keys
@@ -14,6 +15,8 @@
 // scale byte lane group g supplies covers K block 32g..32g+31.  So a lane loads row
 // bytes [16g, 16g+16) and [64+16g, 64+16g+16) and the scale of block g -- memory
 // order is K order.  Di = 64 uses only the low half (K 0..63, the high half zero).
+// fp4 codes take the same instruction with 16 bytes (32 codes, one scale block) per
+// lane: a 128-dim fp4 key is 64 bytes, one load per lane.
 // C comes back as lane (g, c), register r = head 4g+r, key c; the ReLU, the head
 // weights and the sum over the lane's 4 heads run in registers, and two cross-lane
 // adds finish the head sum.  Four key tiles are scored together so that their MFMAs
@@ -33,7 +36,7 @@ namespace {
 constexpr int kWaves = 4;  // waves per workgroup
 constexpr int kU = 4;      // 16-key tiles per wave
 
-template <int DI, int HT, int QG>
+template <int DI, int FMT, int HT, int QG>
 __global__ __launch_bounds__(kWaves * 64) void indexer_scores_kernel(IndexerArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -68,20 +71,20 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_kernel(IndexerArgs
     IdxKeys kb[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-        kb[u] = load_idx_keys<DI>(a, (size_t)b * a.T_cap + min(t0 + 16 * u + c, a.T - 1), g);
+        kb[u] = load_idx_keys<DI, FMT>(a, (size_t)b * a.T_cap + min(t0 + 16 * u + c, a.T - 1), g);
 
-    IdxQuery<DI, HT> qs[QG];
+    IdxQuery<DI, FMT, HT> qs[QG];
 #pragma unroll
     for (int qq = 0; qq < QG; ++qq) {
         const int i = i0 + qq;
-        load_idx_query<DI, HT>(qs[qq], a, bs0 + (i < a.S ? i : 0), i < a.S, g, c);
+        load_idx_query<DI, FMT, HT>(qs[qq], a, bs0 + (i < a.S ? i : 0), i < a.S, g, c);
     }
 
     static_assert(kU == 4, "idx_score4 scores four tiles");
     const int t = t0 + 16 * g + c;  // lane group g receives tile g's scores
 #pragma unroll
     for (int qq = 0; qq < QG; ++qq) {
-        const float s = idx_score4<DI, HT>(qs[qq], kb, g);
+        const float s = idx_score4<DI, FMT, HT>(qs[qq], kb, g);
         const int i = i0 + qq;
         if (i < a.S && t < a.T) {
             const int vis = (a.start_pos + i + 1) / a.ratio;
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_kernel(IndexerArgs
 // consecutive keys and the same queries (their query loads coalesce in the cache).
 constexpr int kQB = 32;
 
-template <int DI, int HT>
+template <int DI, int FMT, int HT>
 __global__ __launch_bounds__(kWaves * 64) void indexer_scores_multi_kernel(IndexerArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_multi_kernel(Index
     IdxKeys kb[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-        kb[u] = load_idx_keys<DI>(a, (size_t)b * a.T_cap + min(t0 + 16 * u + c, a.T - 1), g);
+        kb[u] = load_idx_keys<DI, FMT>(a, (size_t)b * a.T_cap + min(t0 + 16 * u + c, a.T - 1), g);
 
     static_assert(kU == 4, "idx_score4 scores four tiles");
     auto finish = [&](int i, float s) {
@@ -136,51 +139,51 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_multi_kernel(Index
             a.scores[(bs0 + i) * a.ld + t] = t < vis ? s : -INFINITY;
         }
     };
-    IdxQuery<DI, HT> qa, qb;
-    load_idx_query<DI, HT>(qa, a, bs0 + i0, true, g, c);
+    IdxQuery<DI, FMT, HT> qa, qb;
+    load_idx_query<DI, FMT, HT>(qa, a, bs0 + i0, true, g, c);
     for (int i = i0; i < i1; i += 2) {
         const bool second = i + 1 < i1;
-        load_idx_query<DI, HT>(qb, a, bs0 + (second ? i + 1 : i), true, g, c);
-        finish(i, idx_score4<DI, HT>(qa, kb, g));
-        if (i + 2 < i1) load_idx_query<DI, HT>(qa, a, bs0 + i + 2, true, g, c);
-        if (second) finish(i + 1, idx_score4<DI, HT>(qb, kb, g));
+        load_idx_query<DI, FMT, HT>(qb, a, bs0 + (second ? i + 1 : i), true, g, c);
+        finish(i, idx_score4<DI, FMT, HT>(qa, kb, g));
+        if (i + 2 < i1) load_idx_query<DI, FMT, HT>(qa, a, bs0 + i + 2, true, g, c);
+        if (second) finish(i + 1, idx_score4<DI, FMT, HT>(qb, kb, g));
     }
 }
 
-template <int DI, int HT>
+template <int DI, int FMT, int HT>
 hipError_t launch_multi(const IndexerArgs &a, hipStream_t stream) {
     const int keys_per_block = kWaves * 16 * kU;
     dim3 grid((a.T + keys_per_block - 1) / keys_per_block, a.B * ((a.S + kQB - 1) / kQB));
-    hipLaunchKernelGGL((indexer_scores_multi_kernel<DI, HT>), grid, dim3(kWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((indexer_scores_multi_kernel<DI, FMT, HT>), grid, dim3(kWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int DI, int HT, int QG>
+template <int DI, int FMT, int HT, int QG>
 hipError_t launch_cfg(const IndexerArgs &a, hipStream_t stream) {
     const int keys_per_block = kWaves * 16 * kU;
     dim3 grid((a.T + keys_per_block - 1) / keys_per_block, a.B * ((a.S + QG - 1) / QG));
-    hipLaunchKernelGGL((indexer_scores_kernel<DI, HT, QG>), grid, dim3(kWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((indexer_scores_kernel<DI, FMT, HT, QG>), grid, dim3(kWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int DI>
+template <int DI, int FMT>
 hipError_t launch_di(const IndexerArgs &a, hipStream_t stream) {
     const int HT = a.Hi / 16;
     const bool multi = a.S > 1;
     if (a.S >= kQB) {
         switch (HT) {
-            case 1: return launch_multi<DI, 1>(a, stream);
-            case 2: return launch_multi<DI, 2>(a, stream);
-            case 3: return launch_multi<DI, 3>(a, stream);
-            case 4: return launch_multi<DI, 4>(a, stream);
+            case 1: return launch_multi<DI, FMT, 1>(a, stream);
+            case 2: return launch_multi<DI, FMT, 2>(a, stream);
+            case 3: return launch_multi<DI, FMT, 3>(a, stream);
+            case 4: return launch_multi<DI, FMT, 4>(a, stream);
             default: return hipErrorInvalidValue;
         }
     }
     switch (HT) {
-        case 1: return multi ? launch_cfg<DI, 1, 4>(a, stream) : launch_cfg<DI, 1, 1>(a, stream);
-        case 2: return multi ? launch_cfg<DI, 2, 2>(a, stream) : launch_cfg<DI, 2, 1>(a, stream);
-        case 3: return launch_cfg<DI, 3, 1>(a, stream);
-        case 4: return launch_cfg<DI, 4, 1>(a, stream);
+        case 1: return multi ? launch_cfg<DI, FMT, 1, 4>(a, stream) : launch_cfg<DI, FMT, 1, 1>(a, stream);
+        case 2: return multi ? launch_cfg<DI, FMT, 2, 2>(a, stream) : launch_cfg<DI, FMT, 2, 1>(a, stream);
+        case 3: return launch_cfg<DI, FMT, 3, 1>(a, stream);
+        case 4: return launch_cfg<DI, FMT, 4, 1>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -189,8 +192,13 @@ hipError_t launch_di(const IndexerArgs &a, hipStream_t stream) {
 
 hipError_t launch_indexer_scores(const IndexerArgs &a, hipStream_t stream) {
     if (a.T <= 0 || a.B <= 0 || a.S <= 0) return hipSuccess;
-    if (a.Di == 64) return launch_di<64>(a, stream);
-    if (a.Di == 128) return launch_di<128>(a, stream);
+    if (a.fmt == kFmtE2M1) {
+        if (a.Di == 64) return launch_di<64, kFmtE2M1>(a, stream);
+        if (a.Di == 128) return launch_di<128, kFmtE2M1>(a, stream);
+        return hipErrorInvalidValue;
+    }
+    if (a.Di == 64) return launch_di<64, kFmtE4M3>(a, stream);
+    if (a.Di == 128) return launch_di<128, kFmtE4M3>(a, stream);
     return hipErrorInvalidValue;
 }
 

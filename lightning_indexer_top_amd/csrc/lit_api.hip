@@ -1,6 +1,7 @@
 // lit_api.hip -- the C ABI declared in include/lit.h: host-side argument checks,
 // workspace sizing, and the stream-ordered launches of the kernels in indexer.hip,
-// topk.hip and attention.hip.  Nothing here allocates, frees or synchronises.
+// topk.hip, attention.hip and the fused decode kernel.  Nothing here allocates, frees
+// or synchronises.
 #include "../../include/lit.h"
 
 #include <limits.h>
@@ -29,9 +30,10 @@ int topk_width(int S, int start_pos, int ratio, int index_topk) {
     return (int)(index_topk < T ? index_topk : T);
 }
 
-lit_status check_indexer(const uint8_t *q8, const uint8_t *q_sc, const float *w, const uint8_t *k8,
-                         const uint8_t *k_sc, int B, int S, int Hi, int Di, int T_cap, int start_pos,
-                         int ratio, const float *scores, int ld_scores) {
+lit_status check_indexer(int fmt, const uint8_t *q8, const uint8_t *q_sc, const float *w,
+                         const uint8_t *k8, const uint8_t *k_sc, int B, int S, int Hi, int Di, int T_cap,
+                         int start_pos, int ratio, const float *scores, int ld_scores) {
+    if (fmt != LIT_INDEX_E4M3 && fmt != LIT_INDEX_E2M1) return LIT_E_UNSUPPORTED;
     if (B < 0 || S < 0 || start_pos < 0 || ratio < 1 || T_cap < 0) return LIT_E_SHAPE;
     if ((long)start_pos + S > INT_MAX) return LIT_E_SHAPE;
     const long T = ((long)start_pos + S) / ratio;
@@ -108,16 +110,24 @@ const char *lit_status_str(int status) {
 
 int lit_abi_version(void) { return LIT_ABI_VERSION; }
 
+lit_status lit_indexer_scores_fmt(int index_format, const uint8_t *q8, const uint8_t *q_sc,
+                                  const float *w, const uint8_t *k8, const uint8_t *k_sc, int B,
+                                  int S, int Hi, int Di, int T_cap, int start_pos, int ratio,
+                                  float *scores, int ld_scores, void *stream) {
+    lit_status st = check_indexer(index_format, q8, q_sc, w, k8, k_sc, B, S, Hi, Di, T_cap,
+                                  start_pos, ratio, scores, ld_scores);
+    if (st != LIT_OK) return st;
+    IndexerArgs a{q8, q_sc, w, k8, k_sc, index_format, B, S, Hi, Di, T_cap, start_pos, ratio,
+                  (start_pos + S) / ratio, scores, (long)ld_scores};
+    return hip_status(launch_indexer_scores(a, (hipStream_t)stream));
+}
+
 lit_status lit_indexer_scores(const uint8_t *q8, const uint8_t *q_sc, const float *w,
                               const uint8_t *k8, const uint8_t *k_sc, int B, int S, int Hi, int Di,
                               int T_cap, int start_pos, int ratio, float *scores, int ld_scores,
                               void *stream) {
-    lit_status st = check_indexer(q8, q_sc, w, k8, k_sc, B, S, Hi, Di, T_cap, start_pos, ratio,
-                                  scores, ld_scores);
-    if (st != LIT_OK) return st;
-    IndexerArgs a{q8, q_sc, w, k8, k_sc, B, S, Hi, Di, T_cap, start_pos, ratio,
-                  (start_pos + S) / ratio, scores, (long)ld_scores};
-    return hip_status(launch_indexer_scores(a, (hipStream_t)stream));
+    return lit_indexer_scores_fmt(LIT_INDEX_E4M3, q8, q_sc, w, k8, k_sc, B, S, Hi, Di, T_cap,
+                                  start_pos, ratio, scores, ld_scores, stream);
 }
 
 size_t lit_topk_workspace_bytes(int B, int S, int start_pos, int ratio, int index_topk) {
@@ -194,7 +204,8 @@ static FusedPlan step_fused_plan(const lit_step_args *s) {
     p.ok = false;
     if (s->flags & LIT_STEP_UNFUSED) return p;
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
-    return plan_fused(s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D, s->dv, s->W, keff);
+    return plan_fused(s->index_format, s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D, s->dv,
+                      s->W, keff);
 }
 
 static lit_status check_step(const lit_step_args *s) {
@@ -204,8 +215,8 @@ static lit_status check_step(const lit_step_args *s) {
     const long T = ((long)s->start_pos + s->S) / s->ratio;
     if (T > INT_MAX / 4) return LIT_E_SHAPE;
     const int ld = (int)round_up((size_t)(T > 0 ? T : 1), 4);
-    lit_status st = check_indexer(s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->B, s->S, s->Hi, s->Di,
-                                  s->T_cap, s->start_pos, s->ratio, (const float *)16, ld);
+    lit_status st = check_indexer(s->index_format, s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->B, s->S,
+                                  s->Hi, s->Di, s->T_cap, s->start_pos, s->ratio, (const float *)16, ld);
     if (st != LIT_OK) return st;
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
     if (s->index_topk < 0) return LIT_E_SHAPE;
@@ -262,8 +273,8 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
         if (((uintptr_t)s->state & 255u) != 0) return LIT_E_ALIGN;
         if (ws_bytes < fused_ws_bytes(fp, s->dv)) return LIT_E_WORKSPACE;
         FusedArgs f{};
-        f.ia = IndexerArgs{s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->B, s->S, s->Hi, s->Di, s->T_cap,
-                           s->start_pos, s->ratio, T, nullptr, 0};
+        f.ia = IndexerArgs{s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->index_format, s->B, s->S, s->Hi,
+                           s->Di, s->T_cap, s->start_pos, s->ratio, T, nullptr, 0};
         f.aa = AttnArgs{s->q, s->B, s->S, s->H, s->D, s->dv, s->W > 0 ? s->win_kv : nullptr, s->R,
                         nullptr, s->W, s->start_pos, s->comp_kv, s->T_cap, nullptr, keff, s->sink,
                         s->scale, s->out, nullptr};
@@ -276,8 +287,8 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
         return LIT_OK;
     }
     if (keff > 0) {
-        IndexerArgs ia{s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->B, s->S, s->Hi, s->Di, s->T_cap,
-                       s->start_pos, s->ratio, T, scores, ld};
+        IndexerArgs ia{s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->index_format, s->B, s->S, s->Hi,
+                       s->Di, s->T_cap, s->start_pos, s->ratio, T, scores, ld};
         if ((e = launch_indexer_scores(ia, hs)) != hipSuccess) return hip_status(e);
     }
     if ((e = mark(1)) != hipSuccess) return hip_status(e);

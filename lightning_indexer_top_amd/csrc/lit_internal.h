@@ -19,12 +19,20 @@ constexpr float kLog2e = 1.4426950408889634f;
 // ---------------------------------------------------------------------------
 // Indexer scores (indexer.hip)
 // ---------------------------------------------------------------------------
+// Code formats of the index queries and keys (both use one ue8m0 scale per 32
+// elements): one e4m3 byte per element, or two e2m1 (fp4) codes per byte with
+// element 2j in the low nibble of byte j.
+constexpr int kFmtE4M3 = 0;
+constexpr int kFmtE2M1 = 1;
+__host__ __device__ constexpr int idx_row_bytes(int Di, int fmt) { return fmt == kFmtE2M1 ? Di / 2 : Di; }
+
 struct IndexerArgs {
-    const uint8_t *q8;    // [B,S,Hi,Di]
+    const uint8_t *q8;    // [B,S,Hi,E] codes, E = idx_row_bytes(Di, fmt)
     const uint8_t *q_sc;  // [B,S,Hi,Di/32]
     const float *w;       // [B,S,Hi]
-    const uint8_t *k8;    // [B,T_cap,Di]
+    const uint8_t *k8;    // [B,T_cap,E]
     const uint8_t *k_sc;  // [B,T_cap,Di/32]
+    int fmt;              // kFmtE4M3 or kFmtE2M1
     int B, S, Hi, Di, T_cap, start_pos, ratio;
     int T;                // (start_pos + S) / ratio, columns written per row
     float *scores;        // [B,S,ld]
@@ -150,9 +158,16 @@ struct FusedPlan {
     long ld;
     size_t dyn_bytes;
 };
-FusedPlan plan_fused(int B, int S, int start_pos, int ratio, int Hi, int Di, int D, int dv, int W, int keff);
+FusedPlan plan_fused(int fmt, int B, int S, int start_pos, int ratio, int Hi, int Di, int D, int dv, int W,
+                     int keff);
 size_t fused_state_bytes(const FusedPlan &p);  // zero-filled before first use
 size_t fused_ws_bytes(const FusedPlan &p, int dv);
 hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream);
+// The kernels of each index-code format (fused_e4m3.hip, fused_e2m1.hip): launch, and
+// co-resident workgroups per CU for a shape (0 when not instantiated).
+hipError_t launch_fused_e4m3(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
+hipError_t launch_fused_e2m1(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
+int fused_per_cu_e4m3(int D, int DI, int HT, size_t dyn_bytes, bool cached);
+int fused_per_cu_e2m1(int D, int DI, int HT, size_t dyn_bytes, bool cached);
 
 }  // namespace lit

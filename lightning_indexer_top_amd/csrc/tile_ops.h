@@ -18,41 +18,57 @@ __device__ inline void wave_lds_sync() {
 // ---------------------------------------------------------------------------
 // Indexer tile (V_MFMA_SCALE_F32_16X16X128_F8F6F4).
 //
-// Operand layout measured on gfx950: lane l = 16g + c holds row/column c; its bytes
-// 0-15 are K = 16g..16g+15, bytes 16-31 are K = 64+16g..64+16g+15, and the scale byte
-// lane group g supplies covers K block 32g..32g+31.  A lane therefore loads row bytes
-// [16g, 16g+16) and [64+16g, 64+16g+16) and the scale of block g: memory order is K
-// order.  A 64-dim row uses only the low half (K 0..63).  C comes back as lane (g, c),
-// register r = A row 4g+r, B column c.
+// Operand layouts measured on gfx950, lane l = 16g + c holding row/column c:
+//   e4m3: bytes 0-15 are K = 16g..16g+15, bytes 16-31 are K = 64+16g..64+16g+15, and
+//         the scale byte lane group g supplies covers K block 32g..32g+31.  A lane
+//         loads row bytes [16g, 16g+16) and [64+16g, 64+16g+16): memory order is K
+//         order.  A 64-dim row uses only the low half (K 0..63).
+//   e2m1: the first 4 registers are K = 32g..32g+31 (two codes a byte), with the
+//         scale of block g.  A lane loads row bytes [16g, 16g+16) -- one 16-byte load
+//         per key -- and a 64-dim row (32 bytes) fills lane groups 0 and 1, the other
+//         two carrying zeros.
+// C comes back as lane (g, c), register r = A row 4g+r, B column c.
 // ---------------------------------------------------------------------------
-__device__ inline i32x8 mx_operand(const uint8_t *row, int g, bool wide) {
-    const u32x4 lo = *reinterpret_cast<const u32x4 *>(row + 16 * g);
-    u32x4 hi = {0u, 0u, 0u, 0u};
-    if (wide) hi = *reinterpret_cast<const u32x4 *>(row + 64 + 16 * g);
+template <int DI, int FMT>
+__device__ inline i32x8 mx_operand(const uint8_t *row, int g) {
     i32x8 v;
-    v[0] = (int)lo[0]; v[1] = (int)lo[1]; v[2] = (int)lo[2]; v[3] = (int)lo[3];
-    v[4] = (int)hi[0]; v[5] = (int)hi[1]; v[6] = (int)hi[2]; v[7] = (int)hi[3];
+    if constexpr (FMT == kFmtE2M1) {
+        // a 64-dim row: lane groups 2 and 3 re-read group 0 and 1's bytes (in bounds)
+        // and zero them, so no lane's load is conditional
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(row + 16 * (DI == 128 ? g : (g & 1)));
+        const bool live = DI == 128 || g < 2;
+        v[0] = live ? (int)x[0] : 0; v[1] = live ? (int)x[1] : 0;
+        v[2] = live ? (int)x[2] : 0; v[3] = live ? (int)x[3] : 0;
+        v[4] = 0; v[5] = 0; v[6] = 0; v[7] = 0;
+    } else {
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(row + 16 * g);
+        u32x4 hi = {0u, 0u, 0u, 0u};
+        if (DI == 128) hi = *reinterpret_cast<const u32x4 *>(row + 64 + 16 * g);
+        v[0] = (int)lo[0]; v[1] = (int)lo[1]; v[2] = (int)lo[2]; v[3] = (int)lo[3];
+        v[4] = (int)hi[0]; v[5] = (int)hi[1]; v[6] = (int)hi[2]; v[7] = (int)hi[3];
+    }
     return v;
 }
 
 // One query's index heads as MFMA A operands: HT tiles of 16 heads, their scale bytes,
 // and the head weights of the 4 C rows each lane receives.
-template <int DI, int HT>
+template <int DI, int FMT, int HT>
 struct IdxQuery {
     i32x8 a[HT];
     int s[HT];
     float w[HT][4];
 };
 
-template <int DI, int HT>
-__device__ inline void load_idx_query(IdxQuery<DI, HT> &q, const IndexerArgs &a, size_t qi, bool valid,
-                                      int g, int c) {
+template <int DI, int FMT, int HT>
+__device__ inline void load_idx_query(IdxQuery<DI, FMT, HT> &q, const IndexerArgs &a, size_t qi,
+                                      bool valid, int g, int c) {
     constexpr int NB = DI / 32;
+    constexpr int E = idx_row_bytes(DI, FMT);
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const size_t head = qi * a.Hi + 16 * ht + c;
         if (valid) {
-            q.a[ht] = mx_operand(a.q8 + head * DI, g, DI == 128);
+            q.a[ht] = mx_operand<DI, FMT>(a.q8 + head * E, g);
             q.s[ht] = g < NB ? (int)a.q_sc[head * NB + g] : 127;
         } else {
             q.a[ht] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -69,11 +85,11 @@ struct IdxKeys {
     int s;
 };
 
-template <int DI>
+template <int DI, int FMT>
 __device__ inline IdxKeys load_idx_keys(const IndexerArgs &a, size_t row, int g) {
     constexpr int NB = DI / 32;
     IdxKeys k;
-    k.b = mx_operand(a.k8 + row * DI, g, DI == 128);
+    k.b = mx_operand<DI, FMT>(a.k8 + row * idx_row_bytes(DI, FMT), g);
     k.s = g < NB ? (int)a.k_sc[row * NB + g] : 127;
     return k;
 }
@@ -88,15 +104,17 @@ __device__ inline float relu_bits(float x) { return __int_as_float(max(__float_a
 // tile, and the sum over the four lane groups is a packed butterfly: across lanes 32
 // apart each lane keeps two tiles and sends two, across lanes 16 apart it keeps one and
 // sends one.  Lane (g, c) returns the score of key c of tile g.
-template <int DI, int HT>
-__device__ inline float idx_score4(const IdxQuery<DI, HT> &q, const IdxKeys (&k)[4], int g) {
+template <int DI, int FMT, int HT>
+__device__ inline float idx_score4(const IdxQuery<DI, FMT, HT> &q, const IdxKeys (&k)[4], int g) {
+    // operand type codes of the instruction: 0 = e4m3, 4 = e2m1
+    constexpr int kType = FMT == kFmtE2M1 ? 4 : 0;
     f32x4 acc[4][HT];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
             acc[u][ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                q.a[ht], k[u].b, f32x4{0.f, 0.f, 0.f, 0.f}, 0 /*A e4m3*/, 0 /*B e4m3*/, 0, q.s[ht], 0, k[u].s);
+                q.a[ht], k[u].b, f32x4{0.f, 0.f, 0.f, 0.f}, kType, kType, 0, q.s[ht], 0, k[u].s);
     float part[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {

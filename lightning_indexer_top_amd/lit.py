@@ -34,16 +34,19 @@ class lit_step_args(ctypes.Structure):
                 ("H", _I), ("D", _I), ("dv", _I), ("W", _I), ("R", _I),
                 ("q", _P), ("win_kv", _P), ("comp_kv", _P), ("sink", _P), ("scale", _F),
                 ("topk_idx", _P), ("out", _P), ("stage_events", _P * 4), ("state", _P), ("state_bytes", _Z),
-                ("flags", _I)]
+                ("flags", _I), ("index_format", _I)]
 
 
 LIT_STEP_UNFUSED = 1
+# lit_index_format: the code format of the index queries and keys
+INDEX_FORMATS = {"e4m3": 0, "e2m1": 1}
 
 
 SIGNATURES = {
     "lit_status_str": (ctypes.c_char_p, [_I]),
     "lit_abi_version": (_I, []),
     "lit_indexer_scores": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P]),
+    "lit_indexer_scores_fmt": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P]),
     "lit_topk": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "lit_topk_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "lit_window_indices": (_I, [_I, _I, _I, _I, _I, _P, _P]),
@@ -111,20 +114,27 @@ def lit_window_width(S: int, start_pos: int, W: int) -> int:
 
 
 def lit_indexer_scores(q8, q_sc, w, k8, k_sc, start_pos: int, ratio: int, scores=None,
-                       stream=None) -> torch.Tensor:
-    """Scores [B,S,ld] fp32 (ld = T rounded up to 4); columns >= T are untouched."""
+                       stream=None, fmt: str = "e4m3") -> torch.Tensor:
+    """Scores [B,S,ld] fp32 (ld = T rounded up to 4); columns >= T are untouched.
+
+    ``fmt`` is the code format of q8 / k8: "e4m3" (lit_indexer_scores) or "e2m1"
+    (lit_indexer_scores_fmt; rows of Di/2 bytes).  Di comes from the scale arrays."""
     for t, dt, n in ((q8, torch.uint8, "q8"), (q_sc, torch.uint8, "q_sc"), (w, torch.float32, "w"),
                      (k8, torch.uint8, "k8"), (k_sc, torch.uint8, "k_sc")):
         _need(t, dt, n)
-    B, S, Hi, Di = q8.shape
+    B, S, Hi, _ = q8.shape
+    Di = 32 * q_sc.shape[-1]
     T_cap = k8.shape[1]
     T = (start_pos + S) // ratio
     if scores is None:
         scores = torch.empty((B, S, max(4, (T + 3) // 4 * 4)), dtype=torch.float32, device=q8.device)
     _need(scores, torch.float32, "scores")
-    _check("lit_indexer_scores", library().lit_indexer_scores(
-        _ptr(q8), _ptr(q_sc), _ptr(w), _ptr(k8), _ptr(k_sc), B, S, Hi, Di, T_cap, start_pos, ratio,
-        _ptr(scores), scores.shape[-1], _stream(stream)))
+    args = (_ptr(q8), _ptr(q_sc), _ptr(w), _ptr(k8), _ptr(k_sc), B, S, Hi, Di, T_cap, start_pos,
+            ratio, _ptr(scores), scores.shape[-1], _stream(stream))
+    if fmt == "e4m3":
+        _check("lit_indexer_scores", library().lit_indexer_scores(*args))
+    else:
+        _check("lit_indexer_scores_fmt", library().lit_indexer_scores_fmt(INDEX_FORMATS[fmt], *args))
     return scores
 
 
@@ -189,9 +199,11 @@ def lit_sparse_attn(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float, d
 
 def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int, ratio: int,
                    index_topk: int, W: int, scale: float, dv=None, sink=None, topk_idx=None,
-                   out=None, stage_events=None, flags: int = 0) -> tuple:
-    """Build the lit_step_args struct (and allocate outputs the caller did not pass)."""
-    B, S, Hi, Di = q8.shape
+                   out=None, stage_events=None, flags: int = 0, fmt: str = "e4m3") -> tuple:
+    """Build the lit_step_args struct (and allocate outputs the caller did not pass).
+    ``fmt`` is the index-code format ("e4m3" or "e2m1"); Di comes from q_sc."""
+    B, S, Hi, _ = q8.shape
+    Di = 32 * q_sc.shape[-1]
     H, D = q.shape[2], q.shape[3]
     dv = D if dv is None else dv
     keff = topk_width(S, start_pos, ratio, index_topk)
@@ -205,7 +217,8 @@ def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int,
                       H=H, D=D, dv=dv, W=W, R=win_kv.shape[1], q=q.data_ptr(),
                       win_kv=win_kv.data_ptr(), comp_kv=comp_kv.data_ptr(),
                       sink=0 if sink is None else sink.data_ptr(), scale=scale,
-                      topk_idx=topk_idx.data_ptr(), out=out.data_ptr(), flags=flags)
+                      topk_idx=topk_idx.data_ptr(), out=out.data_ptr(), flags=flags,
+                      index_format=INDEX_FORMATS[fmt])
     if stage_events is not None:
         # hipEvent_t handles (e.g. torch.cuda.Event(...).cuda_event after one record)
         for k, ev in enumerate(stage_events):

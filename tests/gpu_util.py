@@ -26,18 +26,27 @@ def step_inputs_dev(inp):
                 sink=None if inp.sink is None else dev(inp.sink))
 
 
-def lib_dequant(codes, scales):
-    """e4m3 codes x ue8m0 scales decoded with torch's casts (for tolerance scales)."""
-    c = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64)
+def lib_dequant(codes, scales, fmt="e4m3"):
+    """Codes x ue8m0 scales (for tolerance scales): e4m3 decoded with torch's casts,
+    fp4 (e2m1, two codes a byte, element 2j low) with a table lookup."""
     s = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e8m0fnu).to(torch.float64)
+    if fmt == "e2m1":
+        from tests.test_oracle_formats import E2M1_TABLE
+        p = np.ascontiguousarray(codes)
+        lut = np.array(E2M1_TABLE + [-v for v in E2M1_TABLE])
+        vals = np.stack([lut[p & 15], lut[p >> 4]], axis=-1).reshape(*p.shape[:-1], 2 * p.shape[-1])
+        c = torch.from_numpy(vals)
+    else:
+        c = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64)
     return (c.unflatten(-1, (-1, 32)) * s.unsqueeze(-1)).flatten(-2).numpy()
 
 
 def score_tolerance(inp):
     """Per-entry bound for fp32/MFMA scores: 1e-4 of sum_h w_h sum_d |q_hd k_td| (the
     magnitude the contraction accumulates) plus 1e-6 relative; see the design doc."""
-    qd = np.abs(lib_dequant(inp.q8, inp.q_sc))          # [B,S,Hi,Di]
-    kd = np.abs(lib_dequant(inp.k8, inp.k_sc))          # [B,T_cap,Di]
+    fmt = getattr(inp, "index_fmt", "e4m3")
+    qd = np.abs(lib_dequant(inp.q8, inp.q_sc, fmt))     # [B,S,Hi,Di]
+    kd = np.abs(lib_dequant(inp.k8, inp.k_sc, fmt))     # [B,T_cap,Di]
     T = inp.T
     out = np.empty((inp.B, inp.S, T))
     for b in range(inp.B):

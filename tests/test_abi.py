@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.lit_abi_version() == 1
+    assert lib.lit_abi_version() == 2
     for code, name in B.STATUS_NAMES.items():
         assert lib.lit_status_str(code).decode().startswith(name)
     assert b"unknown" in lib.lit_status_str(99)
@@ -70,6 +70,21 @@ def test_indexer_refusals(lib):
     assert scores_call(lib, k8=MIS) == 3
     assert scores_call(lib, B=0) == 0                 # nothing to do
     assert scores_call(lib, start_pos=0, S=1, ratio=2) == 0   # T = 0
+
+
+def test_indexer_format_refusals(lib):
+    def fmt_call(fmt, **kw):
+        a = dict(q8=A, q_sc=A, w=A, k8=A, k_sc=A, B=1, S=1, Hi=16, Di=64, T_cap=512,
+                 start_pos=1023, ratio=2, scores=A, ld=512)
+        a.update(kw)
+        return lib.lit_indexer_scores_fmt(fmt, a["q8"], a["q_sc"], a["w"], a["k8"], a["k_sc"],
+                                          a["B"], a["S"], a["Hi"], a["Di"], a["T_cap"],
+                                          a["start_pos"], a["ratio"], a["scores"], a["ld"], None)
+    assert fmt_call(2) == 4 and fmt_call(-1) == 4       # unknown format
+    assert fmt_call(1, Di=96) == 4 and fmt_call(1, Di=48) == 2
+    assert fmt_call(1, k8=None) == 1 and fmt_call(1, q8=MIS) == 3
+    assert fmt_call(1, B=0) == 0
+    assert B.INDEX_FORMATS == {"e4m3": 0, "e2m1": 1}
 
 
 def test_topk_refusals(lib):
@@ -138,6 +153,12 @@ def test_step_refusals(lib):
     assert lib.lit_sparse_step(ctypes.byref(args), A, need, None) == 1
     assert lib.lit_sparse_step_workspace_bytes(None) == 0
     assert lib.lit_sparse_step_state_bytes(None) == 0
+    args.topk_idx = A
+    args.index_format = 3                                                   # unknown format
+    assert lib.lit_sparse_step(ctypes.byref(args), A, need, None) == 4
+    assert lib.lit_sparse_step_workspace_bytes(ctypes.byref(args)) == 0
+    args.index_format = 1
+    assert lib.lit_sparse_step_workspace_bytes(ctypes.byref(args)) >= need
 
 
 def test_step_state_sizes(lib):

@@ -2,9 +2,9 @@
 
 Acceptance rules (the tolerances of the sparse-attention step):
 * window lists and top-k of identical fp32 scores: bit-exact;
-* indexer scores: |gpu - oracle| <= 1e-4 * sum_h w_h sum_d |q_hd k_td| + 1e-6 |s| (the
-  MX-scaled MFMA's accumulation error, bounded by the magnitudes it sums), and -inf
-  exactly where the oracle has -inf;
+* indexer scores (e4m3 and fp4 e2m1 codes): |gpu - oracle| <= 1e-4 * sum_h w_h sum_d
+  |q_hd k_td| + 1e-6 |s| (the MX-scaled MFMA's accumulation error, bounded by the
+  magnitudes it sums), and -inf exactly where the oracle has -inf;
 * top-k from the full pipeline: sets identical, except rows within 1e-3 relative of the
   oracle's k-th score;
 * attention: max |gpu - oracle| <= 2e-2 (bf16 output) given the same selected set.
@@ -46,15 +46,20 @@ INDEXER_CASES = [
 ]
 
 
+FORMATS = ["e4m3", "e2m1"]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("B,S,start_pos,ratio,Hi,Di", INDEXER_CASES)
-def test_indexer_scores(orc, B, S, start_pos, ratio, Hi, Di):
+def test_indexer_scores(orc, B, S, start_pos, ratio, Hi, Di, fmt):
     inp = synth.make_step(B=B, S=S, start_pos=start_pos, ratio=ratio, Hi=Hi, Di=Di, H=16, D=64,
-                          W=8, index_topk=16, seed=1000 + B * 7 + S + Hi + Di)
+                          W=8, index_topk=16, seed=1000 + B * 7 + S + Hi + Di, index_fmt=fmt)
     d = step_inputs_dev(inp)
-    got = L.lit_indexer_scores(d["q8"], d["q_sc"], d["w"], d["k8"], d["k_sc"], start_pos, ratio)
+    got = L.lit_indexer_scores(d["q8"], d["q_sc"], d["w"], d["k8"], d["k_sc"], start_pos, ratio,
+                               fmt=fmt)
     torch.cuda.synchronize()
     got = got.cpu().numpy().astype(np.float64)[..., :inp.T]
-    want = orc.index_scores(inp.q8, inp.q_sc, inp.w, inp.k8, inp.k_sc, start_pos, ratio)
+    want = orc.index_scores(inp.q8, inp.q_sc, inp.w, inp.k8, inp.k_sc, start_pos, ratio, fmt)
     inf = np.isneginf(want)
     assert np.array_equal(np.isneginf(got), inf)
     tol = 1e-4 * score_tolerance(inp) + 1e-6 * np.abs(np.where(inf, 0, want))
@@ -62,13 +67,15 @@ def test_indexer_scores(orc, B, S, start_pos, ratio, Hi, Di):
     assert np.all(err <= tol), f"max err {err.max()} (tol at argmax {tol.flat[err.argmax()]})"
 
 
-def test_indexer_keys_scaled_by_four(orc):
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_indexer_keys_scaled_by_four(orc, fmt):
     """The decode-4k shape whose boosted key rows (x4: +2 on every scale byte) stand out."""
-    inp = synth.workload("decode-4k-r2")
+    inp = synth.workload("decode-4k-r2", index_fmt=fmt)
     d = step_inputs_dev(inp)
     got = L.lit_indexer_scores(d["q8"], d["q_sc"], d["w"], d["k8"], d["k_sc"], inp.start_pos,
-                               inp.ratio).cpu().numpy().astype(np.float64)[..., :inp.T]
-    want = orc.index_scores(inp.q8, inp.q_sc, inp.w, inp.k8, inp.k_sc, inp.start_pos, inp.ratio)
+                               inp.ratio, fmt=fmt).cpu().numpy().astype(np.float64)[..., :inp.T]
+    want = orc.index_scores(inp.q8, inp.q_sc, inp.w, inp.k8, inp.k_sc, inp.start_pos, inp.ratio,
+                            fmt)
     tol = 1e-4 * score_tolerance(inp) + 1e-6 * np.abs(want)
     assert np.all(np.abs(got - want) <= tol)
 
@@ -197,7 +204,8 @@ def _run_step(d, inp, flags=0, state=None):
                                       k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
                                       comp_kv=d["comp_kv"], start_pos=inp.start_pos,
                                       ratio=inp.ratio, index_topk=inp.index_topk, W=inp.W,
-                                      scale=inp.scale, dv=inp.dv, sink=d["sink"], flags=flags)
+                                      scale=inp.scale, dv=inp.dv, sink=d["sink"], flags=flags,
+                                      fmt=inp.index_fmt)
     state = L.attach_state(args, state)
     ws = L.step_workspace(args)
     L.lit_sparse_step(args, ws)
@@ -263,8 +271,18 @@ def test_step_small(orc, cfg, flags):
 
 
 @pytest.mark.parametrize("flags", MODES)
+@pytest.mark.parametrize("cfg", STEP_SMALL[:3] + STEP_SMALL[4:],
+                         ids=lambda c: f"B{c['B']}S{c['S']}p{c['start_pos']}r{c['ratio']}")
+def test_step_small_fp4(orc, cfg, flags):
+    """The small steps with fp4 (e2m1) index queries and keys."""
+    inp = synth.make_step(seed=5252 + cfg["start_pos"], index_fmt="e2m1", **cfg)
+    idx, out = _run_step(step_inputs_dev(inp), inp, flags)
+    _check_step(orc, inp, idx, out)
+
+
+@pytest.mark.parametrize("flags", MODES)
 @pytest.mark.parametrize("name", ["decode-1k", "decode-4k-r2", "decode-4k-r1", "decode-16k",
-                                  "decode-128k"])
+                                  "decode-128k", "decode-16k-fp4", "decode-128k-fp4"])
 def test_step_workloads(orc, name, flags):
     inp = synth.workload(name)
     idx, out = _run_step(step_inputs_dev(inp), inp, flags)
