@@ -75,6 +75,10 @@ def _bind(path: str):
     lib.orc_topk_width.restype = I
     lib.orc_topk.argtypes = [P, I, I, I, I, I, I, P]
     lib.orc_topk.restype = I
+    lib.orc_candidate_blocks_width.argtypes = [I, I, I, I, I]
+    lib.orc_candidate_blocks_width.restype = I
+    lib.orc_candidate_blocks.argtypes = [P, I, I, I, I, I, I, I, P]
+    lib.orc_candidate_blocks.restype = I
     lib.orc_window_width.argtypes = [I, I, I]
     lib.orc_window_width.restype = I
     lib.orc_window_indices.argtypes = [I, I, I, I, I, P]
@@ -206,6 +210,40 @@ def topk(scores, start_pos: int, ratio: int, index_topk: int) -> np.ndarray:
     rc = _load().orc_topk(_ptr(scores), ld, B, S, start_pos, ratio, index_topk, _ptr(out))
     _check(rc, "orc_topk")
     return out
+
+
+def candidate_blocks_width(S: int, start_pos: int, ratio: int, topk_blocks: int,
+                           block_size: int) -> int:
+    return _load().orc_candidate_blocks_width(S, start_pos, ratio, topk_blocks, block_size)
+
+
+def candidate_blocks(scores, start_pos: int, ratio: int, topk_blocks: int,
+                     block_size: int) -> np.ndarray:
+    """Level one of the two-level top-k: kept block numbers [B,S,kb] int32, ascending,
+    -1 padded (kb = min(topk_blocks, ceil(T / block_size)))."""
+    scores = _c(scores, np.float64)
+    B, S, ld = scores.shape
+    kb = candidate_blocks_width(S, start_pos, ratio, topk_blocks, block_size)
+    out = np.empty((B, S, kb), dtype=np.int32)
+    rc = _load().orc_candidate_blocks(_ptr(scores), ld, B, S, start_pos, ratio, topk_blocks,
+                                      block_size, _ptr(out))
+    _check(rc, "orc_candidate_blocks")
+    return out
+
+
+def apply_candidates(scores, blocks, block_size: int) -> np.ndarray:
+    """Level two's mask (DeepSeek-V4.1-Flash-NVFP4 model.py, Indexer.forward): every
+    score outside the listed blocks becomes -inf.  scores [B,S,T], blocks [B,S,kb]."""
+    scores = np.array(scores, dtype=np.float64)
+    B, S, T = scores.shape
+    keep = np.zeros((B, S, T), dtype=bool)
+    for b in range(B):
+        for i in range(S):
+            for j in blocks[b, i]:
+                if j >= 0:
+                    keep[b, i, j * block_size:(j + 1) * block_size] = True
+    scores[~keep] = -np.inf
+    return scores
 
 
 def window_indices(B: int, S: int, start_pos: int, W: int, R: int) -> np.ndarray:

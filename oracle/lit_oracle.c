@@ -251,6 +251,75 @@ int orc_topk(const double *scores, int ld, int B, int S, int start_pos,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Candidate blocks: level one of the two-level top-k.  [V4.1]               */
+/* select_candidate_blocks, with Indexer.forward's compress_lens:            */
+/*   1. the score row (width T, -inf where the query cannot see) is padded   */
+/*      with -inf to a multiple of block_size;                               */
+/*   2. each block scores the max of its positions;                          */
+/*   3. the block holding the query's newest visible row, (n_vis-1) //       */
+/*      block_size, is set to +inf (none when n_vis == 0: Python's floor     */
+/*      division gives block -1);                                            */
+/*   4. the min(topk_blocks, n_blocks) best blocks are taken -- ties by the  */
+/*      lower block, a reading: the pages' topk leaves ties open -- and any  */
+/*      taken block whose score is -inf is dropped.                          */
+/* The pages return this as a mask over positions; here it is the list of    */
+/* kept block numbers in ascending order, -1 padded to                       */
+/* kb = min(topk_blocks, n_blocks) per query, n_blocks = ceil(T/block_size). */
+/* Level two ([V4.1] Indexer.forward, uses_candidates) sets every score      */
+/* outside the kept blocks to -inf and runs the ordinary top-k.              */
+/* scores: [B,S,ld] doubles; blocks: [B,S,kb] int32.                         */
+/* ------------------------------------------------------------------------ */
+int orc_candidate_blocks_width(int S, int start_pos, int ratio, int topk_blocks,
+                               int block_size) {
+    if (ratio <= 0 || block_size <= 0 || topk_blocks < 0) return 0;
+    const int T = (start_pos + S) / ratio;
+    const int nblocks = (T + block_size - 1) / block_size;
+    return topk_blocks < nblocks ? topk_blocks : nblocks;
+}
+
+int orc_candidate_blocks(const double *scores, int ld, int B, int S, int start_pos,
+                         int ratio, int topk_blocks, int block_size, int32_t *blocks) {
+    if (B < 0 || S < 0 || ratio <= 0 || topk_blocks < 0 || block_size <= 0 ||
+        start_pos < 0)
+        return ORC_E_ARG;
+    const int T = (start_pos + S) / ratio;
+    if (ld < T) return ORC_E_ARG;
+    const int nblocks = (T + block_size - 1) / block_size;
+    const int kb = orc_candidate_blocks_width(S, start_pos, ratio, topk_blocks, block_size);
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic) reduction(| : bad)
+    for (int b = 0; b < B; ++b) {
+        for (int i = 0; i < S; ++i) {
+            const double *srow = scores + ((size_t)b * S + i) * ld;
+            int32_t *orow = blocks + ((size_t)b * S + i) * kb;
+            const int nvis = orc_n_visible(start_pos, i, ratio);
+            orc_pick *p = (orc_pick *)malloc(sizeof(orc_pick) * (size_t)(nblocks > 0 ? nblocks : 1));
+            int *sel = (int *)malloc(sizeof(int) * (size_t)(kb > 0 ? kb : 1));
+            for (int j = 0; j < nblocks; ++j) {
+                double m = -INFINITY; /* the -inf padding of the last block */
+                for (int t = j * block_size; t < (j + 1) * block_size && t < T; ++t) {
+                    if (isnan(srow[t])) bad = 1;
+                    if (srow[t] > m) m = srow[t];
+                }
+                p[j].s = m;
+                p[j].t = j;
+            }
+            if (nvis >= 1 && (nvis - 1) / block_size < nblocks)
+                p[(nvis - 1) / block_size].s = INFINITY;
+            qsort(p, (size_t)nblocks, sizeof(orc_pick), orc_pick_cmp);
+            int take = 0;
+            for (int j = 0; j < kb; ++j)
+                if (p[j].s > -INFINITY) sel[take++] = p[j].t;
+            qsort(sel, (size_t)take, sizeof sel[0], orc_int_cmp); /* ascending blocks */
+            for (int j = 0; j < kb; ++j) orow[j] = j < take ? sel[j] : -1;
+            free(p);
+            free(sel);
+        }
+    }
+    return bad ? ORC_E_ARG : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Window rows.  [V4.1] get_window_topk_idxs and Attention._window_kv: a     */
 /* query at absolute position P attends to the window positions              */
 /* max(0, P-W+1) .. P.  The window source is a ring of R slots holding       */

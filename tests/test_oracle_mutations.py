@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_attention as TA
+from tests import test_oracle_candidates as TC
 from tests import test_oracle_formats as TF
 from tests import test_oracle_indexer as TI
 from tests import test_oracle_topk as TT
@@ -66,6 +67,15 @@ MUTANTS = [
      "const size_t E = (size_t)Di;", [_one_hot_fp4, TI.test_fp4_closed_form_constant_blocks]),
     ("fp4 nibble from the wrong byte", "uint8_t byte = row[d / 2];", "uint8_t byte = row[d / 4];",
      [_one_hot_fp4, TI.test_fp4_equals_e4m3_on_shared_values]),
+    ("candidate pin off by one", "p[(nvis - 1) / block_size].s = INFINITY;", "p[nvis / block_size].s = INFINITY;",
+     [TC.test_hand_ranked_blocks, TC.test_prefill_visibility_and_empty_query]),
+    ("candidate -inf blocks not dropped", "if (p[j].s > -INFINITY) sel[take++] = p[j].t;", "sel[take++] = p[j].t;",
+     [TC.test_prefill_visibility_and_empty_query]),
+    ("candidate block min instead of max", "if (srow[t] > m) m = srow[t];", "if (srow[t] < m || m == -INFINITY) m = srow[t];",
+     [TC.test_hand_ranked_blocks, TC.test_monotone_map_and_block_permutation]),
+    ("candidate block overlaps the next", "for (int t = j * block_size; t < (j + 1) * block_size && t < T; ++t) {",
+     "for (int t = j * block_size; t <= (j + 1) * block_size && t < T; ++t) {",
+     [TC.test_hand_ranked_blocks, TC.test_monotone_map_and_block_permutation]),
     ("topk tie rule reversed", "return (x->t > y->t) - (x->t < y->t);",
      "return (x->t < y->t) - (x->t > y->t);", [TT.test_property_checker_with_ties_and_prefill]),
     ("topk ascending sort dropped", "qsort(sel, (size_t)take, sizeof(int), orc_int_cmp);", "",
