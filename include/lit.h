@@ -7,7 +7,8 @@
  *      compressed-KV row for every query (head-weighted ReLU of q.k over e4m3
  *      codes with one ue8m0 scale per 32 values; lit_indexer_scores_fmt also
  *      takes fp4 e2m1 codes with the same scales);
- *   2. lit_topk           : a per-query selector keeps the index_topk best rows;
+ *   2. lit_topk           : a per-query selector keeps the index_topk best rows
+ *      (lit_candidate_blocks / lit_topk_candidates: the two-level form);
  *   3. lit_sparse_attn    : attention with an online softmax over the sliding
  *      window and the selected compressed rows, one shared KV head (K = V).
  *   lit_window_indices builds the window row lists; lit_sparse_step runs 1-3
@@ -17,7 +18,8 @@
  *   [V4.1] DeepSeek-V4.1-Flash-NVFP4, inference/model.py -- module globals
  *          (fp8 and fp4 block size 32, ue8m0 scales), get_window_topk_idxs,
  *          Indexer.__init__/forward, Attention._window_kv/_compress_kv/forward
- *          (the sparse_attn call and its int32 [b, m, topk] index lists).
+ *          (the sparse_attn call and its int32 [b, m, topk] index lists),
+ *          select_candidate_blocks.
  *   [V3.2] DeepSeek-V3.2-Exp, inference/model.py -- Indexer.forward
  *          (fp8_index over e4m3 key cache + block scales), MLA.forward.
  *
@@ -134,6 +136,54 @@ lit_status lit_topk(const float *scores, int ld_scores, int B, int S, int start_
 size_t lit_topk_workspace_bytes(int B, int S, int start_pos, int ratio, int index_topk);
 
 /*
+ * Two-level top-k ([V4.1] select_candidate_blocks and Indexer.forward with
+ * candidate layers): one layer (the candidate source) keeps, per query, the
+ * topk_blocks best blocks of block_size consecutive rows; the layers that use
+ * them score as usual but treat every row outside those blocks as -inf before
+ * their own top-k.
+ *
+ * lit_candidate_blocks -- level one.  A block scores the max of its visible
+ * scores; the block holding the query's newest visible row, (n_vis-1)/block_size,
+ * is always kept; of the others the best are kept (equal block scores: lower
+ * block first) up to kb = min(topk_blocks, ceil(T / block_size)) blocks.  Blocks
+ * a query cannot see are never kept.  Output per query: the kept block numbers
+ * in ascending order, -1 in the slots a query with fewer visible blocks cannot
+ * fill.
+ *
+ *   scores (device) f32 [B, S, ld_scores]  as lit_indexer_scores writes them
+ *                                          (only visible columns are read)
+ *   blocks (device) i32 [B, S, kb]         output
+ *   ws, ws_bytes    workspace of lit_candidate_blocks_workspace_bytes() bytes
+ *                   (the block scores), 16-byte aligned
+ * Requirements: block_size >= 1, topk_blocks >= 0, ld_scores >= T and a multiple
+ * of 4.
+ */
+lit_status lit_candidate_blocks(const float *scores, int ld_scores, int B, int S, int start_pos,
+                                int ratio, int topk_blocks, int block_size, int32_t *blocks,
+                                void *ws, size_t ws_bytes, void *stream);
+size_t lit_candidate_blocks_workspace_bytes(int B, int S, int start_pos, int ratio,
+                                            int block_size);
+int lit_candidate_blocks_width(int S, int start_pos, int ratio, int topk_blocks,
+                               int block_size);
+
+/*
+ * lit_topk_candidates -- level two: lit_topk over the scores with every row
+ * outside the blocks listed for its query counted as -inf.  The result follows
+ * lit_topk's contract (k_eff entries, ascending, -1 padded); when a query has
+ * fewer than k_eff rows inside its blocks, the remaining picks are its lowest
+ * visible rows outside them (they score -inf, and equal scores go to the lower
+ * row), as a top-k over the masked scores gives.
+ *
+ *   blocks (device) i32 [B, S, kb]  block numbers of block_size rows, or -1;
+ *                                   entries out of range are ignored
+ * Requirements: as lit_topk; block_size >= 1; ceil(T / block_size) <= 65536.
+ */
+lit_status lit_topk_candidates(const float *scores, int ld_scores, int B, int S, int start_pos,
+                               int ratio, int index_topk, const int32_t *blocks, int kb,
+                               int block_size, int32_t *idx, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/*
  * lit_window_indices -- [V4.1] get_window_topk_idxs, generalised to a chunk
  * that starts after position 0.
  *
@@ -191,6 +241,11 @@ size_t lit_sparse_attn_workspace_bytes(int B, int S, int H, int dv, int W, int K
  * _compress_topk_idxs; the -1 / position-order contract of the top-k list is
  * that of lit_topk.  Scores and attention partials live in the workspace.
  *
+ * With cand_in / cand_out set the layer also takes part in the two-level top-k:
+ * as the candidate source it writes lit_candidate_blocks of its own scores (its
+ * own top-k stays the plain one), as a level-two layer its top-k is
+ * lit_topk_candidates over cand_in.
+ *
  * Decode-sized batches (B*S queries that fit the device's co-resident
  * workgroups) run as ONE kernel: a team of workgroups per query scores, selects,
  * gathers and merges, synchronising through counters in the workspace.  Larger
@@ -242,6 +297,15 @@ typedef struct lit_step_args {
     size_t state_bytes;
     int flags; /* LIT_STEP_* bits */
     int index_format; /* lit_index_format of q8 / k8 (0 = LIT_INDEX_E4M3) */
+    /* two-level top-k (lit_candidate_blocks / lit_topk_candidates); unused when
+     * cand_in and cand_out are both NULL.  Either one selects the multi-kernel form. */
+    const int32_t *cand_in; /* [B,S,cand_k]: level two -- this layer's rows outside
+                               these blocks count as -inf before its top-k */
+    int cand_k;
+    int32_t *cand_out;      /* [B,S,kb]: candidate source -- this layer writes its
+                               kept blocks (kb = lit_candidate_blocks_width) */
+    int cand_topk_blocks;
+    int cand_block_size;    /* rows per block, for cand_in and cand_out */
 } lit_step_args;
 
 lit_status lit_sparse_step(const lit_step_args *args, void *ws, size_t ws_bytes, void *stream);

@@ -145,6 +145,67 @@ lit_status lit_topk(const float *scores, int ld_scores, int B, int S, int start_
     return hip_status(launch_topk(a, (hipStream_t)stream));
 }
 
+int lit_candidate_blocks_width(int S, int start_pos, int ratio, int topk_blocks, int block_size) {
+    if (S < 0 || start_pos < 0 || ratio < 1 || topk_blocks < 0 || block_size < 1) return 0;
+    if ((long)start_pos + S > INT_MAX) return 0;
+    const long T = ((long)start_pos + S) / ratio;
+    const long nb = (T + block_size - 1) / block_size;
+    return (int)(topk_blocks < nb ? topk_blocks : nb);
+}
+
+static long block_ld(int S, int start_pos, int ratio, int block_size) {
+    const long T = ((long)start_pos + S) / ratio;
+    return (long)round_up((size_t)((T + block_size - 1) / block_size), 4);
+}
+
+size_t lit_candidate_blocks_workspace_bytes(int B, int S, int start_pos, int ratio, int block_size) {
+    if (B <= 0 || S <= 0 || start_pos < 0 || ratio < 1 || block_size < 1) return 0;
+    if ((long)start_pos + S > INT_MAX) return 0;
+    return round_up((size_t)B * S * block_ld(S, start_pos, ratio, block_size) * sizeof(float), 256);
+}
+
+lit_status lit_candidate_blocks(const float *scores, int ld_scores, int B, int S, int start_pos, int ratio,
+                                int topk_blocks, int block_size, int32_t *blocks, void *ws, size_t ws_bytes,
+                                void *stream) {
+    if (block_size < 1 || topk_blocks < 0) return LIT_E_SHAPE;
+    lit_status st = check_topk(scores, ld_scores, B, S, start_pos, ratio, 1, blocks);
+    if (st != LIT_OK) return st;
+    const int kb = lit_candidate_blocks_width(S, start_pos, ratio, topk_blocks, block_size);
+    if (B == 0 || S == 0 || kb == 0) return LIT_OK;
+    const size_t need = lit_candidate_blocks_workspace_bytes(B, S, start_pos, ratio, block_size);
+    if (!ws || ws_bytes < need) return LIT_E_WORKSPACE;
+    if (!aligned16(ws)) return LIT_E_ALIGN;
+    hipStream_t hs = (hipStream_t)stream;
+    const int T = (start_pos + S) / ratio;
+    const long ldb = block_ld(S, start_pos, ratio, block_size);
+    float *bs = (float *)ws;
+    hipError_t e = launch_block_max(scores, ld_scores, B, S, start_pos, ratio, T, block_size, bs, ldb, hs);
+    if (e != hipSuccess) return hip_status(e);
+    TopkArgs a{bs, ldb, B, S, start_pos, ratio, T, kb, blocks};
+    a.vis_block = block_size;
+    return hip_status(launch_topk(a, hs));
+}
+
+lit_status lit_topk_candidates(const float *scores, int ld_scores, int B, int S, int start_pos, int ratio,
+                               int index_topk, const int32_t *blocks, int kb, int block_size, int32_t *idx,
+                               void *ws, size_t ws_bytes, void *stream) {
+    (void)ws; (void)ws_bytes;
+    if (block_size < 1 || kb < 0) return LIT_E_SHAPE;
+    lit_status st = check_topk(scores, ld_scores, B, S, start_pos, ratio, index_topk, idx);
+    if (st != LIT_OK) return st;
+    const int keff = topk_width(S, start_pos, ratio, index_topk);
+    if (B == 0 || S == 0 || keff == 0) return LIT_OK;
+    const long T = ((long)start_pos + S) / ratio;
+    if ((T + block_size - 1) / block_size > kCandMaxBlocks) return LIT_E_UNSUPPORTED;
+    if (kb > 0 && !blocks) return LIT_E_NULL;
+    TopkArgs a{scores, (long)ld_scores, B, S, start_pos, ratio, (int)T, keff, idx};
+    a.masked = true;  // kb == 0: every row is outside the (empty) candidate set
+    a.cand = kb > 0 ? blocks : nullptr;
+    a.cand_k = kb;
+    a.cand_bs = block_size;
+    return hip_status(launch_topk(a, (hipStream_t)stream));
+}
+
 int lit_window_width(int S, int start_pos, int W) {
     if (S < 0 || start_pos < 0) return 0;
     return window_width(S, start_pos, W);
@@ -188,7 +249,10 @@ lit_status lit_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv
     return hip_status(launch_sparse_attn(a, p, (hipStream_t)stream));
 }
 
-// Workspace of the multi-kernel step: scores [B*S, ld] fp32, then the attention partials.
+static bool step_uses_candidates(const lit_step_args *s) { return s->cand_in || s->cand_out; }
+
+// Workspace of the multi-kernel step: scores [B*S, ld] fp32, then the attention partials
+// (level one's block scores share the partials' space: they are used up before).
 static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld, AttnPlan *plan) {
     const long T = ((long)s->start_pos + s->S) / s->ratio;
     *ld = (long)round_up((size_t)(T > 0 ? T : 1), 4);
@@ -196,13 +260,19 @@ static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld
     const int nwin = window_width(s->S, s->start_pos, s->W);
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
     *plan = plan_attention(s->B, s->S, nwin + keff);
-    return *scores_bytes + round_up(attention_partial_bytes(s->B, s->S, s->H, s->dv, *plan), 256);
+    size_t rest = round_up(attention_partial_bytes(s->B, s->S, s->H, s->dv, *plan), 256);
+    if (s->cand_out) {
+        const size_t bb = lit_candidate_blocks_workspace_bytes(s->B, s->S, s->start_pos, s->ratio,
+                                                               s->cand_block_size);
+        if (bb > rest) rest = bb;
+    }
+    return *scores_bytes + rest;
 }
 
 static FusedPlan step_fused_plan(const lit_step_args *s) {
     FusedPlan p{};
     p.ok = false;
-    if (s->flags & LIT_STEP_UNFUSED) return p;
+    if ((s->flags & LIT_STEP_UNFUSED) || step_uses_candidates(s)) return p;
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
     return plan_fused(s->index_format, s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D, s->dv,
                       s->W, keff);
@@ -226,6 +296,11 @@ static lit_status check_step(const lit_step_args *s) {
                     (const int32_t *)16, keff, s->out);
     if (st != LIT_OK) return st;
     if (s->B > 0 && s->S > 0 && keff > 0 && !s->topk_idx) return LIT_E_NULL;
+    if (step_uses_candidates(s)) {
+        if (s->cand_block_size < 1 || s->cand_k < 0 || s->cand_topk_blocks < 0) return LIT_E_SHAPE;
+        if (s->cand_in && (T + s->cand_block_size - 1) / s->cand_block_size > kCandMaxBlocks)
+            return LIT_E_UNSUPPORTED;
+    }
     return LIT_OK;
 }
 
@@ -292,15 +367,35 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
         if ((e = launch_indexer_scores(ia, hs)) != hipSuccess) return hip_status(e);
     }
     if ((e = mark(1)) != hipSuccess) return hip_status(e);
+    char *rest = (char *)ws + scores_bytes;
+    if (s->cand_out) {  // candidate source: level one over this layer's scores
+        const int kb = lit_candidate_blocks_width(s->S, s->start_pos, s->ratio, s->cand_topk_blocks,
+                                                  s->cand_block_size);
+        if (kb > 0 && T > 0) {
+            const long ldb = block_ld(s->S, s->start_pos, s->ratio, s->cand_block_size);
+            if ((e = launch_block_max(scores, ld, s->B, s->S, s->start_pos, s->ratio, T, s->cand_block_size,
+                                      (float *)rest, ldb, hs)) != hipSuccess)
+                return hip_status(e);
+            TopkArgs la{(const float *)rest, ldb, s->B, s->S, s->start_pos, s->ratio, T, kb, s->cand_out};
+            la.vis_block = s->cand_block_size;
+            if ((e = launch_topk(la, hs)) != hipSuccess) return hip_status(e);
+        }
+    }
     if (keff > 0) {
         TopkArgs ta{scores, ld, s->B, s->S, s->start_pos, s->ratio, T, keff, s->topk_idx};
+        if (s->cand_in) {  // level two
+            ta.masked = true;
+            ta.cand = s->cand_k > 0 ? s->cand_in : nullptr;
+            ta.cand_k = s->cand_k;
+            ta.cand_bs = s->cand_block_size;
+        }
         if ((e = launch_topk(ta, hs)) != hipSuccess) return hip_status(e);
     }
     if ((e = mark(2)) != hipSuccess) return hip_status(e);
     AttnArgs aa{s->q, s->B, s->S, s->H, s->D, s->dv, s->W > 0 ? s->win_kv : nullptr, s->R,
                 nullptr, s->W, s->start_pos, keff > 0 ? s->comp_kv : nullptr, s->T_cap,
                 keff > 0 ? s->topk_idx : nullptr, keff, s->sink, s->scale, s->out,
-                (float *)((char *)ws + scores_bytes)};
+                (float *)rest};
     if ((e = launch_sparse_attn(aa, plan, hs)) != hipSuccess) return hip_status(e);
     return hip_status(mark(3));
 }

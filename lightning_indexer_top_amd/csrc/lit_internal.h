@@ -50,8 +50,22 @@ struct TopkArgs {
     int T;                // columns that exist per row
     int keff;             // entries written per row
     int32_t *idx;         // [B,S,keff]
+    // Two-level top-k.  vis_block > 1: the columns are blocks of vis_block rows, and a
+    // query sees ceil(visible rows / vis_block) of them (level one).  masked: a column
+    // outside the blocks listed for its query (cand [B,S,cand_k], blocks of cand_bs
+    // rows, -1 = none; cand may be NULL when cand_k == 0) counts as -inf (level two).
+    int vis_block = 1;
+    bool masked = false;
+    const int32_t *cand = nullptr;
+    int cand_k = 0, cand_bs = 1;
 };
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
+// Level one's block scores: bscores[row, j] = max of the visible scores of block j (rows
+// j*bs .. j*bs+bs-1), +inf for the block holding the query's newest visible row.
+hipError_t launch_block_max(const float *scores, long ld, int B, int S, int start_pos, int ratio, int T, int bs,
+                            float *bscores, long ldb, hipStream_t stream);
+// Most blocks level two can hold as a bitmap in LDS.
+constexpr int kCandMaxBlocks = 65536;
 
 // ---------------------------------------------------------------------------
 // Sparse attention (attention.hip) and window lists

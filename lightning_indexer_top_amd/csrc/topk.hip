@@ -29,25 +29,51 @@ namespace {
 
 constexpr int kThreads = 1024;
 
-template <int ITEMS>
+// Columns a query sees: its visible rows, or (level one) the blocks holding them.
+__device__ inline int visible_columns(const TopkArgs &a, int i) {
+    const int rows = min(a.T, (a.start_pos + i + 1) / a.ratio);
+    return a.vis_block > 1 ? (rows + a.vis_block - 1) / a.vis_block : rows;
+}
+
+template <int ITEMS, bool CAND>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     __shared__ int hist[2048];
     __shared__ uint32_t wsum[kThreads / 64];
     __shared__ int sel_bin;
     __shared__ int sel_above;
+    __shared__ uint32_t keep[CAND ? kCandMaxBlocks / 32 : 1];  // level two: kept-block bitmap
 
     const int row = blockIdx.x;
     const int i = row % a.S;
     const int tid = threadIdx.x;
-    int n = (a.start_pos + i + 1) / a.ratio;
-    if (n > a.T) n = a.T;
+    const int n = visible_columns(a, i);
     int32_t *out = a.idx + (size_t)row * a.keff;
     const float *src = a.scores + (size_t)row * a.ld;
 
-    if (n <= a.keff) {  // every visible row is picked
+    if (n <= a.keff) {  // every visible column is picked
         for (int j = tid; j < a.keff; j += kThreads) out[j] = j < n ? j : -1;
         return;
     }
+
+    if constexpr (CAND) {
+        const int nb = (n + a.cand_bs - 1) / a.cand_bs;  // blocks this query can see
+        for (int j = tid; j < (nb + 31) / 32; j += kThreads) keep[j] = 0u;
+        __syncthreads();
+        const int32_t *cl = a.cand + (size_t)row * a.cand_k;
+        for (int j = tid; j < a.cand_k; j += kThreads) {
+            const int blk = cl[j];
+            if (blk >= 0 && blk < nb) atomicOr(&keep[blk >> 5], 1u << (blk & 31));
+        }
+        __syncthreads();
+    }
+    // masked columns (level two) take the key of -inf
+    auto key_at = [&](int t, float v) -> uint32_t {
+        if constexpr (CAND) {
+            const int blk = t / a.cand_bs;
+            if (!((keep[blk >> 5] >> (blk & 31)) & 1u)) return order_key(-INFINITY);
+        }
+        return order_key(v);
+    };
 
     constexpr int SEG = kThreads * ITEMS;
     const int nseg = (n + SEG - 1) / SEG;
@@ -59,14 +85,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
             for (int u = 0; u < ITEMS; u += 4) {
                 const f32x4 v = *reinterpret_cast<const f32x4 *>(src + base + u);
-                keys[u] = order_key(v[0]);
-                keys[u + 1] = order_key(v[1]);
-                keys[u + 2] = order_key(v[2]);
-                keys[u + 3] = order_key(v[3]);
+                keys[u] = key_at(base + u, v[0]);
+                keys[u + 1] = key_at(base + u + 1, v[1]);
+                keys[u + 2] = key_at(base + u + 2, v[2]);
+                keys[u + 3] = key_at(base + u + 3, v[3]);
             }
         } else {
 #pragma unroll
-            for (int u = 0; u < ITEMS; ++u) keys[u] = u < cnt ? order_key(src[base + u]) : 0u;
+            for (int u = 0; u < ITEMS; ++u) keys[u] = u < cnt ? key_at(base + u, src[base + u]) : 0u;
         }
         return cnt;
     };
@@ -164,7 +190,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(TopkArgs a) {
     const int row = blockIdx.x;
     const int i = row % a.S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n = min(a.T, (a.start_pos + i + 1) / a.ratio);
+    const int n = visible_columns(a, i);
     int32_t *out = a.idx + (size_t)row * a.keff;
     const float *src = a.scores + (size_t)row * a.ld;
 
@@ -283,23 +309,62 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(TopkArgs a) {
             }
 }
 
+__global__ __launch_bounds__(256) void block_max_kernel(const float *scores, long ld, int S, int start_pos,
+                                                        int ratio, int T, int bs, float *bscores, long ldb) {
+    const int row = blockIdx.y;
+    const int i = row % S;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    const int nvis = min(T, (start_pos + i + 1) / ratio);
+    const int nb = (nvis + bs - 1) / bs;
+    if (j >= nb) return;
+    const float *src = scores + (size_t)row * ld;
+    float m = -INFINITY;
+    const int t1 = min(j * bs + bs, nvis);
+    for (int t = j * bs; t < t1; ++t) m = fmaxf(m, src[t]);
+    // the block of the newest visible row is kept whatever its score
+    bscores[(size_t)row * ldb + j] = j == (nvis - 1) / bs ? INFINITY : m;
+}
+
 }  // namespace
+
+hipError_t launch_block_max(const float *scores, long ld, int B, int S, int start_pos, int ratio, int T, int bs,
+                            float *bscores, long ldb, hipStream_t stream) {
+    const int nblocks = (T + bs - 1) / bs;
+    if (B <= 0 || S <= 0 || nblocks <= 0) return hipSuccess;
+    dim3 grid((nblocks + 255) / 256, B * S);
+    hipLaunchKernelGGL(block_max_kernel, grid, dim3(256), 0, stream, scores, ld, S, start_pos, ratio, T, bs,
+                       bscores, ldb);
+    return hipGetLastError();
+}
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
     if (a.B <= 0 || a.S <= 0 || a.keff <= 0) return hipSuccess;
     dim3 grid(a.B * a.S), block(kThreads);
-    if (a.T <= kSelThreads * 4 * kRowQ && a.B * a.S >= 256) {  // many rows (few: the radix kernel)
+    const int cols = a.vis_block > 1 ? (a.T + a.vis_block - 1) / a.vis_block : a.T;
+    if (a.masked) {
+        if ((cols + a.cand_bs - 1) / a.cand_bs > kCandMaxBlocks) return hipErrorInvalidValue;
+        if (cols <= kThreads * 4)
+            hipLaunchKernelGGL((topk_kernel<4, true>), grid, block, 0, stream, a);
+        else if (cols <= kThreads * 8)
+            hipLaunchKernelGGL((topk_kernel<8, true>), grid, block, 0, stream, a);
+        else if (cols <= kThreads * 16)
+            hipLaunchKernelGGL((topk_kernel<16, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((topk_kernel<32, true>), grid, block, 0, stream, a);
+        return hipGetLastError();
+    }
+    if (cols <= kSelThreads * 4 * kRowQ && a.B * a.S >= 256) {  // many rows (few: the radix kernel)
         hipLaunchKernelGGL(topk_rows_kernel, grid, dim3(kSelThreads), 0, stream, a);
         return hipGetLastError();
     }
-    if (a.T <= kThreads * 4)
-        hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, stream, a);
-    else if (a.T <= kThreads * 8)
-        hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, stream, a);
-    else if (a.T <= kThreads * 16)
-        hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, stream, a);
+    if (cols <= kThreads * 4)
+        hipLaunchKernelGGL((topk_kernel<4, false>), grid, block, 0, stream, a);
+    else if (cols <= kThreads * 8)
+        hipLaunchKernelGGL((topk_kernel<8, false>), grid, block, 0, stream, a);
+    else if (cols <= kThreads * 16)
+        hipLaunchKernelGGL((topk_kernel<16, false>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((topk_kernel<32, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

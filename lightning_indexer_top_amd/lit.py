@@ -34,7 +34,9 @@ class lit_step_args(ctypes.Structure):
                 ("H", _I), ("D", _I), ("dv", _I), ("W", _I), ("R", _I),
                 ("q", _P), ("win_kv", _P), ("comp_kv", _P), ("sink", _P), ("scale", _F),
                 ("topk_idx", _P), ("out", _P), ("stage_events", _P * 4), ("state", _P), ("state_bytes", _Z),
-                ("flags", _I), ("index_format", _I)]
+                ("flags", _I), ("index_format", _I),
+                ("cand_in", _P), ("cand_k", _I), ("cand_out", _P), ("cand_topk_blocks", _I),
+                ("cand_block_size", _I)]
 
 
 LIT_STEP_UNFUSED = 1
@@ -49,6 +51,10 @@ SIGNATURES = {
     "lit_indexer_scores_fmt": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P]),
     "lit_topk": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "lit_topk_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "lit_candidate_blocks": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
+    "lit_candidate_blocks_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "lit_candidate_blocks_width": (_I, [_I, _I, _I, _I, _I]),
+    "lit_topk_candidates": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _I, _I, _P, _P, _Z, _P]),
     "lit_window_indices": (_I, [_I, _I, _I, _I, _I, _P, _P]),
     "lit_window_width": (_I, [_I, _I, _I]),
     "lit_sparse_attn": (_I, [_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _I, _P, _F,
@@ -153,6 +159,42 @@ def lit_topk(scores, start_pos: int, ratio: int, index_topk: int, idx=None, ws=N
     return idx
 
 
+def lit_candidate_blocks(scores, start_pos: int, ratio: int, topk_blocks: int, block_size: int,
+                         blocks=None, ws=None, stream=None) -> torch.Tensor:
+    """Level one of the two-level top-k: kept block numbers [B,S,kb] int32 (ascending,
+    -1 padded), kb = min(topk_blocks, ceil(T / block_size))."""
+    _need(scores, torch.float32, "scores")
+    B, S, ld = scores.shape
+    kb = library().lit_candidate_blocks_width(S, start_pos, ratio, topk_blocks, block_size)
+    if blocks is None:
+        blocks = torch.empty((B, S, kb), dtype=torch.int32, device=scores.device)
+    _need(blocks, torch.int32, "blocks")
+    need = library().lit_candidate_blocks_workspace_bytes(B, S, start_pos, ratio, block_size)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("lit_candidate_blocks", library().lit_candidate_blocks(
+        _ptr(scores), ld, B, S, start_pos, ratio, topk_blocks, block_size, _ptr(blocks), _ptr(ws),
+        nbytes, _stream(stream)))
+    return blocks
+
+
+def lit_topk_candidates(scores, start_pos: int, ratio: int, index_topk: int, blocks,
+                        block_size: int, idx=None, stream=None) -> torch.Tensor:
+    """Level two: top-k [B,S,k_eff] over the scores with rows outside ``blocks`` at -inf."""
+    _need(scores, torch.float32, "scores")
+    _need(blocks, torch.int32, "blocks")
+    B, S, ld = scores.shape
+    keff = topk_width(S, start_pos, ratio, index_topk)
+    if idx is None:
+        idx = torch.empty((B, S, keff), dtype=torch.int32, device=scores.device)
+    _need(idx, torch.int32, "idx")
+    _check("lit_topk_candidates", library().lit_topk_candidates(
+        _ptr(scores), ld, B, S, start_pos, ratio, index_topk, _ptr(blocks), blocks.shape[-1],
+        block_size, _ptr(idx), None, 0, _stream(stream)))
+    return idx
+
+
 def lit_window_indices(B: int, S: int, start_pos: int, W: int, R: int, win_idx=None,
                        device="cuda", stream=None) -> torch.Tensor:
     width = lit_window_width(S, start_pos, W)
@@ -199,9 +241,13 @@ def lit_sparse_attn(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float, d
 
 def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int, ratio: int,
                    index_topk: int, W: int, scale: float, dv=None, sink=None, topk_idx=None,
-                   out=None, stage_events=None, flags: int = 0, fmt: str = "e4m3") -> tuple:
+                   out=None, stage_events=None, flags: int = 0, fmt: str = "e4m3",
+                   cand_in=None, cand_out=None, cand_topk_blocks: int = 0,
+                   cand_block_size: int = 0) -> tuple:
     """Build the lit_step_args struct (and allocate outputs the caller did not pass).
-    ``fmt`` is the index-code format ("e4m3" or "e2m1"); Di comes from q_sc."""
+    ``fmt`` is the index-code format ("e4m3" or "e2m1"); Di comes from q_sc.  For the
+    two-level top-k, ``cand_in`` [B,S,cand_k] int32 makes this a level-two layer and
+    ``cand_out`` [B,S,kb] int32 the candidate source (blocks of ``cand_block_size``)."""
     B, S, Hi, _ = q8.shape
     Di = 32 * q_sc.shape[-1]
     H, D = q.shape[2], q.shape[3]
@@ -218,7 +264,14 @@ def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int,
                       win_kv=win_kv.data_ptr(), comp_kv=comp_kv.data_ptr(),
                       sink=0 if sink is None else sink.data_ptr(), scale=scale,
                       topk_idx=topk_idx.data_ptr(), out=out.data_ptr(), flags=flags,
-                      index_format=INDEX_FORMATS[fmt])
+                      index_format=INDEX_FORMATS[fmt],
+                      cand_in=0 if cand_in is None else cand_in.data_ptr(),
+                      cand_k=0 if cand_in is None else cand_in.shape[-1],
+                      cand_out=0 if cand_out is None else cand_out.data_ptr(),
+                      cand_topk_blocks=cand_topk_blocks, cand_block_size=cand_block_size)
+    for t, n in ((cand_in, "cand_in"), (cand_out, "cand_out")):
+        if t is not None:
+            _need(t, torch.int32, n)
     if stage_events is not None:
         # hipEvent_t handles (e.g. torch.cuda.Event(...).cuda_event after one record)
         for k, ev in enumerate(stage_events):

@@ -281,21 +281,34 @@ def sparse_attn(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float,
     return out
 
 
-def step(inp, fp32_scores: bool = True) -> dict:
+def step(inp, fp32_scores: bool = True, cand_in=None, cand_topk_blocks: int = 0,
+         cand_block_size: int = 0) -> dict:
     """The whole step: index scores -> top-k -> window rows -> attention.
 
     ``inp`` is a ``lightning_indexer_top_amd.synth.StepInputs``-like object (numpy
     arrays plus sizes).  With ``fp32_scores`` the scores are rounded to float32 before
     selection, so the oracle takes its top-k decision in the precision the kernel keeps
     its scores in; the scores themselves are still the exact fp64 values.
+
+    Two-level top-k: ``cand_topk_blocks`` > 0 makes this layer the candidate source (its
+    kept blocks are returned as "cand"); ``cand_in`` (blocks [B,S,kb]) makes it a level-two
+    layer whose top-k runs over the scores masked to those blocks ("scores" stay unmasked).
     """
     s = index_scores(inp.q8, inp.q_sc, inp.w, inp.k8, inp.k_sc, inp.start_pos, inp.ratio,
                      getattr(inp, "index_fmt", "e4m3"))
     sel = s.astype(np.float32).astype(np.float64) if fp32_scores else s
+    res = {"scores": s}
+    if cand_topk_blocks > 0:
+        res["cand"] = candidate_blocks(sel, inp.start_pos, inp.ratio, cand_topk_blocks,
+                                       cand_block_size)
+    if cand_in is not None:
+        sel = apply_candidates(sel, cand_in, cand_block_size)
+        res["masked"] = sel
     idx = topk(sel, inp.start_pos, inp.ratio, inp.index_topk)
     win = window_indices(inp.B, inp.S, inp.start_pos, inp.W, inp.R)
     o = sparse_attn(inp.q, inp.win_kv, win, inp.comp_kv, idx, inp.sink, inp.scale, inp.dv)
-    return {"scores": s, "idx": idx, "win_idx": win, "out": o}
+    res.update({"idx": idx, "win_idx": win, "out": o})
+    return res
 
 
 def num_threads() -> int:

@@ -87,6 +87,25 @@ def test_indexer_format_refusals(lib):
     assert B.INDEX_FORMATS == {"e4m3": 0, "e2m1": 1}
 
 
+def test_candidate_refusals(lib):
+    f, g = lib.lit_candidate_blocks, lib.lit_topk_candidates
+    need = lib.lit_candidate_blocks_workspace_bytes(2, 1, 65535, 2, 8)
+    assert need >= 2 * 4096 * 4 and need % 256 == 0
+    assert lib.lit_candidate_blocks_width(1, 65535, 2, 2048, 8) == 2048
+    assert lib.lit_candidate_blocks_width(1, 1023, 2, 2048, 8) == 64
+    assert lib.lit_candidate_blocks_width(1, 1023, 2, 2048, 0) == 0
+    assert f(A, 32768, 2, 1, 65535, 2, 2048, 0, A, A, need, None) == 2      # block size 0
+    assert f(A, 32768, 2, 1, 65535, 2, 2048, 8, A, None, 0, None) == 5      # no workspace
+    assert f(A, 32768, 2, 1, 65535, 2, 2048, 8, A, A, need - 1, None) == 5
+    assert f(A, 32770, 2, 1, 65535, 2, 2048, 8, A, A, need, None) == 3      # ld not a multiple of 4
+    assert f(A, 32764, 2, 1, 65535, 2, 2048, 8, A, A, need, None) == 2      # ld < T
+    assert f(A, 32768, 2, 1, 65535, 2, 2048, 8, None, A, need, None) == 1
+    assert f(A, 32768, 0, 1, 65535, 2, 2048, 8, None, None, 0, None) == 0   # nothing to do
+    assert g(A, 32768, 2, 1, 65535, 2, 2048, A, 2048, 0, A, None, 0, None) == 2
+    assert g(A, 32768, 2, 1, 65535, 2, 2048, None, 2048, 8, A, None, 0, None) == 1
+    assert g(A, 1 << 20, 1, 1, (1 << 20) - 1, 1, 64, A, 8, 1, A, None, 0, None) == 4  # bitmap too big
+
+
 def test_topk_refusals(lib):
     f = lib.lit_topk
     assert f(A, 8, 1, 1, 1023, 2, 64, A, None, 0, None) == 2        # ld < T

@@ -393,3 +393,115 @@ def test_step_matches_separate_calls():
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------------
+# two-level top-k: candidate blocks (level one) and the masked top-k (level two); both
+# are integer results of identical fp32 scores, so they are compared bit-exactly
+# ---------------------------------------------------------------------------------
+CAND_CASES = [
+    # B, S, start_pos, ratio, topk_blocks, block_size, ties
+    (2, 1, 16383, 2, 256, 8, False),      # 1024 blocks, keep 256
+    (2, 1, 131071, 4, 2048, 8, False),    # the released shape at 128K: 4096 blocks, keep 2048
+    (1, 1, 1000, 1, 40, 7, False),        # ragged last block
+    (3, 1, 4095, 2, 64, 8, True),         # many equal block scores
+    (1, 300, 0, 2, 16, 4, False),         # prefill from 0: per-query visibility, short queries
+    (1, 70, 900, 3, 20, 8, False),        # a chunk after cached tokens
+    (2, 1, 500, 2, 4096, 8, False),       # more blocks asked than exist
+]
+
+
+def _visible_scores(B, S, start_pos, ratio, seed, ties):
+    from lightning_indexer_top_amd import synth as sy
+    T = (start_pos + S) // ratio
+    s = sy.random_scores(B, S, T, seed=seed, ties=ties)
+    for i in range(S):
+        s[:, i, min(T, (start_pos + i + 1) // ratio):] = -np.inf
+    ld = max(4, (T + 3) // 4 * 4)
+    buf = np.full((B, S, ld), np.nan, dtype=np.float32)   # columns past T are never read
+    buf[..., :T] = s
+    return s.astype(np.float64), buf
+
+
+@pytest.mark.parametrize("B,S,start_pos,ratio,kb,bs,ties", CAND_CASES)
+def test_candidate_blocks_exact(orc, B, S, start_pos, ratio, kb, bs, ties):
+    s, buf = _visible_scores(B, S, start_pos, ratio, 900 + S + kb, ties)
+    got = L.lit_candidate_blocks(dev(buf), start_pos, ratio, kb, bs).cpu().numpy()
+    want = orc.candidate_blocks(s, start_pos, ratio, kb, bs)
+    assert got.shape == want.shape
+    bad = np.argwhere((got != want).any(-1))
+    assert bad.size == 0, f"first mismatch at {bad[0]}: {got[tuple(bad[0])][:12]} vs {want[tuple(bad[0])][:12]}"
+
+
+@pytest.mark.parametrize("B,S,start_pos,ratio,kb,bs,ties", CAND_CASES)
+def test_topk_candidates_exact(orc, B, S, start_pos, ratio, kb, bs, ties):
+    s, buf = _visible_scores(B, S, start_pos, ratio, 1900 + S + kb, ties)
+    # candidates from another layer's scores (level one of a source layer)
+    s2, buf2 = _visible_scores(B, S, start_pos, ratio, 2900 + S + kb, ties)
+    blocks = orc.candidate_blocks(s2, start_pos, ratio, kb, bs)
+    k = max(1, min(kb * bs // 2, 600))
+    got = L.lit_topk_candidates(dev(buf), start_pos, ratio, k, dev(blocks), bs).cpu().numpy()
+    want = orc.topk(orc.apply_candidates(s, blocks, bs), start_pos, ratio, k)
+    assert np.array_equal(got, want)
+
+
+def test_topk_candidates_short_and_empty_lists(orc):
+    """Fewer rows inside the blocks than k (the rest are the lowest rows outside), and an
+    empty candidate list (every row masked: the lowest visible rows)."""
+    s, buf = _visible_scores(2, 1, 4095, 2, 77, False)
+    blocks = np.full((2, 1, 6), -1, dtype=np.int32)
+    blocks[0, 0, :3] = [5, 40, 255]
+    blocks[1, 0, :1] = [100]
+    got = L.lit_topk_candidates(dev(buf), 4095, 2, 64, dev(blocks), 8).cpu().numpy()
+    want = orc.topk(orc.apply_candidates(s, blocks, 8), 4095, 2, 64)
+    assert np.array_equal(got, want)
+    assert set(range(40, 48)) <= set(got[0, 0]) and set(range(800, 808)) <= set(got[1, 0])
+    empty = torch.empty((2, 1, 0), dtype=torch.int32, device="cuda")
+    got = L.lit_topk_candidates(dev(buf), 4095, 2, 64, empty, 8).cpu().numpy()
+    assert (got == np.arange(64)).all()
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_step_two_level(orc, fmt):
+    """A candidate-source layer and a level-two layer of the 128K decode shape (at 32K
+    context): the source's blocks come out of its step, the second layer's picks lie in
+    them, and both layers match the oracle."""
+    kw = dict(B=2, S=1, start_pos=32767, ratio=4, Hi=64, Di=128, H=16, D=128, W=128,
+              index_topk=512, keys="mixture", index_fmt=fmt)
+    src = synth.make_step(seed=61, **kw)
+    lvl2 = synth.make_step(seed=62, **kw)
+    ds, d2 = step_inputs_dev(src), step_inputs_dev(lvl2)
+    kb = orc.candidate_blocks_width(1, 32767, 4, 256, 8)
+    cand = torch.empty((2, 1, kb), dtype=torch.int32, device="cuda")
+    a1, idx1, out1 = L.make_step_args(q8=ds["q8"], q_sc=ds["q_sc"], w=ds["w"], k8=ds["k8"],
+                                      k_sc=ds["k_sc"], q=ds["q"], win_kv=ds["win_kv"],
+                                      comp_kv=ds["comp_kv"], start_pos=src.start_pos,
+                                      ratio=src.ratio, index_topk=src.index_topk, W=src.W,
+                                      scale=src.scale, fmt=fmt, cand_out=cand,
+                                      cand_topk_blocks=256, cand_block_size=8)
+    L.lit_sparse_step(a1, L.step_workspace(a1))
+    a2, idx2, out2 = L.make_step_args(q8=d2["q8"], q_sc=d2["q_sc"], w=d2["w"], k8=d2["k8"],
+                                      k_sc=d2["k_sc"], q=d2["q"], win_kv=d2["win_kv"],
+                                      comp_kv=d2["comp_kv"], start_pos=lvl2.start_pos,
+                                      ratio=lvl2.ratio, index_topk=lvl2.index_topk, W=lvl2.W,
+                                      scale=lvl2.scale, fmt=fmt, cand_in=cand, cand_block_size=8)
+    L.lit_sparse_step(a2, L.step_workspace(a2))
+    torch.cuda.synchronize()
+    ref1 = orc.step(src, cand_topk_blocks=256, cand_block_size=8)
+    g_cand = cand.cpu().numpy()
+    # level one decides on the kernel's fp32 scores; near-equal block maxima may swap
+    for b in range(2):
+        bmax = ref1["scores"][b, 0].reshape(1024, 8).max(-1)
+        bmax[-1] = np.inf                              # the newest block is pinned
+        ok, why = topk_sets_agree(bmax, ref1["cand"][b, 0], g_cand[b, 0])
+        assert ok, f"candidate blocks of sequence {b}: {why}"
+        assert 1023 in g_cand[b, 0]
+    _check_step(orc, src, idx1, out1)
+    ref2 = orc.step(lvl2, cand_in=g_cand, cand_block_size=8)
+    d_idx2, d_out2 = idx2.cpu().numpy(), bf16_host(out2)
+    for b in range(2):
+        assert set(d_idx2[b, 0] // 8) <= set(g_cand[b, 0])
+        ok, why = topk_sets_agree(ref2["masked"][b, 0], ref2["idx"][b, 0], d_idx2[b, 0])
+        assert ok, f"level-two picks of sequence {b}: {why}"
+        if set(ref2["idx"][b, 0]) == set(d_idx2[b, 0]):
+            assert np.abs(d_out2[b, 0] - ref2["out"][b, 0]).max() <= ATTN_TOL
