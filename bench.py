@@ -60,6 +60,10 @@ def step_bytes(sp: dict) -> dict:
         attn = (4 * B * S * keff + B * R * 2 * D + B * T * 2 * D + B * S * H * (2 * D + 2 * dv))
         step = (B * T * key_row + B * S * Hi * (key_row + 4) + 8 * B * S * keff + B * R * 2 * D
                 + B * T * 2 * D + B * S * H * (2 * D + 2 * dv))
+    kb = sp.get("cand_k", 0)
+    if kb:  # a level-two layer also reads its candidate block list
+        topk += 4 * B * S * kb
+        step += 4 * B * S * kb
     return {"step": step, "indexer": indexer, "topk": topk, "attention": attn}
 
 
@@ -209,6 +213,10 @@ def main() -> int:
 
     spec = dict(synth.WORKLOADS[args.workload])
     fmt = spec.get("index_fmt", "e4m3")
+    cand_kb, cand_bs = spec.get("cand_topk_blocks", 0), spec.get("cand_block_size", 0)
+    if cand_kb:
+        spec["cand_k"] = L.library().lit_candidate_blocks_width(
+            spec["S"], spec["start_pos"], spec["ratio"], cand_kb, cand_bs)
     sb = step_bytes(spec)
     n_inst = args.instances or max(2, min(512, math.ceil(3 * MALL_BYTES / sb["step"])))
     K, Wm = args.steps, args.warmup
@@ -220,13 +228,23 @@ def main() -> int:
     insts, argv, keep = [], [], []
     t0 = time.perf_counter()
     for j in range(n_inst):
-        d = synth.draw_step_device(spec, seed=spec["seed"] * 1000 + j, device=dev)
+        insts.append(synth.draw_step_device(spec, seed=spec["seed"] * 1000 + j, device=dev))
+    # a level-two layer's candidate blocks come from a candidate-source layer: here the
+    # level-one selection over the next instance's index scores
+    cands = [None] * n_inst
+    if cand_kb:
+        for j in range(n_inst):
+            s_ = insts[(j + 1) % n_inst]
+            sc = L.lit_indexer_scores(s_["q8"], s_["q_sc"], s_["w"], s_["k8"], s_["k_sc"],
+                                      spec["start_pos"], spec["ratio"], fmt=fmt)
+            cands[j] = L.lit_candidate_blocks(sc, spec["start_pos"], spec["ratio"], cand_kb, cand_bs)
+    for j, d in enumerate(insts):
         a, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
                                        k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
                                        comp_kv=d["comp_kv"], start_pos=spec["start_pos"],
                                        ratio=spec["ratio"], index_topk=spec["index_topk"],
-                                       W=spec["W"], scale=spec["D"] ** -0.5, fmt=fmt)
-        insts.append(d)
+                                       W=spec["W"], scale=spec["D"] ** -0.5, fmt=fmt,
+                                       cand_in=cands[j], cand_block_size=cand_bs)
         argv.append(a)
         keep.append((idx, out))
     ws = L.step_workspace(argv[0], device=dev)
@@ -296,11 +314,22 @@ def main() -> int:
             spec["start_pos"], spec["ratio"], scores=scores[j], fmt=fmt)) for j in range(n_inst)],
         "topk": [(lambda j=j: L.lit_topk(scores[j], spec["start_pos"], spec["ratio"],
                                          spec["index_topk"], idx=keep[j][0]))
+                 if not cand_kb else
+                 (lambda j=j: L.lit_topk_candidates(scores[j], spec["start_pos"], spec["ratio"],
+                                                    spec["index_topk"], cands[j], cand_bs,
+                                                    idx=keep[j][0]))
                  for j in range(n_inst)],
         "attention": [(lambda j=j: L.lit_sparse_attn(
             insts[j]["q"], insts[j]["win_kv"], win, insts[j]["comp_kv"], keep[j][0], None,
             spec["D"] ** -0.5, out=keep[j][1], ws=ws)) for j in range(n_inst)],
     }
+    if cand_kb:
+        # the candidate source's level one (not part of this layer's step; reported beside it)
+        cws = torch.empty(max(256, L.library().lit_candidate_blocks_workspace_bytes(
+            spec["B"], spec["S"], spec["start_pos"], spec["ratio"], cand_bs)), dtype=torch.uint8, device=dev)
+        stage_calls["candidates"] = [(lambda j=j: L.lit_candidate_blocks(
+            scores[j], spec["start_pos"], spec["ratio"], cand_kb, cand_bs, blocks=cands[j], ws=cws))
+            for j in range(n_inst)]
     stage_reps = max(1, min(20, 2000 // n_inst))
     stages_us = {}
     for name, calls in stage_calls.items():
@@ -322,7 +351,7 @@ def main() -> int:
         dom_us = gpu_ms * 1e3 / K
         dom_bytes = sb["step"]
     else:
-        dom = max(stages_us, key=stages_us.get)
+        dom = max((k for k in stages_us if k in sb), key=stages_us.get)
         kernels = {"indexer": ("indexer_scores_kernel", "indexer.hip"),
                    "topk": ("topk_kernel", "topk.hip"),
                    "attention": ("sparse_attn_kernel+attn_merge_kernel", "attention.hip")}
@@ -360,6 +389,7 @@ def main() -> int:
                    "context": spec["start_pos"] + spec["S"], "compress_ratio": spec["ratio"],
                    "window": spec["W"], "heads": spec["H"], "head_dim": spec["D"],
                    "index_heads": spec["Hi"], "index_dim": spec["Di"], "index_format": fmt,
+                   **({"candidate_blocks": cand_kb, "candidate_block_size": cand_bs} if cand_kb else {}),
                    "index_topk": spec["index_topk"], "input_instances": n_inst,
                    "timing": "HIP graph replay over rotating cold-cache instances",
                    "step_form": "fused single kernel" if fused else "indexer, top-k, attention kernels"},

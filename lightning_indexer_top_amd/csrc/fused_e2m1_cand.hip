@@ -1,0 +1,15 @@
+// fused_e2m1_cand.hip -- the fused decode kernels for fp4 (e2m1) index codes in a level-two layer of the two-level top-k
+// (fused_kernel.h), compiled on their own so that the instantiation sets build in parallel.
+#include "fused_kernel.h"
+
+namespace lit {
+
+hipError_t launch_fused_e2m1_cand(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream) {
+    return FusedKernels<kFmtE2M1, true>::launch(f, grid, dyn_bytes, stream);
+}
+
+int fused_per_cu_e2m1_cand(int D, int DI, int HT, size_t dyn_bytes, bool cached) {
+    return FusedKernels<kFmtE2M1, true>::per_cu(D, DI, HT, dyn_bytes, cached);
+}
+
+}  // namespace lit

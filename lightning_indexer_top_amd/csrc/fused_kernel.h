@@ -1,7 +1,8 @@
 // fused_kernel.h -- the whole sparse-attention step for decode-sized batches in one
 // launch: indexer scores -> exact top-k -> gather attention -> merge.  Included by one
-// source file per index-code format (fused_e4m3.hip, fused_e2m1.hip), each of which
-// instantiates the kernels of its format; fused_decode.hip plans and dispatches.
+// source file per index-code format and masking (fused_e4m3.hip, fused_e2m1.hip and
+// their _cand forms for level-two layers of the two-level top-k), each of which
+// instantiates its kernels; fused_decode.hip plans and dispatches.
 //
 // What is computed is exactly what indexer.hip, topk.hip and attention.hip compute
 // (DeepSeek-V4.1-Flash-NVFP4 inference/model.py, Indexer.forward and
@@ -58,6 +59,8 @@ constexpr int kThreads = kSelThreads;
 constexpr int kHeads = 16;
 constexpr int kCacheQ = 8;      // team score quads per thread kept in registers (and LDS)
 constexpr int kBatch = 16;      // team score quads per thread loaded per round (uncached form)
+constexpr int kChunkMax = 8192;     // largest member chunk the plan takes
+constexpr int kFusedCandMax = 2048; // candidate blocks per query the fused level two takes
 
 // Per-query region of the state buffer, at a fixed stride whatever the team size: the
 // query's launch counter, then one 16-byte flag slot per member for each of the two
@@ -193,7 +196,10 @@ __device__ inline uint32_t wg_sum(uint32_t v, uint32_t *red) {
 // are separate kernels so that the re-reading form's loads never share a code path with
 // the cached form (a load pending on one path of a branch makes the compiler wait for
 // every load in flight where the paths join, which would stall the early row gather).
-template <int D, int DI, int FMT, int HT, bool CACHED>
+// MASK: a level-two layer of the two-level top-k (DeepSeek-V4.1-Flash-NVFP4 model.py,
+// Indexer.forward with candidates): rows outside the query's candidate blocks score
+// -inf before the selection.
+template <int D, int DI, int FMT, int HT, bool CACHED, bool MASK>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     constexpr int LD = D + 4;
     __shared__ FusedLds sm;
@@ -201,6 +207,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     __shared__ float wm[4 * kHeads], wl[4 * kHeads];
     __shared__ float hf[4 * kHeads], hl[kHeads], hm[kHeads];  // per-head merge factors
     extern __shared__ __attribute__((aligned(16))) float dyn[];  // chunk scores, picks (ints), team scores
+    __shared__ uint32_t ckeep[MASK ? kChunkMax / 32 + 2 : 1];  // kept candidate blocks of this chunk
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -237,6 +244,18 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     bf16x8 qb[D / 32];
     load_q_operands<D>(qb, aa.q, (size_t)q, g, c);
 
+    // level two: the query's candidate blocks are requested now and turned into a bitmap
+    // of the blocks that meet this member's chunk after scoring
+    int cblk[MASK ? kFusedCandMax / kThreads : 1];
+    const int blk0 = MASK ? c0 / f.cand_bs : 0;
+    const int nbk = MASK && n > 0 ? (c1 - 1) / f.cand_bs - blk0 + 1 : 0;
+    if constexpr (MASK) {
+        const int32_t *cl = f.cand + (size_t)q * f.cand_k;
+#pragma unroll
+        for (int r = 0; r < kFusedCandMax / kThreads; ++r) cblk[r] = cl[min(tid + kThreads * r, f.cand_k - 1)];
+        for (int j = tid; j < (nbk + 31) / 32; j += kThreads) ckeep[j] = 0u;
+    }
+
     // ------------------------------------------------------------------ phase A
     {
         IdxQuery<DI, FMT, HT> qr;
@@ -252,6 +271,22 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         }
     }
     __syncthreads();
+    if constexpr (MASK) {
+        if (select) {  // (every visible row is picked otherwise, masked or not)
+#pragma unroll
+            for (int r = 0; r < kFusedCandMax / kThreads; ++r) {
+                const int blk = cblk[r] - blk0;
+                if (tid + kThreads * r < f.cand_k && cblk[r] >= 0 && blk >= 0 && blk < nbk)
+                    atomicOr(&ckeep[blk >> 5], 1u << (blk & 31));
+            }
+            __syncthreads();
+            for (int t = tid; t < n; t += kThreads) {
+                const int blk = (c0 + t) / f.cand_bs - blk0;
+                if (!((ckeep[blk >> 5] >> (blk & 31)) & 1u)) sc[t] = -INFINITY;
+            }
+            __syncthreads();
+        }
+    }
     if (select) {
         // publish this chunk's scores (16-byte coherent stores; chunks start at multiples of 256)
         uint32_t kmax = 0u, kminc = 0u;  // team max key, and max of complemented keys (= min)
@@ -263,7 +298,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             for (int e = 0; e < 4; ++e) {
                 const uint32_t k = order_key(v[e]);
                 kmax = max(kmax, k);
-                kminc = max(kminc, ~k);
+                // masked rows (-inf) stay out of the value range; they share its lowest bin
+                if (!MASK || v[e] != -INFINITY) kminc = max(kminc, ~k);
             }
             st128_agent(ts_r, (uint32_t)(c0 + 4 * j) * 4u,
                         u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
@@ -735,17 +771,18 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
 }
 }  // namespace
 
-// The kernels of one index-code format: launch, and co-resident workgroups per CU.
-template <int FMT>
+// The kernels of one index-code format (and level-two masking or not): launch, and
+// co-resident workgroups per CU.
+template <int FMT, bool MASK>
 struct FusedKernels {
     template <int D, int DI, int HT>
     static hipError_t cfg(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream) {
         if (f.cache_lds)
-            hipLaunchKernelGGL((fused_decode_kernel<D, DI, FMT, HT, true>), dim3(grid), dim3(kThreads), dyn_bytes,
-                               stream, f);
+            hipLaunchKernelGGL((fused_decode_kernel<D, DI, FMT, HT, true, MASK>), dim3(grid), dim3(kThreads),
+                               dyn_bytes, stream, f);
         else
-            hipLaunchKernelGGL((fused_decode_kernel<D, DI, FMT, HT, false>), dim3(grid), dim3(kThreads), dyn_bytes,
-                               stream, f);
+            hipLaunchKernelGGL((fused_decode_kernel<D, DI, FMT, HT, false, MASK>), dim3(grid), dim3(kThreads),
+                               dyn_bytes, stream, f);
         return hipGetLastError();
     }
     template <int D, int DI>
@@ -773,10 +810,10 @@ struct FusedKernels {
     }
     template <int D, int DI, int HT>
     static hipError_t occ(int *per_cu, size_t dyn, bool cached) {
-        return cached ? hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, fused_decode_kernel<D, DI, FMT, HT, true>,
-                                                                     kThreads, dyn)
-                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, fused_decode_kernel<D, DI, FMT, HT, false>,
-                                                                     kThreads, dyn);
+        return cached ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            per_cu, fused_decode_kernel<D, DI, FMT, HT, true, MASK>, kThreads, dyn)
+                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            per_cu, fused_decode_kernel<D, DI, FMT, HT, false, MASK>, kThreads, dyn);
     }
     template <int D, int DI>
     static hipError_t occ_di(int HT, int *per_cu, size_t dyn, bool cached) {

@@ -269,12 +269,19 @@ static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld
     return *scores_bytes + rest;
 }
 
+// The fused kernel takes a level-two layer with 1..2048 candidate blocks per query; a
+// candidate source (cand_out) runs the multi-kernel form.
+constexpr int kFusedCandMaxApi = 2048;
+
 static FusedPlan step_fused_plan(const lit_step_args *s) {
     FusedPlan p{};
     p.ok = false;
-    if ((s->flags & LIT_STEP_UNFUSED) || step_uses_candidates(s)) return p;
+    if (s->flags & LIT_STEP_UNFUSED) return p;
+    if (s->cand_out) return p;
+    const bool masked = s->cand_in != nullptr;
+    if (masked && (s->cand_k < 1 || s->cand_k > kFusedCandMaxApi)) return p;
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
-    return plan_fused(s->index_format, s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D, s->dv,
+    return plan_fused(s->index_format, masked, s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D, s->dv,
                       s->W, keff);
 }
 
@@ -355,6 +362,11 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
                         s->scale, s->out, nullptr};
         f.topk_out = s->topk_idx;
         f.keff = keff;
+        if (s->cand_in) {
+            f.cand = s->cand_in;
+            f.cand_k = s->cand_k;
+            f.cand_bs = s->cand_block_size;
+        }
         f.spin_limit = 1u << 22;
         if ((e = launch_fused(f, fp, ws, s->state, hs)) != hipSuccess) return hip_status(e);
         for (int k = 1; k < 4; ++k)

@@ -164,6 +164,10 @@ struct FusedArgs {
     bool cache_lds;               // the team's scores are kept in LDS during selection
     bool lds_bins;                // otherwise: their 16-bit value bins are kept in LDS
     int bins_words;               // 32-bit words those bins take (candidate positions follow)
+    // level two of the two-level top-k: candidate blocks [B*S, cand_k] of cand_bs rows
+    // (masked kernels only; 1 <= cand_k <= 2048)
+    const int32_t *cand = nullptr;
+    int cand_k = 0, cand_bs = 1;
 };
 struct FusedPlan {
     bool ok;
@@ -172,16 +176,21 @@ struct FusedPlan {
     long ld;
     size_t dyn_bytes;
 };
-FusedPlan plan_fused(int fmt, int B, int S, int start_pos, int ratio, int Hi, int Di, int D, int dv, int W,
-                     int keff);
+FusedPlan plan_fused(int fmt, bool masked, int B, int S, int start_pos, int ratio, int Hi, int Di, int D, int dv,
+                     int W, int keff);
 size_t fused_state_bytes(const FusedPlan &p);  // zero-filled before first use
 size_t fused_ws_bytes(const FusedPlan &p, int dv);
 hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream);
 // The kernels of each index-code format (fused_e4m3.hip, fused_e2m1.hip): launch, and
 // co-resident workgroups per CU for a shape (0 when not instantiated).
+// The _cand forms mask the scores of a level-two layer (FusedArgs::cand).
 hipError_t launch_fused_e4m3(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
 hipError_t launch_fused_e2m1(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
+hipError_t launch_fused_e4m3_cand(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
+hipError_t launch_fused_e2m1_cand(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
 int fused_per_cu_e4m3(int D, int DI, int HT, size_t dyn_bytes, bool cached);
 int fused_per_cu_e2m1(int D, int DI, int HT, size_t dyn_bytes, bool cached);
+int fused_per_cu_e4m3_cand(int D, int DI, int HT, size_t dyn_bytes, bool cached);
+int fused_per_cu_e2m1_cand(int D, int DI, int HT, size_t dyn_bytes, bool cached);
 
 }  // namespace lit

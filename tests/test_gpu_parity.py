@@ -461,11 +461,13 @@ def test_topk_candidates_short_and_empty_lists(orc):
     assert (got == np.arange(64)).all()
 
 
+@pytest.mark.parametrize("flags", MODES)
 @pytest.mark.parametrize("fmt", FORMATS)
-def test_step_two_level(orc, fmt):
+def test_step_two_level(orc, fmt, flags):
     """A candidate-source layer and a level-two layer of the 128K decode shape (at 32K
     context): the source's blocks come out of its step, the second layer's picks lie in
-    them, and both layers match the oracle."""
+    them, and both layers match the oracle.  The level-two layer runs fused or as
+    kernels; the source always runs as kernels."""
     kw = dict(B=2, S=1, start_pos=32767, ratio=4, Hi=64, Di=128, H=16, D=128, W=128,
               index_topk=512, keys="mixture", index_fmt=fmt)
     src = synth.make_step(seed=61, **kw)
@@ -484,9 +486,13 @@ def test_step_two_level(orc, fmt):
                                       k_sc=d2["k_sc"], q=d2["q"], win_kv=d2["win_kv"],
                                       comp_kv=d2["comp_kv"], start_pos=lvl2.start_pos,
                                       ratio=lvl2.ratio, index_topk=lvl2.index_topk, W=lvl2.W,
-                                      scale=lvl2.scale, fmt=fmt, cand_in=cand, cand_block_size=8)
+                                      scale=lvl2.scale, fmt=fmt, cand_in=cand, cand_block_size=8,
+                                      flags=flags)
+    st2 = L.attach_state(a2)
+    assert (st2 is not None) == (flags == 0)
     L.lit_sparse_step(a2, L.step_workspace(a2))
     torch.cuda.synchronize()
+    assert L.state_error(st2) == 0
     ref1 = orc.step(src, cand_topk_blocks=256, cand_block_size=8)
     g_cand = cand.cpu().numpy()
     # level one decides on the kernel's fp32 scores; near-equal block maxima may swap
@@ -505,3 +511,30 @@ def test_step_two_level(orc, fmt):
         assert ok, f"level-two picks of sequence {b}: {why}"
         if set(ref2["idx"][b, 0]) == set(d_idx2[b, 0]):
             assert np.abs(d_out2[b, 0] - ref2["out"][b, 0]).max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("flags", MODES)
+def test_step_level_two_short_candidate_list(orc, flags):
+    """Fewer rows inside the candidate blocks than k: the remaining picks are the lowest
+    rows outside them (all at -inf), in both step forms; a second sequence lists one block
+    twice and one out of range."""
+    inp = synth.make_step(B=2, S=1, start_pos=4095, ratio=2, Hi=16, Di=64, H=16, D=128, W=128,
+                          index_topk=64, seed=73)
+    d = step_inputs_dev(inp)
+    blocks = np.array([[[3, 17, 200, 255]], [[9, 9, 4000, -1]]], dtype=np.int32)
+    cand = dev(blocks)
+    args, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
+                                      k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
+                                      comp_kv=d["comp_kv"], start_pos=inp.start_pos,
+                                      ratio=inp.ratio, index_topk=inp.index_topk, W=inp.W,
+                                      scale=inp.scale, cand_in=cand, cand_block_size=8,
+                                      flags=flags)
+    state = L.attach_state(args)
+    L.lit_sparse_step(args, L.step_workspace(args))
+    torch.cuda.synchronize()
+    assert L.state_error(state) == 0
+    ref = orc.step(inp, cand_in=blocks, cand_block_size=8)
+    got = idx.cpu().numpy()
+    assert np.array_equal(got, ref["idx"]), (got[:, 0, :40], ref["idx"][:, 0, :40])
+    err = np.abs(bf16_host(out) - ref["out"]).max()
+    assert err <= ATTN_TOL, err
