@@ -420,8 +420,17 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         const float scale = mx > mn ? (float)kVBins / (mx - mn) : 0.f;
         const float bias = -mn * scale;
         // pass 1: value bins (kept, 16 bits each) and histogram; cached positions past the
-        // visible rows take the spill bin kVBins
+        // visible rows take the spill bin kVBins.  Masked rows (-inf, level two) fall in bin
+        // 0; they are counted per thread and added once per wave, since thousands of LDS
+        // atomics on one counter would serialise.
         uint32_t bins[kCacheQ * 2];
+        uint32_t ninf = 0;
+        auto hist_add = [&](uint32_t bin, float x) {
+            if (MASK && x == -INFINITY)
+                ++ninf;
+            else
+                atomicAdd(&sm.hist[bin], 1u);
+        };
         if (cached) {
             if (full) {
 #pragma unroll
@@ -431,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         bb[e] = (uint32_t)value_bin(__uint_as_float(vals[r][e]), scale, bias);
-                        atomicAdd(&sm.hist[bb[e]], 1u);
+                        hist_add(bb[e], __uint_as_float(vals[r][e]));
                     }
                     bins[2 * r] = bb[0] | (bb[1] << 16);
                     bins[2 * r + 1] = bb[2] | (bb[3] << 16);
@@ -446,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                         bb[e] = 4 * (tid + kThreads * r) + e < nvis
                                     ? (uint32_t)value_bin(__uint_as_float(vals[r][e]), scale, bias)
                                     : (uint32_t)kVBins;
-                        atomicAdd(&sm.hist[bb[e]], 1u);
+                        hist_add(bb[e], bb[e] == (uint32_t)kVBins ? 0.f : __uint_as_float(vals[r][e]));
                     }
                     bins[2 * r] = bb[0] | (bb[1] << 16);
                     bins[2 * r + 1] = bb[2] | (bb[3] << 16);
@@ -458,9 +467,14 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             const bool keep = f.lds_bins;
             each([&](int t, float x) {
                 const int bin = value_bin(x, scale, bias);
-                atomicAdd(&sm.hist[bin], 1u);
+                hist_add((uint32_t)bin, x);
                 if (keep) bins16[t] = (uint16_t)bin;
             });
+        }
+        if constexpr (MASK) {
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) ninf += (uint32_t)__shfl_xor((int)ninf, off);
+            if (lane == 0 && ninf) atomicAdd(&sm.hist[0], ninf);
         }
         __syncthreads();
         find_bin(sm.hist, kVBins, f.keff, sm.wsum, &sm.bin, &sm.above);

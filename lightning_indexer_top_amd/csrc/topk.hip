@@ -28,6 +28,8 @@ namespace lit {
 namespace {
 
 constexpr int kThreads = 1024;
+// order key of -inf: the key every masked column takes (and a visible -inf score too)
+constexpr uint32_t kMaskedKey = 0x007FFFFFu;
 
 // Columns a query sees: its visible rows, or (level one) the blocks holding them.
 __device__ inline int visible_columns(const TopkArgs &a, int i) {
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     auto key_at = [&](int t, float v) -> uint32_t {
         if constexpr (CAND) {
             const int blk = t / a.cand_bs;
-            if (!((keep[blk >> 5] >> (blk & 31)) & 1u)) return order_key(-INFINITY);
+            if (!((keep[blk >> 5] >> (blk & 31)) & 1u)) return kMaskedKey;
         }
         return order_key(v);
     };
@@ -107,12 +109,24 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         const int nbins = pass == 2 ? 1024 : 2048;
         for (int j = tid; j < 2048; j += kThreads) hist[j] = 0;
         __syncthreads();
+        // masked columns (level two) share one key: counted per thread and added once per
+        // wave, since thousands of LDS atomics on one counter would serialise
+        uint32_t nmask = 0;
         for (int seg = 0; seg < nseg; ++seg) {
             const int cnt = nseg == 1 ? cnt0 : load(seg);
 #pragma unroll
             for (int u = 0; u < ITEMS; ++u)
-                if (u < cnt && (keys[u] & pmask) == prefix)
-                    atomicAdd(&hist[(keys[u] >> shift) & (nbins - 1)], 1);
+                if (u < cnt && (keys[u] & pmask) == prefix) {
+                    if (CAND && keys[u] == kMaskedKey)
+                        ++nmask;
+                    else
+                        atomicAdd(&hist[(keys[u] >> shift) & (nbins - 1)], 1);
+                }
+        }
+        if constexpr (CAND) {
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) nmask += (uint32_t)__shfl_xor((int)nmask, off);
+            if ((tid & 63) == 0 && nmask) atomicAdd(&hist[(kMaskedKey >> shift) & (nbins - 1)], (int)nmask);
         }
         __syncthreads();
         // Thread j owns bins hi = nbins-1-2j and hi-1 (descending); the scan over

@@ -209,6 +209,11 @@ WORKLOADS = {
     "decode-128k-2level": dict(B=2, S=1, start_pos=131071, ratio=4, Hi=64, Di=128, H=16, D=128,
                                W=128, index_topk=2048, seed=20261282, keys="mixture",
                                cand_topk_blocks=2048, cand_block_size=8),
+    # decode-16k as a level-two layer: 2048 blocks of 8 cover all 8192 rows, so the masked
+    # kernel runs with nothing masked (the cost of the masking machinery alone)
+    "decode-16k-2level": dict(B=8, S=1, start_pos=16383, ratio=2, Hi=64, Di=128, H=16, D=192,
+                              W=128, index_topk=2048, seed=20261292, cand_topk_blocks=2048,
+                              cand_block_size=8),
     "decode-128k-fp4": dict(B=2, S=1, start_pos=131071, ratio=4, Hi=64, Di=128, H=16, D=128,
                             W=128, index_topk=2048, seed=20261272, keys="mixture",
                             index_fmt="e2m1"),
