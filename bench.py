@@ -64,6 +64,13 @@ def step_bytes(sp: dict) -> dict:
     if kb:  # a level-two layer also reads its candidate block list
         topk += 4 * B * S * kb
         step += 4 * B * S * kb
+    nl = sp.get("layers", 1)
+    if nl > 1 and S == 1:
+        # every further layer reads its queries, window rows and the shared list and writes
+        # its output; the shared compressed rows are counted once
+        extra = (nl - 1) * B * (W * (2 * D + 4) + 4 * keff + 2 * H * D + 2 * H * dv)
+        step += extra
+        attn += extra
     return {"step": step, "indexer": indexer, "topk": topk, "attention": attn}
 
 
@@ -271,7 +278,31 @@ def main() -> int:
         torch.cuda.synchronize()
         return g
 
-    step_calls = [(lambda j=j: L.lit_sparse_step(argv[j], ws)) for j in range(n_inst)]
+    nl = spec.get("layers", 1)
+    if nl > 1:
+        # the layers that reuse this layer's top-k: their own queries and window KV, the
+        # shared compressed KV and list, attention in one call after the step
+        g_ = torch.Generator(device=dev)
+        g_.manual_seed(spec["seed"] + 7)
+        more = [dict(q=torch.randn(nl - 1, spec["B"], spec["S"], spec["H"], spec["D"], device=dev,
+                                   generator=g_).to(torch.bfloat16),
+                     win=torch.randn(nl - 1, spec["B"], insts[j]["R"], spec["D"], device=dev,
+                                     generator=g_).to(torch.bfloat16),
+                     out=torch.empty(nl - 1, spec["B"], spec["S"], spec["H"], spec["D"], device=dev,
+                                     dtype=torch.bfloat16)) for j in range(n_inst)]
+        lws = torch.empty(max(256, L.library().lit_sparse_attn_layers_workspace_bytes(
+            nl - 1, spec["B"], spec["S"], spec["H"], spec["D"],
+            L.lit_window_width(spec["S"], spec["start_pos"], spec["W"]), keep[0][0].shape[-1])),
+            dtype=torch.uint8, device=dev)
+
+        def layers_call(j):
+            L.lit_sparse_attn_layers(more[j]["q"], more[j]["win"], None, insts[j]["comp_kv"], keep[j][0],
+                                     None, spec["D"] ** -0.5, out=more[j]["out"], ws=lws,
+                                     window=spec["W"], start_pos=spec["start_pos"])
+
+        step_calls = [(lambda j=j: (L.lit_sparse_step(argv[j], ws), layers_call(j))) for j in range(n_inst)]
+    else:
+        step_calls = [(lambda j=j: L.lit_sparse_step(argv[j], ws)) for j in range(n_inst)]
     reps, rem = divmod(K, n_inst)
     g_full = capture(step_calls) if reps else None
     g_rem = capture(step_calls[:rem]) if rem else None
@@ -344,8 +375,32 @@ def main() -> int:
         del g
     log("[bench] multi-kernel stage means (us): " + ", ".join(f"{k} {v:.2f}" for k, v in stages_us.items()))
 
+    def timed_graph_us(calls):
+        g = capture(calls)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(stage_reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (stage_reps * len(calls))
+
     step_gbps = sb["step"] / (ms_per_step * 1e-3) / 1e9
-    if fused:
+    if fused and nl > 1:
+        # the source layer's fused kernel and the other layers' attention, timed apart
+        stages_us["fused_step"] = timed_graph_us([(lambda j=j: L.lit_sparse_step(argv[j], ws))
+                                                  for j in range(n_inst)])
+        stages_us["layers"] = timed_graph_us([(lambda j=j: layers_call(j)) for j in range(n_inst)])
+        log(f"[bench] fused step {stages_us['fused_step']:.2f} us, other layers {stages_us['layers']:.2f} us")
+        one = step_bytes({k: v for k, v in spec.items() if k != "layers"})["step"]
+        kv_rows = spec["B"] * keep[0][0].shape[-1] * 2 * spec["D"]
+        if stages_us["layers"] > stages_us["fused_step"]:
+            dom, kname, ksrc = "layers", "sparse_attn_kernel+attn_merge_kernel", "attention.hip"
+            dom_us, dom_bytes = stages_us["layers"], sb["step"] - one + kv_rows
+        else:
+            dom, kname, ksrc = "step", "fused_decode_kernel", fused_sources(spec)
+            dom_us, dom_bytes = stages_us["fused_step"], one
+    elif fused:
         # one kernel per step: its average duration is the event-timed region / K
         dom, kname, ksrc = "step", "fused_decode_kernel", fused_sources(spec)
         dom_us = gpu_ms * 1e3 / K
@@ -390,9 +445,11 @@ def main() -> int:
                    "window": spec["W"], "heads": spec["H"], "head_dim": spec["D"],
                    "index_heads": spec["Hi"], "index_dim": spec["Di"], "index_format": fmt,
                    **({"candidate_blocks": cand_kb, "candidate_block_size": cand_bs} if cand_kb else {}),
+                   **({"layers_sharing_topk": nl} if nl > 1 else {}),
                    "index_topk": spec["index_topk"], "input_instances": n_inst,
                    "timing": "HIP graph replay over rotating cold-cache instances",
-                   "step_form": "fused single kernel" if fused else "indexer, top-k, attention kernels"},
+                   "step_form": ("fused single kernel" if fused else "indexer, top-k, attention kernels")
+                   + (f" + one attention call for {nl - 1} more layers" if nl > 1 else "")},
         "hbm": {"step_bytes": sb["step"], "achieved_gbps": round(step_gbps, 1),
                 "peak_gbps": HBM_PEAK_GBPS, "frac": round(step_gbps / HBM_PEAK_GBPS, 4)},
         "kernel_stages_us": {k: round(v, 3) for k, v in stages_us.items()},

@@ -10,7 +10,8 @@
  *   2. lit_topk           : a per-query selector keeps the index_topk best rows
  *      (lit_candidate_blocks / lit_topk_candidates: the two-level form);
  *   3. lit_sparse_attn    : attention with an online softmax over the sliding
- *      window and the selected compressed rows, one shared KV head (K = V).
+ *      window and the selected compressed rows, one shared KV head (K = V);
+ *      lit_sparse_attn_layers runs several layers over one shared list.
  *   lit_window_indices builds the window row lists; lit_sparse_step runs 1-3
  *   (window rows derived in-kernel) as one stream-ordered sequence.
  *
@@ -233,6 +234,37 @@ lit_status lit_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv
                            int K, const float *sink, float scale, uint16_t *out, void *ws,
                            size_t ws_bytes, void *stream);
 size_t lit_sparse_attn_workspace_bytes(int B, int S, int H, int dv, int W, int K);
+
+/*
+ * lit_sparse_attn_layers -- lit_sparse_attn for L layers that share one row list
+ * and one compressed KV: [V4.1] Attention.forward / _compress_topk_idxs, where
+ * the layers between index sources reuse the source's top-k list
+ * (index_source_layers) and the shared compressed cache (kv_source_layers), each
+ * with its own queries, window KV and sink.  Layer l's output is exactly what
+ * lit_sparse_attn gives for q[l], win_kv[l], sink[l] and the shared lists.
+ *
+ *   q        (device) bf16 [L, B, S, H, D]
+ *   win_kv   (device) bf16 [L, B, R, D]   each layer's window source; NULL if W == 0
+ *   win_idx  (device) i32  [B, S, W]      shared; or NULL with W > 0: the window of
+ *                                         size W is derived from start_pos, as
+ *                                         lit_window_indices lists it (R must cover
+ *                                         it as there)
+ *   comp_kv  (device) bf16 [B, T_cap, D]  shared
+ *   comp_idx (device) i32  [B, S, K]      shared
+ *   sink     (device) f32  [L, H] or NULL
+ *   out      (device) bf16 [L, B, S, H, dv]
+ *   ws, ws_bytes  lit_sparse_attn_layers_workspace_bytes() bytes
+ * Requirements: as lit_sparse_attn; L >= 1 and L*B*S <= 65535.  The workgroups of
+ * one query's layers are launched side by side, so rows one layer gathers are
+ * cache hits for the others.
+ */
+lit_status lit_sparse_attn_layers(int L, const uint16_t *q, int B, int S, int H, int D, int dv,
+                                  const uint16_t *win_kv, int R, const int32_t *win_idx, int W,
+                                  int start_pos, const uint16_t *comp_kv, int T_cap, const int32_t *comp_idx,
+                                  int K, const float *sink, float scale, uint16_t *out, void *ws,
+                                  size_t ws_bytes, void *stream);
+/* W here is the window list's width (lit_window_width for a derived window). */
+size_t lit_sparse_attn_layers_workspace_bytes(int L, int B, int S, int H, int dv, int W, int K);
 
 /*
  * lit_sparse_step -- the whole step for one layer: lit_indexer_scores, lit_topk

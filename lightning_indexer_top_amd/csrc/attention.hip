@@ -22,6 +22,11 @@
 // A query's list is cut into splits (workgroups of 4 waves); the 4 waves of a split
 // merge through LDS, and a second kernel merges splits (log-sum-exp), adds the sink
 // and writes bf16.  With a single split the first kernel writes bf16 itself.
+//
+// Several layers can share one call (DeepSeek-V4.1-Flash-NVFP4 inference/model.py:
+// layers between index sources reuse the source's top-k list and the shared compressed
+// KV, each with its own queries, window KV and sink): the grid then holds every layer's
+// workgroups, those of one query side by side.
 #include "tile_ops.h"
 
 namespace lit {
@@ -44,8 +49,18 @@ __device__ inline const uint16_t *list_row(const AttnArgs &a, int b, int i, int 
     return a.comp_kv + ((size_t)b * a.T_cap + t) * a.D;
 }
 
+// Layer l's view of the arguments (its q, window source, sink and output).
+__device__ inline AttnArgs layer_args(const AttnArgs &a0, int l) {
+    AttnArgs a = a0;
+    a.q += (size_t)l * a.q_ls;
+    if (a.win_kv) a.win_kv += (size_t)l * a.win_ls;
+    if (a.sink) a.sink += (size_t)l * kHeads;
+    a.out += (size_t)l * a.out_ls;
+    return a;
+}
+
 template <int D>
-__global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a, AttnPlan pl) {
+__global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a0, AttnPlan pl) {
     constexpr int LD = D + 4;       // LDS row stride in bf16 (8 bytes of padding)
     __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * 32 * LD];
     __shared__ float wm[kWaves][kHeads], wl[kWaves][kHeads];
@@ -54,7 +69,11 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a, At
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int bs = blockIdx.y;
+    // the layers of one query are neighbours in the grid, so they run together and the
+    // shared rows one of them gathers are cache hits for the others
+    const int layer = blockIdx.y % a0.L;
+    const int bs = blockIdx.y / a0.L;
+    const AttnArgs a = layer_args(a0, layer);
     const int b = bs / a.S;
     const int i = bs % a.S;
     const int split = blockIdx.x;
@@ -97,7 +116,7 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a, At
         if (direct) {
             a.out[((size_t)bs * kHeads + h) * a.dv + d] = attn_finish(O, M, L, a.sink, h);
         } else {
-            float *dst = a.part + (((size_t)bs * pl.n_splits + split) * kHeads + h) * (a.dv + 2);
+            float *dst = a.part + ((((size_t)layer * a.B * a.S + bs) * pl.n_splits + split) * kHeads + h) * (a.dv + 2);
             dst[d] = O;
             if (d == 0) {
                 dst[a.dv] = M;
@@ -113,14 +132,16 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a, At
 // its output dims over the splits with independent loads.
 constexpr int kMaxSplits = 1024;
 
-__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, AttnPlan pl) {
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a0, AttnPlan pl) {
     __shared__ float wgt[kMaxSplits];
-    const int bs = blockIdx.x;
+    const int layer = blockIdx.x % a0.L;
+    const int bs = blockIdx.x / a0.L;
+    const AttnArgs a = layer_args(a0, layer);
     const int h = blockIdx.y;
     const int lane = threadIdx.x;
     const int ns = pl.n_splits;
     const size_t stride = (size_t)kHeads * (a.dv + 2);
-    const float *src = a.part + ((size_t)bs * ns * kHeads + h) * (a.dv + 2);
+    const float *src = a.part + (((size_t)layer * a.B * a.S + bs) * ns * kHeads + h) * (a.dv + 2);
     const float s2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
     float M = s2;
     for (int s = lane; s < ns; s += 64) M = fmaxf(M, src[s * stride + a.dv]);
@@ -165,11 +186,11 @@ __global__ void window_indices_kernel(int B, int S, int start_pos, int W, int R,
 
 template <int D>
 hipError_t launch_d(const AttnArgs &a, const AttnPlan &p, hipStream_t stream) {
-    dim3 grid(p.n_splits, a.B * a.S);
+    dim3 grid(p.n_splits, a.B * a.S * a.L);
     hipLaunchKernelGGL(sparse_attn_kernel<D>, grid, dim3(kWaves * 64), 0, stream, a, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_splits == 1) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.B * a.S, kHeads), dim3(64), 0, stream, a, p);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.B * a.S * a.L, kHeads), dim3(64), 0, stream, a, p);
     return hipGetLastError();
 }
 

@@ -251,6 +251,42 @@ lit_status lit_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv
 
 static bool step_uses_candidates(const lit_step_args *s) { return s->cand_in || s->cand_out; }
 
+size_t lit_sparse_attn_layers_workspace_bytes(int L, int B, int S, int H, int dv, int W, int K) {
+    if (L <= 0 || B <= 0 || S <= 0 || H <= 0 || dv <= 0 || W < 0 || K < 0) return 0;
+    if ((long)L * B * S > kMaxQueries) return 0;
+    const AttnPlan p = plan_attention(L * B, S, W + K);
+    return attention_partial_bytes(L * B, S, H, dv, p);
+}
+
+lit_status lit_sparse_attn_layers(int L, const uint16_t *q, int B, int S, int H, int D, int dv,
+                                  const uint16_t *win_kv, int R, const int32_t *win_idx, int W, int start_pos,
+                                  const uint16_t *comp_kv, int T_cap, const int32_t *comp_idx, int K,
+                                  const float *sink, float scale, uint16_t *out, void *ws, size_t ws_bytes,
+                                  void *stream) {
+    if (L < 1 || start_pos < 0) return LIT_E_SHAPE;
+    // a derived window (win_idx NULL) lists window_width(S, start_pos, W) slots
+    const bool derived = W > 0 && !win_idx;
+    const int nwin = derived ? window_width(S, start_pos, W) : W;
+    lit_status st = check_attn(q, B, S, H, D, dv, win_kv, R, derived ? (const int32_t *)16 : win_idx, nwin,
+                               comp_kv, T_cap, comp_idx, K, out);
+    if (st != LIT_OK) return st;
+    if (derived && R < window_need(S, start_pos, W)) return LIT_E_SHAPE;
+    if ((long)L * B * S > kMaxQueries) return LIT_E_UNSUPPORTED;
+    if (B == 0 || S == 0) return LIT_OK;
+    const AttnPlan p = plan_attention(L * B, S, nwin + K);
+    const size_t need = attention_partial_bytes(L * B, S, H, dv, p);
+    if (need > 0 && (!ws || ws_bytes < need)) return LIT_E_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return LIT_E_ALIGN;
+    AttnArgs a{q, B, S, H, D, dv, W > 0 ? win_kv : nullptr, R, W > 0 ? win_idx : nullptr, W, start_pos,
+               K > 0 ? comp_kv : nullptr, T_cap, K > 0 ? comp_idx : nullptr, K, sink, scale, out,
+               (float *)ws};
+    a.L = L;
+    a.q_ls = (long)B * S * H * D;
+    a.win_ls = (long)B * R * D;
+    a.out_ls = (long)B * S * H * dv;
+    return hip_status(launch_sparse_attn(a, p, (hipStream_t)stream));
+}
+
 // Workspace of the multi-kernel step: scores [B*S, ld] fp32, then the attention partials
 // (level one's block scores share the partials' space: they are used up before).
 static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld, AttnPlan *plan) {

@@ -86,6 +86,11 @@ struct AttnArgs {
     float scale;
     uint16_t *out;            // [B,S,H,dv] bf16
     float *part;              // split partials (workspace), may be NULL when 1 split
+    // Several layers over one row list (cross-layer reuse): layer l reads q, win_kv and
+    // sink at l times their layer strides and writes out (and its partials) likewise;
+    // the lists and comp_kv are shared.
+    int L = 1;
+    long q_ls = 0, win_ls = 0, out_ls = 0;
 };
 // Split plan: how many workgroups share one query's row list.
 struct AttnPlan {
@@ -93,7 +98,7 @@ struct AttnPlan {
     int tiles_per_wave;  // 32-row tiles each wave handles
     int n_splits;        // workgroups per query
 };
-AttnPlan plan_attention(int B, int S, int list_len);
+AttnPlan plan_attention(int B, int S, int list_len);  // B*S: query rows (times layers)
 size_t attention_partial_bytes(int B, int S, int H, int dv, const AttnPlan &p);
 hipError_t launch_sparse_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t stream);
 

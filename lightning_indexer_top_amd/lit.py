@@ -60,6 +60,9 @@ SIGNATURES = {
     "lit_sparse_attn": (_I, [_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _I, _P, _F,
                              _P, _P, _Z, _P]),
     "lit_sparse_attn_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "lit_sparse_attn_layers": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _I, _P, _I, _P, _I,
+                                    _P, _F, _P, _P, _Z, _P]),
+    "lit_sparse_attn_layers_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "lit_sparse_step": (_I, [ctypes.POINTER(lit_step_args), _P, _Z, _P]),
     "lit_sparse_step_workspace_bytes": (_Z, [ctypes.POINTER(lit_step_args)]),
     "lit_sparse_step_state_bytes": (_Z, [ctypes.POINTER(lit_step_args)]),
@@ -235,6 +238,38 @@ def lit_sparse_attn(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float, d
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("lit_sparse_attn", library().lit_sparse_attn(
         _ptr(q), B, S, H, D, dv, _ptr(win_kv), R, _ptr(win_idx), W, _ptr(comp_kv), T_cap,
+        _ptr(comp_idx), K, _ptr(sink), float(scale), _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def lit_sparse_attn_layers(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float, dv=None,
+                           out=None, ws=None, stream=None, window: int = 0,
+                           start_pos: int = 0) -> torch.Tensor:
+    """Attention [L,B,S,H,dv] bf16 for L layers sharing the row lists and comp_kv:
+    q [L,B,S,H,D], win_kv [L,B,R,D] (or None), sink [L,H] (or None).  With win_idx None
+    and ``window`` > 0 the window list is derived from ``start_pos`` in the kernel."""
+    _need(q, torch.bfloat16, "q")
+    L, B, S, H, D = q.shape
+    dv = D if dv is None else dv
+    W = window if win_idx is None else win_idx.shape[-1]
+    K = 0 if comp_idx is None else comp_idx.shape[-1]
+    R = 0 if win_kv is None else win_kv.shape[2]
+    T_cap = 0 if comp_kv is None else comp_kv.shape[1]
+    for t, dt, n in ((win_kv, torch.bfloat16, "win_kv"), (comp_kv, torch.bfloat16, "comp_kv"),
+                     (win_idx, torch.int32, "win_idx"), (comp_idx, torch.int32, "comp_idx"),
+                     (sink, torch.float32, "sink")):
+        if t is not None:
+            _need(t, dt, n)
+    if out is None:
+        out = torch.empty((L, B, S, H, dv), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out")
+    nwin = W if win_idx is not None else lit_window_width(S, start_pos, W)
+    need = library().lit_sparse_attn_layers_workspace_bytes(L, B, S, H, dv, nwin, K)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("lit_sparse_attn_layers", library().lit_sparse_attn_layers(
+        L, _ptr(q), B, S, H, D, dv, _ptr(win_kv), R, _ptr(win_idx), W, start_pos, _ptr(comp_kv), T_cap,
         _ptr(comp_idx), K, _ptr(sink), float(scale), _ptr(out), _ptr(ws), nbytes, _stream(stream)))
     return out
 

@@ -281,6 +281,17 @@ def sparse_attn(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float,
     return out
 
 
+def sparse_attn_layers(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float,
+                       dv: int | None = None) -> np.ndarray:
+    """Several layers over one shared row list (DeepSeek-V4.1-Flash-NVFP4 model.py: layers
+    between index sources reuse the source's top-k and compressed KV): layer l is
+    sparse_attn with its own q[l], win_kv[l] and sink[l].  Returns [L,B,S,H,dv]."""
+    L = q.shape[0]
+    return np.stack([sparse_attn(q[l], None if win_kv is None else win_kv[l], win_idx, comp_kv,
+                                 comp_idx, None if sink is None else sink[l], scale, dv)
+                     for l in range(L)])
+
+
 def step(inp, fp32_scores: bool = True, cand_in=None, cand_topk_blocks: int = 0,
          cand_block_size: int = 0) -> dict:
     """The whole step: index scores -> top-k -> window rows -> attention.

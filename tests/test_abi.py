@@ -143,6 +143,30 @@ def test_attention_refusals(lib):
     assert attn_call(lib, B=0) == 0
 
 
+def test_attention_layers_refusals(lib):
+    f = lib.lit_sparse_attn_layers
+
+    def call(L=3, B=8, S=1, W=128, start_pos=16383, R=128, ws_bytes=1 << 30, win_idx=None, **kw):
+        a = dict(q=A, H=16, D=192, dv=192, win_kv=A, comp_kv=A, T_cap=8192, comp_idx=A, K=2048,
+                 sink=None, out=A, ws=A)
+        a.update(kw)
+        return f(L, a["q"], B, S, a["H"], a["D"], a["dv"], a["win_kv"], R, win_idx, W, start_pos,
+                 a["comp_kv"], a["T_cap"], a["comp_idx"], a["K"], a["sink"], 0.07, a["out"], a["ws"],
+                 ws_bytes, None)
+    assert call(L=0) == 2
+    assert call(L=5000, B=8, S=2, R=129) == 4           # L*B*S > 65535
+    assert call(R=64) == 2                               # derived window needs 128 slots
+    assert call(win_kv=None) == 1
+    assert call(H=32) == 4
+    assert call(start_pos=-1) == 2
+    need = lib.lit_sparse_attn_layers_workspace_bytes(3, 8, 1, 16, 192, 128, 2048)
+    assert need > lib.lit_sparse_attn_workspace_bytes(8, 1, 16, 192, 128, 2048)
+    assert call(ws=None, ws_bytes=0) == 5
+    assert call(ws_bytes=need - 1) == 5
+    assert call(B=0) == 0
+    assert lib.lit_sparse_attn_layers_workspace_bytes(0, 8, 1, 16, 192, 128, 2048) == 0
+
+
 def test_window_refusals(lib):
     assert lib.lit_window_indices(1, 8, 100, 16, 16, A, None) == 2   # needs 23 slots
     assert lib.lit_window_indices(1, 8, 100, 16, 23, None, None) == 1

@@ -538,3 +538,42 @@ def test_step_level_two_short_candidate_list(orc, flags):
     assert np.array_equal(got, ref["idx"]), (got[:, 0, :40], ref["idx"][:, 0, :40])
     err = np.abs(bf16_host(out) - ref["out"]).max()
     assert err <= ATTN_TOL, err
+
+
+# ---------------------------------------------------------------------------------
+# cross-layer reuse: several layers over one shared list and compressed KV
+# ---------------------------------------------------------------------------------
+LAYER_CASES = [
+    # layers, B, S, start_pos, D, dv, W, K, derived window, sink
+    (2, 2, 1, 4095, 128, 128, 128, 64, True, False),
+    (3, 8, 1, 16383, 192, 192, 128, 2048, True, True),   # decode-16k's attention shape
+    (4, 1, 5, 300, 64, 32, 16, 40, False, True),         # explicit lists, dv < D, chunk
+    (1, 2, 1, 1023, 256, 256, 128, 64, True, False),
+]
+
+
+@pytest.mark.parametrize("NL,B,S,start_pos,D,dv,W,K,derived,with_sink", LAYER_CASES)
+def test_sparse_attn_layers(orc, NL, B, S, start_pos, D, dv, W, K, derived, with_sink):
+    rng = np.random.default_rng(4000 + NL * 10 + D)
+    R = max(1, S if start_pos == 0 else W + S - 1)
+    T = (start_pos + S) // 2
+    bits = lambda shape: synth.to_bf16_bits(rng.standard_normal(shape).astype(np.float32))  # noqa: E731
+    q, win_kv, comp_kv = bits((NL, B, S, 16, D)), bits((NL, B, R, D)), bits((B, T, D))
+    comp_idx = np.sort(rng.choice(T, size=(B, S, K), replace=True), axis=-1).astype(np.int32)
+    comp_idx[:, :, -3:] = -1
+    sink = rng.standard_normal((NL, 16)).astype(np.float32) if with_sink else None
+    win_idx = orc.window_indices(B, S, start_pos, W, R)
+    scale = D ** -0.5
+    out = L.lit_sparse_attn_layers(bf16_dev(q), bf16_dev(win_kv), None if derived else dev(win_idx),
+                                    bf16_dev(comp_kv), dev(comp_idx),
+                                    None if sink is None else dev(sink), scale, dv=dv,
+                                    window=W, start_pos=start_pos)
+    torch.cuda.synchronize()
+    got = bf16_host(out)
+    want = orc.sparse_attn_layers(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale, dv)
+    err = np.abs(got - want).max()
+    assert err <= ATTN_TOL, f"max err {err}"
+    # layer l alone through lit_sparse_attn agrees to the same bar
+    one = L.lit_sparse_attn(bf16_dev(q[-1]), bf16_dev(win_kv[-1]), dev(win_idx), bf16_dev(comp_kv),
+                             dev(comp_idx), None if sink is None else dev(sink[-1]), scale, dv=dv)
+    assert np.abs(bf16_host(one) - got[-1]).max() <= ATTN_TOL

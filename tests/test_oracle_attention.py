@@ -143,3 +143,24 @@ def test_refuses_out_of_range_rows(orc):
     bad = np.full((2, 3, 2), 24, np.int32)
     with pytest.raises(orc.OracleError):
         orc.sparse_attn(q, None, None, comp, bad, None, 0.1)
+
+
+def test_layers_are_independent_single_layer_calls(orc):
+    """The multi-layer form is the single-layer attention per layer over the shared lists
+    (cross-layer reuse shares the lists and compressed KV, nothing else)."""
+    rng = np.random.default_rng(8)
+    L, B, S, H, D, R, T = 3, 2, 1, 16, 64, 8, 20
+    bits = lambda shape: synth.to_bf16_bits(rng.standard_normal(shape).astype(np.float32))  # noqa: E731
+    q, win_kv, comp_kv = bits((L, B, S, H, D)), bits((L, B, R, D)), bits((B, T, D))
+    win_idx = np.tile(np.arange(R, dtype=np.int32), (B, S, 1))
+    comp_idx = rng.integers(0, T, size=(B, S, 5)).astype(np.int32)
+    sink = rng.standard_normal((L, H)).astype(np.float32)
+    out = orc.sparse_attn_layers(q, win_kv, win_idx, comp_kv, comp_idx, sink, 0.125)
+    assert out.shape == (L, B, S, H, D)
+    for l in range(L):
+        one = orc.sparse_attn(q[l], win_kv[l], win_idx, comp_kv, comp_idx, sink[l], 0.125)
+        assert np.array_equal(out[l], one)
+    # swapping two layers' inputs swaps their outputs
+    sw = orc.sparse_attn_layers(q[[1, 0, 2]], win_kv[[1, 0, 2]], win_idx, comp_kv, comp_idx,
+                                sink[[1, 0, 2]], 0.125)
+    assert np.array_equal(sw, out[[1, 0, 2]])
