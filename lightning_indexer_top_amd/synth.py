@@ -10,7 +10,9 @@ any rule that yields valid bytes will do, because both sides consume the same by
 
 Recipe (per workload, ``numpy.random.Generator(PCG64(seed))``):
 
-* attention q, window KV, compressed KV ~ N(0, 1), rounded to bf16 (RNE);
+* attention q, window KV, compressed KV ~ N(0, 1), rounded to bf16 (RNE); with
+  ``kv_fmt="quant"`` the window KV is e4m3 with a ue8m0 scale per 32 and the compressed
+  KV fp4 e2m1 with an e4m3 scale per 16 (the smallest e4m3 value >= amax / 6);
 * indexer q and keys ~ N(0, 1), quantised to e4m3 with a ue8m0 scale per 32
   values: scale exponent e = ceil(log2(amax / 448)), codes = RNE(x / 2^e);
   with ``index_fmt="e2m1"`` to fp4 instead: e = ceil(log2(amax / 6)), codes = RNE
@@ -90,6 +92,31 @@ def quantize_e2m1_ue8m0(x: torch.Tensor, block: int = 32):
     return packed, scales
 
 
+def quantize_e2m1_e4m3(x: torch.Tensor, block: int = 16):
+    """fp4 quantiser with e4m3 scales (the compressed-KV format): x [..., D] -> (packed
+    codes uint8 [..., D/2], scales uint8 [..., D/block] e4m3).  The scale is the smallest
+    e4m3 value s with amax / s <= 6 (an all-zero block gets the smallest positive e4m3,
+    code 1); codes round to the nearest e2m1 value, ties to the even code, element 2j in
+    the low nibble of byte j."""
+    assert x.shape[-1] % block == 0 and block % 2 == 0
+    xb = x.float().unflatten(-1, (-1, block))
+    amax = xb.abs().amax(dim=-1)
+    want = torch.where(amax > 0, amax / E2M1_MAX, torch.full_like(amax, 2.0 ** -9))
+    sc = want.clamp(max=E4M3_MAX).to(torch.float8_e4m3fn)
+    # round the scale up where the cast rounded it down
+    low = sc.to(torch.float32) < want
+    codes = sc.view(torch.uint8).to(torch.int32) + low.to(torch.int32)
+    scales = codes.clamp(max=0x7E).to(torch.uint8)
+    s = scales.view(torch.float8_e4m3fn).to(torch.float32)
+    y = (xb / s.unsqueeze(-1)).clamp(-E2M1_MAX, E2M1_MAX)
+    m = y.abs()
+    code = ((m > 0.25).int() + (m >= 0.75).int() + (m > 1.25).int() + (m >= 1.75).int()
+            + (m > 2.5).int() + (m >= 3.5).int() + (m > 5.0).int())
+    code = (code + 8 * (y < 0).int()).flatten(-2)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).to(torch.uint8)
+    return packed, scales
+
+
 def _quant_np(x: np.ndarray, fmt: str = "e4m3"):
     q = quantize_e2m1_ue8m0 if fmt == "e2m1" else quantize_e4m3_ue8m0
     c, s = q(torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)))
@@ -125,6 +152,12 @@ class StepInputs:
     sink: Optional[np.ndarray] = None  # [H] f32 or None
     seed: int = 0
     index_fmt: str = "e4m3"  # code format of q8 / k8: "e4m3" or "e2m1"
+    # quantised attention KV: win_kv "e4m3" -> uint8 [B,R,D] codes + win_sc [B,R,D/32]
+    # ue8m0; comp_kv "e2m1" -> uint8 [B,T_cap,D/2] codes + comp_sc [B,T_cap,D/16] e4m3
+    win_kv_fmt: str = "bf16"
+    comp_kv_fmt: str = "bf16"
+    win_sc: Optional[np.ndarray] = None
+    comp_sc: Optional[np.ndarray] = None
 
     @property
     def end_pos(self) -> int:
@@ -144,7 +177,7 @@ def make_step(*, B: int, S: int, start_pos: int, ratio: int, Hi: int, Di: int, H
               R: Optional[int] = None, T_cap: Optional[int] = None, keys: str = "normal",
               sink: Optional[np.ndarray] = None, scale: Optional[float] = None,
               index_fmt: str = "e4m3", name: str = "custom", cand_topk_blocks: int = 0,
-              cand_block_size: int = 0, layers: int = 1) -> StepInputs:
+              cand_block_size: int = 0, layers: int = 1, kv_fmt: str = "bf16") -> StepInputs:
     """Draw one step's inputs.  R defaults to the smallest window source that holds
     every needed position; T_cap defaults to the visible compressed row count.
     ``cand_topk_blocks`` / ``cand_block_size`` name a level-two workload's candidate
@@ -178,12 +211,23 @@ def make_step(*, B: int, S: int, start_pos: int, ratio: int, Hi: int, Di: int, H
             # x4 = 2^2: codes stay, every block scale of the row rises by 2
             k_sc[b, rows] = np.minimum(k_sc[b, rows].astype(np.int32) + 2, 254).astype(np.uint8)
     q = to_bf16_bits(rng.standard_normal((B, S, H, D), dtype=f32))
-    win_kv = to_bf16_bits(rng.standard_normal((B, R, D), dtype=f32))
-    comp_kv = to_bf16_bits(rng.standard_normal((B, T_cap, D), dtype=f32))
+    win_f = rng.standard_normal((B, R, D), dtype=f32)
+    comp_f = rng.standard_normal((B, T_cap, D), dtype=f32)
+    win_sc = comp_sc = None
+    if kv_fmt == "quant":  # the pages' cache formats: e4m3/ue8m0-32 window, e2m1/e4m3-16 compressed
+        win_kv, win_sc = _quant_np(win_f, "e4m3")
+        c, sc_ = quantize_e2m1_e4m3(torch.from_numpy(comp_f))
+        comp_kv, comp_sc = c.numpy().copy(), sc_.numpy().copy()
+    else:
+        assert kv_fmt == "bf16"
+        win_kv, comp_kv = to_bf16_bits(win_f), to_bf16_bits(comp_f)
     return StepInputs(name=name, B=B, S=S, start_pos=start_pos, ratio=ratio, Hi=Hi, Di=Di,
                       H=H, D=D, dv=dv, W=W, R=R, T_cap=T_cap, index_topk=index_topk,
                       scale=scale, q8=q8, q_sc=q_sc, w=w, k8=k8, k_sc=k_sc, q=q,
-                      win_kv=win_kv, comp_kv=comp_kv, sink=sink, seed=seed, index_fmt=index_fmt)
+                      win_kv=win_kv, comp_kv=comp_kv, sink=sink, seed=seed, index_fmt=index_fmt,
+                      win_kv_fmt="e4m3" if kv_fmt == "quant" else "bf16",
+                      comp_kv_fmt="e2m1" if kv_fmt == "quant" else "bf16",
+                      win_sc=win_sc, comp_sc=comp_sc)
 
 
 # The five workloads of the sparse-attention step.  Decode with "context L" is one query
@@ -220,6 +264,10 @@ WORKLOADS = {
     # over its list in one call
     "decode-16k-3layer": dict(B=8, S=1, start_pos=16383, ratio=2, Hi=64, Di=128, H=16, D=192,
                               W=128, index_topk=2048, seed=20261302, layers=3),
+    # decode-16k with the pages' quantised caches: window KV e4m3 (ue8m0 per 32),
+    # compressed KV fp4 e2m1 (e4m3 scale per 16), dequantised on gather
+    "decode-16k-qkv": dict(B=8, S=1, start_pos=16383, ratio=2, Hi=64, Di=128, H=16, D=192,
+                           W=128, index_topk=2048, seed=20261312, kv_fmt="quant"),
     "decode-128k-fp4": dict(B=2, S=1, start_pos=131071, ratio=4, Hi=64, Di=128, H=16, D=128,
                             W=128, index_topk=2048, seed=20261272, keys="mixture",
                             index_fmt="e2m1"),

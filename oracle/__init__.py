@@ -86,6 +86,9 @@ def _bind(path: str):
     lib.orc_sparse_attn.argtypes = [P, I, I, I, I, I, P, I, P, I, P, I, P, I, P,
                                     ctypes.c_double, P]
     lib.orc_sparse_attn.restype = I
+    lib.orc_sparse_attn_fmt.argtypes = [P, I, I, I, I, I, I, P, P, I, P, I, I, P, P, I, P, I, P,
+                                        ctypes.c_double, P]
+    lib.orc_sparse_attn_fmt.restype = I
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = I
     lib.orc_set_num_threads.argtypes = [I]
@@ -254,30 +257,43 @@ def window_indices(B: int, S: int, start_pos: int, W: int, R: int) -> np.ndarray
     return out
 
 
+# KV row formats: bf16, e4m3 with ue8m0 per 32 (window), fp4 e2m1 with e4m3 per 16
+# (compressed)
+KV_FORMATS = {"bf16": 0, "e4m3": 1, "e2m1": 2}
+
+
 def sparse_attn(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float,
-                dv: int | None = None) -> np.ndarray:
-    """Attention output [B,S,H,dv] float64 from bf16 bit patterns (uint16 arrays)."""
+                dv: int | None = None, win_fmt: str = "bf16", win_sc=None,
+                comp_fmt: str = "bf16", comp_sc=None) -> np.ndarray:
+    """Attention output [B,S,H,dv] float64.  q is bf16 bits; each KV source is bf16 bits
+    (uint16) or, with its format "e4m3" / "e2m1", uint8 codes plus uint8 scales."""
     q = _c(q, np.uint16)
     B, S, H, D = q.shape
     dv = D if dv is None else dv
+
+    def src(kv, sc, fmt):
+        if fmt == "bf16":
+            return _c(kv, np.uint16), None
+        return _c(kv, np.uint8), _c(sc, np.uint8)
     if win_idx is None or win_idx.shape[-1] == 0:
-        W, R, win_kv_c, win_idx_c = 0, 0, None, None
+        W, R, win_kv_c, win_sc_c, win_idx_c = 0, 0, None, None, None
     else:
-        win_kv_c = _c(win_kv, np.uint16)
+        win_kv_c, win_sc_c = src(win_kv, win_sc, win_fmt)
         win_idx_c = _c(win_idx, np.int32)
         W, R = win_idx_c.shape[-1], win_kv_c.shape[1]
     if comp_idx is None or comp_idx.shape[-1] == 0:
-        K, T_cap, comp_kv_c, comp_idx_c = 0, 0, None, None
+        K, T_cap, comp_kv_c, comp_sc_c, comp_idx_c = 0, 0, None, None, None
     else:
-        comp_kv_c = _c(comp_kv, np.uint16)
+        comp_kv_c, comp_sc_c = src(comp_kv, comp_sc, comp_fmt)
         comp_idx_c = _c(comp_idx, np.int32)
         K, T_cap = comp_idx_c.shape[-1], comp_kv_c.shape[1]
     sink_c = None if sink is None else _c(sink, np.float32)
     out = np.empty((B, S, H, dv), dtype=np.float64)
-    rc = _load().orc_sparse_attn(_ptr(q), B, S, H, D, dv, _ptr(win_kv_c), R, _ptr(win_idx_c), W,
-                                 _ptr(comp_kv_c), T_cap, _ptr(comp_idx_c), K, _ptr(sink_c),
-                                 float(scale), _ptr(out))
-    _check(rc, "orc_sparse_attn")
+    rc = _load().orc_sparse_attn_fmt(_ptr(q), B, S, H, D, dv, KV_FORMATS[win_fmt], _ptr(win_kv_c),
+                                     _ptr(win_sc_c), R, _ptr(win_idx_c), W, KV_FORMATS[comp_fmt],
+                                     _ptr(comp_kv_c), _ptr(comp_sc_c), T_cap, _ptr(comp_idx_c), K,
+                                     _ptr(sink_c), float(scale), _ptr(out))
+    _check(rc, "orc_sparse_attn_fmt")
     return out
 
 
@@ -317,7 +333,9 @@ def step(inp, fp32_scores: bool = True, cand_in=None, cand_topk_blocks: int = 0,
         res["masked"] = sel
     idx = topk(sel, inp.start_pos, inp.ratio, inp.index_topk)
     win = window_indices(inp.B, inp.S, inp.start_pos, inp.W, inp.R)
-    o = sparse_attn(inp.q, inp.win_kv, win, inp.comp_kv, idx, inp.sink, inp.scale, inp.dv)
+    o = sparse_attn(inp.q, inp.win_kv, win, inp.comp_kv, idx, inp.sink, inp.scale, inp.dv,
+                    getattr(inp, "win_kv_fmt", "bf16"), getattr(inp, "win_sc", None),
+                    getattr(inp, "comp_kv_fmt", "bf16"), getattr(inp, "comp_sc", None))
     res.update({"idx": idx, "win_idx": win, "out": o})
     return res
 

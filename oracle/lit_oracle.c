@@ -386,39 +386,81 @@ int orc_window_indices(int B, int S, int start_pos, int W, int R,
 /* Two passes over J (max, then sums): the plain definition, not the online  */
 /* recurrence a kernel would use.                                            */
 /*                                                                           */
-/* Layouts: q [B,S,H,D] bf16 bits; win_kv [B,R,D]; win_idx [B,S,W];          */
-/* comp_kv [B,T_cap,D]; comp_idx [B,S,K]; sink [H] float or NULL;            */
-/* out [B,S,H,dv] doubles.  Returns ORC_E_INDEX for an entry out of range.   */
+/* KV rows come in one of three forms, each source with its own:             */
+/*   ORC_KV_BF16: bf16 bits, rows of D;                                      */
+/*   ORC_KV_E4M3: e4m3 codes, rows of D bytes, with one ue8m0 scale per 32   */
+/*     ([V4.1] Attention._window_kv quantises the window KV with act_quant,  */
+/*     fp8 block size 32, ue8m0 scales, over the whole post-RoPE row);       */
+/*   ORC_KV_E2M1: fp4 codes, rows of D/2 bytes (element 2j in the low        */
+/*     nibble of byte j), with one e4m3 scale per 16 ([V4.1]                 */
+/*     Attention._compress_kv quantises the compressed KV with fp4_act_quant */
+/*     in groups of 16 with e4m3 scales).                                    */
+/* A row's values are code * scale, decoded exactly in double.               */
+/*                                                                           */
+/* Layouts: q [B,S,H,D] bf16 bits; win_kv [B,R,*] with win_sc [B,R,*];       */
+/* win_idx [B,S,W]; comp_kv [B,T_cap,*] with comp_sc [B,T_cap,*];            */
+/* comp_idx [B,S,K]; sink [H] float or NULL; out [B,S,H,dv] doubles.         */
+/* Returns ORC_E_INDEX for an entry out of range, ORC_E_ARG for bad sizes.   */
 /* ------------------------------------------------------------------------ */
-int orc_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv,
-                    const uint16_t *win_kv, int R, const int32_t *win_idx,
-                    int W, const uint16_t *comp_kv, int T_cap,
-                    const int32_t *comp_idx, int K, const float *sink,
-                    double scale, double *out) {
+#define ORC_KV_BF16 0
+#define ORC_KV_E4M3 1
+#define ORC_KV_E2M1 2
+
+/* Row `row` of a KV source, decoded into v[0..D). */
+static void orc_kv_row(int fmt, const void *data, const uint8_t *sc, size_t row, int D,
+                       double *v) {
+    if (fmt == ORC_KV_E4M3) {
+        const uint8_t *c = (const uint8_t *)data + row * (size_t)D;
+        const uint8_t *s = sc + row * (size_t)(D / 32);
+        for (int d = 0; d < D; ++d) v[d] = orc_e4m3(c[d]) * orc_e8m0(s[d / 32]);
+    } else if (fmt == ORC_KV_E2M1) {
+        const uint8_t *c = (const uint8_t *)data + row * (size_t)(D / 2);
+        const uint8_t *s = sc + row * (size_t)(D / 16);
+        for (int d = 0; d < D; ++d) {
+            uint8_t nib = (d % 2 == 0) ? (c[d / 2] & 15) : (c[d / 2] >> 4);
+            v[d] = orc_e2m1(nib) * orc_e4m3(s[d / 16]);
+        }
+    } else {
+        const uint16_t *r = (const uint16_t *)data + row * (size_t)D;
+        for (int d = 0; d < D; ++d) v[d] = orc_bf16(r[d]);
+    }
+}
+
+int orc_sparse_attn_fmt(const uint16_t *q, int B, int S, int H, int D, int dv,
+                        int win_fmt, const void *win_kv, const uint8_t *win_sc, int R,
+                        const int32_t *win_idx, int W, int comp_fmt, const void *comp_kv,
+                        const uint8_t *comp_sc, int T_cap, const int32_t *comp_idx, int K,
+                        const float *sink, double scale, double *out) {
     if (B < 0 || S < 0 || H <= 0 || D <= 0 || dv <= 0 || dv > D || W < 0 ||
         K < 0)
         return ORC_E_ARG;
     if ((W > 0 && (win_kv == NULL || win_idx == NULL || R <= 0)) ||
         (K > 0 && (comp_kv == NULL || comp_idx == NULL || T_cap <= 0)))
         return ORC_E_ARG;
+    if (win_fmt < ORC_KV_BF16 || win_fmt > ORC_KV_E2M1 || comp_fmt < ORC_KV_BF16 ||
+        comp_fmt > ORC_KV_E2M1)
+        return ORC_E_ARG;
+    if ((W > 0 && win_fmt != ORC_KV_BF16 && (win_sc == NULL || D % 32 != 0)) ||
+        (K > 0 && comp_fmt != ORC_KV_BF16 && (comp_sc == NULL || D % 32 != 0)))
+        return ORC_E_ARG;
     int bad = 0;
 #pragma omp parallel for collapse(2) schedule(dynamic) reduction(| : bad)
     for (int b = 0; b < B; ++b) {
         for (int i = 0; i < S; ++i) {
             const int n = W + K;
-            const uint16_t **rows = (const uint16_t **)malloc(sizeof(void *) * (size_t)(n > 0 ? n : 1));
+            double *kv = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * (size_t)D);
             int nj = 0;
             for (int j = 0; j < W; ++j) {
                 int32_t s = win_idx[((size_t)b * S + i) * W + j];
                 if (s < 0) continue;
                 if (s >= R) { bad = 1; continue; }
-                rows[nj++] = win_kv + ((size_t)b * R + s) * D;
+                orc_kv_row(win_fmt, win_kv, win_sc, (size_t)b * R + s, D, kv + (size_t)nj++ * D);
             }
             for (int j = 0; j < K; ++j) {
                 int32_t t = comp_idx[((size_t)b * S + i) * K + j];
                 if (t < 0) continue;
                 if (t >= T_cap) { bad = 1; continue; }
-                rows[nj++] = comp_kv + ((size_t)b * T_cap + t) * D;
+                orc_kv_row(comp_fmt, comp_kv, comp_sc, (size_t)b * T_cap + t, D, kv + (size_t)nj++ * D);
             }
             double *l = (double *)malloc(sizeof(double) * (size_t)(nj > 0 ? nj : 1));
             for (int h = 0; h < H; ++h) {
@@ -429,7 +471,7 @@ int orc_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv,
                 double m = -INFINITY;
                 for (int j = 0; j < nj; ++j) {
                     double dot = 0.0;
-                    for (int d = 0; d < D; ++d) dot += orc_bf16(qh[d]) * orc_bf16(rows[j][d]);
+                    for (int d = 0; d < D; ++d) dot += orc_bf16(qh[d]) * kv[(size_t)j * D + d];
                     l[j] = scale * dot;
                     if (l[j] > m) m = l[j];
                 }
@@ -439,14 +481,24 @@ int orc_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv,
                 for (int j = 0; j < nj; ++j) Z += exp(l[j] - m);
                 for (int j = 0; j < nj; ++j) {
                     double p = exp(l[j] - m) / Z;
-                    for (int d = 0; d < dv; ++d) oh[d] += p * orc_bf16(rows[j][d]);
+                    for (int d = 0; d < dv; ++d) oh[d] += p * kv[(size_t)j * D + d];
                 }
             }
             free(l);
-            free(rows);
+            free(kv);
         }
     }
     return bad ? ORC_E_INDEX : 0;
+}
+
+/* The bf16 form of both sources. */
+int orc_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv,
+                    const uint16_t *win_kv, int R, const int32_t *win_idx,
+                    int W, const uint16_t *comp_kv, int T_cap,
+                    const int32_t *comp_idx, int K, const float *sink,
+                    double scale, double *out) {
+    return orc_sparse_attn_fmt(q, B, S, H, D, dv, ORC_KV_BF16, win_kv, NULL, R, win_idx, W,
+                               ORC_KV_BF16, comp_kv, NULL, T_cap, comp_idx, K, sink, scale, out);
 }
 
 /* Threads the OpenMP loops above will use (1 without OpenMP). */

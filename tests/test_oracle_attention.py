@@ -164,3 +164,52 @@ def test_layers_are_independent_single_layer_calls(orc):
     sw = orc.sparse_attn_layers(q[[1, 0, 2]], win_kv[[1, 0, 2]], win_idx, comp_kv, comp_idx,
                                 sink[[1, 0, 2]], 0.125)
     assert np.array_equal(sw, out[[1, 0, 2]])
+
+
+# -- quantised KV sources: DeepSeek-V4.1-Flash-NVFP4 model.py, Attention._window_kv
+# (e4m3, ue8m0 per 32) and Attention._compress_kv (fp4 e2m1, e4m3 scales per 16) ---------
+
+def _lib_rows_e4m3(codes, scales):
+    c = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64)
+    s = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e8m0fnu).to(torch.float64)
+    return (c.unflatten(-1, (-1, 32)) * s.unsqueeze(-1)).flatten(-2).numpy()
+
+
+def _table_rows_e2m1(packed, scales):
+    from tests.test_oracle_formats import E2M1_TABLE
+    p = np.ascontiguousarray(packed)
+    lut = np.array(E2M1_TABLE + [-v for v in E2M1_TABLE])
+    vals = np.stack([lut[p & 15], lut[p >> 4]], axis=-1).reshape(*p.shape[:-1], 2 * p.shape[-1])
+    s = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return (vals.reshape(*vals.shape[:-1], -1, 16) * s[..., None]).reshape(vals.shape)
+
+
+def _exact_bf16_bits(x):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    b = t.to(torch.bfloat16)
+    assert torch.equal(b.to(torch.float64), t), "decoded KV value not exact in bf16"
+    return b.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("D", [64, 192])
+def test_quantised_kv_equals_library_decoded_rows(orc, D):
+    """Rows decoded by torch's fp8 casts (window) and the MX e2m1 table with torch's e4m3
+    cast (compressed) are exact in bf16; the bf16 attention over them is bit-identical to
+    the oracle's quantised-source attention."""
+    inp = synth.make_step(B=2, S=3, start_pos=200, ratio=2, Hi=16, Di=64, H=16, D=D, W=40,
+                          index_topk=30, seed=31 + D, kv_fmt="quant",
+                          sink=np.linspace(-1, 1, 16).astype(np.float32))
+    assert inp.win_kv.shape[-1] == D and inp.comp_kv.shape[-1] == D // 2
+    win = orc.window_indices(inp.B, inp.S, inp.start_pos, inp.W, inp.R)
+    rng = np.random.default_rng(D)
+    idx = rng.integers(-1, inp.T_cap, size=(inp.B, inp.S, 30)).astype(np.int32)
+    got = orc.sparse_attn(inp.q, inp.win_kv, win, inp.comp_kv, idx, inp.sink, inp.scale, D,
+                          "e4m3", inp.win_sc, "e2m1", inp.comp_sc)
+    wb = _exact_bf16_bits(_lib_rows_e4m3(inp.win_kv, inp.win_sc))
+    cb = _exact_bf16_bits(_table_rows_e2m1(inp.comp_kv, inp.comp_sc))
+    want = orc.sparse_attn(inp.q, wb, win, cb, idx, inp.sink, inp.scale, D)
+    assert np.array_equal(got, want)
+    # one source quantised, the other bf16
+    mixed = orc.sparse_attn(inp.q, wb, win, inp.comp_kv, idx, inp.sink, inp.scale, D,
+                            "bf16", None, "e2m1", inp.comp_sc)
+    assert np.array_equal(mixed, want)

@@ -76,6 +76,14 @@ MUTANTS = [
     ("candidate block overlaps the next", "for (int t = j * block_size; t < (j + 1) * block_size && t < T; ++t) {",
      "for (int t = j * block_size; t <= (j + 1) * block_size && t < T; ++t) {",
      [TC.test_hand_ranked_blocks, TC.test_monotone_map_and_block_permutation]),
+    ("KV fp4 scale per 32", "v[d] = orc_e2m1(nib) * orc_e4m3(s[d / 16]);", "v[d] = orc_e2m1(nib) * orc_e4m3(s[d / 32]);",
+     [lambda o: TA.test_quantised_kv_equals_library_decoded_rows(o, 64)]),
+    ("KV fp4 nibbles swapped", "uint8_t nib = (d % 2 == 0) ? (c[d / 2] & 15) : (c[d / 2] >> 4);",
+     "uint8_t nib = (d % 2 == 1) ? (c[d / 2] & 15) : (c[d / 2] >> 4);",
+     [lambda o: TA.test_quantised_kv_equals_library_decoded_rows(o, 64)]),
+    ("KV e4m3 scale dropped", "for (int d = 0; d < D; ++d) v[d] = orc_e4m3(c[d]) * orc_e8m0(s[d / 32]);",
+     "for (int d = 0; d < D; ++d) v[d] = orc_e4m3(c[d]);",
+     [lambda o: TA.test_quantised_kv_equals_library_decoded_rows(o, 64)]),
     ("topk tie rule reversed", "return (x->t > y->t) - (x->t < y->t);",
      "return (x->t < y->t) - (x->t > y->t);", [TT.test_property_checker_with_ties_and_prefill]),
     ("topk ascending sort dropped", "qsort(sel, (size_t)take, sizeof(int), orc_int_cmp);", "",
@@ -87,12 +95,12 @@ MUTANTS = [
      [_window_derived, lambda o: TW.test_brute_force_sets(o, 128, 1, 1023, 128)]),
     ("softmax scale dropped", "l[j] = scale * dot;", "l[j] = dot;",
      [TA.test_all_rows_equals_library_sdpa, TA.test_dense_masked_softmax_two_sources]),
-    ("logit over dv dims only", "for (int d = 0; d < D; ++d) dot += orc_bf16(qh[d]) * orc_bf16(rows[j][d]);",
-     "for (int d = 0; d < dv; ++d) dot += orc_bf16(qh[d]) * orc_bf16(rows[j][d]);",
+    ("logit over dv dims only", "for (int d = 0; d < D; ++d) dot += orc_bf16(qh[d]) * kv[(size_t)j * D + d];",
+     "for (int d = 0; d < dv; ++d) dot += orc_bf16(qh[d]) * kv[(size_t)j * D + d];",
      [TA.test_dense_masked_softmax_two_sources]),
     ("sink left out of normaliser", "double Z = sink ? exp(sk - m) : 0.0;", "double Z = 0.0;",
      [TA.test_sink_closed_forms]),
-    ("window rows dropped", "rows[nj++] = win_kv + ((size_t)b * R + s) * D;", "(void)s;",
+    ("window rows dropped", "orc_kv_row(win_fmt, win_kv, win_sc, (size_t)b * R + s, D, kv + (size_t)nj++ * D);", "(void)s;",
      [TA.test_dense_masked_softmax_two_sources, TA.test_order_permutation_and_duplication_invariance]),
 ]
 

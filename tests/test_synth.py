@@ -57,3 +57,24 @@ def test_fp4_workload_shapes():
     assert inp.q8.shape == (2, 1, 16, 32) and inp.k8.shape == (2, 50, 32)
     assert inp.q_sc.shape == (2, 1, 16, 2) and inp.k_sc.shape == (2, 50, 2)
     assert inp.q8.dtype == np.uint8 and inp.k8.dtype == np.uint8
+
+
+def test_fp4_kv_quantiser_minimal_e4m3_scales():
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(40, 192, generator=g) * 2
+    x[3, :16] = 0.0
+    packed, sc = synth.quantize_e2m1_e4m3(x)
+    assert packed.shape == (40, 96) and sc.shape == (40, 12)
+    s = sc.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    xb = x.double().numpy().reshape(40, 12, 16)
+    amax = np.abs(xb).max(-1)
+    assert np.all(amax / s <= 6.0)
+    # the next smaller e4m3 value would not do (except for the all-zero block)
+    prev = (sc.view(torch.uint8).int() - 1).clamp(min=0).to(torch.uint8)
+    sp = prev.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.all((amax / np.where(sp > 0, sp, 1e-30) > 6.0) | (amax == 0))
+    codes = _unpack(packed).reshape(40, 12, 16)
+    lut = np.array(E2M1_TABLE + [-v for v in E2M1_TABLE])
+    y = xb / s[..., None]
+    best = np.abs(np.abs(y)[..., None] - np.array(E2M1_TABLE)).min(-1)
+    assert np.allclose(np.abs(np.abs(y) - np.abs(lut[codes])), best, atol=1e-9)
