@@ -236,6 +236,33 @@ lit_status lit_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv
 size_t lit_sparse_attn_workspace_bytes(int B, int S, int H, int dv, int W, int K);
 
 /*
+ * KV row formats of the attention sources ([V4.1] Attention._window_kv keeps the
+ * window KV as e4m3 with the module's ue8m0 scales per 32; Attention._compress_kv
+ * stores the compressed KV as fp4 in groups of 16 with e4m3 scales):
+ *   LIT_KV_BF16: bf16 rows of D (the form lit_sparse_attn takes);
+ *   LIT_KV_E4M3: e4m3 codes [*, D] plus ue8m0 scale bytes [*, D/32];
+ *   LIT_KV_E2M1: e2m1 codes [*, D/2] (element 2j in the low nibble of byte j) plus
+ *                e4m3 scale bytes [*, D/16].
+ * A row's values are code * scale; they are dequantised to bf16 (exactly) as they
+ * are gathered.
+ */
+typedef enum { LIT_KV_BF16 = 0, LIT_KV_E4M3 = 1, LIT_KV_E2M1 = 2 } lit_kv_format;
+
+/*
+ * lit_sparse_attn_fmt -- lit_sparse_attn with each source in a lit_kv_format:
+ * the window source bf16 or LIT_KV_E4M3, the compressed source bf16 or
+ * LIT_KV_E2M1 (others: LIT_E_UNSUPPORTED).  win_kv / comp_kv point at the
+ * codes (or bf16 rows), win_scales / comp_scales at the scale bytes (NULL for
+ * bf16).  The workspace is lit_sparse_attn_workspace_bytes().
+ */
+lit_status lit_sparse_attn_fmt(const uint16_t *q, int B, int S, int H, int D, int dv,
+                               int win_format, const void *win_kv, const uint8_t *win_scales,
+                               int R, const int32_t *win_idx, int W, int comp_format,
+                               const void *comp_kv, const uint8_t *comp_scales, int T_cap,
+                               const int32_t *comp_idx, int K, const float *sink, float scale,
+                               uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * lit_sparse_attn_layers -- lit_sparse_attn for L layers that share one row list
  * and one compressed KV: [V4.1] Attention.forward / _compress_topk_idxs, where
  * the layers between index sources reuse the source's top-k list
@@ -339,6 +366,13 @@ typedef struct lit_step_args {
                                kept blocks (kb = lit_candidate_blocks_width) */
     int cand_topk_blocks;
     int cand_block_size;    /* rows per block, for cand_in and cand_out */
+    /* quantised attention KV (lit_kv_format; 0 = bf16): win_kv / comp_kv then hold the
+     * codes (cast to the field's type) and these the scale bytes.  A quantised source
+     * selects the multi-kernel form. */
+    int win_kv_format;
+    const uint8_t *win_kv_scales;
+    int comp_kv_format;
+    const uint8_t *comp_kv_scales;
 } lit_step_args;
 
 lit_status lit_sparse_step(const lit_step_args *args, void *ws, size_t ws_bytes, void *stream);

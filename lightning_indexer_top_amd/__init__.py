@@ -10,4 +10,5 @@ from .lit import (LitError, library, lit_indexer_scores, lit_sparse_attn,  # noq
                   lit_window_indices, lit_window_width, make_step_args, step_workspace,
                   topk_width, LIT_STEP_UNFUSED, attach_state,
                   lit_sparse_step_state_bytes, state_error, lit_candidate_blocks,
-                  lit_topk_candidates, INDEX_FORMATS, lit_sparse_attn_layers)
+                  lit_topk_candidates, INDEX_FORMATS, lit_sparse_attn_layers,
+                  lit_sparse_attn_fmt, KV_FORMATS)

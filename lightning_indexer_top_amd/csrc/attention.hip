@@ -49,18 +49,64 @@ __device__ inline const uint16_t *list_row(const AttnArgs &a, int b, int i, int 
     return a.comp_kv + ((size_t)b * a.T_cap + t) * a.D;
 }
 
+// Row of list entry p as an index into its source ([B*R] window slots or [B*T_cap]
+// compressed rows), or -1; `win` tells which source (padded list: window entries occupy
+// [0, wpad), wpad a multiple of 32).
+__device__ inline long list_row_index(const AttnArgs &a, int b, int i, int nwin, int wpad, const WindowBase &wb,
+                                      int p, bool &win) {
+    const size_t bs = (size_t)b * a.S + i;
+    win = p < wpad;
+    if (win) {
+        if (p >= nwin) return -1;
+        const int slot = a.win_idx ? a.win_idx[bs * a.W + p] : window_slot_at(wb, a.start_pos, a.R, i, p);
+        if (slot < 0 || slot >= a.R) return -1;
+        return (long)b * a.R + slot;
+    }
+    const int t = a.comp_idx[bs * a.K + (p - wpad)];
+    if (t < 0 || t >= a.T_cap) return -1;
+    return (long)b * a.T_cap + t;
+}
+
+// One tile of rows from a quantised list (window tiles and compressed tiles are
+// separate, so the format is uniform over the wave).
+template <int D, int WF, int CF>
+__device__ inline void quant_tile_load(AttnRows<D> &rows, const AttnArgs &a, int b, int i, int nwin, int wpad,
+                                       const WindowBase &wb, int p0, int p1, int end, int g) {
+    bool w0, w1;
+    const long r0 = p0 < end ? list_row_index(a, b, i, nwin, wpad, wb, p0, w0) : -1;
+    const long r1 = p1 < end ? list_row_index(a, b, i, nwin, wpad, wb, p1, w1) : -1;
+    if (p0 - (p0 & 31) < wpad) {  // a window tile
+        if constexpr (WF == kKvBf16)
+            attn_tile_load<D>(rows, r0 >= 0 ? a.win_kv + (size_t)r0 * D : nullptr,
+                              r1 >= 0 ? a.win_kv + (size_t)r1 * D : nullptr, g);
+        else
+            kv_tile_load<D, WF>(rows, a.win_codes, a.win_scales, r0, r1, g);
+    } else {
+        if constexpr (CF == kKvBf16)
+            attn_tile_load<D>(rows, r0 >= 0 ? a.comp_kv + (size_t)r0 * D : nullptr,
+                              r1 >= 0 ? a.comp_kv + (size_t)r1 * D : nullptr, g);
+        else
+            kv_tile_load<D, CF>(rows, a.comp_codes, a.comp_scales, r0, r1, g);
+    }
+}
+
 // Layer l's view of the arguments (its q, window source, sink and output).
 __device__ inline AttnArgs layer_args(const AttnArgs &a0, int l) {
     AttnArgs a = a0;
     a.q += (size_t)l * a.q_ls;
     if (a.win_kv) a.win_kv += (size_t)l * a.win_ls;
+    if (a.win_codes) {  // quantised window: codes and scales per layer
+        a.win_codes += (size_t)l * a.win_ls;
+        a.win_scales += (size_t)l * a.win_ls / (a.win_fmt == kKvE4M3 ? 32 : 16);
+    }
     if (a.sink) a.sink += (size_t)l * kHeads;
     a.out += (size_t)l * a.out_ls;
     return a;
 }
 
-template <int D>
+template <int D, int WF, int CF>
 __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a0, AttnPlan pl) {
+    constexpr bool QUANT = WF != kKvBf16 || CF != kKvBf16;
     constexpr int LD = D + 4;       // LDS row stride in bf16 (8 bytes of padding)
     __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * 32 * LD];
     __shared__ float wm[kWaves][kHeads], wl[kWaves][kHeads];
@@ -79,7 +125,8 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a0, A
     const int split = blockIdx.x;
     const int nwin = a.win_idx ? a.W : (a.W > 0 ? window_width(a.S, a.start_pos, a.W) : 0);
     const WindowBase wb = window_base(a.start_pos, a.W, a.R > 0 ? a.R : 1, i);
-    const int list_len = nwin + a.K;
+    const int list_len = attn_list_len(nwin, a.K, QUANT);
+    const int wpad = list_len - a.K;  // window entries (padded to whole tiles when QUANT)
     const int ndt = a.dv / 16;
     const float sl2 = a.scale * kLog2e;
 
@@ -97,8 +144,11 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a0, A
         if (base >= split_end) break;
         const int p0 = base + c, p1 = base + 16 + c;
         AttnRows<D> rows;
-        attn_tile_load<D>(rows, p0 < split_end ? list_row(a, b, i, nwin, wb, p0) : nullptr,
-                          p1 < split_end ? list_row(a, b, i, nwin, wb, p1) : nullptr, g);
+        if constexpr (QUANT)
+            quant_tile_load<D, WF, CF>(rows, a, b, i, nwin, wpad, wb, p0, p1, split_end, g);
+        else
+            attn_tile_load<D>(rows, p0 < split_end ? list_row(a, b, i, nwin, wb, p0) : nullptr,
+                              p1 < split_end ? list_row(a, b, i, nwin, wb, p1) : nullptr, g);
         attn_tile_compute<D>(st, qb, rows, tile, ndt, sl2, g, c);
     }
     __syncthreads();  // every wave is done with its LDS rows
@@ -184,10 +234,10 @@ __global__ void window_indices_kernel(int B, int S, int start_pos, int W, int R,
     }
 }
 
-template <int D>
+template <int D, int WF, int CF>
 hipError_t launch_d(const AttnArgs &a, const AttnPlan &p, hipStream_t stream) {
     dim3 grid(p.n_splits, a.B * a.S * a.L);
-    hipLaunchKernelGGL(sparse_attn_kernel<D>, grid, dim3(kWaves * 64), 0, stream, a, p);
+    hipLaunchKernelGGL((sparse_attn_kernel<D, WF, CF>), grid, dim3(kWaves * 64), 0, stream, a, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_splits == 1) return e;
     hipLaunchKernelGGL(attn_merge_kernel, dim3(a.B * a.S * a.L, kHeads), dim3(64), 0, stream, a, p);
@@ -219,15 +269,25 @@ size_t attention_partial_bytes(int B, int S, int H, int dv, const AttnPlan &p) {
     return (size_t)B * S * p.n_splits * H * (dv + 2) * sizeof(float);
 }
 
-hipError_t launch_sparse_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t stream) {
-    if (a.B <= 0 || a.S <= 0) return hipSuccess;
+template <int WF, int CF>
+hipError_t launch_fmt(const AttnArgs &a, const AttnPlan &p, hipStream_t stream) {
     switch (a.D) {
-        case 64: return launch_d<64>(a, p, stream);
-        case 128: return launch_d<128>(a, p, stream);
-        case 192: return launch_d<192>(a, p, stream);
-        case 256: return launch_d<256>(a, p, stream);
+        case 64: return launch_d<64, WF, CF>(a, p, stream);
+        case 128: return launch_d<128, WF, CF>(a, p, stream);
+        case 192: return launch_d<192, WF, CF>(a, p, stream);
+        case 256: return launch_d<256, WF, CF>(a, p, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_sparse_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t stream) {
+    if (a.B <= 0 || a.S <= 0) return hipSuccess;
+    const bool qw = a.win_fmt == kKvE4M3, qc = a.comp_fmt == kKvE2M1;
+    if ((a.win_fmt != kKvBf16 && !qw) || (a.comp_fmt != kKvBf16 && !qc)) return hipErrorInvalidValue;
+    if (qw && qc) return launch_fmt<kKvE4M3, kKvE2M1>(a, p, stream);
+    if (qw) return launch_fmt<kKvE4M3, kKvBf16>(a, p, stream);
+    if (qc) return launch_fmt<kKvBf16, kKvE2M1>(a, p, stream);
+    return launch_fmt<kKvBf16, kKvBf16>(a, p, stream);
 }
 
 hipError_t launch_window_indices(int B, int S, int start_pos, int W, int R, int32_t *win_idx,

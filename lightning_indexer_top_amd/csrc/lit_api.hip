@@ -221,10 +221,64 @@ lit_status lit_window_indices(int B, int S, int start_pos, int W, int R, int32_t
     return hip_status(launch_window_indices(B, S, start_pos, W, R, win_idx, (hipStream_t)stream));
 }
 
+// Partial-state bytes for either list form (quantised sources pad the window entries to
+// whole tiles, which can change the split plan).
+static size_t attn_ws_bytes(int B, int S, int H, int dv, int W, int K) {
+    const size_t a = attention_partial_bytes(B, S, H, dv, plan_attention(B, S, attn_list_len(W, K, false)));
+    const size_t b = attention_partial_bytes(B, S, H, dv, plan_attention(B, S, attn_list_len(W, K, true)));
+    return a > b ? a : b;
+}
+
 size_t lit_sparse_attn_workspace_bytes(int B, int S, int H, int dv, int W, int K) {
     if (B <= 0 || S <= 0 || H <= 0 || dv <= 0 || W < 0 || K < 0) return 0;
-    const AttnPlan p = plan_attention(B, S, W + K);
-    return attention_partial_bytes(B, S, H, dv, p);
+    return attn_ws_bytes(B, S, H, dv, W, K);
+}
+
+// Checks of the KV formats and scale pointers; sets the quantised sources of `a`.
+static lit_status set_kv_formats(AttnArgs &a, int win_format, const void *win_kv, const uint8_t *win_scales,
+                                 int comp_format, const void *comp_kv, const uint8_t *comp_scales) {
+    if (win_format != LIT_KV_BF16 && win_format != LIT_KV_E4M3) return LIT_E_UNSUPPORTED;
+    if (comp_format != LIT_KV_BF16 && comp_format != LIT_KV_E2M1) return LIT_E_UNSUPPORTED;
+    if (win_format != LIT_KV_BF16 && a.W > 0) {
+        if (!win_scales) return LIT_E_NULL;
+        a.win_fmt = kKvE4M3;
+        a.win_codes = (const uint8_t *)win_kv;
+        a.win_scales = win_scales;
+        a.win_kv = nullptr;
+    }
+    if (comp_format != LIT_KV_BF16 && a.K > 0) {
+        if (!comp_scales) return LIT_E_NULL;
+        a.comp_fmt = kKvE2M1;
+        a.comp_codes = (const uint8_t *)comp_kv;
+        a.comp_scales = comp_scales;
+        a.comp_kv = nullptr;
+    }
+    return LIT_OK;
+}
+
+lit_status lit_sparse_attn_fmt(const uint16_t *q, int B, int S, int H, int D, int dv, int win_format,
+                               const void *win_kv, const uint8_t *win_scales, int R, const int32_t *win_idx, int W,
+                               int comp_format, const void *comp_kv, const uint8_t *comp_scales, int T_cap,
+                               const int32_t *comp_idx, int K, const float *sink, float scale, uint16_t *out,
+                               void *ws, size_t ws_bytes, void *stream) {
+    lit_status st = check_attn(q, B, S, H, D, dv, (const uint16_t *)win_kv, R, win_idx, W,
+                               (const uint16_t *)comp_kv, T_cap, comp_idx, K, out);
+    if (st != LIT_OK) return st;
+    // An explicit window list of width W (W == 0: no window rows).  The kernel derives
+    // the window itself only when win_idx is NULL with W > 0, which only the steps and
+    // the layered call ask for.
+    AttnArgs a{q, B, S, H, D, dv, W > 0 ? (const uint16_t *)win_kv : nullptr, R, W > 0 ? win_idx : nullptr, W, 0,
+               K > 0 ? (const uint16_t *)comp_kv : nullptr, T_cap, K > 0 ? comp_idx : nullptr, K, sink, scale, out,
+               (float *)ws};
+    if ((st = set_kv_formats(a, win_format, win_kv, win_scales, comp_format, comp_kv, comp_scales)) != LIT_OK)
+        return st;
+    if (B == 0 || S == 0) return LIT_OK;
+    const bool quant = a.win_fmt != kKvBf16 || a.comp_fmt != kKvBf16;
+    const AttnPlan p = plan_attention(B, S, attn_list_len(W, K, quant));
+    const size_t need = attention_partial_bytes(B, S, H, dv, p);
+    if (need > 0 && (!ws || ws_bytes < need)) return LIT_E_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return LIT_E_ALIGN;
+    return hip_status(launch_sparse_attn(a, p, (hipStream_t)stream));
 }
 
 lit_status lit_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv,
@@ -232,30 +286,17 @@ lit_status lit_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv
                            const uint16_t *comp_kv, int T_cap, const int32_t *comp_idx, int K,
                            const float *sink, float scale, uint16_t *out, void *ws, size_t ws_bytes,
                            void *stream) {
-    lit_status st = check_attn(q, B, S, H, D, dv, win_kv, R, win_idx, W, comp_kv, T_cap, comp_idx,
-                               K, out);
-    if (st != LIT_OK) return st;
-    if (B == 0 || S == 0) return LIT_OK;
-    const AttnPlan p = plan_attention(B, S, W + K);
-    const size_t need = attention_partial_bytes(B, S, H, dv, p);
-    if (need > 0 && (!ws || ws_bytes < need)) return LIT_E_WORKSPACE;
-    if (need > 0 && !aligned16(ws)) return LIT_E_ALIGN;
-    // An explicit window list of width W (W == 0: no window rows).  The kernel derives
-    // the window itself only when win_idx is NULL with W > 0, which only the fused
-    // step asks for.
-    AttnArgs a{q, B, S, H, D, dv, W > 0 ? win_kv : nullptr, R, W > 0 ? win_idx : nullptr, W, 0,
-               K > 0 ? comp_kv : nullptr, T_cap, K > 0 ? comp_idx : nullptr, K, sink, scale, out,
-               (float *)ws};
-    return hip_status(launch_sparse_attn(a, p, (hipStream_t)stream));
+    return lit_sparse_attn_fmt(q, B, S, H, D, dv, LIT_KV_BF16, win_kv, nullptr, R, win_idx, W, LIT_KV_BF16,
+                               comp_kv, nullptr, T_cap, comp_idx, K, sink, scale, out, ws, ws_bytes, stream);
 }
 
 static bool step_uses_candidates(const lit_step_args *s) { return s->cand_in || s->cand_out; }
+static bool step_quant_kv(const lit_step_args *s) { return s->win_kv_format != 0 || s->comp_kv_format != 0; }
 
 size_t lit_sparse_attn_layers_workspace_bytes(int L, int B, int S, int H, int dv, int W, int K) {
     if (L <= 0 || B <= 0 || S <= 0 || H <= 0 || dv <= 0 || W < 0 || K < 0) return 0;
     if ((long)L * B * S > kMaxQueries) return 0;
-    const AttnPlan p = plan_attention(L * B, S, W + K);
-    return attention_partial_bytes(L * B, S, H, dv, p);
+    return attn_ws_bytes(L * B, S, H, dv, W, K);
 }
 
 lit_status lit_sparse_attn_layers(int L, const uint16_t *q, int B, int S, int H, int D, int dv,
@@ -295,7 +336,7 @@ static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld
     *scores_bytes = round_up((size_t)s->B * s->S * (*ld) * sizeof(float), 256);
     const int nwin = window_width(s->S, s->start_pos, s->W);
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
-    *plan = plan_attention(s->B, s->S, nwin + keff);
+    *plan = plan_attention(s->B, s->S, attn_list_len(nwin, keff, step_quant_kv(s)));
     size_t rest = round_up(attention_partial_bytes(s->B, s->S, s->H, s->dv, *plan), 256);
     if (s->cand_out) {
         const size_t bb = lit_candidate_blocks_workspace_bytes(s->B, s->S, s->start_pos, s->ratio,
@@ -313,7 +354,7 @@ static FusedPlan step_fused_plan(const lit_step_args *s) {
     FusedPlan p{};
     p.ok = false;
     if (s->flags & LIT_STEP_UNFUSED) return p;
-    if (s->cand_out) return p;
+    if (s->cand_out || step_quant_kv(s)) return p;
     const bool masked = s->cand_in != nullptr;
     if (masked && (s->cand_k < 1 || s->cand_k > kFusedCandMaxApi)) return p;
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
@@ -339,6 +380,14 @@ static lit_status check_step(const lit_step_args *s) {
                     (const int32_t *)16, keff, s->out);
     if (st != LIT_OK) return st;
     if (s->B > 0 && s->S > 0 && keff > 0 && !s->topk_idx) return LIT_E_NULL;
+    if (step_quant_kv(s)) {
+        if ((s->win_kv_format != LIT_KV_BF16 && s->win_kv_format != LIT_KV_E4M3) ||
+            (s->comp_kv_format != LIT_KV_BF16 && s->comp_kv_format != LIT_KV_E2M1))
+            return LIT_E_UNSUPPORTED;
+        if (s->B > 0 && s->S > 0 && ((s->win_kv_format && s->W > 0 && !s->win_kv_scales) ||
+                                     (s->comp_kv_format && keff > 0 && !s->comp_kv_scales)))
+            return LIT_E_NULL;
+    }
     if (step_uses_candidates(s)) {
         if (s->cand_block_size < 1 || s->cand_k < 0 || s->cand_topk_blocks < 0) return LIT_E_SHAPE;
         if (s->cand_in && (T + s->cand_block_size - 1) / s->cand_block_size > kCandMaxBlocks)
@@ -444,6 +493,13 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
                 nullptr, s->W, s->start_pos, keff > 0 ? s->comp_kv : nullptr, s->T_cap,
                 keff > 0 ? s->topk_idx : nullptr, keff, s->sink, s->scale, s->out,
                 (float *)rest};
+    if (step_quant_kv(s)) {
+        // the derived window keeps W as its size; the checks ran in check_step
+        aa.K = keff;
+        if (set_kv_formats(aa, s->win_kv_format, s->win_kv, s->win_kv_scales, s->comp_kv_format, s->comp_kv,
+                           s->comp_kv_scales) != LIT_OK)
+            return LIT_E_UNSUPPORTED;
+    }
     if ((e = launch_sparse_attn(aa, plan, hs)) != hipSuccess) return hip_status(e);
     return hip_status(mark(3));
 }

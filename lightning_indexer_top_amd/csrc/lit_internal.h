@@ -70,6 +70,10 @@ constexpr int kCandMaxBlocks = 65536;
 // ---------------------------------------------------------------------------
 // Sparse attention (attention.hip) and window lists
 // ---------------------------------------------------------------------------
+// KV row formats of the attention sources (dequantised on gather, tile_ops.h).
+constexpr int kKvBf16 = 0;
+constexpr int kKvE4M3 = 1;  // e4m3 codes, ue8m0 scale per 32
+constexpr int kKvE2M1 = 2;  // e2m1 codes (two a byte), e4m3 scale per 16
 struct AttnArgs {
     const uint16_t *q;        // [B,S,H,D] bf16
     int B, S, H, D, dv;
@@ -91,7 +95,18 @@ struct AttnArgs {
     // the lists and comp_kv are shared.
     int L = 1;
     long q_ls = 0, win_ls = 0, out_ls = 0;
+    // Quantised sources (kKvE4M3 window, kKvE2M1 compressed; tile_ops.h): codes and scale
+    // bytes replace win_kv / comp_kv.  The window entries then fill whole 32-row tiles
+    // (the list is padded to a tile boundary) so no tile mixes the two formats.
+    int win_fmt = 0, comp_fmt = 0;
+    const uint8_t *win_codes = nullptr, *win_scales = nullptr;
+    const uint8_t *comp_codes = nullptr, *comp_scales = nullptr;
 };
+// Entries of the list the attention kernel walks: window entries, padded to whole tiles
+// when a source is quantised, then the compressed entries.
+__host__ __device__ inline int attn_list_len(int nwin, int K, bool quant) {
+    return (quant ? (nwin + 31) / 32 * 32 : nwin) + K;
+}
 // Split plan: how many workgroups share one query's row list.
 struct AttnPlan {
     int list_len;        // window width + K

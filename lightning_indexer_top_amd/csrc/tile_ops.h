@@ -209,6 +209,72 @@ __device__ inline void attn_tile_load_rows(AttnRows<D> &t, const uint16_t *rp0, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Quantised KV rows, dequantised on gather into the bf16 operand layout above (lane
+// (g, c) holds dims 32s+8g..32s+8g+7 of its row for each s).
+//   kKvE4M3: D e4m3 bytes a row, one ue8m0 scale byte per 32 dims.  A lane reads 8 code
+//            bytes and the scale of block s per piece; V_CVT_SCALEF32_PK_BF16_FP8 applies
+//            the scale (the instruction uses only the exponent of its f32 scale, which a
+//            power of two is exactly; measured on gfx950).
+//   kKvE2M1: D/2 bytes a row (two e2m1 codes a byte, element 2j low), one e4m3 scale byte
+//            per 16 dims.  A lane reads 4 code bytes and the scale of group 2s + g/2.  The
+//            e4m3 scale is no power of two, so the codes become f32 pairs, are multiplied
+//            by the decoded scale, and the products -- exact in bf16: at most 6
+//            significant bits, magnitudes within 2^-10 .. 2688 -- are truncated to bf16.
+// Indexing a 2-element result of these conversion builtins gave the first element twice
+// in this compiler; the results are therefore bit-cast whole.
+// ---------------------------------------------------------------------------
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline float ue8m0_f32(uint32_t sb) {
+    // 2^(sb-127); sb = 0 is the subnormal 2^-127
+    return __uint_as_float(sb ? sb << 23 : 0x00400000u);
+}
+
+// 8 dims of row `row` (dims 32s+8g..) of a quantised source, as 4 packed bf16 pairs.
+template <int D, int KF>
+__device__ inline u32x4 kv_piece(const uint8_t *codes, const uint8_t *scales, size_t row, int s, int g) {
+    u32x4 out;
+    if constexpr (KF == kKvE4M3) {
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(codes + row * D + 32 * s + 8 * g);
+        const float sf = ue8m0_f32(scales[row * (D / 32) + s]);
+        out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sf, false));
+        out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sf, true));
+        out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sf, false));
+        out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sf, true));
+    } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(codes + row * (D / 2) + 16 * s + 4 * g);
+        const uint32_t sb = scales[row * (D / 16) + 2 * s + (g >> 1)];
+        const uint64_t sp = __builtin_bit_cast(uint64_t, __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.f, false));
+        const float sf = __uint_as_float((uint32_t)sp);
+        uint64_t pr[4];  // byte k's two codes as f32
+        pr[0] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 0));
+        pr[1] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 1));
+        pr[2] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 2));
+        pr[3] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 3));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = __float_as_uint(__uint_as_float((uint32_t)pr[k]) * sf);
+            const uint32_t hi = __float_as_uint(__uint_as_float((uint32_t)(pr[k] >> 32)) * sf);
+            out[k] = (lo >> 16) | (hi & 0xFFFF0000u);
+        }
+    }
+    return out;
+}
+
+// One tile's rows from a quantised source (row0 / row1 < 0: not part of the tile).
+template <int D, int KF>
+__device__ inline void kv_tile_load(AttnRows<D> &t, const uint8_t *codes, const uint8_t *scales, long row0,
+                                    long row1, int g) {
+    t.valid[0] = __ballot(row0 >= 0);
+    t.valid[1] = __ballot(row1 >= 0);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+        t.r[0][s] = row0 >= 0 ? kv_piece<D, KF>(codes, scales, (size_t)row0, s, g) : u32x4{0u, 0u, 0u, 0u};
+        t.r[1][s] = row1 >= 0 ? kv_piece<D, KF>(codes, scales, (size_t)row1, s, g) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
 // One 32-row tile: logits, online softmax, P.V.  `tile` is this wave's LDS region of
 // 32 rows x (D+4) bf16.  ndt = dv/16 output tiles are accumulated.
 template <int D>

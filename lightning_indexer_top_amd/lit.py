@@ -36,12 +36,15 @@ class lit_step_args(ctypes.Structure):
                 ("topk_idx", _P), ("out", _P), ("stage_events", _P * 4), ("state", _P), ("state_bytes", _Z),
                 ("flags", _I), ("index_format", _I),
                 ("cand_in", _P), ("cand_k", _I), ("cand_out", _P), ("cand_topk_blocks", _I),
-                ("cand_block_size", _I)]
+                ("cand_block_size", _I), ("win_kv_format", _I), ("win_kv_scales", _P),
+                ("comp_kv_format", _I), ("comp_kv_scales", _P)]
 
 
 LIT_STEP_UNFUSED = 1
 # lit_index_format: the code format of the index queries and keys
 INDEX_FORMATS = {"e4m3": 0, "e2m1": 1}
+# lit_kv_format: the attention KV sources (window: bf16 or e4m3; compressed: bf16 or e2m1)
+KV_FORMATS = {"bf16": 0, "e4m3": 1, "e2m1": 2}
 
 
 SIGNATURES = {
@@ -60,6 +63,8 @@ SIGNATURES = {
     "lit_sparse_attn": (_I, [_P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _I, _P, _F,
                              _P, _P, _Z, _P]),
     "lit_sparse_attn_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "lit_sparse_attn_fmt": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _I, _I, _P, _P, _I, _P,
+                                 _I, _P, _F, _P, _P, _Z, _P]),
     "lit_sparse_attn_layers": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _I, _P, _I, _P, _I,
                                     _P, _F, _P, _P, _Z, _P]),
     "lit_sparse_attn_layers_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
@@ -242,6 +247,40 @@ def lit_sparse_attn(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float, d
     return out
 
 
+def lit_sparse_attn_fmt(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float, dv=None,
+                        win_fmt: str = "bf16", win_sc=None, comp_fmt: str = "bf16", comp_sc=None,
+                        out=None, ws=None, stream=None) -> torch.Tensor:
+    """lit_sparse_attn with quantised sources: win_kv e4m3 codes uint8 [B,R,D] + win_sc
+    [B,R,D/32], comp_kv e2m1 codes uint8 [B,T_cap,D/2] + comp_sc [B,T_cap,D/16] (or bf16)."""
+    _need(q, torch.bfloat16, "q")
+    B, S, H, D = q.shape
+    dv = D if dv is None else dv
+    W = 0 if win_idx is None else win_idx.shape[-1]
+    K = 0 if comp_idx is None else comp_idx.shape[-1]
+    R = 0 if win_kv is None else win_kv.shape[1]
+    T_cap = 0 if comp_kv is None else comp_kv.shape[1]
+    for t, fmt, n in ((win_kv, win_fmt, "win_kv"), (comp_kv, comp_fmt, "comp_kv")):
+        if t is not None:
+            _need(t, torch.bfloat16 if fmt == "bf16" else torch.uint8, n)
+    for t, dt, n in ((win_sc, torch.uint8, "win_sc"), (comp_sc, torch.uint8, "comp_sc"),
+                     (win_idx, torch.int32, "win_idx"), (comp_idx, torch.int32, "comp_idx"),
+                     (sink, torch.float32, "sink")):
+        if t is not None:
+            _need(t, dt, n)
+    if out is None:
+        out = torch.empty((B, S, H, dv), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out")
+    need = lit_sparse_attn_workspace_bytes(B, S, H, dv, W, K)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("lit_sparse_attn_fmt", library().lit_sparse_attn_fmt(
+        _ptr(q), B, S, H, D, dv, KV_FORMATS[win_fmt], _ptr(win_kv), _ptr(win_sc), R, _ptr(win_idx), W,
+        KV_FORMATS[comp_fmt], _ptr(comp_kv), _ptr(comp_sc), T_cap, _ptr(comp_idx), K, _ptr(sink),
+        float(scale), _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
 def lit_sparse_attn_layers(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: float, dv=None,
                            out=None, ws=None, stream=None, window: int = 0,
                            start_pos: int = 0) -> torch.Tensor:
@@ -278,11 +317,14 @@ def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int,
                    index_topk: int, W: int, scale: float, dv=None, sink=None, topk_idx=None,
                    out=None, stage_events=None, flags: int = 0, fmt: str = "e4m3",
                    cand_in=None, cand_out=None, cand_topk_blocks: int = 0,
-                   cand_block_size: int = 0) -> tuple:
+                   cand_block_size: int = 0, win_fmt: str = "bf16", win_sc=None,
+                   comp_fmt: str = "bf16", comp_sc=None) -> tuple:
     """Build the lit_step_args struct (and allocate outputs the caller did not pass).
     ``fmt`` is the index-code format ("e4m3" or "e2m1"); Di comes from q_sc.  For the
     two-level top-k, ``cand_in`` [B,S,cand_k] int32 makes this a level-two layer and
-    ``cand_out`` [B,S,kb] int32 the candidate source (blocks of ``cand_block_size``)."""
+    ``cand_out`` [B,S,kb] int32 the candidate source (blocks of ``cand_block_size``).
+    Quantised attention KV: ``win_fmt="e4m3"`` (win_kv uint8 codes, win_sc scales) and
+    ``comp_fmt="e2m1"`` (comp_kv uint8 codes, comp_sc scales)."""
     B, S, Hi, _ = q8.shape
     Di = 32 * q_sc.shape[-1]
     H, D = q.shape[2], q.shape[3]
@@ -303,7 +345,11 @@ def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int,
                       cand_in=0 if cand_in is None else cand_in.data_ptr(),
                       cand_k=0 if cand_in is None else cand_in.shape[-1],
                       cand_out=0 if cand_out is None else cand_out.data_ptr(),
-                      cand_topk_blocks=cand_topk_blocks, cand_block_size=cand_block_size)
+                      cand_topk_blocks=cand_topk_blocks, cand_block_size=cand_block_size,
+                      win_kv_format=KV_FORMATS[win_fmt],
+                      win_kv_scales=0 if win_sc is None else win_sc.data_ptr(),
+                      comp_kv_format=KV_FORMATS[comp_fmt],
+                      comp_kv_scales=0 if comp_sc is None else comp_sc.data_ptr())
     for t, n in ((cand_in, "cand_in"), (cand_out, "cand_out")):
         if t is not None:
             _need(t, torch.int32, n)

@@ -19,10 +19,15 @@ def bf16_host(t: torch.Tensor) -> np.ndarray:
 
 
 def step_inputs_dev(inp):
-    """Device copies of every array of a synth.StepInputs."""
+    """Device copies of every array of a synth.StepInputs (quantised KV sources stay
+    uint8 codes, with their scale bytes as win_sc / comp_sc)."""
+    wq = getattr(inp, "win_kv_fmt", "bf16") != "bf16"
+    cq = getattr(inp, "comp_kv_fmt", "bf16") != "bf16"
     return dict(q8=dev(inp.q8), q_sc=dev(inp.q_sc), w=dev(inp.w), k8=dev(inp.k8),
-                k_sc=dev(inp.k_sc), q=bf16_dev(inp.q), win_kv=bf16_dev(inp.win_kv),
-                comp_kv=bf16_dev(inp.comp_kv),
+                k_sc=dev(inp.k_sc), q=bf16_dev(inp.q),
+                win_kv=dev(inp.win_kv) if wq else bf16_dev(inp.win_kv),
+                comp_kv=dev(inp.comp_kv) if cq else bf16_dev(inp.comp_kv),
+                win_sc=dev(inp.win_sc) if wq else None, comp_sc=dev(inp.comp_sc) if cq else None,
                 sink=None if inp.sink is None else dev(inp.sink))
 
 

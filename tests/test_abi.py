@@ -167,6 +167,21 @@ def test_attention_layers_refusals(lib):
     assert lib.lit_sparse_attn_layers_workspace_bytes(0, 8, 1, 16, 192, 128, 2048) == 0
 
 
+def test_quantised_kv_refusals(lib):
+    f = lib.lit_sparse_attn_fmt
+
+    def call(wf=1, cf=2, wsc=A, csc=A, **kw):
+        a = dict(q=A, B=1, S=1, H=16, D=128, dv=128, win_kv=A, R=128, win_idx=A, W=128, comp_kv=A,
+                 T_cap=512, comp_idx=A, K=64, ws=A, ws_bytes=1 << 30)
+        a.update(kw)
+        return f(a["q"], a["B"], a["S"], a["H"], a["D"], a["dv"], wf, a["win_kv"], wsc, a["R"],
+                 a["win_idx"], a["W"], cf, a["comp_kv"], csc, a["T_cap"], a["comp_idx"], a["K"], None,
+                 0.1, A, a["ws"], a["ws_bytes"], None)
+    assert call(wf=2) == 4 and call(cf=1) == 4 and call(wf=7) == 4   # formats per source
+    assert call(wsc=None) == 1 and call(csc=None) == 1
+    assert call(B=0) == 0
+
+
 def test_window_refusals(lib):
     assert lib.lit_window_indices(1, 8, 100, 16, 16, A, None) == 2   # needs 23 slots
     assert lib.lit_window_indices(1, 8, 100, 16, 23, None, None) == 1

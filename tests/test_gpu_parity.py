@@ -205,7 +205,8 @@ def _run_step(d, inp, flags=0, state=None):
                                       comp_kv=d["comp_kv"], start_pos=inp.start_pos,
                                       ratio=inp.ratio, index_topk=inp.index_topk, W=inp.W,
                                       scale=inp.scale, dv=inp.dv, sink=d["sink"], flags=flags,
-                                      fmt=inp.index_fmt)
+                                      fmt=inp.index_fmt, win_fmt=inp.win_kv_fmt, win_sc=d["win_sc"],
+                                      comp_fmt=inp.comp_kv_fmt, comp_sc=d["comp_sc"])
     state = L.attach_state(args, state)
     ws = L.step_workspace(args)
     L.lit_sparse_step(args, ws)
@@ -244,7 +245,9 @@ def _one_query(inp, b, i):
     sub = dataclasses.replace(
         inp, B=1, S=1, start_pos=P, q8=inp.q8[b:b + 1, i:i + 1], q_sc=inp.q_sc[b:b + 1, i:i + 1],
         w=inp.w[b:b + 1, i:i + 1], q=inp.q[b:b + 1, i:i + 1], k8=inp.k8[b:b + 1],
-        k_sc=inp.k_sc[b:b + 1], win_kv=inp.win_kv[b:b + 1], comp_kv=inp.comp_kv[b:b + 1])
+        k_sc=inp.k_sc[b:b + 1], win_kv=inp.win_kv[b:b + 1], comp_kv=inp.comp_kv[b:b + 1],
+        win_sc=None if inp.win_sc is None else inp.win_sc[b:b + 1],
+        comp_sc=None if inp.comp_sc is None else inp.comp_sc[b:b + 1])
     return sub
 
 
@@ -282,7 +285,8 @@ def test_step_small_fp4(orc, cfg, flags):
 
 @pytest.mark.parametrize("flags", MODES)
 @pytest.mark.parametrize("name", ["decode-1k", "decode-4k-r2", "decode-4k-r1", "decode-16k",
-                                  "decode-128k", "decode-16k-fp4", "decode-128k-fp4"])
+                                  "decode-128k", "decode-16k-fp4", "decode-128k-fp4",
+                                  "decode-16k-qkv"])
 def test_step_workloads(orc, name, flags):
     inp = synth.workload(name)
     idx, out = _run_step(step_inputs_dev(inp), inp, flags)
@@ -577,3 +581,43 @@ def test_sparse_attn_layers(orc, NL, B, S, start_pos, D, dv, W, K, derived, with
     one = L.lit_sparse_attn(bf16_dev(q[-1]), bf16_dev(win_kv[-1]), dev(win_idx), bf16_dev(comp_kv),
                              dev(comp_idx), None if sink is None else dev(sink[-1]), scale, dv=dv)
     assert np.abs(bf16_host(one) - got[-1]).max() <= ATTN_TOL
+
+
+
+# ---------------------------------------------------------------------------------
+# quantised attention KV (window e4m3 / ue8m0-32, compressed e2m1 / e4m3-16)
+# ---------------------------------------------------------------------------------
+QKV_CASES = [
+    # B, S, start_pos, D, dv, W, K, window format, compressed format
+    (2, 1, 16383, 192, 192, 128, 2048, "e4m3", "e2m1"),
+    (1, 70, 0, 128, 128, 128, 30, "e4m3", "e2m1"),      # 70 window rows: padded tiles
+    (2, 3, 500, 64, 32, 40, 50, "e4m3", "bf16"),
+    (2, 1, 4095, 256, 256, 128, 64, "bf16", "e2m1"),
+]
+
+
+@pytest.mark.parametrize("B,S,start_pos,D,dv,W,K,wf,cf", QKV_CASES)
+def test_sparse_attn_quantised_kv(orc, B, S, start_pos, D, dv, W, K, wf, cf):
+    inp = synth.make_step(B=B, S=S, start_pos=start_pos, ratio=2, Hi=16, Di=64, H=16, D=D, dv=dv,
+                          W=W, index_topk=K, seed=6000 + D + S, kv_fmt="quant",
+                          sink=np.linspace(-3, 1, 16).astype(np.float32))
+    rng = np.random.default_rng(D + S)
+    win = orc.window_indices(B, S, start_pos, W, inp.R)
+    idx = rng.integers(-1, inp.T_cap, size=(B, S, K)).astype(np.int32)
+    wkv, wsc = (inp.win_kv, inp.win_sc)
+    ckv, csc = (inp.comp_kv, inp.comp_sc)
+    if wf == "bf16":  # the same rows, decoded, as bf16
+        from tests.test_oracle_attention import _exact_bf16_bits, _lib_rows_e4m3
+        wkv, wsc = _exact_bf16_bits(_lib_rows_e4m3(inp.win_kv, inp.win_sc)), None
+    if cf == "bf16":
+        from tests.test_oracle_attention import _exact_bf16_bits, _table_rows_e2m1
+        ckv, csc = _exact_bf16_bits(_table_rows_e2m1(inp.comp_kv, inp.comp_sc)), None
+    to = lambda a, f: bf16_dev(a) if f == "bf16" else dev(a)  # noqa: E731
+    got = L.lit_sparse_attn_fmt(bf16_dev(inp.q), to(wkv, wf), dev(win), to(ckv, cf), dev(idx),
+                                dev(inp.sink), inp.scale, dv=dv, win_fmt=wf,
+                                win_sc=None if wsc is None else dev(wsc), comp_fmt=cf,
+                                comp_sc=None if csc is None else dev(csc))
+    torch.cuda.synchronize()
+    want = orc.sparse_attn(inp.q, wkv, win, ckv, idx, inp.sink, inp.scale, dv, wf, wsc, cf, csc)
+    err = np.abs(bf16_host(got) - want).max()
+    assert err <= ATTN_TOL, f"max err {err}"
