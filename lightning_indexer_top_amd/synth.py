@@ -280,6 +280,44 @@ def workload(name: str, **overrides) -> StepInputs:
     return make_step(name=name, **kw)
 
 
+def rope_table(rd: int, positions: int, base: float) -> np.ndarray:
+    """Rotary table [positions, rd/2, 2] float32 (cos, sin): the frequencies
+    1 / base^(2j/rd) times the position, in float32 as DeepSeek-V4.1-Flash-NVFP4
+    model.py's precompute_freqs_cis tabulates them without YaRN (original_seq_len 0)."""
+    freqs = 1.0 / (base ** (torch.arange(0, rd, 2, dtype=torch.float32) / rd))
+    ang = torch.outer(torch.arange(positions, dtype=torch.float32), freqs)
+    return torch.stack([torch.cos(ang), torch.sin(ang)], dim=-1).numpy().astype(np.float32)
+
+
+@dataclasses.dataclass
+class AppendInputs:
+    """One decode step's producer inputs: the new token's compressor kv / gate score
+    (fp32, after the projections) and window KV row (bf16 bits, after kv_norm), the
+    RMSNorm weight, and the rotary table."""
+    B: int
+    D: int
+    rd: int
+    ratio: int
+    kv: np.ndarray        # [steps, B, D] f32
+    score: np.ndarray     # [steps, B, D] f32
+    win: np.ndarray       # [steps, B, D] bf16 bits
+    norm_w: np.ndarray    # [D] f32
+    freqs: np.ndarray     # [positions, rd/2, 2] f32
+    eps: float = 1e-20
+
+
+def make_append(*, B: int, D: int, rd: int, ratio: int, steps: int, positions: int, seed: int,
+                base: float = 40000.0) -> AppendInputs:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f32 = np.float32
+    return AppendInputs(B=B, D=D, rd=rd, ratio=ratio,
+                        kv=rng.standard_normal((steps, B, D), dtype=f32),
+                        score=rng.standard_normal((steps, B, D), dtype=f32),
+                        win=to_bf16_bits(rng.standard_normal((steps, B, D), dtype=f32)),
+                        norm_w=(0.5 + rng.random(D, dtype=f32)).astype(f32),
+                        freqs=rope_table(rd, positions, base))
+
+
 def random_scores(B: int, S: int, T: int, seed: int, ties: bool = False) -> np.ndarray:
     """fp32 score rows for testing a selector alone; with ``ties`` the values come from
     a small set so that many rows share a score."""
@@ -318,7 +356,16 @@ def draw_step_device(spec: dict, seed: int, device="cuda") -> dict:
             rows = torch.randperm(T_cap, device=device, generator=g)[:n_boost]
             k_sc[b, rows] = (k_sc[b, rows].int() + 2).clamp(max=254).to(torch.uint8)
     bf = torch.bfloat16
+    q = torch.randn(B, S, H, D, **f32).to(bf)
+    win_f, comp_f = torch.randn(B, R, D, **f32), torch.randn(B, T_cap, D, **f32)
+    win_sc = comp_sc = None
+    if spec.get("kv_fmt", "bf16") == "quant":
+        win_kv, win_sc = quantize_e4m3_ue8m0(win_f)
+        comp_kv, comp_sc = quantize_e2m1_e4m3(comp_f)
+        win_kv, win_sc = win_kv.contiguous(), win_sc.contiguous()
+        comp_kv, comp_sc = comp_kv.contiguous(), comp_sc.contiguous()
+    else:
+        win_kv, comp_kv = win_f.to(bf), comp_f.to(bf)
     return dict(q8=q8.contiguous(), q_sc=q_sc.contiguous(), w=w, k8=k8.contiguous(),
-                k_sc=k_sc.contiguous(), q=torch.randn(B, S, H, D, **f32).to(bf),
-                win_kv=torch.randn(B, R, D, **f32).to(bf),
-                comp_kv=torch.randn(B, T_cap, D, **f32).to(bf), R=R, T_cap=T_cap)
+                k_sc=k_sc.contiguous(), q=q, win_kv=win_kv, comp_kv=comp_kv, win_sc=win_sc,
+                comp_sc=comp_sc, R=R, T_cap=T_cap)

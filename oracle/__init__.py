@@ -89,6 +89,18 @@ def _bind(path: str):
     lib.orc_sparse_attn_fmt.argtypes = [P, I, I, I, I, I, I, P, P, I, P, I, I, P, P, I, P, I, P,
                                         ctypes.c_double, P]
     lib.orc_sparse_attn_fmt.restype = I
+    lib.orc_round_bf16.argtypes = [ctypes.c_double]
+    lib.orc_round_bf16.restype = ctypes.c_double
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    lib.orc_quant_e4m3.argtypes = [P, I, P, P]
+    lib.orc_quant_e4m3.restype = None
+    lib.orc_quant_e2m1.argtypes = [P, I, P, P]
+    lib.orc_quant_e2m1.restype = None
+    lib.orc_compress_append.argtypes = [I, I, I, I, P, P, P, P, P, ctypes.c_double, P, I, P, P, I, P]
+    lib.orc_compress_append.restype = I
+    lib.orc_window_append.argtypes = [I, I, I, P, P, I, I, P, P]
+    lib.orc_window_append.restype = I
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = I
     lib.orc_set_num_threads.argtypes = [I]
@@ -338,6 +350,77 @@ def step(inp, fp32_scores: bool = True, cand_in=None, cand_topk_blocks: int = 0,
                     getattr(inp, "comp_kv_fmt", "bf16"), getattr(inp, "comp_sc", None))
     res.update({"idx": idx, "win_idx": win, "out": o})
     return res
+
+
+# -- producer side: the cache writes of one decode step --------------------------
+
+def round_bf16(x: float) -> float:
+    return _load().orc_round_bf16(float(x))
+
+
+def e4m3_encode(y: float) -> int:
+    return int(_load().orc_e4m3_encode(float(y)))
+
+
+def quant_e4m3(x) -> tuple:
+    """e4m3 codes [..., D] and ue8m0 scales [..., D/32] of float64 rows."""
+    x = _c(x, np.float64)
+    D = x.shape[-1]
+    rows = x.reshape(-1, D)
+    codes = np.empty(rows.shape, dtype=np.uint8)
+    scales = np.empty((rows.shape[0], D // 32), dtype=np.uint8)
+    for r in range(rows.shape[0]):
+        _load().orc_quant_e4m3(_ptr(rows[r]), D, _ptr(codes[r]), _ptr(scales[r]))
+    return codes.reshape(x.shape), scales.reshape(*x.shape[:-1], D // 32)
+
+
+def quant_e2m1(x) -> tuple:
+    """Packed e2m1 codes [..., D/2] and e4m3 scales [..., D/16] of float64 rows."""
+    x = _c(x, np.float64)
+    D = x.shape[-1]
+    rows = x.reshape(-1, D)
+    codes = np.empty((rows.shape[0], D // 2), dtype=np.uint8)
+    scales = np.empty((rows.shape[0], D // 16), dtype=np.uint8)
+    for r in range(rows.shape[0]):
+        _load().orc_quant_e2m1(_ptr(np.ascontiguousarray(rows[r])), D, _ptr(codes[r]), _ptr(scales[r]))
+    return codes.reshape(*x.shape[:-1], D // 2), scales.reshape(*x.shape[:-1], D // 16)
+
+
+def compress_append(kv, score, kv_state, score_state, norm_w, eps: float, freqs, rd: int,
+                    codes, scales, start_pos: int, ratio: int):
+    """One decode step of the compressor and the compressed-cache write (in place on
+    kv_state / score_state / codes / scales).  Returns (row written?, latent [B, D])."""
+    kv = _c(kv, np.float32)
+    score = _c(score, np.float32)
+    B, D = kv.shape
+    for a, n in ((kv_state, "kv_state"), (score_state, "score_state")):
+        if ratio > 1 and (a.dtype != np.float32 or not a.flags.c_contiguous):
+            raise OracleError(f"{n} must be contiguous float32 (updated in place)")
+    for a in (codes, scales):
+        if a.dtype != np.uint8 or not a.flags.c_contiguous:
+            raise OracleError("codes / scales must be contiguous uint8 (updated in place)")
+    latent = np.zeros((B, D), dtype=np.float64)
+    rc = _load().orc_compress_append(B, D, ratio, start_pos, _ptr(kv), _ptr(score),
+                                     _ptr(kv_state) if ratio > 1 else None,
+                                     _ptr(score_state) if ratio > 1 else None,
+                                     _ptr(_c(norm_w, np.float32)), float(eps),
+                                     _ptr(_c(freqs, np.float32)), rd, _ptr(codes), _ptr(scales),
+                                     codes.shape[1], _ptr(latent))
+    if rc < 0:
+        _check(rc, "orc_compress_append")
+    return bool(rc), latent
+
+
+def window_append(kv_bits, freqs, rd: int, codes, scales, start_pos: int):
+    """One decode step's window-cache write (in place on codes [B,R,D] / scales)."""
+    kv_bits = _c(kv_bits, np.uint16)
+    B, D = kv_bits.shape
+    for a in (codes, scales):
+        if a.dtype != np.uint8 or not a.flags.c_contiguous:
+            raise OracleError("codes / scales must be contiguous uint8 (updated in place)")
+    rc = _load().orc_window_append(B, D, start_pos, _ptr(kv_bits), _ptr(_c(freqs, np.float32)), rd,
+                                   codes.shape[1], _ptr(codes), _ptr(scales))
+    _check(rc, "orc_window_append")
 
 
 def num_threads() -> int:

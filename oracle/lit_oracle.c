@@ -501,6 +501,202 @@ int orc_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv,
                                ORC_KV_BF16, comp_kv, NULL, T_cap, comp_idx, K, sink, scale, out);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Producer side: the cache writes of one decode step.                       */
+/*                                                                           */
+/* [V4.1] Compressor.forward (decode): the new token's kv and gate score     */
+/* (fp32, after the wkv / wgate projections, which are outside the path)     */
+/* fill slot start_pos % ratio of the sequence's kv_state / score_state; when */
+/* the group completes ((start_pos + 1) % ratio == 0) the latent is           */
+/* sum over slots of kv_state * softmax(score_state over the slots), per     */
+/* feature, cast to bf16 and RMS-normalised (RMSNorm.forward: x / sqrt(mean  */
+/* x^2 + eps) times the weight, computed in float, result in bf16).  Ratio 1 */
+/* has no state: the latent is the norm of the token's kv (cast to bf16).    */
+/* [V4.1] Attention._compress_kv then rotates the latent's last rd dims at   */
+/* position start_pos + 1 - ratio (apply_rotary_emb: adjacent pairs as       */
+/* complex numbers times freqs_cis, result back in bf16), quantises it with  */
+/* fp4_act_quant in groups of 16 with e4m3 scales and writes cache row       */
+/* start_pos / ratio.  [V4.1] Attention._window_kv: the token's window KV    */
+/* (after kv_norm) is rotated at start_pos, quantised with act_quant (e4m3,  */
+/* ue8m0 scale per 32) and written to ring slot start_pos % R.               */
+/*                                                                           */
+/* The quantisers' rounding is not on the pages (their kernels are absent);  */
+/* the readings taken, with every decision made exactly:                     */
+/*   e4m3 / ue8m0: scale 2^e with e the smallest integer such that           */
+/*     amax <= 448 * 2^e (amax 0: e = -127); code = x / 2^e rounded to the   */
+/*     nearest e4m3 value, ties to the even code;                            */
+/*   e2m1 / e4m3: scale s the smallest e4m3 value with 6 s >= amax (amax 0:  */
+/*     the smallest positive e4m3, code 1; amax > 6 * 448: 448); code = the  */
+/*     e2m1 value nearest to x / s, ties to the even code, sign of x kept.   */
+/* Intermediate values are exact (double) and rounded to bf16 where the      */
+/* pages store bf16: after the cast of the pooled kv, after the norm, after  */
+/* the rotation.  freqs: [positions, rd/2, 2] floats (cos, sin), as          */
+/* precompute_freqs_cis tabulates them.                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Round to the nearest bfloat16 value (8 significant bits), ties to even. */
+double orc_round_bf16(double x) {
+    if (x == 0.0 || isnan(x) || isinf(x)) return x;
+    double a = fabs(x);
+    double r;
+    if (a < ldexp(1.0, -126)) { /* subnormal spacing 2^-133 */
+        r = ldexp(nearbyint(ldexp(a, 133)), -133);
+    } else {
+        int e;
+        double m = frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+        r = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+    }
+    return x < 0 ? -r : r;
+}
+
+/* e4m3 code of y, |y| <= 448, to nearest (ties to the even code). */
+uint8_t orc_e4m3_encode(double y) {
+    int neg = y < 0 || (y == 0 && signbit(y));
+    double a = fabs(y);
+    int code;
+    if (a > 448.0) a = 448.0;
+    if (a < ldexp(1.0, -6)) {
+        code = (int)nearbyint(ldexp(a, 9)); /* subnormal steps of 2^-9 (8 = 2^-6) */
+    } else {
+        int e = ilogb(a);
+        int q = (int)nearbyint((ldexp(a, -e) - 1.0) * 8.0);
+        if (q == 8) { ++e; q = 0; }
+        code = ((e + 7) << 3) | q;
+    }
+    return (uint8_t)(code | (neg ? 0x80 : 0));
+}
+
+/* e2m1 code (4 bits) of x / s, to nearest (ties to the even code). */
+static uint8_t orc_e2m1_encode_scaled(double x, double s) {
+    double a = fabs(x);
+    int c = (a > 0.25 * s) + (a >= 0.75 * s) + (a > 1.25 * s) + (a >= 1.75 * s) +
+            (a > 2.5 * s) + (a >= 3.5 * s) + (a > 5.0 * s);
+    return (uint8_t)(c | (x < 0 ? 8 : 0));
+}
+
+/* Quantise D values (D % 32 == 0) into e4m3 codes with ue8m0 scales per 32. */
+void orc_quant_e4m3(const double *x, int D, uint8_t *codes, uint8_t *scales) {
+    for (int b0 = 0; b0 < D; b0 += 32) {
+        double amax = 0.0;
+        for (int d = b0; d < b0 + 32; ++d) if (fabs(x[d]) > amax) amax = fabs(x[d]);
+        int e = -127;
+        if (amax > 0.0) {
+            e = ilogb(amax) - 9;
+            while (amax > 448.0 * ldexp(1.0, e)) ++e;
+            while (e > -127 && amax <= 448.0 * ldexp(1.0, e - 1)) --e;
+        }
+        if (e > 127) e = 127;
+        scales[b0 / 32] = (uint8_t)(e + 127);
+        for (int d = b0; d < b0 + 32; ++d) codes[d] = orc_e4m3_encode(ldexp(x[d], -e));
+    }
+}
+
+/* Quantise D values (D % 16 == 0) into packed e2m1 codes with e4m3 scales per 16. */
+void orc_quant_e2m1(const double *x, int D, uint8_t *codes, uint8_t *scales) {
+    for (int b0 = 0; b0 < D; b0 += 16) {
+        double amax = 0.0;
+        for (int d = b0; d < b0 + 16; ++d) if (fabs(x[d]) > amax) amax = fabs(x[d]);
+        int sc = 1; /* positive e4m3 values rise with the code */
+        while (sc < 0x7E && 6.0 * orc_e4m3((uint8_t)sc) < amax) ++sc;
+        scales[b0 / 16] = (uint8_t)sc;
+        double s = orc_e4m3((uint8_t)sc);
+        for (int d = b0; d < b0 + 16; d += 2) {
+            uint8_t lo = orc_e2m1_encode_scaled(x[d], s), hi = orc_e2m1_encode_scaled(x[d + 1], s);
+            codes[d / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
+/* RMSNorm of D values (each already a bf16 value), result rounded to bf16. */
+static void orc_rmsnorm_bf16(const double *x, const float *w, int D, double eps, double *y) {
+    double ss = 0.0;
+    for (int d = 0; d < D; ++d) ss += x[d] * x[d];
+    double r = 1.0 / sqrt(ss / D + eps);
+    for (int d = 0; d < D; ++d) y[d] = orc_round_bf16((double)w[d] * (x[d] * r));
+}
+
+/* Rotate the last rd of D values at table row `pos`, rounding to bf16. */
+static void orc_rope_bf16(double *x, int D, int rd, const float *freqs, int pos) {
+    const float *f = freqs + (size_t)pos * rd; /* rd/2 (cos, sin) pairs */
+    for (int j = 0; j < rd / 2; ++j) {
+        double a = x[D - rd + 2 * j], b = x[D - rd + 2 * j + 1];
+        double c = f[2 * j], sn = f[2 * j + 1];
+        x[D - rd + 2 * j] = orc_round_bf16(a * c - b * sn);
+        x[D - rd + 2 * j + 1] = orc_round_bf16(a * sn + b * c);
+    }
+}
+
+/* One decode step of the compressor and the compressed-cache write.  kv, score:
+ * [B, D] floats; kv_state, score_state: [B, ratio, D] floats (ratio > 1; updated);
+ * codes [B, T_cap, D/2], scales [B, T_cap, D/16] (row start_pos/ratio written when
+ * the group completes); latent [B, D] doubles (pre-rotation bf16 values, may be
+ * NULL).  Returns 1 when a row was written, 0 when the group is still filling. */
+int orc_compress_append(int B, int D, int ratio, int start_pos, const float *kv,
+                        const float *score, float *kv_state, float *score_state,
+                        const float *norm_w, double eps, const float *freqs, int rd,
+                        uint8_t *codes, uint8_t *scales, int T_cap, double *latent) {
+    if (B < 0 || D <= 0 || D % 32 != 0 || ratio < 1 || start_pos < 0 || rd < 0 ||
+        rd > D || rd % 2 != 0)
+        return ORC_E_ARG;
+    const int done = (start_pos + 1) % ratio == 0;
+    const int row = start_pos / ratio;
+    if (done && row >= T_cap) return ORC_E_ARG;
+    const int pos = start_pos + 1 - ratio; /* the group's first token */
+    for (int b = 0; b < B; ++b) {
+        const float *k = kv + (size_t)b * D, *g = score + (size_t)b * D;
+        double *x = (double *)malloc(sizeof(double) * (size_t)D * 2);
+        double *y = x + D;
+        if (ratio == 1) {
+            for (int d = 0; d < D; ++d) x[d] = orc_round_bf16(k[d]);
+        } else {
+            float *ks = kv_state + (size_t)b * ratio * D, *gs = score_state + (size_t)b * ratio * D;
+            const int slot = start_pos % ratio;
+            for (int d = 0; d < D; ++d) {
+                ks[(size_t)slot * D + d] = k[d];
+                gs[(size_t)slot * D + d] = g[d];
+            }
+            if (!done) { free(x); continue; }
+            for (int d = 0; d < D; ++d) {
+                double m = -INFINITY;
+                for (int r = 0; r < ratio; ++r) if (gs[(size_t)r * D + d] > m) m = gs[(size_t)r * D + d];
+                double z = 0.0, acc = 0.0;
+                for (int r = 0; r < ratio; ++r) {
+                    double e = exp((double)gs[(size_t)r * D + d] - m);
+                    z += e;
+                    acc += e * (double)ks[(size_t)r * D + d];
+                }
+                x[d] = orc_round_bf16(acc / z); /* kv.to(dtype) */
+            }
+        }
+        orc_rmsnorm_bf16(x, norm_w, D, eps, y);
+        if (latent) for (int d = 0; d < D; ++d) latent[(size_t)b * D + d] = y[d];
+        orc_rope_bf16(y, D, rd, freqs, pos);
+        orc_quant_e2m1(y, D, codes + ((size_t)b * T_cap + row) * (D / 2),
+                       scales + ((size_t)b * T_cap + row) * (D / 16));
+        free(x);
+    }
+    return done;
+}
+
+/* One decode step's window-cache write: kv [B, D] bf16 bits (after kv_norm) rotated
+ * at start_pos, quantised to e4m3 / ue8m0-32, written to slot start_pos % R of
+ * codes [B, R, D] and scales [B, R, D/32]. */
+int orc_window_append(int B, int D, int start_pos, const uint16_t *kv, const float *freqs,
+                      int rd, int R, uint8_t *codes, uint8_t *scales) {
+    if (B < 0 || D <= 0 || D % 32 != 0 || start_pos < 0 || R <= 0 || rd < 0 || rd > D ||
+        rd % 2 != 0)
+        return ORC_E_ARG;
+    const int slot = start_pos % R;
+    double *x = (double *)malloc(sizeof(double) * (size_t)D);
+    for (int b = 0; b < B; ++b) {
+        for (int d = 0; d < D; ++d) x[d] = orc_bf16(kv[(size_t)b * D + d]);
+        orc_rope_bf16(x, D, rd, freqs, start_pos);
+        orc_quant_e4m3(x, D, codes + ((size_t)b * R + slot) * D, scales + ((size_t)b * R + slot) * (D / 32));
+    }
+    free(x);
+    return 0;
+}
+
 /* Threads the OpenMP loops above will use (1 without OpenMP). */
 int orc_num_threads(void) {
 #ifdef _OPENMP

@@ -16,6 +16,7 @@ from tests import test_oracle_attention as TA
 from tests import test_oracle_candidates as TC
 from tests import test_oracle_formats as TF
 from tests import test_oracle_indexer as TI
+from tests import test_oracle_producer as TP
 from tests import test_oracle_topk as TT
 from tests import test_oracle_window as TW
 
@@ -84,6 +85,18 @@ MUTANTS = [
     ("KV e4m3 scale dropped", "for (int d = 0; d < D; ++d) v[d] = orc_e4m3(c[d]) * orc_e8m0(s[d / 32]);",
      "for (int d = 0; d < D; ++d) v[d] = orc_e4m3(c[d]);",
      [lambda o: TA.test_quantised_kv_equals_library_decoded_rows(o, 64)]),
+    ("rotation sign", "x[D - rd + 2 * j] = orc_round_bf16(a * c - b * sn);",
+     "x[D - rd + 2 * j] = orc_round_bf16(a * c + b * sn);", [TP.test_rmsnorm_closed_form_and_rotation]),
+    ("compressed rotation at the last token", "const int pos = start_pos + 1 - ratio; /* the group's first token */",
+     "const int pos = start_pos;", [TP.test_compressor_group_timing_and_pooling]),
+    ("fp4 quantiser tie rule", "int c = (a > 0.25 * s) + (a >= 0.75 * s)", "int c = (a > 0.25 * s) + (a > 0.75 * s)",
+     [TP.test_quant_e2m1_brute_force]),
+    ("rms over D-1", "double r = 1.0 / sqrt(ss / D + eps);", "double r = 1.0 / sqrt(ss / (D - 1) + eps);",
+     [TP.test_rmsnorm_closed_form_and_rotation, TP.test_compressor_group_timing_and_pooling]),
+    ("pooling reads slot 0 only", "acc += e * (double)ks[(size_t)r * D + d];", "acc += e * (double)ks[d];",
+     [TP.test_compressor_group_timing_and_pooling]),
+    ("e4m3 encoder truncates", "int q = (int)nearbyint((ldexp(a, -e) - 1.0) * 8.0);", "int q = (int)floor((ldexp(a, -e) - 1.0) * 8.0);",
+     [TP.test_e4m3_encoder_matches_torch, TP.test_quant_e4m3_brute_force]),
     ("topk tie rule reversed", "return (x->t > y->t) - (x->t < y->t);",
      "return (x->t < y->t) - (x->t > y->t);", [TT.test_property_checker_with_ties_and_prefill]),
     ("topk ascending sort dropped", "qsort(sel, (size_t)take, sizeof(int), orc_int_cmp);", "",
