@@ -294,6 +294,57 @@ lit_status lit_sparse_attn_layers(int L, const uint16_t *q, int B, int S, int H,
 size_t lit_sparse_attn_layers_workspace_bytes(int L, int B, int S, int H, int dv, int W, int K);
 
 /*
+ * Producer side: the cache writes of one decode step ([V4.1] Compressor.forward,
+ * RMSNorm.forward, apply_rotary_emb, Attention._compress_kv and _window_kv).  The
+ * projections that make their inputs (wkv, wgate, kv_norm) are outside the path.
+ * Quantiser readings (their kernels are not on the pages): fp4 scale = the
+ * smallest e4m3 value s with 6 s >= the group's amax (amax 0: e4m3 code 1),
+ * codes to the nearest e2m1 value, ties to the even code; e4m3 scale = the
+ * smallest 2^e with amax <= 448 * 2^e, codes to the nearest e4m3 value, ties to
+ * the even code.
+ *
+ * lit_compress_append -- one decode token per sequence into the compressor.  The
+ * token's kv / score fill slot start_pos % ratio of kv_state / score_state; when
+ * (start_pos + 1) % ratio == 0 the group's latent -- sum over the slots of
+ * kv_state * softmax(score_state over the slots), per feature, cast to bf16 and
+ * RMS-normalised with norm_w (fp32 math, bf16 result); for ratio 1 the norm of
+ * the token's kv -- is rotated on its last rd dims at position
+ * start_pos + 1 - ratio, quantised to LIT_KV_E2M1 and written to cache row
+ * start_pos / ratio.  Nothing is written to the cache otherwise.
+ *
+ *   kv, score    (device) f32 [B, D]          the token's compressor inputs
+ *   kv_state     (device) f32 [B, ratio, D]   state (ratio > 1; NULL for ratio 1);
+ *   score_state  (device) f32 [B, ratio, D]   initialise kv 0, score -inf
+ *   norm_w       (device) f32 [D]
+ *   freqs        (device) f32 [n_pos, rd/2, 2] rotary table (cos, sin) per position
+ *   codes        (device) u8  [B, T_cap, D/2] compressed cache (LIT_KV_E2M1)
+ *   scales       (device) u8  [B, T_cap, D/16]
+ *   latent       (device) bf16 [B, D] or NULL: the pre-rotation latent (the
+ *                indexer's key projection reads it), written with the row
+ * Requirements: D a multiple of 32, at most 256; rd even, <= D; the rotation
+ * position < n_pos and the row < T_cap when a row is written.
+ */
+lit_status lit_compress_append(int B, int D, int ratio, int start_pos, const float *kv,
+                               const float *score, float *kv_state, float *score_state,
+                               const float *norm_w, float eps, const float *freqs, int n_pos,
+                               int rd, uint8_t *codes, uint8_t *scales, int T_cap,
+                               uint16_t *latent, void *stream);
+
+/*
+ * lit_window_append -- one decode token per sequence into the window ring: the
+ * bf16 row kv (after kv_norm) is rotated on its last rd dims at start_pos,
+ * quantised to LIT_KV_E4M3 and written to slot start_pos % R.
+ *
+ *   kv     (device) bf16 [B, D]
+ *   freqs  (device) f32  [n_pos, rd/2, 2]
+ *   codes  (device) u8   [B, R, D];  scales (device) u8 [B, R, D/32]
+ * Requirements: D a multiple of 32, at most 256; rd even, <= D; start_pos < n_pos.
+ */
+lit_status lit_window_append(int B, int D, int start_pos, const uint16_t *kv, const float *freqs,
+                             int n_pos, int rd, uint8_t *codes, uint8_t *scales, int R,
+                             void *stream);
+
+/*
  * lit_sparse_step -- the whole step for one layer: lit_indexer_scores, lit_topk
  * and lit_sparse_attn, with the window rows of lit_window_indices derived
  * in-kernel from (start_pos, W, R).  [V4.1] Attention.forward with

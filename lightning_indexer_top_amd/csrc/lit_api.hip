@@ -328,6 +328,49 @@ lit_status lit_sparse_attn_layers(int L, const uint16_t *q, int B, int S, int H,
     return hip_status(launch_sparse_attn(a, p, (hipStream_t)stream));
 }
 
+static lit_status check_produce(int B, int D, int rd, int pos, int n_pos, const void *freqs) {
+    if (B < 0 || D <= 0 || rd < 0 || n_pos < 0) return LIT_E_SHAPE;
+    if (D % 32 != 0 || rd % 2 != 0 || rd > D) return LIT_E_SHAPE;
+    if (D > 256) return LIT_E_UNSUPPORTED;
+    if (B > 0 && (pos < 0 || pos >= n_pos)) return LIT_E_SHAPE;
+    if (B > 0 && rd > 0 && !freqs) return LIT_E_NULL;
+    return LIT_OK;
+}
+
+lit_status lit_compress_append(int B, int D, int ratio, int start_pos, const float *kv, const float *score,
+                               float *kv_state, float *score_state, const float *norm_w, float eps,
+                               const float *freqs, int n_pos, int rd, uint8_t *codes, uint8_t *scales, int T_cap,
+                               uint16_t *latent, void *stream) {
+    if (ratio < 1 || start_pos < 0 || T_cap < 0) return LIT_E_SHAPE;
+    const bool done = (start_pos + 1) % ratio == 0;
+    lit_status st = check_produce(B, D, rd, done ? start_pos + 1 - ratio : 0, done ? n_pos : 1, freqs);
+    if (st != LIT_OK) return st;
+    if (B == 0) return LIT_OK;
+    if (done && start_pos / ratio >= T_cap) return LIT_E_SHAPE;
+    if (!kv || !norm_w || (ratio > 1 && (!score || !kv_state || !score_state))) return LIT_E_NULL;
+    if (done && (!codes || !scales)) return LIT_E_NULL;
+    ProduceArgs p{};
+    p.B = B; p.D = D; p.ratio = ratio; p.start_pos = start_pos; p.rd = rd;
+    p.kv = kv; p.score = score; p.kv_state = kv_state; p.score_state = score_state;
+    p.norm_w = norm_w; p.eps = eps; p.freqs = freqs; p.codes = codes; p.scales = scales;
+    p.T_cap = T_cap; p.latent = latent;
+    return hip_status(launch_compress_append(p, (hipStream_t)stream));
+}
+
+lit_status lit_window_append(int B, int D, int start_pos, const uint16_t *kv, const float *freqs, int n_pos,
+                             int rd, uint8_t *codes, uint8_t *scales, int R, void *stream) {
+    if (start_pos < 0 || R < 0) return LIT_E_SHAPE;
+    lit_status st = check_produce(B, D, rd, start_pos, n_pos, freqs);
+    if (st != LIT_OK) return st;
+    if (B == 0) return LIT_OK;
+    if (R < 1) return LIT_E_SHAPE;
+    if (!kv || !codes || !scales) return LIT_E_NULL;
+    ProduceArgs p{};
+    p.B = B; p.D = D; p.start_pos = start_pos; p.rd = rd; p.freqs = freqs;
+    p.win_in = kv; p.codes = codes; p.scales = scales; p.R = R;
+    return hip_status(launch_window_append(p, (hipStream_t)stream));
+}
+
 // Workspace of the multi-kernel step: scores [B*S, ld] fp32, then the attention partials
 // (level one's block scores share the partials' space: they are used up before).
 static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld, AttnPlan *plan) {

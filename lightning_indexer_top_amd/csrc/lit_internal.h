@@ -166,6 +166,24 @@ __host__ __device__ inline int window_slot_at(const WindowBase &w, int start_pos
 
 
 // ---------------------------------------------------------------------------
+// Producer side: the cache writes of one decode step (produce.hip)
+// ---------------------------------------------------------------------------
+struct ProduceArgs {
+    int B, D, ratio, start_pos, rd;
+    const float *kv, *score;        // [B,D] compressor inputs (fp32)
+    float *kv_state, *score_state;  // [B,ratio,D] (ratio > 1)
+    const float *norm_w;            // [D]
+    float eps;
+    const float *freqs;             // [positions, rd/2, 2] (cos, sin)
+    const uint16_t *win_in;         // [B,D] bf16 window KV row (window append)
+    uint8_t *codes, *scales;        // cache codes / scale bytes
+    int T_cap, R;
+    uint16_t *latent;               // [B,D] bf16 pre-rotation latent, or NULL
+};
+hipError_t launch_compress_append(const ProduceArgs &p, hipStream_t stream);
+hipError_t launch_window_append(const ProduceArgs &p, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
 // Fused decode step (fused_decode.hip)
 // ---------------------------------------------------------------------------
 struct FusedArgs {

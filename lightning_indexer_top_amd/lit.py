@@ -68,6 +68,9 @@ SIGNATURES = {
     "lit_sparse_attn_layers": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _I, _P, _I, _P, _I,
                                     _P, _F, _P, _P, _Z, _P]),
     "lit_sparse_attn_layers_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+    "lit_compress_append": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _F, _P, _I, _I, _P, _P, _I, _P,
+                                 _P]),
+    "lit_window_append": (_I, [_I, _I, _I, _P, _P, _I, _I, _P, _P, _I, _P]),
     "lit_sparse_step": (_I, [ctypes.POINTER(lit_step_args), _P, _Z, _P]),
     "lit_sparse_step_workspace_bytes": (_Z, [ctypes.POINTER(lit_step_args)]),
     "lit_sparse_step_state_bytes": (_Z, [ctypes.POINTER(lit_step_args)]),
@@ -311,6 +314,40 @@ def lit_sparse_attn_layers(q, win_kv, win_idx, comp_kv, comp_idx, sink, scale: f
         L, _ptr(q), B, S, H, D, dv, _ptr(win_kv), R, _ptr(win_idx), W, start_pos, _ptr(comp_kv), T_cap,
         _ptr(comp_idx), K, _ptr(sink), float(scale), _ptr(out), _ptr(ws), nbytes, _stream(stream)))
     return out
+
+
+def lit_compress_append(kv, score, kv_state, score_state, norm_w, eps: float, freqs, rd: int,
+                        codes, scales, start_pos: int, ratio: int, latent=None, stream=None) -> bool:
+    """One decode token per sequence into the compressor (state and cache updated in
+    place); returns whether the group completed and a cache row was written."""
+    _need(kv, torch.float32, "kv")
+    B, D = kv.shape
+    for t, dt, n in ((score, torch.float32, "score"), (norm_w, torch.float32, "norm_w"),
+                     (freqs, torch.float32, "freqs"), (codes, torch.uint8, "codes"),
+                     (scales, torch.uint8, "scales")):
+        _need(t, dt, n)
+    for t, n in ((kv_state, "kv_state"), (score_state, "score_state")):
+        if t is not None:
+            _need(t, torch.float32, n)
+    if latent is not None:
+        _need(latent, torch.bfloat16, "latent")
+    _check("lit_compress_append", library().lit_compress_append(
+        B, D, ratio, start_pos, _ptr(kv), _ptr(score), _ptr(kv_state), _ptr(score_state),
+        _ptr(norm_w), float(eps), _ptr(freqs), freqs.shape[0], rd, _ptr(codes), _ptr(scales),
+        codes.shape[1], _ptr(latent), _stream(stream)))
+    return (start_pos + 1) % ratio == 0
+
+
+def lit_window_append(kv, freqs, rd: int, codes, scales, start_pos: int, stream=None) -> None:
+    """One decode token per sequence into the window ring (codes [B,R,D] e4m3, scales)."""
+    _need(kv, torch.bfloat16, "kv")
+    B, D = kv.shape
+    for t, dt, n in ((freqs, torch.float32, "freqs"), (codes, torch.uint8, "codes"),
+                     (scales, torch.uint8, "scales")):
+        _need(t, dt, n)
+    _check("lit_window_append", library().lit_window_append(
+        B, D, start_pos, _ptr(kv), _ptr(freqs), freqs.shape[0], rd, _ptr(codes), _ptr(scales),
+        codes.shape[1], _stream(stream)))
 
 
 def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int, ratio: int,

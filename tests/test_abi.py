@@ -182,6 +182,25 @@ def test_quantised_kv_refusals(lib):
     assert call(B=0) == 0
 
 
+def test_producer_refusals(lib):
+    f, g = lib.lit_compress_append, lib.lit_window_append
+    def call(**kw):
+        a = dict(B=2, D=192, ratio=4, sp=7, kv=A, sc=A, ks=A, gs=A, w=A, eps=1e-20, fr=A, n=64,
+                 rd=64, c=A, s=A, T=2, lat=None, st=None)
+        a.update(kw)
+        return f(*[a[k] for k in ("B", "D", "ratio", "sp", "kv", "sc", "ks", "gs", "w", "eps",
+                                  "fr", "n", "rd", "c", "s", "T", "lat", "st")])
+    assert call(D=80) == 2 and call(D=288) == 4 and call(rd=63) == 2 and call(rd=224) == 2
+    assert call(T=1) == 2                       # row 7/4 = 1 needs two rows
+    assert call(n=4) == 2                       # rotation position 4 is outside the table
+    assert call(ks=None) == 1 and call(c=None) == 1
+    assert call(ratio=0) == 2 and call(B=0) == 0
+    assert g(2, 192, 70, A, A, 64, 64, A, A, 128, None) == 2   # position 70 outside the table
+    assert g(2, 192, 7, None, A, 64, 64, A, A, 128, None) == 1
+    assert g(2, 192, 7, A, A, 64, 64, A, A, 0, None) == 2
+    assert g(0, 192, 7, A, A, 64, 64, A, A, 128, None) == 0
+
+
 def test_window_refusals(lib):
     assert lib.lit_window_indices(1, 8, 100, 16, 16, A, None) == 2   # needs 23 slots
     assert lib.lit_window_indices(1, 8, 100, 16, 23, None, None) == 1

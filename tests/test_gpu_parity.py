@@ -621,3 +621,73 @@ def test_sparse_attn_quantised_kv(orc, B, S, start_pos, D, dv, W, K, wf, cf):
     want = orc.sparse_attn(inp.q, wkv, win, ckv, idx, inp.sink, inp.scale, dv, wf, wsc, cf, csc)
     err = np.abs(bf16_host(got) - want).max()
     assert err <= ATTN_TOL, f"max err {err}"
+
+
+
+# ---------------------------------------------------------------------------------
+# producer side: the cache writes of decode steps (compressor pooling, norm, rotation,
+# quantised rows).  The pre-quantisation values are bf16 on both sides; they agree
+# exactly unless an fp32 intermediate lands within an ulp of a bf16 rounding midpoint,
+# so codes must agree exactly for all but a few elements, and those few may differ by
+# one code step.
+# ---------------------------------------------------------------------------------
+def _dequant_fp4_rows(codes, scales):
+    from tests.test_oracle_attention import _table_rows_e2m1
+    return _table_rows_e2m1(codes, scales)
+
+
+@pytest.mark.parametrize("ratio,D,rd,B", [(4, 192, 64, 3), (2, 128, 32, 2), (1, 64, 16, 2),
+                                          (4, 256, 64, 1)])
+def test_compress_append_steps(orc, ratio, D, rd, B):
+    steps = 3 * ratio + 1
+    a = synth.make_append(B=B, D=D, rd=rd, ratio=ratio, steps=steps, positions=64, seed=70 + D)
+    T_cap = steps // ratio + 1
+    ks = np.zeros((B, ratio, D), np.float32)
+    gs = np.full((B, ratio, D), -np.inf, np.float32)
+    oc = np.zeros((B, T_cap, D // 2), np.uint8)
+    osc = np.zeros((B, T_cap, D // 16), np.uint8)
+    dks, dgs = dev(ks.copy()), dev(gs.copy())
+    dc, dsc = dev(oc.copy()), dev(osc.copy())
+    dw, dfr = dev(a.norm_w), dev(a.freqs)
+    lat = torch.zeros((B, D), dtype=torch.bfloat16, device="cuda")
+    near = total = 0
+    for t in range(steps):
+        w_o, lat_o = orc.compress_append(a.kv[t], a.score[t], ks if ratio > 1 else None,
+                                         gs if ratio > 1 else None, a.norm_w, a.eps, a.freqs, rd,
+                                         oc, osc, t, ratio)
+        w_g = L.lit_compress_append(dev(a.kv[t]), dev(a.score[t]), dks if ratio > 1 else None,
+                                    dgs if ratio > 1 else None, dw, a.eps, dfr, rd, dc, dsc, t,
+                                    ratio, latent=lat)
+        torch.cuda.synchronize()
+        assert w_g == w_o
+        if ratio > 1:
+            assert np.array_equal(dks.cpu().numpy(), ks) and np.array_equal(dgs.cpu().numpy(), gs)
+        if w_o:
+            lg = bf16_host(lat)
+            assert np.all(np.abs(lg - lat_o) <= 2.0 ** -7 * np.abs(lat_o) + 1e-30), t
+            row = t // ratio
+            cg, sg = dc.cpu().numpy()[:, row], dsc.cpu().numpy()[:, row]
+            assert np.abs(sg.astype(int) - osc[:, row].astype(int)).max() <= 1
+            vg, vo = _dequant_fp4_rows(cg, sg), _dequant_fp4_rows(oc[:, row], osc[:, row])
+            diff = vg != vo
+            near += int(diff.sum())
+            total += vg.size
+            step = np.repeat(np.maximum(osc[:, row], 1), 16, axis=-1)  # noqa: F841
+            assert np.all(np.abs(vg - vo)[diff] <= 2.0 * np.abs(vo)[diff] + 1e-6)
+    assert near <= max(2, total // 1000), f"{near} of {total} codes differ"
+
+
+def test_window_append_steps(orc):
+    B, D, rd, R = 3, 192, 64, 128
+    a = synth.make_append(B=B, D=D, rd=rd, ratio=1, steps=5, positions=300, seed=81)
+    oc = np.zeros((B, R, D), np.uint8)
+    osc = np.zeros((B, R, D // 32), np.uint8)
+    dc, dsc, dfr = dev(oc.copy()), dev(osc.copy()), dev(a.freqs)
+    for t, pos in enumerate([0, 1, 127, 128, 290]):
+        orc.window_append(a.win[t], a.freqs, rd, oc, osc, pos)
+        L.lit_window_append(bf16_dev(a.win[t]), dfr, rd, dc, dsc, pos)
+    torch.cuda.synchronize()
+    cg, sg = dc.cpu().numpy(), dsc.cpu().numpy()
+    assert np.array_equal(sg, osc)
+    mism = int((cg != oc).sum())
+    assert mism <= 2, f"{mism} window codes differ"
