@@ -49,21 +49,30 @@ def step_bytes(sp: dict) -> dict:
     key_row = (Di // 2 if sp.get("index_fmt", "e4m3") == "e2m1" else Di) + Di // 32
     indexer = B * T * key_row + B * S * Hi * (key_row + 4) + 4 * B * S * T
     topk = 4 * B * S * T + 4 * B * S * keff
+    # a gathered row: bf16, or quantised (window e4m3 + ue8m0/32, compressed e2m1 + e4m3/16)
+    quant = sp.get("kv_fmt", "bf16") == "quant"
+    wrow = D + D // 32 if quant else 2 * D
+    crow = D // 2 + D // 16 if quant else 2 * D
     if S == 1:
-        attn = B * ((W + keff) * (2 * D + 4) + 2 * H * D + 2 * H * dv)
+        attn = B * (W * (wrow + 4) + keff * (crow + 4) + 2 * H * D + 2 * H * dv)
         # the survey's per-query figure: keys + q/w + indices written + gathered rows
         # with their indices + q/out
-        step = B * (T * key_row + Hi * key_row + 4 * Hi + 4 * keff + (W + keff) * (2 * D + 4)
+        step = B * (T * key_row + Hi * key_row + 4 * Hi + 4 * keff + W * (wrow + 4) + keff * (crow + 4)
                     + 2 * H * D + 2 * H * dv)
     else:
         R = S if sp0 == 0 else W + S - 1
-        attn = (4 * B * S * keff + B * R * 2 * D + B * T * 2 * D + B * S * H * (2 * D + 2 * dv))
-        step = (B * T * key_row + B * S * Hi * (key_row + 4) + 8 * B * S * keff + B * R * 2 * D
-                + B * T * 2 * D + B * S * H * (2 * D + 2 * dv))
+        attn = (4 * B * S * keff + B * R * wrow + B * T * crow + B * S * H * (2 * D + 2 * dv))
+        step = (B * T * key_row + B * S * Hi * (key_row + 4) + 8 * B * S * keff + B * R * wrow
+                + B * T * crow + B * S * H * (2 * D + 2 * dv))
     kb = sp.get("cand_k", 0)
     if kb:  # a level-two layer also reads its candidate block list
         topk += 4 * B * S * kb
         step += 4 * B * S * kb
+    if sp.get("append_rd", 0):
+        # the cache writes: kv + score read, the state slot written and the group read back,
+        # the compressed row and the window slot written, the window row read
+        app = B * (8 * D + 4 * D + 8 * r * D + D // 2 + D // 16 + 2 * D + D + D // 32)
+        step += app
     nl = sp.get("layers", 1)
     if nl > 1 and S == 1:
         # every further layer reads its queries, window rows and the shared list and writes
@@ -220,6 +229,12 @@ def main() -> int:
 
     spec = dict(synth.WORKLOADS[args.workload])
     fmt = spec.get("index_fmt", "e4m3")
+    kv_quant = spec.get("kv_fmt", "bf16") == "quant"
+
+    def kv_args(d):
+        if not kv_quant:
+            return {}
+        return dict(win_fmt="e4m3", win_sc=d["win_sc"], comp_fmt="e2m1", comp_sc=d["comp_sc"])
     cand_kb, cand_bs = spec.get("cand_topk_blocks", 0), spec.get("cand_block_size", 0)
     if cand_kb:
         spec["cand_k"] = L.library().lit_candidate_blocks_width(
@@ -251,7 +266,8 @@ def main() -> int:
                                        comp_kv=d["comp_kv"], start_pos=spec["start_pos"],
                                        ratio=spec["ratio"], index_topk=spec["index_topk"],
                                        W=spec["W"], scale=spec["D"] ** -0.5, fmt=fmt,
-                                       cand_in=cands[j], cand_block_size=cand_bs)
+                                       cand_in=cands[j], cand_block_size=cand_bs,
+                                       **kv_args(d))
         argv.append(a)
         keep.append((idx, out))
     ws = L.step_workspace(argv[0], device=dev)
@@ -279,7 +295,31 @@ def main() -> int:
         return g
 
     nl = spec.get("layers", 1)
-    if nl > 1:
+    ard = spec.get("append_rd", 0)
+    if ard:
+        # the step's cache writes first: the new token into the compressor (the group
+        # completes, so the compressed row start_pos / ratio is written) and the window
+        # ring; their inputs are drawn per instance
+        g_ = torch.Generator(device=dev)
+        g_.manual_seed(spec["seed"] + 11)
+        Bq, Dq, r_ = spec["B"], spec["D"], spec["ratio"]
+        table = torch.from_numpy(synth.rope_table(ard, spec["start_pos"] + 1, 40000.0)).to(dev)
+        norm_w = (0.5 + torch.rand(Dq, device=dev, generator=g_))
+        app = [dict(kv=torch.randn(Bq, Dq, device=dev, generator=g_),
+                    score=torch.randn(Bq, Dq, device=dev, generator=g_),
+                    ks=torch.zeros(Bq, r_, Dq, device=dev),
+                    gs=torch.full((Bq, r_, Dq), -float("inf"), device=dev),
+                    win=torch.randn(Bq, Dq, device=dev, generator=g_).to(torch.bfloat16))
+               for _ in range(n_inst)]
+
+        def append_call(j):
+            d = insts[j]
+            L.lit_compress_append(app[j]["kv"], app[j]["score"], app[j]["ks"], app[j]["gs"], norm_w,
+                                  1e-20, table, ard, d["comp_kv"], d["comp_sc"], spec["start_pos"], r_)
+            L.lit_window_append(app[j]["win"], table, ard, d["win_kv"], d["win_sc"], spec["start_pos"])
+
+        step_calls = [(lambda j=j: (append_call(j), L.lit_sparse_step(argv[j], ws))) for j in range(n_inst)]
+    elif nl > 1:
         # the layers that reuse this layer's top-k: their own queries and window KV, the
         # shared compressed KV and list, attention in one call after the step
         g_ = torch.Generator(device=dev)
@@ -350,9 +390,9 @@ def main() -> int:
                                                     spec["index_topk"], cands[j], cand_bs,
                                                     idx=keep[j][0]))
                  for j in range(n_inst)],
-        "attention": [(lambda j=j: L.lit_sparse_attn(
+        "attention": [(lambda j=j: L.lit_sparse_attn_fmt(
             insts[j]["q"], insts[j]["win_kv"], win, insts[j]["comp_kv"], keep[j][0], None,
-            spec["D"] ** -0.5, out=keep[j][1], ws=ws)) for j in range(n_inst)],
+            spec["D"] ** -0.5, out=keep[j][1], ws=ws, **kv_args(insts[j]))) for j in range(n_inst)],
     }
     if cand_kb:
         # the candidate source's level one (not part of this layer's step; reported beside it)
@@ -361,6 +401,8 @@ def main() -> int:
         stage_calls["candidates"] = [(lambda j=j: L.lit_candidate_blocks(
             scores[j], spec["start_pos"], spec["ratio"], cand_kb, cand_bs, blocks=cands[j], ws=cws))
             for j in range(n_inst)]
+    if ard:
+        stage_calls["append"] = [(lambda j=j: append_call(j)) for j in range(n_inst)]
     stage_reps = max(1, min(20, 2000 // n_inst))
     stages_us = {}
     for name, calls in stage_calls.items():
@@ -439,17 +481,20 @@ def main() -> int:
         "metric": METRIC, "value": round(value, 1), "unit": "queries/s", "n_gpus": 1,
         "steps": K, "warmup": Wm, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": ("fp4-e2m1" if fmt == "e2m1" else "fp8-e4m3") + "+bf16", "data": "synthetic",
+        "dtype": ("fp4-e2m1" if fmt == "e2m1" else "fp8-e4m3")
+        + ("+kv-e4m3/e2m1" if kv_quant else "+bf16"), "data": "synthetic",
         "config": {"workload": args.workload, "batch": spec["B"], "query_tokens": spec["S"],
                    "context": spec["start_pos"] + spec["S"], "compress_ratio": spec["ratio"],
                    "window": spec["W"], "heads": spec["H"], "head_dim": spec["D"],
                    "index_heads": spec["Hi"], "index_dim": spec["Di"], "index_format": fmt,
                    **({"candidate_blocks": cand_kb, "candidate_block_size": cand_bs} if cand_kb else {}),
                    **({"layers_sharing_topk": nl} if nl > 1 else {}),
+                   **({"cache_writes": "compressor + window ring, rd %d" % ard} if ard else {}),
                    "index_topk": spec["index_topk"], "input_instances": n_inst,
                    "timing": "HIP graph replay over rotating cold-cache instances",
                    "step_form": ("fused single kernel" if fused else "indexer, top-k, attention kernels")
-                   + (f" + one attention call for {nl - 1} more layers" if nl > 1 else "")},
+                   + (f" + one attention call for {nl - 1} more layers" if nl > 1 else "")
+                   + (", after the compressor and window-ring writes" if ard else "")},
         "hbm": {"step_bytes": sb["step"], "achieved_gbps": round(step_gbps, 1),
                 "peak_gbps": HBM_PEAK_GBPS, "frac": round(step_gbps / HBM_PEAK_GBPS, 4)},
         "kernel_stages_us": {k: round(v, 3) for k, v in stages_us.items()},

@@ -418,8 +418,9 @@ typedef struct lit_step_args {
     int cand_topk_blocks;
     int cand_block_size;    /* rows per block, for cand_in and cand_out */
     /* quantised attention KV (lit_kv_format; 0 = bf16): win_kv / comp_kv then hold the
-     * codes (cast to the field's type) and these the scale bytes.  A quantised source
-     * selects the multi-kernel form. */
+     * codes (cast to the field's type) and these the scale bytes.  Both sources
+     * quantised (window LIT_KV_E4M3, compressed LIT_KV_E2M1) run fused unless the
+     * layer uses candidates; one quantised source alone runs as kernels. */
     int win_kv_format;
     const uint8_t *win_kv_scales;
     int comp_kv_format;

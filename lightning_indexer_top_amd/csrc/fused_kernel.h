@@ -1,8 +1,9 @@
 // fused_kernel.h -- the whole sparse-attention step for decode-sized batches in one
 // launch: indexer scores -> exact top-k -> gather attention -> merge.  Included by one
-// source file per index-code format and masking (fused_e4m3.hip, fused_e2m1.hip and
-// their _cand forms for level-two layers of the two-level top-k), each of which
-// instantiates its kernels; fused_decode.hip plans and dispatches.
+// source file per index-code format and variant (fused_e4m3.hip, fused_e2m1.hip, their
+// _cand forms for level-two layers of the two-level top-k and _qkv forms for quantised
+// attention KV), each of which instantiates its kernels; fused_decode.hip plans and
+// dispatches.
 //
 // What is computed is exactly what indexer.hip, topk.hip and attention.hip compute
 // (DeepSeek-V4.1-Flash-NVFP4 inference/model.py, Indexer.forward and
@@ -48,6 +49,8 @@
 // and goes on, so the kernel always finishes; results are then undefined and the
 // error word reports it.
 #pragma once
+
+#include <type_traits>
 
 #include "select_ops.h"
 
@@ -199,8 +202,12 @@ __device__ inline uint32_t wg_sum(uint32_t v, uint32_t *red) {
 // MASK: a level-two layer of the two-level top-k (DeepSeek-V4.1-Flash-NVFP4 model.py,
 // Indexer.forward with candidates): rows outside the query's candidate blocks score
 // -inf before the selection.
-template <int D, int DI, int FMT, int HT, bool CACHED, bool MASK>
+// QKV: the attention KV sources are quantised (window e4m3 / ue8m0-32, compressed
+// e2m1 / e4m3-16); rows are loaded as codes and dequantised when their tile is computed.
+template <int D, int DI, int FMT, int HT, bool CACHED, bool MASK, bool QKV>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
+    using WinRows = std::conditional_t<QKV, KvRows<D, kKvE4M3>, AttnRows<D>>;
+    using PickRows = std::conditional_t<QKV, KvRows<D, kKvE2M1>, AttnRows<D>>;
     constexpr int LD = D + 4;
     __shared__ FusedLds sm;
     __shared__ __attribute__((aligned(16))) uint16_t attn_lds[4 * 32 * LD];  // rows / candidates / merge
@@ -331,14 +338,18 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     // attended), so that the loads need no branch
     const int own_slot = (ia.start_pos + i) % max(aa.R, 1);
     const WindowBase wbase = window_base(ia.start_pos, aa.W, max(aa.R, 1), i);
-    auto win_tile_load = [&](AttnRows<D> &rows, int j) {
+    auto win_tile_load = [&](WinRows &rows, int j) {
         const int p0 = 32 * j + c, p1 = 32 * j + 16 + c;
         const int s0 = p0 < nwin ? window_slot_at(wbase, ia.start_pos, aa.R, i, p0) : -1;
         const int s1 = p1 < nwin ? window_slot_at(wbase, ia.start_pos, aa.R, i, p1) : -1;
-        attn_tile_load_rows<D>(rows, aa.win_kv + ((size_t)b * aa.R + (s0 >= 0 ? s0 : own_slot)) * D, s0 >= 0,
-                               aa.win_kv + ((size_t)b * aa.R + (s1 >= 0 ? s1 : own_slot)) * D, s1 >= 0, g);
+        const size_t r0 = (size_t)b * aa.R + (s0 >= 0 ? s0 : own_slot);
+        const size_t r1 = (size_t)b * aa.R + (s1 >= 0 ? s1 : own_slot);
+        if constexpr (QKV)
+            kv_rows_load<D, kKvE4M3>(rows, aa.win_codes, aa.win_scales, r0, s0 >= 0, r1, s1 >= 0, g);
+        else
+            attn_tile_load_rows<D>(rows, aa.win_kv + r0 * D, s0 >= 0, aa.win_kv + r1 * D, s1 >= 0, g);
     };
-    AttnRows<D> wrows;
+    WinRows wrows;
     if (win_w < my_win) win_tile_load(wrows, m + win_w * f.team_size);
 
     // Attention list: positions of this chunk's rows to attend.  With a cut it holds the
@@ -347,13 +358,16 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     int *al = picks;
     int na = 0;
     // rows of listed tile tt; a lane past the list reads the first listed row instead
-    auto pick_tile_load = [&](AttnRows<D> &rows, int tt) {
+    auto pick_tile_load = [&](PickRows &rows, int tt) {
         const int p0 = 32 * tt + c, p1 = p0 + 16;
         const size_t rb = (size_t)b * aa.T_cap;
-        attn_tile_load_rows<D>(rows, aa.comp_kv + (rb + al[p0 < na ? p0 : 0]) * D, p0 < na,
-                               aa.comp_kv + (rb + al[p1 < na ? p1 : 0]) * D, p1 < na, g);
+        const size_t r0 = rb + al[p0 < na ? p0 : 0], r1 = rb + al[p1 < na ? p1 : 0];
+        if constexpr (QKV)
+            kv_rows_load<D, kKvE2M1>(rows, aa.comp_codes, aa.comp_scales, r0, p0 < na, r1, p1 < na, g);
+        else
+            attn_tile_load_rows<D>(rows, aa.comp_kv + r0 * D, p0 < na, aa.comp_kv + r1 * D, p1 < na, g);
     };
-    AttnRows<D> pre;  // this wave's first tile of listed rows, requested during selection
+    PickRows pre;  // this wave's first tile of listed rows, requested during selection
     bool have_pre = false;
 
     // ------------------------------------------------------------- phase S
@@ -615,20 +629,41 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         AttnState<D> st;
         attn_init<D>(st);
         uint32_t npk = 0;  // picks among this wave's tiles
-        if (win_w < my_win) attn_tile_compute<D>(st, qb, wrows, tile, aa.dv / 16, sl2, g, c);
+        // rows as the MFMA operands (quantised rows are dequantised here)
+        auto as_rows = [&](const auto &raw, AttnRows<D> &rows) {
+            if constexpr (QKV) {
+                using Raw = std::decay_t<decltype(raw)>;
+                if constexpr (std::is_same_v<Raw, KvRows<D, kKvE4M3>>)
+                    kv_rows_convert<D, kKvE4M3>(raw, rows);
+                else
+                    kv_rows_convert<D, kKvE2M1>(raw, rows);
+            } else {
+                rows = raw;
+            }
+        };
+        if (win_w < my_win) {
+            AttnRows<D> rows;
+            as_rows(wrows, rows);
+            attn_tile_compute<D>(st, qb, rows, tile, aa.dv / 16, sl2, g, c);
+        }
         // window tiles beyond the prefetched ones (more than 4 per member)
         for (int w = 4 + wave; w < my_win; w += 4) {
+            WinRows raw;
+            win_tile_load(raw, m + w * f.team_size);
             AttnRows<D> rows;
-            win_tile_load(rows, m + w * f.team_size);
+            as_rows(raw, rows);
             attn_tile_compute<D>(st, qb, rows, tile, aa.dv / 16, sl2, g, c);
         }
         for (int tt = wave; tt < pick_tiles; tt += 4) {
             const int p0 = 32 * tt + c, p1 = 32 * tt + 16 + c;
             AttnRows<D> rows;
-            if (tt == wave && have_pre)
-                rows = pre;
-            else
-                pick_tile_load(rows, tt);
+            if (tt == wave && have_pre) {
+                as_rows(pre, rows);
+            } else {
+                PickRows raw;
+                pick_tile_load(raw, tt);
+                as_rows(raw, rows);
+            }
             rows.valid[0] = __ballot(is_pick(p0));
             rows.valid[1] = __ballot(is_pick(p1));
             npk += __popcll(rows.valid[0] & 0xFFFFull) + __popcll(rows.valid[1] & 0xFFFFull);  // rows c of lanes c
@@ -787,15 +822,15 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
 
 // The kernels of one index-code format (and level-two masking or not): launch, and
 // co-resident workgroups per CU.
-template <int FMT, bool MASK>
+template <int FMT, bool MASK, bool QKV = false>
 struct FusedKernels {
     template <int D, int DI, int HT>
     static hipError_t cfg(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream) {
         if (f.cache_lds)
-            hipLaunchKernelGGL((fused_decode_kernel<D, DI, FMT, HT, true, MASK>), dim3(grid), dim3(kThreads),
+            hipLaunchKernelGGL((fused_decode_kernel<D, DI, FMT, HT, true, MASK, QKV>), dim3(grid), dim3(kThreads),
                                dyn_bytes, stream, f);
         else
-            hipLaunchKernelGGL((fused_decode_kernel<D, DI, FMT, HT, false, MASK>), dim3(grid), dim3(kThreads),
+            hipLaunchKernelGGL((fused_decode_kernel<D, DI, FMT, HT, false, MASK, QKV>), dim3(grid), dim3(kThreads),
                                dyn_bytes, stream, f);
         return hipGetLastError();
     }
@@ -825,9 +860,9 @@ struct FusedKernels {
     template <int D, int DI, int HT>
     static hipError_t occ(int *per_cu, size_t dyn, bool cached) {
         return cached ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                            per_cu, fused_decode_kernel<D, DI, FMT, HT, true, MASK>, kThreads, dyn)
+                            per_cu, fused_decode_kernel<D, DI, FMT, HT, true, MASK, QKV>, kThreads, dyn)
                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                            per_cu, fused_decode_kernel<D, DI, FMT, HT, false, MASK>, kThreads, dyn);
+                            per_cu, fused_decode_kernel<D, DI, FMT, HT, false, MASK, QKV>, kThreads, dyn);
     }
     template <int D, int DI>
     static hipError_t occ_di(int HT, int *per_cu, size_t dyn, bool cached) {

@@ -397,11 +397,14 @@ static FusedPlan step_fused_plan(const lit_step_args *s) {
     FusedPlan p{};
     p.ok = false;
     if (s->flags & LIT_STEP_UNFUSED) return p;
-    if (s->cand_out || step_quant_kv(s)) return p;
+    if (s->cand_out) return p;
     const bool masked = s->cand_in != nullptr;
     if (masked && (s->cand_k < 1 || s->cand_k > kFusedCandMaxApi)) return p;
+    // quantised KV runs fused when both sources are quantised and there is no masking
+    const bool qkv = step_quant_kv(s);
+    if (qkv && (masked || s->win_kv_format != LIT_KV_E4M3 || s->comp_kv_format != LIT_KV_E2M1)) return p;
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
-    return plan_fused(s->index_format, masked, s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D, s->dv,
+    return plan_fused(s->index_format, masked, qkv, s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D, s->dv,
                       s->W, keff);
 }
 
@@ -495,6 +498,9 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
             f.cand_k = s->cand_k;
             f.cand_bs = s->cand_block_size;
         }
+        if (step_quant_kv(s) && set_kv_formats(f.aa, s->win_kv_format, s->win_kv, s->win_kv_scales,
+                                               s->comp_kv_format, s->comp_kv, s->comp_kv_scales) != LIT_OK)
+            return LIT_E_UNSUPPORTED;
         f.spin_limit = 1u << 22;
         if ((e = launch_fused(f, fp, ws, s->state, hs)) != hipSuccess) return hip_status(e);
         for (int k = 1; k < 4; ++k)

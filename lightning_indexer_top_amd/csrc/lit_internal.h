@@ -214,8 +214,8 @@ struct FusedPlan {
     long ld;
     size_t dyn_bytes;
 };
-FusedPlan plan_fused(int fmt, bool masked, int B, int S, int start_pos, int ratio, int Hi, int Di, int D, int dv,
-                     int W, int keff);
+FusedPlan plan_fused(int fmt, bool masked, bool qkv, int B, int S, int start_pos, int ratio, int Hi, int Di, int D,
+                     int dv, int W, int keff);
 size_t fused_state_bytes(const FusedPlan &p);  // zero-filled before first use
 size_t fused_ws_bytes(const FusedPlan &p, int dv);
 hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream);
@@ -230,5 +230,10 @@ int fused_per_cu_e4m3(int D, int DI, int HT, size_t dyn_bytes, bool cached);
 int fused_per_cu_e2m1(int D, int DI, int HT, size_t dyn_bytes, bool cached);
 int fused_per_cu_e4m3_cand(int D, int DI, int HT, size_t dyn_bytes, bool cached);
 int fused_per_cu_e2m1_cand(int D, int DI, int HT, size_t dyn_bytes, bool cached);
+// The _qkv forms read quantised attention KV (AttnArgs win_codes / comp_codes).
+hipError_t launch_fused_e4m3_qkv(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
+hipError_t launch_fused_e2m1_qkv(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
+int fused_per_cu_e4m3_qkv(int D, int DI, int HT, size_t dyn_bytes, bool cached);
+int fused_per_cu_e2m1_qkv(int D, int DI, int HT, size_t dyn_bytes, bool cached);
 
 }  // namespace lit

@@ -231,21 +231,42 @@ __device__ inline float ue8m0_f32(uint32_t sb) {
     return __uint_as_float(sb ? sb << 23 : 0x00400000u);
 }
 
-// 8 dims of row `row` (dims 32s+8g..) of a quantised source, as 4 packed bf16 pairs.
+// Raw codes and scale byte of 8 dims (32s+8g..) of one row: loads only.
 template <int D, int KF>
-__device__ inline u32x4 kv_piece(const uint8_t *codes, const uint8_t *scales, size_t row, int s, int g) {
-    u32x4 out;
+struct KvPiece {
+    uint32_t w[KF == kKvE4M3 ? 2 : 1];
+    uint32_t sb;
+};
+
+template <int D, int KF>
+__device__ inline KvPiece<D, KF> kv_piece_load(const uint8_t *codes, const uint8_t *scales, size_t row, int s,
+                                               int g) {
+    KvPiece<D, KF> p;
     if constexpr (KF == kKvE4M3) {
         const u32x2 w = *reinterpret_cast<const u32x2 *>(codes + row * D + 32 * s + 8 * g);
-        const float sf = ue8m0_f32(scales[row * (D / 32) + s]);
-        out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sf, false));
-        out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sf, true));
-        out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sf, false));
-        out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sf, true));
+        p.w[0] = w[0];
+        p.w[1] = w[1];
+        p.sb = scales[row * (D / 32) + s];
     } else {
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(codes + row * (D / 2) + 16 * s + 4 * g);
-        const uint32_t sb = scales[row * (D / 16) + 2 * s + (g >> 1)];
-        const uint64_t sp = __builtin_bit_cast(uint64_t, __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.f, false));
+        p.w[0] = *reinterpret_cast<const uint32_t *>(codes + row * (D / 2) + 16 * s + 4 * g);
+        p.sb = scales[row * (D / 16) + 2 * s + (g >> 1)];
+    }
+    return p;
+}
+
+// The piece as 4 packed bf16 pairs (no loads).
+template <int D, int KF>
+__device__ inline u32x4 kv_piece_convert(const KvPiece<D, KF> &p) {
+    u32x4 out;
+    if constexpr (KF == kKvE4M3) {
+        const float sf = ue8m0_f32(p.sb);
+        out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(p.w[0], sf, false));
+        out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(p.w[0], sf, true));
+        out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(p.w[1], sf, false));
+        out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(p.w[1], sf, true));
+    } else {
+        const uint32_t w = p.w[0];
+        const uint64_t sp = __builtin_bit_cast(uint64_t, __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(p.sb, 1.f, false));
         const float sf = __uint_as_float((uint32_t)sp);
         uint64_t pr[4];  // byte k's two codes as f32
         pr[0] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 0));
@@ -260,6 +281,45 @@ __device__ inline u32x4 kv_piece(const uint8_t *codes, const uint8_t *scales, si
         }
     }
     return out;
+}
+
+// 8 dims of row `row` (dims 32s+8g..) of a quantised source, as 4 packed bf16 pairs.
+template <int D, int KF>
+__device__ inline u32x4 kv_piece(const uint8_t *codes, const uint8_t *scales, size_t row, int s, int g) {
+    return kv_piece_convert<D, KF>(kv_piece_load<D, KF>(codes, scales, row, s, g));
+}
+
+// A tile's quantised rows as loaded (converted when the tile is computed, so that the
+// loads stay in flight meanwhile).
+template <int D, int KF>
+struct KvRows {
+    KvPiece<D, KF> p[2][D / 32];
+    uint64_t valid[2];
+};
+
+// Unconditional loads of rows row0 / row1 (a lane off the tile passes a stand-in row its
+// wave attends anyway, with v0 / v1 false).
+template <int D, int KF>
+__device__ inline void kv_rows_load(KvRows<D, KF> &t, const uint8_t *codes, const uint8_t *scales, size_t row0,
+                                    bool v0, size_t row1, bool v1, int g) {
+    t.valid[0] = __ballot(v0);
+    t.valid[1] = __ballot(v1);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+        t.p[0][s] = kv_piece_load<D, KF>(codes, scales, row0, s, g);
+        t.p[1][s] = kv_piece_load<D, KF>(codes, scales, row1, s, g);
+    }
+}
+
+template <int D, int KF>
+__device__ inline void kv_rows_convert(const KvRows<D, KF> &t, AttnRows<D> &r) {
+    r.valid[0] = t.valid[0];
+    r.valid[1] = t.valid[1];
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+        r.r[0][s] = kv_piece_convert<D, KF>(t.p[0][s]);
+        r.r[1][s] = kv_piece_convert<D, KF>(t.p[1][s]);
+    }
 }
 
 // One tile's rows from a quantised source (row0 / row1 < 0: not part of the tile).

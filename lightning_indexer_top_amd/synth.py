@@ -177,12 +177,14 @@ def make_step(*, B: int, S: int, start_pos: int, ratio: int, Hi: int, Di: int, H
               R: Optional[int] = None, T_cap: Optional[int] = None, keys: str = "normal",
               sink: Optional[np.ndarray] = None, scale: Optional[float] = None,
               index_fmt: str = "e4m3", name: str = "custom", cand_topk_blocks: int = 0,
-              cand_block_size: int = 0, layers: int = 1, kv_fmt: str = "bf16") -> StepInputs:
+              cand_block_size: int = 0, layers: int = 1, kv_fmt: str = "bf16",
+              append_rd: int = 0) -> StepInputs:
     """Draw one step's inputs.  R defaults to the smallest window source that holds
     every needed position; T_cap defaults to the visible compressed row count.
     ``cand_topk_blocks`` / ``cand_block_size`` name a level-two workload's candidate
-    source (the bench builds the candidates), and ``layers`` the layers sharing one top-k
-    (the bench draws the other layers' inputs); they do not change the draw."""
+    source (the bench builds the candidates), ``layers`` the layers sharing one top-k
+    (the bench draws the other layers' inputs), and ``append_rd`` a step preceded by its
+    cache writes with that many rotated dims; they do not change the draw."""
     rng = np.random.Generator(np.random.PCG64(seed))
     end_pos = start_pos + S
     T = end_pos // ratio if ratio > 0 else 0
@@ -268,6 +270,11 @@ WORKLOADS = {
     # compressed KV fp4 e2m1 (e4m3 scale per 16), dequantised on gather
     "decode-16k-qkv": dict(B=8, S=1, start_pos=16383, ratio=2, Hi=64, Di=128, H=16, D=192,
                            W=128, index_topk=2048, seed=20261312, kv_fmt="quant"),
+    # the same step preceded by its cache writes: the new token into the compressor
+    # (completing a group, so a compressed row is written) and into the window ring
+    "decode-16k-qkv-append": dict(B=8, S=1, start_pos=16383, ratio=2, Hi=64, Di=128, H=16,
+                                  D=192, W=128, index_topk=2048, seed=20261322, kv_fmt="quant",
+                                  append_rd=64),
     "decode-128k-fp4": dict(B=2, S=1, start_pos=131071, ratio=4, Hi=64, Di=128, H=16, D=128,
                             W=128, index_topk=2048, seed=20261272, keys="mixture",
                             index_fmt="e2m1"),

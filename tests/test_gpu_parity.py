@@ -199,7 +199,7 @@ def test_sparse_attn_empty_lists_and_huge_sink(orc):
 # ---------------------------------------------------------------------------------
 # the fused step
 # ---------------------------------------------------------------------------------
-def _run_step(d, inp, flags=0, state=None):
+def _run_step(d, inp, flags=0, state=None, expect_fused=None):
     args, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
                                       k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
                                       comp_kv=d["comp_kv"], start_pos=inp.start_pos,
@@ -279,6 +279,17 @@ def test_step_small(orc, cfg, flags):
 def test_step_small_fp4(orc, cfg, flags):
     """The small steps with fp4 (e2m1) index queries and keys."""
     inp = synth.make_step(seed=5252 + cfg["start_pos"], index_fmt="e2m1", **cfg)
+    idx, out = _run_step(step_inputs_dev(inp), inp, flags)
+    _check_step(orc, inp, idx, out)
+
+
+@pytest.mark.parametrize("flags", MODES)
+@pytest.mark.parametrize("cfg", [STEP_SMALL[0], STEP_SMALL[2], STEP_SMALL[4], STEP_SMALL[5]],
+                         ids=lambda c: f"B{c['B']}S{c['S']}p{c['start_pos']}r{c['ratio']}")
+def test_step_small_qkv(orc, cfg, flags):
+    """The small steps with quantised attention KV (window e4m3, compressed e2m1), fused
+    and as kernels."""
+    inp = synth.make_step(seed=6262 + cfg["start_pos"], kv_fmt="quant", **cfg)
     idx, out = _run_step(step_inputs_dev(inp), inp, flags)
     _check_step(orc, inp, idx, out)
 
