@@ -394,6 +394,10 @@ def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int,
         # hipEvent_t handles (e.g. torch.cuda.Event(...).cuda_event after one record)
         for k, ev in enumerate(stage_events):
             a.stage_events[k] = ev or None
+    # the struct holds raw addresses: keep the tensors behind them alive with it, or a
+    # caller passing temporaries would have their memory reused by the next allocation
+    a._keep = (q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, sink, topk_idx, out, cand_in, cand_out,
+               win_sc, comp_sc)
     return a, topk_idx, out
 
 
@@ -422,6 +426,7 @@ def attach_state(args: lit_step_args, state: Optional[torch.Tensor] = None, devi
         state = torch.zeros(need, dtype=torch.uint8, device=device)
     args.state = state.data_ptr()
     args.state_bytes = state.numel() * state.element_size()
+    args._state = state  # kept alive with the struct that points at it
     return state
 
 

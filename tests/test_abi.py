@@ -248,3 +248,25 @@ def test_step_state_sizes(lib):
     assert n == 0 or n >= 256 + 8 * (32 + 4096 * 4)
     args.flags = 1
     assert lib.lit_sparse_step_state_bytes(ctypes.byref(args)) == 0
+
+
+def test_step_args_keep_their_tensors_alive():
+    """make_step_args stores raw addresses; the struct must keep the tensors behind them
+    alive, or temporaries passed by a caller would be freed and their memory reused."""
+    import gc
+    import weakref
+    import torch
+    t = lambda *shape, dt=torch.uint8: torch.zeros(*shape, dtype=dt)  # noqa: E731
+    q8 = t(1, 1, 16, 64)
+    ref = weakref.ref(q8)
+    args, idx, out = B.make_step_args(
+        q8=q8, q_sc=t(1, 1, 16, 2), w=t(1, 1, 16, dt=torch.float32), k8=t(1, 512, 64),
+        k_sc=t(1, 512, 2), q=t(1, 1, 16, 128, dt=torch.bfloat16),
+        win_kv=t(1, 128, 128, dt=torch.bfloat16), comp_kv=t(1, 512, 128, dt=torch.bfloat16),
+        start_pos=1023, ratio=2, index_topk=64, W=128, scale=0.088)
+    del q8
+    gc.collect()
+    assert ref() is not None and args.q8 == ref().data_ptr()
+    del args
+    gc.collect()
+    assert ref() is None
