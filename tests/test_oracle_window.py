@@ -1,30 +1,36 @@
 """Pins for the oracle's window row lists.
 
 Definition: DeepSeek-V4.1-Flash-NVFP4 model.py, get_window_topk_idxs and
-Attention._window_kv.  The expected lists below were derived by evaluating that
-function's two branches by hand for the given (window, seqlen, start_pos):
-
-* decode, window 4, start 2: oldest slot = 2 % 4 + 1 = 3; slots 3, 0, 1, 2; slot 3 is
-  past start 2, so it is -1 (ring still filling);
-* decode, window 4, start 3: slots 0..3, all filled;
-* decode, window 4, start 5: oldest slot 2; slots 2, 3, 0, 1;
-* prefill, window 3, 5 tokens: row i lists max(0, i-2) + (0, 1, 2), entries past i
-  become -1;
-* prefill, window 4, 2 tokens: width min(2, 4) = 2.
+Attention._window_kv.  The expected lists in ``tests/golden/window_derived.txt`` were
+derived by evaluating that function's two branches by hand for the given (window,
+seqlen, start_pos): decode cases at starts 2, 3 and 5 with a window of 4 (the ring
+filling, full, and wrapped) and prefill cases of 5 tokens with a window of 3 and 2 tokens
+with a window of 4.
 
 A brute-force set check covers the chunk generalisation (start > 0, several queries).
 """
+import os
+
 import numpy as np
 import pytest
 
-DERIVED = [
-    # (W, S, start_pos, expected rows)
-    (4, 1, 2, [[-1, 0, 1, 2]]),
-    (4, 1, 3, [[0, 1, 2, 3]]),
-    (4, 1, 5, [[2, 3, 0, 1]]),
-    (3, 5, 0, [[0, -1, -1], [0, 1, -1], [0, 1, 2], [1, 2, 3], [2, 3, 4]]),
-    (4, 2, 0, [[0, -1], [0, 1]]),
-]
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "window_derived.txt")
+
+
+def _load_derived():
+    cases = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        head, body = line.split("|")
+        W, S, start_pos = (int(x) for x in head.split())
+        rows = [[int(v) for v in row.split(",")] for row in body.split(";")]
+        cases.append((W, S, start_pos, rows))
+    return cases
+
+
+DERIVED = _load_derived()
 
 
 @pytest.mark.parametrize("W,S,start_pos,rows", DERIVED)
