@@ -702,3 +702,58 @@ def test_window_append_steps(orc):
     assert np.array_equal(sg, osc)
     mism = int((cg != oc).sum())
     assert mism <= 2, f"{mism} window codes differ"
+
+
+# ---------------------------------------------------------------------------------
+# the fused kernel's re-reading selection form (more than 8192 visible rows) with level-two
+# masking and with quantised KV
+# ---------------------------------------------------------------------------------
+def test_step_level_two_rereading_form(orc):
+    """16384 rows per query (the re-reading form) as a level-two layer, fused, against
+    the oracle; the candidates keep 1024 of 2048 blocks."""
+    kw = dict(B=2, S=1, start_pos=65535, ratio=4, Hi=64, Di=128, H=16, D=128, W=128,
+              index_topk=1024, keys="mixture")
+    src = synth.make_step(seed=91, **kw)
+    inp = synth.make_step(seed=92, **kw)
+    ref_src = orc.step(src, cand_topk_blocks=1024, cand_block_size=8)
+    blocks = ref_src["cand"]
+    d = step_inputs_dev(inp)
+    args, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
+                                      k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
+                                      comp_kv=d["comp_kv"], start_pos=inp.start_pos,
+                                      ratio=inp.ratio, index_topk=inp.index_topk, W=inp.W,
+                                      scale=inp.scale, cand_in=dev(blocks), cand_block_size=8)
+    state = L.attach_state(args)
+    assert state is not None, "expected the fused form"
+    L.lit_sparse_step(args, L.step_workspace(args))
+    torch.cuda.synchronize()
+    assert L.state_error(state) == 0
+    ref = orc.step(inp, cand_in=blocks, cand_block_size=8)
+    g_idx, g_out = idx.cpu().numpy(), bf16_host(out)
+    for b in range(2):
+        assert set(g_idx[b, 0] // 8) <= set(blocks[b, 0])
+        ok, why = topk_sets_agree(ref["masked"][b, 0], ref["idx"][b, 0], g_idx[b, 0])
+        assert ok, f"sequence {b}: {why}"
+        if set(ref["idx"][b, 0]) == set(g_idx[b, 0]):
+            assert np.abs(g_out[b, 0] - ref["out"][b, 0]).max() <= ATTN_TOL
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_step_qkv_rereading_form(orc, fmt):
+    """Quantised attention KV with 16384 rows per query (the re-reading selection form),
+    fused, against the oracle."""
+    inp = synth.make_step(B=2, S=1, start_pos=65535, ratio=4, Hi=64, Di=128, H=16, D=128, W=128,
+                          index_topk=1024, seed=93, kv_fmt="quant", index_fmt=fmt)
+    d = step_inputs_dev(inp)
+    args, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
+                                      k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
+                                      comp_kv=d["comp_kv"], start_pos=inp.start_pos,
+                                      ratio=inp.ratio, index_topk=inp.index_topk, W=inp.W,
+                                      scale=inp.scale, fmt=fmt, win_fmt="e4m3", win_sc=d["win_sc"],
+                                      comp_fmt="e2m1", comp_sc=d["comp_sc"])
+    state = L.attach_state(args)
+    assert state is not None, "expected the fused form"
+    L.lit_sparse_step(args, L.step_workspace(args))
+    torch.cuda.synchronize()
+    assert L.state_error(state) == 0
+    _check_step(orc, inp, idx, out)
