@@ -260,6 +260,17 @@ def main() -> int:
             sc = L.lit_indexer_scores(s_["q8"], s_["q_sc"], s_["w"], s_["k8"], s_["k_sc"],
                                       spec["start_pos"], spec["ratio"], fmt=fmt)
             cands[j] = L.lit_candidate_blocks(sc, spec["start_pos"], spec["ratio"], cand_kb, cand_bs)
+    nl = spec.get("layers", 1)
+    if nl > 1:
+        # layers that reuse the step's top-k: their own queries and window KV, stacked after
+        # the source layer's (one step call runs them all)
+        g_ = torch.Generator(device=dev)
+        g_.manual_seed(spec["seed"] + 7)
+        for d in insts:
+            d["q"] = torch.cat([d["q"][None], torch.randn(nl - 1, *d["q"].shape, device=dev,
+                                                          generator=g_).to(torch.bfloat16)])
+            d["win_kv"] = torch.cat([d["win_kv"][None], torch.randn(nl - 1, *d["win_kv"].shape, device=dev,
+                                                                    generator=g_).to(torch.bfloat16)])
     for j, d in enumerate(insts):
         a, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
                                        k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
@@ -294,7 +305,6 @@ def main() -> int:
         torch.cuda.synchronize()
         return g
 
-    nl = spec.get("layers", 1)
     ard = spec.get("append_rd", 0)
     if ard:
         # the step's cache writes first: the new token into the compressor (the group
@@ -319,28 +329,6 @@ def main() -> int:
             L.lit_window_append(app[j]["win"], table, ard, d["win_kv"], d["win_sc"], spec["start_pos"])
 
         step_calls = [(lambda j=j: (append_call(j), L.lit_sparse_step(argv[j], ws))) for j in range(n_inst)]
-    elif nl > 1:
-        # the layers that reuse this layer's top-k: their own queries and window KV, the
-        # shared compressed KV and list, attention in one call after the step
-        g_ = torch.Generator(device=dev)
-        g_.manual_seed(spec["seed"] + 7)
-        more = [dict(q=torch.randn(nl - 1, spec["B"], spec["S"], spec["H"], spec["D"], device=dev,
-                                   generator=g_).to(torch.bfloat16),
-                     win=torch.randn(nl - 1, spec["B"], insts[j]["R"], spec["D"], device=dev,
-                                     generator=g_).to(torch.bfloat16),
-                     out=torch.empty(nl - 1, spec["B"], spec["S"], spec["H"], spec["D"], device=dev,
-                                     dtype=torch.bfloat16)) for j in range(n_inst)]
-        lws = torch.empty(max(256, L.library().lit_sparse_attn_layers_workspace_bytes(
-            nl - 1, spec["B"], spec["S"], spec["H"], spec["D"],
-            L.lit_window_width(spec["S"], spec["start_pos"], spec["W"]), keep[0][0].shape[-1])),
-            dtype=torch.uint8, device=dev)
-
-        def layers_call(j):
-            L.lit_sparse_attn_layers(more[j]["q"], more[j]["win"], None, insts[j]["comp_kv"], keep[j][0],
-                                     None, spec["D"] ** -0.5, out=more[j]["out"], ws=lws,
-                                     window=spec["W"], start_pos=spec["start_pos"])
-
-        step_calls = [(lambda j=j: (L.lit_sparse_step(argv[j], ws), layers_call(j))) for j in range(n_inst)]
     else:
         step_calls = [(lambda j=j: L.lit_sparse_step(argv[j], ws)) for j in range(n_inst)]
     reps, rem = divmod(K, n_inst)
@@ -390,9 +378,12 @@ def main() -> int:
                                                     spec["index_topk"], cands[j], cand_bs,
                                                     idx=keep[j][0]))
                  for j in range(n_inst)],
+        # (the first layer's attention when several layers share the top-k)
         "attention": [(lambda j=j: L.lit_sparse_attn_fmt(
-            insts[j]["q"], insts[j]["win_kv"], win, insts[j]["comp_kv"], keep[j][0], None,
-            spec["D"] ** -0.5, out=keep[j][1], ws=ws, **kv_args(insts[j]))) for j in range(n_inst)],
+            insts[j]["q"] if nl == 1 else insts[j]["q"][0],
+            insts[j]["win_kv"] if nl == 1 else insts[j]["win_kv"][0], win, insts[j]["comp_kv"],
+            keep[j][0], None, spec["D"] ** -0.5, out=keep[j][1] if nl == 1 else keep[j][1][0], ws=ws,
+            **kv_args(insts[j]))) for j in range(n_inst)],
     }
     if cand_kb:
         # the candidate source's level one (not part of this layer's step; reported beside it)
@@ -428,21 +419,7 @@ def main() -> int:
         return e0.elapsed_time(e1) * 1e3 / (stage_reps * len(calls))
 
     step_gbps = sb["step"] / (ms_per_step * 1e-3) / 1e9
-    if fused and nl > 1:
-        # the source layer's fused kernel and the other layers' attention, timed apart
-        stages_us["fused_step"] = timed_graph_us([(lambda j=j: L.lit_sparse_step(argv[j], ws))
-                                                  for j in range(n_inst)])
-        stages_us["layers"] = timed_graph_us([(lambda j=j: layers_call(j)) for j in range(n_inst)])
-        log(f"[bench] fused step {stages_us['fused_step']:.2f} us, other layers {stages_us['layers']:.2f} us")
-        one = step_bytes({k: v for k, v in spec.items() if k != "layers"})["step"]
-        kv_rows = spec["B"] * keep[0][0].shape[-1] * 2 * spec["D"]
-        if stages_us["layers"] > stages_us["fused_step"]:
-            dom, kname, ksrc = "layers", "sparse_attn_kernel+attn_merge_kernel", "attention.hip"
-            dom_us, dom_bytes = stages_us["layers"], sb["step"] - one + kv_rows
-        else:
-            dom, kname, ksrc = "step", "fused_decode_kernel", fused_sources(spec)
-            dom_us, dom_bytes = stages_us["fused_step"], one
-    elif fused:
+    if fused:
         # one kernel per step: its average duration is the event-timed region / K
         dom, kname, ksrc = "step", "fused_decode_kernel", fused_sources(spec)
         dom_us = gpu_ms * 1e3 / K
@@ -493,7 +470,7 @@ def main() -> int:
                    "index_topk": spec["index_topk"], "input_instances": n_inst,
                    "timing": "HIP graph replay over rotating cold-cache instances",
                    "step_form": ("fused single kernel" if fused else "indexer, top-k, attention kernels")
-                   + (f" + one attention call for {nl - 1} more layers" if nl > 1 else "")
+                   + (f", {nl} layers over one top-k" if nl > 1 else "")
                    + (", after the compressor and window-ring writes" if ard else "")},
         "hbm": {"step_bytes": sb["step"], "achieved_gbps": round(step_gbps, 1),
                 "peak_gbps": HBM_PEAK_GBPS, "frac": round(step_gbps / HBM_PEAK_GBPS, 4)},

@@ -425,6 +425,12 @@ typedef struct lit_step_args {
     const uint8_t *win_kv_scales;
     int comp_kv_format;
     const uint8_t *comp_kv_scales;
+    /* layers sharing this step's top-k (0 or 1: one).  With layers = L > 1, q, win_kv
+     * (and win_kv_scales), sink and out hold L layers back to back -- q [L,B,S,H,D],
+     * win_kv [L,B,R,*], sink [L,H], out [L,B,S,H,dv] -- and every layer attends over the
+     * one top-k list and comp_kv ([V4.1] index_source_layers / kv_source_layers).  They
+     * run fused with bf16 KV and no candidates, else as kernels. */
+    int layers;
 } lit_step_args;
 
 lit_status lit_sparse_step(const lit_step_args *args, void *ws, size_t ws_bytes, void *stream);

@@ -17,7 +17,7 @@ BUILD = os.path.join(os.path.dirname(HERE), "_build", "lit")
 LIB = os.path.join(HERE, "liblit.so")
 SOURCES = ["lit_api.hip", "indexer.hip", "topk.hip", "attention.hip", "produce.hip", "fused_decode.hip",
            "fused_e4m3.hip", "fused_e2m1.hip", "fused_e4m3_cand.hip", "fused_e2m1_cand.hip",
-           "fused_e4m3_qkv.hip", "fused_e2m1_qkv.hip"]
+           "fused_e4m3_qkv.hip", "fused_e2m1_qkv.hip", "fused_e4m3_layers.hip", "fused_e2m1_layers.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # MFMA results are written to VGPRs rather than AGPRs: no accumulator reads before the

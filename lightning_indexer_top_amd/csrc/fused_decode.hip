@@ -23,13 +23,16 @@ int device_cus(int dev) {
 }
 
 // Co-resident workgroups of the fused kernel on the current device.
-int max_resident(int fmt, bool masked, bool qkv, int D, int DI, int HT, size_t dyn, bool cached) {
+int max_resident(int fmt, bool masked, bool qkv, bool layers, int D, int DI, int HT, size_t dyn, bool cached) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     const int cus = device_cus(dev);
     if (cus <= 0) return 0;
     int per_cu;
-    if (qkv)
+    if (layers)
+        per_cu = fmt == kFmtE2M1 ? fused_per_cu_e2m1_layers(D, DI, HT, dyn, cached)
+                                 : fused_per_cu_e4m3_layers(D, DI, HT, dyn, cached);
+    else if (qkv)
         per_cu = fmt == kFmtE2M1 ? fused_per_cu_e2m1_qkv(D, DI, HT, dyn, cached)
                                  : fused_per_cu_e4m3_qkv(D, DI, HT, dyn, cached);
     else if (fmt == kFmtE2M1)
@@ -41,8 +44,8 @@ int max_resident(int fmt, bool masked, bool qkv, int D, int DI, int HT, size_t d
 
 }  // namespace
 
-FusedPlan plan_fused(int fmt, bool masked, bool qkv, int B, int S, int start_pos, int ratio, int Hi, int Di, int D,
-                     int dv, int W, int keff) {
+FusedPlan plan_fused(int fmt, bool masked, bool qkv, bool layers, int B, int S, int start_pos, int ratio, int Hi,
+                     int Di, int D, int dv, int W, int keff) {
     FusedPlan p{};
     p.ok = false;
     const int n_teams = B * S;
@@ -65,12 +68,12 @@ FusedPlan plan_fused(int fmt, bool masked, bool qkv, int B, int S, int start_pos
         if (!p.cache_lds) {
             // the bins (padded to 16 bytes), then kCandCap candidate positions
             const size_t with_bins = dyn + (size_t)(T + 7) / 8 * 16 + (size_t)kCandCap * 4;
-            if (max_resident(fmt, masked, qkv, D, Di, Hi / 16, with_bins, false) > 0) {
+            if (max_resident(fmt, masked, qkv, layers, D, Di, Hi / 16, with_bins, false) > 0) {
                 dyn = with_bins;
                 p.lds_bins = true;
             }
         }
-        cap = max_resident(fmt, masked, qkv, D, Di, Hi / 16, dyn, p.cache_lds);
+        cap = max_resident(fmt, masked, qkv, layers, D, Di, Hi / 16, dyn, p.cache_lds);
         const long team = (T + chunk - 1) / chunk;
         if (cap > 0 && team <= kThreads && (long)n_teams * team <= cap) {
             p.team_size = (int)team;
@@ -99,9 +102,9 @@ size_t fused_state_bytes(const FusedPlan &p) {
 
 static int slot_floats(int dv) { return (kHeads * dv + 2 * kHeads + 63) / 64 * 64; }  // 16-byte multiple
 
-size_t fused_ws_bytes(const FusedPlan &p, int dv) {
-    return (size_t)p.n_teams * p.ld * 4 + 256 +                              // team scores
-           (size_t)p.n_teams * p.team_size * slot_floats(dv) * 4 + 256;      // partial states
+size_t fused_ws_bytes(const FusedPlan &p, int dv, int layers) {
+    return (size_t)p.n_teams * p.ld * 4 + 256 +                                      // team scores
+           (size_t)p.n_teams * p.team_size * layers * slot_floats(dv) * 4 + 256;     // partial states
 }
 
 hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream) {
@@ -115,7 +118,7 @@ hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, 
         return r;
     };
     f.scores = (float *)bump((size_t)p.n_teams * p.ld * 4);
-    f.part = (float *)bump((size_t)p.n_teams * p.team_size * slot_floats(f.aa.dv) * 4);
+    f.part = (float *)bump((size_t)p.n_teams * p.team_size * f.aa.L * slot_floats(f.aa.dv) * 4);
     f.slot_floats = slot_floats(f.aa.dv);
     f.team_size = p.team_size;
     f.chunk = p.chunk;
@@ -126,6 +129,9 @@ hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, 
     f.lds_bins = p.lds_bins;
     f.bins_words = (int)((p.ld + 7) / 8 * 4);  // 32-bit words of the padded bins
     const bool masked = f.cand != nullptr;
+    if (f.aa.L > 1)  // several layers (bf16 KV, never with masking)
+        return f.ia.fmt == kFmtE2M1 ? launch_fused_e2m1_layers(f, p.grid, p.dyn_bytes, stream)
+                                    : launch_fused_e4m3_layers(f, p.grid, p.dyn_bytes, stream);
     if (f.aa.win_fmt != kKvBf16 || f.aa.comp_fmt != kKvBf16)  // quantised KV (never with masking)
         return f.ia.fmt == kFmtE2M1 ? launch_fused_e2m1_qkv(f, p.grid, p.dyn_bytes, stream)
                                     : launch_fused_e4m3_qkv(f, p.grid, p.dyn_bytes, stream);

@@ -1,9 +1,9 @@
 // fused_kernel.h -- the whole sparse-attention step for decode-sized batches in one
 // launch: indexer scores -> exact top-k -> gather attention -> merge.  Included by one
 // source file per index-code format and variant (fused_e4m3.hip, fused_e2m1.hip, their
-// _cand forms for level-two layers of the two-level top-k and _qkv forms for quantised
-// attention KV), each of which instantiates its kernels; fused_decode.hip plans and
-// dispatches.
+// _cand forms for level-two layers of the two-level top-k, _qkv forms for quantised
+// attention KV and _layers forms for several layers over one top-k), each of which
+// instantiates its kernels; fused_decode.hip plans and dispatches.
 //
 // What is computed is exactly what indexer.hip, topk.hip and attention.hip compute
 // (DeepSeek-V4.1-Flash-NVFP4 inference/model.py, Indexer.forward and
@@ -204,7 +204,9 @@ __device__ inline uint32_t wg_sum(uint32_t v, uint32_t *red) {
 // -inf before the selection.
 // QKV: the attention KV sources are quantised (window e4m3 / ue8m0-32, compressed
 // e2m1 / e4m3-16); rows are loaded as codes and dequantised when their tile is computed.
-template <int D, int DI, int FMT, int HT, bool CACHED, bool MASK, bool QKV>
+// LAYERS: several layers share the step's top-k (AttnArgs::L of them attend); without it
+// the layer count is the constant 1.
+template <int D, int DI, int FMT, int HT, bool CACHED, bool MASK, bool QKV, bool LAYERS>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     using WinRows = std::conditional_t<QKV, KvRows<D, kKvE4M3>, AttnRows<D>>;
     using PickRows = std::conditional_t<QKV, KvRows<D, kKvE2M1>, AttnRows<D>>;
@@ -338,19 +340,22 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     // attended), so that the loads need no branch
     const int own_slot = (ia.start_pos + i) % max(aa.R, 1);
     const WindowBase wbase = window_base(ia.start_pos, aa.W, max(aa.R, 1), i);
-    auto win_tile_load = [&](WinRows &rows, int j) {
+    // (layer l's window source: the layers sharing this top-k each have their own)
+    auto win_tile_load = [&](WinRows &rows, int j, int l) {
         const int p0 = 32 * j + c, p1 = 32 * j + 16 + c;
         const int s0 = p0 < nwin ? window_slot_at(wbase, ia.start_pos, aa.R, i, p0) : -1;
         const int s1 = p1 < nwin ? window_slot_at(wbase, ia.start_pos, aa.R, i, p1) : -1;
         const size_t r0 = (size_t)b * aa.R + (s0 >= 0 ? s0 : own_slot);
         const size_t r1 = (size_t)b * aa.R + (s1 >= 0 ? s1 : own_slot);
         if constexpr (QKV)
-            kv_rows_load<D, kKvE4M3>(rows, aa.win_codes, aa.win_scales, r0, s0 >= 0, r1, s1 >= 0, g);
+            kv_rows_load<D, kKvE4M3>(rows, aa.win_codes + (size_t)l * aa.win_ls,
+                                     aa.win_scales + (size_t)l * aa.win_ls / 32, r0, s0 >= 0, r1, s1 >= 0, g);
         else
-            attn_tile_load_rows<D>(rows, aa.win_kv + r0 * D, s0 >= 0, aa.win_kv + r1 * D, s1 >= 0, g);
+            attn_tile_load_rows<D>(rows, aa.win_kv + (size_t)l * aa.win_ls + r0 * D, s0 >= 0,
+                                   aa.win_kv + (size_t)l * aa.win_ls + r1 * D, s1 >= 0, g);
     };
     WinRows wrows;
-    if (win_w < my_win) win_tile_load(wrows, m + win_w * f.team_size);
+    if (win_w < my_win) win_tile_load(wrows, m + win_w * f.team_size, 0);
 
     // Attention list: positions of this chunk's rows to attend.  With a cut it holds the
     // chunk's scores in bins >= the cut's bin (sure picks and candidates, ascending); the
@@ -612,9 +617,15 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         na = n;
         __syncthreads();
     }
+    // partial states: one slot per (member, layer), member-major
+    const int NL = LAYERS ? aa.L : 1;
     const int slot_bytes = f.slot_floats * 4;
-    const rsrc_t part_r = make_rsrc(f.part + (size_t)q * f.team_size * f.slot_floats,
-                                    (uint32_t)(f.team_size * slot_bytes));
+    const rsrc_t part_r = make_rsrc(f.part + (size_t)q * f.team_size * NL * f.slot_floats,
+                                    (uint32_t)(f.team_size * NL * slot_bytes));
+    // Layer 0 (this step's own layer) attends here, with the rows requested during the
+    // selection; further layers that share the top-k (their own queries, window rows and
+    // sink, the same picked rows) follow in a block of their own below, so that the
+    // one-layer step keeps this code as it is.
     {
         const float sl2 = aa.scale * kLog2e;
         uint16_t *tile = attn_lds + wave * 32 * LD;
@@ -649,7 +660,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         // window tiles beyond the prefetched ones (more than 4 per member)
         for (int w = 4 + wave; w < my_win; w += 4) {
             WinRows raw;
-            win_tile_load(raw, m + w * f.team_size);
+            win_tile_load(raw, m + w * f.team_size, 0);
             AttnRows<D> rows;
             as_rows(raw, rows);
             attn_tile_compute<D>(st, qb, rows, tile, aa.dv / 16, sl2, g, c);
@@ -693,7 +704,92 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         __syncthreads();
         // this member's state: O [16][dv] then (M, L) [16], 16-byte coherent stores
         const int qdv = aa.dv / 4;
-        const uint32_t my_off = (uint32_t)(m * slot_bytes);
+        const uint32_t my_off = (uint32_t)(m * NL * slot_bytes);
+        for (int e = tid; e < kHeads * qdv; e += kThreads) {
+            const int h = e / qdv;
+            const int d = 4 * (e - h * qdv);
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(&ow[(w * kHeads + h) * attn_ow_ld(aa.dv) + d]);
+                O += hf[w * kHeads + h] * x;
+            }
+            st128_agent(part_r, my_off + (uint32_t)(h * aa.dv + d) * 4u, __builtin_bit_cast(u32x4, O));
+        }
+        if (tid < kHeads / 2) {
+            const int h = 2 * tid;
+            st128_agent(part_r, my_off + (uint32_t)(kHeads * aa.dv + 2 * h) * 4u,
+                        u32x4{__float_as_uint(hm[h]), __float_as_uint(hl[h]), __float_as_uint(hm[h + 1]),
+                              __float_as_uint(hl[h + 1])});
+        }
+    }
+    // the further layers (each: its own queries and window rows, the shared picked rows back
+    // from the cache), the same pass without the prefetched rows or the pick count
+    for (int l = 1; l < NL; ++l) {
+        __syncthreads();  // the previous layer's wave states in LDS have been read
+        bf16x8 ql[D / 32];
+        load_q_operands<D>(ql, aa.q + (size_t)l * aa.q_ls, (size_t)q, g, c);
+        const float sl2 = aa.scale * kLog2e;
+        uint16_t *tile = attn_lds + wave * 32 * LD;
+        AttnState<D> st;
+        attn_init<D>(st);
+        auto compute = [&](const auto &raw, uint64_t v0, uint64_t v1, bool mask) {
+            AttnRows<D> rows;
+            if constexpr (QKV) {
+                using Raw = std::decay_t<decltype(raw)>;
+                if constexpr (std::is_same_v<Raw, KvRows<D, kKvE4M3>>)
+                    kv_rows_convert<D, kKvE4M3>(raw, rows);
+                else
+                    kv_rows_convert<D, kKvE2M1>(raw, rows);
+            } else {
+                rows = raw;
+            }
+            if (mask) {
+                rows.valid[0] = v0;
+                rows.valid[1] = v1;
+            }
+            attn_tile_compute<D>(st, ql, rows, tile, aa.dv / 16, sl2, g, c);
+        };
+        for (int w = wave; w < my_win; w += 4) {
+            WinRows raw;
+            win_tile_load(raw, m + w * f.team_size, l);
+            compute(raw, 0, 0, false);
+        }
+        for (int tt = wave; tt < (na + 31) / 32; tt += 4) {
+            const int p0 = 32 * tt + c, p1 = 32 * tt + 16 + c;
+            auto is_pick = [&](int p) {
+                if (p >= na) return false;
+                if (!select) return true;
+                const int pos = al[p];
+                const uint32_t k = order_key(sc[pos - c0]);
+                return k > kstar || (k == kstar && pos <= pstar);
+            };
+            PickRows raw;
+            pick_tile_load(raw, tt);
+            compute(raw, __ballot(is_pick(p0)), __ballot(is_pick(p1)), true);
+        }
+        float *ow = reinterpret_cast<float *>(attn_lds);
+        __syncthreads();
+        attn_wave_publish<D>(st, ow, wm, wl, wave, aa.dv, g, c);
+        __syncthreads();
+        if (tid < kHeads) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w * kHeads + tid]);
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float mw = wm[w * kHeads + tid];
+                const float fw = (mw == -INFINITY || M == -INFINITY) ? 0.f : exp2f(mw - M);
+                hf[w * kHeads + tid] = fw;
+                L += fw * wl[w * kHeads + tid];
+            }
+            hm[tid] = M;
+            hl[tid] = L;
+        }
+        __syncthreads();
+        const int qdv = aa.dv / 4;
+        const uint32_t my_off = (uint32_t)((m * NL + l) * slot_bytes);
         for (int e = tid; e < kHeads * qdv; e += kThreads) {
             const int h = e / qdv;
             const int d = 4 * (e - h * qdv);
@@ -725,7 +821,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         // the (max, normaliser) pair of a stride of the slots, all in one round trip, and
         // the group combines its lanes with DPP exchanges.
         const int qdv = aa.dv / 4;
-        const int n_out = kHeads * qdv;
+        const int n_out = NL * kHeads * qdv;  // (layer, head, dim quad)
         const int per = (n_out + f.team_size - 1) / f.team_size;
         const int e0 = m * per;
         const int items = max(0, min(e0 + per, n_out) - e0);
@@ -737,9 +833,11 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             const int item = i0 + tid / lpi, sub = tid % lpi;
             const bool act = item < items;
             const int e = e0 + (act ? item : 0);
-            const int h = e / qdv;
-            const int d = 4 * (e - h * qdv);
-            const float *mlp = f.part + (size_t)q * f.team_size * f.slot_floats + kHeads * aa.dv + 2 * h;
+            const int ly = e / (kHeads * qdv);
+            const int eh = e - ly * kHeads * qdv;
+            const int h = eh / qdv;
+            const int d = 4 * (eh - h * qdv);
+            const float *mlp = f.part + ((size_t)q * f.team_size * NL + ly) * f.slot_floats + kHeads * aa.dv + 2 * h;
             constexpr int kU = 8;
             f32x4 O = {0.f, 0.f, 0.f, 0.f};
             float M = -INFINITY, L = 0.f;
@@ -750,9 +848,9 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                 for (int u = 0; u < kU; ++u) {
                     const int sl = s0 + u * lpi;
                     const bool ok = act && sl < f.team_size;
-                    o[u] = ok ? ld128_agent(part_r, (uint32_t)(sl * slot_bytes + (h * aa.dv + d) * 4))
+                    o[u] = ok ? ld128_agent(part_r, (uint32_t)((sl * NL + ly) * slot_bytes + (h * aa.dv + d) * 4))
                               : u32x4{0u, 0u, 0u, 0u};
-                    ml[u] = ok ? ld64_agent(reinterpret_cast<const uint64_t *>(mlp + (size_t)sl * f.slot_floats))
+                    ml[u] = ok ? ld64_agent(reinterpret_cast<const uint64_t *>(mlp + (size_t)sl * NL * f.slot_floats))
                                : pack2(-INFINITY, 0.f);
                 }
                 float Mn = M;
@@ -791,8 +889,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             if (lpi > 2) level([](float v) { return dpp_f<0x4E>(v); });   // quad_perm [2,3,0,1]
             if (lpi > 1) level([](float v) { return dpp_f<0xB1>(v); });   // quad_perm [1,0,3,2]
             if (act && sub == 0) {
-                uint16_t *dst = aa.out + ((size_t)q * kHeads + h) * aa.dv + d;
-                *reinterpret_cast<u32x2 *>(dst) = attn_finish4(O, M, L, aa.sink, h);
+                uint16_t *dst = aa.out + (size_t)ly * aa.out_ls + ((size_t)q * kHeads + h) * aa.dv + d;
+                *reinterpret_cast<u32x2 *>(dst) = attn_finish4(O, M, L, aa.sink ? aa.sink + ly * kHeads : nullptr, h);
             }
         }
     }
@@ -822,16 +920,16 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
 
 // The kernels of one index-code format (and level-two masking or not): launch, and
 // co-resident workgroups per CU.
-template <int FMT, bool MASK, bool QKV = false>
+template <int FMT, bool MASK, bool QKV = false, bool LAYERS = false>
 struct FusedKernels {
     template <int D, int DI, int HT>
     static hipError_t cfg(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream) {
         if (f.cache_lds)
-            hipLaunchKernelGGL((fused_decode_kernel<D, DI, FMT, HT, true, MASK, QKV>), dim3(grid), dim3(kThreads),
-                               dyn_bytes, stream, f);
+            hipLaunchKernelGGL((fused_decode_kernel<D, DI, FMT, HT, true, MASK, QKV, LAYERS>), dim3(grid),
+                               dim3(kThreads), dyn_bytes, stream, f);
         else
-            hipLaunchKernelGGL((fused_decode_kernel<D, DI, FMT, HT, false, MASK, QKV>), dim3(grid), dim3(kThreads),
-                               dyn_bytes, stream, f);
+            hipLaunchKernelGGL((fused_decode_kernel<D, DI, FMT, HT, false, MASK, QKV, LAYERS>), dim3(grid),
+                               dim3(kThreads), dyn_bytes, stream, f);
         return hipGetLastError();
     }
     template <int D, int DI>
@@ -860,9 +958,9 @@ struct FusedKernels {
     template <int D, int DI, int HT>
     static hipError_t occ(int *per_cu, size_t dyn, bool cached) {
         return cached ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                            per_cu, fused_decode_kernel<D, DI, FMT, HT, true, MASK, QKV>, kThreads, dyn)
+                            per_cu, fused_decode_kernel<D, DI, FMT, HT, true, MASK, QKV, LAYERS>, kThreads, dyn)
                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                            per_cu, fused_decode_kernel<D, DI, FMT, HT, false, MASK, QKV>, kThreads, dyn);
+                            per_cu, fused_decode_kernel<D, DI, FMT, HT, false, MASK, QKV, LAYERS>, kThreads, dyn);
     }
     template <int D, int DI>
     static hipError_t occ_di(int HT, int *per_cu, size_t dyn, bool cached) {

@@ -292,6 +292,16 @@ lit_status lit_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv
 
 static bool step_uses_candidates(const lit_step_args *s) { return s->cand_in || s->cand_out; }
 static bool step_quant_kv(const lit_step_args *s) { return s->win_kv_format != 0 || s->comp_kv_format != 0; }
+static int step_layers(const lit_step_args *s) { return s->layers > 1 ? s->layers : 1; }
+
+// Layer strides of the per-layer arrays of a step (elements of q / out, codes or bf16
+// elements of the window source).
+static void set_layers(AttnArgs &a, const lit_step_args *s) {
+    a.L = step_layers(s);
+    a.q_ls = (long)s->B * s->S * s->H * s->D;
+    a.win_ls = (long)s->B * s->R * s->D;
+    a.out_ls = (long)s->B * s->S * s->H * s->dv;
+}
 
 size_t lit_sparse_attn_layers_workspace_bytes(int L, int B, int S, int H, int dv, int W, int K) {
     if (L <= 0 || B <= 0 || S <= 0 || H <= 0 || dv <= 0 || W < 0 || K < 0) return 0;
@@ -379,8 +389,8 @@ static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld
     *scores_bytes = round_up((size_t)s->B * s->S * (*ld) * sizeof(float), 256);
     const int nwin = window_width(s->S, s->start_pos, s->W);
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
-    *plan = plan_attention(s->B, s->S, attn_list_len(nwin, keff, step_quant_kv(s)));
-    size_t rest = round_up(attention_partial_bytes(s->B, s->S, s->H, s->dv, *plan), 256);
+    *plan = plan_attention(step_layers(s) * s->B, s->S, attn_list_len(nwin, keff, step_quant_kv(s)));
+    size_t rest = round_up(attention_partial_bytes(step_layers(s) * s->B, s->S, s->H, s->dv, *plan), 256);
     if (s->cand_out) {
         const size_t bb = lit_candidate_blocks_workspace_bytes(s->B, s->S, s->start_pos, s->ratio,
                                                                s->cand_block_size);
@@ -403,9 +413,12 @@ static FusedPlan step_fused_plan(const lit_step_args *s) {
     // quantised KV runs fused when both sources are quantised and there is no masking
     const bool qkv = step_quant_kv(s);
     if (qkv && (masked || s->win_kv_format != LIT_KV_E4M3 || s->comp_kv_format != LIT_KV_E2M1)) return p;
+    // several layers over the top-k run fused with bf16 KV and no masking
+    const bool layers = step_layers(s) > 1;
+    if (layers && (masked || qkv)) return p;
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
-    return plan_fused(s->index_format, masked, qkv, s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D, s->dv,
-                      s->W, keff);
+    return plan_fused(s->index_format, masked, qkv, layers, s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D,
+                      s->dv, s->W, keff);
 }
 
 static lit_status check_step(const lit_step_args *s) {
@@ -426,6 +439,8 @@ static lit_status check_step(const lit_step_args *s) {
                     (const int32_t *)16, keff, s->out);
     if (st != LIT_OK) return st;
     if (s->B > 0 && s->S > 0 && keff > 0 && !s->topk_idx) return LIT_E_NULL;
+    if (s->layers < 0) return LIT_E_SHAPE;
+    if ((long)step_layers(s) * s->B * s->S > kMaxQueries) return LIT_E_UNSUPPORTED;
     if (step_quant_kv(s)) {
         if ((s->win_kv_format != LIT_KV_BF16 && s->win_kv_format != LIT_KV_E4M3) ||
             (s->comp_kv_format != LIT_KV_BF16 && s->comp_kv_format != LIT_KV_E2M1))
@@ -450,7 +465,7 @@ size_t lit_sparse_step_workspace_bytes(const lit_step_args *s) {
     size_t need = step_layout(s, &sb, &ld, &p);
     const FusedPlan fp = step_fused_plan(s);
     if (fp.ok) {
-        const size_t fused = fused_ws_bytes(fp, s->dv);
+        const size_t fused = fused_ws_bytes(fp, s->dv, step_layers(s));
         if (fused > need) need = fused;
     }
     return need;
@@ -484,7 +499,7 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
     const FusedPlan fp = step_fused_plan(s);
     if (fp.ok && s->state && s->state_bytes >= fused_state_bytes(fp)) {
         if (((uintptr_t)s->state & 255u) != 0) return LIT_E_ALIGN;
-        if (ws_bytes < fused_ws_bytes(fp, s->dv)) return LIT_E_WORKSPACE;
+        if (ws_bytes < fused_ws_bytes(fp, s->dv, step_layers(s))) return LIT_E_WORKSPACE;
         FusedArgs f{};
         f.ia = IndexerArgs{s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->index_format, s->B, s->S, s->Hi,
                            s->Di, s->T_cap, s->start_pos, s->ratio, T, nullptr, 0};
@@ -493,6 +508,7 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
                         s->scale, s->out, nullptr};
         f.topk_out = s->topk_idx;
         f.keff = keff;
+        set_layers(f.aa, s);
         if (s->cand_in) {
             f.cand = s->cand_in;
             f.cand_k = s->cand_k;
@@ -542,6 +558,7 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
                 nullptr, s->W, s->start_pos, keff > 0 ? s->comp_kv : nullptr, s->T_cap,
                 keff > 0 ? s->topk_idx : nullptr, keff, s->sink, s->scale, s->out,
                 (float *)rest};
+    set_layers(aa, s);
     if (step_quant_kv(s)) {
         // the derived window keeps W as its size; the checks ran in check_step
         aa.K = keff;

@@ -214,10 +214,10 @@ struct FusedPlan {
     long ld;
     size_t dyn_bytes;
 };
-FusedPlan plan_fused(int fmt, bool masked, bool qkv, int B, int S, int start_pos, int ratio, int Hi, int Di, int D,
-                     int dv, int W, int keff);
+FusedPlan plan_fused(int fmt, bool masked, bool qkv, bool layers, int B, int S, int start_pos, int ratio, int Hi,
+                     int Di, int D, int dv, int W, int keff);
 size_t fused_state_bytes(const FusedPlan &p);  // zero-filled before first use
-size_t fused_ws_bytes(const FusedPlan &p, int dv);
+size_t fused_ws_bytes(const FusedPlan &p, int dv, int layers);
 hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream);
 // The kernels of each index-code format (fused_e4m3.hip, fused_e2m1.hip): launch, and
 // co-resident workgroups per CU for a shape (0 when not instantiated).
@@ -235,5 +235,10 @@ hipError_t launch_fused_e4m3_qkv(const FusedArgs &f, int grid, size_t dyn_bytes,
 hipError_t launch_fused_e2m1_qkv(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
 int fused_per_cu_e4m3_qkv(int D, int DI, int HT, size_t dyn_bytes, bool cached);
 int fused_per_cu_e2m1_qkv(int D, int DI, int HT, size_t dyn_bytes, bool cached);
+// The _layers forms run AttnArgs::L layers over the step's top-k (bf16 KV, no masking).
+hipError_t launch_fused_e4m3_layers(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
+hipError_t launch_fused_e2m1_layers(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
+int fused_per_cu_e4m3_layers(int D, int DI, int HT, size_t dyn_bytes, bool cached);
+int fused_per_cu_e2m1_layers(int D, int DI, int HT, size_t dyn_bytes, bool cached);
 
 }  // namespace lit

@@ -37,7 +37,7 @@ class lit_step_args(ctypes.Structure):
                 ("flags", _I), ("index_format", _I),
                 ("cand_in", _P), ("cand_k", _I), ("cand_out", _P), ("cand_topk_blocks", _I),
                 ("cand_block_size", _I), ("win_kv_format", _I), ("win_kv_scales", _P),
-                ("comp_kv_format", _I), ("comp_kv_scales", _P)]
+                ("comp_kv_format", _I), ("comp_kv_scales", _P), ("layers", _I)]
 
 
 LIT_STEP_UNFUSED = 1
@@ -361,20 +361,25 @@ def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int,
     two-level top-k, ``cand_in`` [B,S,cand_k] int32 makes this a level-two layer and
     ``cand_out`` [B,S,kb] int32 the candidate source (blocks of ``cand_block_size``).
     Quantised attention KV: ``win_fmt="e4m3"`` (win_kv uint8 codes, win_sc scales) and
-    ``comp_fmt="e2m1"`` (comp_kv uint8 codes, comp_sc scales)."""
+    ``comp_fmt="e2m1"`` (comp_kv uint8 codes, comp_sc scales).  Layers sharing the top-k:
+    a 5-D ``q`` [L,B,S,H,D] with win_kv [L,B,R,*] (and sink [L,H]) makes L layers attend
+    over the one list; ``out`` is then [L,B,S,H,dv]."""
     B, S, Hi, _ = q8.shape
     Di = 32 * q_sc.shape[-1]
-    H, D = q.shape[2], q.shape[3]
+    layers = q.shape[0] if q.dim() == 5 else 1
+    H, D = q.shape[-2], q.shape[-1]
+    R = win_kv.shape[-2]
     dv = D if dv is None else dv
     keff = topk_width(S, start_pos, ratio, index_topk)
     if topk_idx is None:
         topk_idx = torch.empty((B, S, keff), dtype=torch.int32, device=q.device)
     if out is None:
-        out = torch.empty((B, S, H, dv), dtype=torch.bfloat16, device=q.device)
+        shape = (layers, B, S, H, dv) if layers > 1 else (B, S, H, dv)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
     a = lit_step_args(B=B, S=S, start_pos=start_pos, ratio=ratio, Hi=Hi, Di=Di,
                       index_topk=index_topk, T_cap=k8.shape[1], q8=q8.data_ptr(),
                       q_sc=q_sc.data_ptr(), w=w.data_ptr(), k8=k8.data_ptr(), k_sc=k_sc.data_ptr(),
-                      H=H, D=D, dv=dv, W=W, R=win_kv.shape[1], q=q.data_ptr(),
+                      H=H, D=D, dv=dv, W=W, R=R, q=q.data_ptr(),
                       win_kv=win_kv.data_ptr(), comp_kv=comp_kv.data_ptr(),
                       sink=0 if sink is None else sink.data_ptr(), scale=scale,
                       topk_idx=topk_idx.data_ptr(), out=out.data_ptr(), flags=flags,
@@ -386,7 +391,8 @@ def make_step_args(*, q8, q_sc, w, k8, k_sc, q, win_kv, comp_kv, start_pos: int,
                       win_kv_format=KV_FORMATS[win_fmt],
                       win_kv_scales=0 if win_sc is None else win_sc.data_ptr(),
                       comp_kv_format=KV_FORMATS[comp_fmt],
-                      comp_kv_scales=0 if comp_sc is None else comp_sc.data_ptr())
+                      comp_kv_scales=0 if comp_sc is None else comp_sc.data_ptr(),
+                      layers=layers)
     for t, n in ((cand_in, "cand_in"), (cand_out, "cand_out")):
         if t is not None:
             _need(t, torch.int32, n)

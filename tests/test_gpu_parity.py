@@ -757,3 +757,57 @@ def test_step_qkv_rereading_form(orc, fmt):
     torch.cuda.synchronize()
     assert L.state_error(state) == 0
     _check_step(orc, inp, idx, out)
+
+
+# ---------------------------------------------------------------------------------
+# layers sharing one top-k inside the step (fused: one launch for every layer)
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("flags", MODES)
+@pytest.mark.parametrize("kv", ["bf16", "quant"])
+def test_step_shared_topk_layers(orc, flags, kv):
+    NL = 3
+    inp = synth.make_step(B=2, S=1, start_pos=4095, ratio=2, Hi=32, Di=128, H=16, D=192, W=128,
+                          index_topk=512, seed=95, kv_fmt=kv,
+                          sink=np.linspace(-1, 2, 16).astype(np.float32))
+    rng = np.random.default_rng(96)
+    bits = lambda shape: synth.to_bf16_bits(rng.standard_normal(shape).astype(np.float32))  # noqa: E731
+    qs = np.concatenate([inp.q[None], bits((NL - 1,) + inp.q.shape)])
+    sinks = np.stack([inp.sink] + [rng.standard_normal(16).astype(np.float32) for _ in range(NL - 1)])
+    if kv == "quant":
+        wq = [synth._quant_np(rng.standard_normal(inp.win_kv.shape).astype(np.float32), "e4m3")
+              for _ in range(NL - 1)]
+        wins = np.concatenate([inp.win_kv[None]] + [w[0][None] for w in wq])
+        win_sc = np.concatenate([inp.win_sc[None]] + [w[1][None] for w in wq])
+    else:
+        wins = np.concatenate([inp.win_kv[None], bits((NL - 1,) + inp.win_kv.shape)])
+        win_sc = None
+    d = step_inputs_dev(inp)
+    q_dev = bf16_dev(qs)
+    win_dev = bf16_dev(wins) if kv == "bf16" else dev(wins)
+    args, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
+                                      k_sc=d["k_sc"], q=q_dev, win_kv=win_dev, comp_kv=d["comp_kv"],
+                                      start_pos=inp.start_pos, ratio=inp.ratio,
+                                      index_topk=inp.index_topk, W=inp.W, scale=inp.scale,
+                                      sink=dev(sinks), flags=flags,
+                                      win_fmt="e4m3" if kv == "quant" else "bf16",
+                                      win_sc=None if win_sc is None else dev(win_sc),
+                                      comp_fmt="e2m1" if kv == "quant" else "bf16",
+                                      comp_sc=d["comp_sc"])
+    state = L.attach_state(args)
+    assert (state is not None) == (flags == 0 and kv == "bf16")  # quantised KV: as kernels
+    L.lit_sparse_step(args, L.step_workspace(args))
+    torch.cuda.synchronize()
+    assert L.state_error(state) == 0
+    assert out.shape == (NL, 2, 1, 16, 192)
+    g_idx, g_out = idx.cpu().numpy(), bf16_host(out)
+    ref = orc.step(inp)
+    win = orc.window_indices(inp.B, inp.S, inp.start_pos, inp.W, inp.R)
+    for b in range(2):
+        ok, why = topk_sets_agree(ref["scores"][b, 0], ref["idx"][b, 0], g_idx[b, 0])
+        assert ok, why
+    wf, cf = ("e4m3", "e2m1") if kv == "quant" else ("bf16", "bf16")
+    for ly in range(NL):  # every layer over the kernel's own list
+        want = orc.sparse_attn(qs[ly], wins[ly], win, inp.comp_kv, g_idx, sinks[ly], inp.scale, None,
+                               wf, None if win_sc is None else win_sc[ly], cf, inp.comp_sc)
+        err = np.abs(g_out[ly] - want).max()
+        assert err <= ATTN_TOL, f"layer {ly}: {err}"
