@@ -11,7 +11,6 @@ A brute-force set check covers the chunk generalisation (start > 0, several quer
 """
 import os
 
-import numpy as np
 import pytest
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "window_derived.txt")
