@@ -13,7 +13,10 @@
  *      window and the selected compressed rows, one shared KV head (K = V);
  *      lit_sparse_attn_layers runs several layers over one shared list.
  *   lit_window_indices builds the window row lists; lit_sparse_step runs 1-3
- *   (window rows derived in-kernel) as one stream-ordered sequence.
+ *   (window rows derived in-kernel) as one stream-ordered sequence, for one
+ *   layer or several layers that share the top-k.  lit_sparse_attn_fmt reads
+ *   quantised KV caches; lit_compress_append / lit_window_append write them
+ *   (the cache writes of a decode step).
  *
  * Sources (page title, symbol):
  *   [V4.1] DeepSeek-V4.1-Flash-NVFP4, inference/model.py -- module globals

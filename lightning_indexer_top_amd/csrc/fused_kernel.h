@@ -16,7 +16,8 @@
 // of the device), and the teams are laid out XCD-major so that a team shares one XCD
 // where the sizes allow.  Member m of a team owns key chunk [m*chunk, (m+1)*chunk) of
 // its query's visible rows and keeps that chunk's scores in LDS.
-//   A. Every member scores its chunk (MX-scaled fp8 or fp4 MFMA, as in indexer.hip).  When the
+//   A. Every member scores its chunk (MX-scaled fp8 or fp4 MFMA, as in indexer.hip; in the
+//      MASK form rows outside the query's candidate blocks then score -inf).  When the
 //      query sees more rows than it keeps, it publishes the chunk's scores to the team
 //      buffer and its chunk's max / min score keys in its barrier-A flag.
 //   -- team barrier A (skipped when every visible row is kept) --
@@ -29,10 +30,11 @@
 //      tile of candidate rows, so the row gather overlaps the rest of the selection.
 //   D. Every member attends over its share of the window rows and over its chunk's picks
 //      (candidates that miss the cut are masked), counts its picks from the tiles'
-//      masks, and publishes its partial state.
+//      masks, and publishes its partial state -- for each layer that shares the top-k,
+//      one after the other, in the LAYERS form.
 //   -- team barrier C (the flag carries the member's pick count) --
 //   M. Members merge the team's partial states (log-sum-exp) for a slice of the
-//      (head, dim) outputs, add the sink, and write bf16.  Meanwhile the wave without
+//      (layer, head, dim) outputs, add the sink, and write bf16.  Meanwhile the wave without
 //      merge work writes the member's picks to the top-k list (ascending), at the offset
 //      the pick counts of the members before it give.
 //
