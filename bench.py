@@ -418,6 +418,16 @@ def main() -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / (stage_reps * len(calls))
 
+    # the indexer's contraction against the fp8 (fp4: 2x) MFMA peak: 2*Hi*Di flops per
+    # visible (query, row), from the standalone indexer kernel's duration
+    nvis_sum = sum(min(T, (spec["start_pos"] + i + 1) // spec["ratio"]) for i in range(spec["S"]))
+    idx_flops = 2.0 * spec["B"] * nvis_sum * spec["Hi"] * spec["Di"]
+    mfma_peak = 10000.0 if fmt == "e2m1" else 5000.0
+    idx_tflops = idx_flops / (stages_us["indexer"] * 1e-6) / 1e12
+    indexer_mfma = {"flops_per_step": int(idx_flops), "kernel_us": round(stages_us["indexer"], 3),
+                    "achieved_tflops": round(idx_tflops, 2), "peak_tflops": mfma_peak,
+                    "frac": round(idx_tflops / mfma_peak, 5)}
+
     step_gbps = sb["step"] / (ms_per_step * 1e-3) / 1e9
     if fused:
         # one kernel per step: its average duration is the event-timed region / K
@@ -433,11 +443,36 @@ def main() -> int:
         dom_us = stages_us[dom]
         dom_bytes = sb[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_for(kname.split("+")[0], args.workload, kernel_sources(ksrc)),
-                "kernel": kname, "stage": dom, "bytes_per_launch": dom_bytes,
-                "avg_launch_us": round(dom_us, 3)}
+    if dom == "indexer" and spec["S"] > 1:
+        # chunked prefill: the indexer's contraction is bound by the MFMA peak, not by HBM
+        roofline = {"bound": "mfma", "achieved": indexer_mfma["achieved_tflops"], "peak": mfma_peak,
+                    "unit": "TFLOP/s", "frac": indexer_mfma["frac"],
+                    "traffic": traffic_for(kname.split("+")[0], args.workload, kernel_sources(ksrc)),
+                    "kernel": kname, "stage": dom, "flops_per_launch": indexer_mfma["flops_per_step"],
+                    "avg_launch_us": round(dom_us, 3)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic_for(kname.split("+")[0], args.workload, kernel_sources(ksrc)),
+                    "kernel": kname, "stage": dom, "bytes_per_launch": dom_bytes,
+                    "avg_launch_us": round(dom_us, 3)}
+
+    # a plain device copy on the same box: the bandwidth a streaming kernel reaches here
+    copy_gbps = None
+    if not args.copy_probe_mb:
+        n = 512 * 2 ** 20 // 4
+        src_t = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst_t = torch.empty_like(src_t)
+        dst_t.copy_(src_t)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(10):
+            dst_t.copy_(src_t)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 10 * 2 * n * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        log(f"[bench] device copy: {copy_gbps:.0f} GB/s (read + write of 512 MiB)")
+        del src_t, dst_t
 
     if args.copy_probe_mb:
         n = args.copy_probe_mb * 2 ** 20 // 4
@@ -473,7 +508,10 @@ def main() -> int:
                    + (f", {nl} layers over one top-k" if nl > 1 else "")
                    + (", after the compressor and window-ring writes" if ard else "")},
         "hbm": {"step_bytes": sb["step"], "achieved_gbps": round(step_gbps, 1),
-                "peak_gbps": HBM_PEAK_GBPS, "frac": round(step_gbps / HBM_PEAK_GBPS, 4)},
+                "peak_gbps": HBM_PEAK_GBPS, "frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+                "device_copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),
+                "frac_of_copy": None if copy_gbps is None else round(step_gbps / copy_gbps, 4)},
+        "indexer_mfma": indexer_mfma,
         "kernel_stages_us": {k: round(v, 3) for k, v in stages_us.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
