@@ -150,8 +150,104 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_multi_kernel(Index
     }
 }
 
+// The same with the block's kQB queries staged in LDS first: the 256 threads copy their
+// codes, scale bytes and head weights once (coalesced 16-byte loads), and every wave then
+// reads its query operands from LDS, so the per-query latency is an LDS read instead of an
+// L2 round trip.  For index heads small enough that kQB queries fit (HT*16 heads of
+// idx_row_bytes + DI/32 + 4 bytes each, at most 2304 bytes a query).
+template <int DI, int FMT, int HT>
+constexpr int staged_query_bytes() {
+    return HT * 16 * (idx_row_bytes(DI, FMT) + DI / 32 + 4);
+}
+
+template <int DI, int FMT, int HT>
+__global__ __launch_bounds__(kWaves * 64) void indexer_scores_staged_kernel(IndexerArgs a) {
+    constexpr int NH = HT * 16;
+    constexpr int E = idx_row_bytes(DI, FMT);
+    constexpr int NB = DI / 32;
+    __shared__ __attribute__((aligned(16))) uint8_t qc[kQB][NH * E];   // codes
+    __shared__ __attribute__((aligned(16))) float qw[kQB][NH];         // head weights
+    __shared__ uint8_t qs[kQB][NH * NB];                               // scale bytes
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+
+    const int n_groups = (a.S + kQB - 1) / kQB;
+    const int b = blockIdx.y / n_groups;
+    const int i0 = (blockIdx.y % n_groups) * kQB;
+    const int i1 = min(i0 + kQB, a.S);
+    const int nq = i1 - i0;
+    const int tb0 = blockIdx.x * kWaves * 16 * kU;  // the block's first key
+    if (tb0 >= a.T) return;
+    const size_t bs0 = (size_t)b * a.S;
+
+    // stage the block's queries (a whole workgroup returns together above, so every
+    // thread reaches the barrier)
+    {
+        const uint8_t *src = a.q8 + (bs0 + i0) * NH * E;
+        const int n16 = nq * NH * E / 16;
+        for (int j = threadIdx.x; j < n16; j += kWaves * 64)
+            reinterpret_cast<u32x4 *>(&qc[0][0])[j] = reinterpret_cast<const u32x4 *>(src)[j];
+        const float *wsrc = a.w + (bs0 + i0) * NH;
+        for (int j = threadIdx.x; j < nq * NH; j += kWaves * 64) (&qw[0][0])[j] = wsrc[j];
+        const uint8_t *ssrc = a.q_sc + (bs0 + i0) * NH * NB;
+        for (int j = threadIdx.x; j < nq * NH * NB; j += kWaves * 64) (&qs[0][0])[j] = ssrc[j];
+    }
+    __syncthreads();
+
+    const int t0 = tb0 + wave * (16 * kU);
+    if (t0 >= a.T) return;
+    const int vis_max = min(a.T, (a.start_pos + i1) / a.ratio);
+    const int t = t0 + 16 * g + c;  // lane group g receives tile g's scores
+    if (t0 >= vis_max) {  // nothing visible to any query of the block in these keys
+        if (g == 0)
+            for (int i = i0; i < i1; ++i)
+                for (int u = 0; u < kU; ++u) {
+                    const int tt = t0 + 16 * u + c;
+                    if (tt < a.T) a.scores[(bs0 + i) * a.ld + tt] = -INFINITY;
+                }
+        return;
+    }
+
+    IdxKeys kb[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+        kb[u] = load_idx_keys<DI, FMT>(a, (size_t)b * a.T_cap + min(t0 + 16 * u + c, a.T - 1), g);
+
+    static_assert(kU == 4, "idx_score4 scores four tiles");
+    auto load_q = [&](IdxQuery<DI, FMT, HT> &q, int qi) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const int h = 16 * ht + c;
+            q.a[ht] = mx_operand<DI, FMT>(&qc[qi][h * E], g);
+            q.s[ht] = g < NB ? (int)qs[qi][h * NB + g] : 127;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) q.w[ht][r] = qw[qi][16 * ht + 4 * g + r];
+        }
+    };
+    for (int i = i0; i < i1; ++i) {
+        IdxQuery<DI, FMT, HT> qv;
+        load_q(qv, i - i0);
+        const float s = idx_score4<DI, FMT, HT>(qv, kb, g);
+        if (t < a.T) {
+            const int vis = (a.start_pos + i + 1) / a.ratio;
+            a.scores[(bs0 + i) * a.ld + t] = t < vis ? s : -INFINITY;
+        }
+    }
+}
+
+template <int DI, int FMT, int HT>
+hipError_t launch_staged(const IndexerArgs &a, hipStream_t stream) {
+    const int keys_per_block = kWaves * 16 * kU;
+    dim3 grid((a.T + keys_per_block - 1) / keys_per_block, a.B * ((a.S + kQB - 1) / kQB));
+    hipLaunchKernelGGL((indexer_scores_staged_kernel<DI, FMT, HT>), grid, dim3(kWaves * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int DI, int FMT, int HT>
 hipError_t launch_multi(const IndexerArgs &a, hipStream_t stream) {
+    if constexpr (staged_query_bytes<DI, FMT, HT>() <= 2304) return launch_staged<DI, FMT, HT>(a, stream);
     const int keys_per_block = kWaves * 16 * kU;
     dim3 grid((a.T + keys_per_block - 1) / keys_per_block, a.B * ((a.S + kQB - 1) / kQB));
     hipLaunchKernelGGL((indexer_scores_multi_kernel<DI, FMT, HT>), grid, dim3(kWaves * 64), 0, stream, a);
