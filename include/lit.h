@@ -228,7 +228,8 @@ int lit_window_width(int S, int start_pos, int W);
  *   out      (device) bf16 [B, S, H, dv] output
  *   ws, ws_bytes  workspace, lit_sparse_attn_workspace_bytes() bytes
  * Requirements: H == 16; D in {64, 128, 192, 256}; B*S <= 65535; dv a multiple of 16 and
- * <= D; every listed slot < R and row < T_cap (checked on the device: an
+ * <= D; R*D*2 and T_cap*D*2 (one sequence's sources in bytes) below 2^31, else
+ * LIT_E_UNSUPPORTED; every listed slot < R and row < T_cap (checked on the device: an
  * out-of-range entry is treated as -1).
  */
 lit_status lit_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv,

@@ -36,19 +36,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kHeads = 16;
 
-__device__ inline const uint16_t *list_row(const AttnArgs &a, int b, int i, int nwin, const WindowBase &wb,
-                                          int p) {
-    const size_t bs = (size_t)b * a.S + i;
-    if (p < nwin) {
-        const int slot = a.win_idx ? a.win_idx[bs * a.W + p] : window_slot_at(wb, a.start_pos, a.R, i, p);
-        if (slot < 0 || slot >= a.R) return nullptr;
-        return a.win_kv + ((size_t)b * a.R + slot) * a.D;
-    }
-    const int t = a.comp_idx[bs * a.K + (p - nwin)];
-    if (t < 0 || t >= a.T_cap) return nullptr;
-    return a.comp_kv + ((size_t)b * a.T_cap + t) * a.D;
-}
-
 // Row of list entry p as an index into its source ([B*R] window slots or [B*T_cap]
 // compressed rows), or -1; `win` tells which source (padded list: window entries occupy
 // [0, wpad), wpad a multiple of 32).
@@ -112,7 +99,7 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a0, A
     __shared__ float wm[kWaves][kHeads], wl[kWaves][kHeads];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: tile bases are scalars
     const int g = lane >> 4;
     const int c = lane & 15;
     // the layers of one query are neighbours in the grid, so they run together and the
@@ -125,8 +112,8 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a0, A
     const int split = blockIdx.x;
     const int nwin = a.win_idx ? a.W : (a.W > 0 ? window_width(a.S, a.start_pos, a.W) : 0);
     const WindowBase wb = window_base(a.start_pos, a.W, a.R > 0 ? a.R : 1, i);
-    const int list_len = attn_list_len(nwin, a.K, QUANT);
-    const int wpad = list_len - a.K;  // window entries (padded to whole tiles when QUANT)
+    const int list_len = attn_list_len(nwin, a.K);
+    const int wpad = list_len - a.K;  // window entries, padded to whole tiles
     const int ndt = a.dv / 16;
     const float sl2 = a.scale * kLog2e;
 
@@ -139,17 +126,63 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a0, A
     const int split_begin = split * kWaves * pl.tiles_per_wave * 32;
     const int split_end = min(list_len, split_begin + kWaves * pl.tiles_per_wave * 32);
 
-    for (int it = 0; it < pl.tiles_per_wave; ++it) {
-        const int base = split_begin + (wave * pl.tiles_per_wave + it) * 32;
-        if (base >= split_end) break;
-        const int p0 = base + c, p1 = base + 16 + c;
-        AttnRows<D> rows;
-        if constexpr (QUANT)
-            quant_tile_load<D, WF, CF>(rows, a, b, i, nwin, wpad, wb, p0, p1, split_end, g);
-        else
-            attn_tile_load<D>(rows, p0 < split_end ? list_row(a, b, i, nwin, wb, p0) : nullptr,
-                              p1 < split_end ? list_row(a, b, i, nwin, wb, p1) : nullptr, g);
-        attn_tile_compute<D>(st, qb, rows, tile, ndt, sl2, g, c);
+    const int first = split_begin + wave * pl.tiles_per_wave * 32;
+    if constexpr (QUANT) {
+        for (int it = 0; it < pl.tiles_per_wave; ++it) {
+            const int base = first + it * 32;
+            if (base >= split_end) break;
+            AttnRows<D> rows;
+            quant_tile_load<D, WF, CF>(rows, a, b, i, nwin, wpad, wb, base + c, base + 16 + c, split_end, g);
+            attn_tile_compute<D>(st, qb, rows, tile, ndt, sl2, g, c);
+        }
+    } else {
+        // bf16 sources by buffer loads: a tile is all window or all compressed entries
+        // (the window part of the list is padded to whole tiles), so its source is
+        // uniform; a lane without a row reads zeros from past the source's end.  The
+        // list entries of the next tile are requested before the current tile's rows
+        // are used, so their round trip overlaps the current tile's.
+        const uint16_t *wsrc = a.win_kv ? a.win_kv + (size_t)b * a.R * D : nullptr;
+        const uint16_t *csrc = a.comp_kv ? a.comp_kv + (size_t)b * a.T_cap * D : nullptr;
+        const rsrc_t win_r = make_rsrc(wsrc, wsrc ? (uint32_t)a.R * D * 2u : 0u);
+        const rsrc_t comp_r = make_rsrc(csrc, csrc ? (uint32_t)a.T_cap * D * 2u : 0u);
+        const rsrc_t widx_r = make_rsrc(a.win_idx ? a.win_idx + (size_t)bs * a.W : nullptr,
+                                        a.win_idx ? (uint32_t)a.W * 4u : 0u);
+        const rsrc_t cidx_r = make_rsrc(a.comp_idx ? a.comp_idx + (size_t)bs * a.K : nullptr,
+                                        a.comp_idx ? (uint32_t)a.K * 4u : 0u);
+        const bool derived = a.win_idx == nullptr;
+        // entries of the tile at `base` for this lane's rows base+c and base+16+c: a
+        // loaded entry (window slot or compressed row), a derived window slot, and
+        // whether the list position is inside the split and the window / list
+        int ld0, ld1, sl0 = -1, sl1 = -1;
+        bool ok0, ok1;
+        auto fetch = [&](int base) {
+            const bool win = base < wpad;
+            const int p0 = base + c, p1 = base + 16 + c;
+            const rsrc_t ir = win ? widx_r : cidx_r;
+            const int o = win ? 0 : wpad;
+            ld0 = (int)__builtin_amdgcn_raw_buffer_load_b32(ir, (int)(4u * (uint32_t)(p0 - o)), 0, 0);
+            ld1 = (int)__builtin_amdgcn_raw_buffer_load_b32(ir, (int)(4u * (uint32_t)(p1 - o)), 0, 0);
+            if (win && derived) {
+                sl0 = window_slot_at(wb, a.start_pos, a.R, i, p0);
+                sl1 = window_slot_at(wb, a.start_pos, a.R, i, p1);
+            }
+            ok0 = p0 < split_end && (!win || p0 < nwin);
+            ok1 = p1 < split_end && (!win || p1 < nwin);
+        };
+        fetch(first);
+        for (int it = 0; it < pl.tiles_per_wave; ++it) {
+            const int base = first + it * 32;
+            if (base >= split_end) break;
+            const bool win = base < wpad;
+            const int e0 = win && derived ? sl0 : ld0, e1 = win && derived ? sl1 : ld1;
+            const uint32_t lim = win ? (uint32_t)a.R : (uint32_t)a.T_cap;
+            const uint32_t off0 = ok0 && (uint32_t)e0 < lim ? (uint32_t)e0 * (2u * D) : kOffNone;
+            const uint32_t off1 = ok1 && (uint32_t)e1 < lim ? (uint32_t)e1 * (2u * D) : kOffNone;
+            AttnRows<D> rows;
+            attn_tile_load_buf<D>(rows, win ? win_r : comp_r, off0, off1, g);
+            fetch(base + 32);  // past the split: every entry comes back not ok
+            attn_tile_compute<D>(st, qb, rows, tile, ndt, sl2, g, c);
+        }
     }
     __syncthreads();  // every wave is done with its LDS rows
     // Reuse the row buffer for the 4 waves' states.

@@ -122,11 +122,7 @@ __device__ inline void st64_agent(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kSc1 = 16;  // buffer cache policy: coherent at agent scope (sc1)
-__device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
-}
 __device__ inline u32x4 ld128_agent(rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kSc1);
 }

@@ -14,6 +14,9 @@ namespace {
 
 // Queries (b, i) index the second grid dimension of the indexer and attention launches.
 constexpr long kMaxQueries = 65535;
+// Bytes of one sequence's bf16 KV source (R or T_cap rows of D): rows are addressed by
+// 32-bit offsets, with the top bit marking a missing row.
+constexpr long kMaxSourceBytes = 0x7fffffffL;
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -82,6 +85,7 @@ lit_status check_attn(const uint16_t *q, int B, int S, int H, int D, int dv, con
     if (dv % 16 != 0) return LIT_E_UNSUPPORTED;
     if (W > 0 && R <= 0) return LIT_E_SHAPE;
     if (K > 0 && T_cap <= 0) return LIT_E_SHAPE;
+    if ((long)R * D * 2 > kMaxSourceBytes || (long)T_cap * D * 2 > kMaxSourceBytes) return LIT_E_UNSUPPORTED;
     if (B == 0 || S == 0) return LIT_OK;
     if (!q || !out) return LIT_E_NULL;
     if (W > 0 && (!win_kv || !win_idx)) return LIT_E_NULL;
@@ -221,12 +225,9 @@ lit_status lit_window_indices(int B, int S, int start_pos, int W, int R, int32_t
     return hip_status(launch_window_indices(B, S, start_pos, W, R, win_idx, (hipStream_t)stream));
 }
 
-// Partial-state bytes for either list form (quantised sources pad the window entries to
-// whole tiles, which can change the split plan).
+// Partial-state bytes of the attention's split plan.
 static size_t attn_ws_bytes(int B, int S, int H, int dv, int W, int K) {
-    const size_t a = attention_partial_bytes(B, S, H, dv, plan_attention(B, S, attn_list_len(W, K, false)));
-    const size_t b = attention_partial_bytes(B, S, H, dv, plan_attention(B, S, attn_list_len(W, K, true)));
-    return a > b ? a : b;
+    return attention_partial_bytes(B, S, H, dv, plan_attention(B, S, attn_list_len(W, K)));
 }
 
 size_t lit_sparse_attn_workspace_bytes(int B, int S, int H, int dv, int W, int K) {
@@ -273,8 +274,7 @@ lit_status lit_sparse_attn_fmt(const uint16_t *q, int B, int S, int H, int D, in
     if ((st = set_kv_formats(a, win_format, win_kv, win_scales, comp_format, comp_kv, comp_scales)) != LIT_OK)
         return st;
     if (B == 0 || S == 0) return LIT_OK;
-    const bool quant = a.win_fmt != kKvBf16 || a.comp_fmt != kKvBf16;
-    const AttnPlan p = plan_attention(B, S, attn_list_len(W, K, quant));
+    const AttnPlan p = plan_attention(B, S, attn_list_len(W, K));
     const size_t need = attention_partial_bytes(B, S, H, dv, p);
     if (need > 0 && (!ws || ws_bytes < need)) return LIT_E_WORKSPACE;
     if (need > 0 && !aligned16(ws)) return LIT_E_ALIGN;
@@ -324,7 +324,7 @@ lit_status lit_sparse_attn_layers(int L, const uint16_t *q, int B, int S, int H,
     if (derived && R < window_need(S, start_pos, W)) return LIT_E_SHAPE;
     if ((long)L * B * S > kMaxQueries) return LIT_E_UNSUPPORTED;
     if (B == 0 || S == 0) return LIT_OK;
-    const AttnPlan p = plan_attention(L * B, S, nwin + K);
+    const AttnPlan p = plan_attention(L * B, S, attn_list_len(nwin, K));
     const size_t need = attention_partial_bytes(L * B, S, H, dv, p);
     if (need > 0 && (!ws || ws_bytes < need)) return LIT_E_WORKSPACE;
     if (need > 0 && !aligned16(ws)) return LIT_E_ALIGN;
@@ -389,7 +389,7 @@ static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld
     *scores_bytes = round_up((size_t)s->B * s->S * (*ld) * sizeof(float), 256);
     const int nwin = window_width(s->S, s->start_pos, s->W);
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
-    *plan = plan_attention(step_layers(s) * s->B, s->S, attn_list_len(nwin, keff, step_quant_kv(s)));
+    *plan = plan_attention(step_layers(s) * s->B, s->S, attn_list_len(nwin, keff));
     size_t rest = round_up(attention_partial_bytes(step_layers(s) * s->B, s->S, s->H, s->dv, *plan), 256);
     if (s->cand_out) {
         const size_t bb = lit_candidate_blocks_workspace_bytes(s->B, s->S, s->start_pos, s->ratio,

@@ -102,11 +102,9 @@ struct AttnArgs {
     const uint8_t *win_codes = nullptr, *win_scales = nullptr;
     const uint8_t *comp_codes = nullptr, *comp_scales = nullptr;
 };
-// Entries of the list the attention kernel walks: window entries, padded to whole tiles
-// when a source is quantised, then the compressed entries.
-__host__ __device__ inline int attn_list_len(int nwin, int K, bool quant) {
-    return (quant ? (nwin + 31) / 32 * 32 : nwin) + K;
-}
+// Entries of the list the attention kernel walks: window entries, padded to whole 32-row
+// tiles so that no tile mixes the two sources, then the compressed entries.
+__host__ __device__ inline int attn_list_len(int nwin, int K) { return (nwin + 31) / 32 * 32 + K; }
 // Split plan: how many workgroups share one query's row list.
 struct AttnPlan {
     int list_len;        // window width + K

@@ -209,6 +209,29 @@ __device__ inline void attn_tile_load_rows(AttnRows<D> &t, const uint16_t *rp0, 
     }
 }
 
+// Raw buffer loads.  A buffer resource covers `bytes` (< 2^31) from `base`; a load at an
+// offset at or past that count returns zeros and touches no memory, so a lane without a
+// row loads from offset kOffNone instead of branching around its load.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOffNone = 0x80000000u;
+__device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// One tile's rows from a bf16 source by buffer loads: lane (g, c) reads dims 32s+8g..+7
+// of the rows at byte offsets off0 / off1 (kOffNone: no row, zeros).
+template <int D>
+__device__ inline void attn_tile_load_buf(AttnRows<D> &t, rsrc_t src, uint32_t off0, uint32_t off1, int g) {
+    t.valid[0] = __ballot(off0 != kOffNone);
+    t.valid[1] = __ballot(off1 != kOffNone);
+    const uint32_t o0 = off0 + 16u * g, o1 = off1 + 16u * g;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+        t.r[0][s] = __builtin_amdgcn_raw_buffer_load_b128(src, (int)(o0 + 64u * s), 0, 0);
+        t.r[1][s] = __builtin_amdgcn_raw_buffer_load_b128(src, (int)(o1 + 64u * s), 0, 0);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Quantised KV rows, dequantised on gather into the bf16 operand layout above (lane
 // (g, c) holds dims 32s+8g..32s+8g+7 of its row for each s).
