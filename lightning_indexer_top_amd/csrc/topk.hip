@@ -213,25 +213,28 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(TopkArgs a) {
         return;
     }
 
-    // thread tid owns positions [32 tid, 32 tid + 32); a quad past the row is not read
-    const int p0 = 32 * tid;
+    // quad r of thread tid holds positions 4 (tid + 256 r) .. +3, so each load of a wave
+    // reads 1 KB of consecutive scores; a quad past the row is not read
     f32x4 v[kRowQ];
 #pragma unroll
-    for (int r = 0; r < kRowQ; ++r)
-        v[r] = p0 + 4 * r < n ? *reinterpret_cast<const f32x4 *>(src + p0 + 4 * r) : f32x4{0.f, 0.f, 0.f, 0.f};
-    auto valid = [&](int r, int e) { return p0 + 4 * r + e < n; };
+    for (int r = 0; r < kRowQ; ++r) {
+        const int q = tid + kSelThreads * r;
+        v[r] = 4 * q < n ? *reinterpret_cast<const f32x4 *>(src + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    auto pos = [&](int r, int e) { return 4 * (tid + kSelThreads * r) + e; };
+    auto valid = [&](int r, int e) { return pos(r, e) < n; };
 
     // the row's max key and max complemented key (its min)
     uint32_t kmax = 0u, kminc = 0u;
 #pragma unroll
     for (int r = 0; r < kRowQ; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (valid(r, e)) {
-                const uint32_t k = order_key(v[r][e]);
-                kmax = max(kmax, k);
-                kminc = max(kminc, ~k);
-            }
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t k = order_key(v[r][e]);
+            const bool ok = valid(r, e);
+            kmax = max(kmax, ok ? k : 0u);
+            kminc = max(kminc, ok ? ~k : 0u);
+        }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
@@ -276,20 +279,28 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(TopkArgs a) {
     const int cnt = (int)sm.hist[vb];
     uint32_t kstar, pstar;
     if (cnt <= kCandCap) {
-        // the scores of bin vb as (key << 32 | ~position), in the histogram's place
+        // the scores of bin vb as (key << 32 | ~position), in the histogram's place; a
+        // block scan over the threads' counts gives each its first slot
         uint64_t *cand = reinterpret_cast<uint64_t *>(sm.hist);
-        __syncthreads();  // every thread has read hist[vb]
-        if (tid == 0) sm.ncand = 0;
-        __syncthreads();
+        uint32_t cm = 0u;
 #pragma unroll
         for (int r = 0; r < kRowQ; ++r)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t bin = (bins[2 * r + (e >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
-                if (bin == (uint32_t)vb)
-                    cand[atomicAdd(&sm.ncand, 1)] =
-                        ((uint64_t)order_key(v[r][e]) << 32) | (uint32_t)~(uint32_t)(p0 + 4 * r + e);
+                cm |= (bin == (uint32_t)vb ? 1u : 0u) << (4 * r + e);
             }
+        uint32_t total;
+        const uint32_t mine = (uint32_t)__popc(cm);
+        int o = (int)(wg_scan<kSelThreads / 64>(mine, sm.wsum, &total) - mine);  // every thread has read hist[vb]
+        if (cm) {
+#pragma unroll
+            for (int r = 0; r < kRowQ; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if ((cm >> (4 * r + e)) & 1u)
+                        cand[o++] = ((uint64_t)order_key(v[r][e]) << 32) | (uint32_t)~(uint32_t)pos(r, e);
+        }
         __syncthreads();
         int ncand = cnt, nneed = need;
         refine_candidates(cand, ncand, nneed, h2, sm);
@@ -300,27 +311,38 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(TopkArgs a) {
     kstar = sm.kstar;
     pstar = (uint32_t)sm.pstar;
 
-    // output: a pick is key > kstar, or key == kstar at a position <= pstar; one block scan
-    // over the threads' pick counts gives each thread its first slot (ascending order)
-    auto picked = [&](int r, int e) {
-        const uint32_t k = order_key(v[r][e]);
-        return valid(r, e) && (k > kstar || (k == kstar && (uint32_t)(p0 + 4 * r + e) <= pstar));
-    };
-    uint32_t mine = 0;
+    // output: a pick is key > kstar, or key == kstar at a position <= pstar.  The picks
+    // become a bitmap over positions in LDS (h2 is free again; word w covers positions
+    // 32w..32w+31, assembled from 8 lanes' nibbles), and thread t then writes the picks
+    // of word t at the offset one block scan gives it, in ascending order.
+    uint32_t *bm = h2;
 #pragma unroll
-    for (int r = 0; r < kRowQ; ++r)
+    for (int r = 0; r < kRowQ; ++r) {
+        uint32_t nib = 0u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mine += picked(r, e) ? 1u : 0u;
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t k = order_key(v[r][e]);
+            const bool pick = valid(r, e) && (k > kstar || (k == kstar && (uint32_t)pos(r, e) <= pstar));
+            nib |= (pick ? 1u : 0u) << e;
+        }
+        // OR over the 8 lanes: swap neighbours, swap pairs (DPP quad permutations), then
+        // mirror within the half-row of 8 lanes
+        int x = (int)(nib << (4 * (tid & 7)));
+        x |= __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);
+        x |= __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);
+        x |= __builtin_amdgcn_update_dpp(0, x, 0x141, 0xf, 0xf, false);
+        if ((tid & 7) == 0) bm[kSelThreads / 8 * r + (tid >> 3)] = (uint32_t)x;
+    }
+    __syncthreads();
+    uint32_t w = bm[tid];
     uint32_t total;
-    int o = (int)(wg_scan<kSelThreads / 64>(mine, sm.wsum, &total) - mine);
-#pragma unroll
-    for (int r = 0; r < kRowQ; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (picked(r, e)) {
-                if (o < a.keff) out[o] = p0 + 4 * r + e;
-                ++o;
-            }
+    int o = (int)(wg_scan<kSelThreads / 64>((uint32_t)__popc(w), sm.wsum, &total) - (uint32_t)__popc(w));
+    while (w) {
+        const int bit = __builtin_ctz(w);
+        w &= w - 1u;
+        if (o < a.keff) out[o] = 32 * tid + bit;
+        ++o;
+    }
 }
 
 __global__ __launch_bounds__(256) void block_max_kernel(const float *scores, long ld, int S, int start_pos,

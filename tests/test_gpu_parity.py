@@ -117,6 +117,33 @@ def test_topk_all_equal_and_signed_zero(orc):
     assert np.array_equal(want[0, 0], np.arange(100))
 
 
+# B*S >= 256 rows of at most 8192 positions take the many-row kernel (one workgroup a
+# row); its clustered forms are the candidate refinement (9 distinct values) and the
+# radix levels (2 distinct values: thousands of scores in the cut's bin).
+ROWS_CASES = [
+    # B, S, start_pos, ratio, k, kind
+    (1, 256, 0, 2, 16, "normal"),        # prefill from 0: short rows padded with -1
+    (2, 160, 16000, 2, 512, "normal"),   # rows of 8000..8079 positions
+    (1, 300, 4000, 2, 512, "ties"),
+    (1, 256, 9000, 2, 700, "two"),
+]
+
+
+@pytest.mark.parametrize("B,S,start_pos,ratio,k,kind", ROWS_CASES)
+def test_topk_many_rows_exact(orc, B, S, start_pos, ratio, k, kind):
+    T = (start_pos + S) // ratio
+    ld = (T + 3) // 4 * 4
+    if kind == "two":
+        rng = np.random.Generator(np.random.PCG64(B * 7 + S))
+        sc = rng.integers(0, 2, size=(B, S, ld)).astype(np.float32)
+    else:
+        sc = synth.random_scores(B, S, ld, seed=B * 131 + S + k, ties=kind == "ties")
+    got = L.lit_topk(dev(sc), start_pos, ratio, k)
+    torch.cuda.synchronize()
+    want = orc.topk(sc.astype(np.float64), start_pos, ratio, k)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
 # ---------------------------------------------------------------------------------
 # window lists
 # ---------------------------------------------------------------------------------
