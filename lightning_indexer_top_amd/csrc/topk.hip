@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 
 constexpr int kRowQ = 8;  // score quads per thread: rows of up to 8192 positions
 
-__global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kSelThreads, 4) void topk_rows_kernel(TopkArgs a) {  // 4 rows a compute unit
     __shared__ SelLds sm;
     __shared__ __attribute__((aligned(16))) uint32_t h2[kBins];  // candidate refinement
     __shared__ uint32_t mm[kSelThreads / 64][2];
@@ -214,46 +214,58 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(TopkArgs a) {
     }
 
     // quad r of thread tid holds positions 4 (tid + 256 r) .. +3, so each load of a wave
-    // reads 1 KB of consecutive scores; a quad past the row is not read
+    // reads 1 KB of consecutive scores.  Positions past the row hold a copy of position
+    // 0's score (a visible row: n > keff >= 1), which leaves the row's min and max
+    // unchanged; their histogram counts are taken back below, and the validity nibbles
+    // vn (bit 4r+e: position valid) keep them out of the candidates and picks.
+    const float v0 = src[0];
     f32x4 v[kRowQ];
+    uint32_t vn = 0u;
 #pragma unroll
     for (int r = 0; r < kRowQ; ++r) {
         const int q = tid + kSelThreads * r;
-        v[r] = 4 * q < n ? *reinterpret_cast<const f32x4 *>(src + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+        v[r] = *reinterpret_cast<const f32x4 *>(src + 4 * (4 * q < n ? q : 0));
+        vn |= ((1u << min(max(n - 4 * q, 0), 4)) - 1u) << (4 * r);
     }
+#pragma unroll
+    for (int r = 0; r < kRowQ; ++r)
+        if (((vn >> (4 * r)) & 0xFu) != 0xFu)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!((vn >> (4 * r + e)) & 1u)) v[r][e] = v0;
     auto pos = [&](int r, int e) { return 4 * (tid + kSelThreads * r) + e; };
-    auto valid = [&](int r, int e) { return pos(r, e) < n; };
 
-    // the row's max key and max complemented key (its min)
-    uint32_t kmax = 0u, kminc = 0u;
+    // the row's min and max by order keys (-0 and +0 need not be told apart here: both
+    // give the float 0)
+    uint32_t kmax = 0u, kmin = ~0u;
 #pragma unroll
     for (int r = 0; r < kRowQ; ++r)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const uint32_t k = order_key(v[r][e]);
-            const bool ok = valid(r, e);
-            kmax = max(kmax, ok ? k : 0u);
-            kminc = max(kminc, ok ? ~k : 0u);
+            const uint32_t u = __float_as_uint(v[r][e]);
+            const uint32_t k = u ^ ((uint32_t)((int)u >> 31) | 0x80000000u);
+            kmax = max(kmax, k);
+            kmin = min(kmin, k);
         }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
-        kminc = max(kminc, (uint32_t)__shfl_xor((int)kminc, off));
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
     }
     if (lane == 0) {
         mm[wave][0] = kmax;
-        mm[wave][1] = kminc;
+        mm[wave][1] = kmin;
     }
     for (int j = tid; j < kVBins / 4 + 1; j += kSelThreads)  // + the spill bin
         reinterpret_cast<u32x4 *>(sm.hist)[j] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     kmax = 0u;
-    kminc = 0u;
+    kmin = ~0u;
     for (int w = 0; w < kSelThreads / 64; ++w) {
         kmax = max(kmax, mm[w][0]);
-        kminc = max(kminc, mm[w][1]);
+        kmin = min(kmin, mm[w][1]);
     }
-    const float mx = key_float(kmax), mn = key_float(~kminc);
+    const float mx = key_float(kmax), mn = key_float(kmin);
     // an infinite end puts every score into one bin; the exact levels below then decide
     const bool finite = mx - mn < INFINITY;
     const float scale = finite && mx > mn ? (float)kVBins / (mx - mn) : 0.f;
@@ -266,12 +278,15 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(TopkArgs a) {
         uint32_t bb[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            bb[e] = valid(r, e) ? (uint32_t)value_bin(v[r][e], scale, bias) : (uint32_t)kVBins;
+            bb[e] = (uint32_t)value_bin(v[r][e], scale, bias);
             atomicAdd(&sm.hist[bb[e]], 1u);
         }
         bins[2 * r] = bb[0] | (bb[1] << 16);
         bins[2 * r + 1] = bb[2] | (bb[3] << 16);
     }
+    // the copies of position 0's score standing in for positions past the row
+    if (tid == 0 && n < kSelThreads * 4 * kRowQ)
+        atomicSub(&sm.hist[value_bin(v0, scale, bias)], (uint32_t)(kSelThreads * 4 * kRowQ - n));
     __syncthreads();
     find_bin(sm.hist, kVBins, a.keff, sm.wsum, &sm.bin, &sm.above);
     const int vb = sm.bin;
@@ -290,6 +305,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(TopkArgs a) {
                 const uint32_t bin = (bins[2 * r + (e >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
                 cm |= (bin == (uint32_t)vb ? 1u : 0u) << (4 * r + e);
             }
+        cm &= vn;
         uint32_t total;
         const uint32_t mine = (uint32_t)__popc(cm);
         int o = (int)(wg_scan<kSelThreads / 64>(mine, sm.wsum, &total) - mine);  // every thread has read hist[vb]
@@ -322,12 +338,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(TopkArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint32_t k = order_key(v[r][e]);
-            const bool pick = valid(r, e) && (k > kstar || (k == kstar && (uint32_t)pos(r, e) <= pstar));
+            const bool pick = k > kstar || (k == kstar && (uint32_t)pos(r, e) <= pstar);
             nib |= (pick ? 1u : 0u) << e;
         }
         // OR over the 8 lanes: swap neighbours, swap pairs (DPP quad permutations), then
         // mirror within the half-row of 8 lanes
-        int x = (int)(nib << (4 * (tid & 7)));
+        nib &= vn >> (4 * r);
+        int x = (int)((nib & 0xFu) << (4 * (tid & 7)));
         x |= __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);
         x |= __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);
         x |= __builtin_amdgcn_update_dpp(0, x, 0x141, 0xf, 0xf, false);
