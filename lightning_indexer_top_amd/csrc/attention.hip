@@ -150,6 +150,7 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a0, A
         const rsrc_t cidx_r = make_rsrc(a.comp_idx ? a.comp_idx + (size_t)bs * a.K : nullptr,
                                         a.comp_idx ? (uint32_t)a.K * 4u : 0u);
         const bool derived = a.win_idx == nullptr;
+        const int wave_end = min(split_end, first + pl.tiles_per_wave * 32);  // this wave's entries
         // entries of the tile at `base` for this lane's rows base+c and base+16+c: a
         // loaded entry (window slot or compressed row), a derived window slot, and
         // whether the list position is inside the split and the window / list
@@ -166,13 +167,13 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a0, A
                 sl0 = window_slot_at(wb, a.start_pos, a.R, i, p0);
                 sl1 = window_slot_at(wb, a.start_pos, a.R, i, p1);
             }
-            ok0 = p0 < split_end && (!win || p0 < nwin);
-            ok1 = p1 < split_end && (!win || p1 < nwin);
+            ok0 = p0 < wave_end && (!win || p0 < nwin);
+            ok1 = p1 < wave_end && (!win || p1 < nwin);
         };
         fetch(first);
         for (int it = 0; it < pl.tiles_per_wave; ++it) {
             const int base = first + it * 32;
-            if (base >= split_end) break;
+            if (base >= wave_end) break;
             const bool win = base < wpad;
             const int e0 = win && derived ? sl0 : ld0, e1 = win && derived ? sl1 : ld1;
             const uint32_t lim = win ? (uint32_t)a.R : (uint32_t)a.T_cap;
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a0, A
             const uint32_t off1 = ok1 && (uint32_t)e1 < lim ? (uint32_t)e1 * (2u * D) : kOffNone;
             AttnRows<D> rows;
             attn_tile_load_buf<D>(rows, win ? win_r : comp_r, off0, off1, g);
-            fetch(base + 32);  // past the split: every entry comes back not ok
+            fetch(base + 32);  // past the wave's entries: every entry comes back not ok
             attn_tile_compute<D>(st, qb, rows, tile, ndt, sl2, g, c);
         }
     }
@@ -228,8 +229,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a0, AttnPlan pl
     const float s2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
     float M = s2;
     for (int s = lane; s < ns; s += 64) M = fmaxf(M, src[s * stride + a.dv]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    M = wave_max_f(M);
     float L = 0.f;
     for (int s = lane; s < ns; s += 64) {
         const float ms = src[s * stride + a.dv];
@@ -237,8 +237,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a0, AttnPlan pl
         wgt[s] = f;
         L += f * src[s * stride + a.dv + 1];
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+    L = wave_sum_f(L);
     if (a.sink && M != -INFINITY) L += exp2f(s2 - M);
     const float inv = L > 0.f ? 1.f / L : 0.f;
     __syncthreads();

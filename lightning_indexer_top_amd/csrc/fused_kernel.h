@@ -163,8 +163,7 @@ __device__ inline u32x4 team_poll(const rsrc_t &slots, int team, uint32_t q, uin
 }
 // Workgroup max / min / sum (every thread gets the result).
 __device__ inline float wg_max(float v, float *red) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    v = wave_max_f(v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
     float r = red[0];
@@ -173,8 +172,7 @@ __device__ inline float wg_max(float v, float *red) {
     return r;
 }
 __device__ inline float wg_min(float v, float *red) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fminf(v, __shfl_xor(v, off));
+    v = wave_min_f(v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
     float r = red[0];
@@ -183,8 +181,7 @@ __device__ inline float wg_min(float v, float *red) {
     return r;
 }
 __device__ inline uint32_t wg_sum(uint32_t v, uint32_t *red) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    v = wave_sum_u32(v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
     uint32_t r = 0;
@@ -312,11 +309,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                         u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                               __float_as_uint(v[3])});
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
-            kminc = max(kminc, (uint32_t)__shfl_xor((int)kminc, off));
-        }
+        kmax = wave_max_u32(kmax);
+        kminc = wave_max_u32(kminc);
         if (lane == 0) {
             sm.mm[wave][0] = kmax;
             sm.mm[wave][1] = kminc;
@@ -414,11 +408,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         // team max / min from the members' slots
         {
             uint32_t a = tid < f.team_size ? sa[0] : 0u, cmin = tid < f.team_size ? sa[1] : 0u;
-#pragma unroll
-            for (int o2 = 32; o2 >= 1; o2 >>= 1) {
-                a = max(a, (uint32_t)__shfl_xor((int)a, o2));
-                cmin = max(cmin, (uint32_t)__shfl_xor((int)cmin, o2));
-            }
+            a = wave_max_u32(a);
+            cmin = wave_max_u32(cmin);
             if (lane == 0) {
                 sm.mm[wave][0] = a;
                 sm.mm[wave][1] = cmin;
@@ -489,8 +480,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             });
         }
         if constexpr (MASK) {
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) ninf += (uint32_t)__shfl_xor((int)ninf, off);
+            ninf = wave_sum_u32(ninf);
             if (lane == 0 && ninf) atomicAdd(&sm.hist[0], ninf);
         }
         __syncthreads();
@@ -898,8 +888,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     if (wave == kThreads / 64 - 1) {
         uint32_t pre = 0;
         for (int j = lane; j < m; j += 64) pre += sm.cnt[j];
-#pragma unroll
-        for (int o2 = 32; o2 >= 1; o2 >>= 1) pre += (uint32_t)__shfl_xor((int)pre, o2);
+        pre = wave_sum_u32(pre);
         const int per = (n + 63) / 64;
         const int t0 = lane * per, t1 = min(t0 + per, n);
         uint32_t mine = 0;

@@ -15,6 +15,78 @@ __device__ inline void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Cross-lane exchanges without LDS traffic.  V_PERMLANE16_SWAP / V_PERMLANE32_SWAP swap a
+// register's odd 16-lane rows with another's even rows (its upper 32 lanes with another's
+// lower 32).  Swapping x with itself leaves, in lane i, x of lane i and of lane i ^ 16
+// (i ^ 32) in the two results: the first holds the partner's value in lanes with bit 4
+// (bit 5) set, the second in the others.  The 2-element results are bit-cast whole.
+__device__ inline uint64_t swap16_pair(uint32_t x) {
+    return __builtin_bit_cast(uint64_t, __builtin_amdgcn_permlane16_swap(x, x, false, false));
+}
+__device__ inline uint64_t swap32_pair(uint32_t x) {
+    return __builtin_bit_cast(uint64_t, __builtin_amdgcn_permlane32_swap(x, x, false, false));
+}
+// x of lane i ^ 16 / i ^ 32
+__device__ inline float xor16_f(float x) {
+    const uint64_t p = swap16_pair(__float_as_uint(x));
+    return __uint_as_float((threadIdx.x & 16) ? (uint32_t)p : (uint32_t)(p >> 32));
+}
+__device__ inline float xor32_f(float x) {
+    const uint64_t p = swap32_pair(__float_as_uint(x));
+    return __uint_as_float((threadIdx.x & 32) ? (uint32_t)p : (uint32_t)(p >> 32));
+}
+// Max / sum over the four lanes i, i^16, i^32, i^48 (every one of them gets it).
+__device__ inline float group4_max(float x) {
+    uint64_t p = swap16_pair(__float_as_uint(x));
+    x = fmaxf(__uint_as_float((uint32_t)p), __uint_as_float((uint32_t)(p >> 32)));
+    p = swap32_pair(__float_as_uint(x));
+    return fmaxf(__uint_as_float((uint32_t)p), __uint_as_float((uint32_t)(p >> 32)));
+}
+__device__ inline float group4_sum(float x) {
+    uint64_t p = swap16_pair(__float_as_uint(x));
+    x = __uint_as_float((uint32_t)p) + __uint_as_float((uint32_t)(p >> 32));
+    p = swap32_pair(__float_as_uint(x));
+    return __uint_as_float((uint32_t)p) + __uint_as_float((uint32_t)(p >> 32));
+}
+// Reduction over the 64 lanes of a wave with a commutative, associative op on 32-bit
+// values, every lane getting the result: quad permutations and the mirrors within 8 and 16
+// lanes (DPP), then the two swaps.  Every lane of the wave must be active.
+template <typename Op>
+__device__ inline uint32_t wave_reduce(uint32_t v, Op op) {
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+    uint64_t p = swap16_pair(v);
+    v = op((uint32_t)p, (uint32_t)(p >> 32));
+    p = swap32_pair(v);
+    return op((uint32_t)p, (uint32_t)(p >> 32));
+}
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+    return wave_reduce(v, [](uint32_t x, uint32_t y) { return max(x, y); });
+}
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+    return wave_reduce(v, [](uint32_t x, uint32_t y) { return min(x, y); });
+}
+__device__ inline uint32_t wave_sum_u32(uint32_t v) {
+    return wave_reduce(v, [](uint32_t x, uint32_t y) { return x + y; });
+}
+__device__ inline float wave_max_f(float v) {
+    return __uint_as_float(wave_reduce(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+        return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
+    }));
+}
+__device__ inline float wave_min_f(float v) {
+    return __uint_as_float(wave_reduce(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+        return __float_as_uint(fminf(__uint_as_float(x), __uint_as_float(y)));
+    }));
+}
+__device__ inline float wave_sum_f(float v) {
+    return __uint_as_float(wave_reduce(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+        return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+    }));
+}
+
 // ---------------------------------------------------------------------------
 // Indexer tile (V_MFMA_SCALE_F32_16X16X128_F8F6F4).
 //
@@ -127,10 +199,10 @@ __device__ inline float idx_score4(const IdxQuery<DI, FMT, HT> &q, const IdxKeys
     const bool hi2 = g >= 2, hi1 = g & 1;
     float k0 = hi2 ? part[2] : part[0], k1 = hi2 ? part[3] : part[1];
     const float s0 = hi2 ? part[0] : part[2], s1 = hi2 ? part[1] : part[3];
-    k0 += __shfl_xor(s0, 32);
-    k1 += __shfl_xor(s1, 32);
+    k0 += xor32_f(s0);
+    k1 += xor32_f(s1);
     float keep = hi1 ? k1 : k0;
-    keep += __shfl_xor(hi1 ? k0 : k1, 16);
+    keep += xor16_f(hi1 ? k0 : k1);
     return keep;
 }
 
@@ -391,8 +463,7 @@ __device__ inline void attn_tile_compute(AttnState<D> &st, const bf16x8 (&qb)[D 
             x[4 * half + r] = val;
             tmax = fmaxf(tmax, val);
         }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = group4_max(tmax);
     // Lazy rescale: the reference max st.m moves (and O and l are rescaled) only when the
     // tile's max exceeds it by more than 8 in log2 units, so probabilities stay <= 2^8
     // (exact in fp32, and within bf16 range for P) and most tiles skip the rescale.  The
@@ -439,8 +510,7 @@ __device__ inline void attn_tile_compute(AttnState<D> &st, const bf16x8 (&qb)[D 
 // Finish a wave: the normaliser summed over the wave (m is already uniform per head).
 template <int D>
 __device__ inline void attn_wave_total(AttnState<D> &st) {
-    st.l += __shfl_xor(st.l, 16);
-    st.l += __shfl_xor(st.l, 32);
+    st.l = group4_sum(st.l);
 }
 
 // Row stride (floats) of the wave states in LDS: dv plus 4, so that the 16 heads of a wave

@@ -247,11 +247,8 @@ __global__ __launch_bounds__(kSelThreads, 4) void topk_rows_kernel(TopkArgs a) {
             kmax = max(kmax, k);
             kmin = min(kmin, k);
         }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
-        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
-    }
+    kmax = wave_max_u32(kmax);
+    kmin = wave_min_u32(kmin);
     if (lane == 0) {
         mm[wave][0] = kmax;
         mm[wave][1] = kmin;
