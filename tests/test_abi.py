@@ -141,6 +141,10 @@ def test_attention_refusals(lib):
     assert attn_call(lib, K=2048, T_cap=4096, ws=None, ws_bytes=0) == 5
     assert attn_call(lib, K=2048, T_cap=4096, ws_bytes=need - 1) == 5
     assert attn_call(lib, B=0) == 0
+    # one sequence's source must stay below 2 GiB (rows are addressed by 32-bit offsets)
+    assert attn_call(lib, T_cap=(1 << 23)) == 4      # 8M rows x 128 dims x 2 bytes = 2 GiB
+    assert attn_call(lib, R=(1 << 23)) == 4
+    assert attn_call(lib, T_cap=(1 << 23) - 1, B=0) == 0
 
 
 def test_attention_layers_refusals(lib):
