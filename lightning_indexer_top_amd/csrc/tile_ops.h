@@ -173,9 +173,9 @@ __device__ inline float relu_bits(float x) { return __int_as_float(max(__float_a
 
 // Scores of four 16-key tiles for one query.  All 4*HT MFMAs are issued first; each
 // lane then holds, per tile, the head-weighted ReLU sum over its 4 heads of every head
-// tile, and the sum over the four lane groups is a packed butterfly: across lanes 32
-// apart each lane keeps two tiles and sends two, across lanes 16 apart it keeps one and
-// sends one.  Lane (g, c) returns the score of key c of tile g.
+// tile, and the sum over the four lane groups takes three lane swaps and three adds:
+// across lanes 32 apart each lane keeps two tiles and sends two, across lanes 16 apart it
+// keeps one and sends one.  Lane (g, c) returns the score of key c of tile g.
 template <int DI, int FMT, int HT>
 __device__ inline float idx_score4(const IdxQuery<DI, FMT, HT> &q, const IdxKeys (&k)[4], int g) {
     // operand type codes of the instruction: 0 = e4m3, 4 = e2m1
@@ -196,14 +196,20 @@ __device__ inline float idx_score4(const IdxQuery<DI, FMT, HT> &q, const IdxKeys
 #pragma unroll
             for (int r = 0; r < 4; ++r) part[u] += q.w[ht][r] * relu_bits(acc[u][ht][r]);
     }
-    const bool hi2 = g >= 2, hi1 = g & 1;
-    float k0 = hi2 ? part[2] : part[0], k1 = hi2 ? part[3] : part[1];
-    const float s0 = hi2 ? part[0] : part[2], s1 = hi2 ? part[1] : part[3];
-    k0 += xor32_f(s0);
-    k1 += xor32_f(s1);
-    float keep = hi1 ? k1 : k0;
-    keep += xor16_f(hi1 ? k0 : k1);
-    return keep;
+    // Lane group g ends with tile g's scores.  Swapping the upper half of tile 0's partials
+    // with the lower half of tile 2's (and 1 with 3) and adding puts the sum over lane
+    // groups {0, 2} / {1, 3} of tile 0 (1) in lanes 0-31 and of tile 2 (3) in lanes 32-63;
+    // swapping the odd 16-lane rows of the first sum with the even rows of the second and
+    // adding completes tile g in row g.
+    const uint64_t a = __builtin_bit_cast(
+        uint64_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false));
+    const uint64_t b = __builtin_bit_cast(
+        uint64_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false));
+    const float k02 = __uint_as_float((uint32_t)a) + __uint_as_float((uint32_t)(a >> 32));
+    const float k13 = __uint_as_float((uint32_t)b) + __uint_as_float((uint32_t)(b >> 32));
+    const uint64_t c2 = __builtin_bit_cast(
+        uint64_t, __builtin_amdgcn_permlane16_swap(__float_as_uint(k02), __float_as_uint(k13), false, false));
+    return __uint_as_float((uint32_t)c2) + __uint_as_float((uint32_t)(c2 >> 32));
 }
 
 // ---------------------------------------------------------------------------
