@@ -240,6 +240,124 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_staged_kernel(Inde
     }
 }
 
+// 16 index heads of 64 e4m3 dims (the chunked-prefill shape): V_MFMA_SCALE_F32_32X32X64_F8F6F4
+// takes two queries' 16 heads as its 32 rows and 32 keys as its columns.  Its 64-deep K is
+// exactly a head's dims, where the 16x16x128 form carries a zero half, so a query needs half
+// the MFMA passes.  Operand layout, measured with an on-GPU probe: lane 32g + r holds row r,
+// its bytes 0-15 belong to K block 0 and bytes 16-31 to K block 1, and lane group g
+// supplies block g's scale; a lane therefore loads row bytes [16g, 16g+16) and
+// [32+16g, 32+16g+16) and the row's scale byte g (the order of K within a block is the same
+// for both operands, so it does not matter).  The result comes back as lane 32g + c,
+// register 4i + r = row 8i + 4g + r, column c: rows 0-15 are the first query's heads.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ inline i32x8 mx32_operand(const uint8_t *row, int g) {
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(row + 16 * g);
+    const u32x4 hi = *reinterpret_cast<const u32x4 *>(row + 32 + 16 * g);
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+__global__ __launch_bounds__(kWaves * 64) void indexer_scores_mx32_kernel(IndexerArgs a) {
+    constexpr int NH = 16, E = 64, NB = 2;
+    __shared__ __attribute__((aligned(16))) uint8_t qc[kQB][NH * E];   // codes
+    __shared__ __attribute__((aligned(16))) float qw[kQB][NH];         // head weights
+    __shared__ uint8_t qs[kQB][NH * NB];                               // scale bytes
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 5;
+    const int c = lane & 31;
+
+    const int n_groups = (a.S + kQB - 1) / kQB;
+    const int b = blockIdx.y / n_groups;
+    const int i0 = (blockIdx.y % n_groups) * kQB;
+    const int i1 = min(i0 + kQB, a.S);
+    const int nq = i1 - i0;
+    const int tb0 = blockIdx.x * kWaves * 64;  // the block's first key
+    if (tb0 >= a.T) return;
+    const size_t bs0 = (size_t)b * a.S;
+
+    // stage the block's queries (a whole workgroup returns together above, so every
+    // thread reaches the barrier)
+    {
+        const uint8_t *src = a.q8 + (bs0 + i0) * NH * E;
+        const int n16 = nq * NH * E / 16;
+        for (int j = threadIdx.x; j < n16; j += kWaves * 64)
+            reinterpret_cast<u32x4 *>(&qc[0][0])[j] = reinterpret_cast<const u32x4 *>(src)[j];
+        const float *wsrc = a.w + (bs0 + i0) * NH;
+        for (int j = threadIdx.x; j < nq * NH; j += kWaves * 64) (&qw[0][0])[j] = wsrc[j];
+        const uint8_t *ssrc = a.q_sc + (bs0 + i0) * NH * NB;
+        for (int j = threadIdx.x; j < nq * NH * NB; j += kWaves * 64) (&qs[0][0])[j] = ssrc[j];
+    }
+    __syncthreads();
+
+    const int t0 = tb0 + wave * 64;  // this wave's 64 keys: columns c of two 32-key operands
+    if (t0 >= a.T) return;
+    const int vis_max = min(a.T, (a.start_pos + i1) / a.ratio);
+    if (t0 >= vis_max) {  // nothing visible to any query of the block in these keys
+        const int tt = t0 + lane;
+        if (tt < a.T)
+            for (int i = i0; i < i1; ++i) a.scores[(bs0 + i) * a.ld + tt] = -INFINITY;
+        return;
+    }
+    i32x8 kb[2];
+    int ks[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const size_t row = (size_t)b * a.T_cap + min(t0 + 32 * m + c, a.T - 1);
+        kb[m] = mx32_operand(a.k8 + row * E, g);
+        ks[m] = a.k_sc[row * NB + g];
+    }
+    const int h = c & 15;
+    for (int qa = 0; qa < nq; qa += 2) {
+        // rows 0-15: query qa's heads, rows 16-31: query qa+1's (query qa again past the
+        // block's end; that half's scores are not stored)
+        const int qb = min(qa + 1, nq - 1);
+        const int qr = c < 16 ? qa : qb;
+        const i32x8 av = mx32_operand(&qc[qr][h * E], g);
+        const int as = qs[qr][h * NB + g];
+        f32x16 acc[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            acc[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, kb[m], f32x16{}, 0, 0, 0, as, 0, ks[m]);
+        // the head weights of the rows this lane receives: heads 4g+r and 8+4g+r of each query
+        const f32x4 wa0 = *reinterpret_cast<const f32x4 *>(&qw[qa][4 * g]);
+        const f32x4 wa1 = *reinterpret_cast<const f32x4 *>(&qw[qa][8 + 4 * g]);
+        const f32x4 wb0 = *reinterpret_cast<const f32x4 *>(&qw[qb][4 * g]);
+        const f32x4 wb1 = *reinterpret_cast<const f32x4 *>(&qw[qb][8 + 4 * g]);
+        float sc[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            float sa = 0.f, sb = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sa += wa0[r] * relu_bits(acc[m][r]);
+                sa += wa1[r] * relu_bits(acc[m][4 + r]);
+                sb += wb0[r] * relu_bits(acc[m][8 + r]);
+                sb += wb1[r] * relu_bits(acc[m][12 + r]);
+            }
+            // lanes 32 apart hold the two halves of each query's heads: swapping the upper
+            // half of sa with the lower half of sb and adding leaves query qa's score in
+            // lanes 0-31 and query qa+1's in lanes 32-63
+            const uint64_t x = __builtin_bit_cast(
+                uint64_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(sa), __float_as_uint(sb), false, false));
+            sc[m] = __uint_as_float((uint32_t)x) + __uint_as_float((uint32_t)(x >> 32));
+        }
+        // the two queries' visible counts on the scalar unit (a lane-dependent numerator would
+        // make this a vector division)
+        const int va = __builtin_amdgcn_readfirstlane((a.start_pos + i0 + qa + 1) / a.ratio);
+        const int vb = __builtin_amdgcn_readfirstlane((a.start_pos + i0 + qa + 2) / a.ratio);
+        if (qa + g < nq) {
+            const int vis = g ? vb : va;
+            float *dst = a.scores + (bs0 + i0 + qa + g) * a.ld;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int t = t0 + 32 * m + c;
+                if (t < a.T) dst[t] = t < vis ? sc[m] : -INFINITY;
+            }
+        }
+    }
+}
+
 template <int DI, int FMT, int HT>
 hipError_t launch_staged(const IndexerArgs &a, hipStream_t stream) {
     const int keys_per_block = kWaves * 16 * kU;
@@ -250,6 +368,11 @@ hipError_t launch_staged(const IndexerArgs &a, hipStream_t stream) {
 
 template <int DI, int FMT, int HT>
 hipError_t launch_multi(const IndexerArgs &a, hipStream_t stream) {
+    if constexpr (DI == 64 && FMT == kFmtE4M3 && HT == 1) {
+        dim3 grid((a.T + kWaves * 64 - 1) / (kWaves * 64), a.B * ((a.S + kQB - 1) / kQB));
+        hipLaunchKernelGGL(indexer_scores_mx32_kernel, grid, dim3(kWaves * 64), 0, stream, a);
+        return hipGetLastError();
+    }
     if constexpr (staged_query_bytes<DI, FMT, HT>() <= 2304) return launch_staged<DI, FMT, HT>(a, stream);
     const int keys_per_block = kWaves * 16 * kU;
     dim3 grid((a.T + keys_per_block - 1) / keys_per_block, a.B * ((a.S + kQB - 1) / kQB));

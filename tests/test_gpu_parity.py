@@ -43,6 +43,8 @@ INDEXER_CASES = [
     (2, 37, 100, 3, 32, 64),     # chunk after cached tokens, groups of 2 queries
     (1, 45, 300, 4, 64, 128),
     (1, 9, 20, 1, 48, 128),      # three head tiles
+    (1, 33, 500, 2, 16, 64),     # 16 heads x 64 in query pairs: a last block of one query
+    (2, 19, 1000, 1, 16, 64),    # two sequences, an odd last block, a ragged key tail
 ]
 
 
