@@ -289,20 +289,32 @@ __global__ __launch_bounds__(kSelThreads, 4) void topk_rows_kernel(TopkArgs a) {
     const int vb = sm.bin;
     const int need = a.keff - sm.above;
     const int cnt = (int)sm.hist[vb];
+    // per element (bit 4r+e): its bin is above vb (gm) or is vb (cm, the candidates).  On
+    // the packed bins (<= kVBins, 16 bits each): adding 0x7fff - vb (0x8000 - vb) to a half
+    // sets its bit 15 exactly when the bin is above (at least) vb, with no carry between
+    // the halves.
+    uint32_t gm = 0u, cm = 0u;
+    {
+        const uint32_t kgt = (0x7fffu - (uint32_t)vb) * 0x10001u;
+        const uint32_t kge = (0x8000u - (uint32_t)vb) * 0x10001u;
+        auto nib = [](uint32_t x0, uint32_t x1) {
+            return ((x0 >> 15) & 1u) | ((x0 >> 30) & 2u) | ((x1 >> 13) & 4u) | ((x1 >> 28) & 8u);
+        };
+#pragma unroll
+        for (int r = 0; r < kRowQ; ++r) {
+            const uint32_t a0 = bins[2 * r] + kgt, a1 = bins[2 * r + 1] + kgt;
+            const uint32_t b0 = bins[2 * r] + kge, b1 = bins[2 * r + 1] + kge;
+            gm |= nib(a0 & 0x80008000u, a1 & 0x80008000u) << (4 * r);
+            cm |= nib((a0 ^ b0) & 0x80008000u, (a1 ^ b1) & 0x80008000u) << (4 * r);
+        }
+        gm &= vn;
+        cm &= vn;
+    }
     uint32_t kstar, pstar;
     if (cnt <= kCandCap) {
         // the scores of bin vb as (key << 32 | ~position), in the histogram's place; a
         // block scan over the threads' counts gives each its first slot
         uint64_t *cand = reinterpret_cast<uint64_t *>(sm.hist);
-        uint32_t cm = 0u;
-#pragma unroll
-        for (int r = 0; r < kRowQ; ++r)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t bin = (bins[2 * r + (e >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
-                cm |= (bin == (uint32_t)vb ? 1u : 0u) << (4 * r + e);
-            }
-        cm &= vn;
         uint32_t total;
         const uint32_t mine = (uint32_t)__popc(cm);
         int o = (int)(wg_scan<kSelThreads / 64>(mine, sm.wsum, &total) - mine);  // every thread has read hist[vb]
@@ -324,24 +336,29 @@ __global__ __launch_bounds__(kSelThreads, 4) void topk_rows_kernel(TopkArgs a) {
     kstar = sm.kstar;
     pstar = (uint32_t)sm.pstar;
 
-    // output: a pick is key > kstar, or key == kstar at a position <= pstar.  The picks
-    // become a bitmap over positions in LDS (h2 is free again; word w covers positions
-    // 32w..32w+31, assembled from 8 lanes' nibbles), and thread t then writes the picks
-    // of word t at the offset one block scan gives it, in ascending order.
+    // output: a pick is key > kstar, or key == kstar at a position <= pstar: every element
+    // above bin vb, and the candidates (bin vb) that pass the test.  The picks become a
+    // bitmap over positions in LDS (h2 is free again; word w covers positions 32w..32w+31,
+    // assembled from 8 lanes' nibbles), and thread t then writes the picks of word t at the
+    // offset one block scan gives it, in ascending order.
+    uint32_t pm = gm;
+    if (cm) {
+#pragma unroll
+        for (int r = 0; r < kRowQ; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if ((cm >> (4 * r + e)) & 1u) {
+                    const uint32_t k = order_key(v[r][e]);
+                    if (k > kstar || (k == kstar && (uint32_t)pos(r, e) <= pstar)) pm |= 1u << (4 * r + e);
+                }
+    }
     uint32_t *bm = h2;
 #pragma unroll
     for (int r = 0; r < kRowQ; ++r) {
-        uint32_t nib = 0u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t k = order_key(v[r][e]);
-            const bool pick = k > kstar || (k == kstar && (uint32_t)pos(r, e) <= pstar);
-            nib |= (pick ? 1u : 0u) << e;
-        }
         // OR over the 8 lanes: swap neighbours, swap pairs (DPP quad permutations), then
         // mirror within the half-row of 8 lanes
-        nib &= vn >> (4 * r);
-        int x = (int)((nib & 0xFu) << (4 * (tid & 7)));
+        const uint32_t nib = (pm >> (4 * r)) & 0xFu;
+        int x = (int)(nib << (4 * (tid & 7)));
         x |= __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);
         x |= __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);
         x |= __builtin_amdgcn_update_dpp(0, x, 0x141, 0xf, 0xf, false);
