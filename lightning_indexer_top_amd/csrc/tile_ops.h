@@ -26,15 +26,6 @@ __device__ inline uint64_t swap16_pair(uint32_t x) {
 __device__ inline uint64_t swap32_pair(uint32_t x) {
     return __builtin_bit_cast(uint64_t, __builtin_amdgcn_permlane32_swap(x, x, false, false));
 }
-// x of lane i ^ 16 / i ^ 32
-__device__ inline float xor16_f(float x) {
-    const uint64_t p = swap16_pair(__float_as_uint(x));
-    return __uint_as_float((threadIdx.x & 16) ? (uint32_t)p : (uint32_t)(p >> 32));
-}
-__device__ inline float xor32_f(float x) {
-    const uint64_t p = swap32_pair(__float_as_uint(x));
-    return __uint_as_float((threadIdx.x & 32) ? (uint32_t)p : (uint32_t)(p >> 32));
-}
 // Max / sum over the four lanes i, i^16, i^32, i^48 (every one of them gets it).
 __device__ inline float group4_max(float x) {
     uint64_t p = swap16_pair(__float_as_uint(x));
