@@ -190,6 +190,7 @@ ATTN_CASES = [
     (1, 200, 1000, 2, 128, 128, 128, 50, {}),               # many queries: one split each
     (1, 40, 0, 2, 128, 64, 16, 8, {"repeat": True}),        # prefill from 0, repeated rows
     (2, 1, 5000, 2, 128, 128, 128, 500, {"sink": "mixed"}),
+    (3, 1, 2000, 2, 128, 128, 45, 333, {"minus_ones": 5}),  # 45 window rows padded to 64; 4 splits
 ]
 
 
