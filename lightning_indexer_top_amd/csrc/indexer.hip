@@ -276,6 +276,21 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_mx32_kernel(Indexe
     if (tb0 >= a.T) return;
     const size_t bs0 = (size_t)b * a.S;
 
+    // this wave's 64 keys (columns c of two 32-key operands), requested before the query
+    // staging so that the two round trips overlap (the barrier below waits for both)
+    const int t0 = tb0 + wave * 64;
+    const int vis_max = min(a.T, (a.start_pos + i1) / a.ratio);
+    i32x8 kb[2] = {};
+    int ks[2] = {127, 127};
+    if (t0 < vis_max) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const size_t row = (size_t)b * a.T_cap + min(t0 + 32 * m + c, a.T - 1);
+            kb[m] = mx32_operand(a.k8 + row * E, g);
+            ks[m] = a.k_sc[row * NB + g];
+        }
+    }
+
     // stage the block's queries (a whole workgroup returns together above, so every
     // thread reaches the barrier)
     {
@@ -290,22 +305,12 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_mx32_kernel(Indexe
     }
     __syncthreads();
 
-    const int t0 = tb0 + wave * 64;  // this wave's 64 keys: columns c of two 32-key operands
     if (t0 >= a.T) return;
-    const int vis_max = min(a.T, (a.start_pos + i1) / a.ratio);
     if (t0 >= vis_max) {  // nothing visible to any query of the block in these keys
         const int tt = t0 + lane;
         if (tt < a.T)
             for (int i = i0; i < i1; ++i) a.scores[(bs0 + i) * a.ld + tt] = -INFINITY;
         return;
-    }
-    i32x8 kb[2];
-    int ks[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const size_t row = (size_t)b * a.T_cap + min(t0 + 32 * m + c, a.T - 1);
-        kb[m] = mx32_operand(a.k8 + row * E, g);
-        ks[m] = a.k_sc[row * NB + g];
     }
     const int h = c & 15;
     for (int qa = 0; qa < nq; qa += 2) {
