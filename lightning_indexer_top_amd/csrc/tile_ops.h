@@ -492,12 +492,20 @@ __device__ inline void attn_tile_compute(AttnState<D> &st, const bf16x8 (&qb)[D 
     // 4g..4g+3; a second read 16 rows down gives rows 16+4g..16+4g+3.
     lds_v4s *v0 = (lds_v4s *)((lds_u16 *)tile + (4 * g + (c >> 2)) * LD + 4 * (c & 3));
     lds_v4s *v1 = (lds_v4s *)((lds_u16 *)tile + (16 + 4 * g + (c >> 2)) * LD + 4 * (c & 3));
+    // Every column tile is read (all within the row's D dims) before the first product, so
+    // the reads' LDS latency is paid once rather than once per output tile; only the ndt
+    // tiles of dv are accumulated.
+    v4s lo[NT], hi[NT];
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+        lo[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v0 + 4 * dt);
+        hi[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v1 + 4 * dt);
+    }
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt) {
         if (dt < ndt) {
-            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v0 + 4 * dt);
-            const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v1 + 4 * dt);
-            const bf16x8 va = __builtin_bit_cast(bf16x8, (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            const bf16x8 va = __builtin_bit_cast(
+                bf16x8, (v8s){lo[dt][0], lo[dt][1], lo[dt][2], lo[dt][3], hi[dt][0], hi[dt][1], hi[dt][2], hi[dt][3]});
             st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.o[dt], 0, 0, 0);
         }
     }
