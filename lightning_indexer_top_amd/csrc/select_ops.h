@@ -1,5 +1,6 @@
-// select_ops.h -- exact k-th selection over fp32 scores in one 256-thread workgroup, shared
-// by the fused decode step and the many-row top-k kernel.
+// select_ops.h -- exact k-th selection over fp32 scores in one workgroup (256 threads, or
+// 1024 for rows of up to 32768 positions), shared by the fused decode step and the row
+// top-k kernel.
 //
 // The selection is exact: the k-th largest score by (order key desc, position asc), so
 // equal scores go to the lower position.  Level one is a 4096-bin histogram of the
@@ -21,15 +22,17 @@ constexpr int kVBins = 4096;      // value bins of the first level (+ one spill 
 constexpr int kCandCap = 2048;    // candidates held in LDS (more take the radix levels)
 constexpr int kRankDirect = 128;  // candidates ranked directly (more are narrowed first)
 
-// LDS of a selecting workgroup.  The histogram doubles as the candidate buffer.
-struct SelLds {
+// LDS of a selecting workgroup of NT threads.  The histogram doubles as the candidate buffer.
+template <int NT>
+struct SelLdsT {
     alignas(16) uint32_t hist[kBins + 4];  // + the spill bin of the value level
-    uint64_t red64[kSelThreads / 64][2];
-    uint32_t wsum[kSelThreads / 64];
+    uint64_t red64[NT / 64][2];
+    uint32_t wsum[NT / 64];
     int bin, above, ncand;
     uint32_t kstar;
     int pstar;
 };
+using SelLds = SelLdsT<kSelThreads>;
 
 // The float of an order key (inverse of order_key; -0 comes back as +0).
 __device__ inline float key_float(uint32_t k) {
@@ -39,13 +42,14 @@ __device__ inline float key_float(uint32_t k) {
 // Bin search from the top over `nbins` LDS counters (256, 1024 or 4096): the bin where
 // the count from the top reaches `need`, and the count strictly above it.  Thread t holds
 // the contiguous bins [nbins - per*(t+1), nbins - per*t), read as 16-byte words.
+template <int NT = kSelThreads>
 __device__ inline void find_bin(const uint32_t *hist, int nbins, int need, uint32_t *wsum, int *out_bin,
                                 int *out_above) {
     if (threadIdx.x == 0) {
         *out_bin = 0;
         *out_above = 0;
     }
-    const int per = nbins / kSelThreads;
+    const int per = nbins / NT;
     const int lo = nbins - per * ((int)threadIdx.x + 1);
     uint32_t cnt[16];
     if (per == 1) {
@@ -64,7 +68,7 @@ __device__ inline void find_bin(const uint32_t *hist, int nbins, int need, uint3
 #pragma unroll
     for (int j = 0; j < 16; ++j) mine += cnt[j];
     uint32_t total;
-    const uint32_t incl = wg_scan<kSelThreads / 64>(mine, wsum, &total);
+    const uint32_t incl = wg_scan<NT / 64>(mine, wsum, &total);
     int above = (int)(incl - mine);
     if (above < need && need <= (int)incl) {
         int found = 0, fa = 0;
@@ -96,9 +100,10 @@ __device__ inline int value_bin(float v, float scale, float bias) {
 // value bin vb, the need-th by (order key desc, position asc).  Threads take contiguous
 // position ranges so the final tie cut can walk positions in order; score(t) reads the
 // score at position t.
-template <typename Score>
-__device__ inline void radix_resolve(SelLds &sm, Score score, int nvis, float scale, float bias, int vb, int need) {
-    const int per = (nvis + kSelThreads - 1) / kSelThreads;
+template <int NT, typename Score>
+__device__ inline void radix_resolve(SelLdsT<NT> &sm, Score score, int nvis, float scale, float bias, int vb,
+                                     int need) {
+    const int per = (nvis + NT - 1) / NT;
     const int t0 = threadIdx.x * per, t1 = min(t0 + per, nvis);
     auto in_bin = [&](float v) { return value_bin(v, scale, bias) == vb; };
     uint32_t prefix = 0u, pmask = 0u;
@@ -106,7 +111,7 @@ __device__ inline void radix_resolve(SelLds &sm, Score score, int nvis, float sc
     const int widths[3] = {12, 12, 8};
     for (int lv = 0; lv < 3; ++lv) {
         const int nb = 1 << widths[lv];
-        for (int j = threadIdx.x; j < kBins; j += kSelThreads) sm.hist[j] = 0u;
+        for (int j = threadIdx.x; j < kBins; j += NT) sm.hist[j] = 0u;
         __syncthreads();
         for (int t = t0; t < t1; ++t) {
             const float v = score(t);
@@ -114,7 +119,7 @@ __device__ inline void radix_resolve(SelLds &sm, Score score, int nvis, float sc
             if (in_bin(v) && (k & pmask) == prefix) atomicAdd(&sm.hist[(k >> shifts[lv]) & (nb - 1)], 1u);
         }
         __syncthreads();
-        find_bin(sm.hist, nb < kSelThreads ? kSelThreads : nb, need, sm.wsum, &sm.bin, &sm.above);
+        find_bin<NT>(sm.hist, nb < NT ? NT : nb, need, sm.wsum, &sm.bin, &sm.above);
         prefix |= (uint32_t)sm.bin << shifts[lv];
         pmask |= (uint32_t)(nb - 1) << shifts[lv];
         need -= sm.above;
@@ -127,7 +132,7 @@ __device__ inline void radix_resolve(SelLds &sm, Score score, int nvis, float sc
         eq += in_bin(v) && order_key(v) == prefix;
     }
     uint32_t total;
-    const uint32_t incl = wg_scan<kSelThreads / 64>(eq, sm.wsum, &total);
+    const uint32_t incl = wg_scan<NT / 64>(eq, sm.wsum, &total);
     int before = (int)(incl - eq);
     if (before < need && need <= (int)incl) {
         for (int t = t0; t < t1; ++t) {
@@ -148,15 +153,16 @@ __device__ inline void radix_resolve(SelLds &sm, Score score, int nvis, float sc
 // where the count from the top reaches need, and only that bin's candidates kept; need
 // becomes the rank within them.  Clustered scores put hundreds of candidates into one
 // value bin, and the direct rank costs cnt^2 comparisons.  h2 is 4096 words of LDS.
-__device__ inline void refine_candidates(uint64_t *cand, int &cnt, int &need, uint32_t *h2, SelLds &sm) {
-    constexpr int kPer = kCandCap / kSelThreads;
+template <int NT>
+__device__ inline void refine_candidates(uint64_t *cand, int &cnt, int &need, uint32_t *h2, SelLdsT<NT> &sm) {
+    constexpr int kPer = kCandCap / NT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int round = 0; round < 8 && cnt > kRankDirect; ++round) {
         uint64_t cv[kPer];
         uint64_t lo = ~0ull, hi = 0ull;
 #pragma unroll
         for (int r = 0; r < kPer; ++r) {
-            const int j = tid + kSelThreads * r;
+            const int j = tid + NT * r;
             cv[r] = j < cnt ? cand[j] : 0ull;
             if (j < cnt) {
                 lo = min(lo, cv[r]);
@@ -176,11 +182,11 @@ __device__ inline void refine_candidates(uint64_t *cand, int &cnt, int &need, ui
             sm.red64[wave][0] = lo;
             sm.red64[wave][1] = hi;
         }
-        for (int j = tid; j < kBins / 4; j += kSelThreads) reinterpret_cast<u32x4 *>(h2)[j] = u32x4{0u, 0u, 0u, 0u};
+        for (int j = tid; j < kBins / 4; j += NT) reinterpret_cast<u32x4 *>(h2)[j] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
         lo = ~0ull;
         hi = 0ull;
-        for (int w = 0; w < kSelThreads / 64; ++w) {
+        for (int w = 0; w < NT / 64; ++w) {
             lo = min(lo, sm.red64[w][0]);
             hi = max(hi, sm.red64[w][1]);
         }
@@ -188,16 +194,16 @@ __device__ inline void refine_candidates(uint64_t *cand, int &cnt, int &need, ui
         auto bin_of = [&](uint64_t v) { return min(kBins - 1, (int)((float)(v - lo) * s2)); };
 #pragma unroll
         for (int r = 0; r < kPer; ++r)
-            if (tid + kSelThreads * r < cnt) atomicAdd(&h2[bin_of(cv[r])], 1u);
+            if (tid + NT * r < cnt) atomicAdd(&h2[bin_of(cv[r])], 1u);
         __syncthreads();
-        find_bin(h2, kBins, need, sm.wsum, &sm.bin, &sm.above);
+        find_bin<NT>(h2, kBins, need, sm.wsum, &sm.bin, &sm.above);
         const int sb = sm.bin;
         need -= sm.above;
         if (tid == 0) sm.ncand = 0;
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < kPer; ++r)
-            if (tid + kSelThreads * r < cnt && bin_of(cv[r]) == sb) cand[atomicAdd(&sm.ncand, 1)] = cv[r];
+            if (tid + NT * r < cnt && bin_of(cv[r]) == sb) cand[atomicAdd(&sm.ncand, 1)] = cv[r];
         __syncthreads();
         cnt = sm.ncand;
     }
@@ -206,8 +212,9 @@ __device__ inline void refine_candidates(uint64_t *cand, int &cnt, int &need, ui
 
 // The direct rank: the candidate with need-1 ahead of it in (key desc, position asc) is
 // the cut; it lands in sm.kstar / sm.pstar.
-__device__ inline void rank_candidates(const uint64_t *cand, int cnt, int need, SelLds &sm) {
-    for (int j = threadIdx.x; j < cnt; j += kSelThreads) {
+template <int NT>
+__device__ inline void rank_candidates(const uint64_t *cand, int cnt, int need, SelLdsT<NT> &sm) {
+    for (int j = threadIdx.x; j < cnt; j += NT) {
         const uint64_t cj = cand[j];
         int rank = 0;
         int o = 0;

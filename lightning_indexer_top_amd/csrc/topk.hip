@@ -196,10 +196,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 
 constexpr int kRowQ = 8;  // score quads per thread: rows of up to 8192 positions
 
-__global__ __launch_bounds__(kSelThreads, 4) void topk_rows_kernel(TopkArgs a) {  // 4 rows a compute unit
-    __shared__ SelLds sm;
+// NT = 256: four rows a compute unit (128 VGPRs); NT = 1024 (rows of up to 32768 positions,
+// few rows): one 16-wave workgroup a row.
+template <int NT>
+__global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void topk_rows_kernel(TopkArgs a) {
+    __shared__ SelLdsT<NT> sm;
     __shared__ __attribute__((aligned(16))) uint32_t h2[kBins];  // candidate refinement
-    __shared__ uint32_t mm[kSelThreads / 64][2];
+    __shared__ uint32_t mm[NT / 64][2];
 
     const int row = blockIdx.x;
     const int i = row % a.S;
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(kSelThreads, 4) void topk_rows_kernel(TopkArgs a) {
     const float *src = a.scores + (size_t)row * a.ld;
 
     if (n <= a.keff) {  // every visible row is picked
-        for (int j = tid; j < a.keff; j += kSelThreads) out[j] = j < n ? j : -1;
+        for (int j = tid; j < a.keff; j += NT) out[j] = j < n ? j : -1;
         return;
     }
 
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(kSelThreads, 4) void topk_rows_kernel(TopkArgs a) {
     uint32_t vn = 0u;
 #pragma unroll
     for (int r = 0; r < kRowQ; ++r) {
-        const int q = tid + kSelThreads * r;
+        const int q = tid + NT * r;
         v[r] = *reinterpret_cast<const f32x4 *>(src + 4 * (4 * q < n ? q : 0));
         vn |= ((1u << min(max(n - 4 * q, 0), 4)) - 1u) << (4 * r);
     }
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(kSelThreads, 4) void topk_rows_kernel(TopkArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (!((vn >> (4 * r + e)) & 1u)) v[r][e] = v0;
-    auto pos = [&](int r, int e) { return 4 * (tid + kSelThreads * r) + e; };
+    auto pos = [&](int r, int e) { return 4 * (tid + NT * r) + e; };
 
     // the row's min and max by order keys (-0 and +0 need not be told apart here: both
     // give the float 0)
@@ -253,12 +256,12 @@ __global__ __launch_bounds__(kSelThreads, 4) void topk_rows_kernel(TopkArgs a) {
         mm[wave][0] = kmax;
         mm[wave][1] = kmin;
     }
-    for (int j = tid; j < kVBins / 4 + 1; j += kSelThreads)  // + the spill bin
+    for (int j = tid; j < kVBins / 4 + 1; j += NT)  // + the spill bin
         reinterpret_cast<u32x4 *>(sm.hist)[j] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     kmax = 0u;
     kmin = ~0u;
-    for (int w = 0; w < kSelThreads / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
         kmax = max(kmax, mm[w][0]);
         kmin = min(kmin, mm[w][1]);
     }
@@ -268,27 +271,32 @@ __global__ __launch_bounds__(kSelThreads, 4) void topk_rows_kernel(TopkArgs a) {
     const float scale = finite && mx > mn ? (float)kVBins / (mx - mn) : 0.f;
     const float bias = finite ? -mn * scale : 0.f;
 
-    // pass 1: value bins (16 bits each, kept) and the histogram
+    // pass 1: value bins (16 bits each, kept) and the histogram.  Quads wholly past the row
+    // add nothing (a wave's quads are consecutive, so this is a wave-uniform skip outside
+    // the boundary wave); thousands of copies of one score would otherwise serialise on one
+    // bin's atomics.
     uint32_t bins[kRowQ * 2];
 #pragma unroll
     for (int r = 0; r < kRowQ; ++r) {
-        uint32_t bb[4];
+        uint32_t bb[4] = {0u, 0u, 0u, 0u};
+        if (4 * (tid + NT * r) < n) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            bb[e] = (uint32_t)value_bin(v[r][e], scale, bias);
-            atomicAdd(&sm.hist[bb[e]], 1u);
+            for (int e = 0; e < 4; ++e) {
+                bb[e] = (uint32_t)value_bin(v[r][e], scale, bias);
+                atomicAdd(&sm.hist[bb[e]], 1u);
+            }
         }
         bins[2 * r] = bb[0] | (bb[1] << 16);
         bins[2 * r + 1] = bb[2] | (bb[3] << 16);
     }
-    // the copies of position 0's score standing in for positions past the row
-    if (tid == 0 && n < kSelThreads * 4 * kRowQ)
-        atomicSub(&sm.hist[value_bin(v0, scale, bias)], (uint32_t)(kSelThreads * 4 * kRowQ - n));
+    // the copies of position 0's score in the row's last, partial quad
+    if (tid == 0 && (n & 3)) atomicSub(&sm.hist[value_bin(v0, scale, bias)], (uint32_t)(4 - (n & 3)));
     __syncthreads();
-    find_bin(sm.hist, kVBins, a.keff, sm.wsum, &sm.bin, &sm.above);
+    find_bin<NT>(sm.hist, kVBins, a.keff, sm.wsum, &sm.bin, &sm.above);
     const int vb = sm.bin;
     const int need = a.keff - sm.above;
     const int cnt = (int)sm.hist[vb];
+    __syncthreads();  // every thread has read hist[vb]: both paths below overwrite the histogram
     // per element (bit 4r+e): its bin is above vb (gm) or is vb (cm, the candidates).  On
     // the packed bins (<= kVBins, 16 bits each): adding 0x7fff - vb (0x8000 - vb) to a half
     // sets its bit 15 exactly when the bin is above (at least) vb, with no carry between
@@ -317,7 +325,7 @@ __global__ __launch_bounds__(kSelThreads, 4) void topk_rows_kernel(TopkArgs a) {
         uint64_t *cand = reinterpret_cast<uint64_t *>(sm.hist);
         uint32_t total;
         const uint32_t mine = (uint32_t)__popc(cm);
-        int o = (int)(wg_scan<kSelThreads / 64>(mine, sm.wsum, &total) - mine);  // every thread has read hist[vb]
+        int o = (int)(wg_scan<NT / 64>(mine, sm.wsum, &total) - mine);
         if (cm) {
 #pragma unroll
             for (int r = 0; r < kRowQ; ++r)
@@ -362,12 +370,12 @@ __global__ __launch_bounds__(kSelThreads, 4) void topk_rows_kernel(TopkArgs a) {
         x |= __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);
         x |= __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);
         x |= __builtin_amdgcn_update_dpp(0, x, 0x141, 0xf, 0xf, false);
-        if ((tid & 7) == 0) bm[kSelThreads / 8 * r + (tid >> 3)] = (uint32_t)x;
+        if ((tid & 7) == 0) bm[NT / 8 * r + (tid >> 3)] = (uint32_t)x;
     }
     __syncthreads();
     uint32_t w = bm[tid];
     uint32_t total;
-    int o = (int)(wg_scan<kSelThreads / 64>((uint32_t)__popc(w), sm.wsum, &total) - (uint32_t)__popc(w));
+    int o = (int)(wg_scan<NT / 64>((uint32_t)__popc(w), sm.wsum, &total) - (uint32_t)__popc(w));
     while (w) {
         const int bit = __builtin_ctz(w);
         w &= w - 1u;
@@ -420,8 +428,13 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL((topk_kernel<32, true>), grid, block, 0, stream, a);
         return hipGetLastError();
     }
-    if (cols <= kSelThreads * 4 * kRowQ && a.B * a.S >= 256) {  // many rows (few: the radix kernel)
-        hipLaunchKernelGGL(topk_rows_kernel, grid, dim3(kSelThreads), 0, stream, a);
+    if (cols <= kSelThreads * 4 * kRowQ && a.B * a.S >= 256) {  // many rows of at most 8192
+        hipLaunchKernelGGL(topk_rows_kernel<kSelThreads>, grid, dim3(kSelThreads), 0, stream, a);
+        return hipGetLastError();
+    }
+    if (cols > kSelThreads * 4 * kRowQ && cols <= 1024 * 4 * kRowQ) {  // few rows of 8193..32768
+        // positions: a 1024-thread workgroup each
+        hipLaunchKernelGGL(topk_rows_kernel<1024>, grid, dim3(1024), 0, stream, a);
         return hipGetLastError();
     }
     if (cols <= kThreads * 4)
