@@ -463,7 +463,9 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                         bb[e] = 4 * (tid + kThreads * r) + e < nvis
                                     ? (uint32_t)value_bin(__uint_as_float(vals[r][e]), scale, bias)
                                     : (uint32_t)kVBins;
-                        hist_add(bb[e], bb[e] == (uint32_t)kVBins ? 0.f : __uint_as_float(vals[r][e]));
+                        // positions past the visible rows add nothing: thousands of them
+                        // counted into the one spill bin would serialise on its atomics
+                        if (bb[e] != (uint32_t)kVBins) hist_add(bb[e], __uint_as_float(vals[r][e]));
                     }
                     bins[2 * r] = bb[0] | (bb[1] << 16);
                     bins[2 * r + 1] = bb[2] | (bb[3] << 16);
