@@ -238,36 +238,51 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void topk_rows_kernel(TopkAr
                 if (!((vn >> (4 * r + e)) & 1u)) v[r][e] = v0;
     auto pos = [&](int r, int e) { return 4 * (tid + NT * r) + e; };
 
-    // the row's min and max by order keys (-0 and +0 need not be told apart here: both
-    // give the float 0)
-    uint32_t kmax = 0u, kmin = ~0u;
+    // the row's min and max by order keys (-0 and +0 need not be told apart here: both give
+    // the float 0), reduced over the workgroup through mm[]
+    auto minmax = [&](bool skip_inf, uint32_t &kmax, uint32_t &kmin) {
+        kmax = 0u;
+        kmin = ~0u;
 #pragma unroll
-    for (int r = 0; r < kRowQ; ++r)
+        for (int r = 0; r < kRowQ; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t u = __float_as_uint(v[r][e]);
-            const uint32_t k = u ^ ((uint32_t)((int)u >> 31) | 0x80000000u);
-            kmax = max(kmax, k);
-            kmin = min(kmin, k);
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t u = __float_as_uint(v[r][e]);
+                const uint32_t k = u ^ ((uint32_t)((int)u >> 31) | 0x80000000u);
+                const bool inf = skip_inf && (u & 0x7fffffffu) == 0x7f800000u;
+                kmax = inf ? kmax : max(kmax, k);
+                kmin = inf ? kmin : min(kmin, k);
+            }
+        kmax = wave_max_u32(kmax);
+        kmin = wave_min_u32(kmin);
+        __syncthreads();  // mm[] of an earlier reduction has been read
+        if (lane == 0) {
+            mm[wave][0] = kmax;
+            mm[wave][1] = kmin;
         }
-    kmax = wave_max_u32(kmax);
-    kmin = wave_min_u32(kmin);
-    if (lane == 0) {
-        mm[wave][0] = kmax;
-        mm[wave][1] = kmin;
-    }
+        __syncthreads();
+        kmax = 0u;
+        kmin = ~0u;
+        for (int w = 0; w < NT / 64; ++w) {
+            kmax = max(kmax, mm[w][0]);
+            kmin = min(kmin, mm[w][1]);
+        }
+    };
     for (int j = tid; j < kVBins / 4 + 1; j += NT)  // + the spill bin
         reinterpret_cast<u32x4 *>(sm.hist)[j] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-    kmax = 0u;
-    kmin = ~0u;
-    for (int w = 0; w < NT / 64; ++w) {
-        kmax = max(kmax, mm[w][0]);
-        kmin = min(kmin, mm[w][1]);
+    uint32_t kmax, kmin;
+    minmax(false, kmax, kmin);
+    float mx = key_float(kmax), mn = key_float(kmin);
+    // An infinite end (level one of the two-level top-k pins one block at +inf) would stretch
+    // the range to nothing: the range is then taken over the finite scores, and an infinity
+    // lands in an end bin, which keeps the map monotone.  No finite score, a NaN, or a span
+    // beyond the float range puts every score into one bin; the exact levels below decide.
+    if (mx == INFINITY || mn == -INFINITY) {
+        minmax(true, kmax, kmin);
+        mx = key_float(kmax);
+        mn = key_float(kmin);
     }
-    const float mx = key_float(kmax), mn = key_float(kmin);
-    // an infinite end puts every score into one bin; the exact levels below then decide
-    const bool finite = mx - mn < INFINITY;
+    const bool finite = kmax >= kmin && mx - mn < INFINITY;
     const float scale = finite && mx > mn ? (float)kVBins / (mx - mn) : 0.f;
     const float bias = finite ? -mn * scale : 0.f;
 
@@ -428,7 +443,7 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL((topk_kernel<32, true>), grid, block, 0, stream, a);
         return hipGetLastError();
     }
-    if (cols <= kSelThreads * 4 * kRowQ && a.B * a.S >= 256) {  // many rows of at most 8192
+    if (cols <= kSelThreads * 4 * kRowQ && cols > 1024) {  // rows of 1025..8192 positions
         hipLaunchKernelGGL(topk_rows_kernel<kSelThreads>, grid, dim3(kSelThreads), 0, stream, a);
         return hipGetLastError();
     }
