@@ -70,6 +70,15 @@ const char *lit_status_str(int status);
 int lit_abi_version(void);
 
 /*
+ * lit_topk_width -- [V4.1] Indexer.forward: the number of entries of each top-k
+ * row, k_eff = min(index_topk, (start_pos + S) / ratio) (integer division), or 0
+ * when ratio < 1 or index_topk < 1.  Every lit_topk / lit_topk_candidates /
+ * lit_sparse_step output list has this width; a query that sees fewer rows pads
+ * its list with -1.  No device work; never fails.
+ */
+int lit_topk_width(int S, int start_pos, int ratio, int index_topk);
+
+/*
  * lit_indexer_scores -- [V4.1] Indexer.forward (score einsum, ReLU, head-weighted
  * sum, then the -inf mask of rows a query cannot see yet); [V3.2] fp8_index.
  *
@@ -296,6 +305,15 @@ lit_status lit_sparse_attn_layers(int L, const uint16_t *q, int B, int S, int H,
                                   size_t ws_bytes, void *stream);
 /* W here is the window list's width (lit_window_width for a derived window). */
 size_t lit_sparse_attn_layers_workspace_bytes(int L, int B, int S, int H, int dv, int W, int K);
+
+/*
+ * lit_compress_writes_row -- [V4.1] Compressor.forward (decode branch): whether
+ * the decode token at start_pos completes its group of ratio tokens, so that
+ * lit_compress_append writes compressed row start_pos / ratio: 1 when
+ * (start_pos + 1) % ratio == 0, else 0 (also 0 for ratio < 1 or start_pos < 0).
+ * No device work; never fails.
+ */
+int lit_compress_writes_row(int start_pos, int ratio);
 
 /*
  * Producer side: the cache writes of one decode step ([V4.1] Compressor.forward,

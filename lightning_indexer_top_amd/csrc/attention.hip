@@ -282,7 +282,7 @@ AttnPlan plan_attention(int B, int S, int list_len) {
     AttnPlan p;
     p.list_len = list_len;
     const int tiles = (list_len + 31) / 32;
-    const int queries = B * S;
+    const int queries = B * S > 0 ? B * S : 1;  // an empty batch sizes like one query
     // Aim for at least ~512 workgroups, but never fewer than one tile per wave.
     int splits = (512 + queries - 1) / queries;
     const int max_splits = (tiles + kWaves - 1) / kWaves;

@@ -107,6 +107,10 @@ size_t fused_ws_bytes(const FusedPlan &p, int dv, int layers) {
            (size_t)p.n_teams * p.team_size * layers * slot_floats(dv) * 4 + 256;     // partial states
 }
 
+size_t fused_part_bytes_per_query(const FusedPlan &p, int dv, int layers) {
+    return (size_t)p.team_size * (size_t)(layers > 0 ? layers : 1) * slot_floats(dv) * 4;
+}
+
 hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream) {
     char *st = (char *)state;
     f.err = (uint32_t *)st;

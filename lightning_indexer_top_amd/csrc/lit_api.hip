@@ -114,6 +114,16 @@ const char *lit_status_str(int status) {
 
 int lit_abi_version(void) { return LIT_ABI_VERSION; }
 
+int lit_topk_width(int S, int start_pos, int ratio, int index_topk) {
+    if (S < 0 || start_pos < 0) return 0;
+    return topk_width(S, start_pos, ratio, index_topk);
+}
+
+int lit_compress_writes_row(int start_pos, int ratio) {
+    if (ratio < 1 || start_pos < 0) return 0;
+    return (start_pos + 1) % ratio == 0 ? 1 : 0;
+}
+
 lit_status lit_indexer_scores_fmt(int index_format, const uint8_t *q8, const uint8_t *q_sc,
                                   const float *w, const uint8_t *k8, const uint8_t *k_sc, int B,
                                   int S, int Hi, int Di, int T_cap, int start_pos, int ratio,
@@ -352,7 +362,7 @@ lit_status lit_compress_append(int B, int D, int ratio, int start_pos, const flo
                                const float *freqs, int n_pos, int rd, uint8_t *codes, uint8_t *scales, int T_cap,
                                uint16_t *latent, void *stream) {
     if (ratio < 1 || start_pos < 0 || T_cap < 0) return LIT_E_SHAPE;
-    const bool done = (start_pos + 1) % ratio == 0;
+    const bool done = lit_compress_writes_row(start_pos, ratio) != 0;
     lit_status st = check_produce(B, D, rd, done ? start_pos + 1 - ratio : 0, done ? n_pos : 1, freqs);
     if (st != LIT_OK) return st;
     if (B == 0) return LIT_OK;
@@ -417,8 +427,11 @@ static FusedPlan step_fused_plan(const lit_step_args *s) {
     const bool layers = step_layers(s) > 1;
     if (layers && (masked || qkv)) return p;
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
-    return plan_fused(s->index_format, masked, qkv, layers, s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D,
-                      s->dv, s->W, keff);
+    p = plan_fused(s->index_format, masked, qkv, layers, s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D,
+                   s->dv, s->W, keff);
+    // partial states are addressed with 32-bit offsets within a query's slots
+    if (p.ok && fused_part_bytes_per_query(p, s->dv, step_layers(s)) >= ((size_t)1 << 31)) p.ok = false;
+    return p;
 }
 
 static lit_status check_step(const lit_step_args *s) {

@@ -16,11 +16,12 @@
 // output offsets, so each selected position lands in its ascending slot with no sort.
 // Rows longer than 1024*ITEMS are processed in segments re-read from L2.
 //
-// Many rows (chunked prefill) of at most 8192 visible scores take a lighter kernel
-// instead: one 256-thread workgroup per row, each thread owning 32
-// consecutive positions in VGPRs, and the value-bin selection of select_ops.h (one
+// Unmasked rows whose score arrays hold 1025..8192 positions take a lighter kernel
+// instead, whatever the number of rows: one 256-thread workgroup per row, each thread
+// owning 32 positions in VGPRs, and the value-bin selection of select_ops.h (one
 // histogram pass, then the few scores of the cut's bin ranked exactly), so a row costs
 // a few workgroup barriers rather than three radix passes of a 1024-thread workgroup.
+// Arrays of 8193..32768 positions take the same kernel with 1024 threads.
 #include "select_ops.h"
 
 namespace lit {

@@ -50,6 +50,8 @@ KV_FORMATS = {"bf16": 0, "e4m3": 1, "e2m1": 2}
 SIGNATURES = {
     "lit_status_str": (ctypes.c_char_p, [_I]),
     "lit_abi_version": (_I, []),
+    "lit_topk_width": (_I, [_I, _I, _I, _I]),
+    "lit_compress_writes_row": (_I, [_I, _I]),
     "lit_indexer_scores": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P]),
     "lit_indexer_scores_fmt": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P]),
     "lit_topk": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
@@ -123,7 +125,7 @@ def _need(t: torch.Tensor, dtype, name: str) -> None:
 
 
 def topk_width(S: int, start_pos: int, ratio: int, index_topk: int) -> int:
-    return min(index_topk, (start_pos + S) // ratio) if ratio > 0 and index_topk > 0 else 0
+    return library().lit_topk_width(S, start_pos, ratio, index_topk)
 
 
 def lit_window_width(S: int, start_pos: int, W: int) -> int:
@@ -335,7 +337,7 @@ def lit_compress_append(kv, score, kv_state, score_state, norm_w, eps: float, fr
         B, D, ratio, start_pos, _ptr(kv), _ptr(score), _ptr(kv_state), _ptr(score_state),
         _ptr(norm_w), float(eps), _ptr(freqs), freqs.shape[0], rd, _ptr(codes), _ptr(scales),
         codes.shape[1], _ptr(latent), _stream(stream)))
-    return (start_pos + 1) % ratio == 0
+    return bool(library().lit_compress_writes_row(start_pos, ratio))
 
 
 def lit_window_append(kv, freqs, rd: int, codes, scales, start_pos: int, stream=None) -> None:

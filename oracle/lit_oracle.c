@@ -28,6 +28,8 @@
 #include <omp.h>
 #endif
 
+int orc_num_threads(void);
+
 #define ORC_E_ARG (-1)   /* a size or pointer argument is invalid  */
 #define ORC_E_CODE (-2)  /* a NaN-coded fp8 / e8m0 byte was met     */
 #define ORC_E_INDEX (-3) /* an index list entry is out of range     */
@@ -140,22 +142,30 @@ int orc_index_scores(int fmt, const uint8_t *q8, const uint8_t *q_sc, const floa
     const int nb = Di / 32;
     const size_t E = fmt == ORC_FMT_E2M1 ? (size_t)Di / 2 : (size_t)Di; /* bytes per row */
     int bad = 0;
-#pragma omp parallel for collapse(2) schedule(dynamic) reduction(| : bad)
+    const size_t nq = (size_t)B * S;
+    /* every query's heads, dequantised */
+    double *qall = (double *)malloc(sizeof(double) * (nq > 0 ? nq : 1) * (size_t)Hi * Di);
+    if (!qall) return ORC_E_ARG;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (size_t qi = 0; qi < nq; ++qi) {
+        double *qh = qall + qi * (size_t)Hi * Di;
+        for (int h = 0; h < Hi; ++h)
+            for (int d = 0; d < Di; ++d) {
+                const uint8_t *qrow = q8 + (qi * Hi + h) * E;
+                size_t si = (qi * Hi + h) * nb + d / 32;
+                double v = orc_code_at(qrow, fmt, d) * orc_e8m0(q_sc[si]);
+                if (isnan(v)) bad = 1;
+                qh[(size_t)h * Di + d] = v;
+            }
+    }
+    /* one score per (query, row); the loops over (b, i, t) are independent */
+#pragma omp parallel for collapse(3) schedule(static) reduction(| : bad)
     for (int b = 0; b < B; ++b) {
         for (int i = 0; i < S; ++i) {
-            const int nvis = orc_n_visible(start_pos, i, ratio);
-            double *srow = scores + ((size_t)b * S + i) * T;
-            double *qh = (double *)malloc(sizeof(double) * (size_t)Hi * Di);
-            /* dequantise this query's heads */
-            for (int h = 0; h < Hi; ++h)
-                for (int d = 0; d < Di; ++d) {
-                    const uint8_t *qrow = q8 + (((size_t)b * S + i) * Hi + h) * E;
-                    size_t si = (((size_t)b * S + i) * Hi + h) * nb + d / 32;
-                    double v = orc_code_at(qrow, fmt, d) * orc_e8m0(q_sc[si]);
-                    if (isnan(v)) bad = 1;
-                    qh[(size_t)h * Di + d] = v;
-                }
             for (int t = 0; t < T; ++t) {
+                const int nvis = orc_n_visible(start_pos, i, ratio);
+                const double *qh = qall + ((size_t)b * S + i) * (size_t)Hi * Di;
+                double *srow = scores + ((size_t)b * S + i) * T;
                 if (t >= nvis) {
                     srow[t] = -INFINITY;
                     continue;
@@ -175,9 +185,9 @@ int orc_index_scores(int fmt, const uint8_t *q8, const uint8_t *q_sc, const floa
                 }
                 srow[t] = s;
             }
-            free(qh);
         }
     }
+    free(qall);
     return bad ? ORC_E_CODE : 0;
 }
 
@@ -444,7 +454,9 @@ int orc_sparse_attn_fmt(const uint16_t *q, int B, int S, int H, int D, int dv,
         (K > 0 && comp_fmt != ORC_KV_BF16 && (comp_sc == NULL || D % 32 != 0)))
         return ORC_E_ARG;
     int bad = 0;
-#pragma omp parallel for collapse(2) schedule(dynamic) reduction(| : bad)
+    /* queries in parallel when there are enough of them, else the heads of each query */
+    const int par_q = (long)B * S >= orc_num_threads();
+#pragma omp parallel for collapse(2) schedule(dynamic) reduction(| : bad) if (par_q)
     for (int b = 0; b < B; ++b) {
         for (int i = 0; i < S; ++i) {
             const int n = W + K;
@@ -462,12 +474,13 @@ int orc_sparse_attn_fmt(const uint16_t *q, int B, int S, int H, int D, int dv,
                 if (t >= T_cap) { bad = 1; continue; }
                 orc_kv_row(comp_fmt, comp_kv, comp_sc, (size_t)b * T_cap + t, D, kv + (size_t)nj++ * D);
             }
-            double *l = (double *)malloc(sizeof(double) * (size_t)(nj > 0 ? nj : 1));
+#pragma omp parallel for schedule(static) if (!par_q)
             for (int h = 0; h < H; ++h) {
                 const uint16_t *qh = q + (((size_t)b * S + i) * H + h) * D;
                 double *oh = out + (((size_t)b * S + i) * H + h) * dv;
                 for (int d = 0; d < dv; ++d) oh[d] = 0.0;
                 if (nj == 0) continue;
+                double *l = (double *)malloc(sizeof(double) * (size_t)nj);
                 double m = -INFINITY;
                 for (int j = 0; j < nj; ++j) {
                     double dot = 0.0;
@@ -483,8 +496,8 @@ int orc_sparse_attn_fmt(const uint16_t *q, int B, int S, int H, int D, int dv,
                     double p = exp(l[j] - m) / Z;
                     for (int d = 0; d < dv; ++d) oh[d] += p * kv[(size_t)j * D + d];
                 }
+                free(l);
             }
-            free(l);
             free(kv);
         }
     }

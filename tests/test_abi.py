@@ -46,6 +46,50 @@ def test_version_and_status_strings(lib):
     assert b"unknown" in lib.lit_status_str(99)
 
 
+def test_topk_width_matches_oracle(lib, orc):
+    """k_eff from the library equals the oracle's rule on a grid of shapes."""
+    for S in (0, 1, 5, 4096):
+        for start_pos in (0, 1, 7, 1023, 12288, 131071):
+            for ratio in (1, 2, 3, 4):
+                for k in (0, 1, 64, 2048):
+                    assert lib.lit_topk_width(S, start_pos, ratio, k) == \
+                        orc.topk_width(S, start_pos, ratio, k), (S, start_pos, ratio, k)
+    assert lib.lit_topk_width(1, 100, 0, 64) == 0
+    assert lib.lit_topk_width(-1, 100, 2, 64) == 0
+
+
+def test_compress_writes_row_matches_oracle(lib, orc):
+    """The library's group-completion answer equals whether the oracle's compressor
+    writes a cache row at that position (one sequence, D = 32, no rotation)."""
+    import numpy as np
+    for ratio in (1, 2, 3, 4):
+        ks = np.zeros((1, ratio, 32), np.float32)
+        gs = np.full((1, ratio, 32), -np.inf, np.float32)
+        codes = np.zeros((1, 8, 16), np.uint8)
+        scales = np.zeros((1, 8, 2), np.uint8)
+        kv = np.ones((1, 32), np.float32)
+        for pos in range(2 * ratio + 1):
+            wrote, _ = orc.compress_append(kv, kv, ks if ratio > 1 else None, gs if ratio > 1 else None,
+                                           np.ones(32, np.float32), 1e-6, np.zeros((16, 0, 2), np.float32),
+                                           0, codes, scales, pos, ratio)
+            assert lib.lit_compress_writes_row(pos, ratio) == int(wrote), (pos, ratio)
+    assert lib.lit_compress_writes_row(5, 0) == 0
+    assert lib.lit_compress_writes_row(-1, 2) == 0
+
+
+def test_step_sizing_of_an_empty_batch(lib):
+    """B = 0 or S = 0: nothing to size (the attention plan once divided by the query count)."""
+    args = B.lit_step_args()
+    args.B, args.S, args.start_pos, args.ratio, args.Hi, args.Di = 0, 1, 1023, 2, 16, 64
+    args.index_topk, args.T_cap, args.H, args.D, args.dv, args.W, args.R = 64, 512, 16, 128, 128, 128, 128
+    for f in ("q8", "q_sc", "w", "k8", "k_sc", "q", "win_kv", "comp_kv", "topk_idx", "out"):
+        setattr(args, f, A)
+    lib.lit_sparse_step_workspace_bytes(ctypes.byref(args))
+    args.B, args.S = 1, 0
+    lib.lit_sparse_step_workspace_bytes(ctypes.byref(args))
+    assert lib.lit_sparse_step(ctypes.byref(args), None, 0, None) == 0
+
+
 def scores_call(lib, **kw):
     a = dict(q8=A, q_sc=A, w=A, k8=A, k_sc=A, B=1, S=1, Hi=16, Di=64, T_cap=512, start_pos=1023,
              ratio=2, scores=A, ld=512)

@@ -49,8 +49,8 @@ MUTANTS = [
     ("key scale block reversed", "size_t ks = ((size_t)b * T_cap + t) * nb + d / 32;",
      "size_t ks = ((size_t)b * T_cap + t) * nb + (nb - 1 - d / 32);",
      [TI.test_closed_form_constant_blocks, _one_hot]),
-    ("query scale block off", "size_t si = (((size_t)b * S + i) * Hi + h) * nb + d / 32;",
-     "size_t si = (((size_t)b * S + i) * Hi + h) * nb;",
+    ("query scale block off", "size_t si = (qi * Hi + h) * nb + d / 32;",
+     "size_t si = (qi * Hi + h) * nb;",
      [TI.test_closed_form_constant_blocks, _one_hot]),
     ("head weight index", "double wh = (double)w[((size_t)b * S + i) * Hi + h];",
      "double wh = (double)w[((size_t)b * S + i) * Hi + (Hi - 1 - h)];",

@@ -1,0 +1,60 @@
+"""Host sanitizer builds, run on the CPU: the oracle (gcc) and the host side of the C ABI
+(hipcc, host pass only), each built with AddressSanitizer and UndefinedBehaviorSanitizer
+and driven over valid, edge-case and invalid inputs by the programs in tests/sanitize/.
+Any out-of-bounds access, use after free, leak (oracle) or undefined operation fails the
+run."""
+import concurrent.futures
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SAN = os.path.join(ROOT, "tests", "sanitize")
+CSRC = os.path.join(ROOT, "lightning_indexer_top_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# the sanitizers apply to the host pass only (-Xarch_host before each flag)
+HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _run(cmd, env=None, timeout=300):
+    r = subprocess.run(cmd, capture_output=True, text=True, env=env, timeout=timeout)
+    return r.returncode, r.stdout + r.stderr
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc missing")
+def test_oracle_under_asan_ubsan(tmp_path):
+    exe = str(tmp_path / "oracle_driver")
+    rc, out = _run(["gcc", "-std=c11", "-O1", "-g", "-fopenmp", "-fno-omit-frame-pointer",
+                    "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-ffp-contract=off",
+                    "-o", exe, os.path.join(ROOT, "oracle", "lit_oracle.c"),
+                    os.path.join(SAN, "oracle_driver.c"), "-lm"])
+    assert rc == 0, out
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", OMP_NUM_THREADS="4")
+    rc, out = _run([exe], env=env)
+    assert rc == 0 and "oracle driver ok" in out, out
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc missing")
+def test_abi_host_side_under_asan_ubsan(tmp_path):
+    srcs = [os.path.join(CSRC, f + ".hip") for f in
+            ("lit_api", "indexer", "topk", "attention", "produce", "fused_decode")]
+    srcs += [os.path.join(SAN, "abi_driver.cpp"), os.path.join(SAN, "fused_stub.cpp")]
+
+    def compile_one(src):
+        obj = str(tmp_path / (os.path.basename(src) + ".o"))
+        return _run([HIPCC, "-O1", "-g", "-std=c++17", "--offload-arch=gfx950", *HOST_SAN,
+                     "-c", src, "-o", obj]) + (obj,)
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        results = list(ex.map(compile_one, srcs))
+    for rc, out, _ in results:
+        assert rc == 0, out
+    exe = str(tmp_path / "abi_driver")
+    rc, out = _run([HIPCC, "--offload-arch=gfx950", *HOST_SAN, "-o", exe, *[o for _, _, o in results]])
+    assert rc == 0, out
+    # the HIP runtime keeps allocations until exit: leak detection is left off here
+    rc, out = _run([exe], env=dict(os.environ, ASAN_OPTIONS="detect_leaks=0"), timeout=120)
+    assert rc == 0 and "abi driver ok" in out, out
