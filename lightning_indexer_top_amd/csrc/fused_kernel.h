@@ -244,9 +244,6 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     int *picks = reinterpret_cast<int *>(dyn + f.chunk);
     float *tsl = dyn + 2 * f.chunk;  // the team's scores in position order (cached form)
 
-    // attention operands that do not depend on the selection: issued first
-    bf16x8 qb[D / 32];
-    load_q_operands<D>(qb, aa.q, (size_t)q, g, c);
 
     // level two: the query's candidate blocks are requested now and turned into a bitmap
     // of the blocks that meet this member's chunk after scoring
@@ -323,6 +320,12 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         }
         team_flag(slot_a, m, a, cmin, (uint32_t)q, ep);  // barrier A: scores published
     }
+
+    // attention operands that do not depend on the selection, requested once the chunk's
+    // scores are published (before, their round trip would delay scoring and the flag,
+    // which waits for every load in flight)
+    bf16x8 qb[D / 32];
+    load_q_operands<D>(qb, aa.q, (size_t)q, g, c);
 
     // window rows of this member, prefetched by waves 3, 2, ... (tile w -> wave 3 - w)
     const int nwin = window_width(ia.S, ia.start_pos, aa.W);
