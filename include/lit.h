@@ -460,6 +460,26 @@ size_t lit_sparse_step_workspace_bytes(const lit_step_args *args);
 /* State bytes the fused form needs for these sizes (0 when it does not apply). */
 size_t lit_sparse_step_state_bytes(const lit_step_args *args);
 
+/*
+ * lit_sparse_step_noalloc -- lit_sparse_step for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the workspace and the fused form's state are the library's own scratch,
+ * a 16 MiB device array per GPU that lives until the process ends.  The call allocates
+ * and frees nothing.  args->state / state_bytes are ignored.
+ *
+ *   err_word  (device) u32, or NULL: a fused team timeout ORs a nonzero value into it
+ *             (the caller zero-fills it; NULL: such a timeout is not reported and that
+ *             call's outputs are undefined)
+ *
+ * The first MiB holds the fused form's state (shapes whose state needs more run as
+ * kernels); the remaining 15 MiB are the workspace: a shape whose
+ * lit_sparse_step_workspace_bytes exceeds 15 MiB (e.g. a 4096-query prefill chunk) is
+ * refused with LIT_E_WORKSPACE before anything is launched.  Every call on one GPU
+ * shares that GPU's scratch, which keeps the last call's contents: calls that overlap
+ * on one GPU (other streams, other host threads) race and must be ordered by the caller.
+ */
+lit_status lit_sparse_step_noalloc(const lit_step_args *args, uint32_t *err_word, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

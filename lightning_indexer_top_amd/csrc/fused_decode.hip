@@ -111,9 +111,10 @@ size_t fused_part_bytes_per_query(const FusedPlan &p, int dv, int layers) {
     return (size_t)p.team_size * (size_t)(layers > 0 ? layers : 1) * slot_floats(dv) * 4;
 }
 
-hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream) {
+hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream,
+                        uint32_t *err_word) {
     char *st = (char *)state;
-    f.err = (uint32_t *)st;
+    f.err = err_word ? err_word : (uint32_t *)st;
     f.qstate = st + 256;
     char *rest = (char *)ws;
     auto bump = [&](size_t bytes) {

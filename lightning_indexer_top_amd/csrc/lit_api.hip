@@ -6,6 +6,9 @@
 
 #include <limits.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "lit_internal.h"
 
 using namespace lit;
@@ -490,7 +493,11 @@ size_t lit_sparse_step_state_bytes(const lit_step_args *s) {
     return fp.ok ? fused_state_bytes(fp) : 0;
 }
 
-lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+// The step on a caller's (or the library's) workspace and state; err_word, when set,
+// receives a fused team timeout instead of the state's first word.
+static lit_status step_run(const lit_step_args *s, void *ws, size_t ws_bytes, uint32_t *err_word, void *stream) {
     lit_status st = check_step(s);
     if (st != LIT_OK) return st;
     if (s->B == 0 || s->S == 0) return LIT_OK;
@@ -531,7 +538,7 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
                                                s->comp_kv_format, s->comp_kv, s->comp_kv_scales) != LIT_OK)
             return LIT_E_UNSUPPORTED;
         f.spin_limit = 1u << 22;
-        if ((e = launch_fused(f, fp, ws, s->state, hs)) != hipSuccess) return hip_status(e);
+        if ((e = launch_fused(f, fp, ws, s->state, hs, err_word)) != hipSuccess) return hip_status(e);
         for (int k = 1; k < 4; ++k)
             if ((e = mark(k)) != hipSuccess) return hip_status(e);
         return LIT_OK;
@@ -581,6 +588,74 @@ lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, vo
     }
     if ((e = launch_sparse_attn(aa, plan, hs)) != hipSuccess) return hip_status(e);
     return hip_status(mark(3));
+}
+
+// ---------------------------------------------------------------------------
+// The no-allocation form: workspace and fused-form state in the library's own scratch.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = (size_t)16 << 20;      // per device
+constexpr size_t kScratchStateBytes = (size_t)1 << 20;  // the fused form's state, first
+// Device memory of lit_sparse_step_noalloc: its workspace and its fused-form state.  Every
+// GPU the library runs on holds its own copy until the process ends (zero at load, which
+// is the state's required initial value).  In host code this name is not a device address:
+// only the address hipGetSymbolAddress gives for the current device is ever passed on.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The current device's copy of `scratch`, looked up once per device.
+lit_status scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return LIT_E_HIP;
+    }
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return LIT_E_HIP;
+            }
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return LIT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+lit_status lit_sparse_step(const lit_step_args *s, void *ws, size_t ws_bytes, void *stream) {
+    return step_run(s, ws, ws_bytes, nullptr, stream);
+}
+
+lit_status lit_sparse_step_noalloc(const lit_step_args *s, uint32_t *err_word, void *stream) {
+    lit_status st = check_step(s);
+    if (st != LIT_OK) return st;
+    if (s->B == 0 || s->S == 0) return LIT_OK;
+    lit_step_args a = *s;
+    a.state = nullptr;
+    a.state_bytes = 0;
+    // the fused form when its state fits the reserved first MiB (else the kernels)
+    const size_t sb = (s->flags & LIT_STEP_UNFUSED) ? 0 : lit_sparse_step_state_bytes(&a);
+    const bool fused = sb > 0 && sb <= kScratchStateBytes;
+    if (!fused) a.flags |= LIT_STEP_UNFUSED;
+    const size_t need = lit_sparse_step_workspace_bytes(&a);
+    if (need > kScratchBytes - kScratchStateBytes) return LIT_E_WORKSPACE;
+    void *p = nullptr;
+    if ((st = scratch_address(&p)) != LIT_OK) return st;
+    if (fused) {
+        a.state = p;
+        a.state_bytes = kScratchStateBytes;
+    }
+    return step_run(&a, (char *)p + kScratchStateBytes, kScratchBytes - kScratchStateBytes, err_word, stream);
 }
 
 }  // extern "C"

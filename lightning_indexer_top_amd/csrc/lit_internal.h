@@ -219,7 +219,9 @@ size_t fused_ws_bytes(const FusedPlan &p, int dv, int layers);
 // Bytes of one query's partial states (every member and layer): the kernel addresses
 // them with 32-bit offsets, so a plan is usable only while this stays below 2^31.
 size_t fused_part_bytes_per_query(const FusedPlan &p, int dv, int layers);
-hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream);
+// err_word: where a team timeout is reported (NULL: the state's first word).
+hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream,
+                        uint32_t *err_word = nullptr);
 // The kernels of each index-code format (fused_e4m3.hip, fused_e2m1.hip): launch, and
 // co-resident workgroups per CU for a shape (0 when not instantiated).
 // The _cand forms mask the scores of a level-two layer (FusedArgs::cand).

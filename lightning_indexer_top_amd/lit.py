@@ -76,6 +76,7 @@ SIGNATURES = {
     "lit_sparse_step": (_I, [ctypes.POINTER(lit_step_args), _P, _Z, _P]),
     "lit_sparse_step_workspace_bytes": (_Z, [ctypes.POINTER(lit_step_args)]),
     "lit_sparse_step_state_bytes": (_Z, [ctypes.POINTER(lit_step_args)]),
+    "lit_sparse_step_noalloc": (_I, [ctypes.POINTER(lit_step_args), _P, _P]),
 }
 
 
@@ -448,3 +449,12 @@ def lit_sparse_step(args: lit_step_args, ws: torch.Tensor, stream=None) -> None:
     nbytes = ws.numel() * ws.element_size()
     _check("lit_sparse_step", library().lit_sparse_step(ctypes.byref(args), _ptr(ws), nbytes,
                                                         _stream(stream)))
+
+
+def lit_sparse_step_noalloc(args: lit_step_args, err: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The step on the library's own scratch (no workspace or state from the caller);
+    err: an optional zero-filled int32 device word that receives a team timeout."""
+    if err is not None:
+        _need(err, torch.int32, "err")
+    _check("lit_sparse_step_noalloc", library().lit_sparse_step_noalloc(ctypes.byref(args), _ptr(err),
+                                                                         _stream(stream)))

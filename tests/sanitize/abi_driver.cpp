@@ -110,6 +110,12 @@ int main() {
         EXPECT(lit_sparse_step(&bad, nullptr, 0, nullptr) != LIT_OK || s0.B == 0);
     }
     EXPECT(lit_sparse_step(nullptr, A, 1 << 20, nullptr) == LIT_E_NULL);
+    EXPECT(lit_sparse_step_noalloc(nullptr, nullptr, nullptr) == LIT_E_NULL);
+    {
+        lit_step_args big = step(1, 4096, 12288, 2, 16, 64, 512, 128, 128);  // workspace beyond the scratch
+        big.R = 4223;
+        EXPECT(lit_sparse_step_noalloc(&big, nullptr, nullptr) == LIT_E_WORKSPACE);
+    }
     if (failures) {
         std::fprintf(stderr, "%d failures\n", failures);
         return 1;

@@ -90,6 +90,21 @@ def test_step_sizing_of_an_empty_batch(lib):
     assert lib.lit_sparse_step(ctypes.byref(args), None, 0, None) == 0
 
 
+def test_noalloc_refusals(lib):
+    """The no-allocation step refuses a workspace beyond its scratch before any launch, and
+    does nothing for an empty batch."""
+    args = B.lit_step_args()
+    args.B, args.S, args.start_pos, args.ratio, args.Hi, args.Di = 1, 4096, 12288, 2, 16, 64
+    args.index_topk, args.T_cap, args.H, args.D, args.dv, args.W, args.R = 512, 8192, 16, 128, 128, 128, 4223
+    for f in ("q8", "q_sc", "w", "k8", "k_sc", "q", "win_kv", "comp_kv", "topk_idx", "out"):
+        setattr(args, f, A)
+    assert lib.lit_sparse_step_noalloc(ctypes.byref(args), None, None) == 5   # LIT_E_WORKSPACE
+    args.B = 0
+    assert lib.lit_sparse_step_noalloc(ctypes.byref(args), None, None) == 0
+    args.B, args.Di = 1, 48
+    assert lib.lit_sparse_step_noalloc(ctypes.byref(args), None, None) == 2
+
+
 def scores_call(lib, **kw):
     a = dict(q8=A, q_sc=A, w=A, k8=A, k_sc=A, B=1, S=1, Hi=16, Di=64, T_cap=512, start_pos=1023,
              ratio=2, scores=A, ld=512)
