@@ -90,6 +90,8 @@ FusedPlan plan_fused(int fmt, bool masked, bool qkv, bool layers, int B, int S, 
     // window tiles are spread one per member
     if ((size_t)p.n_slots * kHeads * 2 * sizeof(float) > (size_t)4 * 32 * (D + 4) * sizeof(uint16_t)) return p;
     p.ld = (T + 3) / 4 * 4;
+    // value bins of the selection: about two visible rows a bin, at least 256, at most 4096
+    p.vbins = T <= 1024 ? 256 : T <= 4096 ? 1024 : 4096;
     p.ok = true;
     (void)dv;
     return p;
@@ -128,6 +130,7 @@ hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, 
     f.team_size = p.team_size;
     f.chunk = p.chunk;
     f.win_tiles = p.win_tiles;
+    f.vbins = p.vbins;
     f.n_slots = p.n_slots;
     f.ld = p.ld;
     f.cache_lds = p.cache_lds;

@@ -418,7 +418,10 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                 sm.mm[wave][1] = cmin;
             }
         }
-        for (int j = tid; j < kVBins / 4 + 1; j += kThreads)  // + the spill bin
+        // value bins between the team's min and max: fewer for short rows (f.vbins: 256, 1024
+        // or 4096), so clearing and searching them costs less
+        const int nbv = f.vbins;
+        for (int j = tid; j < nbv / 4 + 1; j += kThreads)  // + the spill bin
             reinterpret_cast<u32x4 *>(sm.hist)[j] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
         uint32_t kmax = 0u, kminc = 0u;
@@ -428,10 +431,10 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         }
         const float mx = key_float(kmax);
         const float mn = key_float(~kminc);
-        const float scale = mx > mn ? (float)kVBins / (mx - mn) : 0.f;
+        const float scale = mx > mn ? (float)nbv / (mx - mn) : 0.f;
         const float bias = -mn * scale;
         // pass 1: value bins (kept, 16 bits each) and histogram; cached positions past the
-        // visible rows take the spill bin kVBins.  Masked rows (-inf, level two) fall in bin
+        // visible rows take the spill bin nbv.  Masked rows (-inf, level two) fall in bin
         // 0; they are counted per thread and added once per wave, since thousands of LDS
         // atomics on one counter would serialise.
         uint32_t bins[kCacheQ * 2];
@@ -450,25 +453,30 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                     uint32_t bb[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        bb[e] = (uint32_t)value_bin(__uint_as_float(vals[r][e]), scale, bias);
+                        bb[e] = (uint32_t)value_bin_n(__uint_as_float(vals[r][e]), scale, bias, nbv);
                         hist_add(bb[e], __uint_as_float(vals[r][e]));
                     }
                     bins[2 * r] = bb[0] | (bb[1] << 16);
                     bins[2 * r + 1] = bb[2] | (bb[3] << 16);
                 }
             } else {
+                const uint32_t spill2 = (uint32_t)nbv * 0x10001u;  // two spill bins
 #pragma unroll
                 for (int r = 0; r < kCacheQ; ++r) {
-                    if (tid + kThreads * r < nquad) *reinterpret_cast<u32x4 *>(tsl + 4 * (tid + kThreads * r)) = vals[r];
+                    bins[2 * r] = spill2;
+                    bins[2 * r + 1] = spill2;
+                    if (kThreads * r >= nquad) continue;  // (uniform) no thread holds a visible quad
+                    if (tid + kThreads * r < nquad)
+                        *reinterpret_cast<u32x4 *>(tsl + 4 * (tid + kThreads * r)) = vals[r];
                     uint32_t bb[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         bb[e] = 4 * (tid + kThreads * r) + e < nvis
-                                    ? (uint32_t)value_bin(__uint_as_float(vals[r][e]), scale, bias)
-                                    : (uint32_t)kVBins;
+                                    ? (uint32_t)value_bin_n(__uint_as_float(vals[r][e]), scale, bias, nbv)
+                                    : (uint32_t)nbv;
                         // positions past the visible rows add nothing: thousands of them
                         // counted into the one spill bin would serialise on its atomics
-                        if (bb[e] != (uint32_t)kVBins) hist_add(bb[e], __uint_as_float(vals[r][e]));
+                        if (bb[e] != (uint32_t)nbv) hist_add(bb[e], __uint_as_float(vals[r][e]));
                     }
                     bins[2 * r] = bb[0] | (bb[1] << 16);
                     bins[2 * r + 1] = bb[2] | (bb[3] << 16);
@@ -479,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             uint16_t *bins16 = reinterpret_cast<uint16_t *>(dyn + 2 * f.chunk);
             const bool keep = f.lds_bins;
             each([&](int t, float x) {
-                const int bin = value_bin(x, scale, bias);
+                const int bin = value_bin_n(x, scale, bias, nbv);
                 hist_add((uint32_t)bin, x);
                 if (keep) bins16[t] = (uint16_t)bin;
             });
@@ -489,14 +497,14 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             if (lane == 0 && ninf) atomicAdd(&sm.hist[0], ninf);
         }
         __syncthreads();
-        find_bin(sm.hist, kVBins, f.keff, sm.wsum, &sm.bin, &sm.above);
+        find_bin(sm.hist, nbv, f.keff, sm.wsum, &sm.bin, &sm.above);
         const int vb = sm.bin;
         const int need = f.keff - sm.above;
         const int cnt = (int)sm.hist[vb];
         // the attention list, in position order (wave counts summed in wave order)
         for (int j = 0; j * kThreads < n; ++j) {
             const int t = tid + kThreads * j;
-            const bool in = t < n && value_bin(sc[t], scale, bias) >= vb;
+            const bool in = t < n && value_bin_n(sc[t], scale, bias, nbv) >= vb;
             const uint64_t bal = __ballot(in);
             if (lane == 0) sm.wcnt[wave] = (int)__popcll(bal);
             __syncthreads();
@@ -534,7 +542,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         if (cnt <= kCandCap) {
             // pass 2: the candidates (bin vb) into LDS.  Cached: two 16-bit bins per word;
             // adding 0x7fff - vb (0x8000 - vb) to a half sets its bit 15 exactly when the bin is
-            // above (at least) vb, and bins stay <= kVBins, so no half carries into the next.
+            // above (at least) vb, and bins stay <= nbv <= 4096, so no half carries into the next.
             if (cached) {
                 const uint32_t kgt = (0x7fffu - (uint32_t)vb) * 0x10001u;
                 const uint32_t kge = (0x8000u - (uint32_t)vb) * 0x10001u;
@@ -578,7 +586,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing left in flight
                 } else {
                     each([&](int t, float x) {
-                        const int bin = value_bin(x, scale, bias);
+                        const int bin = value_bin_n(x, scale, bias, nbv);
                         if (bin == vb) cand[atomicAdd(&sm.ncand, 1)] = ((uint64_t)order_key(x) << 32) | (uint32_t)~(uint32_t)t;
                     });
                 }
@@ -591,7 +599,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             kstar = sm.kstar;
             pstar = sm.pstar;
         } else {
-            radix_resolve(sm, [&](int t) { return ldf_agent(ts + t); }, nvis, scale, bias, vb, need);
+            radix_resolve(sm, [&](int t) { return ldf_agent(ts + t); }, nvis, scale, bias, vb, need, nbv);
             kstar = sm.kstar;
             pstar = sm.pstar;
         }

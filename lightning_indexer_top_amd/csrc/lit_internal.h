@@ -190,6 +190,7 @@ struct FusedArgs {
     int32_t *topk_out;    // [B,S,keff] output
     int keff;
     int team_size, chunk, win_tiles, n_slots;
+    int vbins;            // value bins of the selection (256, 1024 or 4096; fewer for short rows)
     long ld;              // team score array stride
     uint32_t spin_limit;
     uint32_t *err;                // sticky error word (state)
@@ -207,7 +208,7 @@ struct FusedArgs {
 };
 struct FusedPlan {
     bool ok;
-    int n_teams, team_size, chunk, win_tiles, n_slots, grid;
+    int n_teams, team_size, chunk, win_tiles, n_slots, grid, vbins;
     bool cache_lds, lds_bins;
     long ld;
     size_t dyn_bytes;

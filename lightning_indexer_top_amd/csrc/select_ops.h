@@ -95,6 +95,10 @@ __device__ inline void find_bin(const uint32_t *hist, int nbins, int need, uint3
 __device__ inline int value_bin(float v, float scale, float bias) {
     return (int)fminf(fmaxf(fmaf(v, scale, bias), 0.f), (float)(kVBins - 1));
 }
+// The same over nbins bins (nbins <= kVBins).
+__device__ inline int value_bin_n(float v, float scale, float bias, int nbins) {
+    return (int)fminf(fmaxf(fmaf(v, scale, bias), 0.f), (float)(nbins - 1));
+}
 
 // Exact resolution by radix levels over a row's scores (heavy ties): among the scores in
 // value bin vb, the need-th by (order key desc, position asc).  Threads take contiguous
@@ -102,10 +106,10 @@ __device__ inline int value_bin(float v, float scale, float bias) {
 // score at position t.
 template <int NT, typename Score>
 __device__ inline void radix_resolve(SelLdsT<NT> &sm, Score score, int nvis, float scale, float bias, int vb,
-                                     int need) {
+                                     int need, int nbins = kVBins) {
     const int per = (nvis + NT - 1) / NT;
     const int t0 = threadIdx.x * per, t1 = min(t0 + per, nvis);
-    auto in_bin = [&](float v) { return value_bin(v, scale, bias) == vb; };
+    auto in_bin = [&](float v) { return value_bin_n(v, scale, bias, nbins) == vb; };
     uint32_t prefix = 0u, pmask = 0u;
     const int shifts[3] = {20, 8, 0};
     const int widths[3] = {12, 12, 8};
