@@ -441,8 +441,8 @@ typedef struct lit_step_args {
     int cand_block_size;    /* rows per block, for cand_in and cand_out */
     /* quantised attention KV (lit_kv_format; 0 = bf16): win_kv / comp_kv then hold the
      * codes (cast to the field's type) and these the scale bytes.  Both sources
-     * quantised (window LIT_KV_E4M3, compressed LIT_KV_E2M1) run fused unless the
-     * layer uses candidates; one quantised source alone runs as kernels. */
+     * quantised (window LIT_KV_E4M3, compressed LIT_KV_E2M1) run fused, with or
+     * without level two and layers; one quantised source alone runs as kernels. */
     int win_kv_format;
     const uint8_t *win_kv_scales;
     int comp_kv_format;
@@ -451,7 +451,7 @@ typedef struct lit_step_args {
      * (and win_kv_scales), sink and out hold L layers back to back -- q [L,B,S,H,D],
      * win_kv [L,B,R,*], sink [L,H], out [L,B,S,H,dv] -- and every layer attends over the
      * one top-k list and comp_kv ([V4.1] index_source_layers / kv_source_layers).  They
-     * run fused with bf16 KV and no candidates, else as kernels. */
+     * run fused with either KV format and with or without level two. */
     int layers;
 } lit_step_args;
 

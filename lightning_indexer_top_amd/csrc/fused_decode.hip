@@ -1,8 +1,8 @@
 // fused_decode.hip -- plan, workspace / state layout and dispatch of the fused decode
 // kernel (fused_kernel.h): the team shape (chunk, team size) that fits every workgroup
 // on the device at once, where the team's scores live during selection, and the
-// launch of the kernel of the call's index-code format and masking (fused_e4m3.hip,
-// fused_e2m1.hip and their _cand forms).
+// launch of the kernel form (fused_forms.hip) of the call's index-code format, masking,
+// KV format and layer count.
 #include <atomic>
 
 #include "fused_kernel.h"
@@ -22,24 +22,32 @@ int device_cus(int dev) {
     return v;
 }
 
+// The forms by their traits (LIT_FUSED_FORMS).
+struct FusedForm {
+    int fmt;
+    bool mask, qkv, layers;
+    hipError_t (*launch)(const FusedArgs &, int, size_t, hipStream_t);
+    int (*per_cu)(int, int, int, size_t, bool);
+};
+#define LIT_FUSED_ENTRY(name, fmt, mask, qkv, layers) {fmt, mask, qkv, layers, launch_fused_##name, fused_per_cu_##name},
+constexpr FusedForm kForms[] = {LIT_FUSED_FORMS(LIT_FUSED_ENTRY)};
+#undef LIT_FUSED_ENTRY
+
+const FusedForm *find_form(int fmt, bool mask, bool qkv, bool layers) {
+    for (const FusedForm &f : kForms)
+        if (f.fmt == fmt && f.mask == mask && f.qkv == qkv && f.layers == layers) return &f;
+    return nullptr;
+}
+
 // Co-resident workgroups of the fused kernel on the current device.
 int max_resident(int fmt, bool masked, bool qkv, bool layers, int D, int DI, int HT, size_t dyn, bool cached) {
+    const FusedForm *form = find_form(fmt, masked, qkv, layers);
+    if (!form) return 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     const int cus = device_cus(dev);
     if (cus <= 0) return 0;
-    int per_cu;
-    if (layers)
-        per_cu = fmt == kFmtE2M1 ? fused_per_cu_e2m1_layers(D, DI, HT, dyn, cached)
-                                 : fused_per_cu_e4m3_layers(D, DI, HT, dyn, cached);
-    else if (qkv)
-        per_cu = fmt == kFmtE2M1 ? fused_per_cu_e2m1_qkv(D, DI, HT, dyn, cached)
-                                 : fused_per_cu_e4m3_qkv(D, DI, HT, dyn, cached);
-    else if (fmt == kFmtE2M1)
-        per_cu = masked ? fused_per_cu_e2m1_cand(D, DI, HT, dyn, cached) : fused_per_cu_e2m1(D, DI, HT, dyn, cached);
-    else
-        per_cu = masked ? fused_per_cu_e4m3_cand(D, DI, HT, dyn, cached) : fused_per_cu_e4m3(D, DI, HT, dyn, cached);
-    return cus * per_cu;
+    return cus * form->per_cu(D, DI, HT, dyn, cached);
 }
 
 }  // namespace
@@ -136,18 +144,10 @@ hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, 
     f.cache_lds = p.cache_lds;
     f.lds_bins = p.lds_bins;
     f.bins_words = (int)((p.ld + 7) / 8 * 4);  // 32-bit words of the padded bins
-    const bool masked = f.cand != nullptr;
-    if (f.aa.L > 1)  // several layers (bf16 KV, never with masking)
-        return f.ia.fmt == kFmtE2M1 ? launch_fused_e2m1_layers(f, p.grid, p.dyn_bytes, stream)
-                                    : launch_fused_e4m3_layers(f, p.grid, p.dyn_bytes, stream);
-    if (f.aa.win_fmt != kKvBf16 || f.aa.comp_fmt != kKvBf16)  // quantised KV (never with masking)
-        return f.ia.fmt == kFmtE2M1 ? launch_fused_e2m1_qkv(f, p.grid, p.dyn_bytes, stream)
-                                    : launch_fused_e4m3_qkv(f, p.grid, p.dyn_bytes, stream);
-    if (f.ia.fmt == kFmtE2M1)
-        return masked ? launch_fused_e2m1_cand(f, p.grid, p.dyn_bytes, stream)
-                      : launch_fused_e2m1(f, p.grid, p.dyn_bytes, stream);
-    return masked ? launch_fused_e4m3_cand(f, p.grid, p.dyn_bytes, stream)
-                  : launch_fused_e4m3(f, p.grid, p.dyn_bytes, stream);
+    const FusedForm *form = find_form(f.ia.fmt, f.cand != nullptr, f.aa.win_fmt != kKvBf16 || f.aa.comp_fmt != kKvBf16,
+                                      f.aa.L > 1);
+    if (!form) return hipErrorInvalidValue;
+    return form->launch(f, p.grid, p.dyn_bytes, stream);
 }
 
 }  // namespace lit

@@ -423,12 +423,10 @@ static FusedPlan step_fused_plan(const lit_step_args *s) {
     if (s->cand_out) return p;
     const bool masked = s->cand_in != nullptr;
     if (masked && (s->cand_k < 1 || s->cand_k > kFusedCandMaxApi)) return p;
-    // quantised KV runs fused when both sources are quantised and there is no masking
+    // quantised KV runs fused when both sources are quantised (e4m3 window, e2m1 compressed)
     const bool qkv = step_quant_kv(s);
-    if (qkv && (masked || s->win_kv_format != LIT_KV_E4M3 || s->comp_kv_format != LIT_KV_E2M1)) return p;
-    // several layers over the top-k run fused with bf16 KV and no masking
+    if (qkv && (s->win_kv_format != LIT_KV_E4M3 || s->comp_kv_format != LIT_KV_E2M1)) return p;
     const bool layers = step_layers(s) > 1;
-    if (layers && (masked || qkv)) return p;
     const int keff = topk_width(s->S, s->start_pos, s->ratio, s->index_topk);
     p = plan_fused(s->index_format, masked, qkv, layers, s->B, s->S, s->start_pos, s->ratio, s->Hi, s->Di, s->D,
                    s->dv, s->W, keff);

@@ -223,26 +223,35 @@ size_t fused_part_bytes_per_query(const FusedPlan &p, int dv, int layers);
 // err_word: where a team timeout is reported (NULL: the state's first word).
 hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, hipStream_t stream,
                         uint32_t *err_word = nullptr);
-// The kernels of each index-code format (fused_e4m3.hip, fused_e2m1.hip): launch, and
-// co-resident workgroups per CU for a shape (0 when not instantiated).
-// The _cand forms mask the scores of a level-two layer (FusedArgs::cand).
-hipError_t launch_fused_e4m3(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
-hipError_t launch_fused_e2m1(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
-hipError_t launch_fused_e4m3_cand(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
-hipError_t launch_fused_e2m1_cand(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
-int fused_per_cu_e4m3(int D, int DI, int HT, size_t dyn_bytes, bool cached);
-int fused_per_cu_e2m1(int D, int DI, int HT, size_t dyn_bytes, bool cached);
-int fused_per_cu_e4m3_cand(int D, int DI, int HT, size_t dyn_bytes, bool cached);
-int fused_per_cu_e2m1_cand(int D, int DI, int HT, size_t dyn_bytes, bool cached);
-// The _qkv forms read quantised attention KV (AttnArgs win_codes / comp_codes).
-hipError_t launch_fused_e4m3_qkv(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
-hipError_t launch_fused_e2m1_qkv(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
-int fused_per_cu_e4m3_qkv(int D, int DI, int HT, size_t dyn_bytes, bool cached);
-int fused_per_cu_e2m1_qkv(int D, int DI, int HT, size_t dyn_bytes, bool cached);
-// The _layers forms run AttnArgs::L layers over the step's top-k (bf16 KV, no masking).
-hipError_t launch_fused_e4m3_layers(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
-hipError_t launch_fused_e2m1_layers(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream);
-int fused_per_cu_e4m3_layers(int D, int DI, int HT, size_t dyn_bytes, bool cached);
-int fused_per_cu_e2m1_layers(int D, int DI, int HT, size_t dyn_bytes, bool cached);
+// The fused kernel's forms: index-code format x level-two masking x quantised attention
+// KV x several layers over one top-k.  fused_forms.hip is compiled once per entry, with
+// the entry's fields as macros, and defines that form's launcher and occupancy query.
+//   X(name, index format, masking, quantised KV, layers)
+// masking: rows outside the query's candidate blocks score -inf (FusedArgs::cand);
+// quantised KV: the attention sources are codes (AttnArgs win_codes / comp_codes);
+// layers: AttnArgs::L layers attend over the step's top-k.
+#define LIT_FUSED_FORMS(X)                                  \
+    X(e4m3, kFmtE4M3, false, false, false)                  \
+    X(e2m1, kFmtE2M1, false, false, false)                  \
+    X(e4m3_cand, kFmtE4M3, true, false, false)              \
+    X(e2m1_cand, kFmtE2M1, true, false, false)              \
+    X(e4m3_qkv, kFmtE4M3, false, true, false)               \
+    X(e2m1_qkv, kFmtE2M1, false, true, false)               \
+    X(e4m3_layers, kFmtE4M3, false, false, true)            \
+    X(e2m1_layers, kFmtE2M1, false, false, true)            \
+    X(e4m3_qkv_cand, kFmtE4M3, true, true, false)           \
+    X(e2m1_qkv_cand, kFmtE2M1, true, true, false)           \
+    X(e4m3_qkv_layers, kFmtE4M3, false, true, true)         \
+    X(e2m1_qkv_layers, kFmtE2M1, false, true, true)         \
+    X(e4m3_cand_layers, kFmtE4M3, true, false, true)        \
+    X(e2m1_cand_layers, kFmtE2M1, true, false, true)        \
+    X(e4m3_qkv_cand_layers, kFmtE4M3, true, true, true)     \
+    X(e2m1_qkv_cand_layers, kFmtE2M1, true, true, true)
+// Per form: launch, and co-resident workgroups per CU for a shape (0 when not instantiated).
+#define LIT_FUSED_DECLARE(name, fmt, mask, qkv, layers)                                                   \
+    hipError_t launch_fused_##name(const FusedArgs &f, int grid, size_t dyn_bytes, hipStream_t stream); \
+    int fused_per_cu_##name(int D, int DI, int HT, size_t dyn_bytes, bool cached);
+LIT_FUSED_FORMS(LIT_FUSED_DECLARE)
+#undef LIT_FUSED_DECLARE
 
 }  // namespace lit

@@ -7,16 +7,9 @@
 #include "../../lightning_indexer_top_amd/csrc/lit_internal.h"
 
 namespace lit {
-#define LIT_STUB(name)                                                                           \
+#define LIT_STUB(name, fmt, mask, qkv, layers)                                                            \
     hipError_t launch_fused_##name(const FusedArgs &, int, size_t, hipStream_t) { return hipErrorInvalidValue; } \
     int fused_per_cu_##name(int, int, int, size_t, bool) { return 0; }
-LIT_STUB(e4m3)
-LIT_STUB(e2m1)
-LIT_STUB(e4m3_cand)
-LIT_STUB(e2m1_cand)
-LIT_STUB(e4m3_qkv)
-LIT_STUB(e2m1_qkv)
-LIT_STUB(e4m3_layers)
-LIT_STUB(e2m1_layers)
+LIT_FUSED_FORMS(LIT_STUB)
 #undef LIT_STUB
 }  // namespace lit

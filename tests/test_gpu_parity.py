@@ -906,7 +906,7 @@ def test_step_shared_topk_layers(orc, flags, kv):
                                       comp_fmt="e2m1" if kv == "quant" else "bf16",
                                       comp_sc=d["comp_sc"])
     state = L.attach_state(args)
-    assert (state is not None) == (flags == 0 and kv == "bf16")  # quantised KV: as kernels
+    assert (state is not None) == (flags == 0)
     L.lit_sparse_step(args, L.step_workspace(args))
     torch.cuda.synchronize()
     assert L.state_error(state) == 0
@@ -921,5 +921,65 @@ def test_step_shared_topk_layers(orc, flags, kv):
     for ly in range(NL):  # every layer over the kernel's own list
         want = orc.sparse_attn(qs[ly], wins[ly], win, inp.comp_kv, g_idx, sinks[ly], inp.scale, None,
                                wf, None if win_sc is None else win_sc[ly], cf, inp.comp_sc)
+        err = np.abs(g_out[ly] - want).max()
+        assert err <= ATTN_TOL, f"layer {ly}: {err}"
+
+
+# ---------------------------------------------------------------------------------
+# the fused kernel's combined forms: level two with quantised KV and / or several layers
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("flags", MODES)
+@pytest.mark.parametrize("kv,NL,start_pos", [("quant", 1, 16383), ("bf16", 3, 16383), ("quant", 3, 16383),
+                                             ("quant", 1, 65535), ("quant", 2, 65535)])
+def test_step_level_two_combined_forms(orc, kv, NL, start_pos, flags):
+    """A level-two layer (candidate blocks of a source layer) with quantised KV, several
+    layers over its top-k, or both: one fused launch (the cached selection at 4096 rows,
+    the re-reading one at 16384) or kernels, against the oracle on every layer."""
+    kw = dict(B=2, S=1, start_pos=start_pos, ratio=4, Hi=64, Di=128, H=16, D=128, W=128,
+              index_topk=512, keys="mixture")
+    nblk = (start_pos + 1) // 4 // 8
+    src = synth.make_step(seed=101, **kw)
+    inp = synth.make_step(seed=102, kv_fmt=kv, sink=np.linspace(-1, 1, 16).astype(np.float32), **kw)
+    blocks = orc.step(src, cand_topk_blocks=nblk // 4, cand_block_size=8)["cand"]
+    rng = np.random.default_rng(103)
+    bits = lambda shape: synth.to_bf16_bits(rng.standard_normal(shape).astype(np.float32))  # noqa: E731
+    qs = np.concatenate([inp.q[None], bits((NL - 1,) + inp.q.shape)])
+    sinks = np.stack([inp.sink] + [rng.standard_normal(16).astype(np.float32) for _ in range(NL - 1)])
+    if kv == "quant":
+        wq = [synth._quant_np(rng.standard_normal(inp.win_kv.shape).astype(np.float32), "e4m3")
+              for _ in range(NL - 1)]
+        wins = np.concatenate([inp.win_kv[None]] + [w[0][None] for w in wq])
+        win_sc = np.concatenate([inp.win_sc[None]] + [w[1][None] for w in wq])
+    else:
+        wins = np.concatenate([inp.win_kv[None], bits((NL - 1,) + inp.win_kv.shape)])
+        win_sc = None
+    d = step_inputs_dev(inp)
+    args, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
+                                      k_sc=d["k_sc"], q=bf16_dev(qs) if NL > 1 else d["q"],
+                                      win_kv=(bf16_dev(wins) if kv == "bf16" else dev(wins)) if NL > 1
+                                      else d["win_kv"],
+                                      comp_kv=d["comp_kv"], start_pos=inp.start_pos, ratio=inp.ratio,
+                                      index_topk=inp.index_topk, W=inp.W, scale=inp.scale,
+                                      sink=dev(sinks) if NL > 1 else d["sink"], flags=flags,
+                                      win_fmt="e4m3" if kv == "quant" else "bf16",
+                                      win_sc=None if win_sc is None else dev(win_sc),
+                                      comp_fmt="e2m1" if kv == "quant" else "bf16",
+                                      comp_sc=d["comp_sc"], cand_in=dev(blocks), cand_block_size=8)
+    state = L.attach_state(args)
+    assert (state is not None) == (flags == 0), "expected the fused form"
+    L.lit_sparse_step(args, L.step_workspace(args))
+    torch.cuda.synchronize()
+    assert L.state_error(state) == 0
+    g_idx = idx.cpu().numpy()
+    g_out = bf16_host(out).reshape((NL,) + inp.q.shape[:3] + (inp.q.shape[3],))
+    ref = orc.step(inp, cand_in=blocks, cand_block_size=8)
+    for b in range(2):
+        assert set(g_idx[b, 0] // 8) <= set(blocks[b, 0])
+        ok, why = topk_sets_agree(ref["masked"][b, 0], ref["idx"][b, 0], g_idx[b, 0])
+        assert ok, f"sequence {b}: {why}"
+    wf, cf = ("e4m3", "e2m1") if kv == "quant" else ("bf16", "bf16")
+    for ly in range(NL):  # every layer over the kernel's own list
+        want = orc.sparse_attn(qs[ly], wins[ly], ref["win_idx"], inp.comp_kv, g_idx, sinks[ly], inp.scale,
+                               None, wf, None if win_sc is None else win_sc[ly], cf, inp.comp_sc)
         err = np.abs(g_out[ly] - want).max()
         assert err <= ATTN_TOL, f"layer {ly}: {err}"
