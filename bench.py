@@ -115,8 +115,8 @@ def kernel_sources(ksrc):
 
 
 def fused_sources(spec: dict):
-    fmt = spec.get("index_fmt", "e4m3")
-    return ("fused_kernel.h", f"fused_{fmt}.hip")
+    """The fused kernel's sources (every form is fused_forms.hip instantiating fused_kernel.h)."""
+    return ("fused_kernel.h", "fused_forms.hip")
 
 
 def read_counters(path: str, counter: str) -> dict:

@@ -210,6 +210,109 @@ __global__ __launch_bounds__(kWaves * 64) void sparse_attn_kernel(AttnArgs a0, A
     }
 }
 
+// Many queries (chunked prefill): one wave per (layer, query) walks the query's whole
+// list, so no state is merged across waves or workgroups.  bf16 rows are gathered
+// coalesced into the wave's LDS tile (tile_ops.h, RowPieces): a tile's rows are requested
+// a tile ahead and its list entries two tiles ahead, so the gather overlaps a whole tile
+// of compute.  The four waves of a workgroup share nothing but the launch (a wave past
+// the last query returns at once; no workgroup barrier follows).
+constexpr int kWaveRG = 4;  // V^T tiles read per group (fewer live registers)
+template <int D, int WF, int CF>
+__global__ __launch_bounds__(kWaves * 64) void sparse_attn_wave_kernel(AttnArgs a0, int n_queries) {
+    constexpr bool QUANT = WF != kKvBf16 || CF != kKvBf16;
+    constexpr int LDR = QUANT ? D + 4 : D + 8;  // LDS row stride (16-byte aligned rows for the staged form)
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * 32 * LDR];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int qq = blockIdx.x * kWaves + wave;
+    if (qq >= n_queries) return;
+    const int layer = qq % a0.L;  // the layers of one query are neighbours
+    const int bs = qq / a0.L;
+    const AttnArgs a = layer_args(a0, layer);
+    const int b = bs / a.S;
+    const int i = bs % a.S;
+    const int nwin = a.win_idx ? a.W : (a.W > 0 ? window_width(a.S, a.start_pos, a.W) : 0);
+    const WindowBase wb = window_base(a.start_pos, a.W, a.R > 0 ? a.R : 1, i);
+    const int list_len = attn_list_len(nwin, a.K);
+    const int wpad = list_len - a.K;
+    const int ndt = a.dv / 16;
+    const float sl2 = a.scale * kLog2e;
+
+    bf16x8 qb[D / 32];
+    load_q_operands<D>(qb, a.q, (size_t)bs, g, c);
+    AttnState<D> st;
+    attn_init<D>(st);
+    uint16_t *tile = lds + wave * 32 * LDR;
+
+    if constexpr (QUANT) {
+        AttnRows<D> rows;
+        quant_tile_load<D, WF, CF>(rows, a, b, i, nwin, wpad, wb, c, 16 + c, list_len, g);
+        for (int base = 0; base < list_len; base += 32) {
+            const AttnLogits lg = attn_tile_logits<D>(qb, rows, tile, g, c);
+            const int nb = base + 32;
+            if (nb < list_len)
+                quant_tile_load<D, WF, CF>(rows, a, b, i, nwin, wpad, wb, nb + c, nb + 16 + c, list_len, g);
+            attn_tile_update<D, kWaveRG, LDR>(st, lg, tile, ndt, sl2, g, c);
+        }
+    } else {
+        const uint16_t *wsrc = a.win_kv ? a.win_kv + (size_t)b * a.R * D : nullptr;
+        const uint16_t *csrc = a.comp_kv ? a.comp_kv + (size_t)b * a.T_cap * D : nullptr;
+        const rsrc_t win_r = make_rsrc(wsrc, wsrc ? (uint32_t)a.R * D * 2u : 0u);
+        const rsrc_t comp_r = make_rsrc(csrc, csrc ? (uint32_t)a.T_cap * D * 2u : 0u);
+        const rsrc_t widx_r = make_rsrc(a.win_idx ? a.win_idx + (size_t)bs * a.W : nullptr,
+                                        a.win_idx ? (uint32_t)a.W * 4u : 0u);
+        const rsrc_t cidx_r = make_rsrc(a.comp_idx ? a.comp_idx + (size_t)bs * a.K : nullptr,
+                                        a.comp_idx ? (uint32_t)a.K * 4u : 0u);
+        const bool derived = a.win_idx == nullptr;
+        const int r = lane & 31;  // the tile row whose entry this lane holds
+        // the list entry of row r of the tile at `base` (past a list its buffer reads 0)
+        auto request = [&](int base) {
+            const bool win = base < wpad;
+            return (int)__builtin_amdgcn_raw_buffer_load_b32(win ? widx_r : cidx_r,
+                                                             (int)(4u * (uint32_t)(base + r - (win ? 0 : wpad))), 0, 0);
+        };
+        // its byte offset in the tile's source, kOffNone when the row is not listed
+        auto offset_of = [&](int base, int e) {
+            const bool win = base < wpad;
+            const int p = base + r;
+            const int ent = win && derived ? window_slot_at(wb, a.start_pos, a.R, i, p) : e;
+            const bool ok = p < list_len && (!win || p < nwin);
+            const uint32_t lim = win ? (uint32_t)a.R : (uint32_t)a.T_cap;
+            return ok && (uint32_t)ent < lim ? (uint32_t)ent * (2u * D) : kOffNone;
+        };
+        auto src_of = [&](int base) { return base < wpad ? win_r : comp_r; };
+        RowPieces<D> rp;
+        int ent = request(0);
+        row_pieces_load<D>(rp, src_of(0), offset_of(0, ent), lane);
+        ent = request(32);
+        row_pieces_stage<D, LDR>(rp, tile, lane);
+        uint64_t valid = rp.valid;
+        row_pieces_load<D>(rp, src_of(32), offset_of(32, ent), lane);
+        ent = request(64);
+        wave_lds_sync();
+        for (int base = 0; base < list_len; base += 32) {
+            const AttnLogits lg = attn_tile_logits_lds<D, LDR>(qb, valid, tile, g, c);
+            attn_tile_update<D, kWaveRG, LDR>(st, lg, tile, ndt, sl2, g, c);  // ends with the reads done
+            // the next tile's rows (requested a tile ago) into LDS; the one after is requested
+            row_pieces_stage<D, LDR>(rp, tile, lane);
+            valid = rp.valid;
+            row_pieces_load<D>(rp, src_of(base + 64), offset_of(base + 64, ent), lane);
+            ent = request(base + 96);
+            wave_lds_sync();
+        }
+    }
+
+    // lane (g, h) holds dims 16dt+4g..16dt+4g+3 of head h: normalise and store 4 bf16
+    attn_wave_total<D>(st);
+    uint16_t *orow = a.out + ((size_t)bs * kHeads + c) * a.dv + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        if (dt < ndt) *reinterpret_cast<u32x2 *>(orow + 16 * dt) = attn_finish4(st.o[dt], st.m, st.l, a.sink, c);
+}
+
 // Split merge: one wave per (query, head).  Lane s holds split s's max and
 // normaliser (several splits per lane when there are more than 64); the wave reduces
 // them, leaves each split's weight e^(m_s - M) / L in LDS, and then every lane sums
@@ -268,6 +371,12 @@ __global__ void window_indices_kernel(int B, int S, int start_pos, int W, int R,
 
 template <int D, int WF, int CF>
 hipError_t launch_d(const AttnArgs &a, const AttnPlan &p, hipStream_t stream) {
+    if (p.per_wave) {
+        const int nq = a.B * a.S * a.L;
+        hipLaunchKernelGGL((sparse_attn_wave_kernel<D, WF, CF>), dim3((nq + kWaves - 1) / kWaves),
+                           dim3(kWaves * 64), 0, stream, a, nq);
+        return hipGetLastError();
+    }
     dim3 grid(p.n_splits, a.B * a.S * a.L);
     hipLaunchKernelGGL((sparse_attn_kernel<D, WF, CF>), grid, dim3(kWaves * 64), 0, stream, a, p);
     hipError_t e = hipGetLastError();
@@ -283,6 +392,13 @@ AttnPlan plan_attention(int B, int S, int list_len) {
     p.list_len = list_len;
     const int tiles = (list_len + 31) / 32;
     const int queries = B * S > 0 ? B * S : 1;  // an empty batch sizes like one query
+    // Enough queries to give every SIMD several waves: one wave per query (no merges).
+    p.per_wave = queries >= kWaveFormQueries;
+    if (p.per_wave) {
+        p.n_splits = 1;
+        p.tiles_per_wave = tiles;
+        return p;
+    }
     // Aim for at least ~512 workgroups, but never fewer than one tile per wave.
     int splits = (512 + queries - 1) / queries;
     const int max_splits = (tiles + kWaves - 1) / kWaves;
@@ -297,7 +413,7 @@ AttnPlan plan_attention(int B, int S, int list_len) {
 }
 
 size_t attention_partial_bytes(int B, int S, int H, int dv, const AttnPlan &p) {
-    if (p.n_splits <= 1) return 0;
+    if (p.per_wave || p.n_splits <= 1) return 0;
     return (size_t)B * S * p.n_splits * H * (dv + 2) * sizeof(float);
 }
 

@@ -110,7 +110,10 @@ struct AttnPlan {
     int list_len;        // window width + K
     int tiles_per_wave;  // 32-row tiles each wave handles
     int n_splits;        // workgroups per query
+    bool per_wave;       // one wave per query instead (many queries: chunked prefill)
 };
+// Query rows (times layers) from which every query gets a wave of its own.
+constexpr int kWaveFormQueries = 2048;
 AttnPlan plan_attention(int B, int S, int list_len);  // B*S: query rows (times layers)
 size_t attention_partial_bytes(int B, int S, int H, int dv, const AttnPlan &p);
 hipError_t launch_sparse_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t stream);

@@ -427,21 +427,29 @@ __device__ inline void kv_tile_load(AttnRows<D> &t, const uint8_t *codes, const 
     }
 }
 
-// One 32-row tile: logits, online softmax, P.V.  `tile` is this wave's LDS region of
-// 32 rows x (D+4) bf16.  ndt = dv/16 output tiles are accumulated.
-template <int D>
-__device__ inline void attn_tile_compute(AttnState<D> &st, const bf16x8 (&qb)[D / 32], const AttnRows<D> &t,
-                                         uint16_t *tile, int ndt, float sl2, int g, int c) {
-    constexpr int KS = D / 32;
-    constexpr int NT = D / 16;
-    constexpr int LD = D + 4;
+// A tile's logits (two 16-row halves) and which of its rows are listed.
+struct AttnLogits {
     f32x4 sc[2];
+    uint64_t valid[2];
+};
+
+// First half of a 32-row tile: the logits S^T = rows x Q^T, and the rows copied into this
+// wave's LDS region (`tile`, 32 rows x (D+4) bf16) for the V^T reads.  Once it returns, the
+// row registers may take the next tile's loads.
+template <int D>
+__device__ inline AttnLogits attn_tile_logits(const bf16x8 (&qb)[D / 32], const AttnRows<D> &t, uint16_t *tile,
+                                              int g, int c) {
+    constexpr int KS = D / 32;
+    constexpr int LD = D + 4;
+    AttnLogits lg;
+    lg.valid[0] = t.valid[0];
+    lg.valid[1] = t.valid[1];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-        sc[half] = f32x4{0.f, 0.f, 0.f, 0.f};
+        lg.sc[half] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-            sc[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.r[half][s]), qb[s], sc[half], 0, 0, 0);
+            lg.sc[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.r[half][s]), qb[s], lg.sc[half], 0, 0, 0);
         uint16_t *dst = tile + (16 * half + c) * LD + 8 * g;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -449,14 +457,87 @@ __device__ inline void attn_tile_compute(AttnState<D> &st, const bf16x8 (&qb)[D 
             *reinterpret_cast<u32x2 *>(dst + 32 * s + 4) = u32x2{t.r[half][s][2], t.r[half][s][3]};
         }
     }
+    return lg;
+}
+
+// ---------------------------------------------------------------------------
+// Coalesced row gather, for a wave that walks many tiles.  In the MFMA operand layout 16
+// neighbouring lanes hold 16 different rows, and the vector cache serves every lane's 16
+// bytes as an access of its own (one access a lane a clock bounds such a gather).  Here
+// piece e of a tile -- row e / P, 16-byte piece e % P, P = D / 8 -- is loaded by lane e % 64
+// of load e / 64, so neighbouring lanes read consecutive bytes of one row; the pieces are
+// staged into the wave's LDS tile (row stride LDR bf16) and the logits' row operands are
+// read back from there.
+// ---------------------------------------------------------------------------
+template <int D>
+struct RowPieces {
+    static constexpr int P = D / 8;        // 16-byte pieces a row
+    static constexpr int N = 32 * P / 64;  // loads a lane makes for a tile
+    u32x4 v[N];
+    uint64_t valid;                        // bit r: tile row r is listed
+};
+
+// A tile's loads.  Lane r < 32 passes row r's byte offset in `src` (kOffNone: no row,
+// zeros are read).
+template <int D>
+__device__ inline void row_pieces_load(RowPieces<D> &rp, rsrc_t src, uint32_t off, int lane) {
+    constexpr int P = RowPieces<D>::P;
+    rp.valid = __ballot(lane < 32 && off != kOffNone);
+#pragma unroll
+    for (int j = 0; j < RowPieces<D>::N; ++j) {
+        const int e = 64 * j + lane;
+        const uint32_t o = (uint32_t)__shfl((int)off, e / P);
+        rp.v[j] = __builtin_amdgcn_raw_buffer_load_b128(src, (int)(o + 16u * (uint32_t)(e % P)), 0, 0);
+    }
+}
+
+// The pieces into the wave's LDS tile (rows LDR bf16 apart, LDR a multiple of 8).
+template <int D, int LDR>
+__device__ inline void row_pieces_stage(const RowPieces<D> &rp, uint16_t *tile, int lane) {
+    constexpr int P = RowPieces<D>::P;
+#pragma unroll
+    for (int j = 0; j < RowPieces<D>::N; ++j) {
+        const int e = 64 * j + lane;
+        *reinterpret_cast<u32x4 *>(tile + (e / P) * LDR + 8 * (e % P)) = rp.v[j];
+    }
+}
+
+// attn_tile_logits with the row operands read from the staged LDS tile.
+template <int D, int LDR>
+__device__ inline AttnLogits attn_tile_logits_lds(const bf16x8 (&qb)[D / 32], uint64_t valid, const uint16_t *tile,
+                                                  int g, int c) {
+    constexpr int KS = D / 32;
+    AttnLogits lg;
+    lg.valid[0] = valid & 0xffffull;
+    lg.valid[1] = (valid >> 16) & 0xffffull;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const uint16_t *src = tile + (16 * half + c) * LDR + 8 * g;
+        lg.sc[half] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            lg.sc[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(*reinterpret_cast<const u32x4 *>(src + 32 * s)), qb[s], lg.sc[half], 0, 0, 0);
+    }
+    return lg;
+}
+
+// Second half: online softmax of the logits and O^T += V^T P^T with V^T read transposed
+// from the LDS copy (rows LD bf16 apart).  ndt = dv/16 output tiles are accumulated.  The V^T tiles are read in
+// groups of RG (all D/16 at once by default: one LDS latency per tile; fewer keep fewer
+// registers live).
+template <int D, int RG = D / 16, int LD = D + 4>
+__device__ inline void attn_tile_update(AttnState<D> &st, const AttnLogits &lg, uint16_t *tile, int ndt, float sl2,
+                                        int g, int c) {
+    constexpr int NT = D / 16;
     float x[8];
     float tmax = -INFINITY;
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const bool v = (t.valid[half] >> (4 * g + r)) & 1ull;
-            const float val = v ? sc[half][r] * sl2 : -INFINITY;
+            const bool v = (lg.valid[half] >> (4 * g + r)) & 1ull;
+            const float val = v ? lg.sc[half][r] * sl2 : -INFINITY;
             x[4 * half + r] = val;
             tmax = fmaxf(tmax, val);
         }
@@ -492,24 +573,36 @@ __device__ inline void attn_tile_compute(AttnState<D> &st, const bf16x8 (&qb)[D 
     // 4g..4g+3; a second read 16 rows down gives rows 16+4g..16+4g+3.
     lds_v4s *v0 = (lds_v4s *)((lds_u16 *)tile + (4 * g + (c >> 2)) * LD + 4 * (c & 3));
     lds_v4s *v1 = (lds_v4s *)((lds_u16 *)tile + (16 + 4 * g + (c >> 2)) * LD + 4 * (c & 3));
-    // Every column tile is read (all within the row's D dims) before the first product, so
-    // the reads' LDS latency is paid once rather than once per output tile; only the ndt
-    // tiles of dv are accumulated.
-    v4s lo[NT], hi[NT];
+    // Every column tile of a group is read (all within the row's D dims) before the group's
+    // first product, so the reads' LDS latency is paid once per group rather than once per
+    // output tile; only the ndt tiles of dv are accumulated.
+    static_assert(NT % RG == 0, "groups of whole column tiles");
 #pragma unroll
-    for (int dt = 0; dt < NT; ++dt) {
-        lo[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v0 + 4 * dt);
-        hi[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v1 + 4 * dt);
-    }
+    for (int d0 = 0; d0 < NT; d0 += RG) {
+        v4s lo[RG], hi[RG];
 #pragma unroll
-    for (int dt = 0; dt < NT; ++dt) {
-        if (dt < ndt) {
-            const bf16x8 va = __builtin_bit_cast(
-                bf16x8, (v8s){lo[dt][0], lo[dt][1], lo[dt][2], lo[dt][3], hi[dt][0], hi[dt][1], hi[dt][2], hi[dt][3]});
-            st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.o[dt], 0, 0, 0);
+        for (int u = 0; u < RG; ++u) {
+            lo[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v0 + 4 * (d0 + u));
+            hi[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v1 + 4 * (d0 + u));
+        }
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+            if (d0 + u < ndt) {
+                const bf16x8 va = __builtin_bit_cast(
+                    bf16x8, (v8s){lo[u][0], lo[u][1], lo[u][2], lo[u][3], hi[u][0], hi[u][1], hi[u][2], hi[u][3]});
+                st.o[d0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.o[d0 + u], 0, 0, 0);
+            }
         }
     }
     wave_lds_sync();  // reads done before the next tile overwrites the region
+}
+
+// One 32-row tile: logits, online softmax, P.V.
+template <int D>
+__device__ inline void attn_tile_compute(AttnState<D> &st, const bf16x8 (&qb)[D / 32], const AttnRows<D> &t,
+                                         uint16_t *tile, int ndt, float sl2, int g, int c) {
+    const AttnLogits lg = attn_tile_logits<D>(qb, t, tile, g, c);
+    attn_tile_update<D>(st, lg, tile, ndt, sl2, g, c);
 }
 
 // Finish a wave: the normaliser summed over the wave (m is already uniform per head).
