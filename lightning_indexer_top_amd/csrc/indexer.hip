@@ -240,23 +240,8 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_staged_kernel(Inde
     }
 }
 
-// 16 index heads of 64 e4m3 dims (the chunked-prefill shape): V_MFMA_SCALE_F32_32X32X64_F8F6F4
-// takes two queries' 16 heads as its 32 rows and 32 keys as its columns.  Its 64-deep K is
-// exactly a head's dims, where the 16x16x128 form carries a zero half, so a query needs half
-// the MFMA passes.  Operand layout, measured with an on-GPU probe: lane 32g + r holds row r,
-// its bytes 0-15 belong to K block 0 and bytes 16-31 to K block 1, and lane group g
-// supplies block g's scale; a lane therefore loads row bytes [16g, 16g+16) and
-// [32+16g, 32+16g+16) and the row's scale byte g (the order of K within a block is the same
-// for both operands, so it does not matter).  The result comes back as lane 32g + c,
-// register 4i + r = row 8i + 4g + r, column c: rows 0-15 are the first query's heads.
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ inline i32x8 mx32_operand(const uint8_t *row, int g) {
-    const u32x4 lo = *reinterpret_cast<const u32x4 *>(row + 16 * g);
-    const u32x4 hi = *reinterpret_cast<const u32x4 *>(row + 32 + 16 * g);
-    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-}
-
+// 16 index heads of 64 e4m3 dims (the chunked-prefill shape): two queries' heads against 32
+// keys per V_MFMA_SCALE_F32_32X32X64_F8F6F4 (operand layout and epilogue in tile_ops.h).
 __global__ __launch_bounds__(kWaves * 64) void indexer_scores_mx32_kernel(IndexerArgs a) {
     constexpr int NH = 16, E = 64, NB = 2;
     __shared__ __attribute__((aligned(16))) uint8_t qc[kQB][NH * E];   // codes
@@ -320,33 +305,14 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_mx32_kernel(Indexe
         const int qr = c < 16 ? qa : qb;
         const i32x8 av = mx32_operand(&qc[qr][h * E], g);
         const int as = qs[qr][h * NB + g];
+        const Mx32Weights wt = mx32_weights(&qw[qa][0], &qw[qb][0], g);
         f32x16 acc[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
             acc[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, kb[m], f32x16{}, 0, 0, 0, as, 0, ks[m]);
-        // the head weights of the rows this lane receives: heads 4g+r and 8+4g+r of each query
-        const f32x4 wa0 = *reinterpret_cast<const f32x4 *>(&qw[qa][4 * g]);
-        const f32x4 wa1 = *reinterpret_cast<const f32x4 *>(&qw[qa][8 + 4 * g]);
-        const f32x4 wb0 = *reinterpret_cast<const f32x4 *>(&qw[qb][4 * g]);
-        const f32x4 wb1 = *reinterpret_cast<const f32x4 *>(&qw[qb][8 + 4 * g]);
         float sc[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            float sa = 0.f, sb = 0.f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sa += wa0[r] * relu_bits(acc[m][r]);
-                sa += wa1[r] * relu_bits(acc[m][4 + r]);
-                sb += wb0[r] * relu_bits(acc[m][8 + r]);
-                sb += wb1[r] * relu_bits(acc[m][12 + r]);
-            }
-            // lanes 32 apart hold the two halves of each query's heads: swapping the upper
-            // half of sa with the lower half of sb and adding leaves query qa's score in
-            // lanes 0-31 and query qa+1's in lanes 32-63
-            const uint64_t x = __builtin_bit_cast(
-                uint64_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(sa), __float_as_uint(sb), false, false));
-            sc[m] = __uint_as_float((uint32_t)x) + __uint_as_float((uint32_t)(x >> 32));
-        }
+        for (int m = 0; m < 2; ++m) sc[m] = mx32_pair_scores(acc[m], wt);
         // the two queries' visible counts on the scalar unit (a lane-dependent numerator would
         // make this a vector division)
         const int va = __builtin_amdgcn_readfirstlane((a.start_pos + i0 + qa + 1) / a.ratio);

@@ -162,6 +162,57 @@ __device__ inline IdxKeys load_idx_keys(const IndexerArgs &a, size_t row, int g)
 // to +0.
 __device__ inline float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// ---------------------------------------------------------------------------
+// 16 index heads of 64 e4m3 dims (the chunked-prefill indexer shape):
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 takes two queries' 16 heads as its 32 rows and 32 keys
+// as its columns.  Its 64-deep K is exactly a head's dims, where the 16x16x128 form carries
+// a zero half, so a query needs half the MFMA passes.  Operand layout, measured with an
+// on-GPU probe: lane 32g + r holds row r, its bytes 0-15 belong to K block 0 and bytes
+// 16-31 to K block 1, and lane group g supplies block g's scale; a lane therefore loads row
+// bytes [16g, 16g+16) and [32+16g, 32+16g+16) and the row's scale byte g (the order of K
+// within a block is the same for both operands, so it does not matter).  The result comes
+// back as lane 32g + c, register 4i + r = row 8i + 4g + r, column c: rows 0-15 are the first
+// query's heads.
+// ---------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ inline i32x8 mx32_operand(const uint8_t *row, int g) {
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(row + 16 * g);
+    const u32x4 hi = *reinterpret_cast<const u32x4 *>(row + 32 + 16 * g);
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// The head weights of the rows lane group g receives: heads 4g+r and 8+4g+r of each query.
+struct Mx32Weights {
+    f32x4 a0, a1, b0, b1;
+};
+__device__ inline Mx32Weights mx32_weights(const float *wa, const float *wb, int g) {
+    Mx32Weights w;
+    w.a0 = *reinterpret_cast<const f32x4 *>(wa + 4 * g);
+    w.a1 = *reinterpret_cast<const f32x4 *>(wa + 8 + 4 * g);
+    w.b0 = *reinterpret_cast<const f32x4 *>(wb + 4 * g);
+    w.b1 = *reinterpret_cast<const f32x4 *>(wb + 8 + 4 * g);
+    return w;
+}
+
+// The two queries' scores of one 32-key tile from its MFMA result: the head-weighted ReLU
+// sum, query A's score of key c in lane c, query B's in lane 32 + c.  Lanes 32 apart hold
+// the two halves of each query's heads: swapping the upper half of the A partials with the
+// lower half of the B partials and adding finishes both sums.
+__device__ inline float mx32_pair_scores(const f32x16 &acc, const Mx32Weights &w) {
+    float sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        sa += w.a0[r] * relu_bits(acc[r]);
+        sa += w.a1[r] * relu_bits(acc[4 + r]);
+        sb += w.b0[r] * relu_bits(acc[8 + r]);
+        sb += w.b1[r] * relu_bits(acc[12 + r]);
+    }
+    const uint64_t x = __builtin_bit_cast(
+        uint64_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(sa), __float_as_uint(sb), false, false));
+    return __uint_as_float((uint32_t)x) + __uint_as_float((uint32_t)(x >> 32));
+}
+
 // Scores of four 16-key tiles for one query.  All 4*HT MFMAs are issued first; each
 // lane then holds, per tile, the head-weighted ReLU sum over its 4 heads of every head
 // tile, and the sum over the four lane groups takes three lane swaps and three adds:

@@ -983,3 +983,45 @@ def test_step_level_two_combined_forms(orc, kv, NL, start_pos, flags):
                                None, wf, None if win_sc is None else win_sc[ly], cf, inp.comp_sc)
         err = np.abs(g_out[ly] - want).max()
         assert err <= ATTN_TOL, f"layer {ly}: {err}"
+
+
+# ---------------------------------------------------------------------------------
+# chunked prefill steps (16 index heads of 64 e4m3 dims): exact against the separate calls
+# ---------------------------------------------------------------------------------
+PS_CASES = [
+    # B, S, start_pos, ratio, k, keys, oracle sample (None: every query)
+    (1, 4096, 12288, 2, 512, "normal", 24),   # prefill-16k's shape
+    (2, 301, 0, 2, 64, "normal", None),       # from position 0 (early rows: fewer than k), ragged S
+    (1, 1030, 7000, 4, 300, "mixture", 64),   # clustered scores: several narrowing levels
+    (1, 64, 8128, 1, 2048, "normal", 16),     # T = 8192 rows at ratio 1, large k
+    (2, 96, 4000, 2, 128, "dup", None),       # every key row twice: exactly equal scores
+    (1, 40, 2000, 2, 64, "const", None),      # one key for every row: all scores equal
+]
+
+
+@pytest.mark.parametrize("B,S,start_pos,ratio,k,keys,sample", PS_CASES)
+def test_prefill_step_exact(orc, B, S, start_pos, ratio, k, keys, sample):
+    """Chunked-prefill steps: the step's picks equal lit_indexer_scores followed by lit_topk
+    bit for bit (equal scores lowest row first: duplicated and constant keys), and match the
+    oracle (sets up to near-ties, attention on the GPU's own lists)."""
+    inp = synth.make_step(B=B, S=S, start_pos=start_pos, ratio=ratio, Hi=16, Di=64, H=16, D=128, W=128,
+                          index_topk=k, seed=110 + S, keys="mixture" if keys == "mixture" else "normal")
+    if keys == "dup":
+        n_odd = inp.k8[:, 1::2].shape[1]
+        inp.k8[:, 1::2] = inp.k8[:, 0::2][:, :n_odd]
+        inp.k_sc[:, 1::2] = inp.k_sc[:, 0::2][:, :n_odd]
+    elif keys == "const":
+        inp.k8[:] = inp.k8[:, :1]
+        inp.k_sc[:] = inp.k_sc[:, :1]
+    d = step_inputs_dev(inp)
+    idx, out = _run_step(d, inp, L.LIT_STEP_UNFUSED)
+    sc = L.lit_indexer_scores(d["q8"], d["q_sc"], d["w"], d["k8"], d["k_sc"], inp.start_pos, inp.ratio)
+    idx2 = L.lit_topk(sc, inp.start_pos, inp.ratio, inp.index_topk)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2), torch.nonzero(idx != idx2)[:5].tolist()
+    queries = [(b, i) for b in range(B) for i in range(S)]
+    if sample is not None:
+        rng = np.random.default_rng(7)
+        pick = rng.choice(len(queries), size=sample, replace=False)
+        queries = sorted({queries[j] for j in pick} | {queries[0], queries[-1]})
+    _check_step(orc, inp, idx, out, queries)

@@ -39,8 +39,8 @@ def test_oracle_under_asan_ubsan(tmp_path):
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc missing")
 def test_abi_host_side_under_asan_ubsan(tmp_path):
-    srcs = [os.path.join(CSRC, f + ".hip") for f in
-            ("lit_api", "indexer", "topk", "attention", "produce", "fused_decode")]
+    from lightning_indexer_top_amd import build as lit_build
+    srcs = [os.path.join(CSRC, f) for f in lit_build.SOURCES]
     srcs += [os.path.join(SAN, "abi_driver.cpp"), os.path.join(SAN, "fused_stub.cpp")]
 
     def compile_one(src):
