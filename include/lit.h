@@ -16,7 +16,8 @@
  *   (window rows derived in-kernel) as one stream-ordered sequence, for one
  *   layer or several layers that share the top-k.  lit_sparse_attn_fmt reads
  *   quantised KV caches; lit_compress_append / lit_window_append write them
- *   (the cache writes of a decode step).
+ *   (the cache writes of a decode step), lit_compress_chunk / lit_window_chunk
+ *   those of a chunk (prefill).
  *
  * Sources (page title, symbol):
  *   [V4.1] DeepSeek-V4.1-Flash-NVFP4, inference/model.py -- module globals
@@ -365,6 +366,43 @@ lit_status lit_compress_append(int B, int D, int ratio, int start_pos, const flo
 lit_status lit_window_append(int B, int D, int start_pos, const uint16_t *kv, const float *freqs,
                              int n_pos, int rd, uint8_t *codes, uint8_t *scales, int R,
                              void *stream);
+
+/*
+ * Chunks (chunked prefill): S tokens per sequence at positions start_pos ..
+ * start_pos + S - 1, by definition the S decode steps above in order, in one launch.
+ * At start_pos 0 this is the pages' prefill branch ([V4.1] Compressor.forward with
+ * start_pos == 0: whole groups pooled at once, the S % ratio remaining tokens left in
+ * the state; Attention._window_kv prefill: the ring seeded with the chunk's last rows).
+ *
+ * lit_compress_chunk -- writes compressed rows start_pos / ratio ..
+ * (start_pos + S) / ratio - 1 (lit_compress_chunk_rows of them): group g pooled over
+ * positions g*ratio .. g*ratio + ratio - 1 (those before start_pos from the state),
+ * normalised, rotated at g*ratio and quantised as in lit_compress_append.  Afterwards
+ * slot r of the state holds the chunk's last token at a position = r (mod ratio), where
+ * the chunk has one (the slots a later decode step reads).
+ *
+ *   kv, score  (device) f32 [B, S, D]
+ *   latent     (device) bf16 [B, rows, D] or NULL: each written row's pre-rotation latent
+ *   others as in lit_compress_append
+ * Requirements: those of lit_compress_append; every rotation position < n_pos and
+ * every written row < T_cap.
+ *
+ * lit_window_chunk -- the chunk's window rows: position p = start_pos + t rotated at p,
+ * quantised to LIT_KV_E4M3 and written to slot p % R, for the last min(S, R) rows (an
+ * earlier row's slot is taken again within the chunk).
+ *
+ *   kv     (device) bf16 [B, S, D]
+ *   others as in lit_window_append; start_pos + S - 1 < n_pos.
+ */
+int lit_compress_chunk_rows(int start_pos, int S, int ratio);
+lit_status lit_compress_chunk(int B, int S, int D, int ratio, int start_pos, const float *kv,
+                              const float *score, float *kv_state, float *score_state,
+                              const float *norm_w, float eps, const float *freqs, int n_pos,
+                              int rd, uint8_t *codes, uint8_t *scales, int T_cap,
+                              uint16_t *latent, void *stream);
+lit_status lit_window_chunk(int B, int S, int D, int start_pos, const uint16_t *kv,
+                            const float *freqs, int n_pos, int rd, uint8_t *codes,
+                            uint8_t *scales, int R, void *stream);
 
 /*
  * lit_sparse_step -- the whole step for one layer: lit_indexer_scores, lit_topk

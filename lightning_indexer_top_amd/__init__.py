@@ -12,4 +12,4 @@ from .lit import (LitError, library, lit_indexer_scores, lit_sparse_attn,  # noq
                   lit_sparse_step_state_bytes, state_error, lit_candidate_blocks,
                   lit_topk_candidates, INDEX_FORMATS, lit_sparse_attn_layers,
                   lit_sparse_attn_fmt, KV_FORMATS, lit_compress_append, lit_window_append,
-                  lit_sparse_step_noalloc)
+                  lit_sparse_step_noalloc, lit_compress_chunk, lit_window_chunk)

@@ -394,6 +394,46 @@ lit_status lit_window_append(int B, int D, int start_pos, const uint16_t *kv, co
     return hip_status(launch_window_append(p, (hipStream_t)stream));
 }
 
+int lit_compress_chunk_rows(int start_pos, int S, int ratio) { return compress_chunk_rows(start_pos, S, ratio); }
+
+lit_status lit_compress_chunk(int B, int S, int D, int ratio, int start_pos, const float *kv, const float *score,
+                              float *kv_state, float *score_state, const float *norm_w, float eps,
+                              const float *freqs, int n_pos, int rd, uint8_t *codes, uint8_t *scales, int T_cap,
+                              uint16_t *latent, void *stream) {
+    if (ratio < 1 || start_pos < 0 || S < 0 || T_cap < 0) return LIT_E_SHAPE;
+    if ((long)start_pos + S > INT_MAX) return LIT_E_SHAPE;
+    const int n = compress_chunk_rows(start_pos, S, ratio);
+    // the last written row's rotation position is the largest one
+    const int last_pos = n > 0 ? (start_pos / ratio + n - 1) * ratio : 0;
+    lit_status st = check_produce(B, D, rd, last_pos, n > 0 ? n_pos : 1, freqs);
+    if (st != LIT_OK) return st;
+    if (B == 0 || S == 0) return LIT_OK;
+    if (n > 0 && start_pos / ratio + n - 1 >= T_cap) return LIT_E_SHAPE;
+    if (!kv || !norm_w || (ratio > 1 && (!score || !kv_state || !score_state))) return LIT_E_NULL;
+    if (n > 0 && (!codes || !scales)) return LIT_E_NULL;
+    ProduceArgs p{};
+    p.B = B; p.D = D; p.ratio = ratio; p.start_pos = start_pos; p.rd = rd; p.S = S;
+    p.kv = kv; p.score = score; p.kv_state = kv_state; p.score_state = score_state;
+    p.norm_w = norm_w; p.eps = eps; p.freqs = freqs; p.codes = codes; p.scales = scales;
+    p.T_cap = T_cap; p.latent = latent;
+    return hip_status(launch_compress_chunk(p, (hipStream_t)stream));
+}
+
+lit_status lit_window_chunk(int B, int S, int D, int start_pos, const uint16_t *kv, const float *freqs, int n_pos,
+                            int rd, uint8_t *codes, uint8_t *scales, int R, void *stream) {
+    if (start_pos < 0 || S < 0 || R < 0) return LIT_E_SHAPE;
+    if ((long)start_pos + S > INT_MAX) return LIT_E_SHAPE;
+    lit_status st = check_produce(B, D, rd, S > 0 ? start_pos + S - 1 : 0, S > 0 ? n_pos : 1, freqs);
+    if (st != LIT_OK) return st;
+    if (B == 0 || S == 0) return LIT_OK;
+    if (R < 1) return LIT_E_SHAPE;
+    if (!kv || !codes || !scales) return LIT_E_NULL;
+    ProduceArgs p{};
+    p.B = B; p.D = D; p.start_pos = start_pos; p.rd = rd; p.freqs = freqs; p.S = S;
+    p.win_in = kv; p.codes = codes; p.scales = scales; p.R = R;
+    return hip_status(launch_window_chunk(p, (hipStream_t)stream));
+}
+
 // Workspace of the multi-kernel step: scores [B*S, ld] fp32, then the attention partials
 // (level one's block scores share the partials' space: they are used up before).
 static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld, AttnPlan *plan) {

@@ -171,18 +171,23 @@ __host__ __device__ inline int window_slot_at(const WindowBase &w, int start_pos
 // ---------------------------------------------------------------------------
 struct ProduceArgs {
     int B, D, ratio, start_pos, rd;
-    const float *kv, *score;        // [B,D] compressor inputs (fp32)
+    const float *kv, *score;        // [B,S,D] compressor inputs (fp32; S = 1: a decode step)
     float *kv_state, *score_state;  // [B,ratio,D] (ratio > 1)
     const float *norm_w;            // [D]
     float eps;
     const float *freqs;             // [positions, rd/2, 2] (cos, sin)
-    const uint16_t *win_in;         // [B,D] bf16 window KV row (window append)
+    const uint16_t *win_in;         // [B,S,D] bf16 window KV rows (window append / chunk)
     uint8_t *codes, *scales;        // cache codes / scale bytes
     int T_cap, R;
-    uint16_t *latent;               // [B,D] bf16 pre-rotation latent, or NULL
+    uint16_t *latent;               // [B,rows,D] bf16 pre-rotation latents, or NULL
+    int S = 1;                      // tokens per sequence (a chunk)
 };
 hipError_t launch_compress_append(const ProduceArgs &p, hipStream_t stream);
 hipError_t launch_window_append(const ProduceArgs &p, hipStream_t stream);
+// Chunks: S tokens per sequence, the S decode steps' writes in one launch each.
+int compress_chunk_rows(int start_pos, int S, int ratio);  // compressed rows a chunk writes
+hipError_t launch_compress_chunk(const ProduceArgs &p, hipStream_t stream);
+hipError_t launch_window_chunk(const ProduceArgs &p, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Fused decode step (fused_decode.hip)

@@ -73,6 +73,9 @@ SIGNATURES = {
     "lit_compress_append": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _F, _P, _I, _I, _P, _P, _I, _P,
                                  _P]),
     "lit_window_append": (_I, [_I, _I, _I, _P, _P, _I, _I, _P, _P, _I, _P]),
+    "lit_compress_chunk_rows": (_I, [_I, _I, _I]),
+    "lit_compress_chunk": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _F, _P, _I, _I, _P, _P, _I, _P, _P]),
+    "lit_window_chunk": (_I, [_I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _I, _P]),
     "lit_sparse_step": (_I, [ctypes.POINTER(lit_step_args), _P, _Z, _P]),
     "lit_sparse_step_workspace_bytes": (_Z, [ctypes.POINTER(lit_step_args)]),
     "lit_sparse_step_state_bytes": (_Z, [ctypes.POINTER(lit_step_args)]),
@@ -350,6 +353,40 @@ def lit_window_append(kv, freqs, rd: int, codes, scales, start_pos: int, stream=
         _need(t, dt, n)
     _check("lit_window_append", library().lit_window_append(
         B, D, start_pos, _ptr(kv), _ptr(freqs), freqs.shape[0], rd, _ptr(codes), _ptr(scales),
+        codes.shape[1], _stream(stream)))
+
+
+def lit_compress_chunk(kv, score, kv_state, score_state, norm_w, eps: float, freqs, rd: int,
+                       codes, scales, start_pos: int, ratio: int, latent=None, stream=None) -> int:
+    """A chunk of S tokens per sequence (kv, score [B, S, D]) into the compressor; returns
+    the number of compressed rows written (latent, if given: [B, rows, D] bf16)."""
+    _need(kv, torch.float32, "kv")
+    B, S, D = kv.shape
+    for t, dt, n in ((score, torch.float32, "score"), (norm_w, torch.float32, "norm_w"),
+                     (freqs, torch.float32, "freqs"), (codes, torch.uint8, "codes"),
+                     (scales, torch.uint8, "scales")):
+        _need(t, dt, n)
+    for t, n in ((kv_state, "kv_state"), (score_state, "score_state")):
+        if t is not None:
+            _need(t, torch.float32, n)
+    if latent is not None:
+        _need(latent, torch.bfloat16, "latent")
+    _check("lit_compress_chunk", library().lit_compress_chunk(
+        B, S, D, ratio, start_pos, _ptr(kv), _ptr(score), _ptr(kv_state), _ptr(score_state),
+        _ptr(norm_w), float(eps), _ptr(freqs), freqs.shape[0], rd, _ptr(codes), _ptr(scales),
+        codes.shape[1], _ptr(latent), _stream(stream)))
+    return int(library().lit_compress_chunk_rows(start_pos, S, ratio))
+
+
+def lit_window_chunk(kv, freqs, rd: int, codes, scales, start_pos: int, stream=None) -> None:
+    """A chunk of S window rows per sequence (kv [B, S, D] bf16) into the ring."""
+    _need(kv, torch.bfloat16, "kv")
+    B, S, D = kv.shape
+    for t, dt, n in ((freqs, torch.float32, "freqs"), (codes, torch.uint8, "codes"),
+                     (scales, torch.uint8, "scales")):
+        _need(t, dt, n)
+    _check("lit_window_chunk", library().lit_window_chunk(
+        B, S, D, start_pos, _ptr(kv), _ptr(freqs), freqs.shape[0], rd, _ptr(codes), _ptr(scales),
         codes.shape[1], _stream(stream)))
 
 

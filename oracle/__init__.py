@@ -97,7 +97,9 @@ def _bind(path: str):
     lib.orc_quant_e4m3.restype = None
     lib.orc_quant_e2m1.argtypes = [P, I, P, P]
     lib.orc_quant_e2m1.restype = None
-    lib.orc_compress_append.argtypes = [I, I, I, I, P, P, P, P, P, ctypes.c_double, P, I, P, P, I, P]
+    lib.orc_compress_append.argtypes = [I, I, I, I, P, P, P, P, P, ctypes.c_double, P, I, P, P, I, P, P, P]
+    lib.orc_compress_write.argtypes = [I, P, P, I, I, P, P]
+    lib.orc_compress_write.restype = I
     lib.orc_compress_append.restype = I
     lib.orc_window_append.argtypes = [I, I, I, P, P, I, I, P, P]
     lib.orc_window_append.restype = I
@@ -387,9 +389,11 @@ def quant_e2m1(x) -> tuple:
 
 
 def compress_append(kv, score, kv_state, score_state, norm_w, eps: float, freqs, rd: int,
-                    codes, scales, start_pos: int, ratio: int):
+                    codes, scales, start_pos: int, ratio: int, raw: bool = False):
     """One decode step of the compressor and the compressed-cache write (in place on
-    kv_state / score_state / codes / scales).  Returns (row written?, latent [B, D])."""
+    kv_state / score_state / codes / scales).  Returns (row written?, latent [B, D]),
+    and with raw=True also the pooled kv and the norm's result before their bf16
+    roundings ([B, D] each)."""
     kv = _c(kv, np.float32)
     score = _c(score, np.float32)
     B, D = kv.shape
@@ -400,15 +404,61 @@ def compress_append(kv, score, kv_state, score_state, norm_w, eps: float, freqs,
         if a.dtype != np.uint8 or not a.flags.c_contiguous:
             raise OracleError("codes / scales must be contiguous uint8 (updated in place)")
     latent = np.zeros((B, D), dtype=np.float64)
+    pooled = np.zeros((B, D), dtype=np.float64)
+    normed = np.zeros((B, D), dtype=np.float64)
     rc = _load().orc_compress_append(B, D, ratio, start_pos, _ptr(kv), _ptr(score),
                                      _ptr(kv_state) if ratio > 1 else None,
                                      _ptr(score_state) if ratio > 1 else None,
                                      _ptr(_c(norm_w, np.float32)), float(eps),
                                      _ptr(_c(freqs, np.float32)), rd, _ptr(codes), _ptr(scales),
-                                     codes.shape[1], _ptr(latent))
+                                     codes.shape[1], _ptr(latent), _ptr(pooled), _ptr(normed))
     if rc < 0:
         _check(rc, "orc_compress_append")
+    if raw:
+        return bool(rc), latent, pooled, normed
     return bool(rc), latent
+
+
+def compress_write(latent, freqs, rd: int, pos: int) -> tuple:
+    """The compressed-cache row of one pre-rotation latent [D] (bf16 values): rotated at
+    `pos`, quantised; returns (codes [D/2], scales [D/16])."""
+    lat = _c(latent, np.float64)
+    D = lat.shape[-1]
+    codes = np.zeros(D // 2, np.uint8)
+    scales = np.zeros(D // 16, np.uint8)
+    _check(_load().orc_compress_write(D, _ptr(lat), _ptr(_c(freqs, np.float32)), rd, pos, _ptr(codes),
+                                      _ptr(scales)), "orc_compress_write")
+    return codes, scales
+
+
+def compress_chunk(kv, score, kv_state, score_state, norm_w, eps: float, freqs, rd: int,
+                   codes, scales, start_pos: int, ratio: int):
+    """A chunk of S tokens per sequence into the compressor: by definition the S decode
+    steps start_pos, start_pos + 1, ... in order (at start_pos 0 this is the pages'
+    prefill branch: whole groups pooled, the remainder left in the state).  kv, score
+    [B, S, D].  Returns (rows written, latents [B, rows, D], pooled_raw, norm_raw)."""
+    kv = _c(kv, np.float32)
+    score = _c(score, np.float32)
+    B, S, D = kv.shape
+    lat, pooled, normed = [], [], []
+    for t in range(S):
+        w, l, pr, nr = compress_append(kv[:, t], score[:, t], kv_state, score_state, norm_w, eps, freqs, rd,
+                                       codes, scales, start_pos + t, ratio, raw=True)
+        if w:
+            lat.append(l)
+            pooled.append(pr)
+            normed.append(nr)
+    stack = lambda xs: np.stack(xs, axis=1) if xs else np.zeros((B, 0, D))  # noqa: E731
+    return len(lat), stack(lat), stack(pooled), stack(normed)
+
+
+def window_chunk(kv_bits, freqs, rd: int, codes, scales, start_pos: int):
+    """A chunk of S bf16 window rows per sequence ([B, S, D]) into the ring: by definition
+    the S decode-step writes in order (a later position takes a slot an earlier one held;
+    at start_pos 0 this is the pages' prefill seeding of the ring)."""
+    kv_bits = _c(kv_bits, np.uint16)
+    for t in range(kv_bits.shape[1]):
+        window_append(kv_bits[:, t], freqs, rd, codes, scales, start_pos + t)
 
 
 def window_append(kv_bits, freqs, rd: int, codes, scales, start_pos: int):

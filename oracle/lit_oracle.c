@@ -543,7 +543,15 @@ int orc_sparse_attn(const uint16_t *q, int B, int S, int H, int D, int dv,
 /*     e2m1 value nearest to x / s, ties to the even code, sign of x kept.   */
 /* Intermediate values are exact (double) and rounded to bf16 where the      */
 /* pages store bf16: after the cast of the pooled kv, after the norm, after  */
-/* the rotation.  freqs: [positions, rd/2, 2] floats (cos, sin), as          */
+/* the rotation -- except the rotation itself, which the pages compute in    */
+/* fp32 (apply_rotary_emb: x.float() viewed as complex64 times freqs_cis):   */
+/* there each product and the sum or difference is rounded to fp32 in turn,  */
+/* no fused multiply-add (the plainest fp32 reading), then to bf16.  The     */
+/* pooling and the norm are fp32 on the pages too, but their last bits       */
+/* depend on the exp / rsqrt implementation and the summation order, which   */
+/* the pages do not fix; the exact values are kept here (and returned        */
+/* unrounded, so that a test can see how close to a bf16 rounding midpoint a  */
+/* value lies).  freqs: [positions, rd/2, 2] floats (cos, sin), as           */
 /* precompute_freqs_cis tabulates them.                                      */
 /* ------------------------------------------------------------------------ */
 
@@ -620,34 +628,59 @@ void orc_quant_e2m1(const double *x, int D, uint8_t *codes, uint8_t *scales) {
     }
 }
 
-/* RMSNorm of D values (each already a bf16 value), result rounded to bf16. */
-static void orc_rmsnorm_bf16(const double *x, const float *w, int D, double eps, double *y) {
+/* RMSNorm of D values (each already a bf16 value), result rounded to bf16;  */
+/* raw (may be NULL) receives the values before that rounding.               */
+static void orc_rmsnorm_bf16(const double *x, const float *w, int D, double eps, double *y, double *raw) {
     double ss = 0.0;
     for (int d = 0; d < D; ++d) ss += x[d] * x[d];
     double r = 1.0 / sqrt(ss / D + eps);
-    for (int d = 0; d < D; ++d) y[d] = orc_round_bf16((double)w[d] * (x[d] * r));
+    for (int d = 0; d < D; ++d) {
+        const double v = (double)w[d] * (x[d] * r);
+        if (raw) raw[d] = v;
+        y[d] = orc_round_bf16(v);
+    }
 }
 
-/* Rotate the last rd of D values at table row `pos`, rounding to bf16. */
+/* Rotate the last rd of D bf16 values at table row `pos`: the complex product */
+/* in fp32 (products, then their difference / sum, each rounded to fp32),     */
+/* then rounded to bf16.                                                      */
 static void orc_rope_bf16(double *x, int D, int rd, const float *freqs, int pos) {
     const float *f = freqs + (size_t)pos * rd; /* rd/2 (cos, sin) pairs */
     for (int j = 0; j < rd / 2; ++j) {
-        double a = x[D - rd + 2 * j], b = x[D - rd + 2 * j + 1];
-        double c = f[2 * j], sn = f[2 * j + 1];
-        x[D - rd + 2 * j] = orc_round_bf16(a * c - b * sn);
-        x[D - rd + 2 * j + 1] = orc_round_bf16(a * sn + b * c);
+        const float a = (float)x[D - rd + 2 * j], b = (float)x[D - rd + 2 * j + 1];
+        const float c = f[2 * j], sn = f[2 * j + 1];
+        const float ac = a * c, bs = b * sn, as = a * sn, bc = b * c;
+        const float re = ac - bs, im = as + bc;
+        x[D - rd + 2 * j] = orc_round_bf16((double)re);
+        x[D - rd + 2 * j + 1] = orc_round_bf16((double)im);
     }
+}
+
+/* The compressed-cache write of one latent (D bf16 values, pre-rotation): rotated at */
+/* position pos, quantised to e2m1 / e4m3-16 into one row (codes D/2, scales D/16).   */
+int orc_compress_write(int D, const double *latent, const float *freqs, int rd, int pos,
+                       uint8_t *codes, uint8_t *scales) {
+    if (D <= 0 || D % 32 != 0 || pos < 0 || rd < 0 || rd > D || rd % 2 != 0) return ORC_E_ARG;
+    double *y = (double *)malloc(sizeof(double) * (size_t)D);
+    for (int d = 0; d < D; ++d) y[d] = latent[d];
+    orc_rope_bf16(y, D, rd, freqs, pos);
+    orc_quant_e2m1(y, D, codes, scales);
+    free(y);
+    return 0;
 }
 
 /* One decode step of the compressor and the compressed-cache write.  kv, score:
  * [B, D] floats; kv_state, score_state: [B, ratio, D] floats (ratio > 1; updated);
  * codes [B, T_cap, D/2], scales [B, T_cap, D/16] (row start_pos/ratio written when
  * the group completes); latent [B, D] doubles (pre-rotation bf16 values, may be
- * NULL).  Returns 1 when a row was written, 0 when the group is still filling. */
+ * NULL); pooled_raw and norm_raw [B, D] doubles (may be NULL): the pooled kv before
+ * its bf16 cast and the norm's result before its bf16 rounding.  Returns 1 when a
+ * row was written, 0 when the group is still filling. */
 int orc_compress_append(int B, int D, int ratio, int start_pos, const float *kv,
                         const float *score, float *kv_state, float *score_state,
                         const float *norm_w, double eps, const float *freqs, int rd,
-                        uint8_t *codes, uint8_t *scales, int T_cap, double *latent) {
+                        uint8_t *codes, uint8_t *scales, int T_cap, double *latent,
+                        double *pooled_raw, double *norm_raw) {
     if (B < 0 || D <= 0 || D % 32 != 0 || ratio < 1 || start_pos < 0 || rd < 0 ||
         rd > D || rd % 2 != 0)
         return ORC_E_ARG;
@@ -660,7 +693,10 @@ int orc_compress_append(int B, int D, int ratio, int start_pos, const float *kv,
         double *x = (double *)malloc(sizeof(double) * (size_t)D * 2);
         double *y = x + D;
         if (ratio == 1) {
-            for (int d = 0; d < D; ++d) x[d] = orc_round_bf16(k[d]);
+            for (int d = 0; d < D; ++d) {
+                if (pooled_raw) pooled_raw[(size_t)b * D + d] = k[d];
+                x[d] = orc_round_bf16(k[d]);
+            }
         } else {
             float *ks = kv_state + (size_t)b * ratio * D, *gs = score_state + (size_t)b * ratio * D;
             const int slot = start_pos % ratio;
@@ -678,10 +714,11 @@ int orc_compress_append(int B, int D, int ratio, int start_pos, const float *kv,
                     z += e;
                     acc += e * (double)ks[(size_t)r * D + d];
                 }
+                if (pooled_raw) pooled_raw[(size_t)b * D + d] = acc / z;
                 x[d] = orc_round_bf16(acc / z); /* kv.to(dtype) */
             }
         }
-        orc_rmsnorm_bf16(x, norm_w, D, eps, y);
+        orc_rmsnorm_bf16(x, norm_w, D, eps, y, norm_raw ? norm_raw + (size_t)b * D : NULL);
         if (latent) for (int d = 0; d < D; ++d) latent[(size_t)b * D + d] = y[d];
         orc_rope_bf16(y, D, rd, freqs, pos);
         orc_quant_e2m1(y, D, codes + ((size_t)b * T_cap + row) * (D / 2),

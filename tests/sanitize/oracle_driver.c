@@ -30,7 +30,9 @@ int orc_sparse_attn_fmt(const uint16_t *q, int B, int S, int H, int D, int dv, i
 int orc_compress_append(int B, int D, int ratio, int start_pos, const float *kv, const float *score,
                         float *kv_state, float *score_state, const float *norm_w, double eps,
                         const float *freqs, int rd, uint8_t *codes, uint8_t *scales, int T_cap,
-                        double *latent);
+                        double *latent, double *pooled_raw, double *norm_raw);
+int orc_compress_write(int D, const double *latent, const float *freqs, int rd, int pos, uint8_t *codes,
+                       uint8_t *scales);
 int orc_window_append(int B, int D, int start_pos, const uint16_t *kv, const float *freqs, int rd, int R,
                       uint8_t *codes, uint8_t *scales);
 double orc_e4m3(uint8_t c);
@@ -112,15 +114,19 @@ int main(void) {
     for (int j = 0; j < D; ++j) nw[j] = 1.f;
     for (int j = 0; j < 32 * rd; ++j) fr[j] = (j & 1) ? 0.5f : 0.8660254f;
     uint8_t codes[B * T_cap * D / 2], scales[B * T_cap * D / 16], wc[B * R * D], ws[B * R * D / 32];
-    double lat[B * D];
+    double lat[B * D], praw[B * D], nraw[B * D];
     uint16_t wkv[B * D];
     for (int t = 0; t < 3 * ratio; ++t) {
         for (int j = 0; j < B * D; ++j) { kv[j] = (float)((int)(rnd() % 200) - 100) / 50.f; sc[j] = (float)(rnd() % 100) / 25.f; wkv[j] = (uint16_t)(0x3f00 + rnd() % 0x100); }
-        EXPECT(orc_compress_append(B, D, ratio, t, kv, sc, ks, gs, nw, 1e-6, fr, rd, codes, scales, T_cap, lat) ==
+        EXPECT(orc_compress_append(B, D, ratio, t, kv, sc, ks, gs, nw, 1e-6, fr, rd, codes, scales, T_cap, lat,
+                                   praw, nraw) ==
                ((t + 1) % ratio == 0));
         EXPECT(orc_window_append(B, D, t, wkv, fr, rd, R, wc, ws) == 0);
     }
-    EXPECT(orc_compress_append(B, D, 1, 2, kv, sc, NULL, NULL, nw, 1e-6, fr, rd, codes, scales, T_cap, NULL) == 1);
+    EXPECT(orc_compress_append(B, D, 1, 2, kv, sc, NULL, NULL, nw, 1e-6, fr, rd, codes, scales, T_cap, NULL, NULL,
+                               NULL) == 1);
+    EXPECT(orc_compress_write(D, lat, fr, rd, 3, codes, scales) == 0);
+    EXPECT(orc_compress_write(D + 1, lat, fr, rd, 3, codes, scales) < 0);
     /* refusals */
     EXPECT(orc_topk(NULL, 0, 1, 1, 0, 0, 4, NULL) < 0);
     EXPECT(orc_window_indices(1, 1, 0, 4, 0, NULL) < 0 || 1);

@@ -749,20 +749,83 @@ def test_sparse_attn_quantised_kv(orc, B, S, start_pos, D, dv, W, K, wf, cf):
 
 
 # ---------------------------------------------------------------------------------
-# producer side: the cache writes of decode steps (compressor pooling, norm, rotation,
-# quantised rows).  The pre-quantisation values are bf16 on both sides; they agree
-# exactly unless an fp32 intermediate lands within an ulp of a bf16 rounding midpoint,
-# so codes must agree exactly for all but a few elements, and those few may differ by
-# one code step.
+# producer side: the cache writes of decode steps and chunks (compressor pooling, norm,
+# rotation, quantised rows).  The window rows and every cache row computed from a given
+# latent are exact; the latents themselves may differ from the oracle's only by one bf16 step
+# at a rounding midpoint (the pages' fp32 pooling and norm are not bit-reproducible across exp
+# and rsqrt implementations and summation orders).
 # ---------------------------------------------------------------------------------
 def _dequant_fp4_rows(codes, scales):
     from tests.test_oracle_attention import _table_rows_e2m1
     return _table_rows_e2m1(codes, scales)  # codes x e4m3 scale per 16, exact
 
 
+def _bf16_flip_possible(raw, rel=3e-5):
+    """True where a value lies within `rel` (relative; broadcast) of a bf16 rounding
+    midpoint: there fp32 arithmetic in another order or with another exp / rsqrt may round
+    the other way."""
+    raw = np.asarray(raw, np.float64)
+    lo = torch.from_numpy(raw * (1 - rel)).to(torch.bfloat16).to(torch.float64).numpy()
+    hi = torch.from_numpy(raw * (1 + rel)).to(torch.bfloat16).to(torch.float64).numpy()
+    return lo != hi
+
+
+def _pool_magnitude(kv, score, ratio):
+    """Per pooled value, the sum of softmax(score)_r |kv_r| over the group's slots (kv,
+    score [..., ratio, D]): the scale of the fp32 rounding error of the pooling, which
+    cancellation can make far larger than the result itself."""
+    g = np.asarray(score, np.float64)
+    p = np.exp(g - g.max(axis=-2, keepdims=True))
+    return (p / p.sum(axis=-2, keepdims=True) * np.abs(np.asarray(kv, np.float64))).sum(axis=-2)
+
+
+def _check_latents(lat_g, lat_o, pooled_raw, norm_raw, pool_mag):
+    """The GPU's bf16 latents against the oracle's.  The pages pool and normalise in fp32
+    (the oracle: exactly, then bf16).  A latent may differ from the oracle's only where the
+    exact pooled value lies within fp32 noise of a bf16 rounding midpoint (16 fp32 ulps of
+    its group's magnitude, pool_mag; None: no pooling) -- by up to two bf16 steps -- or
+    where the exact normalised value does -- by one step; the latter within 3e-5 (relative)
+    plus what the pooled values of its row that may round the other way can move the row's
+    norm (each by one bf16 step: the sum of squares by at most 2 x^2 2^-7 per such value)."""
+    diff = lat_g != lat_o
+    if not diff.any():
+        return 0
+    pooled_raw = np.asarray(pooled_raw, np.float64)
+    bf = lambda v: torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()  # noqa: E731
+    if pool_mag is None:
+        near_pool = np.zeros(pooled_raw.shape, bool)
+    else:
+        tol = 16 * 2.0 ** -24 * np.asarray(pool_mag, np.float64)
+        near_pool = bf(pooled_raw - tol) != bf(pooled_raw + tol)
+    x = bf(pooled_raw)
+    ss = (x * x).sum(-1, keepdims=True)
+    dss = (2.0 * x * x * 2.0 ** -7 * near_pool).sum(-1, keepdims=True)
+    rel = 3e-5 + 0.6 * dss / np.maximum(ss, 1e-300)
+    # a pooled value one step off moves its latent by about one step, which may then round
+    # one step further: two steps there, one elsewhere
+    steps = np.abs(lat_g - lat_o) / np.maximum(2.0 ** -7 * np.abs(lat_o), 1e-300)
+    ok = (near_pool & (steps <= 2.0001)) | (_bf16_flip_possible(norm_raw, rel) & (steps <= 1.0001))
+    bad = diff & ~ok
+    assert not bad.any(), (f"{int(bad.sum())} latent(s) differ away from a rounding midpoint: "
+                           f"norm {np.asarray(norm_raw)[bad][:4]}, pooled {pooled_raw[bad][:4]}, "
+                           f"gpu {lat_g[bad][:4]}, oracle {lat_o[bad][:4]}")
+    return int(diff.sum())
+
+
+def _check_rows_from_latents(orc, lat_g, codes_g, scales_g, freqs, rd, positions):
+    """Rotation and quantisation of the GPU's own latents (the oracle's fp32 reading of the
+    rotation): the GPU's cache rows must match exactly."""
+    for b in range(lat_g.shape[0]):
+        for j, pos in enumerate(positions):
+            c, s = orc.compress_write(lat_g[b, j], freqs, rd, pos)
+            assert np.array_equal(codes_g[b, j], c) and np.array_equal(scales_g[b, j], s), (b, j, pos)
+
+
 @pytest.mark.parametrize("ratio,D,rd,B", [(4, 192, 64, 3), (2, 128, 32, 2), (1, 64, 16, 2),
                                           (4, 256, 64, 1)])
 def test_compress_append_steps(orc, ratio, D, rd, B):
+    """Decode steps of the compressor: state exact; latents per _check_latents; every cache
+    row equal to the oracle's rotation and quantisation of the GPU's latent."""
     steps = 3 * ratio + 1
     a = synth.make_append(B=B, D=D, rd=rd, ratio=ratio, steps=steps, positions=64, seed=70 + D)
     T_cap = steps // ratio + 1
@@ -774,11 +837,10 @@ def test_compress_append_steps(orc, ratio, D, rd, B):
     dc, dsc = dev(oc.copy()), dev(osc.copy())
     dw, dfr = dev(a.norm_w), dev(a.freqs)
     lat = torch.zeros((B, D), dtype=torch.bfloat16, device="cuda")
-    near = total = 0
     for t in range(steps):
-        w_o, lat_o = orc.compress_append(a.kv[t], a.score[t], ks if ratio > 1 else None,
-                                         gs if ratio > 1 else None, a.norm_w, a.eps, a.freqs, rd,
-                                         oc, osc, t, ratio)
+        w_o, lat_o, pr, nr = orc.compress_append(a.kv[t], a.score[t], ks if ratio > 1 else None,
+                                                 gs if ratio > 1 else None, a.norm_w, a.eps, a.freqs, rd,
+                                                 oc, osc, t, ratio, raw=True)
         w_g = L.lit_compress_append(dev(a.kv[t]), dev(a.score[t]), dks if ratio > 1 else None,
                                     dgs if ratio > 1 else None, dw, a.eps, dfr, rd, dc, dsc, t,
                                     ratio, latent=lat)
@@ -788,19 +850,18 @@ def test_compress_append_steps(orc, ratio, D, rd, B):
             assert np.array_equal(dks.cpu().numpy(), ks) and np.array_equal(dgs.cpu().numpy(), gs)
         if w_o:
             lg = bf16_host(lat)
-            assert np.all(np.abs(lg - lat_o) <= 2.0 ** -7 * np.abs(lat_o) + 1e-30), t
+            grp = slice(t + 1 - ratio, t + 1)
+            mag = _pool_magnitude(a.kv[grp].transpose(1, 0, 2), a.score[grp].transpose(1, 0, 2), ratio) \
+                if ratio > 1 else None
+            _check_latents(lg, lat_o, pr, nr, mag)
             row = t // ratio
-            cg, sg = dc.cpu().numpy()[:, row], dsc.cpu().numpy()[:, row]
-            assert np.abs(sg.astype(int) - osc[:, row].astype(int)).max() <= 1
-            vg, vo = _dequant_fp4_rows(cg, sg), _dequant_fp4_rows(oc[:, row], osc[:, row])
-            diff = vg != vo
-            near += int(diff.sum())
-            total += vg.size
-            assert np.all(np.abs(vg - vo)[diff] <= 2.0 * np.abs(vo)[diff] + 1e-6)
-    assert near <= max(2, total // 1000), f"{near} of {total} codes differ"
+            _check_rows_from_latents(orc, lg[:, None], dc.cpu().numpy()[:, row:row + 1],
+                                     dsc.cpu().numpy()[:, row:row + 1], a.freqs, rd, [t + 1 - ratio])
 
 
 def test_window_append_steps(orc):
+    """Decode-step window writes: codes and scales equal the oracle's exactly (the rotation
+    in the pages' fp32, the quantiser's decisions exact)."""
     B, D, rd, R = 3, 192, 64, 128
     a = synth.make_append(B=B, D=D, rd=rd, ratio=1, steps=5, positions=300, seed=81)
     oc = np.zeros((B, R, D), np.uint8)
@@ -810,10 +871,84 @@ def test_window_append_steps(orc):
         orc.window_append(a.win[t], a.freqs, rd, oc, osc, pos)
         L.lit_window_append(bf16_dev(a.win[t]), dfr, rd, dc, dsc, pos)
     torch.cuda.synchronize()
-    cg, sg = dc.cpu().numpy(), dsc.cpu().numpy()
-    assert np.array_equal(sg, osc)
-    mism = int((cg != oc).sum())
-    assert mism <= 2, f"{mism} window codes differ"
+    assert np.array_equal(dsc.cpu().numpy(), osc)
+    assert np.array_equal(dc.cpu().numpy(), oc)
+
+
+@pytest.mark.parametrize("ratio,S,start_pos,D,rd,B", [
+    (4, 4096, 0, 128, 64, 1),    # a prefill chunk of whole groups
+    (4, 1030, 0, 192, 64, 2),    # remainder 2 left in the state
+    (2, 301, 0, 128, 32, 2),     # odd chunk at ratio 2
+    (4, 37, 6, 128, 64, 2),      # a chunk starting inside a group (slots 0-1 from the state)
+    (4, 3, 5, 64, 16, 2),        # no group completes: every token to the state
+    (1, 90, 17, 64, 16, 2),      # ratio 1: a row per token
+])
+def test_compress_chunk(orc, ratio, S, start_pos, D, rd, B):
+    """A chunk into the compressor (lit_compress_chunk) against the oracle's chunk (the S
+    decode steps): rows written, the state exactly, latents per _check_latents, cache rows
+    exactly from the GPU's latents.  Earlier tokens (start_pos > 0) are fed first through
+    the same chunk call on both sides."""
+    a = synth.make_append(B=B, D=D, rd=rd, ratio=ratio, steps=start_pos + S, positions=start_pos + S + 1,
+                          seed=120 + S)
+    kv, sc = a.kv.transpose(1, 0, 2).copy(), a.score.transpose(1, 0, 2).copy()
+    T_cap = (start_pos + S) // ratio + 1
+    ks = np.zeros((B, ratio, D), np.float32)
+    gs = np.full((B, ratio, D), -np.inf, np.float32)
+    oc = np.zeros((B, T_cap, D // 2), np.uint8)
+    osc = np.zeros((B, T_cap, D // 16), np.uint8)
+    dks, dgs = dev(ks.copy()), dev(gs.copy())
+    dc, dsc = dev(oc.copy()), dev(osc.copy())
+    dw, dfr = dev(a.norm_w), dev(a.freqs)
+    if start_pos > 0:  # the tokens before the chunk, on both sides
+        orc.compress_chunk(kv[:, :start_pos], sc[:, :start_pos], ks, gs, a.norm_w, a.eps, a.freqs, rd, oc, osc, 0,
+                           ratio)
+        L.lit_compress_chunk(dev(kv[:, :start_pos]), dev(sc[:, :start_pos]), dks if ratio > 1 else None,
+                             dgs if ratio > 1 else None, dw, a.eps, dfr, rd, dc, dsc, 0, ratio)
+        torch.cuda.synchronize()
+        if ratio > 1:
+            assert np.array_equal(dks.cpu().numpy(), ks) and np.array_equal(dgs.cpu().numpy(), gs)
+        dc.copy_(torch.from_numpy(oc).cuda())    # continue from the oracle's rows (compared below)
+        dsc.copy_(torch.from_numpy(osc).cuda())
+    n_o, lat_o, pr, nr = orc.compress_chunk(kv[:, start_pos:], sc[:, start_pos:], ks, gs, a.norm_w, a.eps,
+                                            a.freqs, rd, oc, osc, start_pos, ratio)
+    lat = torch.zeros((B, max(n_o, 1), D), dtype=torch.bfloat16, device="cuda")
+    n_g = L.lit_compress_chunk(dev(kv[:, start_pos:]), dev(sc[:, start_pos:]), dks if ratio > 1 else None,
+                               dgs if ratio > 1 else None, dw, a.eps, dfr, rd, dc, dsc, start_pos, ratio,
+                               latent=lat)
+    torch.cuda.synchronize()
+    assert n_g == n_o == (start_pos + S) // ratio - start_pos // ratio
+    if ratio > 1:
+        assert np.array_equal(dks.cpu().numpy(), ks) and np.array_equal(dgs.cpu().numpy(), gs)
+    if n_o == 0:
+        assert np.array_equal(dc.cpu().numpy(), oc)
+        return
+    lg = bf16_host(lat)[:, :n_o]
+    r0 = start_pos // ratio
+    mag = None
+    if ratio > 1:
+        pos = (r0 + np.arange(n_o))[:, None] * ratio + np.arange(ratio)[None, :]   # [rows, ratio]
+        mag = _pool_magnitude(kv[:, pos], sc[:, pos], ratio)
+    _check_latents(lg, lat_o, pr, nr, mag)
+    _check_rows_from_latents(orc, lg, dc.cpu().numpy()[:, r0:r0 + n_o], dsc.cpu().numpy()[:, r0:r0 + n_o],
+                             a.freqs, rd, [(r0 + j) * ratio for j in range(n_o)])
+
+
+@pytest.mark.parametrize("S,start_pos,R", [(4096, 0, 128), (100, 0, 128), (300, 12288, 4223), (257, 40, 64)])
+def test_window_chunk(orc, S, start_pos, R):
+    """A chunk's window rows into the ring (lit_window_chunk) against the oracle's S
+    decode-step writes: codes and scales exactly, untouched slots unchanged."""
+    B, D, rd = 2, 128, 64
+    a = synth.make_append(B=B, D=D, rd=rd, ratio=1, steps=S, positions=start_pos + S + 1, seed=S + R)
+    win_bits = a.win.transpose(1, 0, 2).copy()
+    rng = np.random.default_rng(5)
+    oc = rng.integers(0, 256, size=(B, R, D), dtype=np.uint8)   # stale ring contents
+    osc = rng.integers(0, 256, size=(B, R, D // 32), dtype=np.uint8)
+    dc, dsc, dfr = dev(oc.copy()), dev(osc.copy()), dev(a.freqs)
+    orc.window_chunk(win_bits, a.freqs, rd, oc, osc, start_pos)
+    L.lit_window_chunk(bf16_dev(win_bits), dfr, rd, dc, dsc, start_pos)
+    torch.cuda.synchronize()
+    assert np.array_equal(dsc.cpu().numpy(), osc)
+    assert np.array_equal(dc.cpu().numpy(), oc)
 
 
 # ---------------------------------------------------------------------------------

@@ -85,8 +85,8 @@ MUTANTS = [
     ("KV e4m3 scale dropped", "for (int d = 0; d < D; ++d) v[d] = orc_e4m3(c[d]) * orc_e8m0(s[d / 32]);",
      "for (int d = 0; d < D; ++d) v[d] = orc_e4m3(c[d]);",
      [lambda o: TA.test_quantised_kv_equals_library_decoded_rows(o, 64)]),
-    ("rotation sign", "x[D - rd + 2 * j] = orc_round_bf16(a * c - b * sn);",
-     "x[D - rd + 2 * j] = orc_round_bf16(a * c + b * sn);", [TP.test_rmsnorm_closed_form_and_rotation]),
+    ("rotation sign", "const float re = ac - bs, im = as + bc;",
+     "const float re = ac + bs, im = as + bc;", [TP.test_rmsnorm_closed_form_and_rotation]),
     ("compressed rotation at the last token", "const int pos = start_pos + 1 - ratio; /* the group's first token */",
      "const int pos = start_pos;", [TP.test_compressor_group_timing_and_pooling]),
     ("fp4 quantiser tie rule", "int c = (a > 0.25 * s) + (a >= 0.75 * s)", "int c = (a > 0.25 * s) + (a > 0.75 * s)",

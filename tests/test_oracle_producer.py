@@ -182,3 +182,90 @@ def test_producer_refuses_bad_arguments(orc):
     with pytest.raises(orc.OracleError):              # row 2 of a 2-row cache
         orc.compress_append(a.kv[0], a.score[0], ks, gs, a.norm_w, a.eps, a.freqs, 16,
                             np.zeros((1, 2, 32), np.uint8), np.zeros((1, 2, 4), np.uint8), 11, 4)
+
+
+# -- chunks: the prefill seeding of the compressor state, the compressed rows and the ring --
+
+@pytest.mark.parametrize("ratio,S", [(4, 14), (2, 9), (4, 4), (4, 3)])
+def test_compress_chunk_is_the_pages_prefill(orc, ratio, S):
+    """At start_pos 0 a chunk is the pages' prefill branch (Compressor.forward): the whole
+    groups pooled at once -- kv times the softmax of the scores over each group's ratio
+    tokens, summed -- the remaining S % ratio tokens left in state slots 0.., and group j's
+    latent rotated at position j * ratio (Attention._compress_kv, freqs_cis[:cutoff:ratio]).
+    The pooled values are recomputed here from that formula (numpy, fp64)."""
+    B, D, rd = 2, 64, 16
+    a = synth.make_append(B=B, D=D, rd=rd, ratio=ratio, steps=S, positions=64, seed=90 + S)
+    kv, sc = a.kv.transpose(1, 0, 2).copy(), a.score.transpose(1, 0, 2).copy()
+    ks = np.zeros((B, ratio, D), np.float32)
+    gs = np.full((B, ratio, D), -np.inf, np.float32)
+    codes = np.zeros((B, S // ratio + 1, D // 2), np.uint8)
+    scales = np.zeros((B, S // ratio + 1, D // 16), np.uint8)
+    n, lat, pooled, _ = orc.compress_chunk(kv, sc, ks, gs, a.norm_w, a.eps, a.freqs, rd, codes, scales, 0, ratio)
+    cutoff = S - S % ratio
+    assert n == S // ratio == cutoff // ratio
+    g = sc[:, :cutoff].astype(np.float64).reshape(B, -1, ratio, D)
+    p = np.exp(g - g.max(axis=2, keepdims=True))
+    want = (kv[:, :cutoff].astype(np.float64).reshape(B, -1, ratio, D) * p / p.sum(axis=2, keepdims=True)).sum(axis=2)
+    np.testing.assert_allclose(pooled, want, rtol=1e-12, atol=0)
+    rem = S % ratio
+    assert np.array_equal(ks[:, :rem], kv[:, cutoff:]) and np.array_equal(gs[:, :rem], sc[:, cutoff:])
+    for b in range(B):
+        for j in range(n):
+            c, s = orc.compress_write(lat[b, j], a.freqs, rd, j * ratio)
+            assert np.array_equal(codes[b, j], c) and np.array_equal(scales[b, j], s)
+
+
+def test_compress_chunk_after_cached_tokens_continues_the_group(orc):
+    """A chunk that starts inside a group (start_pos % ratio != 0) pools that group with the
+    slots the earlier tokens left in the state; at every position the chunk equals the
+    decode steps it stands for."""
+    B, D, rd, ratio = 2, 64, 16, 4
+    a = synth.make_append(B=B, D=D, rd=rd, ratio=ratio, steps=13, positions=64, seed=97)
+    kv, sc = a.kv.transpose(1, 0, 2).copy(), a.score.transpose(1, 0, 2).copy()
+    st = lambda: (np.zeros((B, ratio, D), np.float32), np.full((B, ratio, D), -np.inf, np.float32))  # noqa: E731
+    cache = lambda: (np.zeros((B, 4, D // 2), np.uint8), np.zeros((B, 4, D // 16), np.uint8))  # noqa: E731
+    ks1, gs1 = st()
+    c1, s1 = cache()
+    orc.compress_chunk(kv[:, :6], sc[:, :6], ks1, gs1, a.norm_w, a.eps, a.freqs, rd, c1, s1, 0, ratio)
+    n, lat, _, _ = orc.compress_chunk(kv[:, 6:], sc[:, 6:], ks1, gs1, a.norm_w, a.eps, a.freqs, rd, c1, s1, 6, ratio)
+    assert n == 13 // ratio - 6 // ratio == 2
+    ks2, gs2 = st()
+    c2, s2 = cache()
+    lat2 = []
+    for t in range(13):
+        w, l2 = orc.compress_append(kv[:, t], sc[:, t], ks2, gs2, a.norm_w, a.eps, a.freqs, rd, c2, s2, t, ratio)
+        if w and t >= 6:
+            lat2.append(l2)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    assert np.array_equal(ks1, ks2) and np.array_equal(gs1, gs2)
+    assert np.array_equal(lat, np.stack(lat2, axis=1))
+
+
+@pytest.mark.parametrize("S,win", [(300, 128), (128, 128), (50, 128), (257, 64)])
+def test_window_chunk_seeds_the_ring_like_the_pages(orc, S, win):
+    """The pages' prefill seeding of the window ring (Attention._window_kv, start_pos 0):
+    with S <= win the chunk's rows fill slots 0..S-1; else, with cutoff = S % win, the last
+    win rows are split so that slots cutoff..win-1 take the first win - cutoff of them and
+    slots 0..cutoff-1 the rest.  Each row is rotated at its own position and quantised."""
+    B, D, rd = 2, 64, 16
+    a = synth.make_append(B=B, D=D, rd=rd, ratio=1, steps=S, positions=S + 1, seed=S + win)
+    win_bits = a.win.transpose(1, 0, 2).copy()
+    codes = np.zeros((B, win, D), np.uint8)
+    scales = np.zeros((B, win, D // 32), np.uint8)
+    orc.window_chunk(win_bits, a.freqs, rd, codes, scales, 0)
+    # the pages' split, as token positions per slot
+    slot_tok = np.full(win, -1)
+    if S <= win:
+        slot_tok[:S] = np.arange(S)
+    else:
+        cutoff = S % win
+        last = np.arange(S - win, S)
+        slot_tok[cutoff:win], slot_tok[:cutoff] = last[:win - cutoff], last[win - cutoff:]
+    for slot, t in enumerate(slot_tok):
+        if t < 0:
+            assert not codes[:, slot].any()
+            continue
+        one_c = np.zeros((B, 1, D), np.uint8)
+        one_s = np.zeros((B, 1, D // 32), np.uint8)
+        orc.window_append(win_bits[:, t], a.freqs, rd, one_c, one_s, int(t))  # slot t % 1 == 0
+        assert np.array_equal(codes[:, slot], one_c[:, 0]) and np.array_equal(scales[:, slot], one_s[:, 0]), slot
