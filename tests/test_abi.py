@@ -333,3 +333,46 @@ def test_step_args_keep_their_tensors_alive():
     del args
     gc.collect()
     assert ref() is None
+
+
+def test_compress_chunk_rows_matches_oracle(lib, orc):
+    """The rows a chunk writes (lit_compress_chunk_rows) equal the rows the oracle's chunk
+    writes, for chunks starting on and inside groups, and none for bad arguments."""
+    import numpy as np
+    for ratio in (1, 2, 4):
+        for start_pos in (0, 1, 3, 6):
+            for S in (0, 1, 3, 4, 9):
+                ks = np.zeros((1, ratio, 32), np.float32)
+                gs = np.full((1, ratio, 32), -np.inf, np.float32)
+                codes = np.zeros((1, 32, 16), np.uint8)
+                scales = np.zeros((1, 32, 2), np.uint8)
+                kv = np.ones((1, S, 32), np.float32)
+                n, _, _, _ = orc.compress_chunk(kv, kv, ks if ratio > 1 else None, gs if ratio > 1 else None,
+                                                np.ones(32, np.float32), 1e-6, np.zeros((32, 0, 2), np.float32),
+                                                0, codes, scales, start_pos, ratio) if S else (0, None, None, None)
+                assert lib.lit_compress_chunk_rows(start_pos, S, ratio) == n, (start_pos, S, ratio)
+    assert lib.lit_compress_chunk_rows(0, 8, 0) == 0
+    assert lib.lit_compress_chunk_rows(-1, 8, 2) == 0
+
+
+def test_chunk_producers_refuse_bad_arguments(lib):
+    """Refusals happen on the host, before any launch (no GPU is touched here)."""
+    import ctypes
+    P = ctypes.c_void_p
+    fake = P(256)  # never dereferenced: every call below is refused first
+    # ratio 0, negative start, D not a multiple of 32, D > 256, row past T_cap, rotation past n_pos
+    cases = [
+        dict(ratio=0), dict(start_pos=-1), dict(D=48), dict(D=288), dict(T_cap=1), dict(n_pos=4),
+    ]
+    for over in cases:
+        a = dict(B=1, S=8, D=64, ratio=2, start_pos=0, n_pos=64, rd=16, T_cap=16)
+        a.update(over)
+        st = lib.lit_compress_chunk(a["B"], a["S"], a["D"], a["ratio"], a["start_pos"], fake, fake, fake, fake,
+                                    fake, ctypes.c_float(1e-6), fake, a["n_pos"], a["rd"], fake, fake, a["T_cap"],
+                                    None, None)
+        assert st != 0, over
+    st = lib.lit_window_chunk(1, 8, 64, 0, fake, fake, 64, 16, fake, fake, 0, None)   # R = 0
+    assert st != 0
+    st = lib.lit_window_chunk(1, 8, 64, 60, fake, fake, 64, 16, fake, fake, 128, None)  # position 67 >= n_pos
+    assert st != 0
+    assert lib.lit_window_chunk(0, 8, 64, 0, None, None, 64, 16, None, None, 128, None) == 0  # empty batch
