@@ -90,8 +90,35 @@ def source_sha(srcs) -> str:
     return h.hexdigest()
 
 
+# The kernels a roofline line can name: the pattern their dispatches' names contain, and
+# the sources they are built from (a record is stale once these no longer hash the same).
+KERNELS = {
+    "fused_decode_kernel": ("fused_decode_kernel", ("fused_kernel.h", "fused_forms.hip")),
+    "indexer_scores_kernel": ("indexer_scores", ("indexer.hip",)),
+    "topk_kernel": ("topk", ("topk.hip",)),
+    "sparse_attn_kernel": ("sparse_attn", ("attention.hip",)),
+}
+
+
 def traffic_path(kernel: str, workload: str) -> str:
     return os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+
+
+def mfma_path(kernel: str, workload: str) -> str:
+    return os.path.join(PROFILES, f"{kernel}_{workload}_mfma.json")
+
+
+def mfma_busy_for(kernel: str, workload: str):
+    """The committed counter record of MFMA-busy cycles for this kernel on this workload
+    (the fraction of the launch's SIMD cycles the matrix cores were busy), or None when
+    there is none or the kernel's sources changed since."""
+    path = mfma_path(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("workload") != workload or rec.get("source_sha256") != source_sha(kernel_sources(KERNELS[kernel][1])):
+        return None
+    return rec.get("mfma_busy_frac")
 
 
 def traffic_for(kernel: str, workload: str, srcs):
@@ -112,11 +139,6 @@ def kernel_sources(ksrc):
     csrc = os.path.join(ROOT, "lightning_indexer_top_amd", "csrc")
     own = (ksrc,) if isinstance(ksrc, str) else tuple(ksrc)
     return [os.path.join(csrc, f) for f in own + ("tile_ops.h", "select_ops.h", "lit_internal.h")]
-
-
-def fused_sources(spec: dict):
-    """The fused kernel's sources (every form is fused_forms.hip instantiating fused_kernel.h)."""
-    return ("fused_kernel.h", "fused_forms.hip")
 
 
 def read_counters(path: str, counter: str) -> dict:
@@ -155,8 +177,9 @@ def traffic_record(fetch_path: str, write_path: str, kernel: str, ksrc: str, cop
         top = max(vals)
         return [v for v in vals if v >= 0.9 * top]
 
-    kf = pick(fetch, lambda n: kernel in n)
-    kw = pick(write, lambda n: kernel in n)
+    pat = KERNELS[kernel][0] if kernel in KERNELS else kernel
+    kf = pick(fetch, lambda n: pat in n)
+    kw = pick(write, lambda n: pat in n)
     cf, cw = copy_vals(fetch), copy_vals(write)
     kib = copy_mb * 1024.0
     ff = (sum(cf) / len(cf)) / kib
@@ -168,6 +191,25 @@ def traffic_record(fetch_path: str, write_path: str, kernel: str, ksrc: str, cop
             "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
             "copy_probe_mib": copy_mb, "copy_fetch_factor": round(ff, 4), "copy_write_factor": round(wf, 4),
             "bytes_per_launch": int(round((f_kib / ff + w_kib / wf) * 1024)), "command": cmd}
+
+
+def mfma_record(pmc_path: str, kernel: str, cus: int, xcds: int, cmd: str, workload: str) -> dict:
+    """MFMA utilisation of `kernel` from a rocprofv3 run with SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE: busy cycles summed over the SIMDs / (active cycles x 4 SIMDs x CUs).
+    GRBM_GUI_ACTIVE comes summed over the XCDs (each counts the launch's active cycles), so
+    one XCD's share is the launch's active time."""
+    busy = read_counters(pmc_path, "SQ_VALU_MFMA_BUSY_CYCLES")
+    active = read_counters(pmc_path, "GRBM_GUI_ACTIVE")
+    pat = KERNELS[kernel][0]
+    b = [v for n, vs in busy.items() if pat in n for v in vs]
+    a = [v for n, vs in active.items() if pat in n for v in vs]
+    if not b or not a:
+        raise SystemExit(f"no dispatch matched for {kernel}")
+    bb, aa = sum(b) / len(b), sum(a) / len(a) / xcds
+    return {"kernel": kernel, "workload": workload,
+            "source_sha256": source_sha(kernel_sources(KERNELS[kernel][1])),
+            "dispatches": len(b), "mfma_busy_cycles": round(bb, 1), "gui_active_cycles_per_xcd": round(aa, 1),
+            "compute_units": cus, "xcds": xcds, "mfma_busy_frac": round(bb / (aa * 4 * cus), 5), "command": cmd}
 
 
 def host_cpu() -> dict:
@@ -241,14 +283,24 @@ def main() -> int:
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH", "WRITE"),
                     help="write profiles/<kernel>_<workload>_traffic.json from rocprofv3 FETCH_SIZE / WRITE_SIZE "
                          "counter runs of this script with --copy-probe-mb, then exit (no GPU)")
-    ap.add_argument("--traffic-cmd", default="", help="the profiled command, recorded with --traffic-from")
+    ap.add_argument("--traffic-cmd", default="", help="the profiled command, recorded with --traffic-from / --mfma-from")
+    ap.add_argument("--traffic-kernel", default="fused_decode_kernel", choices=sorted(KERNELS),
+                    help="the kernel --traffic-from / --mfma-from records")
+    ap.add_argument("--mfma-from", metavar="PMC",
+                    help="write profiles/<kernel>_<workload>_mfma.json from a rocprofv3 run with "
+                         "SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE, then exit (no GPU)")
+    ap.add_argument("--cus", type=int, default=256, help="compute units, for --mfma-from")
+    ap.add_argument("--xcds", type=int, default=8, help="XCDs (GRBM_GUI_ACTIVE is summed over them), for --mfma-from")
     args = ap.parse_args()
-    if args.traffic_from:
-        from lightning_indexer_top_amd import synth
-        rec = traffic_record(args.traffic_from[0], args.traffic_from[1], "fused_decode_kernel",
-                             fused_sources(synth.WORKLOADS[args.workload]), args.copy_probe_mb or 256,
-                             args.traffic_cmd, args.workload)
-        path = traffic_path("fused_decode_kernel", args.workload)
+    if args.traffic_from or args.mfma_from:
+        kern = args.traffic_kernel
+        if args.traffic_from:
+            rec = traffic_record(args.traffic_from[0], args.traffic_from[1], kern, KERNELS[kern][1],
+                                 args.copy_probe_mb or 256, args.traffic_cmd, args.workload)
+            path = traffic_path(kern, args.workload)
+        else:
+            rec = mfma_record(args.mfma_from, kern, args.cus, args.xcds, args.traffic_cmd, args.workload)
+            path = mfma_path(kern, args.workload)
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")
@@ -467,34 +519,34 @@ def main() -> int:
     idx_tflops = idx_flops / (stages_us["indexer"] * 1e-6) / 1e12
     indexer_mfma = {"flops_per_step": int(idx_flops), "kernel_us": round(stages_us["indexer"], 3),
                     "achieved_tflops": round(idx_tflops, 2), "peak_tflops": mfma_peak,
-                    "frac": round(idx_tflops / mfma_peak, 5)}
+                    "frac": round(idx_tflops / mfma_peak, 5),
+                    "counter_mfma_busy_frac": mfma_busy_for("indexer_scores_kernel", args.workload)}
 
     step_gbps = sb["step"] / (ms_per_step * 1e-3) / 1e9
     if fused:
         # one kernel per step: its average duration is the event-timed region / K
-        dom, kname, ksrc = "step", "fused_decode_kernel", fused_sources(spec)
+        dom, kname = "step", "fused_decode_kernel"
         dom_us = gpu_ms * 1e3 / K
         dom_bytes = sb["step"]
     else:
         dom = max((k for k in stages_us if k in sb), key=stages_us.get)
-        kernels = {"indexer": ("indexer_scores_kernel", "indexer.hip"),
-                   "topk": ("topk_kernel", "topk.hip"),
-                   "attention": ("sparse_attn_kernel+attn_merge_kernel", "attention.hip")}
-        kname, ksrc = kernels[dom]
+        kname = {"indexer": "indexer_scores_kernel", "topk": "topk_kernel", "attention": "sparse_attn_kernel"}[dom]
         dom_us = stages_us[dom]
         dom_bytes = sb[dom]
+    ksrc = KERNELS[kname][1]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     if dom == "indexer" and spec["S"] > 1:
         # chunked prefill: the indexer's contraction is bound by the MFMA peak, not by HBM
         roofline = {"bound": "mfma", "achieved": indexer_mfma["achieved_tflops"], "peak": mfma_peak,
                     "unit": "TFLOP/s", "frac": indexer_mfma["frac"],
-                    "traffic": traffic_for(kname.split("+")[0], args.workload, kernel_sources(ksrc)),
+                    "traffic": traffic_for(kname, args.workload, kernel_sources(ksrc)),
+                    "mfma_busy_counter": mfma_busy_for(kname, args.workload),
                     "kernel": kname, "stage": dom, "flops_per_launch": indexer_mfma["flops_per_step"],
                     "avg_launch_us": round(dom_us, 3)}
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic_for(kname.split("+")[0], args.workload, kernel_sources(ksrc)),
+                    "traffic": traffic_for(kname, args.workload, kernel_sources(ksrc)),
                     "kernel": kname, "stage": dom, "bytes_per_launch": dom_bytes,
                     "avg_launch_us": round(dom_us, 3)}
 
