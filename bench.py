@@ -511,6 +511,38 @@ def main() -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / (stage_reps * len(calls))
 
+    source = None
+    if cand_kb:
+        # the candidate-source layer's own step (its top-k and attention, and level one of
+        # the two-level top-k into a block list), over the instance its blocks came from
+        src_argv, src_keep = [], []
+        for j in range(n_inst):
+            d = insts[(j + 1) % n_inst]
+            blocks = torch.empty_like(cands[j])
+            a, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
+                                           k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
+                                           comp_kv=d["comp_kv"], start_pos=spec["start_pos"],
+                                           ratio=spec["ratio"], index_topk=spec["index_topk"],
+                                           W=spec["W"], scale=spec["D"] ** -0.5, fmt=fmt,
+                                           cand_out=blocks, cand_topk_blocks=cand_kb,
+                                           cand_block_size=cand_bs, **kv_args(d))
+            src_argv.append(a)
+            src_keep.append((idx, out, blocks))
+        src_ws = L.step_workspace(src_argv[0], device=dev)
+        src_state = L.attach_state(src_argv[0], device=dev)
+        for a in src_argv[1:]:
+            L.attach_state(a, src_state)
+        src_us = timed_graph_us([(lambda j=j: L.lit_sparse_step(src_argv[j], src_ws)) for j in range(n_inst)])
+        if L.state_error(src_state):
+            log("[bench] the candidate source's fused step reported a team timeout: results invalid")
+            return 1
+        source = {"step_us": round(src_us, 3),
+                  "form": "fused kernel + level-one top-k" if src_state is not None
+                  else "indexer, block maxima, top-k x2, attention kernels",
+                  "level_one_kernels_us": round(stages_us["candidates"], 3)}
+        log(f"[bench] candidate-source layer step: {src_us:.2f} us ({source['form']})")
+        del src_argv, src_keep, src_ws, src_state
+
     # the indexer's contraction against the fp8 (fp4: 2x) MFMA peak: 2*Hi*Di flops per
     # visible (query, row), from the standalone indexer kernel's duration
     nvis_sum = sum(min(T, (spec["start_pos"] + i + 1) // spec["ratio"]) for i in range(spec["S"]))
@@ -606,6 +638,7 @@ def main() -> int:
                 "frac_of_copy": None if copy_gbps is None else round(step_gbps / copy_gbps, 4)},
         "indexer_mfma": indexer_mfma,
         "kernel_stages_us": {k: round(v, 3) for k, v in stages_us.items()},
+        **({"candidate_source": source} if source else {}),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

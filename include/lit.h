@@ -469,7 +469,9 @@ typedef struct lit_step_args {
     int index_format; /* lit_index_format of q8 / k8 (0 = LIT_INDEX_E4M3) */
     /* two-level top-k (lit_candidate_blocks / lit_topk_candidates); unused when
      * cand_in and cand_out are both NULL.  A level-two layer with 1..2048 blocks per
-     * query can run fused; a candidate source runs the multi-kernel form. */
+     * query can run fused; so can a candidate source whose cand_block_size divides
+     * the fused members' score chunks (any divisor of 256 does): the fused kernel
+     * writes the block maxima and one top-k kernel over them follows it. */
     const int32_t *cand_in; /* [B,S,cand_k]: level two -- this layer's rows outside
                                these blocks count as -inf before its top-k */
     int cand_k;

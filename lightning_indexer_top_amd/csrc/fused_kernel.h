@@ -272,6 +272,16 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         }
     }
     __syncthreads();
+    if (f.bmax) {  // level one of a candidate source: this chunk's block maxima
+        const int bs = f.bmax_bs;
+        const int jb0 = c0 / bs, jpin = (nvis - 1) / bs;
+        float *bq = f.bmax + (size_t)q * f.ldb;
+        for (int j = tid; j * bs < n; j += kThreads) {
+            float mx = -INFINITY;
+            for (int t = j * bs; t < min(j * bs + bs, n); ++t) mx = fmaxf(mx, sc[t]);
+            bq[jb0 + j] = jb0 + j == jpin ? INFINITY : mx;
+        }
+    }
     if constexpr (MASK) {
         if (select) {  // (every visible row is picked otherwise, masked or not)
 #pragma unroll

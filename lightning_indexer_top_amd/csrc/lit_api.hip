@@ -453,14 +453,14 @@ static size_t step_layout(const lit_step_args *s, size_t *scores_bytes, long *ld
 }
 
 // The fused kernel takes a level-two layer with 1..2048 candidate blocks per query; a
-// candidate source (cand_out) runs the multi-kernel form.
+// candidate source (cand_out) runs fused when its blocks divide the members' chunks (the
+// kernel writes the block maxima, level one's top-k follows as one kernel).
 constexpr int kFusedCandMaxApi = 2048;
 
 static FusedPlan step_fused_plan(const lit_step_args *s) {
     FusedPlan p{};
     p.ok = false;
     if (s->flags & LIT_STEP_UNFUSED) return p;
-    if (s->cand_out) return p;
     const bool masked = s->cand_in != nullptr;
     if (masked && (s->cand_k < 1 || s->cand_k > kFusedCandMaxApi)) return p;
     // quantised KV runs fused when both sources are quantised (e4m3 window, e2m1 compressed)
@@ -472,7 +472,16 @@ static FusedPlan step_fused_plan(const lit_step_args *s) {
                    s->dv, s->W, keff);
     // partial states are addressed with 32-bit offsets within a query's slots
     if (p.ok && fused_part_bytes_per_query(p, s->dv, step_layers(s)) >= ((size_t)1 << 31)) p.ok = false;
+    if (p.ok && s->cand_out && (s->cand_block_size < 1 || p.chunk % s->cand_block_size != 0)) p.ok = false;
     return p;
+}
+
+// Workspace of the fused step: the kernel's, then a candidate source's block maxima.
+static size_t step_fused_ws_bytes(const lit_step_args *s, const FusedPlan &fp) {
+    size_t need = round_up(fused_ws_bytes(fp, s->dv, step_layers(s)), 256);
+    if (s->cand_out)
+        need += lit_candidate_blocks_workspace_bytes(s->B, s->S, s->start_pos, s->ratio, s->cand_block_size);
+    return need;
 }
 
 static lit_status check_step(const lit_step_args *s) {
@@ -519,7 +528,7 @@ size_t lit_sparse_step_workspace_bytes(const lit_step_args *s) {
     size_t need = step_layout(s, &sb, &ld, &p);
     const FusedPlan fp = step_fused_plan(s);
     if (fp.ok) {
-        const size_t fused = fused_ws_bytes(fp, s->dv, step_layers(s));
+        const size_t fused = step_fused_ws_bytes(s, fp);
         if (fused > need) need = fused;
     }
     return need;
@@ -557,7 +566,7 @@ static lit_status step_run(const lit_step_args *s, void *ws, size_t ws_bytes, ui
     const FusedPlan fp = step_fused_plan(s);
     if (fp.ok && s->state && s->state_bytes >= fused_state_bytes(fp)) {
         if (((uintptr_t)s->state & 255u) != 0) return LIT_E_ALIGN;
-        if (ws_bytes < fused_ws_bytes(fp, s->dv, step_layers(s))) return LIT_E_WORKSPACE;
+        if (ws_bytes < step_fused_ws_bytes(s, fp)) return LIT_E_WORKSPACE;
         FusedArgs f{};
         f.ia = IndexerArgs{s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->index_format, s->B, s->S, s->Hi,
                            s->Di, s->T_cap, s->start_pos, s->ratio, T, nullptr, 0};
@@ -575,8 +584,21 @@ static lit_status step_run(const lit_step_args *s, void *ws, size_t ws_bytes, ui
         if (step_quant_kv(s) && set_kv_formats(f.aa, s->win_kv_format, s->win_kv, s->win_kv_scales,
                                                s->comp_kv_format, s->comp_kv, s->comp_kv_scales) != LIT_OK)
             return LIT_E_UNSUPPORTED;
+        const int kb = s->cand_out ? lit_candidate_blocks_width(s->S, s->start_pos, s->ratio, s->cand_topk_blocks,
+                                                                s->cand_block_size)
+                                   : 0;
+        if (kb > 0 && T > 0) {  // candidate source: the kernel writes level one's block maxima
+            f.bmax = (float *)((char *)ws + round_up(fused_ws_bytes(fp, s->dv, step_layers(s)), 256));
+            f.ldb = block_ld(s->S, s->start_pos, s->ratio, s->cand_block_size);
+            f.bmax_bs = s->cand_block_size;
+        }
         f.spin_limit = 1u << 22;
         if ((e = launch_fused(f, fp, ws, s->state, hs, err_word)) != hipSuccess) return hip_status(e);
+        if (f.bmax) {
+            TopkArgs la{f.bmax, f.ldb, s->B, s->S, s->start_pos, s->ratio, T, kb, s->cand_out};
+            la.vis_block = s->cand_block_size;
+            if ((e = launch_topk(la, hs)) != hipSuccess) return hip_status(e);
+        }
         for (int k = 1; k < 4; ++k)
             if ((e = mark(k)) != hipSuccess) return hip_status(e);
         return LIT_OK;

@@ -213,6 +213,12 @@ struct FusedArgs {
     // (masked kernels only; 1 <= cand_k <= 2048)
     const int32_t *cand = nullptr;
     int cand_k = 0, cand_bs = 1;
+    // level one of a candidate source: per query, the maxima of blocks of bmax_bs rows of
+    // the unmasked scores (the newest visible block +inf), [B*S, ldb]; NULL: none.  The
+    // chunk is a multiple of bmax_bs, so each block lies in one member's chunk.
+    float *bmax = nullptr;
+    long ldb = 0;
+    int bmax_bs = 1;
 };
 struct FusedPlan {
     bool ok;

@@ -594,8 +594,7 @@ def test_topk_candidates_short_and_empty_lists(orc):
 def test_step_two_level(orc, fmt, flags):
     """A candidate-source layer and a level-two layer of the 128K decode shape (at 32K
     context): the source's blocks come out of its step, the second layer's picks lie in
-    them, and both layers match the oracle.  The level-two layer runs fused or as
-    kernels; the source always runs as kernels."""
+    them, and both layers match the oracle.  Both layers run fused or as kernels."""
     kw = dict(B=2, S=1, start_pos=32767, ratio=4, Hi=64, Di=128, H=16, D=128, W=128,
               index_topk=512, keys="mixture", index_fmt=fmt)
     src = synth.make_step(seed=61, **kw)
@@ -608,7 +607,9 @@ def test_step_two_level(orc, fmt, flags):
                                       comp_kv=ds["comp_kv"], start_pos=src.start_pos,
                                       ratio=src.ratio, index_topk=src.index_topk, W=src.W,
                                       scale=src.scale, fmt=fmt, cand_out=cand,
-                                      cand_topk_blocks=256, cand_block_size=8)
+                                      cand_topk_blocks=256, cand_block_size=8, flags=flags)
+    st1 = L.attach_state(a1)
+    assert (st1 is not None) == (flags == 0)
     L.lit_sparse_step(a1, L.step_workspace(a1))
     a2, idx2, out2 = L.make_step_args(q8=d2["q8"], q_sc=d2["q_sc"], w=d2["w"], k8=d2["k8"],
                                       k_sc=d2["k_sc"], q=d2["q"], win_kv=d2["win_kv"],
@@ -620,7 +621,7 @@ def test_step_two_level(orc, fmt, flags):
     assert (st2 is not None) == (flags == 0)
     L.lit_sparse_step(a2, L.step_workspace(a2))
     torch.cuda.synchronize()
-    assert L.state_error(st2) == 0
+    assert L.state_error(st1) == 0 and L.state_error(st2) == 0
     ref1 = orc.step(src, cand_topk_blocks=256, cand_block_size=8)
     g_cand = cand.cpu().numpy()
     # level one decides on the kernel's fp32 scores; near-equal block maxima may swap
@@ -639,6 +640,53 @@ def test_step_two_level(orc, fmt, flags):
         assert ok, f"level-two picks of sequence {b}: {why}"
     want2 = _attn_on_list(orc, lvl2, ref2["win_idx"], d_idx2)
     assert np.abs(d_out2 - want2).max() <= ATTN_TOL
+
+
+SRC_STEP_CASES = [
+    # B, S, start_pos, ratio, Hi, Di, index_topk, topk_blocks, block_size, runs fused
+    (2, 1, 32767, 4, 64, 128, 512, 256, 8, True),     # the 128K decode shape at 32K context
+    (3, 1, 5001, 2, 32, 64, 256, 64, 16, True),       # 2501 rows: a short last block
+    (2, 1, 700, 4, 16, 64, 256, 512, 8, True),        # every row picked; more blocks asked than exist
+    (2, 3, 9001, 2, 64, 128, 512, 128, 4, True),      # three queries per sequence
+    (2, 1, 8191, 2, 64, 128, 512, 256, 3, False),     # blocks of 3 do not divide the chunks
+]
+
+
+@pytest.mark.parametrize("B,S,start_pos,ratio,Hi,Di,topk,kb,bs,fused", SRC_STEP_CASES)
+def test_candidate_source_step_exact(orc, B, S, start_pos, ratio, Hi, Di, topk, kb, bs, fused):
+    """A candidate-source step, fused where its blocks divide the members' score chunks.
+    Its block list is the oracle's level one over the GPU's own fp32 scores, exactly (the
+    fused kernel scores a decode query with the indexer kernel's arithmetic); its top-k
+    equals the kernels form's, and both forms meet the oracle's step rules."""
+    inp = synth.make_step(B=B, S=S, start_pos=start_pos, ratio=ratio, Hi=Hi, Di=Di, H=16, D=128,
+                          W=128, index_topk=topk, seed=500 + S + start_pos % 97)
+    d = step_inputs_dev(inp)
+    nb = orc.candidate_blocks_width(S, start_pos, ratio, kb, bs)
+    got = {}
+    for flags in (0, L.LIT_STEP_UNFUSED):
+        cand = torch.full((B, S, nb), -7, dtype=torch.int32, device="cuda")
+        a, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
+                                       k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
+                                       comp_kv=d["comp_kv"], start_pos=start_pos, ratio=ratio,
+                                       index_topk=topk, W=inp.W, scale=inp.scale, fmt=inp.index_fmt,
+                                       cand_out=cand, cand_topk_blocks=kb, cand_block_size=bs,
+                                       flags=flags)
+        st = L.attach_state(a)
+        assert (st is not None) == (flags == 0 and fused)
+        L.lit_sparse_step(a, L.step_workspace(a))
+        torch.cuda.synchronize()
+        assert L.state_error(st) == 0
+        _check_step(orc, inp, idx, out)
+        got[flags] = (cand.cpu().numpy(), idx)
+    sc = L.lit_indexer_scores(d["q8"], d["q_sc"], d["w"], d["k8"], d["k_sc"], start_pos, ratio,
+                              fmt=inp.index_fmt).cpu().numpy().astype(np.float64)
+    for i in range(S):
+        sc[:, i, min(inp.T, (start_pos + i + 1) // ratio):] = -np.inf
+    want = orc.candidate_blocks(sc, start_pos, ratio, kb, bs)
+    for flags, (cand, _) in got.items():
+        bad = np.argwhere((cand != want).any(-1))
+        assert bad.size == 0, (flags, bad[:3], cand[tuple(bad[0])][:12], want[tuple(bad[0])][:12])
+    assert torch.equal(got[0][1], got[L.LIT_STEP_UNFUSED][1])
 
 
 @pytest.mark.parametrize("flags", MODES)
