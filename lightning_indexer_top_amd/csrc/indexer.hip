@@ -242,7 +242,10 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_staged_kernel(Inde
 
 // 16 index heads of 64 e4m3 dims (the chunked-prefill shape): two queries' heads against 32
 // keys per V_MFMA_SCALE_F32_32X32X64_F8F6F4 (operand layout and epilogue in tile_ops.h).
-__global__ __launch_bounds__(kWaves * 64) void indexer_scores_mx32_kernel(IndexerArgs a) {
+// Seven waves a SIMD (at most 72 VGPRs, no spill; the unconstrained build takes 77 and six
+// waves): the kernel issues VALU about 60% of its time and waits on memory the rest, so one
+// more wave per SIMD hides more of the waits.
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(7))) void indexer_scores_mx32_kernel(IndexerArgs a) {
     constexpr int NH = 16, E = 64, NB = 2;
     __shared__ __attribute__((aligned(16))) uint8_t qc[kQB][NH * E];   // codes
     __shared__ __attribute__((aligned(16))) float qw[kQB][NH];         // head weights
