@@ -140,6 +140,14 @@ hipError_t launch_fused(FusedArgs f, const FusedPlan &p, void *ws, void *state, 
     f.win_tiles = p.win_tiles;
     f.vbins = p.vbins;
     f.n_slots = p.n_slots;
+    f.merge_per = (f.aa.L * kHeads * (f.aa.dv / 4) + p.team_size - 1) / p.team_size;
+    f.div_team = fast_div((uint32_t)p.team_size);
+    f.div_S = fast_div((uint32_t)f.ia.S);
+    f.div_ratio = fast_div((uint32_t)f.ia.ratio);
+    f.div_R = fast_div((uint32_t)(f.aa.R > 0 ? f.aa.R : 1));
+    f.div_qdv = fast_div((uint32_t)(f.aa.dv / 4));
+    f.div_hq = fast_div((uint32_t)(kHeads * (f.aa.dv / 4)));
+    f.div_cbs = fast_div((uint32_t)(f.cand_bs > 0 ? f.cand_bs : 1));
     f.ld = p.ld;
     f.cache_lds = p.cache_lds;
     f.lds_bins = p.lds_bins;

@@ -98,7 +98,7 @@ __device__ inline void stores_done() {
 
 struct FusedLds : SelLds {
     float fred[kThreads / 64];
-    int wcnt[kThreads / 64];
+    int wcnt[kThreads / 64];      // per-wave counts (attention list; then the top-k list ranges)
     uint32_t mm[kThreads / 64][2];
     uint32_t cnt[kTeamMax];       // the team's pick counts (from barrier C)
     uint32_t wpick[kThreads / 64];  // this member's picks counted by each wave
@@ -222,13 +222,15 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     // team / member of this workgroup (XCD-major order when the grid allows it)
     const int G = gridDim.x;
     const int lin = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-    const int q = lin / f.team_size;
-    const int m = lin % f.team_size;
+    // (the divisions by launch constants are multiplies by their FastDiv multipliers: they
+    // stand before the first key loads)
+    const int q = fdiv(lin, f.div_team);
+    const int m = lin - q * f.team_size;
     const IndexerArgs &ia = f.ia;
     const AttnArgs &aa = f.aa;
-    const int b = q / ia.S;
-    const int i = q % ia.S;
-    const int nvis = min(ia.T, (ia.start_pos + i + 1) / ia.ratio);
+    const int b = fdiv(q, f.div_S);
+    const int i = q - b * ia.S;
+    const int nvis = min(ia.T, fdiv(ia.start_pos + i + 1, f.div_ratio));
     const bool select = nvis > f.keff;  // otherwise every visible row is picked
     const int c0 = m * f.chunk;
     const int c1 = min(c0 + f.chunk, nvis);
@@ -248,8 +250,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
     // level two: the query's candidate blocks are requested now and turned into a bitmap
     // of the blocks that meet this member's chunk after scoring
     int cblk[MASK ? kFusedCandMax / kThreads : 1];
-    const int blk0 = MASK ? c0 / f.cand_bs : 0;
-    const int nbk = MASK && n > 0 ? (c1 - 1) / f.cand_bs - blk0 + 1 : 0;
+    const int blk0 = MASK ? fdiv(c0, f.div_cbs) : 0;
+    const int nbk = MASK && n > 0 ? fdiv(c1 - 1, f.div_cbs) - blk0 + 1 : 0;
     if constexpr (MASK) {
         const int32_t *cl = f.cand + (size_t)q * f.cand_k;
 #pragma unroll
@@ -292,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             }
             __syncthreads();
             for (int t = tid; t < n; t += kThreads) {
-                const int blk = (c0 + t) / f.cand_bs - blk0;
+                const int blk = fdiv(c0 + t, f.div_cbs) - blk0;
                 if (!((ckeep[blk >> 5] >> (blk & 31)) & 1u)) sc[t] = -INFINITY;
             }
             __syncthreads();
@@ -339,12 +341,15 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
 
     // window rows of this member, prefetched by waves 3, 2, ... (tile w -> wave 3 - w)
     const int nwin = window_width(ia.S, ia.start_pos, aa.W);
-    const int my_win = m < f.win_tiles ? (f.win_tiles - 1 - m) / f.team_size + 1 : 0;
+    const int my_win = m < f.win_tiles ? fdiv(f.win_tiles - 1 - m, f.div_team) + 1 : 0;
     const int win_w = 3 - wave;  // this wave's prefetched window tile, if < my_win
     // rows of a window tile; a lane off the list reads the query's own slot instead (always
     // attended), so that the loads need no branch
-    const int own_slot = (ia.start_pos + i) % max(aa.R, 1);
-    const WindowBase wbase = window_base(ia.start_pos, aa.W, max(aa.R, 1), i);
+    const int Rr = max(aa.R, 1);
+    const int own_slot = ia.start_pos + i - fdiv(ia.start_pos + i, f.div_R) * Rr;
+    WindowBase wbase;  // window_base(), its ring division by the multiplier
+    wbase.p0 = ia.start_pos == 0 ? max(i - aa.W + 1, 0) : ia.start_pos + i - aa.W + 1;
+    wbase.s0 = wbase.p0 >= 0 ? wbase.p0 - fdiv(wbase.p0, f.div_R) * Rr : window_base(ia.start_pos, aa.W, Rr, i).s0;
     // (layer l's window source: the layers sharing this top-k each have their own)
     auto win_tile_load = [&](WinRows &rows, int j, int l) {
         const int p0 = 32 * j + c, p1 = 32 * j + 16 + c;
@@ -717,7 +722,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         const int qdv = aa.dv / 4;
         const uint32_t my_off = (uint32_t)(m * NL * slot_bytes);
         for (int e = tid; e < kHeads * qdv; e += kThreads) {
-            const int h = e / qdv;
+            const int h = fdiv(e, f.div_qdv);
             const int d = 4 * (e - h * qdv);
             f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -802,7 +807,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         const int qdv = aa.dv / 4;
         const uint32_t my_off = (uint32_t)((m * NL + l) * slot_bytes);
         for (int e = tid; e < kHeads * qdv; e += kThreads) {
-            const int h = e / qdv;
+            const int h = fdiv(e, f.div_qdv);
             const int d = 4 * (e - h * qdv);
             f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -819,6 +824,30 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                               __float_as_uint(hl[h + 1])});
         }
     }
+    // The member's merge slice (phase M): `items` (layer, head, dim quad) outputs, each summed
+    // by lpi lanes, so waves [0, merge_waves) have merge work.
+    const int qdv_m = aa.dv / 4;
+    const int n_out_m = NL * kHeads * qdv_m;
+    const int per_m = f.merge_per;  // ceil(n_out_m / team_size)
+    const int items = max(0, min(m * per_m + per_m, n_out_m) - m * per_m);
+    int lpi = 1;
+    while (lpi * 2 * items <= kThreads && lpi < 16) lpi *= 2;
+    const int merge_waves = (min(items * lpi, kThreads) + 63) / 64;
+    // The member's picks go to the top-k list after barrier C, whose pick counts give their
+    // offset.  The last wave writes them when it has no merge work; when every wave merges,
+    // the writing is split into four contiguous ranges of the chunk's positions, one per
+    // wave after its merge work, and each range's pick count is taken here, while the
+    // partial-state stores complete.
+    const int nlw = merge_waves < kThreads / 64 ? 1 : kThreads / 64;  // list waves
+    const int lw0 = kThreads / 64 - nlw;                               // the first of them
+    const int lq = nlw == 1 ? (n + 63) & ~63 : ((n + 255) >> 8) << 6;  // positions per range
+    auto in_range = [&](int r, int p) { return p < n && p < (r + 1) * lq; };
+    if (nlw > 1) {
+        uint32_t cnt = 0;
+        for (int p0 = wave * lq; p0 < min(n, (wave + 1) * lq); p0 += 64)
+            cnt += (uint32_t)__popcll(__ballot(in_range(wave, p0 + lane) && picked(p0 + lane)));
+        if (lane == 0) sm.wcnt[wave] = (int)cnt;
+    }
     // barrier C: partial state published; the flag carries the member's pick count
     team_flag(slot_c, m, sm.wpick[0] + sm.wpick[1] + sm.wpick[2] + sm.wpick[3], 0u, (uint32_t)q, ep);
     team_poll(slot_c, f.team_size, (uint32_t)q, ep, f.spin_limit, f.err, sm.cnt);
@@ -831,22 +860,18 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
         // by a group of lpi <= 16 lanes (a power of two): every lane loads the O quad and
         // the (max, normaliser) pair of a stride of the slots, all in one round trip, and
         // the group combines its lanes with DPP exchanges.
-        const int qdv = aa.dv / 4;
-        const int n_out = NL * kHeads * qdv;  // (layer, head, dim quad)
-        const int per = (n_out + f.team_size - 1) / f.team_size;
-        const int e0 = m * per;
-        const int items = max(0, min(e0 + per, n_out) - e0);
-        int lpi = 1;
-        while (lpi * 2 * items <= kThreads && lpi < 16) lpi *= 2;
+        const int qdv = qdv_m;
+        const int e0 = m * per_m;  // (layer, head, dim quad) outputs items from e0
+        const int ls = __builtin_ctz((unsigned)lpi);  // lpi = 2^ls
         // rounds of kThreads / lpi items (one round unless lpi == 1 and items > kThreads)
-        for (int i0 = 0; i0 < items; i0 += kThreads / lpi) {
-            if (i0 + (wave * 64) / lpi >= items) continue;  // no item for this wave in this round
-            const int item = i0 + tid / lpi, sub = tid % lpi;
+        for (int i0 = 0; i0 < items; i0 += kThreads >> ls) {
+            if (i0 + ((wave * 64) >> ls) >= items) continue;  // no item for this wave in this round
+            const int item = i0 + (tid >> ls), sub = tid & (lpi - 1);
             const bool act = item < items;
             const int e = e0 + (act ? item : 0);
-            const int ly = e / (kHeads * qdv);
+            const int ly = fdiv(e, f.div_hq);
             const int eh = e - ly * kHeads * qdv;
-            const int h = eh / qdv;
+            const int h = fdiv(eh, f.div_qdv);
             const int d = 4 * (eh - h * qdv);
             const float *mlp = f.part + ((size_t)q * f.team_size * NL + ly) * f.slot_floats + kHeads * aa.dv + 2 * h;
             constexpr int kU = 8;
@@ -905,15 +930,19 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
             }
         }
     }
-    // The member's picks into the top-k list, ascending, by the last wave (which usually
-    // has no merge work): they start after the picks of the members before it, whose
-    // counts came with barrier C.
-    if (wave == kThreads / 64 - 1) {
+    // The member's picks into the top-k list, ascending, by the list waves (after their merge
+    // work, if any): range r starts after the picks of the members before this one (their
+    // counts came with barrier C) and of this member's earlier ranges.
+    if (wave >= lw0) {
+        const int r = wave - lw0;
         uint32_t pre = 0;
         for (int j = lane; j < m; j += 64) pre += sm.cnt[j];
         pre = wave_sum_u32(pre);
-        const int per = (n + 63) / 64;
-        const int t0 = lane * per, t1 = min(t0 + per, n);
+        for (int rr = 0; rr < r; ++rr) pre += (uint32_t)sm.wcnt[rr];
+        // lane l takes lq / 64 consecutive positions of the range (their score reads all
+        // issued together), the wave scan orders the lanes
+        const int per = lq / 64;
+        const int t0 = r * lq + lane * per, t1 = min(t0 + per, min(n, (r + 1) * lq));
         uint32_t mine = 0;
         for (int t = t0; t < t1; ++t) mine += picked(t) ? 1u : 0u;
         int o = (int)pre + (int)(wave_scan(mine) - mine);
@@ -922,7 +951,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs f) {
                 if (o < f.keff) idx_row[o] = c0 + t;
                 ++o;
             }
-        if (m == 0 && !select)
+        if (m == 0 && !select && r == nlw - 1)
             for (int j = nvis + lane; j < f.keff; j += 64) idx_row[j] = -1;
     }
 }

@@ -144,20 +144,21 @@ __host__ __device__ inline int window_slot(int S, int start_pos, int W, int R, i
 }
 
 // The same rule with the division done once per query: entry j of query i's list is
-// position p0 + j at ring slot (s0 + j) mod R.
+// position p0 + j at ring slot (s0 + j) mod R.  Positions stay below 2^31 (start_pos + S
+// is checked to fit an int), so 32-bit arithmetic is exact.
 struct WindowBase {
-    long p0;  // position of entry 0
-    int s0;   // its slot, p0 mod R in [0, R)
+    int p0;  // position of entry 0 (negative before the sequence's start)
+    int s0;  // its slot, p0 mod R in [0, R)
 };
 __host__ __device__ inline WindowBase window_base(int start_pos, int W, int R, int i) {
     WindowBase w;
-    w.p0 = start_pos == 0 ? (i - W + 1 > 0 ? i - W + 1 : 0) : (long)start_pos + i - W + 1;
-    const long m = w.p0 % R;
-    w.s0 = (int)(m < 0 ? m + R : m);
+    w.p0 = start_pos == 0 ? (i - W + 1 > 0 ? i - W + 1 : 0) : start_pos + i - W + 1;
+    const int m = w.p0 % R;
+    w.s0 = m < 0 ? m + R : m;
     return w;
 }
 __host__ __device__ inline int window_slot_at(const WindowBase &w, int start_pos, int R, int i, int j) {
-    const long p = w.p0 + j;
+    const int p = w.p0 + j;
     const bool valid = start_pos == 0 ? p <= i : p >= 0;
     int s = w.s0 + j;
     if (s >= R) s -= R;
@@ -192,6 +193,24 @@ hipError_t launch_window_chunk(const ProduceArgs &p, hipStream_t stream);
 // ---------------------------------------------------------------------------
 // Fused decode step (fused_decode.hip)
 // ---------------------------------------------------------------------------
+// Division by a divisor known at launch: for 0 <= n < 2^31, n / d = (n * m) >> s with
+// l = ceil(log2 d), s = 31 + l and m = ceil(2^s / d) < 2^32 (the multiplier of Granlund
+// and Montgomery's division by invariant integers, for 31-bit dividends).  A multiply and
+// a shift instead of a division sequence on the kernel's dependent paths.
+struct FastDiv {
+    uint32_t m = 1u << 31;
+    int s = 31;  // (the divisor 1)
+};
+inline FastDiv fast_div(uint32_t d) {
+    FastDiv f;
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    f.s = 31 + l;
+    f.m = (uint32_t)(((1ull << f.s) + d - 1) / d);
+    return f;
+}
+__device__ inline int fdiv(int n, FastDiv f) { return (int)(((uint64_t)(uint32_t)n * f.m) >> f.s); }
+
 struct FusedArgs {
     IndexerArgs ia;       // scores / ld unused
     AttnArgs aa;          // win_idx unused (window derived), comp_idx unused, part unused
@@ -206,6 +225,11 @@ struct FusedArgs {
     float *scores;                // per team: scores of the visible rows
     float *part;                  // per member: partial attention state
     int slot_floats;              // floats per member state
+    int merge_per;                // (layer, head, dim quad) outputs each member merges
+    // divisors of the kernel's index arithmetic: team size, queries per sequence, compress
+    // ratio, window ring rows, dim quads dv / 4, head-dim quads 16 * dv / 4, candidate
+    // block size
+    FastDiv div_team, div_S, div_ratio, div_R, div_qdv, div_hq, div_cbs;
     bool cache_lds;               // the team's scores are kept in LDS during selection
     bool lds_bins;                // otherwise: their 16-bit value bins are kept in LDS
     int bins_words;               // 32-bit words those bins take (candidate positions follow)
