@@ -68,7 +68,7 @@ __device__ inline void find_bin(const uint32_t *hist, int nbins, int need, uint3
 #pragma unroll
     for (int j = 0; j < 16; ++j) mine += cnt[j];
     uint32_t total;
-    const uint32_t incl = wg_scan<NT / 64>(mine, wsum, &total);
+    const uint32_t incl = wg_scan<NT / 64, false>(mine, wsum, &total);  // (a barrier closes this function)
     int above = (int)(incl - mine);
     if (above < need && need <= (int)incl) {
         int found = 0, fa = 0;

@@ -750,8 +750,10 @@ __device__ inline uint32_t wave_scan(uint32_t v) {
 // Inclusive scan over the workgroup (ascending thread id); *total gets the sum.  Every
 // thread of the workgroup must call it; NW = waves per workgroup (a constant, so that no
 // launch-size load -- and with it a wait on every outstanding load -- is emitted).
-// wsum needs NW entries.
-template <int NW>
+// wsum needs NW entries.  TAIL = false leaves out the closing barrier (which keeps a
+// following scan from overwriting wsum while it is still read) for callers that reach a
+// barrier of their own before wsum is written again.
+template <int NW, bool TAIL = true>
 __device__ inline uint32_t wg_scan(uint32_t v, uint32_t *wsum, uint32_t *total) {
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
@@ -766,7 +768,7 @@ __device__ inline uint32_t wg_scan(uint32_t v, uint32_t *wsum, uint32_t *total) 
         all += x;
     }
     *total = all;
-    __syncthreads();
+    if constexpr (TAIL) __syncthreads();
     return v + before;
 }
 

@@ -341,7 +341,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void topk_rows_kernel(TopkAr
         uint64_t *cand = reinterpret_cast<uint64_t *>(sm.hist);
         uint32_t total;
         const uint32_t mine = (uint32_t)__popc(cm);
-        int o = (int)(wg_scan<NT / 64>(mine, sm.wsum, &total) - mine);
+        int o = (int)(wg_scan<NT / 64, false>(mine, sm.wsum, &total) - mine);  // (a barrier follows the writes)
         if (cm) {
 #pragma unroll
             for (int r = 0; r < kRowQ; ++r)
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void topk_rows_kernel(TopkAr
     __syncthreads();
     uint32_t w = bm[tid];
     uint32_t total;
-    int o = (int)(wg_scan<NT / 64>((uint32_t)__popc(w), sm.wsum, &total) - (uint32_t)__popc(w));
+    int o = (int)(wg_scan<NT / 64, false>((uint32_t)__popc(w), sm.wsum, &total) - (uint32_t)__popc(w));
     while (w) {
         const int bit = __builtin_ctz(w);
         w &= w - 1u;
