@@ -209,7 +209,7 @@ inline FastDiv fast_div(uint32_t d) {
     f.m = (uint32_t)(((1ull << f.s) + d - 1) / d);
     return f;
 }
-__device__ inline int fdiv(int n, FastDiv f) { return (int)(((uint64_t)(uint32_t)n * f.m) >> f.s); }
+__host__ __device__ inline int fdiv(int n, FastDiv f) { return (int)(((uint64_t)(uint32_t)n * f.m) >> f.s); }
 
 struct FusedArgs {
     IndexerArgs ia;       // scores / ld unused
