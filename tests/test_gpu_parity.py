@@ -240,7 +240,7 @@ def test_sparse_attn_empty_lists_and_huge_sink(orc):
 # ---------------------------------------------------------------------------------
 # the fused step
 # ---------------------------------------------------------------------------------
-def _run_step(d, inp, flags=0, state=None):
+def _run_step(d, inp, flags=0, state=None, expect_fused=None):
     args, idx, out = L.make_step_args(q8=d["q8"], q_sc=d["q_sc"], w=d["w"], k8=d["k8"],
                                       k_sc=d["k_sc"], q=d["q"], win_kv=d["win_kv"],
                                       comp_kv=d["comp_kv"], start_pos=inp.start_pos,
@@ -249,6 +249,8 @@ def _run_step(d, inp, flags=0, state=None):
                                       fmt=inp.index_fmt, win_fmt=inp.win_kv_fmt, win_sc=d["win_sc"],
                                       comp_fmt=inp.comp_kv_fmt, comp_sc=d["comp_sc"])
     state = L.attach_state(args, state)
+    if expect_fused is not None:
+        assert (state is not None) == expect_fused, "fused form expected" if expect_fused else "kernels expected"
     ws = L.step_workspace(args)
     L.lit_sparse_step(args, ws)
     torch.cuda.synchronize()
@@ -316,6 +318,10 @@ STEP_SMALL = [
     # one-member teams: the merge covers more output words than a workgroup has threads
     dict(B=1, S=1, start_pos=400, ratio=2, Hi=16, Di=64, H=16, D=128, W=128, index_topk=64),
     dict(B=2, S=1, start_pos=450, ratio=2, Hi=32, Di=128, H=16, D=256, W=64, index_topk=100),
+    # twelve 8192-row queries (three sequences of four): teams of 32 members of 256 rows would
+    # exceed the device's co-resident workgroups, so the fused plan takes 512-row chunks (each
+    # wave scores two 64-key groups) -- ragged visibility across each sequence's queries
+    dict(B=3, S=4, start_pos=16380, ratio=2, Hi=16, Di=64, H=16, D=128, W=128, index_topk=512),
 ]
 
 
@@ -326,7 +332,7 @@ MODES = [pytest.param(0, id="fused"), pytest.param(L.LIT_STEP_UNFUSED, id="kerne
 @pytest.mark.parametrize("cfg", STEP_SMALL, ids=lambda c: f"B{c['B']}S{c['S']}p{c['start_pos']}r{c['ratio']}")
 def test_step_small(orc, cfg, flags):
     inp = synth.make_step(seed=4242 + cfg["start_pos"], **cfg)
-    idx, out = _run_step(step_inputs_dev(inp), inp, flags)
+    idx, out = _run_step(step_inputs_dev(inp), inp, flags, expect_fused=(flags == 0) if inp.T > 0 else None)
     _check_step(orc, inp, idx, out)
 
 
