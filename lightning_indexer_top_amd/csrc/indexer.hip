@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_kernel(IndexerArgs
                 float *dst = a.scores + (bs0 + i) * a.ld;
                 for (int u = 0; u < kU; ++u) {
                     const int t = t0 + 16 * u + c;
-                    if (t < a.T) dst[t] = -INFINITY;
+                    if (t < a.T && !a.visible_only) dst[t] = -INFINITY;
                 }
             }
         }
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_kernel(IndexerArgs
         const int i = i0 + qq;
         if (i < a.S && t < a.T) {
             const int vis = (a.start_pos + i + 1) / a.ratio;
-            a.scores[(bs0 + i) * a.ld + t] = t < vis ? s : -INFINITY;
+            if (t < vis || !a.visible_only) a.scores[(bs0 + i) * a.ld + t] = t < vis ? s : -INFINITY;
         }
     }
 }
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_multi_kernel(Index
             for (int i = i0; i < i1; ++i)
                 for (int u = 0; u < kU; ++u) {
                     const int tt = t0 + 16 * u + c;
-                    if (tt < a.T) a.scores[(bs0 + i) * a.ld + tt] = -INFINITY;
+                    if (tt < a.T && !a.visible_only) a.scores[(bs0 + i) * a.ld + tt] = -INFINITY;
                 }
         return;
     }
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_multi_kernel(Index
     auto finish = [&](int i, float s) {
         if (t < a.T) {
             const int vis = (a.start_pos + i + 1) / a.ratio;
-            a.scores[(bs0 + i) * a.ld + t] = t < vis ? s : -INFINITY;
+            if (t < vis || !a.visible_only) a.scores[(bs0 + i) * a.ld + t] = t < vis ? s : -INFINITY;
         }
     };
     IdxQuery<DI, FMT, HT> qa, qb;
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_staged_kernel(Inde
             for (int i = i0; i < i1; ++i)
                 for (int u = 0; u < kU; ++u) {
                     const int tt = t0 + 16 * u + c;
-                    if (tt < a.T) a.scores[(bs0 + i) * a.ld + tt] = -INFINITY;
+                    if (tt < a.T && !a.visible_only) a.scores[(bs0 + i) * a.ld + tt] = -INFINITY;
                 }
         return;
     }
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_scores_staged_kernel(Inde
         const float s = idx_score4<DI, FMT, HT>(qv, kb, g);
         if (t < a.T) {
             const int vis = (a.start_pos + i + 1) / a.ratio;
-            a.scores[(bs0 + i) * a.ld + t] = t < vis ? s : -INFINITY;
+            if (t < vis || !a.visible_only) a.scores[(bs0 + i) * a.ld + t] = t < vis ? s : -INFINITY;
         }
     }
 }
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(7))
     if (t0 >= a.T) return;
     if (t0 >= vis_max) {  // nothing visible to any query of the block in these keys
         const int tt = t0 + lane;
-        if (tt < a.T)
+        if (tt < a.T && !a.visible_only)
             for (int i = i0; i < i1; ++i) a.scores[(bs0 + i) * a.ld + tt] = -INFINITY;
         return;
     }
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(7))
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int t = t0 + 32 * m + c;
-                if (t < a.T) dst[t] = t < vis ? sc[m] : -INFINITY;
+                if (t < (a.visible_only ? vis : a.T)) dst[t] = t < vis ? sc[m] : -INFINITY;
             }
         }
     }

@@ -606,6 +606,7 @@ static lit_status step_run(const lit_step_args *s, void *ws, size_t ws_bytes, ui
     if (keff > 0) {
         IndexerArgs ia{s->q8, s->q_sc, s->w, s->k8, s->k_sc, s->index_format, s->B, s->S, s->Hi,
                        s->Di, s->T_cap, s->start_pos, s->ratio, T, scores, ld};
+        ia.visible_only = true;  // the top-k reads no column past a query's visible rows
         if ((e = launch_indexer_scores(ia, hs)) != hipSuccess) return hip_status(e);
     }
     if ((e = mark(1)) != hipSuccess) return hip_status(e);

@@ -37,6 +37,9 @@ struct IndexerArgs {
     int T;                // (start_pos + S) / ratio, columns written per row
     float *scores;        // [B,S,ld]
     long ld;
+    // only the visible columns are written (the step's own scores, which nothing reads past a
+    // query's visible rows); otherwise the invisible columns below T get -inf
+    bool visible_only = false;
 };
 hipError_t launch_indexer_scores(const IndexerArgs &a, hipStream_t stream);
 
