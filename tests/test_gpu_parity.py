@@ -322,6 +322,9 @@ STEP_SMALL = [
     # exceed the device's co-resident workgroups, so the fused plan takes 512-row chunks (each
     # wave scores two 64-key groups) -- ragged visibility across each sequence's queries
     dict(B=3, S=4, start_pos=16380, ratio=2, Hi=16, Di=64, H=16, D=128, W=128, index_topk=512),
+    # k_eff = 64 of T = 65: three of each sequence's four queries see at most k rows (all
+    # picked, the list padded with -1), the fourth needs a cut
+    dict(B=2, S=4, start_pos=126, ratio=2, Hi=16, Di=64, H=16, D=128, W=128, index_topk=64),
 ]
 
 
