@@ -418,7 +418,8 @@ lit_status lit_window_chunk(int B, int S, int D, int start_pos, const uint16_t *
  *
  * Decode-sized batches (B*S queries that fit the device's co-resident
  * workgroups) run as ONE kernel: a team of workgroups per query scores, selects,
- * gathers and merges, synchronising through counters in the workspace.  Larger
+ * gathers and merges, exchanging scores and partial attention states through the
+ * workspace and synchronising through flags in the state buffer.  Larger
  * batches (chunked prefill) run the indexer, top-k and attention kernels in turn.
  * flags & LIT_STEP_UNFUSED forces the multi-kernel form.
  *

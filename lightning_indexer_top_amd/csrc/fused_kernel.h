@@ -36,7 +36,8 @@
 //   M. Members merge the team's partial states (log-sum-exp) for a slice of the
 //      (layer, head, dim) outputs, add the sink, and write bf16.  Meanwhile the wave without
 //      merge work writes the member's picks to the top-k list (ascending), at the offset
-//      the pick counts of the members before it give.
+//      the pick counts of the members before it give (when every wave merges, each wave
+//      writes a quarter of the chunk's picks after its merge share).
 //
 // Cross-workgroup data moves through agent-scope relaxed atomic loads and stores and
 // coherent (sc1) 16-byte buffer loads and stores.  The barriers are flag arrays, not
