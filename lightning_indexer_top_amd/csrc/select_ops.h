@@ -39,7 +39,7 @@ __device__ inline float key_float(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
-// Bin search from the top over `nbins` LDS counters (256, 1024 or 4096): the bin where
+// Bin search from the top over `nbins` LDS counters (256, 1024, 2048 or 4096): the bin where
 // the count from the top reaches `need`, and the count strictly above it.  Thread t holds
 // the contiguous bins [nbins - per*(t+1), nbins - per*t), read as 16-byte words.
 template <int NT = kSelThreads>
@@ -152,14 +152,15 @@ __device__ inline void radix_resolve(SelLdsT<NT> &sm, Score score, int nvis, flo
 }
 
 // Narrows the candidates cand[0..cnt) (distinct (key, position) composites) while more
-// than kRankDirect remain: a 4096-bin histogram of the candidates over their own
+// than kRankDirect remain: an NB-bin histogram of the candidates over their own
 // [min, max] range (a monotone map, so bins are ordered like the composites), the bin
 // where the count from the top reaches need, and only that bin's candidates kept; need
 // becomes the rank within them.  Clustered scores put hundreds of candidates into one
-// value bin, and the direct rank costs cnt^2 comparisons.  h2 is 4096 words of LDS.
-template <int NT>
+// value bin, and the direct rank costs cnt^2 comparisons.  cand holds at most CAP
+// candidates; h2 is NB words of LDS (NB a multiple of 4 NT).
+template <int NT, int CAP = kCandCap, int NB = kBins>
 __device__ inline void refine_candidates(uint64_t *cand, int &cnt, int &need, uint32_t *h2, SelLdsT<NT> &sm) {
-    constexpr int kPer = kCandCap / NT;
+    constexpr int kPer = CAP / NT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int round = 0; round < 8 && cnt > kRankDirect; ++round) {
         uint64_t cv[kPer];
@@ -186,7 +187,7 @@ __device__ inline void refine_candidates(uint64_t *cand, int &cnt, int &need, ui
             sm.red64[wave][0] = lo;
             sm.red64[wave][1] = hi;
         }
-        for (int j = tid; j < kBins / 4; j += NT) reinterpret_cast<u32x4 *>(h2)[j] = u32x4{0u, 0u, 0u, 0u};
+        for (int j = tid; j < NB / 4; j += NT) reinterpret_cast<u32x4 *>(h2)[j] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
         lo = ~0ull;
         hi = 0ull;
@@ -194,13 +195,13 @@ __device__ inline void refine_candidates(uint64_t *cand, int &cnt, int &need, ui
             lo = min(lo, sm.red64[w][0]);
             hi = max(hi, sm.red64[w][1]);
         }
-        const float s2 = (float)(kBins - 1) / (float)(hi - lo);
-        auto bin_of = [&](uint64_t v) { return min(kBins - 1, (int)((float)(v - lo) * s2)); };
+        const float s2 = (float)(NB - 1) / (float)(hi - lo);
+        auto bin_of = [&](uint64_t v) { return min(NB - 1, (int)((float)(v - lo) * s2)); };
 #pragma unroll
         for (int r = 0; r < kPer; ++r)
             if (tid + NT * r < cnt) atomicAdd(&h2[bin_of(cv[r])], 1u);
         __syncthreads();
-        find_bin<NT>(h2, kBins, need, sm.wsum, &sm.bin, &sm.above);
+        find_bin<NT>(h2, NB, need, sm.wsum, &sm.bin, &sm.above);
         const int sb = sm.bin;
         need -= sm.above;
         if (tid == 0) sm.ncand = 0;

@@ -195,14 +195,17 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     }
 }
 
-constexpr int kRowQ = 8;  // score quads per thread: rows of up to 8192 positions
+constexpr int kRowQ = 8;                // score quads per thread: rows of up to 8192 positions
+constexpr int kRowCap = kCandCap / 2;   // candidates held in LDS (more take the radix levels)
+constexpr int kRowBins2 = kBins - 2 * kRowCap;  // bins of the candidate refinement
 
-// NT = 256: four rows a compute unit (128 VGPRs); NT = 1024 (rows of up to 32768 positions,
-// few rows): one 16-wave workgroup a row.
+// NT = 256: seven rows a compute unit (72 VGPRs; 16.5 KB of LDS, the row's whole LDS being
+// the selection's histogram, which later holds the candidates in its first half and their
+// refinement histogram in the second); NT = 1024 (rows of up to 32768 positions, few rows):
+// one 16-wave workgroup a row.
 template <int NT>
-__global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void topk_rows_kernel(TopkArgs a) {
+__global__ __launch_bounds__(NT, NT == 256 ? 7 : 1) void topk_rows_kernel(TopkArgs a) {
     __shared__ SelLdsT<NT> sm;
-    __shared__ __attribute__((aligned(16))) uint32_t h2[kBins];  // candidate refinement
     __shared__ uint32_t mm[NT / 64][2];
 
     const int row = blockIdx.x;
@@ -273,6 +276,10 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void topk_rows_kernel(TopkAr
         reinterpret_cast<u32x4 *>(sm.hist)[j] = u32x4{0u, 0u, 0u, 0u};
     uint32_t kmax, kmin;
     minmax(false, kmax, kmin);
+    // the scores pass through an empty asm, so that later uses take their order keys again
+    // rather than keeping these 32 alive
+#pragma unroll
+    for (int r = 0; r < kRowQ; ++r) asm volatile("" : "+v"(v[r]));
     float mx = key_float(kmax), mn = key_float(kmin);
     // An infinite end (level one of the two-level top-k pins one block at +inf) would stretch
     // the range to nothing: the range is then taken over the finite scores, and an infinity
@@ -287,24 +294,14 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void topk_rows_kernel(TopkAr
     const float scale = finite && mx > mn ? (float)kVBins / (mx - mn) : 0.f;
     const float bias = finite ? -mn * scale : 0.f;
 
-    // pass 1: value bins (16 bits each, kept) and the histogram.  Quads wholly past the row
-    // add nothing (a wave's quads are consecutive, so this is a wave-uniform skip outside
-    // the boundary wave); thousands of copies of one score would otherwise serialise on one
-    // bin's atomics.
-    uint32_t bins[kRowQ * 2];
+    // pass 1: the histogram of value bins.  Quads wholly past the row add nothing (a wave's
+    // quads are consecutive, so this is a wave-uniform skip outside the boundary wave);
+    // thousands of copies of one score would otherwise serialise on one bin's atomics.
 #pragma unroll
-    for (int r = 0; r < kRowQ; ++r) {
-        uint32_t bb[4] = {0u, 0u, 0u, 0u};
-        if (4 * (tid + NT * r) < n) {
+    for (int r = 0; r < kRowQ; ++r)
+        if (4 * (tid + NT * r) < n)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bb[e] = (uint32_t)value_bin(v[r][e], scale, bias);
-                atomicAdd(&sm.hist[bb[e]], 1u);
-            }
-        }
-        bins[2 * r] = bb[0] | (bb[1] << 16);
-        bins[2 * r + 1] = bb[2] | (bb[3] << 16);
-    }
+            for (int e = 0; e < 4; ++e) atomicAdd(&sm.hist[value_bin(v[r][e], scale, bias)], 1u);
     // the copies of position 0's score in the row's last, partial quad
     if (tid == 0 && (n & 3)) atomicSub(&sm.hist[value_bin(v0, scale, bias)], (uint32_t)(4 - (n & 3)));
     __syncthreads();
@@ -313,29 +310,32 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void topk_rows_kernel(TopkAr
     const int need = a.keff - sm.above;
     const int cnt = (int)sm.hist[vb];
     __syncthreads();  // every thread has read hist[vb]: both paths below overwrite the histogram
-    // per element (bit 4r+e): its bin is above vb (gm) or is vb (cm, the candidates).  On
-    // the packed bins (<= kVBins, 16 bits each): adding 0x7fff - vb (0x8000 - vb) to a half
-    // sets its bit 15 exactly when the bin is above (at least) vb, with no carry between
-    // the halves.
+    // per element (bit 4r+e): its bin is above vb (gm) or is vb (cm, the candidates).  The
+    // bins are taken again from the scores rather than kept (16 registers fewer): the bin is
+    // the clamped fma truncated, and for an integer c, truncation of a value x >= 0 is at
+    // least c exactly when x is, so the float comparisons below decide the same.
     uint32_t gm = 0u, cm = 0u;
     {
-        const uint32_t kgt = (0x7fffu - (uint32_t)vb) * 0x10001u;
-        const uint32_t kge = (0x8000u - (uint32_t)vb) * 0x10001u;
-        auto nib = [](uint32_t x0, uint32_t x1) {
-            return ((x0 >> 15) & 1u) | ((x0 >> 30) & 2u) | ((x1 >> 13) & 4u) | ((x1 >> 28) & 8u);
-        };
+        // opaque copies of the map, so that the compiler takes the bins again here instead
+        // of keeping pass 1's 32 values alive across the bin search
+        float rscale = scale, rbias = bias;
+        asm volatile("" : "+v"(rscale), "+v"(rbias));
+        const float fgt = (float)(vb + 1), fge = (float)vb;
 #pragma unroll
         for (int r = 0; r < kRowQ; ++r) {
-            const uint32_t a0 = bins[2 * r] + kgt, a1 = bins[2 * r + 1] + kgt;
-            const uint32_t b0 = bins[2 * r] + kge, b1 = bins[2 * r + 1] + kge;
-            gm |= nib(a0 & 0x80008000u, a1 & 0x80008000u) << (4 * r);
-            cm |= nib((a0 ^ b0) & 0x80008000u, (a1 ^ b1) & 0x80008000u) << (4 * r);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x = fminf(fmaxf(fmaf(v[r][e], rscale, rbias), 0.f), (float)(kVBins - 1));
+                gm |= (uint32_t)(x >= fgt) << (4 * r + e);
+                cm |= (uint32_t)(x >= fge && x < fgt) << (4 * r + e);
+            }
+            asm volatile("" : "+v"(gm), "+v"(cm));  // quad r's bins end here
         }
         gm &= vn;
         cm &= vn;
     }
     uint32_t kstar, pstar;
-    if (cnt <= kCandCap) {
+    if (cnt <= kRowCap) {
         // the scores of bin vb as (key << 32 | ~position), in the histogram's place; a
         // block scan over the threads' counts gives each its first slot
         uint64_t *cand = reinterpret_cast<uint64_t *>(sm.hist);
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void topk_rows_kernel(TopkAr
         }
         __syncthreads();
         int ncand = cnt, nneed = need;
-        refine_candidates(cand, ncand, nneed, h2, sm);
+        refine_candidates<NT, kRowCap, kRowBins2>(cand, ncand, nneed, sm.hist + 2 * kRowCap, sm);
         rank_candidates(cand, ncand, nneed, sm);
     } else {
         radix_resolve(sm, [&](int t) { return src[t]; }, n, scale, bias, vb, need);
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void topk_rows_kernel(TopkAr
 
     // output: a pick is key > kstar, or key == kstar at a position <= pstar: every element
     // above bin vb, and the candidates (bin vb) that pass the test.  The picks become a
-    // bitmap over positions in LDS (h2 is free again; word w covers positions 32w..32w+31,
+    // bitmap over positions in LDS (the histogram is free again; word w covers positions 32w..32w+31,
     // assembled from 8 lanes' nibbles), and thread t then writes the picks of word t at the
     // offset one block scan gives it, in ascending order.
     uint32_t pm = gm;
@@ -372,11 +372,11 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void topk_rows_kernel(TopkAr
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if ((cm >> (4 * r + e)) & 1u) {
-                    const uint32_t k = order_key(v[r][e]);
+                    const uint32_t k = order_key(src[pos(r, e)]);
                     if (k > kstar || (k == kstar && (uint32_t)pos(r, e) <= pstar)) pm |= 1u << (4 * r + e);
                 }
     }
-    uint32_t *bm = h2;
+    uint32_t *bm = sm.hist;
 #pragma unroll
     for (int r = 0; r < kRowQ; ++r) {
         // OR over the 8 lanes: swap neighbours, swap pairs (DPP quad permutations), then
