@@ -131,6 +131,9 @@ ROWS_CASES = [
     (1, 256, 9000, 2, 700, "two"),
     (1, 2100, 0, 2, 512, "normal"),      # 1050 positions from 0: rows of fewer than k padded
     (2, 3, 6000, 2, 300, "inf"),         # +inf and -inf among finite visible scores
+    (1, 16, 16000, 2, 512, "levels9"),   # ~890 equal scores in the cut's bin: the refinement
+                                         # near its 1024-candidate capacity
+    (1, 16, 16000, 2, 512, "levels5"),   # ~1600: past that capacity, the radix levels
 ]
 
 
@@ -138,9 +141,9 @@ ROWS_CASES = [
 def test_topk_many_rows_exact(orc, B, S, start_pos, ratio, k, kind):
     T = (start_pos + S) // ratio
     ld = (T + 3) // 4 * 4
-    if kind == "two":
+    if kind == "two" or kind.startswith("levels"):
         rng = np.random.Generator(np.random.PCG64(B * 7 + S))
-        sc = rng.integers(0, 2, size=(B, S, ld)).astype(np.float32)
+        sc = rng.integers(0, 2 if kind == "two" else int(kind[6:]), size=(B, S, ld)).astype(np.float32)
     elif kind == "inf":
         sc = synth.random_scores(B, S, ld, seed=B * 131 + S + k, ties=False)
         rng = np.random.Generator(np.random.PCG64(5))
