@@ -134,6 +134,8 @@ ROWS_CASES = [
     (1, 16, 16000, 2, 512, "levels9"),   # ~890 equal scores in the cut's bin: the refinement
                                          # near its 1024-candidate capacity
     (1, 16, 16000, 2, 512, "levels5"),   # ~1600: past that capacity, the radix levels
+    (1, 1100, 14000, 2, 512, "levels9"), # the same over 1100 rows
+    (1, 1100, 14000, 2, 512, "levels5"),
 ]
 
 
